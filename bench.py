@@ -1,0 +1,279 @@
+"""Benchmark: block-sparse attention over a paged KV cache on one MI355X.
+
+One step = the whole hot path on one batch: gbsa_metadata (task split) + gbsa_forward
+(main kernel and split-KV combine), inputs resident in HBM. The default workload is the
+decode-shaped one (64 sequences x 1 query token, 32768-token paged KV each, N1=32, N2=8,
+bf16, 16 selected pages per query): bound by HBM bytes, so the headline value is GB/s of
+algorithmic traffic. Effective TFLOP/s (selected blocks only) is reported beside it.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "fp8": 5000.0}
+ESIZE = {"f16": 2, "bf16": 2, "fp8": 1}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic_work(p):
+    """(bytes, flops) the method must move / compute, from the selection structure only.
+
+    bytes: K and V rows of every selected block below seqused_kv (once per unit and KV head),
+    Q and O rows of active queries, LSE if returned, the used index / count / page-table
+    entries. flops: 4 * D per (active query row, head, visible-length key) of selected blocks.
+    """
+    import gbsa_inputs as gi
+    D = 128
+    es = ESIZE[p.dtype]
+    G = p.num_heads_q // p.num_heads_kv
+    starts = gi.q_block_starts(p.cu_seqlens_q, p.block_x)
+    kv_bytes = 0
+    flops = 0
+    meta_bytes = 0
+    q_rows = 0
+    for b in range(p.batch):
+        storage = int(p.cu_seqlens_q[b + 1] - p.cu_seqlens_q[b])
+        sq = storage if p.seqused_q is None else min(int(p.seqused_q[b]), storage)
+        skv = int(p.seqused_kv[b])
+        q_rows += sq
+        nact = -(-sq // p.block_x)
+        if nact == 0:
+            continue
+        g = starts[b] + np.arange(nact)
+        rows = np.minimum((np.arange(nact) + 1) * p.block_x, sq) - np.arange(nact) * p.block_x
+        cnt = np.clip(p.sparse_block_count[:, g], 0, p.top_k)  # [N2, nact]
+        idx = p.sparse_block_idx[:, g, :]  # [N2, nact, topK]
+        slot = np.arange(p.top_k)[None, None, :]
+        used = slot < cnt[:, :, None]
+        j = np.where(used, idx, -1)
+        valid_tok = np.clip(skv - 128 * j.astype(np.int64), 0, 128) * (j >= 0)
+        tok = (valid_tok * used).sum(axis=2)  # [N2, nact]
+        kv_bytes += int(tok.sum()) * 2 * D * es
+        flops += int((tok * rows[None, :]).sum()) * 4 * D * G
+        meta_bytes += int(used.sum()) * 8 + cnt.size * 4  # idx + table entries, counts
+    out_es = 2
+    qo_bytes = q_rows * p.num_heads_q * D * (es + out_es)
+    lse_bytes = q_rows * p.num_heads_q * 4 if p.return_lse else 0
+    return kv_bytes + qo_bytes + lse_bytes + meta_bytes, flops
+
+
+def cpu_baseline(p, budget_s: float):
+    """The float64 oracle on a bounded sample of the same workload (rows of whole q-blocks)."""
+    import dataclasses
+
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    import gbsa_inputs as gi
+    from oracle import attention as oa
+
+    starts = gi.q_block_starts(p.cu_seqlens_q, p.block_x)
+    units = []
+    for b in range(p.batch):
+        storage = int(p.cu_seqlens_q[b + 1] - p.cu_seqlens_q[b])
+        sq = storage if p.seqused_q is None else int(p.seqused_q[b])
+        for gl in range(-(-sq // p.block_x)):
+            units.append((b, gl))
+    rng = np.random.default_rng(7)
+    rng.shuffle(units)
+
+    def host_inputs(sample):
+        pages = set()
+        for (b, gl) in sample:
+            g = starts[b] + gl
+            for n2 in range(p.num_heads_kv):
+                c = min(max(int(p.sparse_block_count[n2, g]), 0), p.top_k)
+                for j in p.sparse_block_idx[n2, g, :c]:
+                    if j >= 0 and 128 * int(j) < int(p.seqused_kv[b]):
+                        pages.add(int(p.block_table[b, j]))
+        pages = sorted(pages)
+        remap = np.full(p.num_pages, -1, dtype=np.int64)
+        remap[pages] = np.arange(len(pages))
+        sel = torch.as_tensor(pages, dtype=torch.long, device=p.k.device)
+
+        def host(t):
+            t = t.detach()
+            if p.dtype == "bf16":
+                return t.view(torch.int16).cpu().numpy().view(np.uint16)
+            if p.dtype == "fp8":
+                return t.view(torch.uint8).cpu().numpy()
+            return t.cpu().numpy()
+        table = np.where(p.block_table >= 0, remap[np.maximum(p.block_table, 0)], -1)
+        return oa.Inputs(host(p.q), host(p.k[sel]), host(p.v[sel]), p.sparse_block_idx,
+                         p.sparse_block_count, p.cu_seqlens_q, p.seqused_q, p.seqused_kv,
+                         table, dtype=p.dtype, block_x=p.block_x, scale=p.scale,
+                         mask_mode=p.mask_mode, win_left=p.win_left, win_right=p.win_right,
+                         q_scale=p.q_scale, k_scale=p.k_scale, v_scale=p.v_scale)
+
+    # grow the sample until the oracle has run for about budget_s seconds
+    n, done_units, elapsed = 1, [], 0.0
+    with threadpool_limits(limits=1):
+        while elapsed < budget_s and len(done_units) < len(units):
+            batch_units = units[len(done_units):len(done_units) + n]
+            inp = host_inputs(batch_units)
+            rows = []
+            for (b, gl) in batch_units:
+                lo = gl * p.block_x
+                hi = min((gl + 1) * p.block_x, inp.sq(b), inp.storage(b))
+                rows += list(int(p.cu_seqlens_q[b]) + np.arange(lo, hi))
+            t0 = time.perf_counter()
+            oa.sparse_attention(inp, rows=rows)
+            elapsed += time.perf_counter() - t0
+            done_units += batch_units
+            n *= 2
+    sub = dataclasses.replace(p)
+    # algorithmic bytes of just the sampled units
+    sel_mask = np.zeros(p.sparse_block_count.shape[1], dtype=bool)
+    keep = {(b, gl) for (b, gl) in done_units}
+    cnt = p.sparse_block_count.copy()
+    for b in range(p.batch):
+        storage = int(p.cu_seqlens_q[b + 1] - p.cu_seqlens_q[b])
+        for gl in range(-(-storage // p.block_x)):
+            if (b, gl) not in keep:
+                cnt[:, starts[b] + gl] = 0
+    sub = dataclasses.replace(p, sparse_block_count=cnt)
+    bytes_s, flops_s = algorithmic_work(sub)
+    # remove the Q/O bytes of rows outside the sample
+    return dict(units=len(done_units), seconds=elapsed, bytes=bytes_s, flops=flops_s)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2, help="workload id 1..5 (default 2)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle work for the CPU baseline (0 = skip)")
+    a = ap.parse_args(argv)
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the kernel has no cross-GPU path in this build "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import gbsa_inputs as gi
+    from block_sparse_paged_gbsa_amd import (gbsa_forward, gbsa_metadata, gbsa_num_workers,
+                                             gbsa_workspace_size, make_params)
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating workload {a.config} on the GPU")
+    p = gi.config(a.config, device=dev)
+    params = make_params(batch=p.batch, num_heads_q=p.num_heads_q, num_heads_kv=p.num_heads_kv,
+                         total_q=p.total_q, total_q_blocks=p.total_q_blocks, top_k=p.top_k,
+                         block_x=p.block_x, max_blocks_per_seq=p.block_table.shape[1],
+                         num_pages=p.num_pages, kv_page_stride=p.kv_page_stride,
+                         dtype=gi.TORCH_DTYPES[p.dtype], out_dtype=gi.TORCH_DTYPES[p.out_dtype],
+                         mask_mode=p.mask_mode, win_left=p.win_left, win_right=p.win_right,
+                         quant_mode=p.quant_mode, return_lse=p.return_lse,
+                         has_seqused_q=p.seqused_q is not None, scale=p.scale)
+    t = lambda x: torch.as_tensor(x).to(dev)
+    idx, cnt, cu, skv, table = (t(p.sparse_block_idx), t(p.sparse_block_count),
+                                t(p.cu_seqlens_q), t(p.seqused_kv), t(p.block_table))
+    squ = None if p.seqused_q is None else t(p.seqused_q)
+    f32 = lambda s: None if s is None else torch.as_tensor(s, dtype=torch.float32).to(dev)
+    qs, ks, vs = f32(p.q_scale), f32(p.k_scale), f32(p.v_scale)
+    meta = torch.empty(1024, dtype=torch.int32, device=dev)
+    out = torch.empty(p.q.shape, dtype=gi.TORCH_DTYPES[p.out_dtype], device=dev)
+    lse = torch.empty(p.q.shape[:2], dtype=torch.float32, device=dev) if p.return_lse else None
+    ws = torch.zeros(gbsa_workspace_size(params), dtype=torch.uint8, device=dev)
+    P = gbsa_num_workers(params)
+
+    def step():
+        gbsa_metadata(params, cnt, cu, squ, skv, meta)
+        gbsa_forward(params, p.q, p.k, p.v, idx, cnt, meta, cu, squ, skv, table, qs, ks, vs,
+                     None, out, lse, ws)
+
+    alg_bytes, alg_flops = algorithmic_work(p)
+    log(f"[bench] workers={P} algorithmic bytes={alg_bytes} flops={alg_flops}")
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    # whole steps, back to back
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(a.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / a.steps
+
+    # the forward launch alone (main kernel + split-KV combine), events on its stream
+    fe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(a.steps)]
+    for i in range(a.steps):
+        fe[i][0].record(stream)
+        gbsa_forward(params, p.q, p.k, p.v, idx, cnt, meta, cu, squ, skv, table, qs, ks, vs,
+                     None, out, lse, ws)
+        fe[i][1].record(stream)
+    torch.cuda.synchronize()
+    fwd_ms = float(np.mean([s.elapsed_time(e) for s, e in fe]))
+    status = int(ws[:4].view(torch.int32)[0].item())
+    assert status == 0, "metadata mismatch flagged by the kernels"
+    log(f"[bench] step {ms_step:.4f} ms, forward {fwd_ms:.4f} ms, wall {wall:.3f} s")
+
+    gbs = alg_bytes / (ms_step * 1e-3) / 1e9
+    tflops = alg_flops / (ms_step * 1e-3) / 1e12
+    hbm_bound = a.config == 2
+    if hbm_bound:
+        achieved = alg_bytes / (fwd_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+        metric_value, unit = gbs, "GB/s"
+    else:
+        achieved = alg_flops / (fwd_ms * 1e-3) / 1e12
+        peak = MFMA_PEAK_TFLOPS[p.dtype]
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None}
+        metric_value, unit = tflops, "TFLOP/s"
+
+    cpu = None
+    if a.cpu_budget > 0:
+        log("[bench] timing the float64 oracle on a sample")
+        cb = cpu_baseline(p, a.cpu_budget)
+        v = (cb["bytes"] / cb["seconds"] / 1e9) if hbm_bound else (cb["flops"] / cb["seconds"] / 1e12)
+        cpu = {"value": round(v, 6), "unit": unit, "cores": 1, "kind": "oracle",
+               "sample": f"{cb['units']} q-blocks (all KV heads) of the same workload, "
+                         f"{cb['seconds']:.1f} s of single-threaded float64 numpy"}
+    res = {
+        "metric": "block-sparse attn effective TFLOP/s + HBM GB/s, % of roofline, 1 MI355X",
+        "value": round(metric_value, 3), "unit": unit, "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": p.dtype, "data": "synthetic",
+        "config": {"workload": gi.CONFIG_NAMES[a.config], "batch": p.batch,
+                   "num_heads_q": p.num_heads_q, "num_heads_kv": p.num_heads_kv,
+                   "head_dim": 128, "block_shape": [p.block_x, 128], "top_k": p.top_k,
+                   "kv_pages": p.num_pages, "workers": P},
+        "effective_tflops": round(tflops, 3), "hbm_gbs": round(gbs, 2),
+        "forward_ms": round(fwd_ms, 5), "algorithmic_bytes": alg_bytes,
+        "algorithmic_flops": alg_flops, "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,289 @@
+// Host entry points of libgbsa: validation, launch planning and kernel launches.
+//
+// Mirrors the two-stage interface of the GenericBlockSparseAttention article (cf-1.com):
+// "two-stage call" (metadata operator, then the main operator), "aclnn API" (first stage
+// validates and sizes the workspace, second stage executes on a stream), "general
+// constraints" (D = 128, 128-token pages equal to blockShapeY, N1 % N2 == 0, group <= 128,
+// topK <= 256, empty tensors rejected, tensor values not checked at this stage), "mask" and
+// "quantisation" (mask 1 = causal; quant 0 or 5; scales only with quant 5).
+#include <math.h>
+#include <mutex>
+#include <string.h>
+
+#include "../../include/gbsa.h"
+#include "gbsa_internal.hpp"
+
+using namespace gbsa;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_mu;
+int g_cus[kMaxDevices] = {0};
+
+gbsa_status device_cus(int* cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return GBSA_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return GBSA_ERR_HIP;
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (g_cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            return GBSA_ERR_HIP;
+        g_cus[dev] = n;
+    }
+    *cus = g_cus[dev];
+    return GBSA_OK;
+}
+
+int64_t rows_per_unit(const gbsa_params* p) {
+    return (int64_t)p->block_x * (p->num_heads_q / p->num_heads_kv);
+}
+
+gbsa_status plan_workers(const gbsa_params* p, int* P_out) {
+    if (p->num_workers > 0) {
+        *P_out = p->num_workers;
+        return GBSA_OK;
+    }
+    int cus = 0;
+    gbsa_status st = device_cus(&cus);
+    if (st != GBSA_OK) return st;
+    const int64_t M = rows_per_unit(p);
+    int64_t P;
+    if (M <= kDecodeMaxRows) {
+        P = cus;
+    } else {
+        const int rows = prefill_rows_per_wg((int)M);
+        const int64_t nst = (M + rows - 1) / rows;
+        P = (2 * (int64_t)cus + nst - 1) / nst;
+    }
+    if (P < 1) P = 1;
+    if (P > kMaxWorkers) P = kMaxWorkers;
+    *P_out = (int)P;
+    return GBSA_OK;
+}
+
+void fill_fingerprint(const gbsa_params* p, int32_t* h) {
+    h[7] = p->num_heads_q;
+    h[8] = p->num_heads_kv;
+    h[9] = p->head_dim;
+    h[10] = p->block_x;
+    h[11] = p->block_y;
+    h[12] = p->top_k;
+    h[13] = p->mask_mode;
+    h[14] = p->quant_mode;
+    h[15] = p->total_q_blocks;
+    h[16] = p->batch;
+    h[17] = p->win_left;
+    h[18] = p->win_right;
+    h[19] = p->has_seqused_q;
+    h[20] = p->is_packed_gqa;
+}
+
+}  // namespace
+
+extern "C" {
+
+gbsa_status gbsa_check_params(const gbsa_params* p) {
+    if (p == nullptr) return GBSA_ERR_NULL;
+    if (p->batch == 0 || p->num_heads_q == 0 || p->num_heads_kv == 0 || p->head_dim == 0 ||
+        p->total_q == 0 || p->total_q_blocks == 0 || p->top_k == 0 || p->block_x == 0 ||
+        p->max_blocks_per_seq == 0 || p->num_pages == 0)
+        return GBSA_ERR_EMPTY;
+    if (p->batch < 0 || p->num_heads_q < 0 || p->num_heads_kv < 0 || p->total_q < 0 ||
+        p->total_q_blocks < 0 || p->top_k < 0 || p->block_x < 0 || p->max_blocks_per_seq < 0 ||
+        p->num_pages < 0)
+        return GBSA_ERR_SHAPE;
+    if (p->head_dim != GBSA_HEAD_DIM) return GBSA_ERR_SHAPE;
+    if (p->block_y != GBSA_PAGE_SIZE || p->page_size != GBSA_PAGE_SIZE) return GBSA_ERR_SHAPE;
+    if (p->num_heads_q % p->num_heads_kv != 0) return GBSA_ERR_SHAPE;
+    if (p->num_heads_q / p->num_heads_kv > GBSA_MAX_GROUP) return GBSA_ERR_SHAPE;
+    if (p->top_k > GBSA_MAX_TOPK) return GBSA_ERR_SHAPE;
+    if (p->win_left < -1 || p->win_right < -1) return GBSA_ERR_SHAPE;
+    if (p->num_workers < 0 || p->num_workers > GBSA_MAX_WORKERS) return GBSA_ERR_SHAPE;
+    const int64_t page_elems = (int64_t)GBSA_PAGE_SIZE * p->num_heads_kv * p->head_dim;
+    if (p->kv_page_stride != 0 &&
+        (p->kv_page_stride < page_elems ||
+         p->kv_page_stride % ((int64_t)p->num_heads_kv * p->head_dim) != 0))
+        return GBSA_ERR_SHAPE;
+    if (p->batch > GBSA_MAX_BATCH) return GBSA_ERR_UNSUPPORTED;
+    if ((int64_t)p->num_heads_kv * p->total_q_blocks >= kMaxUnits) return GBSA_ERR_UNSUPPORTED;
+    if (p->dtype < GBSA_DTYPE_F16 || p->dtype > GBSA_DTYPE_FP8_E4M3) return GBSA_ERR_DTYPE;
+    if (p->out_dtype != GBSA_DTYPE_F16 && p->out_dtype != GBSA_DTYPE_BF16) return GBSA_ERR_DTYPE;
+    if (p->quant_mode != GBSA_QUANT_NONE && p->quant_mode != GBSA_QUANT_FP8_E4M3)
+        return GBSA_ERR_UNSUPPORTED;
+    if (p->quant_mode == GBSA_QUANT_FP8_E4M3) {
+        if (p->dtype != GBSA_DTYPE_FP8_E4M3) return GBSA_ERR_DTYPE;
+    } else {
+        if (p->dtype == GBSA_DTYPE_FP8_E4M3) return GBSA_ERR_DTYPE;
+        if (p->out_dtype != p->dtype) return GBSA_ERR_DTYPE;
+    }
+    if (p->mask_mode != GBSA_MASK_NONE && p->mask_mode != GBSA_MASK_CAUSAL)
+        return GBSA_ERR_UNSUPPORTED;
+    if (p->softmax_precision != 0 && p->softmax_precision != 1) return GBSA_ERR_UNSUPPORTED;
+    if (p->is_packed_gqa != 1) return GBSA_ERR_UNSUPPORTED;
+    if (p->has_seqused_q != 0 && p->has_seqused_q != 1) return GBSA_ERR_SHAPE;
+    if (p->return_lse != 0 && p->return_lse != 1) return GBSA_ERR_SHAPE;
+    for (int i = 0; i < 4; ++i)
+        if (p->reserved[i] != 0) return GBSA_ERR_UNSUPPORTED;
+    if (!(p->scale == p->scale)) return GBSA_ERR_SHAPE;  // NaN
+    return GBSA_OK;
+}
+
+gbsa_status gbsa_num_workers(const gbsa_params* p, int32_t* num_workers) {
+    gbsa_status st = gbsa_check_params(p);
+    if (st != GBSA_OK) return st;
+    if (num_workers == nullptr) return GBSA_ERR_NULL;
+    int P = 0;
+    st = plan_workers(p, &P);
+    if (st != GBSA_OK) return st;
+    *num_workers = P;
+    return GBSA_OK;
+}
+
+gbsa_status gbsa_workspace_size(const gbsa_params* p, size_t* bytes) {
+    gbsa_status st = gbsa_check_params(p);
+    if (st != GBSA_OK) return st;
+    if (bytes == nullptr) return GBSA_ERR_NULL;
+    int P = 0;
+    st = plan_workers(p, &P);
+    if (st != GBSA_OK) return st;
+    *bytes = ws_layout(P, rows_per_unit(p)).total;
+    return GBSA_OK;
+}
+
+gbsa_status gbsa_metadata(const gbsa_params* p, const int32_t* sparse_block_count,
+                          const int64_t* cu_seqlens_q, const int32_t* seqused_q,
+                          const int32_t* seqused_kv, int32_t* metadata, hipStream_t stream) {
+    gbsa_status st = gbsa_check_params(p);
+    if (st != GBSA_OK) return st;
+    if (sparse_block_count == nullptr || cu_seqlens_q == nullptr || seqused_kv == nullptr)
+        return GBSA_ERR_NULL;
+    if ((seqused_q != nullptr) != (p->has_seqused_q == 1)) return GBSA_ERR_NULL;
+    if (metadata == nullptr) return GBSA_ERR_METADATA;
+    int P = 0;
+    st = plan_workers(p, &P);
+    if (st != GBSA_OK) return st;
+    MetaArgs a;
+    memset(&a, 0, sizeof(a));
+    a.count = sparse_block_count;
+    a.cu = cu_seqlens_q;
+    a.squ = seqused_q;
+    a.meta = metadata;
+    a.B = p->batch;
+    a.N2 = p->num_heads_kv;
+    a.X = p->block_x;
+    a.topK = p->top_k;
+    a.tqb = p->total_q_blocks;
+    a.P = P;
+    fill_fingerprint(p, a.header);
+    return launch_metadata(a, stream) == hipSuccess ? GBSA_OK : GBSA_ERR_HIP;
+}
+
+gbsa_status gbsa_forward(const gbsa_params* p, const void* query, const void* key,
+                         const void* value, const int32_t* sparse_block_idx,
+                         const int32_t* sparse_block_count, const int32_t* metadata,
+                         const int64_t* cu_seqlens_q, const int32_t* seqused_q,
+                         const int32_t* seqused_kv, const int32_t* block_table,
+                         const float* q_scale, const float* k_scale, const float* v_scale,
+                         const float* p_scale, void* attention_out, float* softmax_lse,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    gbsa_status st = gbsa_check_params(p);
+    if (st != GBSA_OK) return st;
+    if (query == nullptr || key == nullptr || value == nullptr || sparse_block_idx == nullptr ||
+        sparse_block_count == nullptr || cu_seqlens_q == nullptr || seqused_kv == nullptr ||
+        block_table == nullptr || attention_out == nullptr)
+        return GBSA_ERR_NULL;
+    if ((seqused_q != nullptr) != (p->has_seqused_q == 1)) return GBSA_ERR_NULL;
+    if ((softmax_lse != nullptr) != (p->return_lse == 1)) return GBSA_ERR_NULL;
+    if (metadata == nullptr) return GBSA_ERR_METADATA;
+    const bool quant = p->quant_mode == GBSA_QUANT_FP8_E4M3;
+    if (quant && (q_scale == nullptr || k_scale == nullptr || v_scale == nullptr))
+        return GBSA_ERR_DTYPE;
+    if (!quant && (q_scale != nullptr || k_scale != nullptr || v_scale != nullptr))
+        return GBSA_ERR_DTYPE;
+    if (p_scale != nullptr) return GBSA_ERR_UNSUPPORTED;
+    int P = 0;
+    st = plan_workers(p, &P);
+    if (st != GBSA_OK) return st;
+    const int64_t M = rows_per_unit(p);
+    const WsLayout L = ws_layout(P, M);
+    if (workspace == nullptr || workspace_bytes < L.total) return GBSA_ERR_WORKSPACE;
+
+    FwdArgs a;
+    memset(&a, 0, sizeof(a));
+    a.q = query;
+    a.k = key;
+    a.v = value;
+    a.idx = sparse_block_idx;
+    a.cnt = sparse_block_count;
+    a.meta = metadata;
+    a.cu = cu_seqlens_q;
+    a.squ = seqused_q;
+    a.skv = seqused_kv;
+    a.table = block_table;
+    a.qs = q_scale;
+    a.ks = k_scale;
+    a.vs = v_scale;
+    a.out = attention_out;
+    a.lse = softmax_lse;
+    unsigned char* ws = (unsigned char*)workspace;
+    a.ws_status = (int32_t*)(ws + L.status);
+    a.ws_desc = (PieceDesc*)(ws + L.desc);
+    a.ws_o = (float*)(ws + L.o);
+    a.ws_m = (float*)(ws + L.m);
+    a.ws_l = (float*)(ws + L.l);
+    const int64_t page_elems = (int64_t)GBSA_PAGE_SIZE * p->num_heads_kv * p->head_dim;
+    a.kv_stride = p->kv_page_stride != 0 ? p->kv_page_stride : page_elems;
+    a.B = p->batch;
+    a.N1 = p->num_heads_q;
+    a.N2 = p->num_heads_kv;
+    a.G = p->num_heads_q / p->num_heads_kv;
+    a.X = p->block_x;
+    a.topK = p->top_k;
+    a.tqb = p->total_q_blocks;
+    a.maxb = p->max_blocks_per_seq;
+    a.P = P;
+    a.M = (int32_t)M;
+    a.mask = p->mask_mode;
+    a.wl = p->win_left;
+    a.wr = p->win_right;
+    a.return_lse = p->return_lse;
+    const double scale = p->scale > 0.f ? (double)p->scale : 1.0 / sqrt((double)p->head_dim);
+    a.scale_log2 = (float)(scale * 1.4426950408889634);
+    a.expect[0] = (int32_t)kMagic;
+    a.expect[1] = kVersion;
+    a.expect[2] = P;
+    fill_fingerprint(p, a.expect);
+
+    hipError_t e;
+    if (M <= kDecodeMaxRows) {
+        a.nst = 1;
+        e = launch_decode(a, p->dtype, p->out_dtype, stream);
+    } else {
+        const int rows = prefill_rows_per_wg((int)M);
+        a.nst = (int32_t)((M + rows - 1) / rows);
+        e = launch_prefill(a, p->dtype, p->out_dtype, rows, stream);
+    }
+    if (e != hipSuccess) return GBSA_ERR_HIP;
+    e = launch_combine(a, p->out_dtype, stream);
+    return e == hipSuccess ? GBSA_OK : GBSA_ERR_HIP;
+}
+
+const char* gbsa_status_string(gbsa_status s) {
+    switch (s) {
+        case GBSA_OK: return "ok";
+        case GBSA_ERR_NULL: return "a required pointer is NULL (or an optional one is inconsistent with its flag)";
+        case GBSA_ERR_SHAPE: return "a dimension violates a constraint (D=128, page=blockShapeY=128, N1%N2==0, group<=128, topK<=256, strides)";
+        case GBSA_ERR_DTYPE: return "unsupported or inconsistent data type or dequant scales";
+        case GBSA_ERR_UNSUPPORTED: return "attribute value not supported (mask/quant mode, packed GQA, batch or unit count limits)";
+        case GBSA_ERR_EMPTY: return "a required tensor has an empty axis";
+        case GBSA_ERR_WORKSPACE: return "workspace missing or smaller than gbsa_workspace_size";
+        case GBSA_ERR_METADATA: return "metadata buffer missing";
+        case GBSA_ERR_HIP: return "HIP runtime error (device query or kernel launch)";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

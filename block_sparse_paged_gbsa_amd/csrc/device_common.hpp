@@ -1,0 +1,262 @@
+// Device helpers for gfx950: MFMA wrappers, LDS transpose reads, packing, task iteration.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gbsa_internal.hpp"
+
+namespace gbsa {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+#define GBSA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+// ---------------------------------------------------------------------------
+// MFMA: 16x16x32 with fp32 accumulation. Operand lane layout (wave64):
+//   A (16 x 32): lane l holds row l%16, k = (l/16)*8 .. +8
+//   B (32 x 16): lane l holds col l%16, k = (l/16)*8 .. +8
+//   C (16 x 16): lane l holds col l%16, rows (l/16)*4 .. +4
+// ---------------------------------------------------------------------------
+template <int DT>
+__device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c);
+
+template <>
+__device__ __forceinline__ f32x4 mfma_16x16x32<kBF16>(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x4 mfma_16x16x32<kF16>(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+// e4m3 x e4m3 (8 values per lane, same lane layout).
+__device__ __forceinline__ f32x4 mfma_16x16x32_fp8(u32x2 a, u32x2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(__builtin_bit_cast(long, a),
+                                                      __builtin_bit_cast(long, b), c, 0, 0, 0);
+}
+
+// Two fp32 -> packed 16-bit (round to nearest even) of the PV operand type.
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float x, float y);
+template <>
+__device__ __forceinline__ uint32_t pack2<kBF16>(float x, float y) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x, y}, bf16x2));
+}
+template <>
+__device__ __forceinline__ uint32_t pack2<kF16>(float x, float y) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x, y}, f16x2));
+}
+
+// 16-bit transpose read from LDS (ds_read_b64_tr_b16). Within each group of 16 lanes,
+// lane 4r+c supplies the address of elements [4c, 4c+4) of row r of a 4x16 block; lane i
+// receives column i, i.e. the four elements block[0..3][i].
+__device__ __forceinline__ u32x2 lds_read_tr16(const void* p) {
+    bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((GBSA_LDS bf16x4*)(p));
+    return __builtin_bit_cast(u32x2, v);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Four OCP e4m3 values (one dword) -> four bf16 (two dwords), exactly: every e4m3 value is
+// representable in bf16. Uses gfx950's direct conversion with a unit scale. (Reassembling the
+// two fp32 results of v_cvt_pk_f32_fp8 with shifts or v_perm was miscompiled by this
+// toolchain: element 1 was folded onto element 0.)
+__device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t x) {
+    const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x, 1.0f, false);
+    const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x, 1.0f, true);
+    return (u32x2){__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+}
+
+__device__ __forceinline__ float wave_max_cols(float x) {
+    // reduce across the four 16-lane groups that share a column (lanes l, l^16, l^32, l^48)
+    x = fmaxf(x, __shfl_xor(x, 16));
+    x = fmaxf(x, __shfl_xor(x, 32));
+    return x;
+}
+__device__ __forceinline__ float wave_sum_cols(float x) {
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    return x;
+}
+
+// Workgroups are handed to the 8 XCDs round-robin; give each XCD a contiguous range of
+// logical indices so that neighbouring work (same sequence and KV head) shares an L2.
+__device__ __forceinline__ int xcd_remap(int bid, int grid) {
+    constexpr int kXcd = 8;
+    if (grid % kXcd != 0) return bid;
+    const int per = grid / kXcd;
+    return (bid % kXcd) * per + bid / kXcd;
+}
+
+template <typename T>
+__device__ __forceinline__ T load_nt(const T* p) {
+    return __builtin_nontemporal_load(p);
+}
+
+// ---------------------------------------------------------------------------
+// Metadata access shared by the main and combine kernels.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool header_ok(const FwdArgs& a) {
+    const int32_t* m = a.meta;
+    bool ok = (m[0] == a.expect[0]) && (m[1] == a.expect[1]) && (m[2] == a.expect[2]);
+#pragma unroll
+    for (int i = kCheckFirst; i <= kCheckLast; ++i) ok = ok && (m[i] == a.expect[i]);
+    return ok;
+}
+
+struct Bound {
+    int u, s;
+};
+__device__ __forceinline__ Bound read_bound(const int32_t* meta, int w) {
+    uint32_t x = (uint32_t)meta[kHeaderWords + w];
+    return Bound{(int)(x >> kSlotBits), (int)(x & kSlotMask)};
+}
+__device__ __forceinline__ bool bound_less(Bound a, Bound b) {
+    return a.u < b.u || (a.u == b.u && a.s < b.s);
+}
+
+__device__ __forceinline__ int ceil_div_i(int64_t a, int b) { return (int)((a + b - 1) / b); }
+
+// Position in the ordered unit list (b, n2, active q-block gl).
+struct UnitIter {
+    int b, n2, gl;
+    int nact;     // active q-blocks of batch b
+    int qbase;    // global index of batch b's first q-block
+    int64_t row0; // cu_seqlens_q[b]
+    int storage;  // storage length of batch b
+    int sq;       // active length of batch b
+};
+
+__device__ __forceinline__ void batch_lengths(const FwdArgs& a, int b, int64_t* row0, int* storage,
+                                              int* sq) {
+    const int64_t c0 = a.cu[b], c1 = a.cu[b + 1];
+    const int st = (int)(c1 - c0);
+    int s = st;
+    if (a.squ != nullptr) s = min(max(a.squ[b], 0), st);
+    *row0 = c0;
+    *storage = st;
+    *sq = s;
+}
+
+// Block-wide search for the batch holding unit u0 (parallel prefix over the batches).
+// `scratch` needs 2 * blockDim.x + 8 ints of LDS. All threads of the block must call it.
+__device__ inline UnitIter locate_unit(const FwdArgs& a, int u0, int* scratch) {
+    const int tid = threadIdx.x, nt = blockDim.x;
+    int* su = scratch;        // unit counts (inclusive scan)
+    int* sqb = scratch + nt;  // q-block counts (inclusive scan)
+    int* res = scratch + 2 * nt;
+    if (tid == 0) res[0] = -1;
+    int ucarry = 0, qcarry = 0;
+    for (int base = 0; base < a.B; base += nt) {
+        const int b = base + tid;
+        int nu = 0, nq = 0;
+        if (b < a.B) {
+            int64_t r0;
+            int st, sq;
+            batch_lengths(a, b, &r0, &st, &sq);
+            nq = ceil_div_i(st, a.X);
+            nu = a.N2 * ceil_div_i(sq, a.X);
+        }
+        __syncthreads();
+        su[tid] = nu;
+        sqb[tid] = nq;
+        __syncthreads();
+        for (int off = 1; off < nt; off <<= 1) {
+            int x = 0, y = 0;
+            if (tid >= off) {
+                x = su[tid - off];
+                y = sqb[tid - off];
+            }
+            __syncthreads();
+            su[tid] += x;
+            sqb[tid] += y;
+            __syncthreads();
+        }
+        const int uex = ucarry + su[tid] - nu, qex = qcarry + sqb[tid] - nq;
+        if (b < a.B && nu > 0 && u0 >= uex && u0 < uex + nu) {
+            res[0] = b;
+            res[1] = uex;
+            res[2] = qex;
+        }
+        ucarry += su[nt - 1];
+        qcarry += sqb[nt - 1];
+        __syncthreads();
+        if (res[0] >= 0) break;
+    }
+    UnitIter it;
+    const int b = res[0];
+    if (b < 0) {  // u0 beyond the last unit: the caller treats the worker as empty
+        __syncthreads();
+        it.b = -1;
+        return it;
+    }
+    const int local = u0 - res[1];
+    batch_lengths(a, b, &it.row0, &it.storage, &it.sq);
+    it.b = b;
+    it.nact = ceil_div_i(it.sq, a.X);
+    it.n2 = local / it.nact;
+    it.gl = local % it.nact;
+    it.qbase = res[2];
+    __syncthreads();
+    return it;
+}
+
+__device__ __forceinline__ void advance_unit(const FwdArgs& a, UnitIter& it) {
+    if (++it.gl < it.nact) return;
+    it.gl = 0;
+    if (++it.n2 < a.N2) return;
+    it.n2 = 0;
+    do {
+        it.qbase += ceil_div_i(it.storage, a.X);
+        ++it.b;
+        if (it.b >= a.B) return;
+        batch_lengths(a, it.b, &it.row0, &it.storage, &it.sq);
+        it.nact = ceil_div_i(it.sq, a.X);
+    } while (it.nact == 0);
+}
+
+// Key-block visibility classes for one query-row range [t_lo, t_hi] of batch b.
+// Returns 0: nothing visible (skip), 1: everything visible (no mask), 2: mask per element.
+__device__ __forceinline__ int block_class(const FwdArgs& a, int64_t p0, int skv, int off, int t_lo,
+                                           int t_hi) {
+    const int64_t p1 = p0 + 127;
+    const int64_t dlo = (int64_t)t_lo + off, dhi = (int64_t)t_hi + off;
+    if (p0 >= skv) return 0;
+    if (a.mask == 1 && p0 > dhi) return 0;
+    if (a.wl >= 0 && p1 < dlo - a.wl) return 0;
+    if (a.wr >= 0 && p0 > dhi + a.wr) return 0;
+    bool full = p1 < skv;
+    if (a.mask == 1) full = full && (p1 <= dlo);
+    if (a.wl >= 0) full = full && (p0 >= dhi - a.wl);
+    if (a.wr >= 0) full = full && (p1 <= dlo + a.wr);
+    return full ? 1 : 2;
+}
+
+__device__ __forceinline__ bool key_visible(const FwdArgs& a, int64_t p, int skv, int64_t d) {
+    bool ok = p < skv;
+    if (a.mask == 1) ok = ok && (p <= d);
+    if (a.wl >= 0) ok = ok && (p >= d - a.wl);
+    if (a.wr >= 0) ok = ok && (p <= d + a.wr);
+    return ok;
+}
+
+template <int OUT>
+__device__ __forceinline__ uint32_t pack_out2(float x, float y) {
+    return pack2<OUT>(x, y);
+}
+
+}  // namespace gbsa

@@ -1,0 +1,101 @@
+// Internal declarations shared by the host entry points and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gbsa {
+
+// Metadata buffer format (1024 int32 words), written by the scheduler kernel:
+//   [0] magic  [1] version  [2] P (workers)  [3] U (units)  [4..5] total cost (lo, hi)
+//   [6] number of split units  [7] N1 [8] N2 [9] D [10] blockShapeX [11] blockShapeY
+//   [12] topK [13] mask_mode [14] quant_mode [15] totalQBlocks [16] B [17] win_left
+//   [18] win_right [19] seqused_q given [20] is_packed_gqa [21..23] 0
+//   [24 + w], w = 0..P: boundary of worker w, packed (unit << 9) | slot; the rest 0.
+constexpr int kMetaWords = 1024;
+constexpr int kHeaderWords = 24;
+constexpr int kSlotBits = 9;
+constexpr int kSlotMask = (1 << kSlotBits) - 1;
+constexpr uint32_t kMagic = 0x41534247u;  // bytes "GBSA"
+constexpr int kVersion = 1;
+constexpr int kMaxWorkers = kMetaWords - kHeaderWords - 1;
+constexpr int kMaxUnits = 1 << (32 - kSlotBits - 1);
+// header words the main kernels compare against their own parameters
+constexpr int kCheckFirst = 7, kCheckLast = 20;
+
+enum DType : int { kF16 = 0, kBF16 = 1, kFP8 = 2 };
+
+struct MetaArgs {
+    const int32_t* count;  // [N2, tqb]
+    const int64_t* cu;     // [B+1]
+    const int32_t* squ;    // [B] or null
+    int32_t* meta;         // [1024]
+    int32_t B, N2, X, topK, tqb, P;
+    int32_t header[kHeaderWords];  // words 7..20 prefilled by the host; the rest computed
+};
+
+// Per-split-piece descriptor stored in the workspace (one per piece slot 0..2P-1).
+struct PieceDesc {
+    int32_t b, n2, gl, g;
+};
+
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const int32_t* idx;    // [N2, tqb, topK]
+    const int32_t* cnt;    // [N2, tqb]
+    const int32_t* meta;   // [1024]
+    const int64_t* cu;     // [B+1]
+    const int32_t* squ;    // [B] or null
+    const int32_t* skv;    // [B]
+    const int32_t* table;  // [B, maxb]
+    const float* qs;       // [N1] or null
+    const float* ks;       // [N2] or null
+    const float* vs;       // [N2] or null
+    void* out;             // [T, N1, D]
+    float* lse;            // [T, N1] or null
+    int32_t* ws_status;    // workspace word 0: non-zero = metadata mismatch
+    PieceDesc* ws_desc;    // [2P]
+    float* ws_o;           // [2P, M, 128]
+    float* ws_m;           // [2P, M]  running max, log2 domain
+    float* ws_l;           // [2P, M]  running sum
+    int64_t kv_stride;     // elements between pages
+    int32_t B, N1, N2, G, X, topK, tqb, maxb, P, M, nst;
+    int32_t mask, wl, wr, return_lse;
+    float scale_log2;      // softmax scale * log2(e)
+    int32_t expect[kHeaderWords];  // expected header words (0, 1, 2 and 7..20 are checked)
+};
+
+// Workspace layout (byte offsets), a pure function of P and M.
+struct WsLayout {
+    size_t status, desc, o, m, l, total;
+};
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+inline WsLayout ws_layout(int64_t P, int64_t M) {
+    WsLayout w;
+    w.status = 0;
+    w.desc = 256;
+    w.o = align_up(w.desc + sizeof(PieceDesc) * 2 * P, 256);
+    w.m = align_up(w.o + sizeof(float) * 2 * P * M * 128, 256);
+    w.l = align_up(w.m + sizeof(float) * 2 * P * M, 256);
+    w.total = align_up(w.l + sizeof(float) * 2 * P * M, 256);
+    return w;
+}
+
+// Launchers (each defined next to its kernel).
+hipError_t launch_metadata(const MetaArgs& a, hipStream_t s);
+// Main kernel choice: rows per unit M = blockShapeX * G. M <= 16 uses the decode kernel
+// (KV slots spread over the waves), larger M the prefill kernel (rows over the waves).
+hipError_t launch_decode(const FwdArgs& a, int dtype, int out_dtype, hipStream_t s);
+hipError_t launch_prefill(const FwdArgs& a, int dtype, int out_dtype, int rows_per_wg,
+                          hipStream_t s);
+hipError_t launch_combine(const FwdArgs& a, int out_dtype, hipStream_t s);
+
+// Rows a prefill workgroup covers for a given M (16-row MFMA tiles, 2 per wave).
+inline int prefill_rows_per_wg(int M) { return M > 128 ? 256 : 128; }
+constexpr int kDecodeMaxRows = 16;
+
+}  // namespace gbsa

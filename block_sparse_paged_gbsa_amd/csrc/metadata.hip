@@ -1,0 +1,175 @@
+// Scheduler kernel: writes the load-balanced task split into the 1024-int32 metadata buffer.
+//
+// GenericBlockSparseAttention article (cf-1.com), "two-stage call": the metadata operator
+// computes the AICore task split (load balancing) ahead of the main operator and stores it
+// in a fixed (1024,) int32 tensor. The contents are this library's own format (described in
+// gbsa_internal.hpp): work units (b, kv head, active q-block) cost count + 1 each and their
+// kv slots are cut into P contiguous segments of equal cost. Everything is integer
+// arithmetic, so the result is bit-exact and deterministic ("general constraints":
+// deterministic by default).
+#include "device_common.hpp"
+
+namespace gbsa {
+namespace {
+
+template <typename T>
+__device__ T block_exclusive_scan(T x, T* total, T* sh) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    T inc = x;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        T y = __shfl_up(inc, o);
+        if (lane >= o) inc += y;
+    }
+    if (lane == 63) sh[wid] = inc;
+    __syncthreads();
+    if (wid == 0) {
+        T v = lane < nw ? sh[lane] : T(0);
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            T y = __shfl_up(v, o);
+            if (lane >= o) v += y;
+        }
+        if (lane < nw) sh[lane] = v;
+    }
+    __syncthreads();
+    const T prefix = wid > 0 ? sh[wid - 1] : T(0);
+    *total = sh[nw - 1];
+    __syncthreads();
+    return prefix + inc - x;
+}
+
+__device__ __forceinline__ int upper_bound_batch(const int* ubase, int B, int u) {
+    // largest b with ubase[b] <= u (ubase is non-decreasing, ubase[0] = 0)
+    int lo = 0, hi = B;  // invariant: ubase[lo] <= u, answer in [lo, hi)
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (ubase[mid] <= u) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+__device__ __forceinline__ int unit_count(const MetaArgs& a, const int* qbase, const int* ubase,
+                                          int u) {
+    const int b = upper_bound_batch(ubase, a.B, u);
+    const int nu = ubase[b + 1] - ubase[b];
+    const int nact = nu / a.N2;
+    const int local = u - ubase[b];
+    const int n2 = local / nact, gl = local % nact;
+    const int g = qbase[b] + gl;
+    int c = 0;
+    if (g < a.tqb) c = a.count[(int64_t)n2 * a.tqb + g];
+    return min(max(c, 0), a.topK);
+}
+
+__global__ __launch_bounds__(1024) void metadata_kernel(MetaArgs a) {
+    extern __shared__ int tabs[];  // qbase[B+1], ubase[B+1]
+    __shared__ long long sh64[16];
+    __shared__ int sh_split;
+    const int tid = threadIdx.x, nt = blockDim.x;
+    int* qbase = tabs;
+    int* ubase = tabs + a.B + 1;
+
+    // Per-sequence q-block and unit offsets.
+    long long cq = 0, cu = 0;
+    for (int base = 0; base < a.B; base += nt) {
+        const int b = base + tid;
+        long long nq = 0, nu = 0;
+        if (b < a.B) {
+            const int64_t st = a.cu[b + 1] - a.cu[b];
+            int64_t sq = st;
+            if (a.squ != nullptr) sq = min((int64_t)max(a.squ[b], 0), st);
+            nq = (st + a.X - 1) / a.X;
+            nu = (long long)a.N2 * ((sq + a.X - 1) / a.X);
+        }
+        long long tq, tu;
+        const long long eq = block_exclusive_scan<long long>(nq, &tq, sh64);
+        const long long eu = block_exclusive_scan<long long>(nu, &tu, sh64);
+        if (b < a.B) {
+            qbase[b] = (int)(cq + eq);
+            ubase[b] = (int)(cu + eu);
+        }
+        cq += tq;
+        cu += tu;
+    }
+    if (tid == 0) {
+        qbase[a.B] = (int)cq;
+        ubase[a.B] = (int)cu;
+        sh_split = 0;
+    }
+    __syncthreads();
+    const int U = (int)cu;
+    const int P = a.P;
+
+    // Total cost.
+    long long part = 0;
+    for (int u = tid; u < U; u += nt) part += unit_count(a, qbase, ubase, u) + 1;
+    long long W;
+    (void)block_exclusive_scan<long long>(part, &W, sh64);
+
+    // Boundaries: unit u owns the targets floor(w*W/P) that fall in [C_u, C_u + cost_u).
+    long long carry = 0;
+    for (int base = 0; base < U; base += nt) {
+        const int u = base + tid;
+        int c = 0;
+        long long cost = 0;
+        if (u < U) {
+            c = unit_count(a, qbase, ubase, u);
+            cost = c + 1;
+        }
+        long long tot;
+        const long long Cu = carry + block_exclusive_scan<long long>(cost, &tot, sh64);
+        if (u < U) {
+            const int nslots = max(c, 1);
+            bool split = false;
+            for (long long w = (Cu * P + W - 1) / W; w < P; ++w) {
+                const long long t = (w * W) / P;
+                if (t >= Cu + cost) break;
+                const int s = (int)(t - Cu);
+                uint32_t word;
+                if (s < nslots) {
+                    word = ((uint32_t)u << kSlotBits) | (uint32_t)s;
+                    split = split || (s > 0);
+                } else {
+                    word = (uint32_t)(u + 1) << kSlotBits;
+                }
+                a.meta[kHeaderWords + w] = (int32_t)word;
+            }
+            if (split) atomicAdd(&sh_split, 1);
+        }
+        carry += tot;
+    }
+    if (U == 0) {
+        for (int w = tid; w < P; w += nt) a.meta[kHeaderWords + w] = 0;
+    }
+    for (int i = kHeaderWords + P + 1 + tid; i < kMetaWords; i += nt) a.meta[i] = 0;
+    __syncthreads();
+    if (tid == 0) {
+        a.meta[kHeaderWords + P] = (int32_t)((uint32_t)U << kSlotBits);
+        a.meta[0] = (int32_t)kMagic;
+        a.meta[1] = kVersion;
+        a.meta[2] = P;
+        a.meta[3] = U;
+        a.meta[4] = (int32_t)(uint32_t)(W & 0xffffffffll);
+        a.meta[5] = (int32_t)(uint32_t)(W >> 32);
+        a.meta[6] = sh_split;
+        for (int i = kCheckFirst; i <= kCheckLast; ++i) a.meta[i] = a.header[i];
+        for (int i = kCheckLast + 1; i < kHeaderWords; ++i) a.meta[i] = 0;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_metadata(const MetaArgs& a, hipStream_t s) {
+    const size_t lds = sizeof(int) * 2 * (size_t)(a.B + 1);
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute((const void*)metadata_kernel,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(metadata_kernel, dim3(1), dim3(1024), lds, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace gbsa

@@ -89,6 +89,8 @@ class Problem:
 
     @property
     def kv_page_stride(self) -> int:
+        if self.k is None:
+            return PAGE * self.num_heads_kv * HEAD_DIM
         return int(self.k.stride(0))
 
 
@@ -254,8 +256,11 @@ def build_problem(name: str, *, seed: int, q_lens: Sequence[int], kv_lens: Seque
                   mask_mode: int = 0, win_left: int = -1, win_right: int = -1,
                   return_lse: bool = True, out_dtype: Optional[str] = None, std: float = 1.0,
                   scale: float = 0.0, device="cpu", extra_pages: int = 0, page_pad: int = 0,
-                  shuffle_pages: bool = True) -> Problem:
-    """Assemble a problem. kv_lens are the seqused_kv values; kv_storage the cached lengths."""
+                  shuffle_pages: bool = True, values: bool = True) -> Problem:
+    """Assemble a problem. kv_lens are the seqused_kv values; kv_storage the cached lengths.
+
+    values=False leaves q/k/v as None (integer structure only).
+    """
     ss = np.random.SeedSequence(seed)
     s_sel, s_perm = [np.random.Generator(np.random.PCG64(c)) for c in ss.spawn(2)]
     B = len(q_lens)
@@ -275,12 +280,14 @@ def build_problem(name: str, *, seed: int, q_lens: Sequence[int], kv_lens: Seque
     squ = None if seqused_q is None else np.asarray(seqused_q, dtype=np.int32)
     idx, cnt = _fill_selection(num_heads_kv, cu, squ, sk, block_x, top_k, s_sel, select,
                                causal_eligible)
-    gen = torch.Generator(device=device)
-    gen.manual_seed(seed)
     T = int(cu[-1])
-    q, qs = _values(dtype, (T, num_heads_q, HEAD_DIM), std, gen, device, 1)
-    k, ks = _paged_kv(num_pages, num_heads_kv, dtype, std, gen, device, page_pad)
-    v, vs = _paged_kv(num_pages, num_heads_kv, dtype, std, gen, device, page_pad)
+    q = k = v = qs = ks = vs = None
+    if values:
+        gen = torch.Generator(device=device)
+        gen.manual_seed(seed)
+        q, qs = _values(dtype, (T, num_heads_q, HEAD_DIM), std, gen, device, 1)
+        k, ks = _paged_kv(num_pages, num_heads_kv, dtype, std, gen, device, page_pad)
+        v, vs = _paged_kv(num_pages, num_heads_kv, dtype, std, gen, device, page_pad)
     if out_dtype is None:
         out_dtype = "bf16" if dtype == "fp8" else dtype
     return Problem(name=name, batch=B, num_heads_q=num_heads_q, num_heads_kv=num_heads_kv,
@@ -305,7 +312,7 @@ CONFIG_NAMES = {
 }
 
 
-def config(cfg_id: int, device="cpu") -> Problem:
+def config(cfg_id: int, device="cpu", values: bool = True) -> Problem:
     """Workloads 1..5: seeds 1000 + id, shapes and selection recipes as documented."""
     seed = 1000 + cfg_id
     sc = 1.0 / math.sqrt(HEAD_DIM)
@@ -313,31 +320,31 @@ def config(cfg_id: int, device="cpu") -> Problem:
         return build_problem(CONFIG_NAMES[1], seed=seed, q_lens=[256, 384], kv_lens=[256, 384],
                              num_heads_q=8, num_heads_kv=2, block_x=64, top_k=4, dtype="f16",
                              select=select_uniform_count(4), mask_mode=0, return_lse=True,
-                             scale=sc, device=device)
+                             scale=sc, device=device, values=values)
     if cfg_id == 2:
         B = 64
         return build_problem(CONFIG_NAMES[2], seed=seed, q_lens=[1] * B, kv_lens=[32768] * B,
                              num_heads_q=32, num_heads_kv=8, block_x=1, top_k=16, dtype="bf16",
                              select=select_decode_last_plus(15), causal_eligible=False,
-                             mask_mode=0, return_lse=False, scale=sc, device=device)
+                             mask_mode=0, return_lse=False, scale=sc, device=device, values=values)
     if cfg_id == 3:
         B = 4
         return build_problem(CONFIG_NAMES[3], seed=seed, q_lens=[32768] * B, kv_lens=[32768] * B,
                              num_heads_q=32, num_heads_kv=4, block_x=128, top_k=64, dtype="bf16",
                              select=select_sink_recent_random(64, 8), mask_mode=1,
-                             return_lse=False, scale=sc, device=device)
+                             return_lse=False, scale=sc, device=device, values=values)
     if cfg_id == 4:
         return build_problem(CONFIG_NAMES[4], seed=seed, q_lens=[131072], kv_lens=[120000],
                              kv_storage=[131072], seqused_q=[120000], num_heads_q=64,
                              num_heads_kv=8, block_x=64, top_k=256, dtype="f16",
                              select=select_sink_window(4, 252), mask_mode=1, win_left=32256,
-                             win_right=0, return_lse=True, std=0.5, scale=sc, device=device)
+                             win_right=0, return_lse=True, std=0.5, scale=sc, device=device, values=values)
     if cfg_id == 5:
         B = 2
         return build_problem(CONFIG_NAMES[5], seed=seed, q_lens=[32768] * B, kv_lens=[32768] * B,
                              num_heads_q=16, num_heads_kv=16, block_x=128, top_k=256,
                              dtype="fp8", out_dtype="bf16", select=select_all, mask_mode=1,
-                             return_lse=False, scale=sc, device=device)
+                             return_lse=False, scale=sc, device=device, values=values)
     raise ValueError(f"unknown workload {cfg_id}")
 
 
@@ -347,7 +354,7 @@ def random_problem(seed: int, *, device="cpu", dtype: str = "f16", batch: int = 
                    win_left: int = -1, win_right: int = -1, use_seqused_q: bool = False,
                    decode: bool = False, page_pad: int = 0, extra_pages: int = 3,
                    return_lse: bool = True, std: float = 1.0, out_dtype: Optional[str] = None,
-                   causal_eligible: Optional[bool] = None) -> Problem:
+                   causal_eligible: Optional[bool] = None, values: bool = True) -> Problem:
     """A small ragged problem for fuzzing: random lengths, selections, optional dual lengths."""
     rng = np.random.Generator(np.random.PCG64(seed + 7_000_000))
     if decode:
@@ -369,7 +376,7 @@ def random_problem(seed: int, *, device="cpu", dtype: str = "f16", batch: int = 
                          mask_mode=mask_mode, win_left=win_left, win_right=win_right,
                          return_lse=return_lse, std=std, scale=1.0 / math.sqrt(HEAD_DIM),
                          device=device, extra_pages=extra_pages, page_pad=page_pad,
-                         out_dtype=out_dtype)
+                         out_dtype=out_dtype, values=values)
 
 
 def to_device(p: Problem, device) -> Problem:

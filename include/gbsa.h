@@ -1,0 +1,208 @@
+/*
+ * gbsa.h -- block-sparse flash attention over a paged KV cache, for AMD MI355X (gfx950).
+ *
+ * The operation is the one the GenericBlockSparseAttention article (cf-1.com, CANN
+ * ops-transformer GBSA) defines in its "sparse attention mechanism" section:
+ *
+ *     attention_out = softmax(scale * Q * K_sparse^T + mask) * V_sparse
+ *
+ * where every Q block of blockShapeX query rows attends only to the 128-token KV blocks
+ * that sparse_block_idx / sparse_block_count select for it from a paged KV cache, and the
+ * query heads of one KV head share that selection (packed GQA).
+ *
+ * The interface mirrors the article's two-stage problem statement ("two-stage call"
+ * section): gbsa_metadata() first writes the load-balanced task split into a fixed
+ * (1024,) int32 buffer; gbsa_forward() consumes it. As in the article's aclnn interface,
+ * the main call's workspace size is queried from shapes alone (gbsa_workspace_size).
+ *
+ * Conventions for every entry point
+ *  - All tensor pointers are DEVICE pointers owned by the caller. The library never
+ *    allocates, frees or synchronises; work is enqueued on `stream` and completes in
+ *    stream order. Inputs are only read; outputs and the workspace are written.
+ *  - Arguments are validated on the host before any device work; on error nothing is
+ *    enqueued and a gbsa_status other than GBSA_OK is returned. Tensor VALUES (lengths,
+ *    indices, page-table entries) are not validated on the host ("general constraints":
+ *    tiling never reads tensor values); see gbsa_forward for how the kernels treat them.
+ *  - Layouts: query TND [T, N1, D] dense; key/value PA_BBND [num_pages, 128, N2, D] where
+ *    only the page axis may be strided (kv_page_stride elements between pages);
+ *    sparse_block_idx [N2, total_q_blocks, top_k] and sparse_block_count
+ *    [N2, total_q_blocks] dense int32; block_table [B, max_blocks_per_seq] dense int32;
+ *    cu_seqlens_q [B+1] int64; seqused_q / seqused_kv [B] int32; attention_out [T, N1, D];
+ *    softmax_lse [T, N1] float32 (the article's (T, N1, 1)).
+ *  - Thread safety: calls may be made concurrently from several host threads. Two calls
+ *    that share a workspace or metadata buffer must be ordered by the caller.
+ */
+#ifndef GBSA_H_
+#define GBSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Fixed metadata size ("two-stage call": a (1024,) int32 tensor). */
+#define GBSA_METADATA_SIZE 1024
+/* Only D = 128 and 128-token KV pages equal to blockShapeY ("general constraints"). */
+#define GBSA_HEAD_DIM 128
+#define GBSA_PAGE_SIZE 128
+/* topK upper bound and GQA group bound ("general constraints"). */
+#define GBSA_MAX_TOPK 256
+#define GBSA_MAX_GROUP 128
+/* Largest worker count the metadata buffer can describe (24 header words + P+1 bounds). */
+#define GBSA_MAX_WORKERS 999
+/* Largest batch the scheduler kernel accepts (it keeps two per-sequence tables in LDS). */
+#define GBSA_MAX_BATCH 16384
+
+typedef enum gbsa_status {
+    GBSA_OK = 0,
+    GBSA_ERR_NULL = 1,        /* a required pointer is NULL */
+    GBSA_ERR_SHAPE = 2,       /* a dimension violates a constraint */
+    GBSA_ERR_DTYPE = 3,       /* unsupported or inconsistent data type */
+    GBSA_ERR_UNSUPPORTED = 4, /* attribute value the article lists as unsupported */
+    GBSA_ERR_EMPTY = 5,       /* a required tensor has a zero-length axis */
+    GBSA_ERR_WORKSPACE = 6,   /* workspace missing or smaller than gbsa_workspace_size */
+    GBSA_ERR_METADATA = 7,    /* metadata buffer missing */
+    GBSA_ERR_HIP = 8          /* a HIP runtime call failed (device query, launch) */
+} gbsa_status;
+
+typedef enum gbsa_dtype {
+    GBSA_DTYPE_F16 = 0,
+    GBSA_DTYPE_BF16 = 1,
+    GBSA_DTYPE_FP8_E4M3 = 2   /* OCP e4m3fn, the article's FP8 E4M3 full-quant path */
+} gbsa_dtype;
+
+/* "mask" section: 1 = built-in causal. 0 = no mask. */
+typedef enum gbsa_mask_mode { GBSA_MASK_NONE = 0, GBSA_MASK_CAUSAL = 1 } gbsa_mask_mode;
+
+/* "quantisation" section: 0 NO_QUANT, 5 FP8_E4M3_STATIC_CAST_P (1..4 are rejected). */
+typedef enum gbsa_quant_mode { GBSA_QUANT_NONE = 0, GBSA_QUANT_FP8_E4M3 = 5 } gbsa_quant_mode;
+
+/*
+ * Shapes and attributes shared by both stages. The article's "parameters" section gives
+ * the defaults: block_shape [1, 128], is_packed_gqa 1, layout TND / PA_BBND, scale 0.0,
+ * win_left = win_right = -1. Both calls must receive identical values ("general
+ * constraints": metadata and main call must agree); gbsa_forward checks the metadata's
+ * fingerprint and refuses to compute on a mismatch (see gbsa_forward).
+ */
+typedef struct gbsa_params {
+    int32_t batch;              /* B >= 1, <= GBSA_MAX_BATCH */
+    int32_t num_heads_q;        /* N1 */
+    int32_t num_heads_kv;       /* N2; N1 % N2 == 0 and N1 / N2 <= 128 */
+    int32_t head_dim;           /* D; must be 128 */
+    int64_t total_q;            /* T, rows of query and attention_out */
+    int32_t total_q_blocks;     /* dim 1 of sparse_block_idx/count = sum ceil(storage_b / X) */
+    int32_t top_k;              /* dim 2 of sparse_block_idx, 1..256 */
+    int32_t block_x;            /* blockShapeX >= 1 (query rows per Q block) */
+    int32_t block_y;            /* blockShapeY; must be 128 */
+    int32_t page_size;          /* KV page size; must be 128 */
+    int32_t max_blocks_per_seq; /* dim 1 of block_table */
+    int64_t num_pages;          /* dim 0 of key/value */
+    int64_t kv_page_stride;     /* elements between pages; 0 = dense (128*N2*D);
+                                   else >= 128*N2*D and a multiple of N2*D */
+    int32_t dtype;              /* gbsa_dtype of query/key/value (must match) */
+    int32_t out_dtype;          /* gbsa_dtype of attention_out: F16 or BF16. With quant 0 it
+                                   must equal dtype; with quant 5 it is required */
+    int32_t mask_mode;          /* gbsa_mask_mode */
+    int32_t win_left;           /* -1 unbounded, else keys p >= t + off - win_left */
+    int32_t win_right;          /* -1 unbounded, else keys p <= t + off + win_right */
+    int32_t quant_mode;         /* gbsa_quant_mode; 5 requires dtype FP8_E4M3 */
+    int32_t softmax_precision;  /* 0 or 1 ("softmax precision" section); computed in fp32 */
+    int32_t return_lse;         /* 1: write softmax_lse */
+    int32_t is_packed_gqa;      /* must be 1 */
+    int32_t has_seqused_q;      /* 1: seqused_q is passed to both calls */
+    float scale;                /* softmax scale; <= 0 means 1/sqrt(D) */
+    int32_t num_workers;        /* 0 = chosen by the library from the shapes, else 1..999 */
+    int32_t reserved[4];        /* must be 0 */
+} gbsa_params;
+
+/*
+ * Check a parameter block without touching any device. Returns the status that
+ * gbsa_metadata / gbsa_forward would return for these attributes.
+ */
+gbsa_status gbsa_check_params(const gbsa_params* params);
+
+/*
+ * Number of workers (task-split segments) the two calls will use on the current device.
+ * Depends only on the shapes and the device's compute-unit count. Errors: any
+ * gbsa_check_params error; GBSA_ERR_HIP when the device cannot be queried.
+ */
+gbsa_status gbsa_num_workers(const gbsa_params* params, int32_t* num_workers);
+
+/*
+ * Stage 1 ("two-stage call" section; the article's metadata operator).
+ * Enqueues the scheduler kernel, which writes the task split into `metadata`
+ * (GBSA_METADATA_SIZE int32 on the device). Work units are (b, kv head, active q-block)
+ * in that order; a q-block is active when it starts below seqused_q[b] (or the storage
+ * length cu_seqlens_q[b+1]-cu_seqlens_q[b] when seqused_q is NULL) ("general constraints":
+ * the task space follows seqused). Unit cost = clamp(count, 0, top_k) + 1; the units' kv
+ * slots are split into num_workers contiguous segments of equal cost.
+ *   sparse_block_count  [N2, total_q_blocks] int32, device
+ *   cu_seqlens_q        [B+1] int64, device (storage lengths of the TND query)
+ *   seqused_q           [B] int32, device, or NULL (must be non-NULL iff has_seqused_q)
+ *   seqused_kv          [B] int32, device (required with PA_BBND; not read here)
+ *   metadata            [1024] int32, device, written
+ * Errors: gbsa_check_params errors; GBSA_ERR_NULL; GBSA_ERR_METADATA (metadata NULL);
+ * GBSA_ERR_HIP on a failed launch.
+ */
+gbsa_status gbsa_metadata(const gbsa_params* params, const int32_t* sparse_block_count,
+                          const int64_t* cu_seqlens_q, const int32_t* seqused_q,
+                          const int32_t* seqused_kv, int32_t* metadata, hipStream_t stream);
+
+/*
+ * Workspace bytes gbsa_forward needs, from shapes only (the aclnn GetWorkspaceSize
+ * stage). It holds a status word, per-worker split-KV partial results (O, running max,
+ * running sum) and their descriptors.
+ */
+gbsa_status gbsa_workspace_size(const gbsa_params* params, size_t* bytes);
+
+/*
+ * Stage 2 (the main operator, "sparse attention mechanism" formula).
+ *   query        [T, N1, 128]            dtype
+ *   key, value   [num_pages, 128, N2, 128] dtype, page axis stride kv_page_stride
+ *   sparse_block_idx   [N2, total_q_blocks, top_k] int32: LOGICAL block numbers j of the
+ *                      sequence (keys 128*j .. 128*j+127); slots >= count are ignored
+ *   sparse_block_count [N2, total_q_blocks] int32 (clamped to [0, top_k])
+ *   metadata     written by gbsa_metadata with the same params and inputs
+ *   cu_seqlens_q [B+1] int64; seqused_q [B] int32 or NULL; seqused_kv [B] int32
+ *   block_table  [B, max_blocks_per_seq] int32: physical page of logical block j
+ *   q_scale [N1], k_scale [N2], v_scale [N2] float32 dequant scales: required with quant 5,
+ *                must be NULL with quant 0; p_scale is accepted for interface parity and
+ *                must be NULL (P is kept in 16-bit precision)
+ *   attention_out [T, N1, 128] out_dtype; rows t >= seqused_q[b] are not written
+ *   softmax_lse   [T, N1] float32 natural-log LSE of the scaled logits, -inf for a row
+ *                 with no visible key (whose output row is 0); required iff return_lse
+ *   workspace / workspace_bytes: device buffer of at least gbsa_workspace_size bytes
+ * Visibility of key position p = 128*j + r from batch-local query row t: p < seqused_kv[b];
+ * causal: p <= t + off; window: t + off - win_left <= p <= t + off + win_right, with
+ * off = seqused_kv[b] - (seqused_q[b] or the storage length).
+ * Values the caller must guarantee (not checked, as in the article): lengths within
+ * storage, block_table entries in [0, num_pages) for every selected block below
+ * seqused_kv. The kernels skip a slot whose index is negative or whose block starts at or
+ * beyond seqused_kv[b], and never read past the selection arrays.
+ * If the metadata's magic, worker count or parameter fingerprint do not match these
+ * params, the kernels write nothing to the outputs and set word 0 of the workspace to a
+ * non-zero value (readable by the caller after the stream completes).
+ * Errors: gbsa_check_params errors; GBSA_ERR_NULL; GBSA_ERR_METADATA; GBSA_ERR_WORKSPACE;
+ * GBSA_ERR_DTYPE (scales inconsistent with quant_mode); GBSA_ERR_HIP on a failed launch.
+ */
+gbsa_status gbsa_forward(const gbsa_params* params, const void* query, const void* key,
+                         const void* value, const int32_t* sparse_block_idx,
+                         const int32_t* sparse_block_count, const int32_t* metadata,
+                         const int64_t* cu_seqlens_q, const int32_t* seqused_q,
+                         const int32_t* seqused_kv, const int32_t* block_table,
+                         const float* q_scale, const float* k_scale, const float* v_scale,
+                         const float* p_scale, void* attention_out, float* softmax_lse,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Human-readable text for a status (static storage). */
+const char* gbsa_status_string(gbsa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GBSA_H_ */

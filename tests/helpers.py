@@ -38,3 +38,115 @@ def dequant(t: torch.Tensor, dtype: str, scale=None, head_axis=None) -> torch.Te
         shape[head_axis] = -1
         x = x * torch.as_tensor(scale, dtype=torch.float64).view(shape)
     return x
+
+
+# ---------------------------------------------------------------------------
+# GPU side: run a problem through the C ABI (marshalling only)
+# ---------------------------------------------------------------------------
+
+TOL = {"f16": 4e-3, "bf16": 1.6e-2, "fp8": 6e-2}
+LSE_RTOL = 1e-3
+
+
+def gpu_params(p, num_workers: int = 0):
+    import gbsa_inputs as gi
+    from block_sparse_paged_gbsa_amd.api import make_params
+    return make_params(batch=p.batch, num_heads_q=p.num_heads_q, num_heads_kv=p.num_heads_kv,
+                       total_q=p.total_q, total_q_blocks=p.total_q_blocks, top_k=p.top_k,
+                       block_x=p.block_x, max_blocks_per_seq=p.block_table.shape[1],
+                       num_pages=p.num_pages, kv_page_stride=p.kv_page_stride,
+                       dtype=gi.TORCH_DTYPES[p.dtype], out_dtype=gi.TORCH_DTYPES[p.out_dtype],
+                       mask_mode=p.mask_mode, win_left=p.win_left, win_right=p.win_right,
+                       quant_mode=p.quant_mode, return_lse=p.return_lse,
+                       has_seqused_q=p.seqused_q is not None, scale=p.scale,
+                       num_workers=num_workers)
+
+
+class GpuProblem:
+    """Device copies of a problem's integer structure (values must already be on the GPU)."""
+
+    def __init__(self, p, device="cuda"):
+        d = torch.device(device)
+        self.p = p
+        self.idx = torch.as_tensor(p.sparse_block_idx).to(d)
+        self.cnt = torch.as_tensor(p.sparse_block_count).to(d)
+        self.cu = torch.as_tensor(p.cu_seqlens_q).to(d)
+        self.squ = None if p.seqused_q is None else torch.as_tensor(p.seqused_q).to(d)
+        self.skv = torch.as_tensor(p.seqused_kv).to(d)
+        self.table = torch.as_tensor(p.block_table).to(d)
+        f = lambda s: None if s is None else torch.as_tensor(s, dtype=torch.float32).to(d)
+        self.qs, self.ks, self.vs = f(p.q_scale), f(p.k_scale), f(p.v_scale)
+
+    def metadata(self, params, metadata=None):
+        from block_sparse_paged_gbsa_amd.api import gbsa_metadata
+        return gbsa_metadata(params, self.cnt, self.cu, self.squ, self.skv, metadata)
+
+    def forward(self, params, meta, out=None, lse=None, workspace=None):
+        from block_sparse_paged_gbsa_amd.api import gbsa_forward
+        p = self.p
+        return gbsa_forward(params, p.q, p.k, p.v, self.idx, self.cnt, meta, self.cu, self.squ,
+                            self.skv, self.table, self.qs, self.ks, self.vs, None, out, lse,
+                            workspace)
+
+    def run(self, num_workers=0, out=None, lse=None):
+        params = gpu_params(self.p, num_workers)
+        meta = self.metadata(params)
+        out, lse, ws = self.forward(params, meta, out, lse)
+        torch.cuda.synchronize()
+        return params, meta, out, lse, ws
+
+
+def out_f64(out: torch.Tensor) -> np.ndarray:
+    return out.detach().float().cpu().numpy().astype(np.float64)
+
+
+def compare(p, out, lse, O_ref, L_ref, rows_mask, label=""):
+    """Max-abs O error and LSE relative error on the oracle's computed rows; asserts the bar."""
+    O = out_f64(out)[rows_mask]
+    Oref = O_ref[rows_mask]
+    assert np.isfinite(O).all(), f"{label}: non-finite output"
+    err = float(np.max(np.abs(O - Oref))) if O.size else 0.0
+    assert err <= TOL[p.dtype], f"{label}: O max-abs {err} > {TOL[p.dtype]}"
+    lerr = 0.0
+    if lse is not None:
+        L = lse.detach().cpu().numpy().astype(np.float64)[rows_mask]
+        Lr = L_ref[rows_mask]
+        fin = np.isfinite(Lr)
+        assert np.array_equal(fin, np.isfinite(L)), f"{label}: LSE -inf pattern differs"
+        assert np.all(L[~fin] == -np.inf)
+        if fin.any():
+            # relative error with a unit floor: a row whose only visible logit is ~0 has
+            # LSE ~0, where a pure relative error is undefined
+            lerr = float(np.max(np.abs(L[fin] - Lr[fin]) / np.maximum(np.abs(Lr[fin]), 1.0)))
+        assert lerr <= LSE_RTOL, f"{label}: LSE rel {lerr}"
+    return err, lerr
+
+
+def compact_oracle_inputs(p, units):
+    """Oracle inputs restricted to the pages that the given (b, gl) units select.
+
+    Gathers just those pages from the device tensors (all KV heads) and remaps the block
+    table, so full-size problems can be checked on sampled rows without copying the pool.
+    """
+    starts = __import__("gbsa_inputs").q_block_starts(p.cu_seqlens_q, p.block_x)
+    pages = set()
+    for (b, gl) in units:
+        g = starts[b] + gl
+        for n2 in range(p.num_heads_kv):
+            c = min(max(int(p.sparse_block_count[n2, g]), 0), p.top_k)
+            for j in p.sparse_block_idx[n2, g, :c]:
+                if j >= 0 and 128 * int(j) < int(p.seqused_kv[b]):
+                    pages.add(int(p.block_table[b, j]))
+    pages = sorted(pages)
+    remap = np.full(p.num_pages, -1, dtype=np.int64)
+    remap[pages] = np.arange(len(pages))
+    sel = torch.as_tensor(pages, dtype=torch.long, device=p.k.device)
+    k = storage_numpy(p.k[sel], p.dtype)
+    v = storage_numpy(p.v[sel], p.dtype)
+    table = np.where(p.block_table >= 0, remap[np.maximum(p.block_table, 0)], -1)
+    q = storage_numpy(p.q, p.dtype)
+    return Inputs(q, k, v, p.sparse_block_idx, p.sparse_block_count, p.cu_seqlens_q,
+                  p.seqused_q, p.seqused_kv, table, dtype=p.dtype, block_x=p.block_x,
+                  scale=p.scale, mask_mode=p.mask_mode, win_left=p.win_left,
+                  win_right=p.win_right, q_scale=p.q_scale, k_scale=p.k_scale,
+                  v_scale=p.v_scale)

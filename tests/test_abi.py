@@ -1,0 +1,125 @@
+"""The C-ABI library loads, exports what include/gbsa.h declares, matches its struct layout
+and rejects invalid attributes before touching a device (CPU only)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from block_sparse_paged_gbsa_amd import _lib
+from block_sparse_paged_gbsa_amd.api import make_params
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gbsa.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gbsa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = _lib.load()
+    names = _declared_functions()
+    assert set(names) == set(_lib.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (gbsa_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_params_struct_layout_matches_c():
+    """Compile a tiny C program against the header and compare sizeof/offsetof."""
+    fields = [f for f, _ in _lib.GbsaParams._fields_]
+    src = ['#include <stdio.h>', '#include <stddef.h>', '#include "gbsa.h"', 'int main(void){',
+           'printf("%zu\\n", sizeof(gbsa_params));']
+    src += [f'printf("%zu\\n", offsetof(gbsa_params, {f}));' for f in fields]
+    src += ['return 0;}']
+    tmp = os.path.join("/tmp", f"gbsa_layout_{os.getpid()}")
+    with open(tmp + ".c", "w") as fh:
+        fh.write("\n".join(src))
+    subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                    "-I", "/opt/rocm/include", tmp + ".c", "-o", tmp], check=True)
+    vals = [int(x) for x in subprocess.run([tmp], capture_output=True, text=True,
+                                           check=True).stdout.split()]
+    assert vals[0] == ctypes.sizeof(_lib.GbsaParams)
+    for f, off in zip(fields, vals[1:]):
+        assert getattr(_lib.GbsaParams, f).offset == off, f
+
+
+def _good(**kw):
+    base = dict(batch=2, num_heads_q=8, num_heads_kv=2, total_q=640, total_q_blocks=10,
+                top_k=4, block_x=64, max_blocks_per_seq=3, num_pages=5, mask_mode=1,
+                num_workers=7)
+    base.update(kw)
+    return make_params(**base)
+
+
+def _check(p):
+    return _lib.load().gbsa_check_params(ctypes.byref(p))
+
+
+def test_valid_params_pass():
+    assert _check(_good()) == 0
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("head_dim", 64, 2), ("block_y", 64, 2), ("page_size", 256, 2), ("num_heads_kv", 3, 2),
+    ("top_k", 257, 2), ("win_left", -2, 2), ("num_workers", 1000, 2), ("kv_page_stride", 100, 2),
+    ("batch", 0, 5), ("total_q", 0, 5), ("top_k", 0, 5), ("num_pages", 0, 5),
+    ("quant_mode", 3, 4), ("mask_mode", 2, 4), ("is_packed_gqa", 0, 4), ("softmax_precision", 2, 4),
+    ("dtype", 2, 3), ("out_dtype", 2, 3), ("batch", 20000, 4),
+])
+def test_rejections(field, value, code):
+    p = _good()
+    setattr(p, field, value)
+    assert _check(p) == code
+
+
+def test_group_limit_and_quant_dtype_rules():
+    assert _check(_good(num_heads_q=258, num_heads_kv=2)) == 2  # group 129 > 128
+    assert _check(_good(num_heads_q=256, num_heads_kv=2)) == 0  # group 128
+    import torch
+    assert _check(_good(quant_mode=5)) == 3  # quant 5 needs fp8 inputs
+    assert _check(_good(quant_mode=5, dtype=torch.float8_e4m3fn, out_dtype=torch.bfloat16)) == 0
+    assert _check(_good(dtype=torch.bfloat16, out_dtype=torch.float16)) == 3  # quant 0: out=q
+    assert _check(_good(kv_page_stride=128 * 2 * 128 + 256)) == 0
+    assert _check(_good(kv_page_stride=128 * 2 * 128 + 100)) == 2
+
+
+def test_entry_points_validate_before_device_work():
+    lib = _lib.load()
+    bad = _good(head_dim=64)
+    dummy = ctypes.c_void_p(0x1000)
+    assert lib.gbsa_metadata(ctypes.byref(bad), dummy, dummy, None, dummy, dummy, None) == 2
+    assert lib.gbsa_forward(ctypes.byref(bad), *([dummy] * 17), 0, None) == 2
+    good = _good()
+    # missing metadata buffer / workspace / inconsistent optional pointers
+    assert lib.gbsa_metadata(ctypes.byref(good), dummy, dummy, None, dummy, None, None) == 7
+    assert lib.gbsa_metadata(ctypes.byref(good), dummy, dummy, dummy, dummy, dummy, None) == 1
+    args = [dummy] * 17
+    # order: q k v idx cnt meta cu squ skv table qs ks vs ps out lse ws
+    args[7] = None  # seqused_q
+    args[10] = args[11] = args[12] = None  # dequant scales (quant 0)
+    args[13] = None  # p_scale
+    args[15] = None  # lse (return_lse 0)
+    assert lib.gbsa_forward(ctypes.byref(good), *args, 0, None) == 6  # workspace too small
+    args2 = list(args)
+    args2[11] = dummy  # a dequant scale with quant 0
+    assert lib.gbsa_forward(ctypes.byref(good), *args2, 1 << 40, None) == 3
+    args3 = list(args)
+    args3[13] = dummy  # p_scale is not supported
+    assert lib.gbsa_forward(ctypes.byref(good), *args3, 1 << 40, None) == 4
+    sz = ctypes.c_size_t(0)
+    assert lib.gbsa_workspace_size(ctypes.byref(good), ctypes.byref(sz)) == 0 and sz.value > 0
+    n = ctypes.c_int32(0)
+    assert lib.gbsa_num_workers(ctypes.byref(good), ctypes.byref(n)) == 0 and n.value == 7
+
+
+def test_status_strings():
+    for code in range(9):
+        assert len(_lib.status_string(code)) >= 2

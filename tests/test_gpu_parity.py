@@ -1,0 +1,250 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Small problems are compared on every row; the full-size workloads on sampled rows, with the
+same launch configuration the benchmark times. The task split is compared word for word
+with the oracle's reference scheduler.
+"""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import gbsa_inputs as gi
+from helpers import (GpuProblem, compact_oracle_inputs, compare, gpu_params, oracle_inputs,
+                     out_f64)
+from oracle import attention as oa
+from oracle import scheduler as sch
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from block_sparse_paged_gbsa_amd import _lib
+    _lib.load()
+
+
+def _ref_meta(p, P):
+    return sch.reference_metadata(
+        cu_seqlens_q=p.cu_seqlens_q, seqused_q=p.seqused_q,
+        sparse_block_count=p.sparse_block_count, num_heads_q=p.num_heads_q,
+        num_heads_kv=p.num_heads_kv, head_dim=128, block_x=p.block_x, block_y=128,
+        top_k=p.top_k, mask_mode=p.mask_mode, quant_mode=p.quant_mode, win_left=p.win_left,
+        win_right=p.win_right, num_workers=P)
+
+
+def _full_check(p, num_workers=0, label=""):
+    _log(f"[parity] {label or p.name} workers={num_workers}")
+    gp = GpuProblem(p)
+    params, meta, out, lse, ws = gp.run(num_workers)
+    assert int(ws[:4].view(torch.int32)[0].item()) == 0
+    P = params.num_workers if num_workers else __import__(
+        "block_sparse_paged_gbsa_amd").gbsa_num_workers(params)
+    np.testing.assert_array_equal(meta.cpu().numpy(), _ref_meta(p, P))
+    O, L, done = oa.sparse_attention(oracle_inputs(p))
+    return compare(p, out, lse if p.return_lse else None, O, L, done, label or p.name)
+
+
+# ---------------------------------------------------------------------------
+# task split
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_metadata_bit_exact_workloads(cfg):
+    p = gi.config(cfg, values=False)
+    _log(f"[meta] workload {cfg}")
+    gp = GpuProblem(p)
+    params = gpu_params(p)
+    from block_sparse_paged_gbsa_amd import gbsa_num_workers
+    P = gbsa_num_workers(params)
+    meta = gp.metadata(params).cpu().numpy()
+    np.testing.assert_array_equal(meta, _ref_meta(p, P))
+    for P2 in (1, 37, 999):
+        meta = gp.metadata(gpu_params(p, P2)).cpu().numpy()
+        np.testing.assert_array_equal(meta, _ref_meta(p, P2))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_metadata_bit_exact_random(seed):
+    rng = np.random.default_rng(seed)
+    p = gi.random_problem(seed, values=False, batch=int(rng.integers(1, 6)),
+                          use_seqused_q=bool(seed % 2), block_x=int(rng.choice([1, 16, 64, 100])),
+                          top_k=int(rng.integers(1, 9)), num_heads_q=8,
+                          num_heads_kv=int(rng.choice([1, 2, 4, 8])))
+    if seed % 3 == 0:  # some zero-count units
+        p.sparse_block_count[:, ::3] = 0
+    P = int(rng.integers(1, 1000))
+    _log(f"[meta] random seed={seed} P={P}")
+    meta = GpuProblem(p).metadata(gpu_params(p, P)).cpu().numpy()
+    np.testing.assert_array_equal(meta, _ref_meta(p, P))
+
+
+# ---------------------------------------------------------------------------
+# small problems: every row
+# ---------------------------------------------------------------------------
+
+def test_workload1_tiny_prefill_all_rows():
+    p = gi.config(1, device="cuda")
+    err, lerr = _full_check(p, label="workload1")
+    _log(f"workload1 O max-abs {err:.3e} LSE rel {lerr:.3e}")
+
+
+@pytest.mark.parametrize("P", [1, 3, 64, 999])
+def test_workload1_any_worker_count(P):
+    _full_check(gi.config(1, device="cuda"), num_workers=P, label=f"workload1 P={P}")
+
+
+CASES = [
+    dict(seed=101, dtype="f16", mask_mode=1),
+    dict(seed=102, dtype="bf16", mask_mode=0, block_x=16),
+    dict(seed=103, dtype="f16", mask_mode=1, win_left=90, win_right=0, use_seqused_q=True),
+    dict(seed=104, dtype="bf16", mask_mode=0, win_left=40, win_right=30, num_heads_q=8,
+         num_heads_kv=2, block_x=48),
+    dict(seed=105, dtype="fp8", mask_mode=1, std=0.7),
+    dict(seed=106, dtype="fp8", mask_mode=0, out_dtype="f16", block_x=64, num_heads_q=4,
+         num_heads_kv=4),
+    dict(seed=107, dtype="bf16", decode=True, batch=5, block_x=1, num_heads_q=16,
+         num_heads_kv=4, mask_mode=1),
+    dict(seed=108, dtype="f16", decode=True, batch=3, block_x=1, num_heads_q=32,
+         num_heads_kv=2, mask_mode=0, top_k=8),
+    dict(seed=109, dtype="f16", page_pad=512, mask_mode=1, use_seqused_q=True, block_x=40),
+    dict(seed=110, dtype="bf16", num_heads_q=16, num_heads_kv=1, block_x=8, top_k=6),
+    dict(seed=111, dtype="f16", num_heads_q=12, num_heads_kv=4, block_x=5, top_k=3,
+         mask_mode=1, win_left=0, win_right=0),
+    dict(seed=112, dtype="fp8", decode=True, batch=4, block_x=2, num_heads_q=8,
+         num_heads_kv=1, top_k=5),
+    dict(seed=113, dtype="bf16", batch=1, max_len=700, block_x=128, num_heads_q=8,
+         num_heads_kv=1, top_k=6, mask_mode=1),
+    dict(seed=114, dtype="f16", batch=4, block_x=17, num_heads_q=2, num_heads_kv=2,
+         top_k=4, mask_mode=1, return_lse=False),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[str(c["seed"]) for c in CASES])
+def test_random_problem_all_rows(case):
+    kw = dict(case)
+    seed = kw.pop("seed")
+    p = gi.random_problem(seed, device="cuda", **kw)
+    for P in (0, 5, 200):
+        _full_check(p, num_workers=P, label=f"random{seed} P={P}")
+
+
+def test_empty_selections_and_inactive_sequences():
+    p = gi.random_problem(120, device="cuda", batch=4, use_seqused_q=True, mask_mode=1)
+    cnt = p.sparse_block_count.copy()
+    cnt[:, ::2] = 0
+    squ = p.seqused_q.copy()
+    squ[1] = 0  # a sequence with no active rows
+    p = dataclasses.replace(p, sparse_block_count=cnt, seqused_q=squ)
+    for P in (0, 7):
+        _full_check(p, num_workers=P, label=f"empty P={P}")
+
+
+def test_rows_beyond_seqused_are_not_written():
+    p = gi.random_problem(121, device="cuda", batch=3, use_seqused_q=True, mask_mode=1)
+    gp = GpuProblem(p)
+    params = gpu_params(p, 9)
+    meta = gp.metadata(params)
+    out = torch.full(p.q.shape, 7.0, dtype=gi.TORCH_DTYPES[p.out_dtype], device="cuda")
+    lse = torch.full(p.q.shape[:2], 7.0, dtype=torch.float32, device="cuda")
+    gp.forward(params, meta, out, lse)
+    torch.cuda.synchronize()
+    o, l = out_f64(out), lse.cpu().numpy()
+    for b in range(p.batch):
+        c0, c1 = int(p.cu_seqlens_q[b]), int(p.cu_seqlens_q[b + 1])
+        sq = int(p.seqused_q[b])
+        assert np.all(o[c0 + sq:c1] == 7.0) and np.all(l[c0 + sq:c1] == 7.0)
+        assert not np.any(o[c0:c0 + sq] == 7.0)
+
+
+def test_deterministic_and_page_shuffle_invariant():
+    p = gi.random_problem(122, device="cuda", batch=3, mask_mode=1, extra_pages=6)
+    _, _, o1, l1, _ = GpuProblem(p).run(11)
+    _, _, o2, l2, _ = GpuProblem(p).run(11)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    rng = np.random.default_rng(3)
+    perm = rng.permutation(p.num_pages)
+    inv = torch.as_tensor(np.argsort(perm), device="cuda")
+    table2 = np.where(p.block_table >= 0, perm[np.maximum(p.block_table, 0)], -1).astype(np.int32)
+    p2 = dataclasses.replace(p, k=p.k[inv].contiguous(), v=p.v[inv].contiguous(),
+                             block_table=table2)
+    _, _, o3, l3, _ = GpuProblem(p2).run(11)
+    assert torch.equal(o1, o3) and torch.equal(l1, l3)
+
+
+def test_metadata_mismatch_is_refused():
+    p = gi.random_problem(123, device="cuda", mask_mode=1)
+    gp = GpuProblem(p)
+    good = gpu_params(p, 8)
+    other = gpu_params(p, 8)
+    other.mask_mode = 0  # metadata built for different attributes
+    meta = gp.metadata(other)
+    out = torch.full(p.q.shape, 3.0, dtype=gi.TORCH_DTYPES[p.out_dtype], device="cuda")
+    _, _, ws = gp.forward(good, meta, out)
+    torch.cuda.synchronize()
+    assert int(ws[:4].view(torch.int32)[0].item()) != 0
+    assert torch.all(out == 3.0)
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, sampled rows, benchmark launch configuration
+# ---------------------------------------------------------------------------
+
+def _sampled_check(cfg, units, rows_per_unit=None, seed=0):
+    _log(f"[parity] workload {cfg}: generating on the GPU")
+    p = gi.config(cfg, device="cuda")
+    gp = GpuProblem(p)
+    params, meta, out, lse, ws = gp.run(0)
+    assert int(ws[:4].view(torch.int32)[0].item()) == 0
+    _log(f"[parity] workload {cfg}: gpu done, oracle on {len(units)} sampled q-blocks")
+    inp = compact_oracle_inputs(p, units)
+    rng = np.random.default_rng(seed)
+    rows = []
+    for (b, gl) in units:
+        lo = gl * p.block_x
+        hi = min((gl + 1) * p.block_x, inp.sq(b), inp.storage(b))
+        ts = np.arange(lo, hi)
+        if rows_per_unit is not None and len(ts) > rows_per_unit:
+            ts = np.unique(np.concatenate([[lo, hi - 1], rng.choice(ts, rows_per_unit - 2,
+                                                                    replace=False)]))
+        rows += list(int(p.cu_seqlens_q[b]) + ts)
+    O, L, done = oa.sparse_attention(inp, rows=rows)
+    err, lerr = compare(p, out, lse if p.return_lse else None, O, L, done, f"workload{cfg}")
+    _log(f"workload{cfg}: rows {int(done.sum())} O max-abs {err:.3e} LSE rel {lerr:.3e}")
+    # every active row must be finite
+    o = out_f64(out)
+    for b in range(p.batch):
+        c0 = int(p.cu_seqlens_q[b])
+        sq = inp.sq(b)
+        assert np.isfinite(o[c0:c0 + sq]).all()
+    return p, out
+
+
+def test_workload2_decode_sampled():
+    _sampled_check(2, [(b, 0) for b in range(0, 64, 3)])
+
+
+def test_workload3_block_sparse_prefill_sampled():
+    units = [(0, 0), (0, 1), (0, 63), (0, 64), (1, 65), (2, 200), (3, 255)]
+    _sampled_check(3, units, rows_per_unit=12)
+
+
+def test_workload4_long_context_sampled():
+    # first blocks, the window edge (rows 32256.. start dropping the sinks), the partial
+    # last KV block (seqused 120000), the last active q-block
+    units = [(0, 0), (0, 3), (0, 503), (0, 504), (0, 505), (0, 1000), (0, 1873), (0, 1874)]
+    _sampled_check(4, units, rows_per_unit=10)
+
+
+def test_workload5_dense_equivalent_fp8_sampled():
+    units = [(0, 0), (0, 1), (0, 100), (1, 255), (1, 128)]
+    _sampled_check(5, units, rows_per_unit=10)

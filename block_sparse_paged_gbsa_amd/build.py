@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgbsa.so")
-SOURCES = ["api.hip", "metadata.hip", "fwd_decode.hip", "fwd_prefill.hip", "combine.hip"]
+SOURCES = ["api.hip", "metadata.hip", "fwd_decode.hip", "fwd_prefill.hip"]
 ARCH = "gfx950"
 
 

@@ -10,7 +10,7 @@
 #include <mutex>
 #include <string.h>
 
-#include "../../include/gbsa.h"
+#include "gbsa.h"
 #include "gbsa_internal.hpp"
 
 using namespace gbsa;
@@ -52,7 +52,7 @@ gbsa_status plan_workers(const gbsa_params* p, int* P_out) {
     const int64_t M = rows_per_unit(p);
     int64_t P;
     if (M <= kDecodeMaxRows) {
-        P = cus;
+        P = 2 * (int64_t)cus;  // two resident decode workgroups per CU
     } else {
         const int rows = prefill_rows_per_wg((int)M);
         const int64_t nst = (M + rows - 1) / rows;
@@ -149,7 +149,8 @@ gbsa_status gbsa_workspace_size(const gbsa_params* p, size_t* bytes) {
     int P = 0;
     st = plan_workers(p, &P);
     if (st != GBSA_OK) return st;
-    *bytes = ws_layout(P, rows_per_unit(p)).total;
+    const int64_t M = rows_per_unit(p);
+    *bytes = ws_layout(P, M, subtiles(M)).total;
     return GBSA_OK;
 }
 
@@ -208,7 +209,7 @@ gbsa_status gbsa_forward(const gbsa_params* p, const void* query, const void* ke
     st = plan_workers(p, &P);
     if (st != GBSA_OK) return st;
     const int64_t M = rows_per_unit(p);
-    const WsLayout L = ws_layout(P, M);
+    const WsLayout L = ws_layout(P, M, subtiles(M));
     if (workspace == nullptr || workspace_bytes < L.total) return GBSA_ERR_WORKSPACE;
 
     FwdArgs a;
@@ -230,7 +231,7 @@ gbsa_status gbsa_forward(const gbsa_params* p, const void* query, const void* ke
     a.lse = softmax_lse;
     unsigned char* ws = (unsigned char*)workspace;
     a.ws_status = (int32_t*)(ws + L.status);
-    a.ws_desc = (PieceDesc*)(ws + L.desc);
+    a.ws_arrive = (int32_t*)(ws + L.arrive);
     a.ws_o = (float*)(ws + L.o);
     a.ws_m = (float*)(ws + L.m);
     a.ws_l = (float*)(ws + L.l);
@@ -257,17 +258,12 @@ gbsa_status gbsa_forward(const gbsa_params* p, const void* query, const void* ke
     a.expect[2] = P;
     fill_fingerprint(p, a.expect);
 
+    a.nst = (int32_t)subtiles(M);
     hipError_t e;
-    if (M <= kDecodeMaxRows) {
-        a.nst = 1;
+    if (M <= kDecodeMaxRows)
         e = launch_decode(a, p->dtype, p->out_dtype, stream);
-    } else {
-        const int rows = prefill_rows_per_wg((int)M);
-        a.nst = (int32_t)((M + rows - 1) / rows);
-        e = launch_prefill(a, p->dtype, p->out_dtype, rows, stream);
-    }
-    if (e != hipSuccess) return GBSA_ERR_HIP;
-    e = launch_combine(a, p->out_dtype, stream);
+    else
+        e = launch_prefill(a, p->dtype, p->out_dtype, prefill_rows_per_wg((int)M), stream);
     return e == hipSuccess ? GBSA_OK : GBSA_ERR_HIP;
 }
 

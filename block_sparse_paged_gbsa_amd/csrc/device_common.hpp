@@ -81,17 +81,24 @@ __device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t x) {
     return (u32x2){__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
 }
 
-__device__ __forceinline__ float wave_max_cols(float x) {
-    // reduce across the four 16-lane groups that share a column (lanes l, l^16, l^32, l^48)
-    x = fmaxf(x, __shfl_xor(x, 16));
-    x = fmaxf(x, __shfl_xor(x, 32));
-    return x;
+// Reductions across the four 16-lane groups that share an MFMA column (lanes l, l^16, l^32,
+// l^48), with the gfx950 lane-swap VALU ops. With both operands equal, permlane16_swap returns
+// the pair {x[l], x[l^16]} (in a fixed order) in both lanes of the pair, permlane32_swap the
+// pair {x[l], x[l^32]}; the results are therefore bit-identical across the four lanes.
+__device__ __forceinline__ float pair_max(float x, bool wide) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    auto r = wide ? __builtin_amdgcn_permlane32_swap(u, u, false, false)
+                  : __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
 }
-__device__ __forceinline__ float wave_sum_cols(float x) {
-    x += __shfl_xor(x, 16);
-    x += __shfl_xor(x, 32);
-    return x;
+__device__ __forceinline__ float pair_sum(float x, bool wide) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    auto r = wide ? __builtin_amdgcn_permlane32_swap(u, u, false, false)
+                  : __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }
+__device__ __forceinline__ float wave_max_cols(float x) { return pair_max(pair_max(x, false), true); }
+__device__ __forceinline__ float wave_sum_cols(float x) { return pair_sum(pair_sum(x, false), true); }
 
 // Workgroups are handed to the 8 XCDs round-robin; give each XCD a contiguous range of
 // logical indices so that neighbouring work (same sequence and KV head) shares an L2.
@@ -105,6 +112,23 @@ __device__ __forceinline__ int xcd_remap(int bid, int grid) {
 template <typename T>
 __device__ __forceinline__ T load_nt(const T* p) {
     return __builtin_nontemporal_load(p);
+}
+
+// Buffer resource over a wave-uniform base: one VGPR offset per lane, per-instruction
+// constants in the scalar offset. Records limit 2^31-1 bytes from the base (gfx9 format word).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff,
+                                             0x00020000);
+}
+// kNT: non-temporal streaming hint (data read once).
+constexpr int kCached = 0, kNT = 2;
+template <int POLICY = kCached>
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, int voff, int soff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, POLICY));
+}
+__device__ __forceinline__ u32x2 buf_load8(rsrc_t r, int voff, int soff) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
 }
 
 // ---------------------------------------------------------------------------
@@ -152,17 +176,14 @@ __device__ __forceinline__ void batch_lengths(const FwdArgs& a, int b, int64_t* 
     *sq = s;
 }
 
-// Block-wide search for the batch holding unit u0 (parallel prefix over the batches).
-// `scratch` needs 2 * blockDim.x + 8 ints of LDS. All threads of the block must call it.
-__device__ inline UnitIter locate_unit(const FwdArgs& a, int u0, int* scratch) {
-    const int tid = threadIdx.x, nt = blockDim.x;
-    int* su = scratch;        // unit counts (inclusive scan)
-    int* sqb = scratch + nt;  // q-block counts (inclusive scan)
-    int* res = scratch + 2 * nt;
-    if (tid == 0) res[0] = -1;
-    int ucarry = 0, qcarry = 0;
-    for (int base = 0; base < a.B; base += nt) {
-        const int b = base + tid;
+// Find the batch holding unit u0. Every wave scans the batches on its own (64 per step, wave
+// prefix sums, no LDS and no barrier), so all lanes of the block end with the same answer.
+// Returns it.b = -1 when u0 lies beyond the last unit.
+__device__ inline UnitIter locate_unit(const FwdArgs& a, int u0) {
+    const int lane = threadIdx.x & 63;
+    int ucarry = 0, qcarry = 0, found_b = -1, found_u = 0, found_q = 0;
+    for (int base = 0; base < a.B && found_b < 0; base += 64) {
+        const int b = base + lane;
         int nu = 0, nq = 0;
         if (b < a.B) {
             int64_t r0;
@@ -171,47 +192,36 @@ __device__ inline UnitIter locate_unit(const FwdArgs& a, int u0, int* scratch) {
             nq = ceil_div_i(st, a.X);
             nu = a.N2 * ceil_div_i(sq, a.X);
         }
-        __syncthreads();
-        su[tid] = nu;
-        sqb[tid] = nq;
-        __syncthreads();
-        for (int off = 1; off < nt; off <<= 1) {
-            int x = 0, y = 0;
-            if (tid >= off) {
-                x = su[tid - off];
-                y = sqb[tid - off];
+        int iu = nu, iq = nq;  // inclusive wave scans
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int xu = __shfl_up(iu, o), xq = __shfl_up(iq, o);
+            if (lane >= o) {
+                iu += xu;
+                iq += xq;
             }
-            __syncthreads();
-            su[tid] += x;
-            sqb[tid] += y;
-            __syncthreads();
         }
-        const int uex = ucarry + su[tid] - nu, qex = qcarry + sqb[tid] - nq;
-        if (b < a.B && nu > 0 && u0 >= uex && u0 < uex + nu) {
-            res[0] = b;
-            res[1] = uex;
-            res[2] = qex;
+        const int uex = ucarry + iu - nu, qex = qcarry + iq - nq;
+        const uint64_t hit = __ballot(b < a.B && nu > 0 && u0 >= uex && u0 < uex + nu);
+        // values read across lanes are uniform: tell the compiler (scalar registers)
+        if (hit) {
+            const int l = __builtin_ctzll(hit);
+            found_b = base + l;
+            found_u = __builtin_amdgcn_readlane(uex, l);
+            found_q = __builtin_amdgcn_readlane(qex, l);
         }
-        ucarry += su[nt - 1];
-        qcarry += sqb[nt - 1];
-        __syncthreads();
-        if (res[0] >= 0) break;
+        ucarry += __builtin_amdgcn_readlane(iu, 63);
+        qcarry += __builtin_amdgcn_readlane(iq, 63);
     }
     UnitIter it;
-    const int b = res[0];
-    if (b < 0) {  // u0 beyond the last unit: the caller treats the worker as empty
-        __syncthreads();
-        it.b = -1;
-        return it;
-    }
-    const int local = u0 - res[1];
-    batch_lengths(a, b, &it.row0, &it.storage, &it.sq);
-    it.b = b;
+    it.b = found_b;
+    if (found_b < 0) return it;
+    const int local = u0 - found_u;
+    batch_lengths(a, found_b, &it.row0, &it.storage, &it.sq);
     it.nact = ceil_div_i(it.sq, a.X);
     it.n2 = local / it.nact;
     it.gl = local % it.nact;
-    it.qbase = res[2];
-    __syncthreads();
+    it.qbase = found_q;
     return it;
 }
 

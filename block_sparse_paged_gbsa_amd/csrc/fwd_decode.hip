@@ -1,36 +1,183 @@
 // Main kernel for units with at most 16 query rows (packed-GQA tile M = blockShapeX * G <= 16),
-// the decode shape. These units are bound by the bytes of the gathered KV pages, so the
-// design goal is many page loads in flight per compute unit:
-//  * one workgroup of 4 waves per worker; the task's KV slots are dealt round-robin to the
-//    waves, each wave keeping its own online-softmax state for the (<= 16) query columns;
-//  * K goes straight from HBM into MFMA A-operand registers (S^T = K Q^T, 16x16x32);
-//  * V is loaded with full-row coalescing, staged through a wave-private LDS buffer and read
-//    back with the gfx950 transpose read as the A operand of O^T = V^T P^T;
-//  * at the end of a task the four wave states are merged through LDS (fixed order).
+// the decode shape. These units are bound by the bytes of the gathered KV pages, so the design
+// keeps many page loads in flight on every compute unit:
+//  * a workgroup of 4 waves per worker, two workgroups per CU (<= 256 VGPRs per lane);
+//  * wave q owns token quarter q (32 tokens) of every selected page of the task and keeps its
+//    own online-softmax state for the <= 16 query columns; the four states are merged through
+//    LDS at the end of the task (fixed order);
+//  * the next page's quarter is loaded into registers while the current one is computed;
+//  * K goes straight from HBM into MFMA A-operand registers (S^T = K Q^T, 16x16x32); V is
+//    loaded with full-row coalescing, staged in a wave-private LDS buffer and read back with the
+//    gfx950 transpose read as the A operand of O^T = V^T P^T;
+//  * split units are merged in-kernel by the last arriving workgroup (split_merge.hpp).
 // GenericBlockSparseAttention article (cf-1.com), "sparse attention mechanism" and
 // "implementation architecture"; FlashAttention article (ai6s.net), "three steps".
-#include "device_common.hpp"
+#include "split_merge.hpp"
 
 namespace gbsa {
 namespace {
 
 constexpr int kNW = 4;
-constexpr int kVPitch = 288;            // bytes per staged V row (bf16/f16)
-constexpr int kStageRows = 64;          // V rows staged per half page
-constexpr int kStageBytes = kStageRows * kVPitch;
-constexpr int kMergeFloats = 16 * 128 + 32;  // per wave: O^T tile + m + l
+constexpr int kVPitch = 288;                       // bytes per staged V row (16-bit)
+template <int DT>
+struct KPitch {
+    static constexpr int value = (DT == kFP8) ? 136 : 272;  // bytes per staged K row
+};
+template <int DT>
+struct Stage {
+    static constexpr int k_bytes = 32 * KPitch<DT>::value;
+    static constexpr int bytes = k_bytes + 32 * kVPitch;  // one quarter page per wave
+};
+constexpr int kMergeFloats = 16 * 128 + 32;        // per wave: O^T tile + m + l
+template <int DT>
+struct Lds {
+    static constexpr int a = kNW * Stage<DT>::bytes, b = kNW * kMergeFloats * 4;
+    static constexpr int bytes = a > b ? a : b;
+};
+
+// Registers of one quarter page (32 tokens), loaded with full-row coalescing:
+// 16-bit rows are 256 B (16 lanes per row, 4 rows per load), fp8 rows 128 B (8 lanes, 8 rows).
+struct Quarter {
+    u32x4 k[8];
+    u32x4 v[8];
+};
+
+__device__ __forceinline__ int row_off(int rs, int lane, int esz) {
+    return esz == 2 ? (lane >> 4) * rs + (lane & 15) * 16 : (lane >> 3) * rs + (lane & 7) * 16;
+}
+
+// kq / vq: wave-uniform base of this wave's 32-token quarter of the K / V page slice.
+template <int DT>
+__device__ __forceinline__ void load_quarter(Quarter& qt, const unsigned char* kq,
+                                             const unsigned char* vq, int rs, int loff) {
+    const rsrc_t rk = make_rsrc(kq), rv = make_rsrc(vq);
+    if constexpr (DT == kFP8) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) qt.k[q] = buf_load16<kNT>(rk, loff, q * 8 * rs);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) qt.v[q] = buf_load16<kNT>(rv, loff, q * 8 * rs);
+    } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) qt.k[q] = buf_load16<kNT>(rk, loff, q * 4 * rs);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) qt.v[q] = buf_load16<kNT>(rv, loff, q * 4 * rs);
+    }
+}
+
+struct WaveState {
+    float m, l;
+    f32x4 o[8];
+};
+
+__device__ __forceinline__ void wave_sync_lds() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int DT>
+__device__ __forceinline__ void compute_quarter(const FwdArgs& a, const Quarter& qt,
+                                                const u32x4 (&qf)[4], const u32x2 (&q8)[4],
+                                                float cs, int64_t p0, int cls, int skv, int64_t d,
+                                                unsigned char* stage, int lane, WaveState& st) {
+    constexpr int PT = (DT == kF16) ? kF16 : kBF16;
+    constexpr int KP = KPitch<DT>::value;
+    const int lrow = lane & 15, lgrp = lane >> 4;
+    unsigned char* ks = stage;
+    unsigned char* vs = stage + Stage<DT>::k_bytes;
+    // stage K and V rows in LDS: K is re-read in MFMA A layout, V with the transpose read
+    if constexpr (DT == kFP8) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int row = q * 8 + (lane >> 3);
+            u32x2* kd = (u32x2*)(ks + row * KP + (lane & 7) * 16);
+            kd[0] = (u32x2){qt.k[q][0], qt.k[q][1]};
+            kd[1] = (u32x2){qt.k[q][2], qt.k[q][3]};
+            const u32x4 vx = qt.v[q];
+            const u32x2 c0 = fp8x4_to_bf16x4(vx[0]), c1 = fp8x4_to_bf16x4(vx[1]);
+            const u32x2 c2 = fp8x4_to_bf16x4(vx[2]), c3 = fp8x4_to_bf16x4(vx[3]);
+            u32x4* vd = (u32x4*)(vs + row * kVPitch + (lane & 7) * 32);
+            vd[0] = (u32x4){c0[0], c0[1], c1[0], c1[1]};
+            vd[1] = (u32x4){c2[0], c2[1], c3[0], c3[1]};
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            *(u32x4*)(ks + (q * 4 + lgrp) * KP + lrow * 16) = qt.k[q];
+            *(u32x4*)(vs + (q * 4 + lgrp) * kVPitch + lrow * 16) = qt.v[q];
+        }
+    }
+    wave_sync_lds();
+    f32x4 sacc[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+        f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+        const unsigned char* kr = ks + (tt * 16 + lrow) * KP;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            if constexpr (DT == kFP8) {
+                acc = mfma_16x16x32_fp8(*(const u32x2*)(kr + kk * 32 + lgrp * 8), q8[kk], acc);
+            } else {
+                acc = mfma_16x16x32<DT>(*(const u32x4*)(kr + (kk * 32 + lgrp * 8) * 2), qf[kk], acc);
+            }
+        }
+        sacc[tt] = acc;
+    }
+    if (cls == 2) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (!key_visible(a, p0 + tt * 16 + lgrp * 4 + i, skv, d)) sacc[tt][i] = kNegInf;
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[tt][i]);
+    mx = wave_max_cols(mx);
+    const float mnew = fmaxf(st.m, mx == kNegInf ? kNegInf : mx * cs);
+    const float muse = (mnew == kNegInf) ? 0.f : mnew;
+    const float alpha = fast_exp2(st.m - muse);
+    st.m = mnew;
+    uint32_t pk[2][2];
+    float ls = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+        float pv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pv[i] = fast_exp2(__builtin_fmaf(sacc[tt][i], cs, -muse));
+            ls += pv[i];
+        }
+        pk[tt][0] = pack2<PT>(pv[0], pv[1]);
+        pk[tt][1] = pack2<PT>(pv[2], pv[3]);
+    }
+    st.l = st.l * alpha + ls;
+    if (__ballot(alpha != 1.f)) {  // skip the rescale when no running max moved
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) st.o[dt] *= alpha;
+    }
+
+    const u32x4 pb = (u32x4){pk[0][0], pk[0][1], pk[1][0], pk[1][1]};
+    const unsigned char* vrow = vs + (lgrp * 4 + (lrow >> 2)) * kVPitch + (lane & 3) * 8;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+        const u32x2 v0 = lds_read_tr16(vrow + dt * 32);
+        const u32x2 v1 = lds_read_tr16(vrow + 16 * kVPitch + dt * 32);
+        st.o[dt] = mfma_16x16x32<PT>((u32x4){v0[0], v0[1], v1[0], v1[1]}, pb, st.o[dt]);
+    }
+    wave_sync_lds();
+}
 
 template <int DT, int OUT>
-__global__ __launch_bounds__(256) void fwd_decode_kernel(FwdArgs a) {
-    constexpr int kLdsBytes = (kNW * kStageBytes > kNW * kMergeFloats * 4)
-                                  ? kNW * kStageBytes
-                                  : kNW * kMergeFloats * 4;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes];
-    __shared__ int scratch[2 * 256 + 8];
-    constexpr int PT = (DT == kF16) ? kF16 : kBF16;  // PV operand type
+__global__ __launch_bounds__(256, 2) void fwd_decode_kernel(FwdArgs a) {
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Lds<DT>::bytes];
+    __shared__ int flag[1];
     constexpr int esz = (DT == kFP8) ? 1 : 2;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform for the compiler
     const int lrow = lane & 15, lgrp = lane >> 4;
     const int w = xcd_remap(blockIdx.x, gridDim.x);
 
@@ -41,11 +188,12 @@ __global__ __launch_bounds__(256) void fwd_decode_kernel(FwdArgs a) {
     const Bound b0 = read_bound(a.meta, w), b1 = read_bound(a.meta, w + 1);
     const int U = a.meta[3];
     if (!bound_less(b0, b1) || b0.u >= U) return;
-    UnitIter it = locate_unit(a, b0.u, scratch);
+    UnitIter it = locate_unit(a, b0.u);
     if (it.b < 0) return;
 
-    unsigned char* stage = smem + wave * kStageBytes;
-    const int64_t rs = (int64_t)a.N2 * 128 * esz;  // bytes between tokens of a page
+    unsigned char* stage = smem + wave * Stage<DT>::bytes;
+    const int rs = a.N2 * 128 * esz;  // bytes between tokens of a page
+    const int loff = row_off(rs, lane, esz);
 
     for (int u = b0.u;; ++u) {
         const int sa = (u == b0.u) ? b0.s : 0;
@@ -64,7 +212,6 @@ __global__ __launch_bounds__(256) void fwd_decode_kernel(FwdArgs a) {
         const bool exists = lrow < rows_exist;
         const int t = t0 + (exists ? lrow / a.G : 0);
         const int h = it.n2 * a.G + (exists ? lrow % a.G : 0);
-        const bool rvalid = exists && t < it.sq;
         float cs = a.scale_log2;
         if constexpr (DT == kFP8) cs *= a.qs[h] * a.ks[it.n2];
         const int64_t qoff = ((it.row0 + t) * a.N1 + h) * 128;
@@ -75,159 +222,89 @@ __global__ __launch_bounds__(256) void fwd_decode_kernel(FwdArgs a) {
             const int d = kk * 32 + lgrp * 8;
             if constexpr (DT == kFP8) {
                 q8[kk] = exists ? *(const u32x2*)((const uint8_t*)a.q + qoff + d) : (u32x2){0, 0};
+                qf[kk] = (u32x4){0, 0, 0, 0};
             } else {
                 qf[kk] = exists ? *(const u32x4*)((const uint16_t*)a.q + qoff + d)
                                 : (u32x4){0, 0, 0, 0};
+                q8[kk] = (u32x2){0, 0};
             }
         }
         const int t_lo = t0, t_hi = t0 + (rows_exist - 1) / a.G;
+        const int64_t dpos = (int64_t)t + off;
 
-        float mrun = kNegInf, lrun = 0.f;
-        f32x4 o[8];
+        WaveState st;
+        st.m = kNegInf;
+        st.l = 0.f;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) o[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        for (int dt = 0; dt < 8; ++dt) st.o[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
         const int32_t* sel = a.idx + ((int64_t)it.n2 * a.tqb + g) * a.topK;
-        for (int s = sa + wave; s < se; s += kNW) {
-            const int j = sel[s];
-            if (j < 0) continue;
-            const int64_t p0 = (int64_t)j * 128;
-            const int cls = block_class(a, p0, skv, off, t_lo, t_hi);
-            if (cls == 0) continue;
-            const int page = a.table[(int64_t)it.b * a.maxb + j];
-            const int64_t pbase = ((int64_t)page * a.kv_stride + (int64_t)it.n2 * 128) * esz;
-            const unsigned char* kg = (const unsigned char*)a.k + pbase;
-            const unsigned char* vg = (const unsigned char*)a.v + pbase;
-
-            // ---- issue all loads of the page ------------------------------------------
-            u32x4 kf[8][4];
-            u32x2 k8[8][4];
-            u32x4 vr[32];
-#pragma unroll
-            for (int tt = 0; tt < 8; ++tt)
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const unsigned char* kp = kg + (tt * 16 + lrow) * rs + (kk * 32 + lgrp * 8) * esz;
-                    if constexpr (DT == kFP8) k8[tt][kk] = load_nt((const u32x2*)kp);
-                    else kf[tt][kk] = load_nt((const u32x4*)kp);
+        const int32_t* trow = a.table + (int64_t)it.b * a.maxb;
+        const int64_t qbyte = (int64_t)wave * 32 * rs;  // this wave's token quarter
+        for (int c0 = sa; c0 < se; c0 += 64) {
+            // slots c0 .. c0+63: lane l holds slot c0 + l
+            const int n = min(64, se - c0);
+            int jl = -1, pl = 0, cl = 0;
+            if (lane < n) {
+                jl = sel[c0 + lane];
+                if (jl >= 0) {
+                    cl = block_class(a, (int64_t)jl * 128, skv, off, t_lo, t_hi);
+                    if (cl != 0) pl = trow[jl];
                 }
-            if constexpr (DT == kFP8) {
-                // 128 B rows: 8 lanes per row, 16 rows per load
-#pragma unroll
-                for (int q = 0; q < 16; ++q)
-                    vr[q] = load_nt((const u32x4*)(vg + (q * 8 + (lane >> 3)) * rs + (lane & 7) * 16));
-            } else {
-                // 256 B rows: 16 lanes per row, 4 rows per load
-#pragma unroll
-                for (int q = 0; q < 32; ++q)
-                    vr[q] = load_nt((const u32x4*)(vg + (q * 4 + lgrp) * rs + lrow * 16));
             }
-
-            // ---- S^T = K Q^T ---------------------------------------------------------
-            f32x4 sacc[8];
-#pragma unroll
-            for (int tt = 0; tt < 8; ++tt) {
-                f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    if constexpr (DT == kFP8) acc = mfma_16x16x32_fp8(k8[tt][kk], q8[kk], acc);
-                    else acc = mfma_16x16x32<DT>(kf[tt][kk], qf[kk], acc);
+            uint64_t todo = __ballot(cl != 0);
+            if (todo == 0) continue;
+            auto base_of = [&](int i, const void* p) {
+                const int page = __builtin_amdgcn_readlane(pl, i);
+                return (const unsigned char*)p +
+                       ((int64_t)page * a.kv_stride + (int64_t)it.n2 * 128) * esz + qbyte;
+            };
+            Quarter qa, qb;
+            int ia = __builtin_ctzll(todo);
+            todo &= todo - 1;
+            load_quarter<DT>(qa, base_of(ia, a.k), base_of(ia, a.v), rs, loff);
+            while (true) {
+                int ib = -1;
+                if (todo) {
+                    ib = __builtin_ctzll(todo);
+                    todo &= todo - 1;
+                    load_quarter<DT>(qb, base_of(ib, a.k), base_of(ib, a.v), rs, loff);
                 }
-                sacc[tt] = acc;
-            }
-            if (cls == 2) {
-                const int64_t d = (int64_t)t + off;
-#pragma unroll
-                for (int tt = 0; tt < 8; ++tt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int64_t p = p0 + tt * 16 + lgrp * 4 + i;
-                        if (!key_visible(a, p, skv, d)) sacc[tt][i] = kNegInf;
-                    }
-            }
-            // ---- online softmax ------------------------------------------------------
-            float mx = kNegInf;
-#pragma unroll
-            for (int tt = 0; tt < 8; ++tt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[tt][i]);
-            mx = wave_max_cols(mx);
-            const float mnew = fmaxf(mrun, mx == kNegInf ? kNegInf : mx * cs);
-            const float muse = (mnew == kNegInf) ? 0.f : mnew;
-            const float alpha = fast_exp2(mrun - muse);
-            mrun = mnew;
-            uint32_t pk[8][2];
-            float ls = 0.f;
-#pragma unroll
-            for (int tt = 0; tt < 8; ++tt) {
-                float pv[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    pv[i] = fast_exp2(__builtin_fmaf(sacc[tt][i], cs, -muse));
-                    ls += pv[i];
+                {
+                    const int j = __builtin_amdgcn_readlane(jl, ia);
+                    const int cls = __builtin_amdgcn_readlane(cl, ia);
+                    compute_quarter<DT>(a, qa, qf, q8, cs, (int64_t)j * 128 + wave * 32, cls, skv,
+                                        dpos, stage, lane, st);
                 }
-                pk[tt][0] = pack2<PT>(pv[0], pv[1]);
-                pk[tt][1] = pack2<PT>(pv[2], pv[3]);
-            }
-            lrun = lrun * alpha + ls;
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
-
-            // ---- O^T += V^T P^T, V staged 64 rows at a time --------------------------
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                if constexpr (DT == kFP8) {
-#pragma unroll
-                    for (int q = 0; q < 8; ++q) {
-                        const u32x4 vx = vr[half * 8 + q];
-                        const u32x2 c0 = fp8x4_to_bf16x4(vx[0]), c1 = fp8x4_to_bf16x4(vx[1]);
-                        const u32x2 c2 = fp8x4_to_bf16x4(vx[2]), c3 = fp8x4_to_bf16x4(vx[3]);
-                        const u32x4 lo = (u32x4){c0[0], c0[1], c1[0], c1[1]};
-                        const u32x4 hi = (u32x4){c2[0], c2[1], c3[0], c3[1]};
-                        u32x4* vd = (u32x4*)(stage + (q * 8 + (lane >> 3)) * kVPitch + (lane & 7) * 32);
-                        vd[0] = lo;
-                        vd[1] = hi;
-                    }
-                } else {
-#pragma unroll
-                    for (int q = 0; q < 16; ++q)
-                        *(u32x4*)(stage + (q * 4 + lgrp) * kVPitch + lrow * 16) = vr[half * 16 + q];
+                if (ib < 0) break;
+                ia = -1;
+                if (todo) {
+                    ia = __builtin_ctzll(todo);
+                    todo &= todo - 1;
+                    load_quarter<DT>(qa, base_of(ia, a.k), base_of(ia, a.v), rs, loff);
                 }
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-                for (int kc2 = 0; kc2 < 2; ++kc2) {
-                    const int kc = half * 2 + kc2;
-                    const u32x4 pb = (u32x4){pk[2 * kc][0], pk[2 * kc][1], pk[2 * kc + 1][0],
-                                             pk[2 * kc + 1][1]};
-                    const unsigned char* vrow =
-                        stage + (kc2 * 32 + lgrp * 4 + (lrow >> 2)) * kVPitch + (lane & 3) * 8;
-#pragma unroll
-                    for (int dt = 0; dt < 8; ++dt) {
-                        const u32x2 v0 = lds_read_tr16(vrow + dt * 32);
-                        const u32x2 v1 = lds_read_tr16(vrow + 16 * kVPitch + dt * 32);
-                        o[dt] = mfma_16x16x32<PT>((u32x4){v0[0], v0[1], v1[0], v1[1]}, pb, o[dt]);
-                    }
+                {
+                    const int j = __builtin_amdgcn_readlane(jl, ib);
+                    const int cls = __builtin_amdgcn_readlane(cl, ib);
+                    compute_quarter<DT>(a, qb, qf, q8, cs, (int64_t)j * 128 + wave * 32, cls, skv,
+                                        dpos, stage, lane, st);
                 }
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                if (ia < 0) break;
             }
         }
 
         // ---- merge the four wave states (fixed order) ----------------------------------
-        lrun = wave_sum_cols(lrun);
+        st.l = wave_sum_cols(st.l);
         __syncthreads();  // staging buffers are reused for the merge
         float* mg = (float*)smem + wave * kMergeFloats;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-            *(f32x4*)(mg + lrow * 128 + dt * 16 + lgrp * 4) = o[dt];
+        for (int dt = 0; dt < 8; ++dt) *(f32x4*)(mg + lrow * 128 + dt * 16 + lgrp * 4) = st.o[dt];
         if (lgrp == 0) {
-            mg[16 * 128 + lrow] = mrun;
-            mg[16 * 128 + 16 + lrow] = lrun;
+            mg[16 * 128 + lrow] = st.m;
+            mg[16 * 128 + 16 + lrow] = st.l;
         }
         __syncthreads();
+        const int slot = 2 * w + (sa > 0 ? 0 : 1);
         {
             // thread -> (column c, 8 consecutive head-dim values)
             const int c = tid & 15, d0 = (tid >> 4) * 8;
@@ -265,7 +342,6 @@ __global__ __launch_bounds__(256) void fwd_decode_kernel(FwdArgs a) {
                     if (a.return_lse && d0 == 0)
                         a.lse[orow] = lsum > 0.f ? (mstar + __log2f(lsum)) * kLn2 : kNegInf;
                 } else {
-                    const int slot = 2 * w + (sa > 0 ? 0 : 1);
                     float* po = a.ws_o + ((int64_t)slot * a.M + c) * 128 + d0;
                     *(f32x4*)po = (f32x4){acc[0], acc[1], acc[2], acc[3]} * vscale;
                     *(f32x4*)(po + 4) = (f32x4){acc[4], acc[5], acc[6], acc[7]} * vscale;
@@ -275,8 +351,12 @@ __global__ __launch_bounds__(256) void fwd_decode_kernel(FwdArgs a) {
                     }
                 }
             }
-            if (!complete && tid == 0)
-                a.ws_desc[2 * w + (sa > 0 ? 0 : 1)] = PieceDesc{it.b, it.n2, it.gl, g};
+        }
+        if (!complete) {
+            const int w_a = unit_starter(a.meta, w, u);
+            const int np = count_pieces(a.meta, w_a, u);
+            if (piece_arrive(a, w_a, np, flag))
+                merge_rows<OUT>(a, w_a, u, 0, rows_exist, it.b, it.n2, t0, it.row0, it.sq);
         }
         __syncthreads();
         advance_unit(a, it);

@@ -12,7 +12,7 @@
 // 16-row tiles and computes S^T = K Q^T so that the 16x16 MFMA result already has the
 // layout PV needs as its B operand (P^T); V^T is read from LDS with the gfx950 transpose
 // read. Running max / sum live in registers, in the log2 domain.
-#include "device_common.hpp"
+#include "split_merge.hpp"
 
 namespace gbsa {
 namespace {
@@ -30,11 +30,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_prefill_kernel(FwdArgs a) {
     constexpr int R = NW * NQ * 16;
     constexpr int KP = KLds<DT>::pitch;
     __shared__ __attribute__((aligned(16))) unsigned char smem[128 * KP + 128 * kVPitch];
-    __shared__ int scratch[2 * NT + 8];
+    __shared__ int flag[1];
     unsigned char* Ks = smem;
     unsigned char* Vs = smem + 128 * KP;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform for the compiler
     const int lin = xcd_remap(blockIdx.x, gridDim.x);
     const int w = lin / a.nst, st = lin - (lin / a.nst) * a.nst;
 
@@ -46,7 +47,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_prefill_kernel(FwdArgs a) {
     const int U = a.meta[3];
     if (!bound_less(b0, b1) || b0.u >= U) return;
 
-    UnitIter it = locate_unit(a, b0.u, scratch);
+    UnitIter it = locate_unit(a, b0.u);
     if (it.b < 0) return;
 
     const int esz = (DT == kFP8) ? 1 : 2;
@@ -254,7 +255,6 @@ __global__ __launch_bounds__(NW * 64) void fwd_prefill_kernel(FwdArgs a) {
             // ---- epilogue: normalised output + LSE, or a split-KV partial --------------
             const float vscale = (DT == kFP8) ? a.vs[it.n2] : 1.f;
             const int slot = 2 * w + (sa > 0 ? 0 : 1);
-            if (!complete && tid == 0) a.ws_desc[slot] = PieceDesc{it.b, it.n2, it.gl, g};
 #pragma unroll
             for (int nq = 0; nq < NQ; ++nq) {
                 const float ltot = wave_sum_cols(lrun[nq]);
@@ -287,6 +287,14 @@ __global__ __launch_bounds__(NW * 64) void fwd_prefill_kernel(FwdArgs a) {
                         a.ws_l[(int64_t)slot * a.M + r] = ltot;
                     }
                 }
+            }
+            if (!complete) {
+                const int w_a = unit_starter(a.meta, w, u);
+                const int np = count_pieces(a.meta, w_a, u);
+                if (piece_arrive(a, w_a * a.nst + st, np, flag))
+                    merge_rows<OUT>(a, w_a, u, row_base, min(row_base + R, rows_exist), it.b,
+                                    it.n2, t0, it.row0, it.sq);
+                __syncthreads();
             }
         }
         advance_unit(a, it);

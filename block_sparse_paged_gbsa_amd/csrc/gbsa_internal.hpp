@@ -34,11 +34,6 @@ struct MetaArgs {
     int32_t header[kHeaderWords];  // words 7..20 prefilled by the host; the rest computed
 };
 
-// Per-split-piece descriptor stored in the workspace (one per piece slot 0..2P-1).
-struct PieceDesc {
-    int32_t b, n2, gl, g;
-};
-
 struct FwdArgs {
     const void* q;
     const void* k;
@@ -56,7 +51,7 @@ struct FwdArgs {
     void* out;             // [T, N1, D]
     float* lse;            // [T, N1] or null
     int32_t* ws_status;    // workspace word 0: non-zero = metadata mismatch
-    PieceDesc* ws_desc;    // [2P]
+    int32_t* ws_arrive;    // [P * nst] arrival counters of split units (left at zero)
     float* ws_o;           // [2P, M, 128]
     float* ws_m;           // [2P, M]  running max, log2 domain
     float* ws_l;           // [2P, M]  running sum
@@ -69,16 +64,16 @@ struct FwdArgs {
 
 // Workspace layout (byte offsets), a pure function of P and M.
 struct WsLayout {
-    size_t status, desc, o, m, l, total;
+    size_t status, arrive, o, m, l, total;
 };
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-inline WsLayout ws_layout(int64_t P, int64_t M) {
+inline WsLayout ws_layout(int64_t P, int64_t M, int64_t nst) {
     WsLayout w;
     w.status = 0;
-    w.desc = 256;
-    w.o = align_up(w.desc + sizeof(PieceDesc) * 2 * P, 256);
+    w.arrive = 256;
+    w.o = align_up(w.arrive + sizeof(int32_t) * P * nst, 256);
     w.m = align_up(w.o + sizeof(float) * 2 * P * M * 128, 256);
     w.l = align_up(w.m + sizeof(float) * 2 * P * M, 256);
     w.total = align_up(w.l + sizeof(float) * 2 * P * M, 256);
@@ -92,10 +87,15 @@ hipError_t launch_metadata(const MetaArgs& a, hipStream_t s);
 hipError_t launch_decode(const FwdArgs& a, int dtype, int out_dtype, hipStream_t s);
 hipError_t launch_prefill(const FwdArgs& a, int dtype, int out_dtype, int rows_per_wg,
                           hipStream_t s);
-hipError_t launch_combine(const FwdArgs& a, int out_dtype, hipStream_t s);
 
 // Rows a prefill workgroup covers for a given M (16-row MFMA tiles, 2 per wave).
 inline int prefill_rows_per_wg(int M) { return M > 128 ? 256 : 128; }
 constexpr int kDecodeMaxRows = 16;
+// Row subtiles per unit (workgroups per worker) for a given M.
+inline int64_t subtiles(int64_t M) {
+    if (M <= kDecodeMaxRows) return 1;
+    const int r = prefill_rows_per_wg((int)M);
+    return (M + r - 1) / r;
+}
 
 }  // namespace gbsa

@@ -22,6 +22,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "block_sparse_paged_gbsa_amd", "csrc")
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "fp8": 5000.0}
 ESIZE = {"f16": 2, "bf16": 2, "fp8": 1}
 
@@ -30,39 +32,81 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def algorithmic_work(p):
+def kernel_source_hash() -> str:
+    """sha256 over the HIP sources; counter summaries are valid only for the same sources."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as fh:
+            h.update(name.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if it matches these sources."""
+    path = os.path.join(PROFILES, f"{kernel}__{workload}__pmc.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if line.startswith("- ") and ":" in line:
+            k, v = line[2:].split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(float(vals["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(mib: int) -> int:
+    """A plain device-to-device copy of a known size (scale reference for FETCH/WRITE_SIZE)."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_dispatch": n}), flush=True)
+    return 0
+
+
+def algorithmic_work(p, units=None):
     """(bytes, flops) the method must move / compute, from the selection structure only.
 
     bytes: K and V rows of every selected block below seqused_kv (once per unit and KV head),
     Q and O rows of active queries, LSE if returned, the used index / count / page-table
     entries. flops: 4 * D per (active query row, head, visible-length key) of selected blocks.
+    units: optional set of (b, q-block) to restrict the count to (a sample).
     """
     import gbsa_inputs as gi
     D = 128
     es = ESIZE[p.dtype]
     G = p.num_heads_q // p.num_heads_kv
     starts = gi.q_block_starts(p.cu_seqlens_q, p.block_x)
-    kv_bytes = 0
-    flops = 0
-    meta_bytes = 0
-    q_rows = 0
+    kv_bytes = flops = meta_bytes = q_rows = 0
     for b in range(p.batch):
         storage = int(p.cu_seqlens_q[b + 1] - p.cu_seqlens_q[b])
         sq = storage if p.seqused_q is None else min(int(p.seqused_q[b]), storage)
         skv = int(p.seqused_kv[b])
-        q_rows += sq
-        nact = -(-sq // p.block_x)
-        if nact == 0:
+        gls = np.arange(-(-sq // p.block_x))
+        if units is not None:
+            gls = np.array([gl for gl in gls if (b, int(gl)) in units], dtype=np.int64)
+        if len(gls) == 0:
             continue
-        g = starts[b] + np.arange(nact)
-        rows = np.minimum((np.arange(nact) + 1) * p.block_x, sq) - np.arange(nact) * p.block_x
-        cnt = np.clip(p.sparse_block_count[:, g], 0, p.top_k)  # [N2, nact]
-        idx = p.sparse_block_idx[:, g, :]  # [N2, nact, topK]
+        g = starts[b] + gls
+        rows = np.minimum((gls + 1) * p.block_x, sq) - gls * p.block_x
+        q_rows += int(rows.sum())
+        cnt = np.clip(p.sparse_block_count[:, g], 0, p.top_k)  # [N2, n]
+        idx = p.sparse_block_idx[:, g, :]  # [N2, n, topK]
         slot = np.arange(p.top_k)[None, None, :]
         used = slot < cnt[:, :, None]
-        j = np.where(used, idx, -1)
-        valid_tok = np.clip(skv - 128 * j.astype(np.int64), 0, 128) * (j >= 0)
-        tok = (valid_tok * used).sum(axis=2)  # [N2, nact]
+        j = np.where(used, idx, -1).astype(np.int64)
+        valid_tok = np.clip(skv - 128 * j, 0, 128) * (j >= 0)
+        tok = (valid_tok * used).sum(axis=2)  # [N2, n]
         kv_bytes += int(tok.sum()) * 2 * D * es
         flops += int((tok * rows[None, :]).sum()) * 4 * D * G
         meta_bytes += int(used.sum()) * 8 + cnt.size * 4  # idx + table entries, counts
@@ -74,8 +118,6 @@ def algorithmic_work(p):
 
 def cpu_baseline(p, budget_s: float):
     """The float64 oracle on a bounded sample of the same workload (rows of whole q-blocks)."""
-    import dataclasses
-
     import torch
     from threadpoolctl import threadpool_limits
 
@@ -136,19 +178,7 @@ def cpu_baseline(p, budget_s: float):
             elapsed += time.perf_counter() - t0
             done_units += batch_units
             n *= 2
-    sub = dataclasses.replace(p)
-    # algorithmic bytes of just the sampled units
-    sel_mask = np.zeros(p.sparse_block_count.shape[1], dtype=bool)
-    keep = {(b, gl) for (b, gl) in done_units}
-    cnt = p.sparse_block_count.copy()
-    for b in range(p.batch):
-        storage = int(p.cu_seqlens_q[b + 1] - p.cu_seqlens_q[b])
-        for gl in range(-(-storage // p.block_x)):
-            if (b, gl) not in keep:
-                cnt[:, starts[b] + gl] = 0
-    sub = dataclasses.replace(p, sparse_block_count=cnt)
-    bytes_s, flops_s = algorithmic_work(sub)
-    # remove the Q/O bytes of rows outside the sample
+    bytes_s, flops_s = algorithmic_work(p, set(done_units))
     return dict(units=len(done_units), seconds=elapsed, bytes=bytes_s, flops=flops_s)
 
 
@@ -160,7 +190,11 @@ def main(argv=None):
     ap.add_argument("--config", type=int, default=2, help="workload id 1..5 (default 2)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain copy of MIB MiB (counter scale reference)")
     a = ap.parse_args(argv)
+    if a.copy_calibration:
+        return copy_calibration(a.copy_calibration)
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the kernel has no cross-GPU path in this build "
               "(run with --gpus 1)", file=sys.stderr)
@@ -238,16 +272,19 @@ def main(argv=None):
     gbs = alg_bytes / (ms_step * 1e-3) / 1e9
     tflops = alg_flops / (ms_step * 1e-3) / 1e12
     hbm_bound = a.config == 2
+    kernel = "fwd_decode_kernel" if p.block_x * p.num_heads_q // p.num_heads_kv <= 16 \
+        else "fwd_prefill_kernel"
+    traffic = measured_traffic(kernel, gi.CONFIG_NAMES[a.config])
     if hbm_bound:
         achieved = alg_bytes / (fwd_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
         metric_value, unit = gbs, "GB/s"
     else:
         achieved = alg_flops / (fwd_ms * 1e-3) / 1e12
         peak = MFMA_PEAK_TFLOPS[p.dtype]
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None}
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic}
         metric_value, unit = tflops, "TFLOP/s"
 
     cpu = None
@@ -268,7 +305,7 @@ def main(argv=None):
                    "head_dim": 128, "block_shape": [p.block_x, 128], "top_k": p.top_k,
                    "kv_pages": p.num_pages, "workers": P},
         "effective_tflops": round(tflops, 3), "hbm_gbs": round(gbs, 2),
-        "forward_ms": round(fwd_ms, 5), "algorithmic_bytes": alg_bytes,
+        "forward_ms": round(fwd_ms, 5), "kernel": kernel, "algorithmic_bytes": alg_bytes,
         "algorithmic_flops": alg_flops, "roofline": roof, "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

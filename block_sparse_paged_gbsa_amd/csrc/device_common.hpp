@@ -21,6 +21,11 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 #define GBSA_LDS __attribute__((address_space(3)))
 
 constexpr float kLog2e = 1.4426950408889634f;
+// Lazy rescaling: the running max of a column only moves when a new block exceeds it by more
+// than kLazyMax (log2 units). Probabilities are then bounded by 2^kLazyMax = 256, which fp32
+// sums and 16-bit P represent without loss of relative precision, and the O rescale is skipped
+// for most blocks. The result is unchanged: numerator and denominator use the same max.
+constexpr float kLazyMax = 8.f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_inff();
 
@@ -262,6 +267,25 @@ __device__ __forceinline__ bool key_visible(const FwdArgs& a, int64_t p, int skv
     if (a.wl >= 0) ok = ok && (p >= d - a.wl);
     if (a.wr >= 0) ok = ok && (p <= d + a.wr);
     return ok;
+}
+
+// Visible key positions of query row d = t + off inside the block starting at p0, as an
+// inclusive range of offsets [*lo, *hi] relative to p0 (empty when *lo > *hi).
+__device__ __forceinline__ void key_range(const FwdArgs& a, int64_t p0, int skv, int64_t d,
+                                          int* lo, int* hi) {
+    int64_t l = 0, h = (int64_t)skv - 1;
+    if (a.mask == 1) h = min(h, d);
+    if (a.wl >= 0) l = max(l, d - a.wl);
+    if (a.wr >= 0) h = min(h, d + a.wr);
+    l -= p0;
+    h -= p0;
+    *lo = (int)max((int64_t)0, min(l, (int64_t)128));
+    *hi = (int)max((int64_t)-1, min(h, (int64_t)127));
+}
+
+// New running max (log2 domain) under lazy rescaling; mx is the block max already scaled.
+__device__ __forceinline__ float lazy_max(float mrun, float mx) {
+    return (mx > mrun + kLazyMax) ? mx : mrun;
 }
 
 template <int OUT>

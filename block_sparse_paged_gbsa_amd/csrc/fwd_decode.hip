@@ -136,7 +136,7 @@ __device__ __forceinline__ void compute_quarter(const FwdArgs& a, const Quarter&
 #pragma unroll
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[tt][i]);
     mx = wave_max_cols(mx);
-    const float mnew = fmaxf(st.m, mx == kNegInf ? kNegInf : mx * cs);
+    const float mnew = lazy_max(st.m, mx == kNegInf ? kNegInf : mx * cs);
     const float muse = (mnew == kNegInf) ? 0.f : mnew;
     const float alpha = fast_exp2(st.m - muse);
     st.m = mnew;

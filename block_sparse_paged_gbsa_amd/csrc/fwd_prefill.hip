@@ -6,36 +6,225 @@
 // article (ai6s.net), "three steps": blockwise loads, online softmax with rescale, blockwise
 // weighted sum, exact.
 //
-// One workgroup = (worker w, row subtile st). The worker's task range comes from the
-// metadata; for each task (unit, slots [a, e)) the workgroup keeps R = NW * NQ * 16 query
-// rows in registers and streams the selected KV pages through LDS. Each wave owns NQ
-// 16-row tiles and computes S^T = K Q^T so that the 16x16 MFMA result already has the
-// layout PV needs as its B operand (P^T); V^T is read from LDS with the gfx950 transpose
-// read. Running max / sum live in registers, in the log2 domain.
+// One workgroup = (worker w, row subtile st) with NW waves; each wave keeps NQ 16-row query
+// tiles in registers. The selected KV pages of the task stream through a double-buffered LDS
+// stage: while the waves compute on page s, each thread's share of page s+1 is already in
+// flight into registers and is written to the other LDS buffer afterwards, so there is one
+// barrier per page. A page is processed as two 64-token halves (online-softmax update per
+// half). S^T = K Q^T on 16x16x32 MFMA (16x16x128 for fp8) leaves P^T in the B-operand layout
+// of O^T = V^T P^T; V^T is read with the gfx950 transpose read. Split units are merged in
+// kernel by the last arriving workgroup (split_merge.hpp).
 #include "split_merge.hpp"
 
 namespace gbsa {
 namespace {
 
-constexpr int kVPitch = 288;  // bytes per V row in LDS (256 + 32: conflict-free tr reads)
+constexpr int kVPitch = 288;  // bytes per V row in LDS (16-bit values, 256 + 32)
 
 template <int DT>
 struct KLds {
-    static constexpr int pitch = (DT == kFP8) ? 136 : 272;  // bytes per K row in LDS
+    // bytes per K row in LDS (288 B measured fastest for the 16-row fragment reads)
+    static constexpr int pitch = (DT == kFP8) ? 144 : 288;
 };
 
+template <int DT>
+struct PageStage {
+    static constexpr int k_bytes = 128 * KLds<DT>::pitch;
+    static constexpr int bytes = k_bytes + 128 * kVPitch;
+};
+
+// Per-thread share of one page (K and V rows) while it travels HBM/L2 -> registers -> LDS.
+template <int DT, int NT>
+struct PageRegs {
+    static constexpr int n16 = (DT == kFP8) ? 1024 / NT : 2048 / NT;  // 16-B chunks of K (= of V)
+    u32x4 k[n16];
+    u32x4 v[n16];
+};
+
+template <int DT, int NT>
+__device__ __forceinline__ void page_load(PageRegs<DT, NT>& r, const unsigned char* kpage,
+                                          const unsigned char* vpage, int rs, int tid) {
+    const rsrc_t rk = make_rsrc(kpage), rv = make_rsrc(vpage);
+    constexpr int lanes_per_row = (DT == kFP8) ? 8 : 16;
+    constexpr int rows_per_pass = NT / lanes_per_row;
+    const int voff = (tid / lanes_per_row) * rs + (tid % lanes_per_row) * 16;
+#pragma unroll
+    for (int i = 0; i < PageRegs<DT, NT>::n16; ++i) r.k[i] = buf_load16(rk, voff, i * rows_per_pass * rs);
+#pragma unroll
+    for (int i = 0; i < PageRegs<DT, NT>::n16; ++i) r.v[i] = buf_load16(rv, voff, i * rows_per_pass * rs);
+}
+
+template <int DT, int NT>
+__device__ __forceinline__ void page_store(const PageRegs<DT, NT>& r, unsigned char* stage,
+                                           int tid) {
+    constexpr int KP = KLds<DT>::pitch;
+    unsigned char* ks = stage;
+    unsigned char* vs = stage + PageStage<DT>::k_bytes;
+    constexpr int lanes_per_row = (DT == kFP8) ? 8 : 16;
+    constexpr int rows_per_pass = NT / lanes_per_row;
+    const int row0 = tid / lanes_per_row, col = tid % lanes_per_row;
+#pragma unroll
+    for (int i = 0; i < PageRegs<DT, NT>::n16; ++i) {
+        const int row = row0 + i * rows_per_pass;
+        *(u32x4*)(ks + row * KP + col * 16) = r.k[i];
+        if constexpr (DT == kFP8) {
+            const u32x4 vx = r.v[i];
+            const u32x2 c0 = fp8x4_to_bf16x4(vx[0]), c1 = fp8x4_to_bf16x4(vx[1]);
+            const u32x2 c2 = fp8x4_to_bf16x4(vx[2]), c3 = fp8x4_to_bf16x4(vx[3]);
+            u32x4* vd = (u32x4*)(vs + row * kVPitch + col * 32);
+            vd[0] = (u32x4){c0[0], c0[1], c1[0], c1[1]};
+            vd[1] = (u32x4){c2[0], c2[1], c3[0], c3[1]};
+        } else {
+            *(u32x4*)(vs + row * kVPitch + col * 16) = r.v[i];
+        }
+    }
+}
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// e4m3 x e4m3 with K = 128 per instruction (a 16-token tile against the whole head dim).
+// A and B are loaded with the same head-dim assignment, so the product is the full dot
+// product whatever order the instruction uses internally.
+__device__ __forceinline__ f32x4 mfma_16x16x128_fp8(u32x4 a0, u32x4 a1, u32x4 b0, u32x4 b1,
+                                                    f32x4 c) {
+    const i32x8 a = (i32x8){(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                            (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+    const i32x8 b = (i32x8){(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
+                            (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+template <int NQ>
+struct QTile {
+    // 16-bit: [tile][head-dim chunk kk]: lane holds d = kk*32 + (lane/16)*8 .. +8
+    // fp8:    [tile][0..1]: lane holds d = (lane/16)*32 .. +32
+    u32x4 q[NQ][4];
+};
+
+// One page (128 tokens) of QK^T, mask, online softmax and PV for this wave's NQ tiles.
+template <int DT, int NQ>
+__device__ __forceinline__ void compute_page(const FwdArgs& a, const unsigned char* stage,
+                                             const QTile<NQ>& qt, const float (&colscale)[NQ],
+                                             const int (&trow)[NQ], int j, int cls, int skv,
+                                             int off, int lane, float (&mrun)[NQ],
+                                             float (&lrun)[NQ], f32x4 (&o)[8][NQ]) {
+    constexpr int KP = KLds<DT>::pitch;
+    constexpr int PT = (DT == kF16) ? kF16 : kBF16;
+    const int lrow = lane & 15, lgrp = lane >> 4;
+    const unsigned char* ks = stage;
+    const unsigned char* vs = stage + PageStage<DT>::k_bytes;
+    // visible key range of each query column, relative to the page start (int32)
+    int vlo[NQ], vhi[NQ];
+    if (cls == 2) {
+#pragma unroll
+        for (int nq = 0; nq < NQ; ++nq) key_range(a, (int64_t)j * 128, skv, (int64_t)trow[nq] + off, &vlo[nq], &vhi[nq]);
+    }
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        f32x4 sacc[4][NQ];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int nq = 0; nq < NQ; ++nq) sacc[tt][nq] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            const unsigned char* kr = ks + (half * 64 + tt * 16 + lrow) * KP;
+            if constexpr (DT == kFP8) {
+                const u32x4 a0 = *(const u32x4*)(kr + lgrp * 32);
+                const u32x4 a1 = *(const u32x4*)(kr + lgrp * 32 + 16);
+#pragma unroll
+                for (int nq = 0; nq < NQ; ++nq)
+                    sacc[tt][nq] = mfma_16x16x128_fp8(a0, a1, qt.q[nq][0], qt.q[nq][1], sacc[tt][nq]);
+            } else {
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    const u32x4 ka = *(const u32x4*)(kr + (kk * 32 + lgrp * 8) * 2);
+#pragma unroll
+                    for (int nq = 0; nq < NQ; ++nq)
+                        sacc[tt][nq] = mfma_16x16x32<DT>(ka, qt.q[nq][kk], sacc[tt][nq]);
+                }
+            }
+            // keep the K fragments of one token tile live at a time (register budget)
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (cls == 2) {
+#pragma unroll
+            for (int nq = 0; nq < NQ; ++nq) {
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int rel = half * 64 + tt * 16 + lgrp * 4 + i;
+                        if (rel < vlo[nq] || rel > vhi[nq]) sacc[tt][nq][i] = kNegInf;
+                    }
+            }
+        }
+        uint32_t pk[4][NQ][2];
+#pragma unroll
+        for (int nq = 0; nq < NQ; ++nq) {
+            float mx = kNegInf;
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[tt][nq][i]);
+            mx = wave_max_cols(mx);
+            const float cs = colscale[nq];
+            const float mnew = lazy_max(mrun[nq], mx == kNegInf ? kNegInf : mx * cs);
+            const float muse = (mnew == kNegInf) ? 0.f : mnew;
+            const float alpha = fast_exp2(mrun[nq] - muse);
+            mrun[nq] = mnew;
+            float ls = 0.f;
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                float pv[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    pv[i] = fast_exp2(__builtin_fmaf(sacc[tt][nq][i], cs, -muse));
+                    ls += pv[i];
+                }
+                pk[tt][nq][0] = pack2<PT>(pv[0], pv[1]);
+                pk[tt][nq][1] = pack2<PT>(pv[2], pv[3]);
+            }
+            lrun[nq] = lrun[nq] * alpha + ls;
+            if (__ballot(alpha != 1.f)) {  // skip the rescale when no running max moved
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt) o[dt][nq] *= alpha;
+            }
+        }
+#pragma unroll
+        for (int kc2 = 0; kc2 < 2; ++kc2) {
+            const int kc = half * 2 + kc2;
+            u32x4 pb[NQ];
+#pragma unroll
+            for (int nq = 0; nq < NQ; ++nq)
+                pb[nq] = (u32x4){pk[2 * kc2][nq][0], pk[2 * kc2][nq][1], pk[2 * kc2 + 1][nq][0],
+                                 pk[2 * kc2 + 1][nq][1]};
+            const unsigned char* vrow =
+                vs + (kc * 32 + lgrp * 4 + (lrow >> 2)) * kVPitch + (lane & 3) * 8;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                const u32x2 v0 = lds_read_tr16(vrow + dt * 32);
+                const u32x2 v1 = lds_read_tr16(vrow + 16 * kVPitch + dt * 32);
+                const u32x4 va = (u32x4){v0[0], v0[1], v1[0], v1[1]};
+#pragma unroll
+                for (int nq = 0; nq < NQ; ++nq) o[dt][nq] = mfma_16x16x32<PT>(va, pb[nq], o[dt][nq]);
+                if (dt & 1) __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+}
+
 template <int DT, int OUT, int NW, int NQ>
-__global__ __launch_bounds__(NW * 64) void fwd_prefill_kernel(FwdArgs a) {
+__global__ __launch_bounds__(NW * 64, 1) void fwd_prefill_kernel(FwdArgs a) {
     constexpr int NT = NW * 64;
     constexpr int R = NW * NQ * 16;
-    constexpr int KP = KLds<DT>::pitch;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[128 * KP + 128 * kVPitch];
+    constexpr int esz = (DT == kFP8) ? 1 : 2;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * PageStage<DT>::bytes];
     __shared__ int flag[1];
-    unsigned char* Ks = smem;
-    unsigned char* Vs = smem + 128 * KP;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform for the compiler
+    const int lrow = lane & 15, lgrp = lane >> 4;
     const int lin = xcd_remap(blockIdx.x, gridDim.x);
     const int w = lin / a.nst, st = lin - (lin / a.nst) * a.nst;
 
@@ -46,13 +235,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_prefill_kernel(FwdArgs a) {
     const Bound b0 = read_bound(a.meta, w), b1 = read_bound(a.meta, w + 1);
     const int U = a.meta[3];
     if (!bound_less(b0, b1) || b0.u >= U) return;
-
     UnitIter it = locate_unit(a, b0.u);
     if (it.b < 0) return;
 
-    const int esz = (DT == kFP8) ? 1 : 2;
-    const int64_t kv_row = (int64_t)a.N2 * 128;  // elements between tokens of a page
-    const int lrow = lane & 15, lgrp = lane >> 4;
+    const int rs = a.N2 * 128 * esz;  // bytes between tokens of a page
 
     for (int u = b0.u;; ++u) {
         const int sa = (u == b0.u) ? b0.s : 0;
@@ -69,9 +255,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_prefill_kernel(FwdArgs a) {
         if (row_base < rows_exist) {
             const int skv = a.skv[it.b];
             const int off = skv - it.sq;
-            // ---- Q tile (B operand of S^T = K Q^T) and per-column state -------------
-            u32x4 qf[NQ][4];
-            u32x2 q8[NQ][4];
+            // ---- Q tiles (B operand of S^T = K Q^T) and per-column state ---------------
+            QTile<NQ> qt;
             float colscale[NQ];
             int trow[NQ];
             bool rvalid[NQ];
@@ -84,18 +269,19 @@ __global__ __launch_bounds__(NW * 64) void fwd_prefill_kernel(FwdArgs a) {
                 trow[nq] = t;
                 rvalid[nq] = exists && t < it.sq;
                 float cs = a.scale_log2;
-                if (DT == kFP8) cs *= a.qs[h] * a.ks[it.n2];
+                if constexpr (DT == kFP8) cs *= a.qs[h] * a.ks[it.n2];
                 colscale[nq] = cs;
                 const int64_t qoff = ((it.row0 + t) * a.N1 + h) * 128;
+                if constexpr (DT == kFP8) {
+                    const u32x4* qp = (const u32x4*)((const uint8_t*)a.q + qoff + lgrp * 32);
+                    qt.q[nq][0] = exists ? qp[0] : (u32x4){0, 0, 0, 0};
+                    qt.q[nq][1] = exists ? qp[1] : (u32x4){0, 0, 0, 0};
+                    qt.q[nq][2] = qt.q[nq][3] = (u32x4){0, 0, 0, 0};
+                } else {
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const int d = kk * 32 + lgrp * 8;
-                    if (DT == kFP8) {
-                        const uint8_t* qp = (const uint8_t*)a.q + qoff + d;
-                        q8[nq][kk] = exists ? *(const u32x2*)qp : (u32x2){0, 0};
-                    } else {
-                        const uint16_t* qp = (const uint16_t*)a.q + qoff + d;
-                        qf[nq][kk] = exists ? *(const u32x4*)qp : (u32x4){0, 0, 0, 0};
+                    for (int kk = 0; kk < 4; ++kk) {
+                        const uint16_t* qp = (const uint16_t*)a.q + qoff + kk * 32 + lgrp * 8;
+                        qt.q[nq][kk] = exists ? *(const u32x4*)qp : (u32x4){0, 0, 0, 0};
                     }
                 }
             }
@@ -113,144 +299,51 @@ __global__ __launch_bounds__(NW * 64) void fwd_prefill_kernel(FwdArgs a) {
             const int t_hi = t0 + (min(row_base + R, rows_exist) - 1) / a.G;
 
             const int32_t* sel = a.idx + ((int64_t)it.n2 * a.tqb + g) * a.topK;
-            for (int s = sa; s < se; ++s) {
-                const int j = sel[s];
-                if (j < 0) continue;
-                const int64_t p0 = (int64_t)j * 128;
-                const int cls = block_class(a, p0, skv, off, t_lo, t_hi);
-                if (cls == 0) continue;
-                const int page = a.table[(int64_t)it.b * a.maxb + j];
-                const int64_t pbase = ((int64_t)page * a.kv_stride + (int64_t)it.n2 * 128) * esz;
-                const unsigned char* kg = (const unsigned char*)a.k + pbase;
-                const unsigned char* vg = (const unsigned char*)a.v + pbase;
-                const int64_t rs = kv_row * esz;  // bytes between tokens
+            const int32_t* ttab = a.table + (int64_t)it.b * a.maxb;
+            const int64_t head_off = (int64_t)it.n2 * 128 * esz;
 
-                __syncthreads();  // previous page fully consumed
-                if (DT == kFP8) {
-                    // K: 128 rows x 128 B; V: 128 rows x 128 B -> widened to bf16 in LDS
-#pragma unroll
-                    for (int i = 0; i < 1024 / NT; ++i) {
-                        const int c = tid + i * NT, row = c >> 3, col = c & 7;
-                        const u32x4 kx = *(const u32x4*)(kg + row * rs + col * 16);
-                        u32x2* kd = (u32x2*)(Ks + row * KP + col * 16);
-                        kd[0] = (u32x2){kx[0], kx[1]};
-                        kd[1] = (u32x2){kx[2], kx[3]};
-                        const u32x4 vx = *(const u32x4*)(vg + row * rs + col * 16);
-                        const u32x2 c0 = fp8x4_to_bf16x4(vx[0]), c1 = fp8x4_to_bf16x4(vx[1]);
-                        const u32x2 c2 = fp8x4_to_bf16x4(vx[2]), c3 = fp8x4_to_bf16x4(vx[3]);
-                        const u32x4 lo = (u32x4){c0[0], c0[1], c1[0], c1[1]};
-                        const u32x4 hi = (u32x4){c2[0], c2[1], c3[0], c3[1]};
-                        u32x4* vd = (u32x4*)(Vs + row * kVPitch + col * 32);
-                        vd[0] = lo;
-                        vd[1] = hi;
-                    }
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 2048 / NT; ++i) {
-                        const int c = tid + i * NT, row = c >> 4, col = c & 15;
-                        const u32x4 kx = *(const u32x4*)(kg + row * rs + col * 16);
-                        const u32x4 vx = *(const u32x4*)(vg + row * rs + col * 16);
-                        *(u32x4*)(Ks + row * KP + col * 16) = kx;
-                        *(u32x4*)(Vs + row * kVPitch + col * 16) = vx;
+            // ---- stream the task's visible pages through the double-buffered stage ------
+            // lane l of every wave holds slot c0 + l of the current 64-slot chunk
+            PageRegs<DT, NT> pr;
+            int buf = 0;
+            bool have_prev = false;  // a page is waiting in stage[buf]
+            int prev_j = 0, prev_cls = 0;
+            for (int c0 = sa; c0 < se; c0 += 64) {
+                const int n = min(64, se - c0);
+                int jl = -1, pl = 0, cl = 0;
+                if (lane < n) {
+                    jl = sel[c0 + lane];
+                    if (jl >= 0) {
+                        cl = block_class(a, (int64_t)jl * 128, skv, off, t_lo, t_hi);
+                        if (cl != 0) pl = ttab[jl];
                     }
                 }
-                __syncthreads();
-
-                // ---- S^T = K Q^T : 8 token tiles x NQ query tiles --------------------
-                f32x4 sacc[8][NQ];
-#pragma unroll
-                for (int tt = 0; tt < 8; ++tt)
-#pragma unroll
-                    for (int nq = 0; nq < NQ; ++nq) sacc[tt][nq] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-#pragma unroll
-                    for (int tt = 0; tt < 8; ++tt) {
-                        const unsigned char* kp =
-                            Ks + (tt * 16 + lrow) * KP + (kk * 32 + lgrp * 8) * esz;
-                        if (DT == kFP8) {
-                            const u32x2 ka = *(const u32x2*)kp;
-#pragma unroll
-                            for (int nq = 0; nq < NQ; ++nq)
-                                sacc[tt][nq] = mfma_16x16x32_fp8(ka, q8[nq][kk], sacc[tt][nq]);
-                        } else {
-                            const u32x4 ka = *(const u32x4*)kp;
-#pragma unroll
-                            for (int nq = 0; nq < NQ; ++nq)
-                                sacc[tt][nq] = mfma_16x16x32<DT == kFP8 ? kBF16 : DT>(
-                                    ka, qf[nq][kk], sacc[tt][nq]);
-                        }
+                uint64_t todo = __ballot(cl != 0);
+                while (todo) {
+                    const int i = __builtin_ctzll(todo);
+                    todo &= todo - 1;
+                    const int page = __builtin_amdgcn_readlane(pl, i);
+                    const int64_t pb = (int64_t)page * a.kv_stride * esz + head_off;
+                    page_load<DT, NT>(pr, (const unsigned char*)a.k + pb,
+                                      (const unsigned char*)a.v + pb, rs, tid);
+                    if (have_prev) {
+                        compute_page<DT, NQ>(a, smem + buf * PageStage<DT>::bytes, qt, colscale,
+                                             trow, prev_j, prev_cls, skv, off, lane, mrun, lrun,
+                                             o);
+                        buf ^= 1;
                     }
-                }
-                // ---- mask ------------------------------------------------------------
-                if (cls == 2) {
-#pragma unroll
-                    for (int nq = 0; nq < NQ; ++nq) {
-                        const int64_t d = (int64_t)trow[nq] + off;
-#pragma unroll
-                        for (int tt = 0; tt < 8; ++tt)
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                const int64_t p = p0 + tt * 16 + lgrp * 4 + i;
-                                if (!key_visible(a, p, skv, d)) sacc[tt][nq][i] = kNegInf;
-                            }
-                    }
-                }
-                // ---- online softmax (log2 domain) --------------------------------------
-                uint32_t pk[8][NQ][2];
-#pragma unroll
-                for (int nq = 0; nq < NQ; ++nq) {
-                    float mx = kNegInf;
-#pragma unroll
-                    for (int tt = 0; tt < 8; ++tt)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[tt][nq][i]);
-                    mx = wave_max_cols(mx);
-                    const float cs = colscale[nq];
-                    const float mnew = fmaxf(mrun[nq], mx == kNegInf ? kNegInf : mx * cs);
-                    const float muse = (mnew == kNegInf) ? 0.f : mnew;
-                    const float alpha = fast_exp2(mrun[nq] - muse);
-                    mrun[nq] = mnew;
-                    float ls = 0.f;
-#pragma unroll
-                    for (int tt = 0; tt < 8; ++tt) {
-                        float pv[4];
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            pv[i] = fast_exp2(__builtin_fmaf(sacc[tt][nq][i], cs, -muse));
-                            ls += pv[i];
-                        }
-                        constexpr int PT = (DT == kF16) ? kF16 : kBF16;
-                        pk[tt][nq][0] = pack2<PT>(pv[0], pv[1]);
-                        pk[tt][nq][1] = pack2<PT>(pv[2], pv[3]);
-                    }
-                    lrun[nq] = lrun[nq] * alpha + ls;
-#pragma unroll
-                    for (int dt = 0; dt < 8; ++dt) o[dt][nq] *= alpha;
-                }
-                // ---- O^T += V^T P^T --------------------------------------------------
-#pragma unroll
-                for (int kc = 0; kc < 4; ++kc) {
-                    u32x4 pb[NQ];
-#pragma unroll
-                    for (int nq = 0; nq < NQ; ++nq)
-                        pb[nq] = (u32x4){pk[2 * kc][nq][0], pk[2 * kc][nq][1],
-                                         pk[2 * kc + 1][nq][0], pk[2 * kc + 1][nq][1]};
-                    const unsigned char* vrow =
-                        Vs + (kc * 32 + lgrp * 4 + (lrow >> 2)) * kVPitch + (lane & 3) * 8;
-#pragma unroll
-                    for (int dt = 0; dt < 8; ++dt) {
-                        const u32x2 v0 = lds_read_tr16(vrow + dt * 32);
-                        const u32x2 v1 = lds_read_tr16(vrow + 16 * kVPitch + dt * 32);
-                        const u32x4 va = (u32x4){v0[0], v0[1], v1[0], v1[1]};
-#pragma unroll
-                        for (int nq = 0; nq < NQ; ++nq) {
-                            constexpr int PT = (DT == kF16) ? kF16 : kBF16;
-                            o[dt][nq] = mfma_16x16x32<PT>(va, pb[nq], o[dt][nq]);
-                        }
-                    }
+                    page_store<DT, NT>(pr, smem + buf * PageStage<DT>::bytes, tid);
+                    __syncthreads();
+                    have_prev = true;
+                    prev_j = __builtin_amdgcn_readlane(jl, i);
+                    prev_cls = __builtin_amdgcn_readlane(cl, i);
                 }
             }
+            if (have_prev) {
+                compute_page<DT, NQ>(a, smem + buf * PageStage<DT>::bytes, qt, colscale, trow,
+                                     prev_j, prev_cls, skv, off, lane, mrun, lrun, o);
+            }
+            __syncthreads();  // the stage is reused by the next task
 
             // ---- epilogue: normalised output + LSE, or a split-KV partial --------------
             const float vscale = (DT == kFP8) ? a.vs[it.n2] : 1.f;
@@ -269,9 +362,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_prefill_kernel(FwdArgs a) {
 #pragma unroll
                     for (int dt = 0; dt < 8; ++dt) {
                         const int d = dt * 16 + lgrp * 4;
-                        const u32x2 pr = (u32x2){pack2<OUT>(o[dt][nq][0] * inv, o[dt][nq][1] * inv),
+                        const u32x2 v2 = (u32x2){pack2<OUT>(o[dt][nq][0] * inv, o[dt][nq][1] * inv),
                                                  pack2<OUT>(o[dt][nq][2] * inv, o[dt][nq][3] * inv)};
-                        *(u32x2*)(op + d) = pr;
+                        *(u32x2*)(op + d) = v2;
                     }
                     if (a.return_lse && lgrp == 0)
                         a.lse[orow] = ltot > 0.f ? (mrun[nq] + __log2f(ltot)) * kLn2 : kNegInf;

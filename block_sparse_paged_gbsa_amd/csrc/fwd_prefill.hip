@@ -101,14 +101,119 @@ struct QTile {
     u32x4 q[NQ][4];
 };
 
-// One page (128 tokens) of QK^T, mask, online softmax and PV for this wave's NQ tiles.
+// QK^T for one 16-token tile of a half page: sacc[nq] += K_tile Q^T.
+template <int DT, int NQ>
+__device__ __forceinline__ void qk_tile(const unsigned char* ks, const QTile<NQ>& qt, int row,
+                                        int lgrp, f32x4 (&sacc)[NQ]) {
+    constexpr int KP = KLds<DT>::pitch;
+    const unsigned char* kr = ks + row * KP;
+#pragma unroll
+    for (int nq = 0; nq < NQ; ++nq) sacc[nq] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    if constexpr (DT == kFP8) {
+        const u32x4 a0 = *(const u32x4*)(kr + lgrp * 32);
+        const u32x4 a1 = *(const u32x4*)(kr + lgrp * 32 + 16);
+#pragma unroll
+        for (int nq = 0; nq < NQ; ++nq)
+            sacc[nq] = mfma_16x16x128_fp8(a0, a1, qt.q[nq][0], qt.q[nq][1], sacc[nq]);
+    } else {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const u32x4 ka = *(const u32x4*)(kr + (kk * 32 + lgrp * 8) * 2);
+#pragma unroll
+            for (int nq = 0; nq < NQ; ++nq) sacc[nq] = mfma_16x16x32<DT>(ka, qt.q[nq][kk], sacc[nq]);
+        }
+    }
+}
+
+// Mask (when needed) and the running-max update of one half page; returns the max to use.
+template <int NQ>
+__device__ __forceinline__ void half_max(f32x4 (&s)[4][NQ], int half, int cls, const int (&vlo)[NQ],
+                                         const int (&vhi)[NQ], const float (&colscale)[NQ],
+                                         int lgrp, float (&mrun)[NQ], float (&muse)[NQ],
+                                         float (&alpha)[NQ]) {
+    if (cls == 2) {
+#pragma unroll
+        for (int nq = 0; nq < NQ; ++nq)
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int rel = half * 64 + tt * 16 + lgrp * 4 + i;
+                    if (rel < vlo[nq] || rel > vhi[nq]) s[tt][nq][i] = kNegInf;
+                }
+    }
+#pragma unroll
+    for (int nq = 0; nq < NQ; ++nq) {
+        float mx = kNegInf;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[tt][nq][i]);
+        mx = wave_max_cols(mx);
+        const float mnew = lazy_max(mrun[nq], mx == kNegInf ? kNegInf : mx * colscale[nq]);
+        muse[nq] = (mnew == kNegInf) ? 0.f : mnew;
+        alpha[nq] = fast_exp2(mrun[nq] - muse[nq]);
+        mrun[nq] = mnew;
+    }
+}
+
+// exp2 of one 16-token tile of S^T (all NQ columns) into packed 16-bit P^T, with row sums.
+template <int PT, int NQ>
+__device__ __forceinline__ void exp_tile(const f32x4 (&s)[NQ], const float (&colscale)[NQ],
+                                         const float (&muse)[NQ], uint32_t (&pk)[NQ][2],
+                                         float (&ls)[NQ]) {
+#pragma unroll
+    for (int nq = 0; nq < NQ; ++nq) {
+        float pv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pv[i] = fast_exp2(__builtin_fmaf(s[nq][i], colscale[nq], -muse[nq]));
+            ls[nq] += pv[i];
+        }
+        pk[nq][0] = pack2<PT>(pv[0], pv[1]);
+        pk[nq][1] = pack2<PT>(pv[2], pv[3]);
+    }
+}
+
+// O^T += V^T P^T for one 32-token chunk kc of the page (P^T from token tiles 2kc2, 2kc2+1).
+template <int PT, int NQ>
+__device__ __forceinline__ void pv_chunk(const unsigned char* vs, int kc, const uint32_t (&pa)[NQ][2],
+                                         const uint32_t (&pb2)[NQ][2], int lane, f32x4 (&o)[8][NQ]) {
+    const int lrow = lane & 15, lgrp = lane >> 4;
+    u32x4 pb[NQ];
+#pragma unroll
+    for (int nq = 0; nq < NQ; ++nq) pb[nq] = (u32x4){pa[nq][0], pa[nq][1], pb2[nq][0], pb2[nq][1]};
+    const unsigned char* vrow = vs + (kc * 32 + lgrp * 4 + (lrow >> 2)) * kVPitch + (lane & 3) * 8;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+        const u32x2 v0 = lds_read_tr16(vrow + dt * 32);
+        const u32x2 v1 = lds_read_tr16(vrow + 16 * kVPitch + dt * 32);
+        const u32x4 va = (u32x4){v0[0], v0[1], v1[0], v1[1]};
+#pragma unroll
+        for (int nq = 0; nq < NQ; ++nq) o[dt][nq] = mfma_16x16x32<PT>(va, pb[nq], o[dt][nq]);
+    }
+}
+
+template <int NQ>
+__device__ __forceinline__ void rescale(float (&alpha)[NQ], f32x4 (&o)[8][NQ]) {
+#pragma unroll
+    for (int nq = 0; nq < NQ; ++nq) {
+        if (__ballot(alpha[nq] != 1.f)) {  // skipped unless some running max moved
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) o[dt][nq] *= alpha[nq];
+        }
+    }
+}
+
+// One page (128 tokens) for this wave's NQ query tiles, software-pipelined in two halves so
+// that independent MFMA and VALU work sit next to each other in the instruction stream:
+//   QK(h0); [QK(h1) | exp(h0)]; [PV(h0) | exp(h1)]; PV(h1).
 template <int DT, int NQ>
 __device__ __forceinline__ void compute_page(const FwdArgs& a, const unsigned char* stage,
                                              const QTile<NQ>& qt, const float (&colscale)[NQ],
                                              const int (&trow)[NQ], int j, int cls, int skv,
                                              int off, int lane, float (&mrun)[NQ],
                                              float (&lrun)[NQ], f32x4 (&o)[8][NQ]) {
-    constexpr int KP = KLds<DT>::pitch;
     constexpr int PT = (DT == kF16) ? kF16 : kBF16;
     const int lrow = lane & 15, lgrp = lane >> 4;
     const unsigned char* ks = stage;
@@ -117,100 +222,51 @@ __device__ __forceinline__ void compute_page(const FwdArgs& a, const unsigned ch
     int vlo[NQ], vhi[NQ];
     if (cls == 2) {
 #pragma unroll
-        for (int nq = 0; nq < NQ; ++nq) key_range(a, (int64_t)j * 128, skv, (int64_t)trow[nq] + off, &vlo[nq], &vhi[nq]);
+        for (int nq = 0; nq < NQ; ++nq)
+            key_range(a, (int64_t)j * 128, skv, (int64_t)trow[nq] + off, &vlo[nq], &vhi[nq]);
+    }
+    f32x4 s0[4][NQ], s1[4][NQ];
+    uint32_t p0[4][NQ][2], p1[4][NQ][2];
+    float muse[NQ], alpha[NQ], ls[NQ];
+
+    // QK(h0)
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+        qk_tile<DT, NQ>(ks, qt, tt * 16 + lrow, lgrp, s0[tt]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    half_max<NQ>(s0, 0, cls, vlo, vhi, colscale, lgrp, mrun, muse, alpha);
+    rescale<NQ>(alpha, o);
+#pragma unroll
+    for (int nq = 0; nq < NQ; ++nq) ls[nq] = 0.f;
+    // QK(h1) | exp(h0)
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+        qk_tile<DT, NQ>(ks, qt, 64 + tt * 16 + lrow, lgrp, s1[tt]);
+        exp_tile<PT, NQ>(s0[tt], colscale, muse, p0[tt], ls);
+        __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        f32x4 sacc[4][NQ];
+    for (int nq = 0; nq < NQ; ++nq) lrun[nq] = lrun[nq] * alpha[nq] + ls[nq];
+    half_max<NQ>(s1, 1, cls, vlo, vhi, colscale, lgrp, mrun, muse, alpha);
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
+    for (int nq = 0; nq < NQ; ++nq) ls[nq] = 0.f;
+    // PV(h0) | exp(h1)
 #pragma unroll
-            for (int nq = 0; nq < NQ; ++nq) sacc[tt][nq] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int kc2 = 0; kc2 < 2; ++kc2) {
+        pv_chunk<PT, NQ>(vs, kc2, p0[2 * kc2], p0[2 * kc2 + 1], lane, o);
+        exp_tile<PT, NQ>(s1[2 * kc2], colscale, muse, p1[2 * kc2], ls);
+        exp_tile<PT, NQ>(s1[2 * kc2 + 1], colscale, muse, p1[2 * kc2 + 1], ls);
+        __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            const unsigned char* kr = ks + (half * 64 + tt * 16 + lrow) * KP;
-            if constexpr (DT == kFP8) {
-                const u32x4 a0 = *(const u32x4*)(kr + lgrp * 32);
-                const u32x4 a1 = *(const u32x4*)(kr + lgrp * 32 + 16);
+    for (int nq = 0; nq < NQ; ++nq) lrun[nq] = lrun[nq] * alpha[nq] + ls[nq];
+    rescale<NQ>(alpha, o);  // after PV(h0): the new max applies to everything accumulated
+    // PV(h1)
 #pragma unroll
-                for (int nq = 0; nq < NQ; ++nq)
-                    sacc[tt][nq] = mfma_16x16x128_fp8(a0, a1, qt.q[nq][0], qt.q[nq][1], sacc[tt][nq]);
-            } else {
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const u32x4 ka = *(const u32x4*)(kr + (kk * 32 + lgrp * 8) * 2);
-#pragma unroll
-                    for (int nq = 0; nq < NQ; ++nq)
-                        sacc[tt][nq] = mfma_16x16x32<DT>(ka, qt.q[nq][kk], sacc[tt][nq]);
-                }
-            }
-            // keep the K fragments of one token tile live at a time (register budget)
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        if (cls == 2) {
-#pragma unroll
-            for (int nq = 0; nq < NQ; ++nq) {
-#pragma unroll
-                for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int rel = half * 64 + tt * 16 + lgrp * 4 + i;
-                        if (rel < vlo[nq] || rel > vhi[nq]) sacc[tt][nq][i] = kNegInf;
-                    }
-            }
-        }
-        uint32_t pk[4][NQ][2];
-#pragma unroll
-        for (int nq = 0; nq < NQ; ++nq) {
-            float mx = kNegInf;
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[tt][nq][i]);
-            mx = wave_max_cols(mx);
-            const float cs = colscale[nq];
-            const float mnew = lazy_max(mrun[nq], mx == kNegInf ? kNegInf : mx * cs);
-            const float muse = (mnew == kNegInf) ? 0.f : mnew;
-            const float alpha = fast_exp2(mrun[nq] - muse);
-            mrun[nq] = mnew;
-            float ls = 0.f;
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-                float pv[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    pv[i] = fast_exp2(__builtin_fmaf(sacc[tt][nq][i], cs, -muse));
-                    ls += pv[i];
-                }
-                pk[tt][nq][0] = pack2<PT>(pv[0], pv[1]);
-                pk[tt][nq][1] = pack2<PT>(pv[2], pv[3]);
-            }
-            lrun[nq] = lrun[nq] * alpha + ls;
-            if (__ballot(alpha != 1.f)) {  // skip the rescale when no running max moved
-#pragma unroll
-                for (int dt = 0; dt < 8; ++dt) o[dt][nq] *= alpha;
-            }
-        }
-#pragma unroll
-        for (int kc2 = 0; kc2 < 2; ++kc2) {
-            const int kc = half * 2 + kc2;
-            u32x4 pb[NQ];
-#pragma unroll
-            for (int nq = 0; nq < NQ; ++nq)
-                pb[nq] = (u32x4){pk[2 * kc2][nq][0], pk[2 * kc2][nq][1], pk[2 * kc2 + 1][nq][0],
-                                 pk[2 * kc2 + 1][nq][1]};
-            const unsigned char* vrow =
-                vs + (kc * 32 + lgrp * 4 + (lrow >> 2)) * kVPitch + (lane & 3) * 8;
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
-                const u32x2 v0 = lds_read_tr16(vrow + dt * 32);
-                const u32x2 v1 = lds_read_tr16(vrow + 16 * kVPitch + dt * 32);
-                const u32x4 va = (u32x4){v0[0], v0[1], v1[0], v1[1]};
-#pragma unroll
-                for (int nq = 0; nq < NQ; ++nq) o[dt][nq] = mfma_16x16x32<PT>(va, pb[nq], o[dt][nq]);
-                if (dt & 1) __builtin_amdgcn_sched_barrier(0);
-            }
-        }
+    for (int kc2 = 0; kc2 < 2; ++kc2) {
+        pv_chunk<PT, NQ>(vs, 2 + kc2, p1[2 * kc2], p1[2 * kc2 + 1], lane, o);
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -397,10 +453,12 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_prefill_kernel(FwdArgs a) {
 template <int DT, int OUT>
 hipError_t launch_t(const FwdArgs& a, int rows, hipStream_t s) {
     const int grid = a.P * a.nst;
+    // 8 waves per workgroup either way: 32 rows per wave for large units, 16 below (more
+    // workgroups, fewer registers)
     if (rows == 256) {
         hipLaunchKernelGGL((fwd_prefill_kernel<DT, OUT, 8, 2>), dim3(grid), dim3(512), 0, s, a);
     } else {
-        hipLaunchKernelGGL((fwd_prefill_kernel<DT, OUT, 4, 2>), dim3(grid), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((fwd_prefill_kernel<DT, OUT, 8, 1>), dim3(grid), dim3(512), 0, s, a);
     }
     return hipGetLastError();
 }

@@ -88,8 +88,8 @@ hipError_t launch_decode(const FwdArgs& a, int dtype, int out_dtype, hipStream_t
 hipError_t launch_prefill(const FwdArgs& a, int dtype, int out_dtype, int rows_per_wg,
                           hipStream_t s);
 
-// Rows a prefill workgroup covers for a given M (16-row MFMA tiles, 2 per wave).
-inline int prefill_rows_per_wg(int M) { return M > 128 ? 256 : 128; }
+// Rows a prefill workgroup covers for a given M (8 waves of one or two 16-row MFMA tiles).
+inline int prefill_rows_per_wg(int M) { return M > 256 ? 256 : 128; }
 constexpr int kDecodeMaxRows = 16;
 // Row subtiles per unit (workgroups per worker) for a given M.
 inline int64_t subtiles(int64_t M) {

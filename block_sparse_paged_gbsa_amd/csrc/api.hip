@@ -178,6 +178,13 @@ gbsa_status gbsa_metadata(const gbsa_params* p, const int32_t* sparse_block_coun
     a.topK = p->top_k;
     a.tqb = p->total_q_blocks;
     a.P = P;
+    {
+        const int64_t lds_cap = 160 * 1024 / (int64_t)sizeof(int) - 2 * ((int64_t)p->batch + 1);
+        int64_t ucap = (int64_t)p->num_heads_kv * p->total_q_blocks;
+        if (ucap > 16384) ucap = 16384;
+        if (ucap > lds_cap) ucap = lds_cap;
+        a.ucap = (int32_t)(ucap > 0 ? ucap : 0);
+    }
     fill_fingerprint(p, a.header);
     return launch_metadata(a, stream) == hipSuccess ? GBSA_OK : GBSA_ERR_HIP;
 }

@@ -31,6 +31,7 @@ struct MetaArgs {
     const int32_t* squ;    // [B] or null
     int32_t* meta;         // [1024]
     int32_t B, N2, X, topK, tqb, P;
+    int32_t ucap;  // units whose clamped counts the kernel keeps in LDS between its passes
     int32_t header[kHeaderWords];  // words 7..20 prefilled by the host; the rest computed
 };
 

@@ -63,13 +63,15 @@ __device__ __forceinline__ int unit_count(const MetaArgs& a, const int* qbase, c
     return min(max(c, 0), a.topK);
 }
 
+
 __global__ __launch_bounds__(1024) void metadata_kernel(MetaArgs a) {
-    extern __shared__ int tabs[];  // qbase[B+1], ubase[B+1]
+    extern __shared__ int tabs[];  // qbase[B+1], ubase[B+1], counts of the first ucap units
     __shared__ long long sh64[16];
     __shared__ int sh_split;
     const int tid = threadIdx.x, nt = blockDim.x;
     int* qbase = tabs;
     int* ubase = tabs + a.B + 1;
+    int* ucount = tabs + 2 * (a.B + 1);
 
     // Per-sequence q-block and unit offsets.
     long long cq = 0, cu = 0;
@@ -102,11 +104,15 @@ __global__ __launch_bounds__(1024) void metadata_kernel(MetaArgs a) {
     const int U = (int)cu;
     const int P = a.P;
 
-    // Total cost.
+    // Total cost (counts kept in LDS for the boundary pass).
     long long part = 0;
-    for (int u = tid; u < U; u += nt) part += unit_count(a, qbase, ubase, u) + 1;
+    for (int u = tid; u < U; u += nt) {
+        const int c = unit_count(a, qbase, ubase, u);
+        if (u < a.ucap) ucount[u] = c;
+        part += c + 1;
+    }
     long long W;
-    (void)block_exclusive_scan<long long>(part, &W, sh64);
+    (void)block_exclusive_scan<long long>(part, &W, sh64);  // ends with a barrier
 
     // Boundaries: unit u owns the targets floor(w*W/P) that fall in [C_u, C_u + cost_u).
     long long carry = 0;
@@ -115,7 +121,7 @@ __global__ __launch_bounds__(1024) void metadata_kernel(MetaArgs a) {
         int c = 0;
         long long cost = 0;
         if (u < U) {
-            c = unit_count(a, qbase, ubase, u);
+            c = u < a.ucap ? ucount[u] : unit_count(a, qbase, ubase, u);
             cost = c + 1;
         }
         long long tot;
@@ -162,7 +168,10 @@ __global__ __launch_bounds__(1024) void metadata_kernel(MetaArgs a) {
 }  // namespace
 
 hipError_t launch_metadata(const MetaArgs& a, hipStream_t s) {
-    const size_t lds = sizeof(int) * 2 * (size_t)(a.B + 1);
+    // per-sequence tables plus the cached counts (the unit count is at most N2 * tqb),
+    // within 160 KiB of LDS
+    const size_t tab_bytes = sizeof(int) * 2 * (size_t)(a.B + 1);
+    const size_t lds = tab_bytes + sizeof(int) * (size_t)a.ucap;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void*)metadata_kernel,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

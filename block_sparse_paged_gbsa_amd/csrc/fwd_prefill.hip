@@ -33,49 +33,57 @@ struct PageStage {
     static constexpr int bytes = k_bytes + 128 * kVPitch;
 };
 
-// Per-thread share of one page (K and V rows) while it travels HBM/L2 -> registers -> LDS.
-template <int DT, int NT>
+// Per-thread share of one K or V page slice while it travels HBM/L2 -> registers -> LDS.
+template <int DT, int NT, int ROWS = 128>
 struct PageRegs {
-    static constexpr int n16 = (DT == kFP8) ? 1024 / NT : 2048 / NT;  // 16-B chunks of K (= of V)
-    u32x4 k[n16];
-    u32x4 v[n16];
+    static constexpr int n16 = ROWS * ((DT == kFP8) ? 8 : 16) / NT;  // 16-B chunks per thread
+    u32x4 x[n16];
 };
 
-template <int DT, int NT>
-__device__ __forceinline__ void page_load(PageRegs<DT, NT>& r, const unsigned char* kpage,
-                                          const unsigned char* vpage, int rs, int tid) {
-    const rsrc_t rk = make_rsrc(kpage), rv = make_rsrc(vpage);
+template <int DT, int NT, int ROWS>
+__device__ __forceinline__ void page_load(PageRegs<DT, NT, ROWS>& r, const unsigned char* page,
+                                          int rs, int tid) {
+    const rsrc_t rk = make_rsrc(page);
     constexpr int lanes_per_row = (DT == kFP8) ? 8 : 16;
     constexpr int rows_per_pass = NT / lanes_per_row;
     const int voff = (tid / lanes_per_row) * rs + (tid % lanes_per_row) * 16;
 #pragma unroll
-    for (int i = 0; i < PageRegs<DT, NT>::n16; ++i) r.k[i] = buf_load16(rk, voff, i * rows_per_pass * rs);
-#pragma unroll
-    for (int i = 0; i < PageRegs<DT, NT>::n16; ++i) r.v[i] = buf_load16(rv, voff, i * rows_per_pass * rs);
+    for (int i = 0; i < PageRegs<DT, NT, ROWS>::n16; ++i)
+        r.x[i] = buf_load16(rk, voff, i * rows_per_pass * rs);
 }
 
-template <int DT, int NT>
-__device__ __forceinline__ void page_store(const PageRegs<DT, NT>& r, unsigned char* stage,
-                                           int tid) {
+// K rows into the K area of an LDS stage
+template <int DT, int NT, int ROWS>
+__device__ __forceinline__ void store_k(const PageRegs<DT, NT, ROWS>& r, unsigned char* stage,
+                                        int tid) {
     constexpr int KP = KLds<DT>::pitch;
-    unsigned char* ks = stage;
-    unsigned char* vs = stage + PageStage<DT>::k_bytes;
     constexpr int lanes_per_row = (DT == kFP8) ? 8 : 16;
     constexpr int rows_per_pass = NT / lanes_per_row;
     const int row0 = tid / lanes_per_row, col = tid % lanes_per_row;
 #pragma unroll
-    for (int i = 0; i < PageRegs<DT, NT>::n16; ++i) {
+    for (int i = 0; i < PageRegs<DT, NT, ROWS>::n16; ++i)
+        *(u32x4*)(stage + (row0 + i * rows_per_pass) * KP + col * 16) = r.x[i];
+}
+
+// V rows (fp8 widened to bf16) into the V area `vs` of an LDS stage
+template <int DT, int NT, int ROWS>
+__device__ __forceinline__ void store_v(const PageRegs<DT, NT, ROWS>& r, unsigned char* vs,
+                                        int tid) {
+    constexpr int lanes_per_row = (DT == kFP8) ? 8 : 16;
+    constexpr int rows_per_pass = NT / lanes_per_row;
+    const int row0 = tid / lanes_per_row, col = tid % lanes_per_row;
+#pragma unroll
+    for (int i = 0; i < PageRegs<DT, NT, ROWS>::n16; ++i) {
         const int row = row0 + i * rows_per_pass;
-        *(u32x4*)(ks + row * KP + col * 16) = r.k[i];
         if constexpr (DT == kFP8) {
-            const u32x4 vx = r.v[i];
+            const u32x4 vx = r.x[i];
             const u32x2 c0 = fp8x4_to_bf16x4(vx[0]), c1 = fp8x4_to_bf16x4(vx[1]);
             const u32x2 c2 = fp8x4_to_bf16x4(vx[2]), c3 = fp8x4_to_bf16x4(vx[3]);
             u32x4* vd = (u32x4*)(vs + row * kVPitch + col * 32);
             vd[0] = (u32x4){c0[0], c0[1], c1[0], c1[1]};
             vd[1] = (u32x4){c2[0], c2[1], c3[0], c3[1]};
         } else {
-            *(u32x4*)(vs + row * kVPitch + col * 16) = r.v[i];
+            *(u32x4*)(vs + row * kVPitch + col * 16) = r.x[i];
         }
     }
 }
@@ -175,14 +183,12 @@ __device__ __forceinline__ void exp_tile(const f32x4 (&s)[NQ], const float (&col
     }
 }
 
-// O^T += V^T P^T for one 32-token chunk kc of the page (P^T from token tiles 2kc2, 2kc2+1).
+// O^T += V^T P^T for one 32-token chunk kc of the staged V rows; pb[nq] is the B operand
+// (P^T of token tiles 2kc, 2kc + 1 for query tile nq).
 template <int PT, int NQ>
-__device__ __forceinline__ void pv_chunk(const unsigned char* vs, int kc, const uint32_t (&pa)[NQ][2],
-                                         const uint32_t (&pb2)[NQ][2], int lane, f32x4 (&o)[8][NQ]) {
+__device__ __forceinline__ void pv_chunk4(const unsigned char* vs, int kc, const u32x4 (&pb)[NQ],
+                                          int lane, f32x4 (&o)[8][NQ]) {
     const int lrow = lane & 15, lgrp = lane >> 4;
-    u32x4 pb[NQ];
-#pragma unroll
-    for (int nq = 0; nq < NQ; ++nq) pb[nq] = (u32x4){pa[nq][0], pa[nq][1], pb2[nq][0], pb2[nq][1]};
     const unsigned char* vrow = vs + (kc * 32 + lgrp * 4 + (lrow >> 2)) * kVPitch + (lane & 3) * 8;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
@@ -191,6 +197,33 @@ __device__ __forceinline__ void pv_chunk(const unsigned char* vs, int kc, const 
         const u32x4 va = (u32x4){v0[0], v0[1], v1[0], v1[1]};
 #pragma unroll
         for (int nq = 0; nq < NQ; ++nq) o[dt][nq] = mfma_16x16x32<PT>(va, pb[nq], o[dt][nq]);
+    }
+}
+
+template <int PT, int NQ>
+__device__ __forceinline__ void pv_chunk(const unsigned char* vs, int kc, const uint32_t (&pa)[NQ][2],
+                                         const uint32_t (&pb2)[NQ][2], int lane, f32x4 (&o)[8][NQ]) {
+    u32x4 pb[NQ];
+#pragma unroll
+    for (int nq = 0; nq < NQ; ++nq) pb[nq] = (u32x4){pa[nq][0], pa[nq][1], pb2[nq][0], pb2[nq][1]};
+    pv_chunk4<PT, NQ>(vs, kc, pb, lane, o);
+}
+
+// exp2 of one 16-token tile of S^T into half `h` (elements 2h, 2h + 1) of the PV B operand.
+template <int PT, int NQ>
+__device__ __forceinline__ void exp_tile4(const f32x4 (&s)[NQ], const float (&colscale)[NQ],
+                                          const float (&muse)[NQ], u32x4 (&pq)[NQ], int h,
+                                          float (&ls)[NQ]) {
+#pragma unroll
+    for (int nq = 0; nq < NQ; ++nq) {
+        float pv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pv[i] = fast_exp2(__builtin_fmaf(s[nq][i], colscale[nq], -muse[nq]));
+            ls[nq] += pv[i];
+        }
+        pq[nq][2 * h] = pack2<PT>(pv[0], pv[1]);
+        pq[nq][2 * h + 1] = pack2<PT>(pv[2], pv[3]);
     }
 }
 
@@ -205,68 +238,159 @@ __device__ __forceinline__ void rescale(float (&alpha)[NQ], f32x4 (&o)[8][NQ]) {
     }
 }
 
+// State carried from the first to the second part of a page.
+template <int NQ>
+struct PageMid {
+    f32x4 s1[4][NQ];
+    uint32_t p0[4][NQ][2];
+    float muse[NQ], alpha[NQ];
+};
+
 // One page (128 tokens) for this wave's NQ query tiles, software-pipelined in two halves so
 // that independent MFMA and VALU work sit next to each other in the instruction stream:
-//   QK(h0); [QK(h1) | exp(h0)]; [PV(h0) | exp(h1)]; PV(h1).
+//   part A: QK(h0); [QK(h1) | exp(h0)]      part B: [PV(h0) | exp(h1)]; PV(h1)
+// The caller moves the next page's K (between the parts) and V (after part B) into the other
+// LDS buffer, so only one tensor's share is held in registers at a time.
 template <int DT, int NQ>
-__device__ __forceinline__ void compute_page(const FwdArgs& a, const unsigned char* stage,
-                                             const QTile<NQ>& qt, const float (&colscale)[NQ],
-                                             const int (&trow)[NQ], int j, int cls, int skv,
-                                             int off, int lane, float (&mrun)[NQ],
-                                             float (&lrun)[NQ], f32x4 (&o)[8][NQ]) {
+__device__ __forceinline__ void page_part_a(const FwdArgs& a, const unsigned char* stage,
+                                            const QTile<NQ>& qt, const float (&colscale)[NQ],
+                                            const int (&trow)[NQ], int j, int cls, int skv,
+                                            int off, int lane, float (&mrun)[NQ],
+                                            float (&lrun)[NQ], f32x4 (&o)[8][NQ],
+                                            PageMid<NQ>& mid) {
     constexpr int PT = (DT == kF16) ? kF16 : kBF16;
     const int lrow = lane & 15, lgrp = lane >> 4;
     const unsigned char* ks = stage;
-    const unsigned char* vs = stage + PageStage<DT>::k_bytes;
-    // visible key range of each query column, relative to the page start (int32)
     int vlo[NQ], vhi[NQ];
     if (cls == 2) {
 #pragma unroll
         for (int nq = 0; nq < NQ; ++nq)
             key_range(a, (int64_t)j * 128, skv, (int64_t)trow[nq] + off, &vlo[nq], &vhi[nq]);
     }
-    f32x4 s0[4][NQ], s1[4][NQ];
-    uint32_t p0[4][NQ][2], p1[4][NQ][2];
-    float muse[NQ], alpha[NQ], ls[NQ];
-
-    // QK(h0)
+    f32x4 s0[4][NQ];
+    float ls[NQ];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
         qk_tile<DT, NQ>(ks, qt, tt * 16 + lrow, lgrp, s0[tt]);
         __builtin_amdgcn_sched_barrier(0);
     }
-    half_max<NQ>(s0, 0, cls, vlo, vhi, colscale, lgrp, mrun, muse, alpha);
-    rescale<NQ>(alpha, o);
+    half_max<NQ>(s0, 0, cls, vlo, vhi, colscale, lgrp, mrun, mid.muse, mid.alpha);
+    rescale<NQ>(mid.alpha, o);
 #pragma unroll
     for (int nq = 0; nq < NQ; ++nq) ls[nq] = 0.f;
-    // QK(h1) | exp(h0)
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
-        qk_tile<DT, NQ>(ks, qt, 64 + tt * 16 + lrow, lgrp, s1[tt]);
-        exp_tile<PT, NQ>(s0[tt], colscale, muse, p0[tt], ls);
+        qk_tile<DT, NQ>(ks, qt, 64 + tt * 16 + lrow, lgrp, mid.s1[tt]);
+        exp_tile<PT, NQ>(s0[tt], colscale, mid.muse, mid.p0[tt], ls);
         __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int nq = 0; nq < NQ; ++nq) lrun[nq] = lrun[nq] * alpha[nq] + ls[nq];
-    half_max<NQ>(s1, 1, cls, vlo, vhi, colscale, lgrp, mrun, muse, alpha);
+    for (int nq = 0; nq < NQ; ++nq) lrun[nq] = lrun[nq] * mid.alpha[nq] + ls[nq];
+    half_max<NQ>(mid.s1, 1, cls, vlo, vhi, colscale, lgrp, mrun, mid.muse, mid.alpha);
+}
+
+template <int DT, int NQ>
+__device__ __forceinline__ void page_part_b(const unsigned char* stage, const float (&colscale)[NQ],
+                                            int lane, float (&lrun)[NQ], f32x4 (&o)[8][NQ],
+                                            PageMid<NQ>& mid) {
+    constexpr int PT = (DT == kF16) ? kF16 : kBF16;
+    const unsigned char* vs = stage + PageStage<DT>::k_bytes;
+    uint32_t p1[4][NQ][2];
+    float ls[NQ];
 #pragma unroll
     for (int nq = 0; nq < NQ; ++nq) ls[nq] = 0.f;
-    // PV(h0) | exp(h1)
 #pragma unroll
     for (int kc2 = 0; kc2 < 2; ++kc2) {
-        pv_chunk<PT, NQ>(vs, kc2, p0[2 * kc2], p0[2 * kc2 + 1], lane, o);
-        exp_tile<PT, NQ>(s1[2 * kc2], colscale, muse, p1[2 * kc2], ls);
-        exp_tile<PT, NQ>(s1[2 * kc2 + 1], colscale, muse, p1[2 * kc2 + 1], ls);
+        pv_chunk<PT, NQ>(vs, kc2, mid.p0[2 * kc2], mid.p0[2 * kc2 + 1], lane, o);
+        exp_tile<PT, NQ>(mid.s1[2 * kc2], colscale, mid.muse, p1[2 * kc2], ls);
+        exp_tile<PT, NQ>(mid.s1[2 * kc2 + 1], colscale, mid.muse, p1[2 * kc2 + 1], ls);
         __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int nq = 0; nq < NQ; ++nq) lrun[nq] = lrun[nq] * alpha[nq] + ls[nq];
-    rescale<NQ>(alpha, o);  // after PV(h0): the new max applies to everything accumulated
-    // PV(h1)
+    for (int nq = 0; nq < NQ; ++nq) lrun[nq] = lrun[nq] * mid.alpha[nq] + ls[nq];
+    rescale<NQ>(mid.alpha, o);  // after PV(h0): the new max applies to everything accumulated
 #pragma unroll
     for (int kc2 = 0; kc2 < 2; ++kc2) {
         pv_chunk<PT, NQ>(vs, 2 + kc2, p1[2 * kc2], p1[2 * kc2 + 1], lane, o);
         __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+
+// Query tiles of this wave (B operand of S^T = K Q^T) and the per-column state.
+template <int DT, int NQ>
+__device__ __forceinline__ void load_q(const FwdArgs& a, const UnitIter& it, int t0, int rows_exist,
+                                       int row0, int lane, QTile<NQ>& qt, float (&colscale)[NQ],
+                                       int (&trow)[NQ], bool (&rvalid)[NQ]) {
+    const int lrow = lane & 15, lgrp = lane >> 4;
+#pragma unroll
+    for (int nq = 0; nq < NQ; ++nq) {
+        const int r = row0 + nq * 16 + lrow;
+        const bool exists = r < rows_exist;
+        const int t = t0 + (exists ? r / a.G : 0);
+        const int h = it.n2 * a.G + (exists ? r % a.G : 0);
+        trow[nq] = t;
+        rvalid[nq] = exists && t < it.sq;
+        float cs = a.scale_log2;
+        if constexpr (DT == kFP8) cs *= a.qs[h] * a.ks[it.n2];
+        colscale[nq] = cs;
+        const int64_t qoff = ((it.row0 + t) * a.N1 + h) * 128;
+        if constexpr (DT == kFP8) {
+            const u32x4* qp = (const u32x4*)((const uint8_t*)a.q + qoff + lgrp * 32);
+            qt.q[nq][0] = exists ? qp[0] : (u32x4){0, 0, 0, 0};
+            qt.q[nq][1] = exists ? qp[1] : (u32x4){0, 0, 0, 0};
+            qt.q[nq][2] = qt.q[nq][3] = (u32x4){0, 0, 0, 0};
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const uint16_t* qp = (const uint16_t*)a.q + qoff + kk * 32 + lgrp * 8;
+                qt.q[nq][kk] = exists ? *(const u32x4*)qp : (u32x4){0, 0, 0, 0};
+            }
+        }
+    }
+}
+
+// Normalised O and LSE of this wave's rows (whole selection), or the unnormalised partial
+// (O, running max, row sum) of a split unit into workspace slot `slot`.
+template <int DT, int OUT, int NQ>
+__device__ __forceinline__ void write_rows(const FwdArgs& a, const UnitIter& it, bool complete,
+                                           int slot, int row0, int lane, const int (&trow)[NQ],
+                                           const bool (&rvalid)[NQ], const float (&mrun)[NQ],
+                                           const float (&lrun)[NQ], const f32x4 (&o)[8][NQ]) {
+    const int lrow = lane & 15, lgrp = lane >> 4;
+    const float vscale = (DT == kFP8) ? a.vs[it.n2] : 1.f;
+#pragma unroll
+    for (int nq = 0; nq < NQ; ++nq) {
+        const float ltot = wave_sum_cols(lrun[nq]);
+        const int r = row0 + nq * 16 + lrow;
+        if (!rvalid[nq]) continue;
+        if (complete) {
+            const float inv = ltot > 0.f ? vscale / ltot : 0.f;
+            const int t = trow[nq];
+            const int h = it.n2 * a.G + r % a.G;
+            const int64_t orow = ((it.row0 + t) * a.N1 + h);
+            uint16_t* op = (uint16_t*)a.out + orow * 128;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                const int d = dt * 16 + lgrp * 4;
+                const u32x2 v2 = (u32x2){pack2<OUT>(o[dt][nq][0] * inv, o[dt][nq][1] * inv),
+                                         pack2<OUT>(o[dt][nq][2] * inv, o[dt][nq][3] * inv)};
+                *(u32x2*)(op + d) = v2;
+            }
+            if (a.return_lse && lgrp == 0)
+                a.lse[orow] = ltot > 0.f ? (mrun[nq] + __log2f(ltot)) * kLn2 : kNegInf;
+        } else {
+            float* po = a.ws_o + ((int64_t)slot * a.M + r) * 128;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                const int d = dt * 16 + lgrp * 4;
+                *(f32x4*)(po + d) = o[dt][nq] * vscale;
+            }
+            if (lgrp == 0) {
+                a.ws_m[(int64_t)slot * a.M + r] = mrun[nq];
+                a.ws_l[(int64_t)slot * a.M + r] = ltot;
+            }
+        }
     }
 }
 
@@ -311,36 +435,12 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_prefill_kernel(FwdArgs a) {
         if (row_base < rows_exist) {
             const int skv = a.skv[it.b];
             const int off = skv - it.sq;
-            // ---- Q tiles (B operand of S^T = K Q^T) and per-column state ---------------
             QTile<NQ> qt;
             float colscale[NQ];
             int trow[NQ];
             bool rvalid[NQ];
-#pragma unroll
-            for (int nq = 0; nq < NQ; ++nq) {
-                const int r = row_base + wave * NQ * 16 + nq * 16 + lrow;
-                const bool exists = r < rows_exist;
-                const int t = t0 + (exists ? r / a.G : 0);
-                const int h = it.n2 * a.G + (exists ? r % a.G : 0);
-                trow[nq] = t;
-                rvalid[nq] = exists && t < it.sq;
-                float cs = a.scale_log2;
-                if constexpr (DT == kFP8) cs *= a.qs[h] * a.ks[it.n2];
-                colscale[nq] = cs;
-                const int64_t qoff = ((it.row0 + t) * a.N1 + h) * 128;
-                if constexpr (DT == kFP8) {
-                    const u32x4* qp = (const u32x4*)((const uint8_t*)a.q + qoff + lgrp * 32);
-                    qt.q[nq][0] = exists ? qp[0] : (u32x4){0, 0, 0, 0};
-                    qt.q[nq][1] = exists ? qp[1] : (u32x4){0, 0, 0, 0};
-                    qt.q[nq][2] = qt.q[nq][3] = (u32x4){0, 0, 0, 0};
-                } else {
-#pragma unroll
-                    for (int kk = 0; kk < 4; ++kk) {
-                        const uint16_t* qp = (const uint16_t*)a.q + qoff + kk * 32 + lgrp * 8;
-                        qt.q[nq][kk] = exists ? *(const u32x4*)qp : (u32x4){0, 0, 0, 0};
-                    }
-                }
-            }
+            load_q<DT, NQ>(a, it, t0, rows_exist, row_base + wave * NQ * 16, lane, qt, colscale,
+                           trow, rvalid);
             float mrun[NQ], lrun[NQ];
             f32x4 o[8][NQ];
 #pragma unroll
@@ -360,7 +460,8 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_prefill_kernel(FwdArgs a) {
 
             // ---- stream the task's visible pages through the double-buffered stage ------
             // lane l of every wave holds slot c0 + l of the current 64-slot chunk
-            PageRegs<DT, NT> pr;
+            PageRegs<DT, NT, 128> pr;
+            PageMid<NQ> mid;
             int buf = 0;
             bool have_prev = false;  // a page is waiting in stage[buf]
             int prev_j = 0, prev_cls = 0;
@@ -380,15 +481,19 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_prefill_kernel(FwdArgs a) {
                     todo &= todo - 1;
                     const int page = __builtin_amdgcn_readlane(pl, i);
                     const int64_t pb = (int64_t)page * a.kv_stride * esz + head_off;
-                    page_load<DT, NT>(pr, (const unsigned char*)a.k + pb,
-                                      (const unsigned char*)a.v + pb, rs, tid);
-                    if (have_prev) {
-                        compute_page<DT, NQ>(a, smem + buf * PageStage<DT>::bytes, qt, colscale,
-                                             trow, prev_j, prev_cls, skv, off, lane, mrun, lrun,
-                                             o);
-                        buf ^= 1;
-                    }
-                    page_store<DT, NT>(pr, smem + buf * PageStage<DT>::bytes, tid);
+                    // the first page goes straight into stage[buf]; later ones into the
+                    // other buffer while stage[buf] is consumed
+                    unsigned char* cur = smem + buf * PageStage<DT>::bytes;
+                    unsigned char* dst = have_prev ? smem + (buf ^ 1) * PageStage<DT>::bytes : cur;
+                    page_load<DT, NT>(pr, (const unsigned char*)a.k + pb, rs, tid);
+                    if (have_prev)
+                        page_part_a<DT, NQ>(a, cur, qt, colscale, trow, prev_j, prev_cls, skv,
+                                            off, lane, mrun, lrun, o, mid);
+                    store_k<DT, NT>(pr, dst, tid);
+                    page_load<DT, NT>(pr, (const unsigned char*)a.v + pb, rs, tid);
+                    if (have_prev) page_part_b<DT, NQ>(cur, colscale, lane, lrun, o, mid);
+                    store_v<DT, NT>(pr, dst + PageStage<DT>::k_bytes, tid);
+                    if (have_prev) buf ^= 1;
                     __syncthreads();
                     have_prev = true;
                     prev_j = __builtin_amdgcn_readlane(jl, i);
@@ -396,47 +501,279 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_prefill_kernel(FwdArgs a) {
                 }
             }
             if (have_prev) {
-                compute_page<DT, NQ>(a, smem + buf * PageStage<DT>::bytes, qt, colscale, trow,
-                                     prev_j, prev_cls, skv, off, lane, mrun, lrun, o);
+                unsigned char* cur = smem + buf * PageStage<DT>::bytes;
+                page_part_a<DT, NQ>(a, cur, qt, colscale, trow, prev_j, prev_cls, skv, off, lane,
+                                    mrun, lrun, o, mid);
+                page_part_b<DT, NQ>(cur, colscale, lane, lrun, o, mid);
             }
             __syncthreads();  // the stage is reused by the next task
 
             // ---- epilogue: normalised output + LSE, or a split-KV partial --------------
-            const float vscale = (DT == kFP8) ? a.vs[it.n2] : 1.f;
-            const int slot = 2 * w + (sa > 0 ? 0 : 1);
+            write_rows<DT, OUT, NQ>(a, it, complete, 2 * w + (sa > 0 ? 0 : 1),
+                                    row_base + wave * NQ * 16, lane, trow, rvalid, mrun, lrun, o);
+            if (!complete) {
+                const int w_a = unit_starter(a.meta, w, u);
+                const int np = count_pieces(a.meta, w_a, u);
+                if (piece_arrive(a, w_a * a.nst + st, np, flag))
+                    merge_rows<OUT>(a, w_a, u, row_base, min(row_base + R, rows_exist), it.b,
+                                    it.n2, t0, it.row0, it.sq);
+                __syncthreads();
+            }
+        }
+        advance_unit(a, it);
+    }
+}
+
+
+// ---------------------------------------------------------------------------------------------
+// 256-row units: two-group ping-pong over half pages.
+//
+// Waves w and w + 4 of a workgroup share a SIMD. Waves 0-3 (group 0) and 4-7 (group 1) each
+// hold 32 query rows per wave and run the same sequence of items over the task's 2n visible
+// half pages (64 tokens each), group 1 one barrier slot behind group 0:
+//   MFMA item k (k = 0..2n):      S_k = K_k Q^T (k < 2n)  and  O += V_{k-1}^T P_{k-1}^T (k > 0)
+//   softmax item k (k < 2n):      mask, running max, rescale of O, P_k = exp2(.), row sums
+// so in every slot one wave of each SIMD issues MFMAs while its partner does the softmax and
+// moves its group's share of the KV stream into LDS (group 0: V_k, group 1: K_{k+2}). K_k and
+// V_k live in LDS buffer k % 2; each is written one slot after the last read of the half page
+// that used the buffer before it, which the slot order guarantees.
+// ---------------------------------------------------------------------------------------------
+
+static_assert(KLds<kBF16>::pitch == kVPitch && KLds<kF16>::pitch == kVPitch,
+              "16-bit K and V rows share one LDS pitch");
+
+template <int DT>
+struct HalfStage {
+    static constexpr int k_bytes = 64 * KLds<DT>::pitch;
+    static constexpr int v_bytes = 64 * kVPitch;
+};
+
+// MFMA item: QK^T of half page k and PV of half page k - 1, interleaved by 32-token chunk.
+template <int DT, int NQ, bool qk, bool pv>
+__device__ __forceinline__ void mfma_item(const unsigned char* ks, const unsigned char* vs,
+                                          const QTile<NQ>& qt, f32x4 (&s)[4][NQ],
+                                          const u32x4 (&p)[2][NQ], f32x4 (&o)[8][NQ], int lane) {
+    constexpr int PT = (DT == kF16) ? kF16 : kBF16;
+    const int lrow = lane & 15, lgrp = lane >> 4;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        if constexpr (qk) {
+            qk_tile<DT, NQ>(ks, qt, (2 * c) * 16 + lrow, lgrp, s[2 * c]);
+            qk_tile<DT, NQ>(ks, qt, (2 * c + 1) * 16 + lrow, lgrp, s[2 * c + 1]);
+        }
+        if constexpr (pv) pv_chunk4<PT, NQ>(vs, c, p[c], lane, o);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// Softmax item for half page `half` of block j (class cls): P = exp2(S * colscale - max)
+// with the online update. Masked keys are set to -inf by bit selection (no compare masks).
+template <int DT, int NQ>
+__device__ __forceinline__ void softmax_item(const FwdArgs& a, f32x4 (&s)[4][NQ],
+                                             u32x4 (&p)[2][NQ],
+                                             const float (&colscale)[NQ], const int (&trow)[NQ],
+                                             int j, int half, int cls, int skv, int off, int lane,
+                                             float (&mrun)[NQ], float (&lrun)[NQ],
+                                             f32x4 (&o)[8][NQ]) {
+    constexpr int PT = (DT == kF16) ? kF16 : kBF16;
+    const int lgrp = lane >> 4;
+    if (cls == 2) {
+#pragma unroll
+        for (int nq = 0; nq < NQ; ++nq) {
+            int vlo, vhi;
+            key_range(a, (int64_t)j * 128, skv, (int64_t)trow[nq] + off, &vlo, &vhi);
+            // element (tt, i) of this lane is key half * 64 + tt * 16 + lgrp * 4 + i of the page
+            const int lo = vlo - half * 64 - lgrp * 4, hi = vhi - half * 64 - lgrp * 4;
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int c = tt * 16 + i;
+                    const uint32_t out = (uint32_t)(((c - lo) | (hi - c)) >> 31);  // ~0 outside
+                    // (bit_cast of a vector element reads element 0: go through a scalar copy)
+                    const float x = s[tt][nq][i];
+                    s[tt][nq][i] = __uint_as_float((__float_as_uint(x) & ~out) | (0xff800000u & out));
+                }
+        }
+    }
+    float muse[NQ], alpha[NQ], ls[NQ];
+#pragma unroll
+    for (int nq = 0; nq < NQ; ++nq) {
+        float mx = kNegInf;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[tt][nq][i]);
+        mx = wave_max_cols(mx);
+        const float mnew = lazy_max(mrun[nq], mx == kNegInf ? kNegInf : mx * colscale[nq]);
+        muse[nq] = (mnew == kNegInf) ? 0.f : mnew;
+        alpha[nq] = fast_exp2(mrun[nq] - muse[nq]);
+        mrun[nq] = mnew;
+        ls[nq] = 0.f;
+    }
+    rescale<NQ>(alpha, o);
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) exp_tile4<PT, NQ>(s[tt], colscale, muse, p[tt >> 1], tt & 1, ls);
+#pragma unroll
+    for (int nq = 0; nq < NQ; ++nq) lrun[nq] = lrun[nq] * alpha[nq] + ls[nq];
+}
+
+template <int DT, int OUT>
+__global__ __launch_bounds__(512, 1) void fwd_prefill_pp_kernel(FwdArgs a) {
+    constexpr int NQ = 2;
+    constexpr int R = 256;
+    constexpr int esz = (DT == kFP8) ? 1 : 2;
+    constexpr int KB = HalfStage<DT>::k_bytes, VB = HalfStage<DT>::v_bytes;
+    // [K buffer 0][K buffer 1][V buffer 0][V buffer 1]
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * KB + 2 * VB];
+    __shared__ int plist_page[256], plist_jc[256];  // the task's visible pages, in order
+    __shared__ int flag[2];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2;  // waves w and w + 4 share a SIMD
+    const int tg = tid & 255;   // thread index within the group
+    const int lin = xcd_remap(blockIdx.x, gridDim.x);
+    const int w = lin / a.nst, st = lin - (lin / a.nst) * a.nst;
+
+    if (!header_ok(a)) {
+        if (tid == 0) atomicOr(a.ws_status, 1);
+        return;
+    }
+    const Bound b0 = read_bound(a.meta, w), b1 = read_bound(a.meta, w + 1);
+    const int U = a.meta[3];
+    if (!bound_less(b0, b1) || b0.u >= U) return;
+    UnitIter it = locate_unit(a, b0.u);
+    if (it.b < 0) return;
+
+    const int rs = a.N2 * 128 * esz;  // bytes between tokens of a page
+    const unsigned char* kbase = (const unsigned char*)a.k;
+    const unsigned char* vbase = (const unsigned char*)a.v;
+    unsigned char* const kst = smem;
+    unsigned char* const vst = smem + 2 * KB;
+
+    for (int u = b0.u;; ++u) {
+        const int sa = (u == b0.u) ? b0.s : 0;
+        if (u >= U || u > b1.u || (u == b1.u && sa >= b1.s)) break;
+        const int g = it.qbase + it.gl;
+        int cnt = 0;
+        if (g < a.tqb) cnt = min(max(a.cnt[(int64_t)it.n2 * a.tqb + g], 0), a.topK);
+        const int se = (u == b1.u) ? b1.s : cnt;
+        const bool complete = (sa == 0) && (se == cnt);
+
+        const int t0 = it.gl * a.X;
+        const int rows_exist = min(a.X, it.storage - t0) * a.G;
+        const int row_base = st * R;
+        if (row_base < rows_exist) {
+            const int skv = a.skv[it.b];
+            const int off = skv - it.sq;
+            const int row0 = row_base + wave * NQ * 16;
+            QTile<NQ> qt;
+            float colscale[NQ];
+            int trow[NQ];
+            bool rvalid[NQ];
+            load_q<DT, NQ>(a, it, t0, rows_exist, row0, lane, qt, colscale, trow, rvalid);
+            float mrun[NQ], lrun[NQ];
+            f32x4 o[8][NQ];
 #pragma unroll
             for (int nq = 0; nq < NQ; ++nq) {
-                const float ltot = wave_sum_cols(lrun[nq]);
-                const int r = row_base + wave * NQ * 16 + nq * 16 + lrow;
-                if (!rvalid[nq]) continue;
-                if (complete) {
-                    const float inv = ltot > 0.f ? vscale / ltot : 0.f;
-                    const int t = trow[nq];
-                    const int h = it.n2 * a.G + r % a.G;
-                    const int64_t orow = ((it.row0 + t) * a.N1 + h);
-                    uint16_t* op = (uint16_t*)a.out + orow * 128;
+                mrun[nq] = kNegInf;
+                lrun[nq] = 0.f;
 #pragma unroll
-                    for (int dt = 0; dt < 8; ++dt) {
-                        const int d = dt * 16 + lgrp * 4;
-                        const u32x2 v2 = (u32x2){pack2<OUT>(o[dt][nq][0] * inv, o[dt][nq][1] * inv),
-                                                 pack2<OUT>(o[dt][nq][2] * inv, o[dt][nq][3] * inv)};
-                        *(u32x2*)(op + d) = v2;
-                    }
-                    if (a.return_lse && lgrp == 0)
-                        a.lse[orow] = ltot > 0.f ? (mrun[nq] + __log2f(ltot)) * kLn2 : kNegInf;
-                } else {
-                    float* po = a.ws_o + ((int64_t)slot * a.M + r) * 128;
-#pragma unroll
-                    for (int dt = 0; dt < 8; ++dt) {
-                        const int d = dt * 16 + lgrp * 4;
-                        *(f32x4*)(po + d) = o[dt][nq] * vscale;
-                    }
-                    if (lgrp == 0) {
-                        a.ws_m[(int64_t)slot * a.M + r] = mrun[nq];
-                        a.ws_l[(int64_t)slot * a.M + r] = ltot;
-                    }
-                }
+                for (int dt = 0; dt < 8; ++dt) o[dt][nq] = (f32x4){0.f, 0.f, 0.f, 0.f};
             }
+            const int t_lo = t0 + row_base / a.G;
+            const int t_hi = t0 + (min(row_base + R, rows_exist) - 1) / a.G;
+            const int32_t* sel = a.idx + ((int64_t)it.n2 * a.tqb + g) * a.topK;
+            const int32_t* ttab = a.table + (int64_t)it.b * a.maxb;
+            const int64_t head_off = (int64_t)it.n2 * 128 * esz;
+
+            // ---- visible pages of this task's selection range, compacted in order ---------
+            if (wave == 0) {
+                int n = 0;
+                for (int c0 = sa; c0 < se; c0 += 64) {
+                    int jl = -1, pl = 0, cl = 0;
+                    if (c0 + lane < se) {
+                        jl = sel[c0 + lane];
+                        if (jl >= 0) {
+                            cl = block_class(a, (int64_t)jl * 128, skv, off, t_lo, t_hi);
+                            if (cl != 0) pl = ttab[jl];
+                        }
+                    }
+                    const uint64_t m = __ballot(cl != 0);
+                    if (cl != 0) {
+                        const int pos = n + __builtin_amdgcn_mbcnt_hi(
+                                                (uint32_t)(m >> 32),
+                                                __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+                        plist_page[pos] = pl;
+                        plist_jc[pos] = jl * 4 + cl;
+                    }
+                    n += __builtin_popcountll(m);
+                }
+                if (lane == 0) flag[1] = n;
+            }
+            __syncthreads();
+            const int nh = 2 * __builtin_amdgcn_readfirstlane(flag[1]);  // half pages
+
+            // address of half page q (K or V) of this head in HBM
+            auto half_src = [&](const unsigned char* base, int q) {
+                const int page = __builtin_amdgcn_readfirstlane(plist_page[q >> 1]);
+                return base + (int64_t)page * a.kv_stride * esz + head_off + (q & 1) * 64 * rs;
+            };
+            if (nh > 0) {
+                f32x4 s[4][NQ];
+                u32x4 p[2][NQ];  // P^T of the last softmax item, as PV B operands
+                {  // K_0 by the whole workgroup before the first slot
+                    PageRegs<DT, 512, 64> pr;
+                    page_load<DT, 512, 64>(pr, half_src(kbase, 0), rs, tid);
+                    store_k<DT, 512, 64>(pr, kst, tid);
+                }
+                __syncthreads();
+                // group 1 starts one slot late; it spends that slot moving K_1 into LDS
+                if (grp == 1) {
+                    PageRegs<DT, 256, 64> pr;
+                    page_load<DT, 256, 64>(pr, half_src(kbase, 1), rs, tg);
+                    store_k<DT, 256, 64>(pr, kst + KB, tg);
+                    __syncthreads();
+                }
+                // softmax item k + this group's share of the KV stream
+                auto softmax_and_move = [&](int k) {
+                    const int jc = __builtin_amdgcn_readfirstlane(plist_jc[k >> 1]);
+                    // half page whose V (group 0) or K (group 1) moves now; past the end of the
+                    // stream group 1 repeats the last K half into a buffer nobody reads again
+                    const int kl = min((grp == 0) ? k : k + 2, nh - 1);
+                    PageRegs<DT, 256, 64> pr;
+                    page_load<DT, 256, 64>(pr, half_src(grp == 0 ? vbase : kbase, kl), rs, tg);
+                    __builtin_amdgcn_sched_barrier(0);
+                    softmax_item<DT, NQ>(a, s, p, colscale, trow, jc >> 2, k & 1, jc & 3, skv, off,
+                                         lane, mrun, lrun, o);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if constexpr (DT == kFP8) {  // V is widened to bf16 on its way into LDS
+                        if (grp == 0)
+                            store_v<DT, 256, 64>(pr, vst + (k & 1) * VB, tg);
+                        else
+                            store_k<DT, 256, 64>(pr, kst + (k & 1) * KB, tg);
+                    } else {  // K and V rows have the same LDS pitch: one store for both groups
+                        store_k<DT, 256, 64>(pr, grp == 0 ? vst + (k & 1) * VB : kst + (k & 1) * KB, tg);
+                    }
+                    __syncthreads();
+                };
+                mfma_item<DT, NQ, true, false>(kst, vst, qt, s, p, o, lane);
+                __syncthreads();
+                softmax_and_move(0);
+                for (int k = 1; k < nh; ++k) {
+                    mfma_item<DT, NQ, true, true>(kst + (k & 1) * KB, vst + ((k - 1) & 1) * VB, qt, s,
+                                                  p, o, lane);
+                    __syncthreads();
+                    softmax_and_move(k);
+                }
+                mfma_item<DT, NQ, false, true>(kst, vst + ((nh - 1) & 1) * VB, qt, s, p, o, lane);
+                if (grp == 0) __syncthreads();
+            }
+            __syncthreads();  // LDS (stages, page list) is reused by the next task
+
+            write_rows<DT, OUT, NQ>(a, it, complete, 2 * w + (sa > 0 ? 0 : 1), row0, lane, trow,
+                                    rvalid, mrun, lrun, o);
             if (!complete) {
                 const int w_a = unit_starter(a.meta, w, u);
                 const int np = count_pieces(a.meta, w_a, u);
@@ -456,7 +793,7 @@ hipError_t launch_t(const FwdArgs& a, int rows, hipStream_t s) {
     // 8 waves per workgroup either way: 32 rows per wave for large units, 16 below (more
     // workgroups, fewer registers)
     if (rows == 256) {
-        hipLaunchKernelGGL((fwd_prefill_kernel<DT, OUT, 8, 2>), dim3(grid), dim3(512), 0, s, a);
+        hipLaunchKernelGGL((fwd_prefill_pp_kernel<DT, OUT>), dim3(grid), dim3(512), 0, s, a);
     } else {
         hipLaunchKernelGGL((fwd_prefill_kernel<DT, OUT, 8, 1>), dim3(grid), dim3(512), 0, s, a);
     }

@@ -548,20 +548,83 @@ struct HalfStage {
     static constexpr int v_bytes = 64 * kVPitch;
 };
 
-// MFMA item: QK^T of half page k and PV of half page k - 1, interleaved by 32-token chunk.
+#ifndef GBSA_PIPE_DEPTH
+#define GBSA_PIPE_DEPTH 4
+#endif
+
+// One LDS operand fragment of the MFMA item (b is used by the fp8 QK step only).
+struct Frag {
+    u32x4 a, b;
+};
+
+// MFMA item: QK^T of half page k and PV of half page k - 1 as one software-pipelined sequence
+// of steps. A step is one LDS fragment and the MFMAs that use it (a K fragment against every
+// query tile, or a V^T fragment against every P^T tile); the fragments of the next
+// GBSA_PIPE_DEPTH steps are in flight while a step's MFMAs issue. Per 32-token chunk c: the QK
+// steps of token tiles 2c, 2c + 1, then the PV steps of chunk c.
 template <int DT, int NQ, bool qk, bool pv>
 __device__ __forceinline__ void mfma_item(const unsigned char* ks, const unsigned char* vs,
                                           const QTile<NQ>& qt, f32x4 (&s)[4][NQ],
                                           const u32x4 (&p)[2][NQ], f32x4 (&o)[8][NQ], int lane) {
     constexpr int PT = (DT == kF16) ? kF16 : kBF16;
+    constexpr int KP = KLds<DT>::pitch;
+    constexpr int QS = qk ? ((DT == kFP8) ? 2 : 8) : 0;  // QK steps per chunk
+    constexpr int VS = pv ? 8 : 0;                       // PV steps per chunk
+    constexpr int PC = QS + VS, NS = 2 * PC, D = GBSA_PIPE_DEPTH;
     const int lrow = lane & 15, lgrp = lane >> 4;
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-        if constexpr (qk) {
-            qk_tile<DT, NQ>(ks, qt, (2 * c) * 16 + lrow, lgrp, s[2 * c]);
-            qk_tile<DT, NQ>(ks, qt, (2 * c + 1) * 16 + lrow, lgrp, s[2 * c + 1]);
+    const unsigned char* krow = ks + lrow * KP;
+    const unsigned char* vrow = vs + (lgrp * 4 + (lrow >> 2)) * kVPitch + (lane & 3) * 8;
+    const f32x4 zero = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+    auto load = [&](int st) {
+        Frag f;
+        const int c = st / PC, j = st % PC;
+        if (j < QS) {
+            if constexpr (DT == kFP8) {
+                const unsigned char* kr = krow + (2 * c + j) * 16 * KP + lgrp * 32;
+                f.a = *(const u32x4*)kr;
+                f.b = *(const u32x4*)(kr + 16);
+            } else {
+                const int tile = 2 * c + j / 4, kk = j % 4;
+                f.a = *(const u32x4*)(krow + tile * 16 * KP + (kk * 32 + lgrp * 8) * 2);
+            }
+        } else {
+            const int dt = j - QS;
+            const u32x2 v0 = lds_read_tr16(vrow + c * 32 * kVPitch + dt * 32);
+            const u32x2 v1 = lds_read_tr16(vrow + (c * 32 + 16) * kVPitch + dt * 32);
+            f.a = (u32x4){v0[0], v0[1], v1[0], v1[1]};
         }
-        if constexpr (pv) pv_chunk4<PT, NQ>(vs, c, p[c], lane, o);
+        return f;
+    };
+    auto compute = [&](int st, const Frag& f) {
+        const int c = st / PC, j = st % PC;
+        if (j < QS) {
+            if constexpr (DT == kFP8) {
+                const int tile = 2 * c + j;
+#pragma unroll
+                for (int nq = 0; nq < NQ; ++nq)
+                    s[tile][nq] = mfma_16x16x128_fp8(f.a, f.b, qt.q[nq][0], qt.q[nq][1], zero);
+            } else {
+                const int tile = 2 * c + j / 4, kk = j % 4;
+#pragma unroll
+                for (int nq = 0; nq < NQ; ++nq)
+                    s[tile][nq] = mfma_16x16x32<DT>(f.a, qt.q[nq][kk], kk == 0 ? zero : s[tile][nq]);
+            }
+        } else {
+            const int dt = j - QS;
+#pragma unroll
+            for (int nq = 0; nq < NQ; ++nq) o[dt][nq] = mfma_16x16x32<PT>(f.a, p[c][nq], o[dt][nq]);
+        }
+    };
+    Frag fr[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i)
+        if (i < NS) fr[i] = load(i);
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+        const Frag f = fr[st % D];
+        if (st + D < NS) fr[st % D] = load(st + D);
+        compute(st, f);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -724,30 +787,33 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp_kernel(FwdArgs a) {
                 f32x4 s[4][NQ];
                 u32x4 p[2][NQ];  // P^T of the last softmax item, as PV B operands
                 {  // K_0 by the whole workgroup before the first slot
-                    PageRegs<DT, 512, 64> pr;
-                    page_load<DT, 512, 64>(pr, half_src(kbase, 0), rs, tid);
-                    store_k<DT, 512, 64>(pr, kst, tid);
+                    PageRegs<DT, 512, 64> pr0;
+                    page_load<DT, 512, 64>(pr0, half_src(kbase, 0), rs, tid);
+                    store_k<DT, 512, 64>(pr0, kst, tid);
                 }
                 __syncthreads();
-                // group 1 starts one slot late; it spends that slot moving K_1 into LDS
-                if (grp == 1) {
-                    PageRegs<DT, 256, 64> pr;
-                    page_load<DT, 256, 64>(pr, half_src(kbase, 1), rs, tg);
-                    store_k<DT, 256, 64>(pr, kst + KB, tg);
+                // Each group's share of the KV stream is loaded one softmax item ahead of its
+                // store, so the load latency spans an MFMA and a softmax item. Softmax item k
+                // stores V_k (group 0) or K_{k+2} (group 1) into buffer k % 2. Past the end of
+                // the stream the index is clamped: group 1 then rewrites a K half that nobody
+                // reads again, and the last load is simply not stored.
+                auto move_half = [&](int k) { return min(grp == 0 ? k : k + 2, nh - 1); };
+                PageRegs<DT, 256, 64> pr;  // the group's next move, in flight
+                if (grp == 1) {            // group 1 starts one slot late: K_1 moves meanwhile
+                    PageRegs<DT, 256, 64> pr1;
+                    page_load<DT, 256, 64>(pr1, half_src(kbase, 1), rs, tg);
+                    page_load<DT, 256, 64>(pr, half_src(kbase, move_half(0)), rs, tg);
+                    store_k<DT, 256, 64>(pr1, kst + KB, tg);
                     __syncthreads();
+                } else {
+                    page_load<DT, 256, 64>(pr, half_src(vbase, move_half(0)), rs, tg);
                 }
-                // softmax item k + this group's share of the KV stream
+                // page-list entries for the next softmax item, read before its LDS stores are
+                // queued (a wait on the list read would otherwise also wait for the stores)
+                int jc_next = __builtin_amdgcn_readfirstlane(plist_jc[0]);
+                int mv_page = __builtin_amdgcn_readfirstlane(plist_page[move_half(1) >> 1]);
                 auto softmax_and_move = [&](int k) {
-                    const int jc = __builtin_amdgcn_readfirstlane(plist_jc[k >> 1]);
-                    // half page whose V (group 0) or K (group 1) moves now; past the end of the
-                    // stream group 1 repeats the last K half into a buffer nobody reads again
-                    const int kl = min((grp == 0) ? k : k + 2, nh - 1);
-                    PageRegs<DT, 256, 64> pr;
-                    page_load<DT, 256, 64>(pr, half_src(grp == 0 ? vbase : kbase, kl), rs, tg);
-                    __builtin_amdgcn_sched_barrier(0);
-                    softmax_item<DT, NQ>(a, s, p, colscale, trow, jc >> 2, k & 1, jc & 3, skv, off,
-                                         lane, mrun, lrun, o);
-                    __builtin_amdgcn_sched_barrier(0);
+                    const int jc = jc_next;
                     if constexpr (DT == kFP8) {  // V is widened to bf16 on its way into LDS
                         if (grp == 0)
                             store_v<DT, 256, 64>(pr, vst + (k & 1) * VB, tg);
@@ -756,7 +822,22 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp_kernel(FwdArgs a) {
                     } else {  // K and V rows have the same LDS pitch: one store for both groups
                         store_k<DT, 256, 64>(pr, grp == 0 ? vst + (k & 1) * VB : kst + (k & 1) * KB, tg);
                     }
+                    {
+                        const int q = move_half(k + 1);
+                        const unsigned char* src = (grp == 0 ? vbase : kbase) +
+                                                   (int64_t)mv_page * a.kv_stride * esz + head_off +
+                                                   (q & 1) * 64 * rs;
+                        page_load<DT, 256, 64>(pr, src, rs, tg);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    softmax_item<DT, NQ>(a, s, p, colscale, trow, jc >> 2, k & 1, jc & 3, skv, off,
+                                         lane, mrun, lrun, o);
+                    __builtin_amdgcn_sched_barrier(0);
+                    const int jn = plist_jc[min(k + 1, nh - 1) >> 1];
+                    const int pn = plist_page[move_half(k + 2) >> 1];
                     __syncthreads();
+                    jc_next = __builtin_amdgcn_readfirstlane(jn);
+                    mv_page = __builtin_amdgcn_readfirstlane(pn);
                 };
                 mfma_item<DT, NQ, true, false>(kst, vst, qt, s, p, o, lane);
                 __syncthreads();

@@ -32,11 +32,20 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    """sha256 over the HIP sources; counter summaries are valid only for the same sources."""
+# HIP sources each main kernel is compiled from (its own file plus the shared headers)
+KERNEL_SOURCES = {
+    "fwd_decode_kernel": ["fwd_decode.hip"],
+    "fwd_prefill_kernel": ["fwd_prefill.hip"],
+    "fwd_prefill_pp_kernel": ["fwd_prefill.hip"],
+}
+SHARED_SOURCES = ["device_common.hpp", "gbsa_internal.hpp", "split_merge.hpp"]
+
+
+def kernel_source_hash(kernel: str) -> str:
+    """sha256 over the sources of one kernel; its counter summary is valid only for them."""
     import hashlib
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
+    for name in sorted(KERNEL_SOURCES[kernel] + SHARED_SOURCES):
         with open(os.path.join(CSRC, name), "rb") as fh:
             h.update(name.encode() + b"\0" + fh.read())
     return h.hexdigest()
@@ -52,7 +61,7 @@ def measured_traffic(kernel: str, workload: str):
         if line.startswith("- ") and ":" in line:
             k, v = line[2:].split(":", 1)
             vals[k.strip()] = v.strip().strip("`")
-    if vals.get("source_sha256") != kernel_source_hash():
+    if kernel not in KERNEL_SOURCES or vals.get("source_sha256") != kernel_source_hash(kernel):
         return None
     try:
         return int(float(vals["hbm_bytes_per_launch"]))
@@ -272,8 +281,9 @@ def main(argv=None):
     gbs = alg_bytes / (ms_step * 1e-3) / 1e9
     tflops = alg_flops / (ms_step * 1e-3) / 1e12
     hbm_bound = a.config == 2
-    kernel = "fwd_decode_kernel" if p.block_x * p.num_heads_q // p.num_heads_kv <= 16 \
-        else "fwd_prefill_kernel"
+    rows = p.block_x * p.num_heads_q // p.num_heads_kv  # packed GQA rows per unit
+    kernel = ("fwd_decode_kernel" if rows <= 16 else
+              "fwd_prefill_pp_kernel" if rows > 256 else "fwd_prefill_kernel")
     traffic = measured_traffic(kernel, gi.CONFIG_NAMES[a.config])
     if hbm_bound:
         achieved = alg_bytes / (fwd_ms * 1e-3) / 1e9

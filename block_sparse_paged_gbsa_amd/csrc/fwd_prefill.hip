@@ -868,6 +868,238 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp_kernel(FwdArgs a) {
     }
 }
 
+
+// ---------------------------------------------------------------------------------------------
+// Units of 65-256 rows: 128-row subtiles, two-group ping-pong with the keys split.
+//
+// Both groups hold the same 128 query rows (4 waves x 32 rows). Group 0 takes the first half
+// (64 tokens) of every visible page, group 1 the second half, one barrier slot behind, with the
+// same MFMA / softmax item sequence as above. Global half page q = 2k + g is group g's item k;
+// in slot s the MFMA item reads K_s and V_{s-2}, which always sit in the LDS buffers of the
+// group that owns them (K and V buffer g for group g). Moves: group g's softmax item k brings
+// K of its next half page (2k + 2 + g) into its own K buffer; its MFMA item k brings V of the
+// half page the partner has just exponentiated (2k + g - 1) into the partner's V buffer. Each
+// buffer is rewritten one slot after its last reader. At the end the two groups' online-softmax
+// states of each row are merged through LDS (FA article, "three steps": partial results over
+// disjoint key sets combine exactly after rescaling to the common max).
+// ---------------------------------------------------------------------------------------------
+template <int DT, int OUT>
+__global__ __launch_bounds__(512, 1) void fwd_prefill_ks_kernel(FwdArgs a) {
+    constexpr int NQ = 2;
+    constexpr int R = 128;
+    constexpr int esz = (DT == kFP8) ? 1 : 2;
+    constexpr int KB = HalfStage<DT>::k_bytes, VB = HalfStage<DT>::v_bytes;
+    constexpr int kStateBytes = 4 * (64 * 64 * 4 + 64 * 16);  // group 1's O, m, l for the merge
+    constexpr int kLds = (2 * KB + 2 * VB > kStateBytes) ? 2 * KB + 2 * VB : kStateBytes;
+    // [K buffer 0][K buffer 1][V buffer 0][V buffer 1]; reused for the final merge
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kLds];
+    __shared__ int plist_page[256], plist_jc[256];
+    __shared__ int flag[2];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2;  // waves w and w + 4 share a SIMD and the same query rows
+    const int tg = tid & 255;
+    const int lin = xcd_remap(blockIdx.x, gridDim.x);
+    const int w = lin / a.nst, st = lin - (lin / a.nst) * a.nst;
+
+    if (!header_ok(a)) {
+        if (tid == 0) atomicOr(a.ws_status, 1);
+        return;
+    }
+    const Bound b0 = read_bound(a.meta, w), b1 = read_bound(a.meta, w + 1);
+    const int U = a.meta[3];
+    if (!bound_less(b0, b1) || b0.u >= U) return;
+    UnitIter it = locate_unit(a, b0.u);
+    if (it.b < 0) return;
+
+    const int rs = a.N2 * 128 * esz;
+    const unsigned char* kbase = (const unsigned char*)a.k;
+    const unsigned char* vbase = (const unsigned char*)a.v;
+    unsigned char* const kst = smem;
+    unsigned char* const vst = smem + 2 * KB;
+
+    for (int u = b0.u;; ++u) {
+        const int sa = (u == b0.u) ? b0.s : 0;
+        if (u >= U || u > b1.u || (u == b1.u && sa >= b1.s)) break;
+        const int g = it.qbase + it.gl;
+        int cnt = 0;
+        if (g < a.tqb) cnt = min(max(a.cnt[(int64_t)it.n2 * a.tqb + g], 0), a.topK);
+        const int se = (u == b1.u) ? b1.s : cnt;
+        const bool complete = (sa == 0) && (se == cnt);
+
+        const int t0 = it.gl * a.X;
+        const int rows_exist = min(a.X, it.storage - t0) * a.G;
+        const int row_base = st * R;
+        if (row_base < rows_exist) {
+            const int skv = a.skv[it.b];
+            const int off = skv - it.sq;
+            const int row0 = row_base + (wave & 3) * NQ * 16;
+            QTile<NQ> qt;
+            float colscale[NQ];
+            int trow[NQ];
+            bool rvalid[NQ];
+            load_q<DT, NQ>(a, it, t0, rows_exist, row0, lane, qt, colscale, trow, rvalid);
+            float mrun[NQ], lrun[NQ];
+            f32x4 o[8][NQ];
+#pragma unroll
+            for (int nq = 0; nq < NQ; ++nq) {
+                mrun[nq] = kNegInf;
+                lrun[nq] = 0.f;
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt) o[dt][nq] = (f32x4){0.f, 0.f, 0.f, 0.f};
+            }
+            const int t_lo = t0 + row_base / a.G;
+            const int t_hi = t0 + (min(row_base + R, rows_exist) - 1) / a.G;
+            const int32_t* sel = a.idx + ((int64_t)it.n2 * a.tqb + g) * a.topK;
+            const int32_t* ttab = a.table + (int64_t)it.b * a.maxb;
+            const int64_t head_off = (int64_t)it.n2 * 128 * esz;
+
+            if (wave == 0) {
+                int n = 0;
+                for (int c0 = sa; c0 < se; c0 += 64) {
+                    int jl = -1, pl = 0, cl = 0;
+                    if (c0 + lane < se) {
+                        jl = sel[c0 + lane];
+                        if (jl >= 0) {
+                            cl = block_class(a, (int64_t)jl * 128, skv, off, t_lo, t_hi);
+                            if (cl != 0) pl = ttab[jl];
+                        }
+                    }
+                    const uint64_t m = __ballot(cl != 0);
+                    if (cl != 0) {
+                        const int pos = n + __builtin_amdgcn_mbcnt_hi(
+                                                (uint32_t)(m >> 32),
+                                                __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+                        plist_page[pos] = pl;
+                        plist_jc[pos] = jl * 4 + cl;
+                    }
+                    n += __builtin_popcountll(m);
+                }
+                if (lane == 0) flag[1] = n;
+            }
+            __syncthreads();
+            const int n = __builtin_amdgcn_readfirstlane(flag[1]);  // items per group
+            const int nh = 2 * n;                                   // half pages
+
+            // address of half page q (K or V) of this head in HBM; q is clamped into the stream
+            auto half_src = [&](const unsigned char* base, int q) {
+                q = min(max(q, 0), nh - 1);
+                const int page = __builtin_amdgcn_readfirstlane(plist_page[q >> 1]);
+                return base + (int64_t)page * a.kv_stride * esz + head_off + (q & 1) * 64 * rs;
+            };
+            if (n > 0) {
+                f32x4 s[4][NQ];
+                u32x4 p[2][NQ];
+                {  // K_0 by the whole workgroup before the first slot
+                    PageRegs<DT, 512, 64> pr0;
+                    page_load<DT, 512, 64>(pr0, half_src(kbase, 0), rs, tid);
+                    store_k<DT, 512, 64>(pr0, kst, tid);
+                }
+                __syncthreads();
+                if (grp == 1) {  // group 1 starts one slot late: K_1 moves meanwhile
+                    PageRegs<DT, 256, 64> pr1;
+                    page_load<DT, 256, 64>(pr1, half_src(kbase, 1), rs, tg);
+                    store_k<DT, 256, 64>(pr1, kst + KB, tg);
+                    __syncthreads();
+                }
+                unsigned char* const my_k = kst + grp * KB;
+                unsigned char* const my_v = vst + grp * VB;
+                unsigned char* const other_v = vst + (grp ^ 1) * VB;
+                // V of the half page the partner has just exponentiated, into its V buffer
+                auto v_move_store = [&](const PageRegs<DT, 256, 64>& pr) {
+                    if constexpr (DT == kFP8)
+                        store_v<DT, 256, 64>(pr, other_v, tg);
+                    else
+                        store_k<DT, 256, 64>(pr, other_v, tg);  // same row pitch as K
+                };
+                auto softmax_and_move = [&](int k) {
+                    const int jc = __builtin_amdgcn_readfirstlane(plist_jc[k]);
+                    PageRegs<DT, 256, 64> pr;
+                    page_load<DT, 256, 64>(pr, half_src(kbase, 2 * k + 2 + grp), rs, tg);
+                    __builtin_amdgcn_sched_barrier(0);
+                    softmax_item<DT, NQ>(a, s, p, colscale, trow, jc >> 2, grp, jc & 3, skv, off,
+                                         lane, mrun, lrun, o);
+                    __builtin_amdgcn_sched_barrier(0);
+                    store_k<DT, 256, 64>(pr, my_k, tg);
+                    __syncthreads();
+                };
+                {
+                    PageRegs<DT, 256, 64> pr;
+                    page_load<DT, 256, 64>(pr, half_src(vbase, grp - 1), rs, tg);
+                    __builtin_amdgcn_sched_barrier(0);
+                    mfma_item<DT, NQ, true, false>(my_k, my_v, qt, s, p, o, lane);
+                    __builtin_amdgcn_sched_barrier(0);
+                    v_move_store(pr);
+                }
+                __syncthreads();
+                softmax_and_move(0);
+                for (int k = 1; k < n; ++k) {
+                    PageRegs<DT, 256, 64> pr;
+                    page_load<DT, 256, 64>(pr, half_src(vbase, 2 * k + grp - 1), rs, tg);
+                    __builtin_amdgcn_sched_barrier(0);
+                    mfma_item<DT, NQ, true, true>(my_k, my_v, qt, s, p, o, lane);
+                    __builtin_amdgcn_sched_barrier(0);
+                    v_move_store(pr);
+                    __syncthreads();
+                    softmax_and_move(k);
+                }
+                {
+                    PageRegs<DT, 256, 64> pr;
+                    page_load<DT, 256, 64>(pr, half_src(vbase, 2 * n + grp - 1), rs, tg);
+                    __builtin_amdgcn_sched_barrier(0);
+                    mfma_item<DT, NQ, false, true>(my_k, my_v, qt, s, p, o, lane);
+                    __builtin_amdgcn_sched_barrier(0);
+                    v_move_store(pr);
+                }
+                if (grp == 0) __syncthreads();
+            }
+            __syncthreads();  // stages are free: group 1 hands its row states to group 0
+
+            if (grp == 1) {
+                f32x4* so = (f32x4*)(smem + (wave - 4) * (64 * 64 * 4 + 64 * 16));
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+                    for (int nq = 0; nq < NQ; ++nq) so[(dt * NQ + nq) * 64 + lane] = o[dt][nq];
+                so[16 * 64 + lane] = (f32x4){mrun[0], mrun[1], lrun[0], lrun[1]};
+            }
+            __syncthreads();
+            if (grp == 0) {
+                const f32x4* so = (const f32x4*)(smem + wave * (64 * 64 * 4 + 64 * 16));
+                const f32x4 ml = so[16 * 64 + lane];
+                const float m1[NQ] = {ml[0], ml[1]}, l1[NQ] = {ml[2], ml[3]};
+                float a0[NQ], a1[NQ];
+#pragma unroll
+                for (int nq = 0; nq < NQ; ++nq) {
+                    const float m = fmaxf(mrun[nq], m1[nq]);
+                    a0[nq] = (m == kNegInf) ? 0.f : fast_exp2(mrun[nq] - m);
+                    a1[nq] = (m == kNegInf) ? 0.f : fast_exp2(m1[nq] - m);
+                    mrun[nq] = m;
+                    lrun[nq] = lrun[nq] * a0[nq] + l1[nq] * a1[nq];
+                }
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+                    for (int nq = 0; nq < NQ; ++nq)
+                        o[dt][nq] = o[dt][nq] * a0[nq] + so[(dt * NQ + nq) * 64 + lane] * a1[nq];
+                write_rows<DT, OUT, NQ>(a, it, complete, 2 * w + (sa > 0 ? 0 : 1), row0, lane, trow,
+                                        rvalid, mrun, lrun, o);
+            }
+            __syncthreads();  // LDS is reused by the next task
+            if (!complete) {
+                const int w_a = unit_starter(a.meta, w, u);
+                const int np = count_pieces(a.meta, w_a, u);
+                if (piece_arrive(a, w_a * a.nst + st, np, flag))
+                    merge_rows<OUT>(a, w_a, u, row_base, min(row_base + R, rows_exist), it.b,
+                                    it.n2, t0, it.row0, it.sq);
+                __syncthreads();
+            }
+        }
+        advance_unit(a, it);
+    }
+}
+
 template <int DT, int OUT>
 hipError_t launch_t(const FwdArgs& a, int rows, hipStream_t s) {
     const int grid = a.P * a.nst;
@@ -875,6 +1107,8 @@ hipError_t launch_t(const FwdArgs& a, int rows, hipStream_t s) {
     // workgroups, fewer registers)
     if (rows == 256) {
         hipLaunchKernelGGL((fwd_prefill_pp_kernel<DT, OUT>), dim3(grid), dim3(512), 0, s, a);
+    } else if (a.M > 64) {
+        hipLaunchKernelGGL((fwd_prefill_ks_kernel<DT, OUT>), dim3(grid), dim3(512), 0, s, a);
     } else {
         hipLaunchKernelGGL((fwd_prefill_kernel<DT, OUT, 8, 1>), dim3(grid), dim3(512), 0, s, a);
     }

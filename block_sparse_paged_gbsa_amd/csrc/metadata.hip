@@ -39,6 +39,34 @@ __device__ T block_exclusive_scan(T x, T* total, T* sh) {
     return prefix + inc - x;
 }
 
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves: shifts by 1, 2, 4, 8
+// within each row of 16 lanes, then lane 15 of each row into the next row and lane 31 into
+// the upper half (lanes whose source is outside the row receive 0).
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15, rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31, rows 2, 3
+    return x;
+}
+
+// Exclusive prefix sum over a 1024-thread workgroup (16 waves); sh holds 16 ints and must not
+// be reused by the caller before the next barrier. One barrier.
+__device__ __forceinline__ int block_exclusive_scan32(int x, int* total, int* sh) {
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int inc = wave_inclusive_scan(x);
+    if (lane == 63) sh[wid] = inc;
+    __syncthreads();
+    const int winc = wave_inclusive_scan(lane < 16 ? sh[lane] : 0);  // every wave, redundantly
+    const int before = wid > 0 ? __builtin_amdgcn_readlane(winc, wid - 1) : 0;
+    *total = __builtin_amdgcn_readlane(winc, 15);
+    return before + inc - x;
+}
+
 __device__ __forceinline__ int upper_bound_batch(const int* ubase, int B, int u) {
     // largest b with ubase[b] <= u (ubase is non-decreasing, ubase[0] = 0)
     int lo = 0, hi = B;  // invariant: ubase[lo] <= u, answer in [lo, hi)
@@ -165,9 +193,136 @@ __global__ __launch_bounds__(1024) void metadata_kernel(MetaArgs a) {
     }
 }
 
+
+// Same task split for problems whose tables fit in LDS (at most kFastMaxB sequences and
+// N2 * totalQBlocks clamped counts): every input is loaded at once, the unit costs are scanned
+// once (each thread owns a contiguous run of units), and each worker's boundary is found by a
+// binary search of its cost target in the unit prefix. Boundary w is the first cut position
+// whose consumed cost reaches floor(w * W / P), exactly as above.
+__global__ __launch_bounds__(1024) void metadata_fast_kernel(MetaArgs a) {
+    extern __shared__ int tabs[];  // qbase[B+1], ubase[B+1], counts[N2*tqb], pre[N2*tqb+1], sp[1024]
+    __shared__ int sh_a[16], sh_b[16], sh_c[16];
+    __shared__ int sh_split;
+    const int tid = threadIdx.x, nt = blockDim.x;
+    const int NC = a.N2 * a.tqb;
+    int* qbase = tabs;
+    int* ubase = tabs + a.B + 1;
+    int* counts = tabs + 2 * (a.B + 1);
+    int* pre = counts + NC;
+    int* sp = pre + NC + 1;
+
+    // all global reads are issued up front
+    // (all values below fit in 32 bits: at most N2 * tqb units, each costing at most topK + 1)
+    int nq = 0, nu = 0;
+    if (tid < a.B) {
+        const int64_t st = a.cu[tid + 1] - a.cu[tid];
+        int64_t sq = st;
+        if (a.squ != nullptr) sq = min((int64_t)max(a.squ[tid], 0), st);
+        nq = (int)((st + a.X - 1) / a.X);
+        nu = a.N2 * (int)((sq + a.X - 1) / a.X);
+    }
+    for (int i = tid; i < NC; i += nt) counts[i] = min(max(a.count[i], 0), a.topK);
+    if (tid == 0) sh_split = 0;
+    int tq, tu;
+    const int eq = block_exclusive_scan32(nq, &tq, sh_a);
+    const int eu = block_exclusive_scan32(nu, &tu, sh_b);
+    if (tid < a.B) {
+        qbase[tid] = eq;
+        ubase[tid] = eu;
+    }
+    if (tid == 0) {
+        qbase[a.B] = tq;
+        ubase[a.B] = tu;
+    }
+    __syncthreads();
+    const int U = tu;
+    const int P = a.P;
+
+    // unit costs (count + 1) and their exclusive prefix
+    const int R = (U + nt - 1) / nt;
+    const int u0 = min(tid * R, U), u1 = min(u0 + R, U);
+    int run = 0;
+    for (int u = u0; u < u1; ++u) {
+        const int b = upper_bound_batch(ubase, a.B, u);
+        const int nact = (ubase[b + 1] - ubase[b]) / a.N2;
+        const int local = u - ubase[b];
+        const int n2 = local / nact, g = qbase[b] + local % nact;
+        const int c = (g < a.tqb) ? counts[n2 * a.tqb + g] : 0;
+        pre[u] = c + 1;  // cost, replaced by the prefix below
+        run += c + 1;
+    }
+    int W;
+    int acc = block_exclusive_scan32(run, &W, sh_c);
+    for (int u = u0; u < u1; ++u) {
+        const int cost = pre[u];
+        pre[u] = acc;
+        acc += cost;
+    }
+    if (tid == 0) pre[U] = W;
+    __syncthreads();
+
+    // boundary of worker w: the unit whose cost range holds the target t = floor(w W / P)
+    if (tid < P) {
+        const int w = tid;
+        uint32_t word = 0;
+        int spu = -1;
+        if (U > 0) {
+            const int t = (int)(((long long)w * W) / P);
+            int lo = 0, hi = U;  // largest u with pre[u] <= t (pre[0] = 0 <= t < pre[U] = W)
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (pre[mid] <= t) lo = mid;
+                else hi = mid;
+            }
+            const int u = lo;
+            const int s = (int)(t - pre[u]);
+            const int nslots = max(pre[u + 1] - pre[u] - 1, 1);
+            if (s < nslots) {
+                word = ((uint32_t)u << kSlotBits) | (uint32_t)s;
+                if (s > 0) spu = u;
+            } else {
+                word = (uint32_t)(u + 1) << kSlotBits;
+            }
+        }
+        a.meta[kHeaderWords + w] = (int32_t)word;
+        sp[w] = spu;
+    }
+    for (int i = kHeaderWords + P + 1 + tid; i < kMetaWords; i += nt) a.meta[i] = 0;
+    __syncthreads();
+    // split units: distinct units holding a boundary strictly inside (consecutive in w)
+    if (tid < P && sp[tid] >= 0 && (tid == 0 || sp[tid - 1] != sp[tid])) atomicAdd(&sh_split, 1);
+    __syncthreads();
+    if (tid == 0) {
+        a.meta[kHeaderWords + P] = (int32_t)((uint32_t)U << kSlotBits);
+        a.meta[0] = (int32_t)kMagic;
+        a.meta[1] = kVersion;
+        a.meta[2] = P;
+        a.meta[3] = U;
+        a.meta[4] = W;  // the total fits in 32 bits here
+        a.meta[5] = 0;
+        a.meta[6] = sh_split;
+        for (int i = kCheckFirst; i <= kCheckLast; ++i) a.meta[i] = a.header[i];
+        for (int i = kCheckLast + 1; i < kHeaderWords; ++i) a.meta[i] = 0;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_metadata(const MetaArgs& a, hipStream_t s) {
+    const size_t lds_max = 160 * 1024;
+    // fast path: every table in LDS (the unit count is at most N2 * tqb)
+    const size_t nc = (size_t)a.N2 * (size_t)a.tqb;
+    const size_t fast_bytes = sizeof(int) * (2 * ((size_t)a.B + 1) + 2 * nc + 1 + 1024);
+    if (a.B <= 1024 && a.P <= 1024 && fast_bytes <= lds_max) {
+        if (fast_bytes > 64 * 1024) {
+            hipError_t e = hipFuncSetAttribute((const void*)metadata_fast_kernel,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               (int)fast_bytes);
+            if (e != hipSuccess) return e;
+        }
+        hipLaunchKernelGGL(metadata_fast_kernel, dim3(1), dim3(1024), fast_bytes, s, a);
+        return hipGetLastError();
+    }
     // per-sequence tables plus the cached counts (the unit count is at most N2 * tqb),
     // within 160 KiB of LDS
     const size_t tab_bytes = sizeof(int) * 2 * (size_t)(a.B + 1);

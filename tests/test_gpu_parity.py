@@ -88,6 +88,24 @@ def test_metadata_bit_exact_random(seed):
     np.testing.assert_array_equal(meta, _ref_meta(p, P))
 
 
+@pytest.mark.parametrize("case", ["many_sequences", "large_tables"])
+def test_metadata_bit_exact_beyond_lds(case):
+    """More than 1024 sequences, or N2 x q-block tables larger than LDS: the scheduler's chunked
+    path, which must give the same split word for word."""
+    if case == "many_sequences":
+        p = gi.random_problem(31, values=False, decode=True, batch=1500, num_heads_q=8,
+                              num_heads_kv=2, block_x=1, top_k=4, use_seqused_q=True)
+    else:
+        p = gi.random_problem(32, values=False, batch=12, max_len=4096, block_x=8,
+                              num_heads_q=16, num_heads_kv=16, top_k=6, use_seqused_q=True)
+    from block_sparse_paged_gbsa_amd import gbsa_num_workers
+    gp = GpuProblem(p)
+    for P in (1, 999, gbsa_num_workers(gpu_params(p))):
+        _log(f"[meta] {case} P={P}")
+        meta = gp.metadata(gpu_params(p, P)).cpu().numpy()
+        np.testing.assert_array_equal(meta, _ref_meta(p, P))
+
+
 # ---------------------------------------------------------------------------
 # small problems: every row
 # ---------------------------------------------------------------------------

@@ -144,6 +144,18 @@ CASES = [
          num_heads_kv=1, top_k=6, mask_mode=1),
     dict(seed=114, dtype="f16", batch=4, block_x=17, num_heads_q=2, num_heads_kv=2,
          top_k=4, mask_mode=1, return_lse=False),
+    # 256-row subtiles (row-split ping-pong): fp8, and f16 with a window and dual lengths
+    dict(seed=115, dtype="fp8", batch=1, max_len=600, block_x=128, num_heads_q=8,
+         num_heads_kv=2, top_k=5, mask_mode=1),
+    dict(seed=116, dtype="f16", batch=2, max_len=500, block_x=40, num_heads_q=16,
+         num_heads_kv=2, top_k=6, mask_mode=1, win_left=100, win_right=0, use_seqused_q=True),
+    # 128-row subtiles (key-split ping-pong): 65 and 96 rows, fp8 with f16 output, 2 x 128 rows
+    dict(seed=117, dtype="bf16", batch=2, max_len=400, block_x=65, num_heads_q=2,
+         num_heads_kv=2, top_k=5, mask_mode=0),
+    dict(seed=118, dtype="fp8", batch=2, max_len=500, block_x=96, num_heads_q=4,
+         num_heads_kv=4, top_k=4, mask_mode=1, out_dtype="f16"),
+    dict(seed=119, dtype="f16", batch=3, max_len=300, block_x=32, num_heads_q=8,
+         num_heads_kv=1, top_k=4, mask_mode=1, win_left=50, win_right=-1),
 ]
 
 

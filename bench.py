@@ -264,16 +264,18 @@ def main(argv=None):
     wall = time.perf_counter() - t0
     ms_step = e0.elapsed_time(e1) / a.steps
 
-    # the forward launch alone (main kernel + split-KV combine), events on its stream
-    fe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(a.steps)]
-    for i in range(a.steps):
-        fe[i][0].record(stream)
+    # the forward launch alone (main kernel with its fused split-KV combine): K launches back
+    # to back between two events on their stream, so the average is the kernel's duration
+    # without per-launch gaps
+    f0 = torch.cuda.Event(enable_timing=True)
+    f1 = torch.cuda.Event(enable_timing=True)
+    f0.record(stream)
+    for _ in range(a.steps):
         gbsa_forward(params, p.q, p.k, p.v, idx, cnt, meta, cu, squ, skv, table, qs, ks, vs,
                      None, out, lse, ws)
-        fe[i][1].record(stream)
+    f1.record(stream)
     torch.cuda.synchronize()
-    fwd_ms = float(np.mean([s.elapsed_time(e) for s, e in fe]))
+    fwd_ms = f0.elapsed_time(f1) / a.steps
     status = int(ws[:4].view(torch.int32)[0].item())
     assert status == 0, "metadata mismatch flagged by the kernels"
     log(f"[bench] step {ms_step:.4f} ms, forward {fwd_ms:.4f} ms, wall {wall:.3f} s")

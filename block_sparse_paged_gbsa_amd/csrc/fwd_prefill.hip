@@ -19,12 +19,12 @@
 namespace gbsa {
 namespace {
 
-constexpr int kVPitch = 288;  // bytes per V row in LDS (16-bit values, 256 + 32)
+constexpr int kVPitch = 304;  // bytes per V row in LDS (16-bit values, 256 + 48)
 
 template <int DT>
 struct KLds {
-    // bytes per K row in LDS (288 B measured fastest for the 16-row fragment reads)
-    static constexpr int pitch = (DT == kFP8) ? 144 : 288;
+    // bytes per K row in LDS (304 B measured fastest with the 32x32 tiles' 32-row reads)
+    static constexpr int pitch = (DT == kFP8) ? 144 : 304;
 };
 
 template <int DT>
@@ -681,6 +681,237 @@ __device__ __forceinline__ void softmax_item(const FwdArgs& a, f32x4 (&s)[4][NQ]
     for (int nq = 0; nq < NQ; ++nq) lrun[nq] = lrun[nq] * alpha[nq] + ls[nq];
 }
 
+
+// ---------------------------------------------------------------------------------------------
+// 32x32 MFMA tiles (v_mfma_f32_32x32x16_{bf16,f16}; fp8 QK^T: v_mfma_scale_f32_32x32x64_f8f6f4).
+// Half the instructions of the 16x16 forms for the same work, which leaves the partner wave of
+// a SIMD more VALU issue. Lane layouts (checked on the hardware): A (32 x K): lane l holds row
+// l % 32 and k slots (h = l / 32, j); B (K x 32): lane l holds column l % 32 and the same k
+// slots; C (32 x 32): lane l holds column l % 32, element i at row 8 (i / 4) + 4 h + i % 4.
+// With S^T = K Q^T a lane therefore holds, for its query row, keys 8 (i / 4) + 4 h + i % 4 of
+// each 32-key tile. PV contracts over keys in whatever order the lane's P values come: k slot
+// (h, j) of chunk c = 2 t + a is key 32 t + 16 a + 8 (j / 4) + 4 h + j % 4, and the V^T operand
+// is read with the transpose read in that same order.
+// ---------------------------------------------------------------------------------------------
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <int DT>
+__device__ __forceinline__ f32x16 mfma_32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+    if constexpr (DT == kF16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// e4m3 x e4m3, K = 64 per instruction: lane holds 32 consecutive head dims (h = l / 32).
+__device__ __forceinline__ f32x16 mfma_32x32x64_fp8(u32x4 a0, u32x4 a1, u32x4 b0, u32x4 b1,
+                                                    f32x16 c) {
+    const i32x8 a = (i32x8){(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                            (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+    const i32x8 b = (i32x8){(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
+                            (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// Query column of a wave (32 rows, one per lane pair l, l + 32) as B operands of S^T = K Q^T.
+//  16-bit: q[kk] holds head dims 16 kk + 8 h .. + 8.   fp8: q[2 ks + e] holds 64 ks + 32 h + 16 e .. + 16.
+struct QCol32 {
+    u32x4 q[8];
+};
+
+template <int DT>
+__device__ __forceinline__ void load_q32(const FwdArgs& a, const UnitIter& it, int t0,
+                                         int rows_exist, int row0, int lane, QCol32& qc,
+                                         float& colscale, int& trow, bool& rvalid) {
+    const int h2 = lane >> 5;
+    const int r = row0 + (lane & 31);
+    const bool exists = r < rows_exist;
+    const int t = t0 + (exists ? r / a.G : 0);
+    const int h = it.n2 * a.G + (exists ? r % a.G : 0);
+    trow = t;
+    rvalid = exists && t < it.sq;
+    float cs = a.scale_log2;
+    if constexpr (DT == kFP8) cs *= a.qs[h] * a.ks[it.n2];
+    colscale = cs;
+    const int64_t qoff = ((it.row0 + t) * a.N1 + h) * 128;
+    const u32x4 z = (u32x4){0, 0, 0, 0};
+    if constexpr (DT == kFP8) {
+        const uint8_t* qp = (const uint8_t*)a.q + qoff;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+                qc.q[2 * ks + e] = exists ? *(const u32x4*)(qp + 64 * ks + 32 * h2 + 16 * e) : z;
+#pragma unroll
+        for (int kk = 4; kk < 8; ++kk) qc.q[kk] = z;
+    } else {
+        const uint16_t* qp = (const uint16_t*)a.q + qoff;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) qc.q[kk] = exists ? *(const u32x4*)(qp + 16 * kk + 8 * h2) : z;
+    }
+}
+
+// MFMA item on 32x32 tiles: QK^T of a half page (two 32-key tiles) and PV of the previous one,
+// as a software-pipelined sequence of steps (one LDS fragment and the MFMA that uses it).
+template <int DT, bool qk, bool pv>
+__device__ __forceinline__ void mfma_item32(const unsigned char* ks, const unsigned char* vs,
+                                            const QCol32& qc, f32x16 (&s)[2],
+                                            const u32x4 (&p)[4], f32x16 (&o)[4], int lane) {
+    constexpr int PT = (DT == kF16) ? kF16 : kBF16;
+    constexpr int KP = KLds<DT>::pitch;
+    constexpr int QS = qk ? ((DT == kFP8) ? 2 : 8) : 0;  // QK steps per 32-key tile
+    constexpr int VS = pv ? 8 : 0;                       // PV steps per 32-key tile (2 chunks x 4 d)
+    constexpr int PC = QS + VS, NS = 2 * PC, D = GBSA_PIPE_DEPTH;
+    const int h2 = lane >> 5;
+    const unsigned char* krow = ks + (lane & 31) * KP;
+    // transpose-read address of this lane (row offset within a 4-row group, column block)
+    const unsigned char* vbase = vs + (4 * h2 + ((lane & 15) >> 2)) * kVPitch +
+                                 (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+    const f32x16 zero = {};
+
+    auto load = [&](int st) {
+        Frag f;
+        const int t = st / PC, j = st % PC;
+        if (j < QS) {
+            if constexpr (DT == kFP8) {
+                const unsigned char* kr = krow + t * 32 * KP + 64 * j + 32 * h2;
+                f.a = *(const u32x4*)kr;
+                f.b = *(const u32x4*)(kr + 16);
+            } else {
+                f.a = *(const u32x4*)(krow + t * 32 * KP + (16 * j + 8 * h2) * 2);
+            }
+        } else {
+            const int v = j - QS, a2 = v >> 2, dt = v & 3;  // chunk 2t + a2, d tile dt
+            const unsigned char* vr = vbase + (32 * t + 16 * a2) * kVPitch + dt * 64;
+            const u32x2 v0 = lds_read_tr16(vr);
+            const u32x2 v1 = lds_read_tr16(vr + 8 * kVPitch);
+            f.a = (u32x4){v0[0], v0[1], v1[0], v1[1]};
+        }
+        return f;
+    };
+    auto compute = [&](int st, const Frag& f) {
+        const int t = st / PC, j = st % PC;
+        if (j < QS) {
+            if constexpr (DT == kFP8)
+                s[t] = mfma_32x32x64_fp8(f.a, f.b, qc.q[2 * j], qc.q[2 * j + 1], j == 0 ? zero : s[t]);
+            else
+                s[t] = mfma_32x32x16<DT>(f.a, qc.q[j], j == 0 ? zero : s[t]);
+        } else {
+            const int v = j - QS, a2 = v >> 2, dt = v & 3;
+            o[dt] = mfma_32x32x16<PT>(f.a, p[2 * t + a2], o[dt]);
+        }
+    };
+    Frag fr[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i)
+        if (i < NS) fr[i] = load(i);
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+        const Frag f = fr[st % D];
+        if (st + D < NS) fr[st % D] = load(st + D);
+        compute(st, f);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// Softmax item on 32x32 tiles for half page `half` of block j (class cls): mask, lazy running
+// max (in-lane max over 32 keys, then the lane pair l, l ^ 32), rescale, P^T as PV B operands.
+template <int DT>
+__device__ __forceinline__ void softmax_item32(const FwdArgs& a, f32x16 (&s)[2], u32x4 (&p)[4],
+                                               float colscale, int trow, int j, int half, int cls,
+                                               int skv, int off, int lane, float& mrun,
+                                               float& lrun, f32x16 (&o)[4]) {
+    constexpr int PT = (DT == kF16) ? kF16 : kBF16;
+    const int h2 = lane >> 5;
+    if (cls == 2) {
+        int vlo, vhi;
+        key_range(a, (int64_t)j * 128, skv, (int64_t)trow + off, &vlo, &vhi);
+        // element (t, i) of this lane is key half * 64 + 32 t + 8 (i / 4) + 4 h + i % 4 of the page
+        const int lo = vlo - half * 64 - 4 * h2, hi = vhi - half * 64 - 4 * h2;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int c = 32 * t + 8 * (i / 4) + (i % 4);
+                const uint32_t out = (uint32_t)(((c - lo) | (hi - c)) >> 31);  // ~0 outside
+                // (bit_cast of a vector element reads element 0: go through a scalar copy)
+                const float x = s[t][i];
+                s[t][i] = __uint_as_float((__float_as_uint(x) & ~out) | (0xff800000u & out));
+            }
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[t][i]);
+    mx = pair_max(mx, true);
+    const float mnew = lazy_max(mrun, mx == kNegInf ? kNegInf : mx * colscale);
+    const float muse = (mnew == kNegInf) ? 0.f : mnew;
+    const float alpha = fast_exp2(mrun - muse);
+    mrun = mnew;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {  // skipped unless some running max moved
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+    }
+    float ls = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {  // chunk c = 2 t + a: elements 8 a .. 8 a + 7 of tile t
+        float pv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            pv[e] = fast_exp2(__builtin_fmaf(s[c >> 1][8 * (c & 1) + e], colscale, -muse));
+            ls += pv[e];
+        }
+        p[c] = (u32x4){pack2<PT>(pv[0], pv[1]), pack2<PT>(pv[2], pv[3]), pack2<PT>(pv[4], pv[5]),
+                       pack2<PT>(pv[6], pv[7])};
+    }
+    lrun = lrun * alpha + ls;
+}
+
+// Normalised O and LSE of a wave's 32 rows (lane pair l, l + 32 per row), or the split partial.
+template <int DT, int OUT>
+__device__ __forceinline__ void write_rows32(const FwdArgs& a, const UnitIter& it, bool complete,
+                                             int slot, int row0, int lane, int trow, bool rvalid,
+                                             float mrun, float lrun, const f32x16 (&o)[4]) {
+    const int h2 = lane >> 5;
+    const float ltot = pair_sum(lrun, true);
+    const int r = row0 + (lane & 31);
+    if (!rvalid) return;
+    const float vscale = (DT == kFP8) ? a.vs[it.n2] : 1.f;
+    if (complete) {
+        const float inv = ltot > 0.f ? vscale / ltot : 0.f;
+        const int h = it.n2 * a.G + r % a.G;
+        const int64_t orow = ((it.row0 + trow) * a.N1 + h);
+        uint16_t* op = (uint16_t*)a.out + orow * 128;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {  // elements 4 g .. 4 g + 3: head dims dt*32 + 8 g + 4 h ..
+                const int d = dt * 32 + 8 * g + 4 * h2;
+                *(u32x2*)(op + d) = (u32x2){pack2<OUT>(o[dt][4 * g] * inv, o[dt][4 * g + 1] * inv),
+                                            pack2<OUT>(o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv)};
+            }
+        if (a.return_lse && h2 == 0)
+            a.lse[orow] = ltot > 0.f ? (mrun + __log2f(ltot)) * kLn2 : kNegInf;
+    } else {
+        float* po = a.ws_o + ((int64_t)slot * a.M + r) * 128;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d = dt * 32 + 8 * g + 4 * h2;
+                *(f32x4*)(po + d) = (f32x4){o[dt][4 * g], o[dt][4 * g + 1], o[dt][4 * g + 2],
+                                            o[dt][4 * g + 3]} * vscale;
+            }
+        if (h2 == 0) {
+            a.ws_m[(int64_t)slot * a.M + r] = mrun;
+            a.ws_l[(int64_t)slot * a.M + r] = ltot;
+        }
+    }
+}
+
 template <int DT, int OUT>
 __global__ __launch_bounds__(512, 1) void fwd_prefill_pp_kernel(FwdArgs a) {
     constexpr int NQ = 2;
@@ -855,6 +1086,188 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp_kernel(FwdArgs a) {
 
             write_rows<DT, OUT, NQ>(a, it, complete, 2 * w + (sa > 0 ? 0 : 1), row0, lane, trow,
                                     rvalid, mrun, lrun, o);
+            if (!complete) {
+                const int w_a = unit_starter(a.meta, w, u);
+                const int np = count_pieces(a.meta, w_a, u);
+                if (piece_arrive(a, w_a * a.nst + st, np, flag))
+                    merge_rows<OUT>(a, w_a, u, row_base, min(row_base + R, rows_exist), it.b,
+                                    it.n2, t0, it.row0, it.sq);
+                __syncthreads();
+            }
+        }
+        advance_unit(a, it);
+    }
+}
+
+// 256-row units with 32x32 MFMA tiles: same two-group ping-pong schedule, page stream and LDS
+// stages as the kernel above; each wave's 32 query rows are one 32-column tile.
+template <int DT, int OUT>
+__global__ __launch_bounds__(512, 1) void fwd_prefill_pp32_kernel(FwdArgs a) {
+    constexpr int R = 256;
+    constexpr int esz = (DT == kFP8) ? 1 : 2;
+    constexpr int KB = HalfStage<DT>::k_bytes, VB = HalfStage<DT>::v_bytes;
+    // [K buffer 0][K buffer 1][V buffer 0][V buffer 1]
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * KB + 2 * VB];
+    __shared__ int plist_page[256], plist_jc[256];  // the task's visible pages, in order
+    __shared__ int flag[2];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2;  // waves w and w + 4 share a SIMD
+    const int tg = tid & 255;   // thread index within the group
+    const int lin = xcd_remap(blockIdx.x, gridDim.x);
+    const int w = lin / a.nst, st = lin - (lin / a.nst) * a.nst;
+
+    if (!header_ok(a)) {
+        if (tid == 0) atomicOr(a.ws_status, 1);
+        return;
+    }
+    const Bound b0 = read_bound(a.meta, w), b1 = read_bound(a.meta, w + 1);
+    const int U = a.meta[3];
+    if (!bound_less(b0, b1) || b0.u >= U) return;
+    UnitIter it = locate_unit(a, b0.u);
+    if (it.b < 0) return;
+
+    const int rs = a.N2 * 128 * esz;  // bytes between tokens of a page
+    const unsigned char* kbase = (const unsigned char*)a.k;
+    const unsigned char* vbase = (const unsigned char*)a.v;
+    unsigned char* const kst = smem;
+    unsigned char* const vst = smem + 2 * KB;
+
+    for (int u = b0.u;; ++u) {
+        const int sa = (u == b0.u) ? b0.s : 0;
+        if (u >= U || u > b1.u || (u == b1.u && sa >= b1.s)) break;
+        const int g = it.qbase + it.gl;
+        int cnt = 0;
+        if (g < a.tqb) cnt = min(max(a.cnt[(int64_t)it.n2 * a.tqb + g], 0), a.topK);
+        const int se = (u == b1.u) ? b1.s : cnt;
+        const bool complete = (sa == 0) && (se == cnt);
+
+        const int t0 = it.gl * a.X;
+        const int rows_exist = min(a.X, it.storage - t0) * a.G;
+        const int row_base = st * R;
+        if (row_base < rows_exist) {
+            const int skv = a.skv[it.b];
+            const int off = skv - it.sq;
+            const int row0 = row_base + wave * 32;
+            QCol32 qc;
+            float colscale, mrun = kNegInf, lrun = 0.f;
+            int trow;
+            bool rvalid;
+            load_q32<DT>(a, it, t0, rows_exist, row0, lane, qc, colscale, trow, rvalid);
+            f32x16 o[4];
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) o[dt] = (f32x16){};
+            const int t_lo = t0 + row_base / a.G;
+            const int t_hi = t0 + (min(row_base + R, rows_exist) - 1) / a.G;
+            const int32_t* sel = a.idx + ((int64_t)it.n2 * a.tqb + g) * a.topK;
+            const int32_t* ttab = a.table + (int64_t)it.b * a.maxb;
+            const int64_t head_off = (int64_t)it.n2 * 128 * esz;
+
+            // ---- visible pages of this task's selection range, compacted in order ---------
+            if (wave == 0) {
+                int n = 0;
+                for (int c0 = sa; c0 < se; c0 += 64) {
+                    int jl = -1, pl = 0, cl = 0;
+                    if (c0 + lane < se) {
+                        jl = sel[c0 + lane];
+                        if (jl >= 0) {
+                            cl = block_class(a, (int64_t)jl * 128, skv, off, t_lo, t_hi);
+                            if (cl != 0) pl = ttab[jl];
+                        }
+                    }
+                    const uint64_t m = __ballot(cl != 0);
+                    if (cl != 0) {
+                        const int pos = n + __builtin_amdgcn_mbcnt_hi(
+                                                (uint32_t)(m >> 32),
+                                                __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+                        plist_page[pos] = pl;
+                        plist_jc[pos] = jl * 4 + cl;
+                    }
+                    n += __builtin_popcountll(m);
+                }
+                if (lane == 0) flag[1] = n;
+            }
+            __syncthreads();
+            const int nh = 2 * __builtin_amdgcn_readfirstlane(flag[1]);  // half pages
+
+            // address of half page q (K or V) of this head in HBM
+            auto half_src = [&](const unsigned char* base, int q) {
+                const int page = __builtin_amdgcn_readfirstlane(plist_page[q >> 1]);
+                return base + (int64_t)page * a.kv_stride * esz + head_off + (q & 1) * 64 * rs;
+            };
+            if (nh > 0) {
+                f32x16 s[2];
+                u32x4 p[4];  // P^T of the last softmax item, as PV B operands
+                {  // K_0 by the whole workgroup before the first slot
+                    PageRegs<DT, 512, 64> pr0;
+                    page_load<DT, 512, 64>(pr0, half_src(kbase, 0), rs, tid);
+                    store_k<DT, 512, 64>(pr0, kst, tid);
+                }
+                __syncthreads();
+                // Each group's share of the KV stream is loaded one softmax item ahead of its
+                // store, so the load latency spans an MFMA and a softmax item. Softmax item k
+                // stores V_k (group 0) or K_{k+2} (group 1) into buffer k % 2. Past the end of
+                // the stream the index is clamped: group 1 then rewrites a K half that nobody
+                // reads again, and the last load is simply not stored.
+                auto move_half = [&](int k) { return min(grp == 0 ? k : k + 2, nh - 1); };
+                PageRegs<DT, 256, 64> pr;  // the group's next move, in flight
+                if (grp == 1) {            // group 1 starts one slot late: K_1 moves meanwhile
+                    PageRegs<DT, 256, 64> pr1;
+                    page_load<DT, 256, 64>(pr1, half_src(kbase, 1), rs, tg);
+                    page_load<DT, 256, 64>(pr, half_src(kbase, move_half(0)), rs, tg);
+                    store_k<DT, 256, 64>(pr1, kst + KB, tg);
+                    __syncthreads();
+                } else {
+                    page_load<DT, 256, 64>(pr, half_src(vbase, move_half(0)), rs, tg);
+                }
+                // page-list entries for the next softmax item, read before its LDS stores are
+                // queued (a wait on the list read would otherwise also wait for the stores)
+                int jc_next = __builtin_amdgcn_readfirstlane(plist_jc[0]);
+                int mv_page = __builtin_amdgcn_readfirstlane(plist_page[move_half(1) >> 1]);
+                auto softmax_and_move = [&](int k) {
+                    const int jc = jc_next;
+                    if constexpr (DT == kFP8) {  // V is widened to bf16 on its way into LDS
+                        if (grp == 0)
+                            store_v<DT, 256, 64>(pr, vst + (k & 1) * VB, tg);
+                        else
+                            store_k<DT, 256, 64>(pr, kst + (k & 1) * KB, tg);
+                    } else {  // K and V rows have the same LDS pitch: one store for both groups
+                        store_k<DT, 256, 64>(pr, grp == 0 ? vst + (k & 1) * VB : kst + (k & 1) * KB, tg);
+                    }
+                    {
+                        const int q = move_half(k + 1);
+                        const unsigned char* src = (grp == 0 ? vbase : kbase) +
+                                                   (int64_t)mv_page * a.kv_stride * esz + head_off +
+                                                   (q & 1) * 64 * rs;
+                        page_load<DT, 256, 64>(pr, src, rs, tg);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    softmax_item32<DT>(a, s, p, colscale, trow, jc >> 2, k & 1, jc & 3, skv, off,
+                                       lane, mrun, lrun, o);
+                    __builtin_amdgcn_sched_barrier(0);
+                    const int jn = plist_jc[min(k + 1, nh - 1) >> 1];
+                    const int pn = plist_page[move_half(k + 2) >> 1];
+                    __syncthreads();
+                    jc_next = __builtin_amdgcn_readfirstlane(jn);
+                    mv_page = __builtin_amdgcn_readfirstlane(pn);
+                };
+                mfma_item32<DT, true, false>(kst, vst, qc, s, p, o, lane);
+                __syncthreads();
+                softmax_and_move(0);
+                for (int k = 1; k < nh; ++k) {
+                    mfma_item32<DT, true, true>(kst + (k & 1) * KB, vst + ((k - 1) & 1) * VB, qc, s,
+                                                p, o, lane);
+                    __syncthreads();
+                    softmax_and_move(k);
+                }
+                mfma_item32<DT, false, true>(kst, vst + ((nh - 1) & 1) * VB, qc, s, p, o, lane);
+                if (grp == 0) __syncthreads();
+            }
+            __syncthreads();  // LDS (stages, page list) is reused by the next task
+
+            write_rows32<DT, OUT>(a, it, complete, 2 * w + (sa > 0 ? 0 : 1), row0, lane, trow, rvalid,
+                                  mrun, lrun, o);
             if (!complete) {
                 const int w_a = unit_starter(a.meta, w, u);
                 const int np = count_pieces(a.meta, w_a, u);
@@ -1106,7 +1519,7 @@ hipError_t launch_t(const FwdArgs& a, int rows, hipStream_t s) {
     // 8 waves per workgroup either way: 32 rows per wave for large units, 16 below (more
     // workgroups, fewer registers)
     if (rows == 256) {
-        hipLaunchKernelGGL((fwd_prefill_pp_kernel<DT, OUT>), dim3(grid), dim3(512), 0, s, a);
+        hipLaunchKernelGGL((fwd_prefill_pp32_kernel<DT, OUT>), dim3(grid), dim3(512), 0, s, a);
     } else if (a.M > 64) {
         hipLaunchKernelGGL((fwd_prefill_ks_kernel<DT, OUT>), dim3(grid), dim3(512), 0, s, a);
     } else {

@@ -36,7 +36,8 @@ def log(msg):
 KERNEL_SOURCES = {
     "fwd_decode_kernel": ["fwd_decode.hip"],
     "fwd_prefill_kernel": ["fwd_prefill.hip"],
-    "fwd_prefill_pp_kernel": ["fwd_prefill.hip"],
+    "fwd_prefill_pp32_kernel": ["fwd_prefill.hip"],
+    "fwd_prefill_ks32_kernel": ["fwd_prefill.hip"],
 }
 SHARED_SOURCES = ["device_common.hpp", "gbsa_internal.hpp", "split_merge.hpp"]
 
@@ -285,7 +286,8 @@ def main(argv=None):
     hbm_bound = a.config == 2
     rows = p.block_x * p.num_heads_q // p.num_heads_kv  # packed GQA rows per unit
     kernel = ("fwd_decode_kernel" if rows <= 16 else
-              "fwd_prefill_pp_kernel" if rows > 256 else "fwd_prefill_kernel")
+              "fwd_prefill_pp32_kernel" if rows > 256 else
+              "fwd_prefill_ks32_kernel" if rows > 64 else "fwd_prefill_kernel")
     traffic = measured_traffic(kernel, gi.CONFIG_NAMES[a.config])
     if hbm_bound:
         achieved = alg_bytes / (fwd_ms * 1e-3) / 1e9

@@ -1,4 +1,4 @@
-// Main kernel for units with many query rows (packed-GQA tile M = blockShapeX * G > 16).
+// Main kernels for units with many query rows (packed-GQA tile M = blockShapeX * G > 16).
 //
 // GenericBlockSparseAttention article (cf-1.com): "sparse attention mechanism" (only the
 // selected KV blocks take part in QK^T, softmax and PV), "implementation architecture"
@@ -6,14 +6,16 @@
 // article (ai6s.net), "three steps": blockwise loads, online softmax with rescale, blockwise
 // weighted sum, exact.
 //
-// One workgroup = (worker w, row subtile st) with NW waves; each wave keeps NQ 16-row query
-// tiles in registers. The selected KV pages of the task stream through a double-buffered LDS
-// stage: while the waves compute on page s, each thread's share of page s+1 is already in
-// flight into registers and is written to the other LDS buffer afterwards, so there is one
-// barrier per page. A page is processed as two 64-token halves (online-softmax update per
-// half). S^T = K Q^T on 16x16x32 MFMA (16x16x128 for fp8) leaves P^T in the B-operand layout
-// of O^T = V^T P^T; V^T is read with the gfx950 transpose read. Split units are merged in
-// kernel by the last arriving workgroup (split_merge.hpp).
+// One workgroup = (worker w, row subtile st) of 8 waves. Throughout, S^T = K Q^T is computed so
+// that the MFMA result is already P^T in the B-operand layout of O^T = V^T P^T, and V^T is read
+// with the gfx950 transpose read. Split units are merged in kernel by the last arriving
+// workgroup (split_merge.hpp). Three kernels by unit size:
+//  * fwd_prefill_pp32_kernel (more than 256 rows, 256-row subtiles) and
+//    fwd_prefill_ks32_kernel (65-256 rows, 128-row subtiles): two wave groups alternate MFMA and
+//    softmax items on the same SIMDs over half pages (schedules described with each), on 32x32
+//    MFMA tiles;
+//  * fwd_prefill_kernel (17-64 rows): all waves in phase, 16 rows each, whole pages through a
+//    double-buffered LDS stage with one barrier per page, 16x16 MFMA tiles.
 #include "split_merge.hpp"
 
 namespace gbsa {
@@ -207,24 +209,6 @@ __device__ __forceinline__ void pv_chunk(const unsigned char* vs, int kc, const 
 #pragma unroll
     for (int nq = 0; nq < NQ; ++nq) pb[nq] = (u32x4){pa[nq][0], pa[nq][1], pb2[nq][0], pb2[nq][1]};
     pv_chunk4<PT, NQ>(vs, kc, pb, lane, o);
-}
-
-// exp2 of one 16-token tile of S^T into half `h` (elements 2h, 2h + 1) of the PV B operand.
-template <int PT, int NQ>
-__device__ __forceinline__ void exp_tile4(const f32x4 (&s)[NQ], const float (&colscale)[NQ],
-                                          const float (&muse)[NQ], u32x4 (&pq)[NQ], int h,
-                                          float (&ls)[NQ]) {
-#pragma unroll
-    for (int nq = 0; nq < NQ; ++nq) {
-        float pv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            pv[i] = fast_exp2(__builtin_fmaf(s[nq][i], colscale[nq], -muse[nq]));
-            ls[nq] += pv[i];
-        }
-        pq[nq][2 * h] = pack2<PT>(pv[0], pv[1]);
-        pq[nq][2 * h + 1] = pack2<PT>(pv[2], pv[3]);
-    }
 }
 
 template <int NQ>
@@ -557,131 +541,6 @@ struct Frag {
     u32x4 a, b;
 };
 
-// MFMA item: QK^T of half page k and PV of half page k - 1 as one software-pipelined sequence
-// of steps. A step is one LDS fragment and the MFMAs that use it (a K fragment against every
-// query tile, or a V^T fragment against every P^T tile); the fragments of the next
-// GBSA_PIPE_DEPTH steps are in flight while a step's MFMAs issue. Per 32-token chunk c: the QK
-// steps of token tiles 2c, 2c + 1, then the PV steps of chunk c.
-template <int DT, int NQ, bool qk, bool pv>
-__device__ __forceinline__ void mfma_item(const unsigned char* ks, const unsigned char* vs,
-                                          const QTile<NQ>& qt, f32x4 (&s)[4][NQ],
-                                          const u32x4 (&p)[2][NQ], f32x4 (&o)[8][NQ], int lane) {
-    constexpr int PT = (DT == kF16) ? kF16 : kBF16;
-    constexpr int KP = KLds<DT>::pitch;
-    constexpr int QS = qk ? ((DT == kFP8) ? 2 : 8) : 0;  // QK steps per chunk
-    constexpr int VS = pv ? 8 : 0;                       // PV steps per chunk
-    constexpr int PC = QS + VS, NS = 2 * PC, D = GBSA_PIPE_DEPTH;
-    const int lrow = lane & 15, lgrp = lane >> 4;
-    const unsigned char* krow = ks + lrow * KP;
-    const unsigned char* vrow = vs + (lgrp * 4 + (lrow >> 2)) * kVPitch + (lane & 3) * 8;
-    const f32x4 zero = (f32x4){0.f, 0.f, 0.f, 0.f};
-
-    auto load = [&](int st) {
-        Frag f;
-        const int c = st / PC, j = st % PC;
-        if (j < QS) {
-            if constexpr (DT == kFP8) {
-                const unsigned char* kr = krow + (2 * c + j) * 16 * KP + lgrp * 32;
-                f.a = *(const u32x4*)kr;
-                f.b = *(const u32x4*)(kr + 16);
-            } else {
-                const int tile = 2 * c + j / 4, kk = j % 4;
-                f.a = *(const u32x4*)(krow + tile * 16 * KP + (kk * 32 + lgrp * 8) * 2);
-            }
-        } else {
-            const int dt = j - QS;
-            const u32x2 v0 = lds_read_tr16(vrow + c * 32 * kVPitch + dt * 32);
-            const u32x2 v1 = lds_read_tr16(vrow + (c * 32 + 16) * kVPitch + dt * 32);
-            f.a = (u32x4){v0[0], v0[1], v1[0], v1[1]};
-        }
-        return f;
-    };
-    auto compute = [&](int st, const Frag& f) {
-        const int c = st / PC, j = st % PC;
-        if (j < QS) {
-            if constexpr (DT == kFP8) {
-                const int tile = 2 * c + j;
-#pragma unroll
-                for (int nq = 0; nq < NQ; ++nq)
-                    s[tile][nq] = mfma_16x16x128_fp8(f.a, f.b, qt.q[nq][0], qt.q[nq][1], zero);
-            } else {
-                const int tile = 2 * c + j / 4, kk = j % 4;
-#pragma unroll
-                for (int nq = 0; nq < NQ; ++nq)
-                    s[tile][nq] = mfma_16x16x32<DT>(f.a, qt.q[nq][kk], kk == 0 ? zero : s[tile][nq]);
-            }
-        } else {
-            const int dt = j - QS;
-#pragma unroll
-            for (int nq = 0; nq < NQ; ++nq) o[dt][nq] = mfma_16x16x32<PT>(f.a, p[c][nq], o[dt][nq]);
-        }
-    };
-    Frag fr[D];
-#pragma unroll
-    for (int i = 0; i < D; ++i)
-        if (i < NS) fr[i] = load(i);
-#pragma unroll
-    for (int st = 0; st < NS; ++st) {
-        const Frag f = fr[st % D];
-        if (st + D < NS) fr[st % D] = load(st + D);
-        compute(st, f);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-}
-
-// Softmax item for half page `half` of block j (class cls): P = exp2(S * colscale - max)
-// with the online update. Masked keys are set to -inf by bit selection (no compare masks).
-template <int DT, int NQ>
-__device__ __forceinline__ void softmax_item(const FwdArgs& a, f32x4 (&s)[4][NQ],
-                                             u32x4 (&p)[2][NQ],
-                                             const float (&colscale)[NQ], const int (&trow)[NQ],
-                                             int j, int half, int cls, int skv, int off, int lane,
-                                             float (&mrun)[NQ], float (&lrun)[NQ],
-                                             f32x4 (&o)[8][NQ]) {
-    constexpr int PT = (DT == kF16) ? kF16 : kBF16;
-    const int lgrp = lane >> 4;
-    if (cls == 2) {
-#pragma unroll
-        for (int nq = 0; nq < NQ; ++nq) {
-            int vlo, vhi;
-            key_range(a, (int64_t)j * 128, skv, (int64_t)trow[nq] + off, &vlo, &vhi);
-            // element (tt, i) of this lane is key half * 64 + tt * 16 + lgrp * 4 + i of the page
-            const int lo = vlo - half * 64 - lgrp * 4, hi = vhi - half * 64 - lgrp * 4;
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int c = tt * 16 + i;
-                    const uint32_t out = (uint32_t)(((c - lo) | (hi - c)) >> 31);  // ~0 outside
-                    // (bit_cast of a vector element reads element 0: go through a scalar copy)
-                    const float x = s[tt][nq][i];
-                    s[tt][nq][i] = __uint_as_float((__float_as_uint(x) & ~out) | (0xff800000u & out));
-                }
-        }
-    }
-    float muse[NQ], alpha[NQ], ls[NQ];
-#pragma unroll
-    for (int nq = 0; nq < NQ; ++nq) {
-        float mx = kNegInf;
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[tt][nq][i]);
-        mx = wave_max_cols(mx);
-        const float mnew = lazy_max(mrun[nq], mx == kNegInf ? kNegInf : mx * colscale[nq]);
-        muse[nq] = (mnew == kNegInf) ? 0.f : mnew;
-        alpha[nq] = fast_exp2(mrun[nq] - muse[nq]);
-        mrun[nq] = mnew;
-        ls[nq] = 0.f;
-    }
-    rescale<NQ>(alpha, o);
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) exp_tile4<PT, NQ>(s[tt], colscale, muse, p[tt >> 1], tt & 1, ls);
-#pragma unroll
-    for (int nq = 0; nq < NQ; ++nq) lrun[nq] = lrun[nq] * alpha[nq] + ls[nq];
-}
-
-
 // ---------------------------------------------------------------------------------------------
 // 32x32 MFMA tiles (v_mfma_f32_32x32x16_{bf16,f16}; fp8 QK^T: v_mfma_scale_f32_32x32x64_f8f6f4).
 // Half the instructions of the 16x16 forms for the same work, which leaves the partner wave of
@@ -912,195 +771,9 @@ __device__ __forceinline__ void write_rows32(const FwdArgs& a, const UnitIter& i
     }
 }
 
-template <int DT, int OUT>
-__global__ __launch_bounds__(512, 1) void fwd_prefill_pp_kernel(FwdArgs a) {
-    constexpr int NQ = 2;
-    constexpr int R = 256;
-    constexpr int esz = (DT == kFP8) ? 1 : 2;
-    constexpr int KB = HalfStage<DT>::k_bytes, VB = HalfStage<DT>::v_bytes;
-    // [K buffer 0][K buffer 1][V buffer 0][V buffer 1]
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * KB + 2 * VB];
-    __shared__ int plist_page[256], plist_jc[256];  // the task's visible pages, in order
-    __shared__ int flag[2];
 
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int grp = wave >> 2;  // waves w and w + 4 share a SIMD
-    const int tg = tid & 255;   // thread index within the group
-    const int lin = xcd_remap(blockIdx.x, gridDim.x);
-    const int w = lin / a.nst, st = lin - (lin / a.nst) * a.nst;
-
-    if (!header_ok(a)) {
-        if (tid == 0) atomicOr(a.ws_status, 1);
-        return;
-    }
-    const Bound b0 = read_bound(a.meta, w), b1 = read_bound(a.meta, w + 1);
-    const int U = a.meta[3];
-    if (!bound_less(b0, b1) || b0.u >= U) return;
-    UnitIter it = locate_unit(a, b0.u);
-    if (it.b < 0) return;
-
-    const int rs = a.N2 * 128 * esz;  // bytes between tokens of a page
-    const unsigned char* kbase = (const unsigned char*)a.k;
-    const unsigned char* vbase = (const unsigned char*)a.v;
-    unsigned char* const kst = smem;
-    unsigned char* const vst = smem + 2 * KB;
-
-    for (int u = b0.u;; ++u) {
-        const int sa = (u == b0.u) ? b0.s : 0;
-        if (u >= U || u > b1.u || (u == b1.u && sa >= b1.s)) break;
-        const int g = it.qbase + it.gl;
-        int cnt = 0;
-        if (g < a.tqb) cnt = min(max(a.cnt[(int64_t)it.n2 * a.tqb + g], 0), a.topK);
-        const int se = (u == b1.u) ? b1.s : cnt;
-        const bool complete = (sa == 0) && (se == cnt);
-
-        const int t0 = it.gl * a.X;
-        const int rows_exist = min(a.X, it.storage - t0) * a.G;
-        const int row_base = st * R;
-        if (row_base < rows_exist) {
-            const int skv = a.skv[it.b];
-            const int off = skv - it.sq;
-            const int row0 = row_base + wave * NQ * 16;
-            QTile<NQ> qt;
-            float colscale[NQ];
-            int trow[NQ];
-            bool rvalid[NQ];
-            load_q<DT, NQ>(a, it, t0, rows_exist, row0, lane, qt, colscale, trow, rvalid);
-            float mrun[NQ], lrun[NQ];
-            f32x4 o[8][NQ];
-#pragma unroll
-            for (int nq = 0; nq < NQ; ++nq) {
-                mrun[nq] = kNegInf;
-                lrun[nq] = 0.f;
-#pragma unroll
-                for (int dt = 0; dt < 8; ++dt) o[dt][nq] = (f32x4){0.f, 0.f, 0.f, 0.f};
-            }
-            const int t_lo = t0 + row_base / a.G;
-            const int t_hi = t0 + (min(row_base + R, rows_exist) - 1) / a.G;
-            const int32_t* sel = a.idx + ((int64_t)it.n2 * a.tqb + g) * a.topK;
-            const int32_t* ttab = a.table + (int64_t)it.b * a.maxb;
-            const int64_t head_off = (int64_t)it.n2 * 128 * esz;
-
-            // ---- visible pages of this task's selection range, compacted in order ---------
-            if (wave == 0) {
-                int n = 0;
-                for (int c0 = sa; c0 < se; c0 += 64) {
-                    int jl = -1, pl = 0, cl = 0;
-                    if (c0 + lane < se) {
-                        jl = sel[c0 + lane];
-                        if (jl >= 0) {
-                            cl = block_class(a, (int64_t)jl * 128, skv, off, t_lo, t_hi);
-                            if (cl != 0) pl = ttab[jl];
-                        }
-                    }
-                    const uint64_t m = __ballot(cl != 0);
-                    if (cl != 0) {
-                        const int pos = n + __builtin_amdgcn_mbcnt_hi(
-                                                (uint32_t)(m >> 32),
-                                                __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-                        plist_page[pos] = pl;
-                        plist_jc[pos] = jl * 4 + cl;
-                    }
-                    n += __builtin_popcountll(m);
-                }
-                if (lane == 0) flag[1] = n;
-            }
-            __syncthreads();
-            const int nh = 2 * __builtin_amdgcn_readfirstlane(flag[1]);  // half pages
-
-            // address of half page q (K or V) of this head in HBM
-            auto half_src = [&](const unsigned char* base, int q) {
-                const int page = __builtin_amdgcn_readfirstlane(plist_page[q >> 1]);
-                return base + (int64_t)page * a.kv_stride * esz + head_off + (q & 1) * 64 * rs;
-            };
-            if (nh > 0) {
-                f32x4 s[4][NQ];
-                u32x4 p[2][NQ];  // P^T of the last softmax item, as PV B operands
-                {  // K_0 by the whole workgroup before the first slot
-                    PageRegs<DT, 512, 64> pr0;
-                    page_load<DT, 512, 64>(pr0, half_src(kbase, 0), rs, tid);
-                    store_k<DT, 512, 64>(pr0, kst, tid);
-                }
-                __syncthreads();
-                // Each group's share of the KV stream is loaded one softmax item ahead of its
-                // store, so the load latency spans an MFMA and a softmax item. Softmax item k
-                // stores V_k (group 0) or K_{k+2} (group 1) into buffer k % 2. Past the end of
-                // the stream the index is clamped: group 1 then rewrites a K half that nobody
-                // reads again, and the last load is simply not stored.
-                auto move_half = [&](int k) { return min(grp == 0 ? k : k + 2, nh - 1); };
-                PageRegs<DT, 256, 64> pr;  // the group's next move, in flight
-                if (grp == 1) {            // group 1 starts one slot late: K_1 moves meanwhile
-                    PageRegs<DT, 256, 64> pr1;
-                    page_load<DT, 256, 64>(pr1, half_src(kbase, 1), rs, tg);
-                    page_load<DT, 256, 64>(pr, half_src(kbase, move_half(0)), rs, tg);
-                    store_k<DT, 256, 64>(pr1, kst + KB, tg);
-                    __syncthreads();
-                } else {
-                    page_load<DT, 256, 64>(pr, half_src(vbase, move_half(0)), rs, tg);
-                }
-                // page-list entries for the next softmax item, read before its LDS stores are
-                // queued (a wait on the list read would otherwise also wait for the stores)
-                int jc_next = __builtin_amdgcn_readfirstlane(plist_jc[0]);
-                int mv_page = __builtin_amdgcn_readfirstlane(plist_page[move_half(1) >> 1]);
-                auto softmax_and_move = [&](int k) {
-                    const int jc = jc_next;
-                    if constexpr (DT == kFP8) {  // V is widened to bf16 on its way into LDS
-                        if (grp == 0)
-                            store_v<DT, 256, 64>(pr, vst + (k & 1) * VB, tg);
-                        else
-                            store_k<DT, 256, 64>(pr, kst + (k & 1) * KB, tg);
-                    } else {  // K and V rows have the same LDS pitch: one store for both groups
-                        store_k<DT, 256, 64>(pr, grp == 0 ? vst + (k & 1) * VB : kst + (k & 1) * KB, tg);
-                    }
-                    {
-                        const int q = move_half(k + 1);
-                        const unsigned char* src = (grp == 0 ? vbase : kbase) +
-                                                   (int64_t)mv_page * a.kv_stride * esz + head_off +
-                                                   (q & 1) * 64 * rs;
-                        page_load<DT, 256, 64>(pr, src, rs, tg);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                    softmax_item<DT, NQ>(a, s, p, colscale, trow, jc >> 2, k & 1, jc & 3, skv, off,
-                                         lane, mrun, lrun, o);
-                    __builtin_amdgcn_sched_barrier(0);
-                    const int jn = plist_jc[min(k + 1, nh - 1) >> 1];
-                    const int pn = plist_page[move_half(k + 2) >> 1];
-                    __syncthreads();
-                    jc_next = __builtin_amdgcn_readfirstlane(jn);
-                    mv_page = __builtin_amdgcn_readfirstlane(pn);
-                };
-                mfma_item<DT, NQ, true, false>(kst, vst, qt, s, p, o, lane);
-                __syncthreads();
-                softmax_and_move(0);
-                for (int k = 1; k < nh; ++k) {
-                    mfma_item<DT, NQ, true, true>(kst + (k & 1) * KB, vst + ((k - 1) & 1) * VB, qt, s,
-                                                  p, o, lane);
-                    __syncthreads();
-                    softmax_and_move(k);
-                }
-                mfma_item<DT, NQ, false, true>(kst, vst + ((nh - 1) & 1) * VB, qt, s, p, o, lane);
-                if (grp == 0) __syncthreads();
-            }
-            __syncthreads();  // LDS (stages, page list) is reused by the next task
-
-            write_rows<DT, OUT, NQ>(a, it, complete, 2 * w + (sa > 0 ? 0 : 1), row0, lane, trow,
-                                    rvalid, mrun, lrun, o);
-            if (!complete) {
-                const int w_a = unit_starter(a.meta, w, u);
-                const int np = count_pieces(a.meta, w_a, u);
-                if (piece_arrive(a, w_a * a.nst + st, np, flag))
-                    merge_rows<OUT>(a, w_a, u, row_base, min(row_base + R, rows_exist), it.b,
-                                    it.n2, t0, it.row0, it.sq);
-                __syncthreads();
-            }
-        }
-        advance_unit(a, it);
-    }
-}
-
-// 256-row units with 32x32 MFMA tiles: same two-group ping-pong schedule, page stream and LDS
-// stages as the kernel above; each wave's 32 query rows are one 32-column tile.
+// The 256-row kernel (schedule above) on 32x32 tiles: each wave's 32 query rows are one
+// 32-column tile.
 template <int DT, int OUT>
 __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32_kernel(FwdArgs a) {
     constexpr int R = 256;
@@ -1296,9 +969,10 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32_kernel(FwdArgs a) {
 // states of each row are merged through LDS (FA article, "three steps": partial results over
 // disjoint key sets combine exactly after rescaling to the common max).
 // ---------------------------------------------------------------------------------------------
+// The 128-row kernel (schedule above) on 32x32 tiles: each wave's 32 query rows are one
+// 32-column tile.
 template <int DT, int OUT>
-__global__ __launch_bounds__(512, 1) void fwd_prefill_ks_kernel(FwdArgs a) {
-    constexpr int NQ = 2;
+__global__ __launch_bounds__(512, 1) void fwd_prefill_ks32_kernel(FwdArgs a) {
     constexpr int R = 128;
     constexpr int esz = (DT == kFP8) ? 1 : 2;
     constexpr int KB = HalfStage<DT>::k_bytes, VB = HalfStage<DT>::v_bytes;
@@ -1347,21 +1021,15 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks_kernel(FwdArgs a) {
         if (row_base < rows_exist) {
             const int skv = a.skv[it.b];
             const int off = skv - it.sq;
-            const int row0 = row_base + (wave & 3) * NQ * 16;
-            QTile<NQ> qt;
-            float colscale[NQ];
-            int trow[NQ];
-            bool rvalid[NQ];
-            load_q<DT, NQ>(a, it, t0, rows_exist, row0, lane, qt, colscale, trow, rvalid);
-            float mrun[NQ], lrun[NQ];
-            f32x4 o[8][NQ];
+            const int row0 = row_base + (wave & 3) * 32;
+            QCol32 qc;
+            float colscale, mrun = kNegInf, lrun = 0.f;
+            int trow;
+            bool rvalid;
+            load_q32<DT>(a, it, t0, rows_exist, row0, lane, qc, colscale, trow, rvalid);
+            f32x16 o[4];
 #pragma unroll
-            for (int nq = 0; nq < NQ; ++nq) {
-                mrun[nq] = kNegInf;
-                lrun[nq] = 0.f;
-#pragma unroll
-                for (int dt = 0; dt < 8; ++dt) o[dt][nq] = (f32x4){0.f, 0.f, 0.f, 0.f};
-            }
+            for (int dt = 0; dt < 4; ++dt) o[dt] = (f32x16){};
             const int t_lo = t0 + row_base / a.G;
             const int t_hi = t0 + (min(row_base + R, rows_exist) - 1) / a.G;
             const int32_t* sel = a.idx + ((int64_t)it.n2 * a.tqb + g) * a.topK;
@@ -1402,8 +1070,8 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks_kernel(FwdArgs a) {
                 return base + (int64_t)page * a.kv_stride * esz + head_off + (q & 1) * 64 * rs;
             };
             if (n > 0) {
-                f32x4 s[4][NQ];
-                u32x4 p[2][NQ];
+                f32x16 s[2];
+                u32x4 p[4];
                 {  // K_0 by the whole workgroup before the first slot
                     PageRegs<DT, 512, 64> pr0;
                     page_load<DT, 512, 64>(pr0, half_src(kbase, 0), rs, tid);
@@ -1431,8 +1099,8 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks_kernel(FwdArgs a) {
                     PageRegs<DT, 256, 64> pr;
                     page_load<DT, 256, 64>(pr, half_src(kbase, 2 * k + 2 + grp), rs, tg);
                     __builtin_amdgcn_sched_barrier(0);
-                    softmax_item<DT, NQ>(a, s, p, colscale, trow, jc >> 2, grp, jc & 3, skv, off,
-                                         lane, mrun, lrun, o);
+                    softmax_item32<DT>(a, s, p, colscale, trow, jc >> 2, grp, jc & 3, skv, off, lane,
+                                       mrun, lrun, o);
                     __builtin_amdgcn_sched_barrier(0);
                     store_k<DT, 256, 64>(pr, my_k, tg);
                     __syncthreads();
@@ -1441,7 +1109,7 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks_kernel(FwdArgs a) {
                     PageRegs<DT, 256, 64> pr;
                     page_load<DT, 256, 64>(pr, half_src(vbase, grp - 1), rs, tg);
                     __builtin_amdgcn_sched_barrier(0);
-                    mfma_item<DT, NQ, true, false>(my_k, my_v, qt, s, p, o, lane);
+                    mfma_item32<DT, true, false>(my_k, my_v, qc, s, p, o, lane);
                     __builtin_amdgcn_sched_barrier(0);
                     v_move_store(pr);
                 }
@@ -1451,7 +1119,7 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks_kernel(FwdArgs a) {
                     PageRegs<DT, 256, 64> pr;
                     page_load<DT, 256, 64>(pr, half_src(vbase, 2 * k + grp - 1), rs, tg);
                     __builtin_amdgcn_sched_barrier(0);
-                    mfma_item<DT, NQ, true, true>(my_k, my_v, qt, s, p, o, lane);
+                    mfma_item32<DT, true, true>(my_k, my_v, qc, s, p, o, lane);
                     __builtin_amdgcn_sched_barrier(0);
                     v_move_store(pr);
                     __syncthreads();
@@ -1461,7 +1129,7 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks_kernel(FwdArgs a) {
                     PageRegs<DT, 256, 64> pr;
                     page_load<DT, 256, 64>(pr, half_src(vbase, 2 * n + grp - 1), rs, tg);
                     __builtin_amdgcn_sched_barrier(0);
-                    mfma_item<DT, NQ, false, true>(my_k, my_v, qt, s, p, o, lane);
+                    mfma_item32<DT, false, true>(my_k, my_v, qc, s, p, o, lane);
                     __builtin_amdgcn_sched_barrier(0);
                     v_move_store(pr);
                 }
@@ -1472,32 +1140,32 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks_kernel(FwdArgs a) {
             if (grp == 1) {
                 f32x4* so = (f32x4*)(smem + (wave - 4) * (64 * 64 * 4 + 64 * 16));
 #pragma unroll
-                for (int dt = 0; dt < 8; ++dt)
+                for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-                    for (int nq = 0; nq < NQ; ++nq) so[(dt * NQ + nq) * 64 + lane] = o[dt][nq];
-                so[16 * 64 + lane] = (f32x4){mrun[0], mrun[1], lrun[0], lrun[1]};
+                    for (int g4 = 0; g4 < 4; ++g4)
+                        so[(dt * 4 + g4) * 64 + lane] = (f32x4){o[dt][4 * g4], o[dt][4 * g4 + 1],
+                                                               o[dt][4 * g4 + 2], o[dt][4 * g4 + 3]};
+                so[16 * 64 + lane] = (f32x4){mrun, lrun, 0.f, 0.f};
             }
             __syncthreads();
             if (grp == 0) {
                 const f32x4* so = (const f32x4*)(smem + wave * (64 * 64 * 4 + 64 * 16));
                 const f32x4 ml = so[16 * 64 + lane];
-                const float m1[NQ] = {ml[0], ml[1]}, l1[NQ] = {ml[2], ml[3]};
-                float a0[NQ], a1[NQ];
+                const float m = fmaxf(mrun, ml[0]);
+                const float a0 = (m == kNegInf) ? 0.f : fast_exp2(mrun - m);
+                const float a1 = (m == kNegInf) ? 0.f : fast_exp2(ml[0] - m);
+                mrun = m;
+                lrun = lrun * a0 + ml[1] * a1;
 #pragma unroll
-                for (int nq = 0; nq < NQ; ++nq) {
-                    const float m = fmaxf(mrun[nq], m1[nq]);
-                    a0[nq] = (m == kNegInf) ? 0.f : fast_exp2(mrun[nq] - m);
-                    a1[nq] = (m == kNegInf) ? 0.f : fast_exp2(m1[nq] - m);
-                    mrun[nq] = m;
-                    lrun[nq] = lrun[nq] * a0[nq] + l1[nq] * a1[nq];
-                }
+                for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-                for (int dt = 0; dt < 8; ++dt)
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const f32x4 x = so[(dt * 4 + g4) * 64 + lane];
 #pragma unroll
-                    for (int nq = 0; nq < NQ; ++nq)
-                        o[dt][nq] = o[dt][nq] * a0[nq] + so[(dt * NQ + nq) * 64 + lane] * a1[nq];
-                write_rows<DT, OUT, NQ>(a, it, complete, 2 * w + (sa > 0 ? 0 : 1), row0, lane, trow,
-                                        rvalid, mrun, lrun, o);
+                        for (int e = 0; e < 4; ++e) o[dt][4 * g4 + e] = o[dt][4 * g4 + e] * a0 + x[e] * a1;
+                    }
+                write_rows32<DT, OUT>(a, it, complete, 2 * w + (sa > 0 ? 0 : 1), row0, lane, trow,
+                                      rvalid, mrun, lrun, o);
             }
             __syncthreads();  // LDS is reused by the next task
             if (!complete) {
@@ -1521,7 +1189,7 @@ hipError_t launch_t(const FwdArgs& a, int rows, hipStream_t s) {
     if (rows == 256) {
         hipLaunchKernelGGL((fwd_prefill_pp32_kernel<DT, OUT>), dim3(grid), dim3(512), 0, s, a);
     } else if (a.M > 64) {
-        hipLaunchKernelGGL((fwd_prefill_ks_kernel<DT, OUT>), dim3(grid), dim3(512), 0, s, a);
+        hipLaunchKernelGGL((fwd_prefill_ks32_kernel<DT, OUT>), dim3(grid), dim3(512), 0, s, a);
     } else {
         hipLaunchKernelGGL((fwd_prefill_kernel<DT, OUT, 8, 1>), dim3(grid), dim3(512), 0, s, a);
     }

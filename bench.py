@@ -101,7 +101,7 @@ def algorithmic_work(p, units=None):
     for b in range(p.batch):
         storage = int(p.cu_seqlens_q[b + 1] - p.cu_seqlens_q[b])
         sq = storage if p.seqused_q is None else min(int(p.seqused_q[b]), storage)
-        skv = int(p.seqused_kv[b])
+        skv = p.kv_len(b)
         gls = np.arange(-(-sq // p.block_x))
         if units is not None:
             gls = np.array([gl for gl in gls if (b, int(gl)) in units], dtype=np.int64)
@@ -119,7 +119,8 @@ def algorithmic_work(p, units=None):
         tok = (valid_tok * used).sum(axis=2)  # [N2, n]
         kv_bytes += int(tok.sum()) * 2 * D * es
         flops += int((tok * rows[None, :]).sum()) * 4 * D * G
-        meta_bytes += int(used.sum()) * 8 + cnt.size * 4  # idx + table entries, counts
+        # indices (+ page-table entries for paged key/value) and counts
+        meta_bytes += int(used.sum()) * (4 if p.kv_layout == "TND" else 8) + cnt.size * 4
     out_es = 2
     qo_bytes = q_rows * p.num_heads_q * D * (es + out_es)
     lse_bytes = q_rows * p.num_heads_q * 4 if p.return_lse else 0
@@ -144,7 +145,33 @@ def cpu_baseline(p, budget_s: float):
     rng = np.random.default_rng(7)
     rng.shuffle(units)
 
+    def host(t):
+        t = t.detach()
+        if p.dtype == "bf16":
+            return t.view(torch.int16).cpu().numpy().view(np.uint16)
+        if p.dtype == "fp8":
+            return t.view(torch.uint8).cpu().numpy()
+        return t.cpu().numpy()
+
+    def host_inputs_tnd(sample):
+        # the sampled sequences' rows only; every other sequence becomes an empty range
+        seqs = {b for (b, _) in sample}
+        cu = p.cu_seqlens_kv
+        new_cu = np.zeros(p.batch + 1, dtype=np.int64)
+        for b in range(p.batch):
+            new_cu[b + 1] = new_cu[b] + (int(cu[b + 1] - cu[b]) if b in seqs else 0)
+        sel = torch.cat([torch.arange(int(cu[b]), int(cu[b + 1]), device=p.k.device)
+                         for b in sorted(seqs)])
+        return oa.Inputs(host(p.q), host(p.k[sel]), host(p.v[sel]), p.sparse_block_idx,
+                         p.sparse_block_count, p.cu_seqlens_q, p.seqused_q, p.seqused_kv,
+                         None, dtype=p.dtype, block_x=p.block_x, scale=p.scale,
+                         mask_mode=p.mask_mode, win_left=p.win_left, win_right=p.win_right,
+                         q_scale=p.q_scale, k_scale=p.k_scale, v_scale=p.v_scale,
+                         cu_seqlens_kv=new_cu)
+
     def host_inputs(sample):
+        if p.kv_layout == "TND":
+            return host_inputs_tnd(sample)
         pages = set()
         for (b, gl) in sample:
             g = starts[b] + gl
@@ -157,14 +184,6 @@ def cpu_baseline(p, budget_s: float):
         remap = np.full(p.num_pages, -1, dtype=np.int64)
         remap[pages] = np.arange(len(pages))
         sel = torch.as_tensor(pages, dtype=torch.long, device=p.k.device)
-
-        def host(t):
-            t = t.detach()
-            if p.dtype == "bf16":
-                return t.view(torch.int16).cpu().numpy().view(np.uint16)
-            if p.dtype == "fp8":
-                return t.view(torch.uint8).cpu().numpy()
-            return t.cpu().numpy()
         table = np.where(p.block_table >= 0, remap[np.maximum(p.block_table, 0)], -1)
         return oa.Inputs(host(p.q), host(p.k[sel]), host(p.v[sel]), p.sparse_block_idx,
                          p.sparse_block_count, p.cu_seqlens_q, p.seqused_q, p.seqused_kv,
@@ -198,6 +217,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2, help="workload id 1..5 (default 2)")
+    ap.add_argument("--kv-layout", choices=["pa_bbnd", "tnd"], default="pa_bbnd",
+                    help="key/value layout: paged (default) or token-major TND")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -213,24 +234,34 @@ def main(argv=None):
     import torch
 
     import gbsa_inputs as gi
-    from block_sparse_paged_gbsa_amd import (gbsa_forward, gbsa_metadata, gbsa_num_workers,
-                                             gbsa_workspace_size, make_params)
+    from block_sparse_paged_gbsa_amd import (gbsa_forward, gbsa_forward_tnd, gbsa_metadata,
+                                             gbsa_num_workers, gbsa_workspace_size,
+                                             make_params)
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     log(f"[bench] generating workload {a.config} on the GPU")
     p = gi.config(a.config, device=dev)
+    tnd = a.kv_layout == "tnd"
+    if tnd:
+        log("[bench] rewriting key/value into the token-major TND layout")
+        p = gi.to_tnd(p)
+        torch.cuda.empty_cache()
     params = make_params(batch=p.batch, num_heads_q=p.num_heads_q, num_heads_kv=p.num_heads_kv,
                          total_q=p.total_q, total_q_blocks=p.total_q_blocks, top_k=p.top_k,
-                         block_x=p.block_x, max_blocks_per_seq=p.block_table.shape[1],
+                         block_x=p.block_x,
+                         max_blocks_per_seq=0 if tnd else p.block_table.shape[1],
                          num_pages=p.num_pages, kv_page_stride=p.kv_page_stride,
                          dtype=gi.TORCH_DTYPES[p.dtype], out_dtype=gi.TORCH_DTYPES[p.out_dtype],
                          mask_mode=p.mask_mode, win_left=p.win_left, win_right=p.win_right,
                          quant_mode=p.quant_mode, return_lse=p.return_lse,
-                         has_seqused_q=p.seqused_q is not None, scale=p.scale)
-    t = lambda x: torch.as_tensor(x).to(dev)
-    idx, cnt, cu, skv, table = (t(p.sparse_block_idx), t(p.sparse_block_count),
-                                t(p.cu_seqlens_q), t(p.seqused_kv), t(p.block_table))
+                         has_seqused_q=p.seqused_q is not None, scale=p.scale,
+                         kv_layout=1 if tnd else 0)
+    t = lambda x: None if x is None else torch.as_tensor(x).to(dev)
+    idx, cnt, cu, skv = (t(p.sparse_block_idx), t(p.sparse_block_count), t(p.cu_seqlens_q),
+                         t(p.seqused_kv))
+    table = None if tnd else t(p.block_table)
+    cu_kv = t(p.cu_seqlens_kv) if tnd else None
     squ = None if p.seqused_q is None else t(p.seqused_q)
     f32 = lambda s: None if s is None else torch.as_tensor(s, dtype=torch.float32).to(dev)
     qs, ks, vs = f32(p.q_scale), f32(p.k_scale), f32(p.v_scale)
@@ -240,10 +271,17 @@ def main(argv=None):
     ws = torch.zeros(gbsa_workspace_size(params), dtype=torch.uint8, device=dev)
     P = gbsa_num_workers(params)
 
+    def forward():
+        if tnd:
+            gbsa_forward_tnd(params, p.q, p.k, p.v, idx, cnt, meta, cu, squ, cu_kv, skv, qs,
+                             ks, vs, None, out, lse, ws)
+        else:
+            gbsa_forward(params, p.q, p.k, p.v, idx, cnt, meta, cu, squ, skv, table, qs, ks,
+                         vs, None, out, lse, ws)
+
     def step():
         gbsa_metadata(params, cnt, cu, squ, skv, meta)
-        gbsa_forward(params, p.q, p.k, p.v, idx, cnt, meta, cu, squ, skv, table, qs, ks, vs,
-                     None, out, lse, ws)
+        forward()
 
     alg_bytes, alg_flops = algorithmic_work(p)
     log(f"[bench] workers={P} algorithmic bytes={alg_bytes} flops={alg_flops}")
@@ -272,8 +310,7 @@ def main(argv=None):
     f1 = torch.cuda.Event(enable_timing=True)
     f0.record(stream)
     for _ in range(a.steps):
-        gbsa_forward(params, p.q, p.k, p.v, idx, cnt, meta, cu, squ, skv, table, qs, ks, vs,
-                     None, out, lse, ws)
+        forward()
     f1.record(stream)
     torch.cuda.synchronize()
     fwd_ms = f0.elapsed_time(f1) / a.steps
@@ -288,7 +325,8 @@ def main(argv=None):
     kernel = ("fwd_decode_kernel" if rows <= 16 else
               "fwd_prefill_pp32_kernel" if rows > 256 else
               "fwd_prefill_ks32_kernel" if rows > 64 else "fwd_prefill_kernel")
-    traffic = measured_traffic(kernel, gi.CONFIG_NAMES[a.config])
+    workload = gi.CONFIG_NAMES[a.config] + ("_tnd" if tnd else "")
+    traffic = measured_traffic(kernel, workload)
     if hbm_bound:
         achieved = alg_bytes / (fwd_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
@@ -314,10 +352,11 @@ def main(argv=None):
         "value": round(metric_value, 3), "unit": unit, "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": p.dtype, "data": "synthetic",
-        "config": {"workload": gi.CONFIG_NAMES[a.config], "batch": p.batch,
+        "config": {"workload": workload, "kv_layout": "TND" if tnd else "PA_BBND",
+                   "batch": p.batch,
                    "num_heads_q": p.num_heads_q, "num_heads_kv": p.num_heads_kv,
                    "head_dim": 128, "block_shape": [p.block_x, 128], "top_k": p.top_k,
-                   "kv_pages": p.num_pages, "workers": P},
+                   ("kv_rows" if tnd else "kv_pages"): p.num_pages, "workers": P},
         "effective_tflops": round(tflops, 3), "hbm_gbs": round(gbs, 2),
         "forward_ms": round(fwd_ms, 5), "kernel": kernel, "algorithmic_bytes": alg_bytes,
         "algorithmic_flops": alg_flops, "roofline": roof, "cpu_baseline": cpu,

@@ -8,6 +8,7 @@ from .api import (  # noqa: F401
     generic_block_sparse_attention_metadata,
     gbsa_check_params,
     gbsa_forward,
+    gbsa_forward_tnd,
     gbsa_metadata,
     gbsa_num_workers,
     gbsa_workspace_size,

@@ -25,9 +25,11 @@ STATUS = {
     7: "GBSA_ERR_METADATA", 8: "GBSA_ERR_HIP",
 }
 DTYPE_F16, DTYPE_BF16, DTYPE_FP8_E4M3 = 0, 1, 2
+KV_PA_BBND, KV_TND = 0, 1
+MAX_KV_ROWS = 2147483520
 
 EXPORTED = ("gbsa_check_params", "gbsa_num_workers", "gbsa_metadata", "gbsa_workspace_size",
-            "gbsa_forward", "gbsa_status_string")
+            "gbsa_forward", "gbsa_forward_tnd", "gbsa_status_string")
 
 
 class GbsaParams(ctypes.Structure):
@@ -57,7 +59,8 @@ class GbsaParams(ctypes.Structure):
         ("has_seqused_q", ctypes.c_int32),
         ("scale", ctypes.c_float),
         ("num_workers", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 4),
+        ("kv_layout", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 3),
     ]
 
 
@@ -91,6 +94,8 @@ def load() -> ctypes.CDLL:
     lib.gbsa_metadata.restype = ctypes.c_int
     lib.gbsa_forward.argtypes = [P] + [vp] * 17 + [ctypes.c_size_t, vp]
     lib.gbsa_forward.restype = ctypes.c_int
+    lib.gbsa_forward_tnd.argtypes = [P] + [vp] * 17 + [ctypes.c_size_t, vp]
+    lib.gbsa_forward_tnd.restype = ctypes.c_int
     lib.gbsa_status_string.argtypes = [ctypes.c_int]
     lib.gbsa_status_string.restype = ctypes.c_char_p
     _lib = lib

@@ -1,7 +1,8 @@
 """Torch-facing wrappers of the C ABI (device memory and streams come from PyTorch).
 
 Two layers:
-  * gbsa_metadata / gbsa_workspace_size / gbsa_forward / gbsa_num_workers / gbsa_check_params:
+  * gbsa_metadata / gbsa_workspace_size / gbsa_forward / gbsa_forward_tnd / gbsa_num_workers /
+    gbsa_check_params:
     the C entry points with the same names, taking a GbsaParams block and tensors;
   * generic_block_sparse_attention_metadata / generic_block_sparse_attention: the keyword
     interface of the GenericBlockSparseAttention article's PyTorch section (TND query,
@@ -48,7 +49,8 @@ def make_params(*, batch: int, num_heads_q: int, num_heads_kv: int, total_q: int
                 out_dtype=None, mask_mode: int = 1, win_left: int = -1, win_right: int = -1,
                 quant_mode: int = 0, softmax_precision: int = 1, return_lse: bool = False,
                 has_seqused_q: bool = False, scale: float = 0.0, num_workers: int = 0,
-                block_y: int = 128, head_dim: int = 128) -> GbsaParams:
+                block_y: int = 128, head_dim: int = 128, kv_layout: int = 0) -> GbsaParams:
+    """kv_layout 0 = PA_BBND (num_pages pages), 1 = TND (num_pages = rows of key/value)."""
     p = GbsaParams()
     p.batch = batch
     p.num_heads_q = num_heads_q
@@ -76,6 +78,7 @@ def make_params(*, batch: int, num_heads_q: int, num_heads_kv: int, total_q: int
     p.has_seqused_q = int(bool(has_seqused_q))
     p.scale = float(scale)
     p.num_workers = int(num_workers)
+    p.kv_layout = int(kv_layout)
     return p
 
 
@@ -102,11 +105,12 @@ def gbsa_workspace_size(params: GbsaParams) -> int:
 
 def gbsa_metadata(params: GbsaParams, sparse_block_count: torch.Tensor,
                   cu_seqlens_q: torch.Tensor, seqused_q: Optional[torch.Tensor],
-                  seqused_kv: torch.Tensor, metadata: Optional[torch.Tensor] = None,
+                  seqused_kv: Optional[torch.Tensor], metadata: Optional[torch.Tensor] = None,
                   stream=None) -> torch.Tensor:
     _need(sparse_block_count, "sparse_block_count", torch.int32)
     _need(cu_seqlens_q, "cu_seqlens_q", torch.int64)
-    _need(seqused_kv, "seqused_kv", torch.int32)
+    if seqused_kv is not None:
+        _need(seqused_kv, "seqused_kv", torch.int32)
     if seqused_q is not None:
         _need(seqused_q, "seqused_q", torch.int32)
     if metadata is None:
@@ -154,6 +158,39 @@ def gbsa_forward(params: GbsaParams, q, k, v, sparse_block_idx, sparse_block_cou
     return out, lse, workspace
 
 
+def gbsa_forward_tnd(params: GbsaParams, q, k, v, sparse_block_idx, sparse_block_count,
+                     metadata, cu_seqlens_q, seqused_q, cu_seqlens_kv, seqused_kv=None,
+                     q_scale=None, k_scale=None, v_scale=None, p_scale=None, out=None, lse=None,
+                     workspace=None, stream=None
+                     ) -> Tuple[torch.Tensor, Optional[torch.Tensor], torch.Tensor]:
+    """Token-major key/value [T_kv, N2, D]; returns (attention_out, softmax_lse or None,
+    workspace)."""
+    _need(q, "query")
+    _need(k, "key")
+    _need(v, "value")
+    if k.shape != v.shape or k.dim() != 3:
+        raise ValueError("key and value must both be [T_kv, N2, D]")
+    _need(sparse_block_idx, "sparse_block_idx", torch.int32)
+    _need(sparse_block_count, "sparse_block_count", torch.int32)
+    _need(cu_seqlens_kv, "cu_seqlens_kv", torch.int64)
+    if seqused_kv is not None:
+        _need(seqused_kv, "seqused_kv", torch.int32)
+    if out is None:
+        out = torch.empty(q.shape, dtype=_CODE_DTYPE[params.out_dtype], device=q.device)
+    if lse is None and params.return_lse:
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.zeros(gbsa_workspace_size(params), dtype=torch.uint8, device=q.device)
+    code = _lib.load().gbsa_forward_tnd(
+        ctypes.byref(params), _ptr(q), _ptr(k), _ptr(v), _ptr(sparse_block_idx),
+        _ptr(sparse_block_count), _ptr(metadata), _ptr(cu_seqlens_q), _ptr(seqused_q),
+        _ptr(cu_seqlens_kv), _ptr(seqused_kv), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale),
+        _ptr(p_scale), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+        _stream(stream))
+    check("gbsa_forward_tnd", code)
+    return out, lse, workspace
+
+
 def workspace_status(workspace: torch.Tensor) -> int:
     """Word 0 of the workspace: non-zero after a metadata/parameter mismatch (sticky)."""
     return int(workspace[:4].view(torch.int32)[0].item())
@@ -166,10 +203,12 @@ def workspace_status(workspace: torch.Tensor) -> int:
 def _common_params(sparse_block_idx, num_heads_q, num_heads_kv, head_dim, block_shape,
                    cu_seqlens_q, seqused_q, mask_mode, quant_mode, softmax_precision,
                    win_left, win_right, is_packed_gqa, layout_q, layout_kv, cu_seqlens_kv):
-    if layout_q != "TND" or layout_kv != "PA_BBND":
-        raise ValueError("only layout_q='TND' with layout_kv='PA_BBND' is supported")
-    if cu_seqlens_kv is not None:
+    if layout_q != "TND" or layout_kv not in ("PA_BBND", "TND"):
+        raise ValueError("layout_q must be 'TND' and layout_kv 'PA_BBND' or 'TND'")
+    if layout_kv == "PA_BBND" and cu_seqlens_kv is not None:
         raise ValueError("PA_BBND takes seqused_kv, not cu_seqlens_kv")
+    if layout_kv == "TND" and cu_seqlens_kv is None:
+        raise ValueError("layout_kv 'TND' requires cu_seqlens_kv")
     if not is_packed_gqa:
         raise ValueError("only is_packed_gqa=True is supported")
     if cu_seqlens_q is None:
@@ -180,7 +219,8 @@ def _common_params(sparse_block_idx, num_heads_q, num_heads_kv, head_dim, block_
                 total_q_blocks=sparse_block_idx.shape[1], top_k=sparse_block_idx.shape[2],
                 block_x=bx, block_y=by, mask_mode=int(mask_mode), win_left=int(win_left),
                 win_right=int(win_right), quant_mode=int(quant_mode),
-                softmax_precision=int(softmax_precision), has_seqused_q=seqused_q is not None)
+                softmax_precision=int(softmax_precision), has_seqused_q=seqused_q is not None,
+                kv_layout=_lib.KV_TND if layout_kv == "TND" else _lib.KV_PA_BBND)
 
 
 def generic_block_sparse_attention_metadata(
@@ -192,7 +232,7 @@ def generic_block_sparse_attention_metadata(
     c = _common_params(sparse_block_idx, num_heads_q, num_heads_kv, head_dim, block_shape,
                        cu_seqlens_q, seqused_q, mask_mode, quant_mode, softmax_precision,
                        win_left, win_right, is_packed_gqa, layout_q, layout_kv, cu_seqlens_kv)
-    if seqused_kv is None:
+    if seqused_kv is None and layout_kv == "PA_BBND":
         raise ValueError("seqused_kv is required with PA_BBND")
     dt = torch.float8_e4m3fn if int(quant_mode) == 5 else torch.float16
     # total_q, max_blocks_per_seq and num_pages do not enter the task split
@@ -201,7 +241,7 @@ def generic_block_sparse_attention_metadata(
                     num_workers=num_workers, **c)
     return gbsa_metadata(p, sparse_block_count.contiguous(), cu_seqlens_q.contiguous(),
                          None if seqused_q is None else seqused_q.contiguous(),
-                         seqused_kv.contiguous())
+                         None if seqused_kv is None else seqused_kv.contiguous())
 
 
 def generic_block_sparse_attention(
@@ -219,9 +259,13 @@ def generic_block_sparse_attention(
         raise ValueError("dst_type_max must be 0.0")
     if metadata is None:
         raise ValueError("metadata from generic_block_sparse_attention_metadata is required")
-    if block_table is None or seqused_kv is None:
+    tnd = layout_kv == "TND"
+    if not tnd and (block_table is None or seqused_kv is None):
         raise ValueError("PA_BBND requires block_table and seqused_kv")
-    c = _common_params(sparse_block_idx, q.shape[1], k.shape[2], q.shape[2], block_shape,
+    if tnd and block_table is not None:
+        raise ValueError("layout_kv 'TND' takes cu_seqlens_kv, not block_table")
+    c = _common_params(sparse_block_idx, q.shape[1], k.shape[1 if tnd else 2], q.shape[2],
+                       block_shape,
                        cu_seqlens_q, seqused_q, mask_mode, quant_mode, softmax_precision,
                        win_left, win_right, is_packed_gqa, layout_q, layout_kv, cu_seqlens_kv)
     if int(quant_mode) == 0:
@@ -230,16 +274,26 @@ def generic_block_sparse_attention(
         if attention_out_dtype is None:
             raise ValueError("attention_out_dtype is required when quant_mode != 0")
         out_dtype = attention_out_dtype
-    p = make_params(total_q=q.shape[0], max_blocks_per_seq=block_table.shape[1],
-                    num_pages=k.shape[0], kv_page_stride=k.stride(0), dtype=q.dtype,
-                    out_dtype=out_dtype, return_lse=return_softmax_lse,
-                    scale=float(softmax_scale), num_workers=num_workers, **c)
-    out, lse, _ = gbsa_forward(
-        p, q.contiguous(), k, v, sparse_block_idx.contiguous(), sparse_block_count.contiguous(),
-        metadata, cu_seqlens_q.contiguous(),
-        None if seqused_q is None else seqused_q.contiguous(), seqused_kv.contiguous(),
-        block_table.contiguous(), q_dequant_scale, k_dequant_scale, v_dequant_scale,
-        p_quant_scale)
+    squ = None if seqused_q is None else seqused_q.contiguous()
+    if tnd:
+        p = make_params(total_q=q.shape[0], max_blocks_per_seq=0, num_pages=k.shape[0],
+                        dtype=q.dtype, out_dtype=out_dtype, return_lse=return_softmax_lse,
+                        scale=float(softmax_scale), num_workers=num_workers, **c)
+        out, lse, _ = gbsa_forward_tnd(
+            p, q.contiguous(), k.contiguous(), v.contiguous(), sparse_block_idx.contiguous(),
+            sparse_block_count.contiguous(), metadata, cu_seqlens_q.contiguous(), squ,
+            cu_seqlens_kv.contiguous(), None if seqused_kv is None else seqused_kv.contiguous(),
+            q_dequant_scale, k_dequant_scale, v_dequant_scale, p_quant_scale)
+    else:
+        p = make_params(total_q=q.shape[0], max_blocks_per_seq=block_table.shape[1],
+                        num_pages=k.shape[0], kv_page_stride=k.stride(0), dtype=q.dtype,
+                        out_dtype=out_dtype, return_lse=return_softmax_lse,
+                        scale=float(softmax_scale), num_workers=num_workers, **c)
+        out, lse, _ = gbsa_forward(
+            p, q.contiguous(), k, v, sparse_block_idx.contiguous(),
+            sparse_block_count.contiguous(), metadata, cu_seqlens_q.contiguous(), squ,
+            seqused_kv.contiguous(), block_table.contiguous(), q_dequant_scale,
+            k_dequant_scale, v_dequant_scale, p_quant_scale)
     if lse is None:
         lse = torch.empty(0, dtype=torch.float32, device=q.device)
     else:

@@ -79,6 +79,7 @@ void fill_fingerprint(const gbsa_params* p, int32_t* h) {
     h[18] = p->win_right;
     h[19] = p->has_seqused_q;
     h[20] = p->is_packed_gqa;
+    h[21] = p->kv_layout;
 }
 
 }  // namespace
@@ -87,9 +88,12 @@ extern "C" {
 
 gbsa_status gbsa_check_params(const gbsa_params* p) {
     if (p == nullptr) return GBSA_ERR_NULL;
+    if (p->kv_layout != GBSA_KV_PA_BBND && p->kv_layout != GBSA_KV_TND)
+        return GBSA_ERR_UNSUPPORTED;
+    const bool tnd = p->kv_layout == GBSA_KV_TND;
     if (p->batch == 0 || p->num_heads_q == 0 || p->num_heads_kv == 0 || p->head_dim == 0 ||
         p->total_q == 0 || p->total_q_blocks == 0 || p->top_k == 0 || p->block_x == 0 ||
-        p->max_blocks_per_seq == 0 || p->num_pages == 0)
+        (!tnd && p->max_blocks_per_seq == 0) || p->num_pages == 0)
         return GBSA_ERR_EMPTY;
     if (p->batch < 0 || p->num_heads_q < 0 || p->num_heads_kv < 0 || p->total_q < 0 ||
         p->total_q_blocks < 0 || p->top_k < 0 || p->block_x < 0 || p->max_blocks_per_seq < 0 ||
@@ -103,10 +107,14 @@ gbsa_status gbsa_check_params(const gbsa_params* p) {
     if (p->win_left < -1 || p->win_right < -1) return GBSA_ERR_SHAPE;
     if (p->num_workers < 0 || p->num_workers > GBSA_MAX_WORKERS) return GBSA_ERR_SHAPE;
     const int64_t page_elems = (int64_t)GBSA_PAGE_SIZE * p->num_heads_kv * p->head_dim;
-    if (p->kv_page_stride != 0 &&
-        (p->kv_page_stride < page_elems ||
-         p->kv_page_stride % ((int64_t)p->num_heads_kv * p->head_dim) != 0))
+    if (tnd) {
+        // rows are dense; the last block of a sequence must start at an int32 row
+        if (p->kv_page_stride != 0 || p->num_pages > GBSA_MAX_KV_ROWS) return GBSA_ERR_SHAPE;
+    } else if (p->kv_page_stride != 0 &&
+               (p->kv_page_stride < page_elems ||
+                p->kv_page_stride % ((int64_t)p->num_heads_kv * p->head_dim) != 0)) {
         return GBSA_ERR_SHAPE;
+    }
     if (p->batch > GBSA_MAX_BATCH) return GBSA_ERR_UNSUPPORTED;
     if ((int64_t)p->num_heads_kv * p->total_q_blocks >= kMaxUnits) return GBSA_ERR_UNSUPPORTED;
     if (p->dtype < GBSA_DTYPE_F16 || p->dtype > GBSA_DTYPE_FP8_E4M3) return GBSA_ERR_DTYPE;
@@ -125,7 +133,7 @@ gbsa_status gbsa_check_params(const gbsa_params* p) {
     if (p->is_packed_gqa != 1) return GBSA_ERR_UNSUPPORTED;
     if (p->has_seqused_q != 0 && p->has_seqused_q != 1) return GBSA_ERR_SHAPE;
     if (p->return_lse != 0 && p->return_lse != 1) return GBSA_ERR_SHAPE;
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 3; ++i)
         if (p->reserved[i] != 0) return GBSA_ERR_UNSUPPORTED;
     if (!(p->scale == p->scale)) return GBSA_ERR_SHAPE;  // NaN
     return GBSA_OK;
@@ -159,8 +167,9 @@ gbsa_status gbsa_metadata(const gbsa_params* p, const int32_t* sparse_block_coun
                           const int32_t* seqused_kv, int32_t* metadata, hipStream_t stream) {
     gbsa_status st = gbsa_check_params(p);
     if (st != GBSA_OK) return st;
-    if (sparse_block_count == nullptr || cu_seqlens_q == nullptr || seqused_kv == nullptr)
-        return GBSA_ERR_NULL;
+    if (sparse_block_count == nullptr || cu_seqlens_q == nullptr) return GBSA_ERR_NULL;
+    // "general constraints": PA_BBND requires seqused_kv; with TND it is optional
+    if (p->kv_layout == GBSA_KV_PA_BBND && seqused_kv == nullptr) return GBSA_ERR_NULL;
     if ((seqused_q != nullptr) != (p->has_seqused_q == 1)) return GBSA_ERR_NULL;
     if (metadata == nullptr) return GBSA_ERR_METADATA;
     int P = 0;
@@ -189,19 +198,22 @@ gbsa_status gbsa_metadata(const gbsa_params* p, const int32_t* sparse_block_coun
     return launch_metadata(a, stream) == hipSuccess ? GBSA_OK : GBSA_ERR_HIP;
 }
 
-gbsa_status gbsa_forward(const gbsa_params* p, const void* query, const void* key,
-                         const void* value, const int32_t* sparse_block_idx,
-                         const int32_t* sparse_block_count, const int32_t* metadata,
-                         const int64_t* cu_seqlens_q, const int32_t* seqused_q,
-                         const int32_t* seqused_kv, const int32_t* block_table,
-                         const float* q_scale, const float* k_scale, const float* v_scale,
-                         const float* p_scale, void* attention_out, float* softmax_lse,
-                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+static gbsa_status forward_impl(const gbsa_params* p, const void* query, const void* key,
+                                const void* value, const int32_t* sparse_block_idx,
+                                const int32_t* sparse_block_count, const int32_t* metadata,
+                                const int64_t* cu_seqlens_q, const int32_t* seqused_q,
+                                const int32_t* seqused_kv, const int32_t* block_table,
+                                const int64_t* cu_seqlens_kv, const float* q_scale,
+                                const float* k_scale, const float* v_scale, const float* p_scale,
+                                void* attention_out, float* softmax_lse, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
     gbsa_status st = gbsa_check_params(p);
     if (st != GBSA_OK) return st;
+    const bool tnd = p->kv_layout == GBSA_KV_TND;
     if (query == nullptr || key == nullptr || value == nullptr || sparse_block_idx == nullptr ||
-        sparse_block_count == nullptr || cu_seqlens_q == nullptr || seqused_kv == nullptr ||
-        block_table == nullptr || attention_out == nullptr)
+        sparse_block_count == nullptr || cu_seqlens_q == nullptr || attention_out == nullptr)
+        return GBSA_ERR_NULL;
+    if (tnd ? cu_seqlens_kv == nullptr : (seqused_kv == nullptr || block_table == nullptr))
         return GBSA_ERR_NULL;
     if ((seqused_q != nullptr) != (p->has_seqused_q == 1)) return GBSA_ERR_NULL;
     if ((softmax_lse != nullptr) != (p->return_lse == 1)) return GBSA_ERR_NULL;
@@ -230,7 +242,8 @@ gbsa_status gbsa_forward(const gbsa_params* p, const void* query, const void* ke
     a.cu = cu_seqlens_q;
     a.squ = seqused_q;
     a.skv = seqused_kv;
-    a.table = block_table;
+    a.table = tnd ? nullptr : block_table;
+    a.cu_kv = tnd ? cu_seqlens_kv : nullptr;
     a.qs = q_scale;
     a.ks = k_scale;
     a.vs = v_scale;
@@ -242,8 +255,13 @@ gbsa_status gbsa_forward(const gbsa_params* p, const void* query, const void* ke
     a.ws_o = (float*)(ws + L.o);
     a.ws_m = (float*)(ws + L.m);
     a.ws_l = (float*)(ws + L.l);
-    const int64_t page_elems = (int64_t)GBSA_PAGE_SIZE * p->num_heads_kv * p->head_dim;
-    a.kv_stride = p->kv_page_stride != 0 ? p->kv_page_stride : page_elems;
+    const int64_t row_elems = (int64_t)p->num_heads_kv * p->head_dim;
+    if (tnd) {
+        a.kv_stride = row_elems;  // a storage unit is one token row
+        a.kv_rows = p->num_pages;
+    } else {
+        a.kv_stride = p->kv_page_stride != 0 ? p->kv_page_stride : GBSA_PAGE_SIZE * row_elems;
+    }
     a.B = p->batch;
     a.N1 = p->num_heads_q;
     a.N2 = p->num_heads_kv;
@@ -274,13 +292,47 @@ gbsa_status gbsa_forward(const gbsa_params* p, const void* query, const void* ke
     return e == hipSuccess ? GBSA_OK : GBSA_ERR_HIP;
 }
 
+gbsa_status gbsa_forward(const gbsa_params* p, const void* query, const void* key,
+                         const void* value, const int32_t* sparse_block_idx,
+                         const int32_t* sparse_block_count, const int32_t* metadata,
+                         const int64_t* cu_seqlens_q, const int32_t* seqused_q,
+                         const int32_t* seqused_kv, const int32_t* block_table,
+                         const float* q_scale, const float* k_scale, const float* v_scale,
+                         const float* p_scale, void* attention_out, float* softmax_lse,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    gbsa_status st = gbsa_check_params(p);
+    if (st != GBSA_OK) return st;
+    if (p->kv_layout != GBSA_KV_PA_BBND) return GBSA_ERR_UNSUPPORTED;
+    return forward_impl(p, query, key, value, sparse_block_idx, sparse_block_count, metadata,
+                        cu_seqlens_q, seqused_q, seqused_kv, block_table, nullptr, q_scale,
+                        k_scale, v_scale, p_scale, attention_out, softmax_lse, workspace,
+                        workspace_bytes, stream);
+}
+
+gbsa_status gbsa_forward_tnd(const gbsa_params* p, const void* query, const void* key,
+                             const void* value, const int32_t* sparse_block_idx,
+                             const int32_t* sparse_block_count, const int32_t* metadata,
+                             const int64_t* cu_seqlens_q, const int32_t* seqused_q,
+                             const int64_t* cu_seqlens_kv, const int32_t* seqused_kv,
+                             const float* q_scale, const float* k_scale, const float* v_scale,
+                             const float* p_scale, void* attention_out, float* softmax_lse,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    gbsa_status st = gbsa_check_params(p);
+    if (st != GBSA_OK) return st;
+    if (p->kv_layout != GBSA_KV_TND) return GBSA_ERR_UNSUPPORTED;
+    return forward_impl(p, query, key, value, sparse_block_idx, sparse_block_count, metadata,
+                        cu_seqlens_q, seqused_q, seqused_kv, nullptr, cu_seqlens_kv, q_scale,
+                        k_scale, v_scale, p_scale, attention_out, softmax_lse, workspace,
+                        workspace_bytes, stream);
+}
+
 const char* gbsa_status_string(gbsa_status s) {
     switch (s) {
         case GBSA_OK: return "ok";
         case GBSA_ERR_NULL: return "a required pointer is NULL (or an optional one is inconsistent with its flag)";
         case GBSA_ERR_SHAPE: return "a dimension violates a constraint (D=128, page=blockShapeY=128, N1%N2==0, group<=128, topK<=256, strides)";
         case GBSA_ERR_DTYPE: return "unsupported or inconsistent data type or dequant scales";
-        case GBSA_ERR_UNSUPPORTED: return "attribute value not supported (mask/quant mode, packed GQA, batch or unit count limits)";
+        case GBSA_ERR_UNSUPPORTED: return "attribute value not supported (mask/quant mode, packed GQA, KV layout or entry point, batch or unit count limits)";
         case GBSA_ERR_EMPTY: return "a required tensor has an empty axis";
         case GBSA_ERR_WORKSPACE: return "workspace missing or smaller than gbsa_workspace_size";
         case GBSA_ERR_METADATA: return "metadata buffer missing";

@@ -120,10 +120,12 @@ __device__ __forceinline__ T load_nt(const T* p) {
 }
 
 // Buffer resource over a wave-uniform base: one VGPR offset per lane, per-instruction
-// constants in the scalar offset. Records limit 2^31-1 bytes from the base (gfx9 format word).
+// constants in the scalar offset. `records` bytes from the base are readable (at most
+// 2^31-1); a dword at or beyond it reads as zero without a memory access. The range check
+// counts the scalar offset too (checked on gfx950 hardware).
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff,
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int records = 0x7fffffff) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, records,
                                              0x00020000);
 }
 // kNT: non-temporal streaming hint (data read once).
@@ -134,6 +136,65 @@ __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, int voff, int soff) {
 }
 __device__ __forceinline__ u32x2 buf_load8(rsrc_t r, int voff, int soff) {
     return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+
+// ---------------------------------------------------------------------------
+// KV side of a sequence. Paged key/value (PA_BBND) locate logical block j through the
+// block table; token-major key/value (TND) hold block j at rows cu_kv[b] + 128 j onwards
+// (GenericBlockSparseAttention article, "general constraints": layoutKv TND takes
+// cu_seqlens_kv, with seqused_kv as the optional visible length). Both give a storage unit
+// whose byte address is unit * kv_stride * element size.
+// ---------------------------------------------------------------------------
+// The layout is fixed at compile time (kPaged, kTnd) or read from the arguments (kAnyLayout).
+enum KvLayout : int { kAnyLayout = 0, kPaged = 1, kTnd = 2 };
+template <int L>
+__device__ __forceinline__ bool is_tnd(const FwdArgs& a) {
+    return L == kAnyLayout ? a.cu_kv != nullptr : L == kTnd;
+}
+struct KvSeq {
+    const int32_t* table;  // block-table row of the sequence, or null (token-major)
+    int row0;              // token-major: first row of the sequence
+    int len;               // visible keys
+    template <int L = kAnyLayout>
+    __device__ __forceinline__ int unit(int j) const {
+        if constexpr (L == kPaged) return table[j];
+        if constexpr (L == kTnd) return row0 + 128 * j;
+        return table ? table[j] : row0 + 128 * j;
+    }
+};
+template <int L = kAnyLayout>
+__device__ __forceinline__ KvSeq kv_seq(const FwdArgs& a, int b) {
+    KvSeq s;
+    if (!is_tnd<L>(a)) {
+        s.table = a.table + (int64_t)b * a.maxb;
+        s.row0 = 0;
+        s.len = a.skv[b];
+    } else {
+        // the sequence's rows, kept inside the tensor whatever cu_kv holds
+        const int64_t c0 = min(max(a.cu_kv[b], (int64_t)0), a.kv_rows);
+        const int64_t c1 = min(max(a.cu_kv[b + 1], c0), a.kv_rows);
+        const int st = (int)(c1 - c0);
+        s.table = nullptr;
+        s.row0 = (int)c0;
+        s.len = a.skv != nullptr ? min(a.skv[b], st) : st;
+    }
+    return s;
+}
+// A load window `off` bytes into key or value whose first `nv` rows are visible keys (rows
+// are `rs` bytes apart). Its records end after those rows, so the rows past the visible
+// length read as zeros without a memory access: whatever they hold (stale or unset cache
+// memory, another sequence's keys) cannot reach the output through a zero softmax weight,
+// and a token-major block that runs past the tensor's last row never reads beyond it (the
+// visible length ends inside the tensor).
+__device__ __forceinline__ int kv_records(int rs, int nv) {
+    return (int)min((int64_t)max(nv, 0) * rs, (int64_t)0x7fffffff);
+}
+struct KvSrc {
+    const unsigned char* p;
+    int records;
+};
+__device__ __forceinline__ KvSrc kv_src(const void* base, int64_t off, int rs, int nv) {
+    return KvSrc{(const unsigned char*)base + off, kv_records(rs, nv)};
 }
 
 // ---------------------------------------------------------------------------

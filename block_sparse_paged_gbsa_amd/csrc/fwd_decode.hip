@@ -46,11 +46,10 @@ __device__ __forceinline__ int row_off(int rs, int lane, int esz) {
     return esz == 2 ? (lane >> 4) * rs + (lane & 15) * 16 : (lane >> 3) * rs + (lane & 7) * 16;
 }
 
-// kq / vq: wave-uniform base of this wave's 32-token quarter of the K / V page slice.
+// kq / vq: wave-uniform window of this wave's 32-token quarter of the K / V block slice.
 template <int DT>
-__device__ __forceinline__ void load_quarter(Quarter& qt, const unsigned char* kq,
-                                             const unsigned char* vq, int rs, int loff) {
-    const rsrc_t rk = make_rsrc(kq), rv = make_rsrc(vq);
+__device__ __forceinline__ void load_quarter(Quarter& qt, KvSrc kq, KvSrc vq, int rs, int loff) {
+    const rsrc_t rk = make_rsrc(kq.p, kq.records), rv = make_rsrc(vq.p, vq.records);
     if constexpr (DT == kFP8) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) qt.k[q] = buf_load16<kNT>(rk, loff, q * 8 * rs);
@@ -170,7 +169,7 @@ __device__ __forceinline__ void compute_quarter(const FwdArgs& a, const Quarter&
     wave_sync_lds();
 }
 
-template <int DT, int OUT>
+template <int DT, int OUT, int LAYOUT>
 __global__ __launch_bounds__(256, 2) void fwd_decode_kernel(FwdArgs a) {
     __shared__ __attribute__((aligned(16))) unsigned char smem[Lds<DT>::bytes];
     __shared__ int flag[1];
@@ -205,7 +204,8 @@ __global__ __launch_bounds__(256, 2) void fwd_decode_kernel(FwdArgs a) {
         const bool complete = (sa == 0) && (se == cnt);
         const int t0 = it.gl * a.X;
         const int rows_exist = min(a.X, it.storage - t0) * a.G;
-        const int skv = a.skv[it.b];
+        const KvSeq kv = kv_seq<LAYOUT>(a, it.b);
+        const int skv = kv.len;
         const int off = skv - it.sq;
 
         // Q as the B operand: column = query row (lane & 15), k = head dim.
@@ -239,25 +239,32 @@ __global__ __launch_bounds__(256, 2) void fwd_decode_kernel(FwdArgs a) {
         for (int dt = 0; dt < 8; ++dt) st.o[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
         const int32_t* sel = a.idx + ((int64_t)it.n2 * a.tqb + g) * a.topK;
-        const int32_t* trow = a.table + (int64_t)it.b * a.maxb;
         const int64_t qbyte = (int64_t)wave * 32 * rs;  // this wave's token quarter
         for (int c0 = sa; c0 < se; c0 += 64) {
             // slots c0 .. c0+63: lane l holds slot c0 + l
             const int n = min(64, se - c0);
-            int jl = -1, pl = 0, cl = 0;
+            // per slot: block index and class packed as j * 4 + class, its storage unit and
+            // the records of this wave's quarter window
+            int jcl = 0, pl = 0, rl = 0;
             if (lane < n) {
-                jl = sel[c0 + lane];
+                const int jl = sel[c0 + lane];
                 if (jl >= 0) {
-                    cl = block_class(a, (int64_t)jl * 128, skv, off, t_lo, t_hi);
-                    if (cl != 0) pl = trow[jl];
+                    const int cl = block_class(a, (int64_t)jl * 128, skv, off, t_lo, t_hi);
+                    if (cl != 0) {
+                        jcl = jl * 4 + cl;
+                        pl = kv.unit<LAYOUT>(jl);
+                        rl = kv_records(rs, skv - 128 * jl - 32 * wave);
+                    }
                 }
             }
-            uint64_t todo = __ballot(cl != 0);
+            uint64_t todo = __ballot(jcl != 0);
             if (todo == 0) continue;
             auto base_of = [&](int i, const void* p) {
-                const int page = __builtin_amdgcn_readlane(pl, i);
-                return (const unsigned char*)p +
-                       ((int64_t)page * a.kv_stride + (int64_t)it.n2 * 128) * esz + qbyte;
+                const int unit = __builtin_amdgcn_readlane(pl, i);
+                return KvSrc{(const unsigned char*)p +
+                                 ((int64_t)unit * a.kv_stride + (int64_t)it.n2 * 128) * esz +
+                                 qbyte,
+                             __builtin_amdgcn_readlane(rl, i)};
             };
             Quarter qa, qb;
             int ia = __builtin_ctzll(todo);
@@ -271,8 +278,8 @@ __global__ __launch_bounds__(256, 2) void fwd_decode_kernel(FwdArgs a) {
                     load_quarter<DT>(qb, base_of(ib, a.k), base_of(ib, a.v), rs, loff);
                 }
                 {
-                    const int j = __builtin_amdgcn_readlane(jl, ia);
-                    const int cls = __builtin_amdgcn_readlane(cl, ia);
+                    const int jc = __builtin_amdgcn_readlane(jcl, ia);
+                    const int j = jc >> 2, cls = jc & 3;
                     compute_quarter<DT>(a, qa, qf, q8, cs, (int64_t)j * 128 + wave * 32, cls, skv,
                                         dpos, stage, lane, st);
                 }
@@ -284,8 +291,8 @@ __global__ __launch_bounds__(256, 2) void fwd_decode_kernel(FwdArgs a) {
                     load_quarter<DT>(qa, base_of(ia, a.k), base_of(ia, a.v), rs, loff);
                 }
                 {
-                    const int j = __builtin_amdgcn_readlane(jl, ib);
-                    const int cls = __builtin_amdgcn_readlane(cl, ib);
+                    const int jc = __builtin_amdgcn_readlane(jcl, ib);
+                    const int j = jc >> 2, cls = jc & 3;
                     compute_quarter<DT>(a, qb, qf, q8, cs, (int64_t)j * 128 + wave * 32, cls, skv,
                                         dpos, stage, lane, st);
                 }
@@ -342,12 +349,15 @@ __global__ __launch_bounds__(256, 2) void fwd_decode_kernel(FwdArgs a) {
                     if (a.return_lse && d0 == 0)
                         a.lse[orow] = lsum > 0.f ? (mstar + __log2f(lsum)) * kLn2 : kNegInf;
                 } else {
-                    float* po = a.ws_o + ((int64_t)slot * a.M + c) * 128 + d0;
+                    // 32-bit unsigned indices (2P x 16 rows fit): the compiler cannot split
+                    // them into a per-lane 64-bit part and keep it live across the unit loop
+                    const uint32_t mi = (uint32_t)slot * (uint32_t)a.M + (uint32_t)c;
+                    float* po = a.ws_o + (mi * 128u + (uint32_t)d0);
                     *(f32x4*)po = (f32x4){acc[0], acc[1], acc[2], acc[3]} * vscale;
                     *(f32x4*)(po + 4) = (f32x4){acc[4], acc[5], acc[6], acc[7]} * vscale;
                     if (d0 == 0) {
-                        a.ws_m[(int64_t)slot * a.M + c] = mstar;
-                        a.ws_l[(int64_t)slot * a.M + c] = lsum;
+                        a.ws_m[mi] = mstar;
+                        a.ws_l[mi] = lsum;
                     }
                 }
             }
@@ -365,7 +375,11 @@ __global__ __launch_bounds__(256, 2) void fwd_decode_kernel(FwdArgs a) {
 
 template <int DT, int OUT>
 hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL((fwd_decode_kernel<DT, OUT>), dim3(a.P), dim3(256), 0, s, a);
+    // the layout is a template argument: a run-time one costs the paged path a spill
+    if (a.cu_kv != nullptr)
+        hipLaunchKernelGGL((fwd_decode_kernel<DT, OUT, kTnd>), dim3(a.P), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((fwd_decode_kernel<DT, OUT, kPaged>), dim3(a.P), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -43,9 +43,9 @@ struct PageRegs {
 };
 
 template <int DT, int NT, int ROWS>
-__device__ __forceinline__ void page_load(PageRegs<DT, NT, ROWS>& r, const unsigned char* page,
-                                          int rs, int tid) {
-    const rsrc_t rk = make_rsrc(page);
+__device__ __forceinline__ void page_load(PageRegs<DT, NT, ROWS>& r, KvSrc page, int rs,
+                                          int tid) {
+    const rsrc_t rk = make_rsrc(page.p, page.records);
     constexpr int lanes_per_row = (DT == kFP8) ? 8 : 16;
     constexpr int rows_per_pass = NT / lanes_per_row;
     const int voff = (tid / lanes_per_row) * rs + (tid % lanes_per_row) * 16;
@@ -378,7 +378,7 @@ __device__ __forceinline__ void write_rows(const FwdArgs& a, const UnitIter& it,
     }
 }
 
-template <int DT, int OUT, int NW, int NQ>
+template <int DT, int OUT, int NW, int NQ, int LAYOUT>
 __global__ __launch_bounds__(NW * 64, 1) void fwd_prefill_kernel(FwdArgs a) {
     constexpr int NT = NW * 64;
     constexpr int R = NW * NQ * 16;
@@ -417,7 +417,8 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_prefill_kernel(FwdArgs a) {
         const int rows_exist = min(a.X, it.storage - t0) * a.G;
         const int row_base = st * R;
         if (row_base < rows_exist) {
-            const int skv = a.skv[it.b];
+            const KvSeq kv = kv_seq<LAYOUT>(a, it.b);
+            const int skv = kv.len;
             const int off = skv - it.sq;
             QTile<NQ> qt;
             float colscale[NQ];
@@ -439,7 +440,6 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_prefill_kernel(FwdArgs a) {
             const int t_hi = t0 + (min(row_base + R, rows_exist) - 1) / a.G;
 
             const int32_t* sel = a.idx + ((int64_t)it.n2 * a.tqb + g) * a.topK;
-            const int32_t* ttab = a.table + (int64_t)it.b * a.maxb;
             const int64_t head_off = (int64_t)it.n2 * 128 * esz;
 
             // ---- stream the task's visible pages through the double-buffered stage ------
@@ -456,25 +456,26 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_prefill_kernel(FwdArgs a) {
                     jl = sel[c0 + lane];
                     if (jl >= 0) {
                         cl = block_class(a, (int64_t)jl * 128, skv, off, t_lo, t_hi);
-                        if (cl != 0) pl = ttab[jl];
+                        if (cl != 0) pl = kv.unit<LAYOUT>(jl);
                     }
                 }
                 uint64_t todo = __ballot(cl != 0);
                 while (todo) {
                     const int i = __builtin_ctzll(todo);
                     todo &= todo - 1;
-                    const int page = __builtin_amdgcn_readlane(pl, i);
-                    const int64_t pb = (int64_t)page * a.kv_stride * esz + head_off;
+                    const int unit = __builtin_amdgcn_readlane(pl, i);
+                    const int64_t pb = (int64_t)unit * a.kv_stride * esz + head_off;
+                    const int nv = skv - 128 * __builtin_amdgcn_readlane(jl, i);
                     // the first page goes straight into stage[buf]; later ones into the
                     // other buffer while stage[buf] is consumed
                     unsigned char* cur = smem + buf * PageStage<DT>::bytes;
                     unsigned char* dst = have_prev ? smem + (buf ^ 1) * PageStage<DT>::bytes : cur;
-                    page_load<DT, NT>(pr, (const unsigned char*)a.k + pb, rs, tid);
+                    page_load<DT, NT>(pr, kv_src(a.k, pb, rs, nv), rs, tid);
                     if (have_prev)
                         page_part_a<DT, NQ>(a, cur, qt, colscale, trow, prev_j, prev_cls, skv,
                                             off, lane, mrun, lrun, o, mid);
                     store_k<DT, NT>(pr, dst, tid);
-                    page_load<DT, NT>(pr, (const unsigned char*)a.v + pb, rs, tid);
+                    page_load<DT, NT>(pr, kv_src(a.v, pb, rs, nv), rs, tid);
                     if (have_prev) page_part_b<DT, NQ>(cur, colscale, lane, lrun, o, mid);
                     store_v<DT, NT>(pr, dst + PageStage<DT>::k_bytes, tid);
                     if (have_prev) buf ^= 1;
@@ -774,14 +775,15 @@ __device__ __forceinline__ void write_rows32(const FwdArgs& a, const UnitIter& i
 
 // The 256-row kernel (schedule above) on 32x32 tiles: each wave's 32 query rows are one
 // 32-column tile.
-template <int DT, int OUT>
+template <int DT, int OUT, int LAYOUT>
 __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32_kernel(FwdArgs a) {
     constexpr int R = 256;
     constexpr int esz = (DT == kFP8) ? 1 : 2;
     constexpr int KB = HalfStage<DT>::k_bytes, VB = HalfStage<DT>::v_bytes;
     // [K buffer 0][K buffer 1][V buffer 0][V buffer 1]
     __shared__ __attribute__((aligned(16))) unsigned char smem[2 * KB + 2 * VB];
-    __shared__ int plist_page[256], plist_jc[256];  // the task's visible pages, in order
+    // the task's visible blocks in order: (unit, j * 4 + class, records of half 0, of half 1)
+    __shared__ int4 plist[256];
     __shared__ int flag[2];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -820,7 +822,8 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32_kernel(FwdArgs a) {
         const int rows_exist = min(a.X, it.storage - t0) * a.G;
         const int row_base = st * R;
         if (row_base < rows_exist) {
-            const int skv = a.skv[it.b];
+            const KvSeq kv = kv_seq<LAYOUT>(a, it.b);
+            const int skv = kv.len;
             const int off = skv - it.sq;
             const int row0 = row_base + wave * 32;
             QCol32 qc;
@@ -834,7 +837,6 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32_kernel(FwdArgs a) {
             const int t_lo = t0 + row_base / a.G;
             const int t_hi = t0 + (min(row_base + R, rows_exist) - 1) / a.G;
             const int32_t* sel = a.idx + ((int64_t)it.n2 * a.tqb + g) * a.topK;
-            const int32_t* ttab = a.table + (int64_t)it.b * a.maxb;
             const int64_t head_off = (int64_t)it.n2 * 128 * esz;
 
             // ---- visible pages of this task's selection range, compacted in order ---------
@@ -846,7 +848,7 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32_kernel(FwdArgs a) {
                         jl = sel[c0 + lane];
                         if (jl >= 0) {
                             cl = block_class(a, (int64_t)jl * 128, skv, off, t_lo, t_hi);
-                            if (cl != 0) pl = ttab[jl];
+                            if (cl != 0) pl = kv.unit<LAYOUT>(jl);
                         }
                     }
                     const uint64_t m = __ballot(cl != 0);
@@ -854,8 +856,9 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32_kernel(FwdArgs a) {
                         const int pos = n + __builtin_amdgcn_mbcnt_hi(
                                                 (uint32_t)(m >> 32),
                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-                        plist_page[pos] = pl;
-                        plist_jc[pos] = jl * 4 + cl;
+                        plist[pos] = make_int4(pl, jl * 4 + cl,
+                                               kv_records(rs, skv - 128 * jl),
+                                               kv_records(rs, skv - 128 * jl - 64));
                     }
                     n += __builtin_popcountll(m);
                 }
@@ -866,8 +869,12 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32_kernel(FwdArgs a) {
 
             // address of half page q (K or V) of this head in HBM
             auto half_src = [&](const unsigned char* base, int q) {
-                const int page = __builtin_amdgcn_readfirstlane(plist_page[q >> 1]);
-                return base + (int64_t)page * a.kv_stride * esz + head_off + (q & 1) * 64 * rs;
+                const int4 e = plist[q >> 1];
+                const int unit = __builtin_amdgcn_readfirstlane(e.x);
+                const int rec = __builtin_amdgcn_readfirstlane((q & 1) ? e.w : e.z);
+                return KvSrc{base + (int64_t)unit * a.kv_stride * esz + head_off +
+                                 (q & 1) * 64 * rs,
+                             rec};
             };
             if (nh > 0) {
                 f32x16 s[2];
@@ -896,8 +903,10 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32_kernel(FwdArgs a) {
                 }
                 // page-list entries for the next softmax item, read before its LDS stores are
                 // queued (a wait on the list read would otherwise also wait for the stores)
-                int jc_next = __builtin_amdgcn_readfirstlane(plist_jc[0]);
-                int mv_page = __builtin_amdgcn_readfirstlane(plist_page[move_half(1) >> 1]);
+                int jc_next = __builtin_amdgcn_readfirstlane(plist[0].y);
+                const int4 m1 = plist[move_half(1) >> 1];
+                int mv_page = __builtin_amdgcn_readfirstlane(m1.x);
+                int mv_rec = __builtin_amdgcn_readfirstlane((move_half(1) & 1) ? m1.w : m1.z);
                 auto softmax_and_move = [&](int k) {
                     const int jc = jc_next;
                     if constexpr (DT == kFP8) {  // V is widened to bf16 on its way into LDS
@@ -910,20 +919,23 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32_kernel(FwdArgs a) {
                     }
                     {
                         const int q = move_half(k + 1);
-                        const unsigned char* src = (grp == 0 ? vbase : kbase) +
-                                                   (int64_t)mv_page * a.kv_stride * esz + head_off +
-                                                   (q & 1) * 64 * rs;
+                        const KvSrc src{(grp == 0 ? vbase : kbase) +
+                                            (int64_t)mv_page * a.kv_stride * esz + head_off +
+                                            (q & 1) * 64 * rs,
+                                        mv_rec};
                         page_load<DT, 256, 64>(pr, src, rs, tg);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                     softmax_item32<DT>(a, s, p, colscale, trow, jc >> 2, k & 1, jc & 3, skv, off,
                                        lane, mrun, lrun, o);
                     __builtin_amdgcn_sched_barrier(0);
-                    const int jn = plist_jc[min(k + 1, nh - 1) >> 1];
-                    const int pn = plist_page[move_half(k + 2) >> 1];
+                    const int jn = plist[min(k + 1, nh - 1) >> 1].y;
+                    const int qn = move_half(k + 2);
+                    const int4 mn = plist[qn >> 1];
                     __syncthreads();
                     jc_next = __builtin_amdgcn_readfirstlane(jn);
-                    mv_page = __builtin_amdgcn_readfirstlane(pn);
+                    mv_page = __builtin_amdgcn_readfirstlane(mn.x);
+                    mv_rec = __builtin_amdgcn_readfirstlane((qn & 1) ? mn.w : mn.z);
                 };
                 mfma_item32<DT, true, false>(kst, vst, qc, s, p, o, lane);
                 __syncthreads();
@@ -971,7 +983,7 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32_kernel(FwdArgs a) {
 // ---------------------------------------------------------------------------------------------
 // The 128-row kernel (schedule above) on 32x32 tiles: each wave's 32 query rows are one
 // 32-column tile.
-template <int DT, int OUT>
+template <int DT, int OUT, int LAYOUT>
 __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32_kernel(FwdArgs a) {
     constexpr int R = 128;
     constexpr int esz = (DT == kFP8) ? 1 : 2;
@@ -980,7 +992,7 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32_kernel(FwdArgs a) {
     constexpr int kLds = (2 * KB + 2 * VB > kStateBytes) ? 2 * KB + 2 * VB : kStateBytes;
     // [K buffer 0][K buffer 1][V buffer 0][V buffer 1]; reused for the final merge
     __shared__ __attribute__((aligned(16))) unsigned char smem[kLds];
-    __shared__ int plist_page[256], plist_jc[256];
+    __shared__ int4 plist[256];  // as in the row-split kernel
     __shared__ int flag[2];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -1019,7 +1031,8 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32_kernel(FwdArgs a) {
         const int rows_exist = min(a.X, it.storage - t0) * a.G;
         const int row_base = st * R;
         if (row_base < rows_exist) {
-            const int skv = a.skv[it.b];
+            const KvSeq kv = kv_seq<LAYOUT>(a, it.b);
+            const int skv = kv.len;
             const int off = skv - it.sq;
             const int row0 = row_base + (wave & 3) * 32;
             QCol32 qc;
@@ -1033,7 +1046,6 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32_kernel(FwdArgs a) {
             const int t_lo = t0 + row_base / a.G;
             const int t_hi = t0 + (min(row_base + R, rows_exist) - 1) / a.G;
             const int32_t* sel = a.idx + ((int64_t)it.n2 * a.tqb + g) * a.topK;
-            const int32_t* ttab = a.table + (int64_t)it.b * a.maxb;
             const int64_t head_off = (int64_t)it.n2 * 128 * esz;
 
             if (wave == 0) {
@@ -1044,7 +1056,7 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32_kernel(FwdArgs a) {
                         jl = sel[c0 + lane];
                         if (jl >= 0) {
                             cl = block_class(a, (int64_t)jl * 128, skv, off, t_lo, t_hi);
-                            if (cl != 0) pl = ttab[jl];
+                            if (cl != 0) pl = kv.unit<LAYOUT>(jl);
                         }
                     }
                     const uint64_t m = __ballot(cl != 0);
@@ -1052,8 +1064,9 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32_kernel(FwdArgs a) {
                         const int pos = n + __builtin_amdgcn_mbcnt_hi(
                                                 (uint32_t)(m >> 32),
                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-                        plist_page[pos] = pl;
-                        plist_jc[pos] = jl * 4 + cl;
+                        plist[pos] = make_int4(pl, jl * 4 + cl,
+                                               kv_records(rs, skv - 128 * jl),
+                                               kv_records(rs, skv - 128 * jl - 64));
                     }
                     n += __builtin_popcountll(m);
                 }
@@ -1066,8 +1079,12 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32_kernel(FwdArgs a) {
             // address of half page q (K or V) of this head in HBM; q is clamped into the stream
             auto half_src = [&](const unsigned char* base, int q) {
                 q = min(max(q, 0), nh - 1);
-                const int page = __builtin_amdgcn_readfirstlane(plist_page[q >> 1]);
-                return base + (int64_t)page * a.kv_stride * esz + head_off + (q & 1) * 64 * rs;
+                const int4 e = plist[q >> 1];
+                const int unit = __builtin_amdgcn_readfirstlane(e.x);
+                const int rec = __builtin_amdgcn_readfirstlane((q & 1) ? e.w : e.z);
+                return KvSrc{base + (int64_t)unit * a.kv_stride * esz + head_off +
+                                 (q & 1) * 64 * rs,
+                             rec};
             };
             if (n > 0) {
                 f32x16 s[2];
@@ -1095,7 +1112,7 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32_kernel(FwdArgs a) {
                         store_k<DT, 256, 64>(pr, other_v, tg);  // same row pitch as K
                 };
                 auto softmax_and_move = [&](int k) {
-                    const int jc = __builtin_amdgcn_readfirstlane(plist_jc[k]);
+                    const int jc = __builtin_amdgcn_readfirstlane(plist[k].y);
                     PageRegs<DT, 256, 64> pr;
                     page_load<DT, 256, 64>(pr, half_src(kbase, 2 * k + 2 + grp), rs, tg);
                     __builtin_amdgcn_sched_barrier(0);
@@ -1181,19 +1198,29 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32_kernel(FwdArgs a) {
     }
 }
 
-template <int DT, int OUT>
-hipError_t launch_t(const FwdArgs& a, int rows, hipStream_t s) {
+template <int DT, int OUT, int LAYOUT>
+hipError_t launch_l(const FwdArgs& a, int rows, hipStream_t s) {
     const int grid = a.P * a.nst;
     // 8 waves per workgroup either way: 32 rows per wave for large units, 16 below (more
     // workgroups, fewer registers)
     if (rows == 256) {
-        hipLaunchKernelGGL((fwd_prefill_pp32_kernel<DT, OUT>), dim3(grid), dim3(512), 0, s, a);
+        hipLaunchKernelGGL((fwd_prefill_pp32_kernel<DT, OUT, LAYOUT>), dim3(grid), dim3(512), 0,
+                           s, a);
     } else if (a.M > 64) {
-        hipLaunchKernelGGL((fwd_prefill_ks32_kernel<DT, OUT>), dim3(grid), dim3(512), 0, s, a);
+        hipLaunchKernelGGL((fwd_prefill_ks32_kernel<DT, OUT, LAYOUT>), dim3(grid), dim3(512), 0,
+                           s, a);
     } else {
-        hipLaunchKernelGGL((fwd_prefill_kernel<DT, OUT, 8, 1>), dim3(grid), dim3(512), 0, s, a);
+        hipLaunchKernelGGL((fwd_prefill_kernel<DT, OUT, 8, 1, LAYOUT>), dim3(grid), dim3(512), 0,
+                           s, a);
     }
     return hipGetLastError();
+}
+
+// The KV layout is a template argument so that the paged kernels carry no layout test.
+template <int DT, int OUT>
+hipError_t launch_t(const FwdArgs& a, int rows, hipStream_t s) {
+    return a.cu_kv != nullptr ? launch_l<DT, OUT, kTnd>(a, rows, s)
+                              : launch_l<DT, OUT, kPaged>(a, rows, s);
 }
 
 }  // namespace

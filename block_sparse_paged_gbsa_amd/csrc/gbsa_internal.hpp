@@ -10,7 +10,7 @@ namespace gbsa {
 //   [0] magic  [1] version  [2] P (workers)  [3] U (units)  [4..5] total cost (lo, hi)
 //   [6] number of split units  [7] N1 [8] N2 [9] D [10] blockShapeX [11] blockShapeY
 //   [12] topK [13] mask_mode [14] quant_mode [15] totalQBlocks [16] B [17] win_left
-//   [18] win_right [19] seqused_q given [20] is_packed_gqa [21..23] 0
+//   [18] win_right [19] seqused_q given [20] is_packed_gqa [21] kv_layout [22..23] 0
 //   [24 + w], w = 0..P: boundary of worker w, packed (unit << 9) | slot; the rest 0.
 constexpr int kMetaWords = 1024;
 constexpr int kHeaderWords = 24;
@@ -21,7 +21,7 @@ constexpr int kVersion = 1;
 constexpr int kMaxWorkers = kMetaWords - kHeaderWords - 1;
 constexpr int kMaxUnits = 1 << (32 - kSlotBits - 1);
 // header words the main kernels compare against their own parameters
-constexpr int kCheckFirst = 7, kCheckLast = 20;
+constexpr int kCheckFirst = 7, kCheckLast = 21;
 
 enum DType : int { kF16 = 0, kBF16 = 1, kFP8 = 2 };
 
@@ -32,7 +32,7 @@ struct MetaArgs {
     int32_t* meta;         // [1024]
     int32_t B, N2, X, topK, tqb, P;
     int32_t ucap;  // units whose clamped counts the kernel keeps in LDS between its passes
-    int32_t header[kHeaderWords];  // words 7..20 prefilled by the host; the rest computed
+    int32_t header[kHeaderWords];  // words 7..21 prefilled by the host; the rest computed
 };
 
 struct FwdArgs {
@@ -44,8 +44,9 @@ struct FwdArgs {
     const int32_t* meta;   // [1024]
     const int64_t* cu;     // [B+1]
     const int32_t* squ;    // [B] or null
-    const int32_t* skv;    // [B]
-    const int32_t* table;  // [B, maxb]
+    const int32_t* skv;    // [B]; may be null with token-major key/value
+    const int32_t* table;  // [B, maxb] (paged key/value) or null (token-major)
+    const int64_t* cu_kv;  // [B+1] token-major key/value, else null
     const float* qs;       // [N1] or null
     const float* ks;       // [N2] or null
     const float* vs;       // [N2] or null
@@ -56,11 +57,12 @@ struct FwdArgs {
     float* ws_o;           // [2P, M, 128]
     float* ws_m;           // [2P, M]  running max, log2 domain
     float* ws_l;           // [2P, M]  running sum
-    int64_t kv_stride;     // elements between pages
+    int64_t kv_stride;     // elements per storage unit: a page (paged) or a row (token-major)
+    int64_t kv_rows;       // token-major: rows of key (= of value); paged: unused
     int32_t B, N1, N2, G, X, topK, tqb, maxb, P, M, nst;
     int32_t mask, wl, wr, return_lse;
     float scale_log2;      // softmax scale * log2(e)
-    int32_t expect[kHeaderWords];  // expected header words (0, 1, 2 and 7..20 are checked)
+    int32_t expect[kHeaderWords];  // expected header words (0, 1, 2 and 7..21 are checked)
 };
 
 // Workspace layout (byte offsets), a pure function of P and M.
@@ -89,7 +91,8 @@ hipError_t launch_decode(const FwdArgs& a, int dtype, int out_dtype, hipStream_t
 hipError_t launch_prefill(const FwdArgs& a, int dtype, int out_dtype, int rows_per_wg,
                           hipStream_t s);
 
-// Rows a prefill workgroup covers for a given M (8 waves of one or two 16-row MFMA tiles).
+// Rows a prefill workgroup covers for a given M: 256 (eight waves of 32 rows) above 256,
+// else 128 (two groups of four waves sharing the same rows, or eight 16-row waves).
 inline int prefill_rows_per_wg(int M) { return M > 256 ? 256 : 128; }
 constexpr int kDecodeMaxRows = 16;
 // Row subtiles per unit (workgroups per worker) for a given M.

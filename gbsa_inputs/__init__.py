@@ -12,6 +12,10 @@ sparse_block_idx is [N2, totalQBlocks, topK] and sparse_block_count is
 [N2, totalQBlocks], where totalQBlocks sums ceil(storage_len / blockShapeX)
 over the batch.
 
+to_tnd() rewrites a problem's key/value into the token-major TND layout
+[T_kv, N2, D] located by cu_seqlens_kv (the article's layoutKv "TND"): the same
+logical sequences, copied out of their pages back to back.
+
 Value tensors are drawn with a seeded torch.Generator on the requested
 device (CPU for small problems, the GPU for the full-size ones); all integer
 structure (lengths, page permutation, selections) is drawn with numpy PCG64
@@ -58,18 +62,21 @@ class Problem:
     scale: float
     cu_seqlens_q: np.ndarray  # int64 [B+1]
     seqused_q: Optional[np.ndarray]  # int32 [B] or None
-    seqused_kv: np.ndarray  # int32 [B]
-    block_table: np.ndarray  # int32 [B, max_blocks]
-    num_pages: int
+    seqused_kv: Optional[np.ndarray]  # int32 [B]; None only with TND key/value
+    block_table: Optional[np.ndarray]  # int32 [B, max_blocks]; None with TND key/value
+    num_pages: int  # pages of the pool, or rows of TND key/value
     sparse_block_idx: np.ndarray  # int32 [N2, totalQBlocks, topK]
     sparse_block_count: np.ndarray  # int32 [N2, totalQBlocks]
     q: torch.Tensor  # [T, N1, D]
-    k: torch.Tensor  # [num_pages, 128, N2, D] (page axis may be strided)
+    k: torch.Tensor  # [num_pages, 128, N2, D] (page axis may be strided), or TND [T_kv, N2, D]
     v: torch.Tensor
     q_scale: Optional[np.ndarray] = None  # float32 [N1] (fp8 only)
     k_scale: Optional[np.ndarray] = None  # float32 [N2]
     v_scale: Optional[np.ndarray] = None  # float32 [N2]
     seed: int = 0
+    kv_storage: Optional[np.ndarray] = None  # int64 [B]: cached KV length of each sequence
+    kv_layout: str = "PA_BBND"  # or "TND"
+    cu_seqlens_kv: Optional[np.ndarray] = None  # int64 [B+1] (TND only)
 
     @property
     def total_q(self) -> int:
@@ -89,9 +96,17 @@ class Problem:
 
     @property
     def kv_page_stride(self) -> int:
+        if self.kv_layout == "TND":
+            return 0
         if self.k is None:
             return PAGE * self.num_heads_kv * HEAD_DIM
         return int(self.k.stride(0))
+
+    def kv_len(self, b: int) -> int:
+        """Visible KV length of sequence b: seqused_kv, or the TND storage length."""
+        if self.seqused_kv is not None:
+            return int(self.seqused_kv[b])
+        return int(self.cu_seqlens_kv[b + 1] - self.cu_seqlens_kv[b])
 
 
 # ---------------------------------------------------------------------------
@@ -296,7 +311,8 @@ def build_problem(name: str, *, seed: int, q_lens: Sequence[int], kv_lens: Seque
                    win_right=win_right, return_lse=return_lse, scale=scale, cu_seqlens_q=cu,
                    seqused_q=squ, seqused_kv=sk, block_table=table, num_pages=num_pages,
                    sparse_block_idx=idx, sparse_block_count=cnt, q=q, k=k, v=v,
-                   q_scale=qs, k_scale=ks, v_scale=vs, seed=seed)
+                   q_scale=qs, k_scale=ks, v_scale=vs, seed=seed,
+                   kv_storage=np.asarray(kv_storage, dtype=np.int64))
 
 
 # ---------------------------------------------------------------------------
@@ -387,4 +403,45 @@ def to_device(p: Problem, device) -> Problem:
         base = t.as_strided((t.shape[0], t.stride(0)), (t.stride(0), 1))
         nb = base.to(device)
         return nb.as_strided(t.shape, t.stride())
+    if p.kv_layout == "TND":
+        return dataclasses.replace(p, q=p.q.to(device), k=p.k.to(device), v=p.v.to(device))
     return dataclasses.replace(p, q=p.q.to(device), k=mv(p.k), v=mv(p.v))
+
+
+def to_tnd(p: Problem, keep_seqused_kv: bool = True, tail_rows: int = 0) -> Problem:
+    """The same problem with token-major key/value [T_kv, N2, D] (layoutKv "TND").
+
+    Sequence b's rows are its logical KV positions 0 .. storage_b - 1, copied out of its
+    pages; sequences follow each other and cu_seqlens_kv holds the prefix of the storage
+    lengths. keep_seqused_kv=False trims every storage to seqused_kv and drops seqused_kv
+    (the single-length form). tail_rows extra rows follow the last sequence (zeros); with
+    none, the last block of the last sequence runs past the tensor unless its length is a
+    multiple of 128.
+    """
+    assert p.kv_layout == "PA_BBND"
+    storage = (np.asarray(p.kv_storage, dtype=np.int64) if p.kv_storage is not None
+               else np.asarray(p.seqused_kv, dtype=np.int64))
+    if not keep_seqused_kv:
+        storage = np.minimum(storage, np.asarray(p.seqused_kv, dtype=np.int64))
+    cu_kv = np.zeros(p.batch + 1, dtype=np.int64)
+    cu_kv[1:] = np.cumsum(storage)
+    fp8 = p.k.dtype == torch.float8_e4m3fn
+
+    def rows(t: torch.Tensor) -> torch.Tensor:
+        src = t.view(torch.uint8) if fp8 else t
+        out = torch.zeros((int(cu_kv[-1]) + tail_rows, p.num_heads_kv, HEAD_DIM),
+                          dtype=src.dtype, device=src.device)
+        for b in range(p.batch):
+            st = int(storage[b])
+            nblk = _ceil_div(st, PAGE)
+            if nblk == 0:
+                continue
+            pages = torch.as_tensor(p.block_table[b, :nblk].astype(np.int64), device=src.device)
+            out[int(cu_kv[b]):int(cu_kv[b]) + st] = src[pages].reshape(-1, p.num_heads_kv,
+                                                                        HEAD_DIM)[:st]
+        return out.view(torch.float8_e4m3fn) if fp8 else out
+
+    return dataclasses.replace(
+        p, name=p.name + "_tnd", k=rows(p.k), v=rows(p.v), block_table=None,
+        num_pages=int(cu_kv[-1]) + tail_rows, kv_storage=storage, kv_layout="TND",
+        cu_seqlens_kv=cu_kv, seqused_kv=p.seqused_kv if keep_seqused_kv else None)

@@ -24,7 +24,8 @@
  *    indices, page-table entries) are not validated on the host ("general constraints":
  *    tiling never reads tensor values); see gbsa_forward for how the kernels treat them.
  *  - Layouts: query TND [T, N1, D] dense; key/value PA_BBND [num_pages, 128, N2, D] where
- *    only the page axis may be strided (kv_page_stride elements between pages);
+ *    only the page axis may be strided (kv_page_stride elements between pages), or, with
+ *    kv_layout = GBSA_KV_TND (gbsa_forward_tnd), token-major TND [T_kv, N2, D] dense;
  *    sparse_block_idx [N2, total_q_blocks, top_k] and sparse_block_count
  *    [N2, total_q_blocks] dense int32; block_table [B, max_blocks_per_seq] dense int32;
  *    cu_seqlens_q [B+1] int64; seqused_q / seqused_kv [B] int32; attention_out [T, N1, D];
@@ -78,6 +79,13 @@ typedef enum gbsa_dtype {
 /* "mask" section: 1 = built-in causal. 0 = no mask. */
 typedef enum gbsa_mask_mode { GBSA_MASK_NONE = 0, GBSA_MASK_CAUSAL = 1 } gbsa_mask_mode;
 
+/* Key/value layouts ("parameters" section: layoutKv). PA_BBND pages are located through
+ * block_table; TND rows through cu_seqlens_kv ("general constraints": dual lengths, which
+ * apply to the KV side when layoutKv is TND). */
+typedef enum gbsa_kv_layout { GBSA_KV_PA_BBND = 0, GBSA_KV_TND = 1 } gbsa_kv_layout;
+/* Rows a TND key/value tensor may hold: the last block of a sequence must start below 2^31. */
+#define GBSA_MAX_KV_ROWS 2147483520LL
+
 /* "quantisation" section: 0 NO_QUANT, 5 FP8_E4M3_STATIC_CAST_P (1..4 are rejected). */
 typedef enum gbsa_quant_mode { GBSA_QUANT_NONE = 0, GBSA_QUANT_FP8_E4M3 = 5 } gbsa_quant_mode;
 
@@ -99,10 +107,11 @@ typedef struct gbsa_params {
     int32_t block_x;            /* blockShapeX >= 1 (query rows per Q block) */
     int32_t block_y;            /* blockShapeY; must be 128 */
     int32_t page_size;          /* KV page size; must be 128 */
-    int32_t max_blocks_per_seq; /* dim 1 of block_table */
-    int64_t num_pages;          /* dim 0 of key/value */
-    int64_t kv_page_stride;     /* elements between pages; 0 = dense (128*N2*D);
-                                   else >= 128*N2*D and a multiple of N2*D */
+    int32_t max_blocks_per_seq; /* dim 1 of block_table (PA_BBND; not read with TND) */
+    int64_t num_pages;          /* dim 0 of key/value: pages (PA_BBND) or rows T_kv (TND,
+                                   at most GBSA_MAX_KV_ROWS) */
+    int64_t kv_page_stride;     /* PA_BBND: elements between pages; 0 = dense (128*N2*D);
+                                   else >= 128*N2*D and a multiple of N2*D. TND: must be 0 */
     int32_t dtype;              /* gbsa_dtype of query/key/value (must match) */
     int32_t out_dtype;          /* gbsa_dtype of attention_out: F16 or BF16. With quant 0 it
                                    must equal dtype; with quant 5 it is required */
@@ -116,7 +125,9 @@ typedef struct gbsa_params {
     int32_t has_seqused_q;      /* 1: seqused_q is passed to both calls */
     float scale;                /* softmax scale; <= 0 means 1/sqrt(D) */
     int32_t num_workers;        /* 0 = chosen by the library from the shapes, else 1..999 */
-    int32_t reserved[4];        /* must be 0 */
+    int32_t kv_layout;          /* gbsa_kv_layout: GBSA_KV_PA_BBND (gbsa_forward) or
+                                   GBSA_KV_TND (gbsa_forward_tnd) */
+    int32_t reserved[3];        /* must be 0 */
 } gbsa_params;
 
 /*
@@ -143,7 +154,8 @@ gbsa_status gbsa_num_workers(const gbsa_params* params, int32_t* num_workers);
  *   sparse_block_count  [N2, total_q_blocks] int32, device
  *   cu_seqlens_q        [B+1] int64, device (storage lengths of the TND query)
  *   seqused_q           [B] int32, device, or NULL (must be non-NULL iff has_seqused_q)
- *   seqused_kv          [B] int32, device (required with PA_BBND; not read here)
+ *   seqused_kv          [B] int32, device: required with PA_BBND, optional (NULL) with TND;
+ *                       not read here (the task split does not depend on KV lengths)
  *   metadata            [1024] int32, device, written
  * Errors: gbsa_check_params errors; GBSA_ERR_NULL; GBSA_ERR_METADATA (metadata NULL);
  * GBSA_ERR_HIP on a failed launch.
@@ -160,7 +172,8 @@ gbsa_status gbsa_metadata(const gbsa_params* params, const int32_t* sparse_block
 gbsa_status gbsa_workspace_size(const gbsa_params* params, size_t* bytes);
 
 /*
- * Stage 2 (the main operator, "sparse attention mechanism" formula).
+ * Stage 2 (the main operator, "sparse attention mechanism" formula), PA_BBND key/value
+ * (params->kv_layout must be GBSA_KV_PA_BBND).
  *   query        [T, N1, 128]            dtype
  *   key, value   [num_pages, 128, N2, 128] dtype, page axis stride kv_page_stride
  *   sparse_block_idx   [N2, total_q_blocks, top_k] int32: LOGICAL block numbers j of the
@@ -187,7 +200,8 @@ gbsa_status gbsa_workspace_size(const gbsa_params* params, size_t* bytes);
  * params, the kernels write nothing to the outputs and set word 0 of the workspace to a
  * non-zero value (readable by the caller after the stream completes).
  * Errors: gbsa_check_params errors; GBSA_ERR_NULL; GBSA_ERR_METADATA; GBSA_ERR_WORKSPACE;
- * GBSA_ERR_DTYPE (scales inconsistent with quant_mode); GBSA_ERR_HIP on a failed launch.
+ * GBSA_ERR_DTYPE (scales inconsistent with quant_mode); GBSA_ERR_UNSUPPORTED (kv_layout is
+ * not PA_BBND); GBSA_ERR_HIP on a failed launch.
  */
 gbsa_status gbsa_forward(const gbsa_params* params, const void* query, const void* key,
                          const void* value, const int32_t* sparse_block_idx,
@@ -197,6 +211,35 @@ gbsa_status gbsa_forward(const gbsa_params* params, const void* query, const voi
                          const float* q_scale, const float* k_scale, const float* v_scale,
                          const float* p_scale, void* attention_out, float* softmax_lse,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Stage 2 with token-major TND key/value (params->kv_layout must be GBSA_KV_TND): the
+ * article's layoutKv "TND" with cu_seqlens_kv and the dual-length rule of its "general
+ * constraints" section applied to the KV side. Same computation and arguments as
+ * gbsa_forward except:
+ *   key, value     [T_kv, N2, 128] dtype, dense; T_kv = params->num_pages
+ *   cu_seqlens_kv  [B+1] int64: sequence b owns rows cu_seqlens_kv[b] .. cu_seqlens_kv[b+1]-1
+ *                  (its KV storage length); logical block j is rows cu_seqlens_kv[b] + 128*j
+ *                  .. +127 of that sequence
+ *   seqused_kv     [B] int32 or NULL: visible KV length of each sequence; NULL means the
+ *                  storage length. Values above the storage length are clamped to it.
+ * Key position p of sequence b is visible iff p < kv_len[b] (kv_len = seqused_kv or storage)
+ * and the mask keeps it, with off = kv_len[b] - (seqused_q[b] or the q storage length).
+ * cu_seqlens_kv should be non-decreasing with cu_seqlens_kv[B] <= T_kv; the kernels clamp
+ * each sequence's row range into [0, T_kv], so no load leaves the tensor. The rows a block
+ * spans past kv_len (the next sequence's, or past the tensor's end) read as zeros without a
+ * memory access, as do page-tail rows past seqused_kv in gbsa_forward: cached rows beyond
+ * the visible length never reach the output, whatever they hold.
+ * Errors: as gbsa_forward; GBSA_ERR_UNSUPPORTED if kv_layout is not TND.
+ */
+gbsa_status gbsa_forward_tnd(const gbsa_params* params, const void* query, const void* key,
+                             const void* value, const int32_t* sparse_block_idx,
+                             const int32_t* sparse_block_count, const int32_t* metadata,
+                             const int64_t* cu_seqlens_q, const int32_t* seqused_q,
+                             const int64_t* cu_seqlens_kv, const int32_t* seqused_kv,
+                             const float* q_scale, const float* k_scale, const float* v_scale,
+                             const float* p_scale, void* attention_out, float* softmax_lse,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Human-readable text for a status (static storage). */
 const char* gbsa_status_string(gbsa_status status);

@@ -2,8 +2,9 @@
 
 TEST INFRASTRUCTURE ONLY (see the package docstring). No online softmax, no
 tiling, no fusion: for every query row the selected KV blocks are gathered
-through the page table, the scaled logits are formed, masked positions are set
-to -inf and an explicit full-row softmax is applied.
+through the page table (or, for token-major key/value, from the sequence's rows),
+the scaled logits are formed, masked positions are set to -inf and an explicit
+full-row softmax is applied.
 
 Sources (GenericBlockSparseAttention article, cf-1.com, CANN ops-transformer):
   * "sparse attention mechanism": out = softmax(scale * q * k_sparse^T + mask) * v_sparse,
@@ -33,6 +34,12 @@ Readings where the pages are silent (each is listed in the design notes):
   * fp8: per-head dequant scales q_scale[N1], k_scale[N2], v_scale[N2]; the
     oracle works on exactly dequantised values and never quantises P.
   * Rows t >= sq[b] are not part of the output (left as NaN here).
+  * Token-major (TND) key/value ("general constraints": layoutKv TND comes with
+    cu_seqlens_kv, and the dual-length rule then holds on the KV side): sequence
+    b owns rows cu_seqlens_kv[b] .. cu_seqlens_kv[b+1]-1, logical block j is its
+    rows 128*j .. 128*j+127, and the visible length is seqused_kv[b] when given,
+    else the storage length. A seqused_kv above the storage length (which the
+    pages forbid) is read as the storage length.
 """
 from __future__ import annotations
 
@@ -81,14 +88,21 @@ class Inputs:
     def __init__(self, q, k, v, sparse_block_idx, sparse_block_count, cu_seqlens_q, seqused_q,
                  seqused_kv, block_table, *, dtype: str, block_x: int, scale: float,
                  mask_mode: int, win_left: int = -1, win_right: int = -1,
-                 q_scale=None, k_scale=None, v_scale=None):
+                 q_scale=None, k_scale=None, v_scale=None, cu_seqlens_kv=None):
+        """Paged key/value [pages, 128, N2, D] with block_table and seqused_kv, or, when
+        cu_seqlens_kv is given, token-major key/value [T_kv, N2, D] (block_table unused,
+        seqused_kv optional)."""
         self.q, self.k, self.v = q, k, v
         self.idx = np.asarray(sparse_block_idx)
         self.cnt = np.asarray(sparse_block_count)
         self.cu = np.asarray(cu_seqlens_q, dtype=np.int64)
         self.squ = None if seqused_q is None else np.asarray(seqused_q, dtype=np.int64)
-        self.skv = np.asarray(seqused_kv, dtype=np.int64)
-        self.table = np.asarray(block_table)
+        self.tnd = cu_seqlens_kv is not None
+        self.cu_kv = np.asarray(cu_seqlens_kv, dtype=np.int64) if self.tnd else None
+        if seqused_kv is None and not self.tnd:
+            raise ValueError("paged key/value need seqused_kv")
+        self.skv = None if seqused_kv is None else np.asarray(seqused_kv, dtype=np.int64)
+        self.table = None if self.tnd else np.asarray(block_table)
         self.dtype = dtype
         self.X = int(block_x)
         self.D = int(q.shape[-1])
@@ -96,7 +110,7 @@ class Inputs:
         self.mask_mode = int(mask_mode)
         self.wl, self.wr = int(win_left), int(win_right)
         self.N1 = int(q.shape[1])
-        self.N2 = int(k.shape[2])
+        self.N2 = int(k.shape[1] if self.tnd else k.shape[2])
         self.G = self.N1 // self.N2
         self.top_k = int(self.idx.shape[2])
         self.qs = None if q_scale is None else np.asarray(q_scale, dtype=np.float64)
@@ -114,6 +128,13 @@ class Inputs:
     def sq(self, b: int) -> int:
         return int(self.squ[b]) if self.squ is not None else self.storage(b)
 
+    def kv_len(self, b: int) -> int:
+        """Visible keys of sequence b (seqused_kv; token-major: capped at the storage)."""
+        if not self.tnd:
+            return int(self.skv[b])
+        st = int(self.cu_kv[b + 1] - self.cu_kv[b])
+        return st if self.skv is None else min(int(self.skv[b]), st)
+
 
 def gather_unit(inp: Inputs, b: int, n2: int, g: int):
     """Visible-length-trimmed key positions, K rows and V rows selected for unit (b, n2, g).
@@ -121,7 +142,7 @@ def gather_unit(inp: Inputs, b: int, n2: int, g: int):
     Returns positions [n], K [n, D] and V [n, D] in float64 (dequantised).
     """
     c = min(max(int(inp.cnt[n2, g]), 0), inp.top_k)
-    skv = int(inp.skv[b])
+    skv = inp.kv_len(b)
     pos, ks, vs = [], [], []
     r = np.arange(PAGE)
     for s in range(c):
@@ -132,10 +153,17 @@ def gather_unit(inp: Inputs, b: int, n2: int, g: int):
         keep = p < skv
         if not keep.any():
             continue
+        pos.append(p[keep])
+        if inp.tnd:
+            rows = int(inp.cu_kv[b]) + p[keep]
+            if rows[-1] >= inp.k.shape[0]:
+                raise ValueError(f"batch {b} block {j} reads past the key/value rows")
+            ks.append(decode(np.asarray(inp.k[rows, n2, :]), inp.dtype))
+            vs.append(decode(np.asarray(inp.v[rows, n2, :]), inp.dtype))
+            continue
         page = int(inp.table[b, j])
         if page < 0 or page >= inp.k.shape[0]:
             raise ValueError(f"block table entry {page} for batch {b} block {j} out of range")
-        pos.append(p[keep])
         ks.append(decode(np.asarray(inp.k[page, :, n2, :])[keep], inp.dtype))
         vs.append(decode(np.asarray(inp.v[page, :, n2, :])[keep], inp.dtype))
     if not pos:
@@ -172,8 +200,9 @@ def attention_unit(inp: Inputs, b: int, n2: int, gl: int, rows: Optional[np.ndar
     if inp.qs is not None:
         qv = qv * inp.qs[heads][None, :, None]
     z = inp.scale * np.einsum("rgd,nd->rgn", qv, K)  # [r, G, n]
-    off = int(inp.skv[b]) - sq
-    vis = visible(pos, rows, int(inp.skv[b]), off, inp.mask_mode, inp.wl, inp.wr)  # [r, n]
+    skv = inp.kv_len(b)
+    off = skv - sq
+    vis = visible(pos, rows, skv, off, inp.mask_mode, inp.wl, inp.wr)  # [r, n]
     z = np.where(vis[:, None, :], z, -np.inf)
     O = np.zeros((len(rows), G, inp.D))
     lse = np.full((len(rows), G), -np.inf)

@@ -29,7 +29,7 @@ Buffer layout (int32 words):
   [2] P   [3] U   [4] W mod 2^32   [5] W div 2^32   [6] number of split units
   [7] N1  [8] N2  [9] D  [10] blockShapeX  [11] blockShapeY  [12] topK
   [13] mask_mode  [14] quant_mode  [15] totalQBlocks  [16] B  [17] win_left
-  [18] win_right  [19] seqused_q given (0/1)  [20] is_packed_gqa  [21..23] 0
+  [18] win_right  [19] seqused_q given (0/1)  [20] is_packed_gqa  [21] kv_layout (0 paged, 1 TND)  [22..23] 0
   [24 + w] boundary w for w = 0..P, packed as (u << 9) | s
   remaining words 0.
 A unit is "split" when a boundary falls strictly inside it (s > 0).
@@ -114,8 +114,11 @@ def reference_metadata(*, cu_seqlens_q, seqused_q, sparse_block_count: np.ndarra
                        num_heads_q: int, num_heads_kv: int, head_dim: int, block_x: int,
                        block_y: int, top_k: int, mask_mode: int, quant_mode: int,
                        win_left: int, win_right: int, num_workers: int,
-                       is_packed_gqa: int = 1) -> np.ndarray:
-    """The full 1024-word metadata buffer for the given inputs and worker count."""
+                       is_packed_gqa: int = 1, kv_layout: int = 0) -> np.ndarray:
+    """The full 1024-word metadata buffer for the given inputs and worker count.
+
+    kv_layout (0 paged, 1 token-major) is recorded in the header only: the split depends
+    on the selection counts and the query lengths alone."""
     P = int(num_workers)
     assert 1 <= P <= MAX_WORKERS
     cnt = np.asarray(sparse_block_count)
@@ -137,6 +140,7 @@ def reference_metadata(*, cu_seqlens_q, seqused_q, sparse_block_count: np.ndarra
     meta[7:21] = [num_heads_q, num_heads_kv, head_dim, block_x, block_y, top_k, mask_mode,
                   quant_mode, cnt.shape[1], len(cu_seqlens_q) - 1, win_left, win_right,
                   0 if seqused_q is None else 1, is_packed_gqa]
+    meta[21] = kv_layout
     for w, (u, s) in enumerate(bnd):
         meta[HEADER_WORDS + w] = (u << SLOT_BITS) | s
     return meta.astype(np.uint32).view(np.int32)

@@ -27,7 +27,8 @@ def oracle_inputs(p, q=None, k=None, v=None) -> Inputs:
                   p.seqused_q, p.seqused_kv, p.block_table, dtype=p.dtype, block_x=p.block_x,
                   scale=p.scale, mask_mode=p.mask_mode, win_left=p.win_left,
                   win_right=p.win_right, q_scale=p.q_scale, k_scale=p.k_scale,
-                  v_scale=p.v_scale)
+                  v_scale=p.v_scale,
+                  cu_seqlens_kv=p.cu_seqlens_kv if p.kv_layout == "TND" else None)
 
 
 def dequant(t: torch.Tensor, dtype: str, scale=None, head_axis=None) -> torch.Tensor:
@@ -51,9 +52,12 @@ LSE_RTOL = 1e-3
 def gpu_params(p, num_workers: int = 0):
     import gbsa_inputs as gi
     from block_sparse_paged_gbsa_amd.api import make_params
+    tnd = p.kv_layout == "TND"
     return make_params(batch=p.batch, num_heads_q=p.num_heads_q, num_heads_kv=p.num_heads_kv,
                        total_q=p.total_q, total_q_blocks=p.total_q_blocks, top_k=p.top_k,
-                       block_x=p.block_x, max_blocks_per_seq=p.block_table.shape[1],
+                       block_x=p.block_x,
+                       max_blocks_per_seq=0 if tnd else p.block_table.shape[1],
+                       kv_layout=1 if tnd else 0,
                        num_pages=p.num_pages, kv_page_stride=p.kv_page_stride,
                        dtype=gi.TORCH_DTYPES[p.dtype], out_dtype=gi.TORCH_DTYPES[p.out_dtype],
                        mask_mode=p.mask_mode, win_left=p.win_left, win_right=p.win_right,
@@ -72,8 +76,10 @@ class GpuProblem:
         self.cnt = torch.as_tensor(p.sparse_block_count).to(d)
         self.cu = torch.as_tensor(p.cu_seqlens_q).to(d)
         self.squ = None if p.seqused_q is None else torch.as_tensor(p.seqused_q).to(d)
-        self.skv = torch.as_tensor(p.seqused_kv).to(d)
-        self.table = torch.as_tensor(p.block_table).to(d)
+        self.skv = None if p.seqused_kv is None else torch.as_tensor(p.seqused_kv).to(d)
+        self.tnd = p.kv_layout == "TND"
+        self.table = None if self.tnd else torch.as_tensor(p.block_table).to(d)
+        self.cu_kv = torch.as_tensor(p.cu_seqlens_kv).to(d) if self.tnd else None
         f = lambda s: None if s is None else torch.as_tensor(s, dtype=torch.float32).to(d)
         self.qs, self.ks, self.vs = f(p.q_scale), f(p.k_scale), f(p.v_scale)
 
@@ -82,8 +88,12 @@ class GpuProblem:
         return gbsa_metadata(params, self.cnt, self.cu, self.squ, self.skv, metadata)
 
     def forward(self, params, meta, out=None, lse=None, workspace=None):
-        from block_sparse_paged_gbsa_amd.api import gbsa_forward
+        from block_sparse_paged_gbsa_amd.api import gbsa_forward, gbsa_forward_tnd
         p = self.p
+        if self.tnd:
+            return gbsa_forward_tnd(params, p.q, p.k, p.v, self.idx, self.cnt, meta, self.cu,
+                                    self.squ, self.cu_kv, self.skv, self.qs, self.ks, self.vs,
+                                    None, out, lse, workspace)
         return gbsa_forward(params, p.q, p.k, p.v, self.idx, self.cnt, meta, self.cu, self.squ,
                             self.skv, self.table, self.qs, self.ks, self.vs, None, out, lse,
                             workspace)
@@ -122,12 +132,35 @@ def compare(p, out, lse, O_ref, L_ref, rows_mask, label=""):
     return err, lerr
 
 
+def _compact_tnd(p, units):
+    """Token-major form of compact_oracle_inputs: copies only the rows of the sequences the
+    units belong to; every other sequence becomes an empty range (the sampled rows never
+    read it)."""
+    seqs = {b for (b, _) in units}
+    cu = p.cu_seqlens_kv
+    new_cu = np.zeros(p.batch + 1, dtype=np.int64)
+    for b in range(p.batch):
+        new_cu[b + 1] = new_cu[b] + (int(cu[b + 1] - cu[b]) if b in seqs else 0)
+    sel = torch.cat([torch.arange(int(cu[b]), int(cu[b + 1]), device=p.k.device)
+                     for b in sorted(seqs)])
+    k = storage_numpy(p.k[sel], p.dtype)
+    v = storage_numpy(p.v[sel], p.dtype)
+    q = storage_numpy(p.q, p.dtype)
+    return Inputs(q, k, v, p.sparse_block_idx, p.sparse_block_count, p.cu_seqlens_q,
+                  p.seqused_q, p.seqused_kv, None, dtype=p.dtype, block_x=p.block_x,
+                  scale=p.scale, mask_mode=p.mask_mode, win_left=p.win_left,
+                  win_right=p.win_right, q_scale=p.q_scale, k_scale=p.k_scale,
+                  v_scale=p.v_scale, cu_seqlens_kv=new_cu)
+
+
 def compact_oracle_inputs(p, units):
     """Oracle inputs restricted to the pages that the given (b, gl) units select.
 
     Gathers just those pages from the device tensors (all KV heads) and remaps the block
     table, so full-size problems can be checked on sampled rows without copying the pool.
     """
+    if p.kv_layout == "TND":
+        return _compact_tnd(p, units)
     starts = __import__("gbsa_inputs").q_block_starts(p.cu_seqlens_q, p.block_x)
     pages = set()
     for (b, gl) in units:

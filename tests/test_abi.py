@@ -123,3 +123,39 @@ def test_entry_points_validate_before_device_work():
 def test_status_strings():
     for code in range(9):
         assert len(_lib.status_string(code)) >= 2
+
+
+def test_tnd_layout_rules():
+    """Token-major key/value: rows in num_pages, no page stride, block table not needed."""
+    tnd = _lib.KV_TND
+    assert _check(_good(kv_layout=tnd, max_blocks_per_seq=0, num_pages=1000)) == 0
+    assert _check(_good(kv_layout=2)) == 4
+    assert _check(_good(kv_layout=tnd, kv_page_stride=128 * 2 * 128)) == 2
+    assert _check(_good(kv_layout=tnd, num_pages=_lib.MAX_KV_ROWS)) == 0
+    assert _check(_good(kv_layout=tnd, num_pages=_lib.MAX_KV_ROWS + 1)) == 2
+    assert _check(_good(max_blocks_per_seq=0)) == 5  # the paged layout needs a block table
+
+
+def test_tnd_entry_point_validation():
+    lib = _lib.load()
+    dummy = ctypes.c_void_p(0x1000)
+    paged = _good()
+    tnd = _good(kv_layout=_lib.KV_TND, max_blocks_per_seq=0, num_pages=1000)
+    # order: q k v idx cnt meta cu squ cu_kv skv qs ks vs ps out lse ws
+    args = [dummy] * 17
+    args[7] = None  # seqused_q
+    args[10] = args[11] = args[12] = args[13] = None  # scales
+    args[15] = None  # lse
+    # each layout has its own entry point
+    assert lib.gbsa_forward(ctypes.byref(tnd), *args, 1 << 40, None) == 4
+    assert lib.gbsa_forward_tnd(ctypes.byref(paged), *args, 1 << 40, None) == 4
+    assert lib.gbsa_forward_tnd(ctypes.byref(tnd), *args, 0, None) == 6  # workspace too small
+    a2 = list(args)
+    a2[8] = None  # cu_seqlens_kv is required
+    assert lib.gbsa_forward_tnd(ctypes.byref(tnd), *a2, 1 << 40, None) == 1
+    a3 = list(args)
+    a3[9] = None  # seqused_kv is optional with TND
+    assert lib.gbsa_forward_tnd(ctypes.byref(tnd), *a3, 0, None) == 6
+    # metadata: seqused_kv optional with TND, required with PA_BBND
+    assert lib.gbsa_metadata(ctypes.byref(tnd), dummy, dummy, None, None, None, None) == 7
+    assert lib.gbsa_metadata(ctypes.byref(paged), dummy, dummy, None, None, dummy, None) == 1

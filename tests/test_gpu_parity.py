@@ -39,7 +39,7 @@ def _ref_meta(p, P):
         sparse_block_count=p.sparse_block_count, num_heads_q=p.num_heads_q,
         num_heads_kv=p.num_heads_kv, head_dim=128, block_x=p.block_x, block_y=128,
         top_k=p.top_k, mask_mode=p.mask_mode, quant_mode=p.quant_mode, win_left=p.win_left,
-        win_right=p.win_right, num_workers=P)
+        win_right=p.win_right, num_workers=P, kv_layout=1 if p.kv_layout == "TND" else 0)
 
 
 def _full_check(p, num_workers=0, label=""):
@@ -211,6 +211,109 @@ def test_deterministic_and_page_shuffle_invariant():
     assert torch.equal(o1, o3) and torch.equal(l1, l3)
 
 
+# ---------------------------------------------------------------------------
+# token-major (TND) key/value, and rows past the visible KV length
+# ---------------------------------------------------------------------------
+
+# one case per kernel: decode (M <= 16), 16-row waves (M <= 64), key-split (M <= 256) and
+# row-split (M > 256) ping-pong; `keep` passes seqused_kv below the storage length (dual
+# lengths), else none; tail rows follow the last sequence (0: its last block runs past the
+# tensor's end)
+TND_CASES = [
+    dict(seed=131, dtype="f16", mask_mode=1, use_seqused_q=True, block_x=32, keep=True, tail=0),
+    dict(seed=132, dtype="bf16", decode=True, batch=5, block_x=1, num_heads_q=16,
+         num_heads_kv=4, mask_mode=1, keep=False, tail=0),
+    dict(seed=133, dtype="fp8", batch=2, max_len=500, block_x=96, num_heads_q=4,
+         num_heads_kv=4, top_k=4, mask_mode=1, out_dtype="f16", keep=True, tail=0),
+    dict(seed=134, dtype="f16", batch=2, max_len=500, block_x=40, num_heads_q=16,
+         num_heads_kv=2, top_k=6, mask_mode=1, win_left=100, win_right=0, use_seqused_q=True,
+         keep=True, tail=0),
+    dict(seed=135, dtype="bf16", batch=3, max_len=400, block_x=64, num_heads_q=4,
+         num_heads_kv=2, top_k=5, mask_mode=0, keep=False, tail=64),
+    dict(seed=136, dtype="fp8", decode=True, batch=4, block_x=2, num_heads_q=8,
+         num_heads_kv=2, top_k=5, keep=True, tail=0),
+    dict(seed=137, dtype="bf16", batch=1, max_len=700, block_x=128, num_heads_q=8,
+         num_heads_kv=1, top_k=6, mask_mode=1, keep=True, tail=0),
+]
+
+
+@pytest.mark.parametrize("case", TND_CASES, ids=[str(c["seed"]) for c in TND_CASES])
+def test_tnd_layout_all_rows(case):
+    kw = dict(case)
+    seed, keep, tail = kw.pop("seed"), kw.pop("keep"), kw.pop("tail")
+    p = gi.to_tnd(gi.random_problem(seed, device="cuda", **kw), keep_seqused_kv=keep,
+                  tail_rows=tail)
+    assert p.num_pages == p.k.shape[0]
+    for P in (0, 5, 200):
+        _full_check(p, num_workers=P, label=f"tnd{seed} P={P}")
+
+
+def test_tnd_matches_paged_bit_exact():
+    """The kernels see the same bytes in the same order in either layout."""
+    p = gi.random_problem(138, device="cuda", batch=3, mask_mode=1, use_seqused_q=True)
+    res = []
+    for prob in (p, gi.to_tnd(p)):
+        # rows past seqused_q are not written: start both outputs from the same bytes
+        out = torch.zeros(p.q.shape, dtype=gi.TORCH_DTYPES[p.out_dtype], device="cuda")
+        lse = torch.zeros(p.q.shape[:2], dtype=torch.float32, device="cuda")
+        res.append(GpuProblem(prob).run(9, out=out, lse=lse)[2:4])
+    (o1, l1), (o2, l2) = res
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+POISON_CASES = [
+    dict(seed=141, dtype="bf16", decode=True, batch=4, block_x=1, num_heads_q=8, num_heads_kv=2),
+    dict(seed=142, dtype="f16", block_x=32, mask_mode=0),
+    dict(seed=143, dtype="fp8", batch=2, max_len=400, block_x=100, num_heads_q=2,
+         num_heads_kv=2, mask_mode=0),
+    dict(seed=144, dtype="f16", batch=2, max_len=400, block_x=40, num_heads_q=8,
+         num_heads_kv=1, mask_mode=0),
+]
+
+
+def _poison(t, dtype, rows_of):
+    """NaN (fp8: its NaN byte) into the given KV positions of every head."""
+    if dtype == "fp8":
+        u = t.view(torch.uint8)
+        for idx in rows_of:
+            u[idx] = 0x7F
+    else:
+        for idx in rows_of:
+            t[idx] = float("nan")
+
+
+@pytest.mark.parametrize("layout", ["PA_BBND", "TND"])
+@pytest.mark.parametrize("case", POISON_CASES, ids=[str(c["seed"]) for c in POISON_CASES])
+def test_keys_past_visible_length_never_reach_the_output(case, layout):
+    """NaN in every cached key/value row past seqused_kv (the page tails, or the TND storage
+    rows past seqused_kv) leaves the output equal to the oracle's, which never reads them."""
+    kw = dict(case)
+    seed = kw.pop("seed")
+    p = gi.random_problem(seed, device="cuda", mask_mode=kw.pop("mask_mode", 1), **kw)
+    if layout == "TND":
+        p = gi.to_tnd(p)
+        k, v = p.k.clone(), p.v.clone()
+        idx = []
+        for b in range(p.batch):
+            r0, r1 = int(p.cu_seqlens_kv[b]) + p.kv_len(b), int(p.cu_seqlens_kv[b + 1])
+            if r1 > r0:
+                idx.append(slice(r0, r1))
+    else:
+        k, v = p.k.clone(), p.v.clone()
+        idx = []
+        for b in range(p.batch):
+            skv = int(p.seqused_kv[b])
+            for j in range(skv // 128, (int(p.kv_storage[b]) + 127) // 128):
+                page = int(p.block_table[b, j])
+                idx.append((page, slice(max(skv - 128 * j, 0), 128)))
+    assert idx, "the case has no rows past the visible length"
+    _poison(k, p.dtype, idx)
+    _poison(v, p.dtype, idx)
+    pp = dataclasses.replace(p, k=k, v=v)
+    for P in (0, 7):
+        _full_check(pp, num_workers=P, label=f"poison{seed} {layout} P={P}")
+
+
 def test_metadata_mismatch_is_refused():
     p = gi.random_problem(123, device="cuda", mask_mode=1)
     gp = GpuProblem(p)
@@ -229,9 +332,11 @@ def test_metadata_mismatch_is_refused():
 # full-size workloads, sampled rows, benchmark launch configuration
 # ---------------------------------------------------------------------------
 
-def _sampled_check(cfg, units, rows_per_unit=None, seed=0):
-    _log(f"[parity] workload {cfg}: generating on the GPU")
+def _sampled_check(cfg, units, rows_per_unit=None, seed=0, tnd=False):
+    _log(f"[parity] workload {cfg}{' TND' if tnd else ''}: generating on the GPU")
     p = gi.config(cfg, device="cuda")
+    if tnd:
+        p = gi.to_tnd(p)
     gp = GpuProblem(p)
     params, meta, out, lse, ws = gp.run(0)
     assert int(ws[:4].view(torch.int32)[0].item()) == 0
@@ -278,3 +383,15 @@ def test_workload4_long_context_sampled():
 def test_workload5_dense_equivalent_fp8_sampled():
     units = [(0, 0), (0, 1), (0, 100), (1, 255), (1, 128)]
     _sampled_check(5, units, rows_per_unit=10)
+
+
+def test_workload2_decode_tnd_sampled():
+    _sampled_check(2, [(b, 0) for b in range(0, 64, 9)], tnd=True)
+
+
+def test_workload3_block_sparse_prefill_tnd_sampled():
+    _sampled_check(3, [(0, 0), (1, 64), (3, 255)], rows_per_unit=12, tnd=True)
+
+
+def test_workload5_dense_equivalent_fp8_tnd_sampled():
+    _sampled_check(5, [(0, 1), (1, 255)], rows_per_unit=10, tnd=True)

@@ -80,7 +80,12 @@ def test_visibility_golden():
 
 def _logical_kv(p, b, n2):
     """K, V of sequence b / head n2 as a contiguous float64 [skv, D] via torch indexing."""
-    skv = int(p.seqused_kv[b])
+    skv = p.kv_len(b)
+    if p.kv_layout == "TND":  # the sequence's own rows of the token-major tensor
+        r0 = int(p.cu_seqlens_kv[b])
+        k = dequant(p.k, p.dtype, p.k_scale, 1)[r0:r0 + skv, n2, :]
+        v = dequant(p.v, p.dtype, p.v_scale, 1)[r0:r0 + skv, n2, :]
+        return k, v
     nblk = -(-skv // 128)
     pages = torch.as_tensor(p.block_table[b, :nblk].astype(np.int64))
     k = dequant(p.k, p.dtype, p.k_scale, 2)[pages, :, n2, :].reshape(-1, 128)[:skv]
@@ -101,7 +106,7 @@ def _sdpa_reference(p):
         c0 = int(p.cu_seqlens_q[b])
         storage = int(p.cu_seqlens_q[b + 1]) - c0
         sq = storage if p.seqused_q is None else int(p.seqused_q[b])
-        skv = int(p.seqused_kv[b])
+        skv = p.kv_len(b)
         off = skv - sq
         for n2 in range(p.num_heads_kv):
             k, v = _logical_kv(p, b, n2)
@@ -157,6 +162,63 @@ def test_oracle_matches_sdpa(seed, kw):
     np.testing.assert_allclose(L[rows][fin], Lr[rows][fin], rtol=1e-12, atol=1e-12)
     # rows beyond seqused_q are not part of the output
     assert np.isnan(O[~rows]).all()
+
+
+@pytest.mark.parametrize("seed,kw,keep", [
+    (51, dict(mask_mode=1, use_seqused_q=True), True),
+    (52, dict(mask_mode=0, win_left=70, win_right=10, num_heads_q=8, num_heads_kv=2), True),
+    (53, dict(mask_mode=1, batch=3), False),
+    (54, dict(mask_mode=1, dtype="fp8", std=0.7), True),
+    (55, dict(mask_mode=1, dtype="bf16", decode=True, batch=4, block_x=1), True),
+])
+def test_tnd_oracle_matches_sdpa(seed, kw, keep):
+    """Token-major key/value: SDPA over each sequence's own rows, with seqused_kv below the
+    storage length (dual lengths) or without seqused_kv (keep=False)."""
+    p = gi.to_tnd(gi.random_problem(seed, **kw), keep_seqused_kv=keep)
+    assert p.cu_seqlens_kv[-1] == p.k.shape[0]
+    O, L, done = oa.sparse_attention(oracle_inputs(p))
+    Or, Lr = _sdpa_reference(p)
+    assert done.sum() > 0
+    np.testing.assert_allclose(O[done], Or[done], rtol=0, atol=1e-12)
+    fin = np.isfinite(Lr[done])
+    assert np.array_equal(fin, np.isfinite(L[done]))
+    np.testing.assert_allclose(L[done][fin], Lr[done][fin], rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("keep", [True, False])
+def test_tnd_equals_paged_bit_identical(keep):
+    """Layout independence: the same logical keys give bit-identical results."""
+    p = gi.random_problem(56, mask_mode=1, use_seqused_q=True, batch=3, extra_pages=4)
+    t = gi.to_tnd(p, keep_seqused_kv=keep, tail_rows=5)
+    O1, L1, _ = oa.sparse_attention(oracle_inputs(p))
+    O2, L2, _ = oa.sparse_attention(oracle_inputs(t))
+    assert np.array_equal(O1, O2, equal_nan=True) and np.array_equal(L1, L2, equal_nan=True)
+
+
+def test_tnd_rows_of_other_sequences_are_never_used():
+    """Poisoning every row outside [cu_kv[b], cu_kv[b] + kv_len[b]) changes nothing."""
+    p = gi.to_tnd(gi.random_problem(57, mask_mode=0, batch=3))
+    O1, L1, _ = oa.sparse_attention(oracle_inputs(p))
+    used = np.zeros(p.k.shape[0], dtype=bool)
+    for b in range(p.batch):
+        used[int(p.cu_seqlens_kv[b]):int(p.cu_seqlens_kv[b]) + p.kv_len(b)] = True
+    k, v = p.k.clone(), p.v.clone()
+    k[torch.as_tensor(~used)] = 1000.0
+    v[torch.as_tensor(~used)] = float("nan")
+    O2, L2, _ = oa.sparse_attention(oracle_inputs(_set(p, k=k, v=v)))
+    assert (~used).any()
+    assert np.array_equal(O1, O2, equal_nan=True) and np.array_equal(L1, L2, equal_nan=True)
+
+
+def test_tnd_seqused_kv_above_storage_reads_as_storage():
+    p = gi.to_tnd(gi.random_problem(58, mask_mode=1, batch=2))
+    st = np.diff(p.cu_seqlens_kv)
+    a = oa.sparse_attention(oracle_inputs(_set(p, seqused_kv=st.astype(np.int32))))
+    b = oa.sparse_attention(oracle_inputs(_set(p, seqused_kv=(st + 300).astype(np.int32))))
+    c = oa.sparse_attention(oracle_inputs(_set(p, seqused_kv=None)))
+    for x, y in ((a, b), (a, c)):
+        assert np.array_equal(x[0], y[0], equal_nan=True)
+        assert np.array_equal(x[1], y[1], equal_nan=True)
 
 
 def test_all_causal_blocks_equal_dense_causal():

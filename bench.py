@@ -219,6 +219,10 @@ def main(argv=None):
     ap.add_argument("--config", type=int, default=2, help="workload id 1..5 (default 2)")
     ap.add_argument("--kv-layout", choices=["pa_bbnd", "tnd"], default="pa_bbnd",
                     help="key/value layout: paged (default) or token-major TND")
+    ap.add_argument("--user-mask", choices=["none", "causal"], default="none",
+                    help="causal: replace the built-in causal mask of a causal workload with an "
+                         "equal user attention mask (same visible keys, timed through the "
+                         "per-element mask path)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -234,9 +238,9 @@ def main(argv=None):
     import torch
 
     import gbsa_inputs as gi
-    from block_sparse_paged_gbsa_amd import (gbsa_forward, gbsa_forward_tnd, gbsa_metadata,
-                                             gbsa_num_workers, gbsa_workspace_size,
-                                             make_params)
+    from block_sparse_paged_gbsa_amd import (gbsa_forward, gbsa_forward_ex, gbsa_forward_tnd,
+                                             gbsa_metadata, gbsa_num_workers,
+                                             gbsa_workspace_size, make_params)
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
@@ -247,6 +251,24 @@ def main(argv=None):
         log("[bench] rewriting key/value into the token-major TND layout")
         p = gi.to_tnd(p)
         torch.cuda.empty_cache()
+    umask = None
+    if a.user_mask == "causal":
+        offs = {p.kv_len(b) - (int(p.seqused_q[b]) if p.seqused_q is not None
+                               else int(p.cu_seqlens_q[b + 1] - p.cu_seqlens_q[b]))
+                for b in range(p.batch)}
+        if p.mask_mode != 1 or p.win_left >= 0 or p.win_right >= 0 or len(offs) != 1:
+            print("--user-mask causal needs a causal workload without a window whose "
+                  "sequences share one diagonal (workloads 3 and 5)", file=sys.stderr)
+            return 2
+        off = offs.pop()
+        rows = int((p.cu_seqlens_q[1:] - p.cu_seqlens_q[:-1]).max())
+        cols = max(p.kv_len(b) for b in range(p.batch))
+        log(f"[bench] user mask [{rows}, {cols}] uint8 equal to the causal mask")
+        t_idx = torch.arange(rows, device=dev, dtype=torch.int32)[:, None]
+        p_idx = torch.arange(cols, device=dev, dtype=torch.int32)[None, :]
+        umask = (p_idx > t_idx + off).to(torch.uint8)
+        del t_idx, p_idx
+        p.mask_mode = 0
     params = make_params(batch=p.batch, num_heads_q=p.num_heads_q, num_heads_kv=p.num_heads_kv,
                          total_q=p.total_q, total_q_blocks=p.total_q_blocks, top_k=p.top_k,
                          block_x=p.block_x,
@@ -272,7 +294,12 @@ def main(argv=None):
     P = gbsa_num_workers(params)
 
     def forward():
-        if tnd:
+        if umask is not None:
+            gbsa_forward_ex(params, p.q, p.k, p.v, idx, cnt, meta, cu, squ,
+                            cu_seqlens_kv=cu_kv, seqused_kv=skv, block_table=table, q_scale=qs,
+                            k_scale=ks, v_scale=vs, atten_mask=umask, out=out, lse=lse,
+                            workspace=ws)
+        elif tnd:
             gbsa_forward_tnd(params, p.q, p.k, p.v, idx, cnt, meta, cu, squ, cu_kv, skv, qs,
                              ks, vs, None, out, lse, ws)
         else:
@@ -325,7 +352,8 @@ def main(argv=None):
     kernel = ("fwd_decode_kernel" if rows <= 16 else
               "fwd_prefill_pp32_kernel" if rows > 256 else
               "fwd_prefill_ks32_kernel" if rows > 64 else "fwd_prefill_kernel")
-    workload = gi.CONFIG_NAMES[a.config] + ("_tnd" if tnd else "")
+    workload = (gi.CONFIG_NAMES[a.config] + ("_tnd" if tnd else "") +
+                ("_user_mask" if umask is not None else ""))
     traffic = measured_traffic(kernel, workload)
     if hbm_bound:
         achieved = alg_bytes / (fwd_ms * 1e-3) / 1e9
@@ -340,7 +368,7 @@ def main(argv=None):
         metric_value, unit = tflops, "TFLOP/s"
 
     cpu = None
-    if a.cpu_budget > 0:
+    if a.cpu_budget > 0 and umask is None:
         log("[bench] timing the float64 oracle on a sample")
         cb = cpu_baseline(p, a.cpu_budget)
         v = (cb["bytes"] / cb["seconds"] / 1e9) if hbm_bound else (cb["flops"] / cb["seconds"] / 1e12)
@@ -353,6 +381,8 @@ def main(argv=None):
         "warmup": a.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": p.dtype, "data": "synthetic",
         "config": {"workload": workload, "kv_layout": "TND" if tnd else "PA_BBND",
+                   "mask": "user (causal pattern)" if umask is not None else
+                           {0: "none", 1: "causal", 2: "causal top-left"}[p.mask_mode],
                    "batch": p.batch,
                    "num_heads_q": p.num_heads_q, "num_heads_kv": p.num_heads_kv,
                    "head_dim": 128, "block_shape": [p.block_x, 128], "top_k": p.top_k,

@@ -9,6 +9,7 @@ from .api import (  # noqa: F401
     gbsa_check_params,
     gbsa_forward,
     gbsa_forward_tnd,
+    gbsa_forward_ex,
     gbsa_metadata,
     gbsa_num_workers,
     gbsa_workspace_size,

@@ -29,7 +29,8 @@ KV_PA_BBND, KV_TND = 0, 1
 MAX_KV_ROWS = 2147483520
 
 EXPORTED = ("gbsa_check_params", "gbsa_num_workers", "gbsa_metadata", "gbsa_workspace_size",
-            "gbsa_forward", "gbsa_forward_tnd", "gbsa_status_string")
+            "gbsa_forward", "gbsa_forward_tnd", "gbsa_forward_ex", "gbsa_status_string")
+MASK_NONE, MASK_CAUSAL, MASK_CAUSAL_TOP_LEFT = 0, 1, 2
 
 
 class GbsaParams(ctypes.Structure):
@@ -61,6 +62,37 @@ class GbsaParams(ctypes.Structure):
         ("num_workers", ctypes.c_int32),
         ("kv_layout", ctypes.c_int32),
         ("reserved", ctypes.c_int32 * 3),
+    ]
+
+
+class GbsaForwardArgs(ctypes.Structure):
+    """gbsa_forward_args: every tensor of the main call (device pointers), the user mask's
+    geometry, the workspace."""
+    _fields_ = [
+        ("query", ctypes.c_void_p),
+        ("key", ctypes.c_void_p),
+        ("value", ctypes.c_void_p),
+        ("sparse_block_idx", ctypes.c_void_p),
+        ("sparse_block_count", ctypes.c_void_p),
+        ("metadata", ctypes.c_void_p),
+        ("cu_seqlens_q", ctypes.c_void_p),
+        ("seqused_q", ctypes.c_void_p),
+        ("cu_seqlens_kv", ctypes.c_void_p),
+        ("seqused_kv", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p),
+        ("q_scale", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p),
+        ("p_scale", ctypes.c_void_p),
+        ("atten_mask", ctypes.c_void_p),
+        ("mask_batch_stride", ctypes.c_int64),
+        ("mask_row_stride", ctypes.c_int64),
+        ("mask_rows", ctypes.c_int32),
+        ("mask_cols", ctypes.c_int32),
+        ("attention_out", ctypes.c_void_p),
+        ("softmax_lse", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
     ]
 
 
@@ -96,6 +128,8 @@ def load() -> ctypes.CDLL:
     lib.gbsa_forward.restype = ctypes.c_int
     lib.gbsa_forward_tnd.argtypes = [P] + [vp] * 17 + [ctypes.c_size_t, vp]
     lib.gbsa_forward_tnd.restype = ctypes.c_int
+    lib.gbsa_forward_ex.argtypes = [P, ctypes.POINTER(GbsaForwardArgs), vp]
+    lib.gbsa_forward_ex.restype = ctypes.c_int
     lib.gbsa_status_string.argtypes = [ctypes.c_int]
     lib.gbsa_status_string.restype = ctypes.c_char_p
     _lib = lib

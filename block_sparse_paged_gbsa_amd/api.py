@@ -191,6 +191,79 @@ def gbsa_forward_tnd(params: GbsaParams, q, k, v, sparse_block_idx, sparse_block
     return out, lse, workspace
 
 
+def _mask_geometry(atten_mask: torch.Tensor):
+    """(batch stride, row stride, rows, cols) of a uint8 or bool mask [rows, cols] or
+    [B, rows, cols] whose last axis is dense."""
+    if atten_mask.dtype not in (torch.uint8, torch.bool):
+        raise ValueError("atten_mask must be uint8 or bool")
+    if atten_mask.dim() not in (2, 3) or atten_mask.stride(-1) != 1:
+        raise ValueError("atten_mask must be [rows, cols] or [B, rows, cols] with dense rows")
+    rows, cols = atten_mask.shape[-2], atten_mask.shape[-1]
+    bstride = 0 if atten_mask.dim() == 2 else atten_mask.stride(0)
+    return bstride, atten_mask.stride(-2), rows, cols
+
+
+def aligned_mask(atten_mask: torch.Tensor) -> torch.Tensor:
+    """A copy of the mask as uint8 with its row stride padded to a multiple of 4 (the layout
+    gbsa_forward_ex requires), or the mask itself when it already qualifies."""
+    m = atten_mask.view(torch.uint8) if atten_mask.dtype == torch.bool else atten_mask
+    bs, rs, rows, cols = _mask_geometry(m)
+    if rs % 4 == 0 and bs % 4 == 0 and m.data_ptr() % 4 == 0:
+        return m
+    stride = -(-max(cols, 1) // 4) * 4
+    shape = m.shape[:-1] + (stride,)
+    out = torch.zeros(shape, dtype=torch.uint8, device=m.device)
+    out[..., :cols] = m
+    return out[..., :cols]
+
+
+def gbsa_forward_ex(params: GbsaParams, q, k, v, sparse_block_idx, sparse_block_count,
+                    metadata, cu_seqlens_q, seqused_q=None, *, cu_seqlens_kv=None,
+                    seqused_kv=None, block_table=None, q_scale=None, k_scale=None,
+                    v_scale=None, p_scale=None, atten_mask=None, out=None, lse=None,
+                    workspace=None, stream=None
+                    ) -> Tuple[torch.Tensor, Optional[torch.Tensor], torch.Tensor]:
+    """Either key/value layout (params.kv_layout) with an optional user attention mask
+    (uint8 or bool [rows, cols] or [B, rows, cols], nonzero = masked out; rows must be dense
+    and 4-byte aligned, see aligned_mask). Returns (attention_out, softmax_lse or None,
+    workspace)."""
+    _need(q, "query")
+    _need(sparse_block_idx, "sparse_block_idx", torch.int32)
+    _need(sparse_block_count, "sparse_block_count", torch.int32)
+    if out is None:
+        out = torch.empty(q.shape, dtype=_CODE_DTYPE[params.out_dtype], device=q.device)
+    if lse is None and params.return_lse:
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.zeros(gbsa_workspace_size(params), dtype=torch.uint8, device=q.device)
+    g = _lib.GbsaForwardArgs()
+    g.query, g.key, g.value = q.data_ptr(), k.data_ptr(), v.data_ptr()
+    ptr = lambda t: None if t is None else t.data_ptr()
+    g.sparse_block_idx = ptr(sparse_block_idx)
+    g.sparse_block_count = ptr(sparse_block_count)
+    g.metadata = ptr(metadata)
+    g.cu_seqlens_q = ptr(cu_seqlens_q)
+    g.seqused_q = ptr(seqused_q)
+    g.cu_seqlens_kv = ptr(cu_seqlens_kv)
+    g.seqused_kv = ptr(seqused_kv)
+    g.block_table = ptr(block_table)
+    g.q_scale, g.k_scale, g.v_scale, g.p_scale = (ptr(q_scale), ptr(k_scale), ptr(v_scale),
+                                                  ptr(p_scale))
+    if atten_mask is not None:
+        _need(atten_mask, "atten_mask", contiguous=False)
+        m = atten_mask.view(torch.uint8) if atten_mask.dtype == torch.bool else atten_mask
+        bs, rs, rows, cols = _mask_geometry(m)
+        g.atten_mask = m.data_ptr()
+        g.mask_batch_stride, g.mask_row_stride, g.mask_rows, g.mask_cols = bs, rs, rows, cols
+    g.attention_out = out.data_ptr()
+    g.softmax_lse = ptr(lse)
+    g.workspace = workspace.data_ptr()
+    g.workspace_bytes = workspace.numel()
+    check("gbsa_forward_ex", _lib.load().gbsa_forward_ex(ctypes.byref(params), ctypes.byref(g),
+                                                         _stream(stream)))
+    return out, lse, workspace
+
+
 def workspace_status(workspace: torch.Tensor) -> int:
     """Word 0 of the workspace: non-zero after a metadata/parameter mismatch (sticky)."""
     return int(workspace[:4].view(torch.int32)[0].item())
@@ -252,9 +325,12 @@ def generic_block_sparse_attention(
         layout_kv="PA_BBND", softmax_scale=0.0, mask_mode=1, quant_mode=0, dst_type_max=0.0,
         softmax_precision=1, win_left=-1, win_right=-1, return_softmax_lse=False,
         attention_out_dtype=None, num_workers: int = 0):
-    """Returns (attention_out, softmax_lse) with softmax_lse of shape (T, N1, 1) or empty."""
-    if attn_mask is not None:
-        raise ValueError("attn_mask must be None (only the built-in mask modes are supported)")
+    """Returns (attention_out, softmax_lse) with softmax_lse of shape (T, N1, 1) or empty.
+
+    attn_mask: optional uint8/bool [rows, cols] (shared by all sequences) or [B, rows, cols];
+    a nonzero entry (t, p) removes key position p for the batch-local query row t, on top of
+    mask_mode (0 none, 1 causal bottom-right, 2 causal top-left) and the window.
+    """
     if dst_type_max != 0.0:
         raise ValueError("dst_type_max must be 0.0")
     if metadata is None:
@@ -275,7 +351,22 @@ def generic_block_sparse_attention(
             raise ValueError("attention_out_dtype is required when quant_mode != 0")
         out_dtype = attention_out_dtype
     squ = None if seqused_q is None else seqused_q.contiguous()
-    if tnd:
+    if attn_mask is not None:
+        p = make_params(total_q=q.shape[0],
+                        max_blocks_per_seq=0 if tnd else block_table.shape[1],
+                        num_pages=k.shape[0], kv_page_stride=0 if tnd else k.stride(0),
+                        dtype=q.dtype, out_dtype=out_dtype, return_lse=return_softmax_lse,
+                        scale=float(softmax_scale), num_workers=num_workers, **c)
+        out, lse, _ = gbsa_forward_ex(
+            p, q.contiguous(), k.contiguous() if tnd else k, v.contiguous() if tnd else v,
+            sparse_block_idx.contiguous(), sparse_block_count.contiguous(), metadata,
+            cu_seqlens_q.contiguous(), squ,
+            cu_seqlens_kv=cu_seqlens_kv.contiguous() if tnd else None,
+            seqused_kv=None if seqused_kv is None else seqused_kv.contiguous(),
+            block_table=None if tnd else block_table.contiguous(), q_scale=q_dequant_scale,
+            k_scale=k_dequant_scale, v_scale=v_dequant_scale, p_scale=p_quant_scale,
+            atten_mask=aligned_mask(attn_mask))
+    elif tnd:
         p = make_params(total_q=q.shape[0], max_blocks_per_seq=0, num_pages=k.shape[0],
                         dtype=q.dtype, out_dtype=out_dtype, return_lse=return_softmax_lse,
                         scale=float(softmax_scale), num_workers=num_workers, **c)

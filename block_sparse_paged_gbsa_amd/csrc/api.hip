@@ -127,7 +127,8 @@ gbsa_status gbsa_check_params(const gbsa_params* p) {
         if (p->dtype == GBSA_DTYPE_FP8_E4M3) return GBSA_ERR_DTYPE;
         if (p->out_dtype != p->dtype) return GBSA_ERR_DTYPE;
     }
-    if (p->mask_mode != GBSA_MASK_NONE && p->mask_mode != GBSA_MASK_CAUSAL)
+    if (p->mask_mode != GBSA_MASK_NONE && p->mask_mode != GBSA_MASK_CAUSAL &&
+        p->mask_mode != GBSA_MASK_CAUSAL_TOP_LEFT)
         return GBSA_ERR_UNSUPPORTED;
     if (p->softmax_precision != 0 && p->softmax_precision != 1) return GBSA_ERR_UNSUPPORTED;
     if (p->is_packed_gqa != 1) return GBSA_ERR_UNSUPPORTED;
@@ -198,15 +199,27 @@ gbsa_status gbsa_metadata(const gbsa_params* p, const int32_t* sparse_block_coun
     return launch_metadata(a, stream) == hipSuccess ? GBSA_OK : GBSA_ERR_HIP;
 }
 
-static gbsa_status forward_impl(const gbsa_params* p, const void* query, const void* key,
-                                const void* value, const int32_t* sparse_block_idx,
-                                const int32_t* sparse_block_count, const int32_t* metadata,
-                                const int64_t* cu_seqlens_q, const int32_t* seqused_q,
-                                const int32_t* seqused_kv, const int32_t* block_table,
-                                const int64_t* cu_seqlens_kv, const float* q_scale,
-                                const float* k_scale, const float* v_scale, const float* p_scale,
-                                void* attention_out, float* softmax_lse, void* workspace,
-                                size_t workspace_bytes, hipStream_t stream) {
+static gbsa_status forward_impl(const gbsa_params* p, const gbsa_forward_args* g,
+                                hipStream_t stream) {
+    const void* query = g->query;
+    const void* key = g->key;
+    const void* value = g->value;
+    const int32_t* sparse_block_idx = g->sparse_block_idx;
+    const int32_t* sparse_block_count = g->sparse_block_count;
+    const int32_t* metadata = g->metadata;
+    const int64_t* cu_seqlens_q = g->cu_seqlens_q;
+    const int32_t* seqused_q = g->seqused_q;
+    const int32_t* seqused_kv = g->seqused_kv;
+    const int32_t* block_table = g->block_table;
+    const int64_t* cu_seqlens_kv = g->cu_seqlens_kv;
+    const float* q_scale = g->q_scale;
+    const float* k_scale = g->k_scale;
+    const float* v_scale = g->v_scale;
+    const float* p_scale = g->p_scale;
+    void* attention_out = g->attention_out;
+    float* softmax_lse = g->softmax_lse;
+    void* workspace = g->workspace;
+    const size_t workspace_bytes = g->workspace_bytes;
     gbsa_status st = gbsa_check_params(p);
     if (st != GBSA_OK) return st;
     const bool tnd = p->kv_layout == GBSA_KV_TND;
@@ -224,6 +237,13 @@ static gbsa_status forward_impl(const gbsa_params* p, const void* query, const v
     if (!quant && (q_scale != nullptr || k_scale != nullptr || v_scale != nullptr))
         return GBSA_ERR_DTYPE;
     if (p_scale != nullptr) return GBSA_ERR_UNSUPPORTED;
+    if (g->atten_mask != nullptr) {
+        const int64_t rs = g->mask_row_stride, bs = g->mask_batch_stride;
+        if (((uintptr_t)g->atten_mask & 3) != 0 || g->mask_rows < 0 || g->mask_cols < 0 ||
+            rs < g->mask_cols || rs % 4 != 0 || bs < 0 || bs % 4 != 0 ||
+            (int64_t)g->mask_rows * rs > 0x7fffffff)
+            return GBSA_ERR_SHAPE;
+    }
     int P = 0;
     st = plan_workers(p, &P);
     if (st != GBSA_OK) return st;
@@ -248,6 +268,13 @@ static gbsa_status forward_impl(const gbsa_params* p, const void* query, const v
     a.ks = k_scale;
     a.vs = v_scale;
     a.out = attention_out;
+    if (g->atten_mask != nullptr) {
+        a.umask = g->atten_mask;
+        a.um_bstride = g->mask_batch_stride;
+        a.um_rstride = (int32_t)g->mask_row_stride;
+        a.um_rows = g->mask_rows;
+        a.um_cols = g->mask_cols;
+    }
     a.lse = softmax_lse;
     unsigned char* ws = (unsigned char*)workspace;
     a.ws_status = (int32_t*)(ws + L.status);
@@ -303,10 +330,27 @@ gbsa_status gbsa_forward(const gbsa_params* p, const void* query, const void* ke
     gbsa_status st = gbsa_check_params(p);
     if (st != GBSA_OK) return st;
     if (p->kv_layout != GBSA_KV_PA_BBND) return GBSA_ERR_UNSUPPORTED;
-    return forward_impl(p, query, key, value, sparse_block_idx, sparse_block_count, metadata,
-                        cu_seqlens_q, seqused_q, seqused_kv, block_table, nullptr, q_scale,
-                        k_scale, v_scale, p_scale, attention_out, softmax_lse, workspace,
-                        workspace_bytes, stream);
+    gbsa_forward_args g;
+    memset(&g, 0, sizeof(g));
+    g.query = query;
+    g.key = key;
+    g.value = value;
+    g.sparse_block_idx = sparse_block_idx;
+    g.sparse_block_count = sparse_block_count;
+    g.metadata = metadata;
+    g.cu_seqlens_q = cu_seqlens_q;
+    g.seqused_q = seqused_q;
+    g.seqused_kv = seqused_kv;
+    g.block_table = block_table;
+    g.q_scale = q_scale;
+    g.k_scale = k_scale;
+    g.v_scale = v_scale;
+    g.p_scale = p_scale;
+    g.attention_out = attention_out;
+    g.softmax_lse = softmax_lse;
+    g.workspace = workspace;
+    g.workspace_bytes = workspace_bytes;
+    return forward_impl(p, &g, stream);
 }
 
 gbsa_status gbsa_forward_tnd(const gbsa_params* p, const void* query, const void* key,
@@ -320,10 +364,39 @@ gbsa_status gbsa_forward_tnd(const gbsa_params* p, const void* query, const void
     gbsa_status st = gbsa_check_params(p);
     if (st != GBSA_OK) return st;
     if (p->kv_layout != GBSA_KV_TND) return GBSA_ERR_UNSUPPORTED;
-    return forward_impl(p, query, key, value, sparse_block_idx, sparse_block_count, metadata,
-                        cu_seqlens_q, seqused_q, seqused_kv, nullptr, cu_seqlens_kv, q_scale,
-                        k_scale, v_scale, p_scale, attention_out, softmax_lse, workspace,
-                        workspace_bytes, stream);
+    gbsa_forward_args g;
+    memset(&g, 0, sizeof(g));
+    g.query = query;
+    g.key = key;
+    g.value = value;
+    g.sparse_block_idx = sparse_block_idx;
+    g.sparse_block_count = sparse_block_count;
+    g.metadata = metadata;
+    g.cu_seqlens_q = cu_seqlens_q;
+    g.seqused_q = seqused_q;
+    g.cu_seqlens_kv = cu_seqlens_kv;
+    g.seqused_kv = seqused_kv;
+    g.q_scale = q_scale;
+    g.k_scale = k_scale;
+    g.v_scale = v_scale;
+    g.p_scale = p_scale;
+    g.attention_out = attention_out;
+    g.softmax_lse = softmax_lse;
+    g.workspace = workspace;
+    g.workspace_bytes = workspace_bytes;
+    return forward_impl(p, &g, stream);
+}
+
+gbsa_status gbsa_forward_ex(const gbsa_params* p, const gbsa_forward_args* args,
+                            hipStream_t stream) {
+    gbsa_status st = gbsa_check_params(p);
+    if (st != GBSA_OK) return st;
+    if (args == nullptr) return GBSA_ERR_NULL;
+    // the layout not in use takes no tensors
+    if (p->kv_layout == GBSA_KV_TND ? args->block_table != nullptr
+                                    : args->cu_seqlens_kv != nullptr)
+        return GBSA_ERR_NULL;
+    return forward_impl(p, args, stream);
 }
 
 const char* gbsa_status_string(gbsa_status s) {

@@ -312,11 +312,11 @@ __device__ __forceinline__ int block_class(const FwdArgs& a, int64_t p0, int skv
     const int64_t p1 = p0 + 127;
     const int64_t dlo = (int64_t)t_lo + off, dhi = (int64_t)t_hi + off;
     if (p0 >= skv) return 0;
-    if (a.mask == 1 && p0 > dhi) return 0;
+    if (a.mask != 0 && p0 > dhi) return 0;
     if (a.wl >= 0 && p1 < dlo - a.wl) return 0;
     if (a.wr >= 0 && p0 > dhi + a.wr) return 0;
     bool full = p1 < skv;
-    if (a.mask == 1) full = full && (p1 <= dlo);
+    if (a.mask != 0) full = full && (p1 <= dlo);
     if (a.wl >= 0) full = full && (p0 >= dhi - a.wl);
     if (a.wr >= 0) full = full && (p1 <= dlo + a.wr);
     return full ? 1 : 2;
@@ -324,10 +324,41 @@ __device__ __forceinline__ int block_class(const FwdArgs& a, int64_t p0, int skv
 
 __device__ __forceinline__ bool key_visible(const FwdArgs& a, int64_t p, int skv, int64_t d) {
     bool ok = p < skv;
-    if (a.mask == 1) ok = ok && (p <= d);
+    if (a.mask != 0) ok = ok && (p <= d);
     if (a.wl >= 0) ok = ok && (p >= d - a.wl);
     if (a.wr >= 0) ok = ok && (p <= d + a.wr);
     return ok;
+}
+
+// Offset of the causal diagonal: bottom-right (off = kv length - query length) for mask modes
+// 0 and 1, top-left (off = 0) for mode 2. Windows are relative to the same diagonal.
+__device__ __forceinline__ int diag_off(const FwdArgs& a, int skv, int sq) {
+    return a.mask == 2 ? 0 : skv - sq;
+}
+
+// ---------------------------------------------------------------------------
+// User attention mask: uint8, nonzero = the key is masked out for that query row, indexed by
+// the batch-local query row t and the key position p; one [rows, cols] array per sequence or
+// one shared by all. Entries outside the extent do not mask.
+// ---------------------------------------------------------------------------
+struct UMaskRow {
+    rsrc_t r;  // the sequence's mask, records = rows x row stride
+    int roff;  // byte offset of this lane's row, or -1 (no row, or a row past the extent)
+};
+__device__ __forceinline__ UMaskRow umask_row(const FwdArgs& a, int b, int t, bool valid) {
+    UMaskRow m;
+    m.r = make_rsrc(a.umask + (int64_t)b * a.um_bstride, a.um_rows * a.um_rstride);
+    m.roff = (valid && t < a.um_rows) ? t * a.um_rstride : -1;
+    return m;
+}
+// Mask bytes of keys p .. p + 3 (p a multiple of 4) in this lane's row, 0 for a visible key.
+__device__ __forceinline__ uint32_t umask_word(const FwdArgs& a, const UMaskRow& m, int64_t p) {
+    const bool in = m.roff >= 0 && p < a.um_cols;
+    const int voff = in ? m.roff + (int)p : 0x7fffffff;  // past the records: reads 0
+    uint32_t w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(m.r, voff, 0, 0));
+    const int64_t n = (int64_t)a.um_cols - p;  // keys of the group inside the extent
+    if (n < 4) w &= (n <= 0) ? 0u : (0xffffffffu >> (32 - 8 * (int)n));
+    return w;
 }
 
 // Visible key positions of query row d = t + off inside the block starting at p0, as an
@@ -335,7 +366,7 @@ __device__ __forceinline__ bool key_visible(const FwdArgs& a, int64_t p, int skv
 __device__ __forceinline__ void key_range(const FwdArgs& a, int64_t p0, int skv, int64_t d,
                                           int* lo, int* hi) {
     int64_t l = 0, h = (int64_t)skv - 1;
-    if (a.mask == 1) h = min(h, d);
+    if (a.mask != 0) h = min(h, d);
     if (a.wl >= 0) l = max(l, d - a.wl);
     if (a.wr >= 0) h = min(h, d + a.wr);
     l -= p0;

@@ -74,11 +74,12 @@ __device__ __forceinline__ void wave_sync_lds() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int DT>
+template <int DT, bool UM>
 __device__ __forceinline__ void compute_quarter(const FwdArgs& a, const Quarter& qt,
                                                 const u32x4 (&qf)[4], const u32x2 (&q8)[4],
                                                 float cs, int64_t p0, int cls, int skv, int64_t d,
-                                                unsigned char* stage, int lane, WaveState& st) {
+                                                const UMaskRow& um, unsigned char* stage,
+                                                int lane, WaveState& st) {
     constexpr int PT = (DT == kF16) ? kF16 : kBF16;
     constexpr int KP = KPitch<DT>::value;
     const int lrow = lane & 15, lgrp = lane >> 4;
@@ -129,6 +130,15 @@ __device__ __forceinline__ void compute_quarter(const FwdArgs& a, const Quarter&
             for (int i = 0; i < 4; ++i)
                 if (!key_visible(a, p0 + tt * 16 + lgrp * 4 + i, skv, d)) sacc[tt][i] = kNegInf;
     }
+    if constexpr (UM) {  // the user mask applies to every visible block
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const uint32_t w = umask_word(a, um, p0 + tt * 16 + lgrp * 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if ((w >> (8 * i)) & 0xffu) sacc[tt][i] = kNegInf;
+        }
+    }
     float mx = kNegInf;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
@@ -169,7 +179,7 @@ __device__ __forceinline__ void compute_quarter(const FwdArgs& a, const Quarter&
     wave_sync_lds();
 }
 
-template <int DT, int OUT, int LAYOUT>
+template <int DT, int OUT, int LAYOUT, bool UM>
 __global__ __launch_bounds__(256, 2) void fwd_decode_kernel(FwdArgs a) {
     __shared__ __attribute__((aligned(16))) unsigned char smem[Lds<DT>::bytes];
     __shared__ int flag[1];
@@ -206,11 +216,13 @@ __global__ __launch_bounds__(256, 2) void fwd_decode_kernel(FwdArgs a) {
         const int rows_exist = min(a.X, it.storage - t0) * a.G;
         const KvSeq kv = kv_seq<LAYOUT>(a, it.b);
         const int skv = kv.len;
-        const int off = skv - it.sq;
+        const int off = diag_off(a, skv, it.sq);
 
         // Q as the B operand: column = query row (lane & 15), k = head dim.
         const bool exists = lrow < rows_exist;
         const int t = t0 + (exists ? lrow / a.G : 0);
+        const UMaskRow um =
+            UM ? umask_row(a, it.b, t, exists) : UMaskRow{make_rsrc(nullptr, 0), -1};
         const int h = it.n2 * a.G + (exists ? lrow % a.G : 0);
         float cs = a.scale_log2;
         if constexpr (DT == kFP8) cs *= a.qs[h] * a.ks[it.n2];
@@ -280,8 +292,8 @@ __global__ __launch_bounds__(256, 2) void fwd_decode_kernel(FwdArgs a) {
                 {
                     const int jc = __builtin_amdgcn_readlane(jcl, ia);
                     const int j = jc >> 2, cls = jc & 3;
-                    compute_quarter<DT>(a, qa, qf, q8, cs, (int64_t)j * 128 + wave * 32, cls, skv,
-                                        dpos, stage, lane, st);
+                    compute_quarter<DT, UM>(a, qa, qf, q8, cs, (int64_t)j * 128 + wave * 32, cls,
+                                            skv, dpos, um, stage, lane, st);
                 }
                 if (ib < 0) break;
                 ia = -1;
@@ -293,8 +305,8 @@ __global__ __launch_bounds__(256, 2) void fwd_decode_kernel(FwdArgs a) {
                 {
                     const int jc = __builtin_amdgcn_readlane(jcl, ib);
                     const int j = jc >> 2, cls = jc & 3;
-                    compute_quarter<DT>(a, qb, qf, q8, cs, (int64_t)j * 128 + wave * 32, cls, skv,
-                                        dpos, stage, lane, st);
+                    compute_quarter<DT, UM>(a, qb, qf, q8, cs, (int64_t)j * 128 + wave * 32, cls,
+                                            skv, dpos, um, stage, lane, st);
                 }
                 if (ia < 0) break;
             }
@@ -375,11 +387,20 @@ __global__ __launch_bounds__(256, 2) void fwd_decode_kernel(FwdArgs a) {
 
 template <int DT, int OUT>
 hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
-    // the layout is a template argument: a run-time one costs the paged path a spill
-    if (a.cu_kv != nullptr)
-        hipLaunchKernelGGL((fwd_decode_kernel<DT, OUT, kTnd>), dim3(a.P), dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL((fwd_decode_kernel<DT, OUT, kPaged>), dim3(a.P), dim3(256), 0, s, a);
+    // the layout and the user mask are template arguments: run-time ones cost the plain paged
+    // path registers
+    const dim3 g(a.P), b(256);
+    const bool tnd = a.cu_kv != nullptr;
+    if (a.umask != nullptr) {
+        if (tnd)
+            hipLaunchKernelGGL((fwd_decode_kernel<DT, OUT, kTnd, true>), g, b, 0, s, a);
+        else
+            hipLaunchKernelGGL((fwd_decode_kernel<DT, OUT, kPaged, true>), g, b, 0, s, a);
+    } else if (tnd) {
+        hipLaunchKernelGGL((fwd_decode_kernel<DT, OUT, kTnd, false>), g, b, 0, s, a);
+    } else {
+        hipLaunchKernelGGL((fwd_decode_kernel<DT, OUT, kPaged, false>), g, b, 0, s, a);
+    }
     return hipGetLastError();
 }
 

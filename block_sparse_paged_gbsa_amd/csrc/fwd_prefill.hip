@@ -136,9 +136,10 @@ __device__ __forceinline__ void qk_tile(const unsigned char* ks, const QTile<NQ>
 }
 
 // Mask (when needed) and the running-max update of one half page; returns the max to use.
-template <int NQ>
-__device__ __forceinline__ void half_max(f32x4 (&s)[4][NQ], int half, int cls, const int (&vlo)[NQ],
-                                         const int (&vhi)[NQ], const float (&colscale)[NQ],
+template <int NQ, bool UM>
+__device__ __forceinline__ void half_max(const FwdArgs& a, f32x4 (&s)[4][NQ], int half, int cls,
+                                         const int (&vlo)[NQ], const int (&vhi)[NQ], int64_t p0,
+                                         const UMaskRow (&um)[NQ], const float (&colscale)[NQ],
                                          int lgrp, float (&mrun)[NQ], float (&muse)[NQ],
                                          float (&alpha)[NQ]) {
     if (cls == 2) {
@@ -151,6 +152,17 @@ __device__ __forceinline__ void half_max(f32x4 (&s)[4][NQ], int half, int cls, c
                     const int rel = half * 64 + tt * 16 + lgrp * 4 + i;
                     if (rel < vlo[nq] || rel > vhi[nq]) s[tt][nq][i] = kNegInf;
                 }
+    }
+    if constexpr (UM) {  // the user mask applies to every visible block
+#pragma unroll
+        for (int nq = 0; nq < NQ; ++nq)
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                const uint32_t w = umask_word(a, um[nq], p0 + half * 64 + tt * 16 + lgrp * 4);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if ((w >> (8 * i)) & 0xffu) s[tt][nq][i] = kNegInf;
+            }
     }
 #pragma unroll
     for (int nq = 0; nq < NQ; ++nq) {
@@ -235,11 +247,12 @@ struct PageMid {
 //   part A: QK(h0); [QK(h1) | exp(h0)]      part B: [PV(h0) | exp(h1)]; PV(h1)
 // The caller moves the next page's K (between the parts) and V (after part B) into the other
 // LDS buffer, so only one tensor's share is held in registers at a time.
-template <int DT, int NQ>
+template <int DT, int NQ, bool UM>
 __device__ __forceinline__ void page_part_a(const FwdArgs& a, const unsigned char* stage,
                                             const QTile<NQ>& qt, const float (&colscale)[NQ],
-                                            const int (&trow)[NQ], int j, int cls, int skv,
-                                            int off, int lane, float (&mrun)[NQ],
+                                            const int (&trow)[NQ], const UMaskRow (&um)[NQ],
+                                            int j, int cls, int skv, int off, int lane,
+                                            float (&mrun)[NQ],
                                             float (&lrun)[NQ], f32x4 (&o)[8][NQ],
                                             PageMid<NQ>& mid) {
     constexpr int PT = (DT == kF16) ? kF16 : kBF16;
@@ -258,7 +271,8 @@ __device__ __forceinline__ void page_part_a(const FwdArgs& a, const unsigned cha
         qk_tile<DT, NQ>(ks, qt, tt * 16 + lrow, lgrp, s0[tt]);
         __builtin_amdgcn_sched_barrier(0);
     }
-    half_max<NQ>(s0, 0, cls, vlo, vhi, colscale, lgrp, mrun, mid.muse, mid.alpha);
+    half_max<NQ, UM>(a, s0, 0, cls, vlo, vhi, (int64_t)j * 128, um, colscale, lgrp, mrun,
+                     mid.muse, mid.alpha);
     rescale<NQ>(mid.alpha, o);
 #pragma unroll
     for (int nq = 0; nq < NQ; ++nq) ls[nq] = 0.f;
@@ -270,7 +284,8 @@ __device__ __forceinline__ void page_part_a(const FwdArgs& a, const unsigned cha
     }
 #pragma unroll
     for (int nq = 0; nq < NQ; ++nq) lrun[nq] = lrun[nq] * mid.alpha[nq] + ls[nq];
-    half_max<NQ>(mid.s1, 1, cls, vlo, vhi, colscale, lgrp, mrun, mid.muse, mid.alpha);
+    half_max<NQ, UM>(a, mid.s1, 1, cls, vlo, vhi, (int64_t)j * 128, um, colscale, lgrp, mrun,
+                     mid.muse, mid.alpha);
 }
 
 template <int DT, int NQ>
@@ -378,7 +393,7 @@ __device__ __forceinline__ void write_rows(const FwdArgs& a, const UnitIter& it,
     }
 }
 
-template <int DT, int OUT, int NW, int NQ, int LAYOUT>
+template <int DT, int OUT, int NW, int NQ, int LAYOUT, bool UM>
 __global__ __launch_bounds__(NW * 64, 1) void fwd_prefill_kernel(FwdArgs a) {
     constexpr int NT = NW * 64;
     constexpr int R = NW * NQ * 16;
@@ -419,13 +434,18 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_prefill_kernel(FwdArgs a) {
         if (row_base < rows_exist) {
             const KvSeq kv = kv_seq<LAYOUT>(a, it.b);
             const int skv = kv.len;
-            const int off = skv - it.sq;
+            const int off = diag_off(a, skv, it.sq);
             QTile<NQ> qt;
             float colscale[NQ];
             int trow[NQ];
             bool rvalid[NQ];
             load_q<DT, NQ>(a, it, t0, rows_exist, row_base + wave * NQ * 16, lane, qt, colscale,
                            trow, rvalid);
+            UMaskRow um[NQ];
+#pragma unroll
+            for (int nq = 0; nq < NQ; ++nq)
+                um[nq] = UM ? umask_row(a, it.b, trow[nq], rvalid[nq])
+                            : UMaskRow{make_rsrc(nullptr, 0), -1};
             float mrun[NQ], lrun[NQ];
             f32x4 o[8][NQ];
 #pragma unroll
@@ -472,8 +492,8 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_prefill_kernel(FwdArgs a) {
                     unsigned char* dst = have_prev ? smem + (buf ^ 1) * PageStage<DT>::bytes : cur;
                     page_load<DT, NT>(pr, kv_src(a.k, pb, rs, nv), rs, tid);
                     if (have_prev)
-                        page_part_a<DT, NQ>(a, cur, qt, colscale, trow, prev_j, prev_cls, skv,
-                                            off, lane, mrun, lrun, o, mid);
+                        page_part_a<DT, NQ, UM>(a, cur, qt, colscale, trow, um, prev_j, prev_cls,
+                                                skv, off, lane, mrun, lrun, o, mid);
                     store_k<DT, NT>(pr, dst, tid);
                     page_load<DT, NT>(pr, kv_src(a.v, pb, rs, nv), rs, tid);
                     if (have_prev) page_part_b<DT, NQ>(cur, colscale, lane, lrun, o, mid);
@@ -487,8 +507,8 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_prefill_kernel(FwdArgs a) {
             }
             if (have_prev) {
                 unsigned char* cur = smem + buf * PageStage<DT>::bytes;
-                page_part_a<DT, NQ>(a, cur, qt, colscale, trow, prev_j, prev_cls, skv, off, lane,
-                                    mrun, lrun, o, mid);
+                page_part_a<DT, NQ, UM>(a, cur, qt, colscale, trow, um, prev_j, prev_cls, skv,
+                                        off, lane, mrun, lrun, o, mid);
                 page_part_b<DT, NQ>(cur, colscale, lane, lrun, o, mid);
             }
             __syncthreads();  // the stage is reused by the next task
@@ -678,11 +698,25 @@ __device__ __forceinline__ void mfma_item32(const unsigned char* ks, const unsig
 
 // Softmax item on 32x32 tiles for half page `half` of block j (class cls): mask, lazy running
 // max (in-lane max over 32 keys, then the lane pair l, l ^ 32), rescale, P^T as PV B operands.
-template <int DT>
+// User-mask words of one softmax item (keys half * 64 .. + 63 of block j) for this lane's
+// row, in element order: word 4 t + q holds keys 32 t + 8 q + 4 h .. + 3 of the half page.
+// Loaded one MFMA item ahead of their use, so the latency hides behind it.
+__device__ __forceinline__ void umask_words32(const FwdArgs& a, const UMaskRow& um, int j,
+                                              int half, int lane, uint32_t (&w)[8]) {
+    const int h2 = lane >> 5;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            w[4 * t + q] = umask_word(a, um, (int64_t)j * 128 + half * 64 + 32 * t + 8 * q + 4 * h2);
+}
+
+template <int DT, bool UM>
 __device__ __forceinline__ void softmax_item32(const FwdArgs& a, f32x16 (&s)[2], u32x4 (&p)[4],
-                                               float colscale, int trow, int j, int half, int cls,
-                                               int skv, int off, int lane, float& mrun,
-                                               float& lrun, f32x16 (&o)[4]) {
+                                               float colscale, int trow, const uint32_t (&umw)[8],
+                                               int j, int half, int cls, int skv, int off,
+                                               int lane, float& mrun, float& lrun,
+                                               f32x16 (&o)[4]) {
     constexpr int PT = (DT == kF16) ? kF16 : kBF16;
     const int h2 = lane >> 5;
     if (cls == 2) {
@@ -700,6 +734,15 @@ __device__ __forceinline__ void softmax_item32(const FwdArgs& a, f32x16 (&s)[2],
                 const float x = s[t][i];
                 s[t][i] = __uint_as_float((__float_as_uint(x) & ~out) | (0xff800000u & out));
             }
+    }
+    if constexpr (UM) {  // the user mask applies to every visible block
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if ((umw[4 * t + q] >> (8 * r)) & 0xffu) s[t][4 * q + r] = kNegInf;
     }
     float mx = kNegInf;
 #pragma unroll
@@ -775,7 +818,7 @@ __device__ __forceinline__ void write_rows32(const FwdArgs& a, const UnitIter& i
 
 // The 256-row kernel (schedule above) on 32x32 tiles: each wave's 32 query rows are one
 // 32-column tile.
-template <int DT, int OUT, int LAYOUT>
+template <int DT, int OUT, int LAYOUT, bool UM>
 __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32_kernel(FwdArgs a) {
     constexpr int R = 256;
     constexpr int esz = (DT == kFP8) ? 1 : 2;
@@ -824,13 +867,15 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32_kernel(FwdArgs a) {
         if (row_base < rows_exist) {
             const KvSeq kv = kv_seq<LAYOUT>(a, it.b);
             const int skv = kv.len;
-            const int off = skv - it.sq;
+            const int off = diag_off(a, skv, it.sq);
             const int row0 = row_base + wave * 32;
             QCol32 qc;
             float colscale, mrun = kNegInf, lrun = 0.f;
             int trow;
             bool rvalid;
             load_q32<DT>(a, it, t0, rows_exist, row0, lane, qc, colscale, trow, rvalid);
+            const UMaskRow um =
+                UM ? umask_row(a, it.b, trow, rvalid) : UMaskRow{make_rsrc(nullptr, 0), -1};
             f32x16 o[4];
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) o[dt] = (f32x16){};
@@ -904,6 +949,7 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32_kernel(FwdArgs a) {
                 // page-list entries for the next softmax item, read before its LDS stores are
                 // queued (a wait on the list read would otherwise also wait for the stores)
                 int jc_next = __builtin_amdgcn_readfirstlane(plist[0].y);
+                uint32_t umw[8];  // user-mask words of the next softmax item
                 const int4 m1 = plist[move_half(1) >> 1];
                 int mv_page = __builtin_amdgcn_readfirstlane(m1.x);
                 int mv_rec = __builtin_amdgcn_readfirstlane((move_half(1) & 1) ? m1.w : m1.z);
@@ -926,8 +972,8 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32_kernel(FwdArgs a) {
                         page_load<DT, 256, 64>(pr, src, rs, tg);
                     }
                     __builtin_amdgcn_sched_barrier(0);
-                    softmax_item32<DT>(a, s, p, colscale, trow, jc >> 2, k & 1, jc & 3, skv, off,
-                                       lane, mrun, lrun, o);
+                    softmax_item32<DT, UM>(a, s, p, colscale, trow, umw, jc >> 2, k & 1, jc & 3,
+                                           skv, off, lane, mrun, lrun, o);
                     __builtin_amdgcn_sched_barrier(0);
                     const int jn = plist[min(k + 1, nh - 1) >> 1].y;
                     const int qn = move_half(k + 2);
@@ -937,10 +983,12 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32_kernel(FwdArgs a) {
                     mv_page = __builtin_amdgcn_readfirstlane(mn.x);
                     mv_rec = __builtin_amdgcn_readfirstlane((qn & 1) ? mn.w : mn.z);
                 };
+                if constexpr (UM) umask_words32(a, um, jc_next >> 2, 0, lane, umw);
                 mfma_item32<DT, true, false>(kst, vst, qc, s, p, o, lane);
                 __syncthreads();
                 softmax_and_move(0);
                 for (int k = 1; k < nh; ++k) {
+                    if constexpr (UM) umask_words32(a, um, jc_next >> 2, k & 1, lane, umw);
                     mfma_item32<DT, true, true>(kst + (k & 1) * KB, vst + ((k - 1) & 1) * VB, qc, s,
                                                 p, o, lane);
                     __syncthreads();
@@ -983,7 +1031,7 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32_kernel(FwdArgs a) {
 // ---------------------------------------------------------------------------------------------
 // The 128-row kernel (schedule above) on 32x32 tiles: each wave's 32 query rows are one
 // 32-column tile.
-template <int DT, int OUT, int LAYOUT>
+template <int DT, int OUT, int LAYOUT, bool UM>
 __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32_kernel(FwdArgs a) {
     constexpr int R = 128;
     constexpr int esz = (DT == kFP8) ? 1 : 2;
@@ -1033,13 +1081,15 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32_kernel(FwdArgs a) {
         if (row_base < rows_exist) {
             const KvSeq kv = kv_seq<LAYOUT>(a, it.b);
             const int skv = kv.len;
-            const int off = skv - it.sq;
+            const int off = diag_off(a, skv, it.sq);
             const int row0 = row_base + (wave & 3) * 32;
             QCol32 qc;
             float colscale, mrun = kNegInf, lrun = 0.f;
             int trow;
             bool rvalid;
             load_q32<DT>(a, it, t0, rows_exist, row0, lane, qc, colscale, trow, rvalid);
+            const UMaskRow um =
+                UM ? umask_row(a, it.b, trow, rvalid) : UMaskRow{make_rsrc(nullptr, 0), -1};
             f32x16 o[4];
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) o[dt] = (f32x16){};
@@ -1111,13 +1161,19 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32_kernel(FwdArgs a) {
                     else
                         store_k<DT, 256, 64>(pr, other_v, tg);  // same row pitch as K
                 };
+                uint32_t umw[8];  // user-mask words of the next softmax item
+                auto mask_words = [&](int k) {
+                    if constexpr (UM)
+                        umask_words32(a, um, __builtin_amdgcn_readfirstlane(plist[k].y) >> 2, grp,
+                                      lane, umw);
+                };
                 auto softmax_and_move = [&](int k) {
                     const int jc = __builtin_amdgcn_readfirstlane(plist[k].y);
                     PageRegs<DT, 256, 64> pr;
                     page_load<DT, 256, 64>(pr, half_src(kbase, 2 * k + 2 + grp), rs, tg);
                     __builtin_amdgcn_sched_barrier(0);
-                    softmax_item32<DT>(a, s, p, colscale, trow, jc >> 2, grp, jc & 3, skv, off, lane,
-                                       mrun, lrun, o);
+                    softmax_item32<DT, UM>(a, s, p, colscale, trow, umw, jc >> 2, grp, jc & 3,
+                                           skv, off, lane, mrun, lrun, o);
                     __builtin_amdgcn_sched_barrier(0);
                     store_k<DT, 256, 64>(pr, my_k, tg);
                     __syncthreads();
@@ -1125,6 +1181,7 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32_kernel(FwdArgs a) {
                 {
                     PageRegs<DT, 256, 64> pr;
                     page_load<DT, 256, 64>(pr, half_src(vbase, grp - 1), rs, tg);
+                    mask_words(0);
                     __builtin_amdgcn_sched_barrier(0);
                     mfma_item32<DT, true, false>(my_k, my_v, qc, s, p, o, lane);
                     __builtin_amdgcn_sched_barrier(0);
@@ -1135,6 +1192,7 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32_kernel(FwdArgs a) {
                 for (int k = 1; k < n; ++k) {
                     PageRegs<DT, 256, 64> pr;
                     page_load<DT, 256, 64>(pr, half_src(vbase, 2 * k + grp - 1), rs, tg);
+                    mask_words(k);
                     __builtin_amdgcn_sched_barrier(0);
                     mfma_item32<DT, true, true>(my_k, my_v, qc, s, p, o, lane);
                     __builtin_amdgcn_sched_barrier(0);
@@ -1198,29 +1256,34 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32_kernel(FwdArgs a) {
     }
 }
 
-template <int DT, int OUT, int LAYOUT>
+template <int DT, int OUT, int LAYOUT, bool UM>
 hipError_t launch_l(const FwdArgs& a, int rows, hipStream_t s) {
     const int grid = a.P * a.nst;
     // 8 waves per workgroup either way: 32 rows per wave for large units, 16 below (more
     // workgroups, fewer registers)
     if (rows == 256) {
-        hipLaunchKernelGGL((fwd_prefill_pp32_kernel<DT, OUT, LAYOUT>), dim3(grid), dim3(512), 0,
-                           s, a);
+        hipLaunchKernelGGL((fwd_prefill_pp32_kernel<DT, OUT, LAYOUT, UM>), dim3(grid), dim3(512),
+                           0, s, a);
     } else if (a.M > 64) {
-        hipLaunchKernelGGL((fwd_prefill_ks32_kernel<DT, OUT, LAYOUT>), dim3(grid), dim3(512), 0,
-                           s, a);
+        hipLaunchKernelGGL((fwd_prefill_ks32_kernel<DT, OUT, LAYOUT, UM>), dim3(grid), dim3(512),
+                           0, s, a);
     } else {
-        hipLaunchKernelGGL((fwd_prefill_kernel<DT, OUT, 8, 1, LAYOUT>), dim3(grid), dim3(512), 0,
-                           s, a);
+        hipLaunchKernelGGL((fwd_prefill_kernel<DT, OUT, 8, 1, LAYOUT, UM>), dim3(grid), dim3(512),
+                           0, s, a);
     }
     return hipGetLastError();
 }
 
-// The KV layout is a template argument so that the paged kernels carry no layout test.
+// The KV layout and the user mask are template arguments, so that the plain paged kernels
+// carry neither test.
 template <int DT, int OUT>
 hipError_t launch_t(const FwdArgs& a, int rows, hipStream_t s) {
-    return a.cu_kv != nullptr ? launch_l<DT, OUT, kTnd>(a, rows, s)
-                              : launch_l<DT, OUT, kPaged>(a, rows, s);
+    const bool tnd = a.cu_kv != nullptr;
+    if (a.umask != nullptr)
+        return tnd ? launch_l<DT, OUT, kTnd, true>(a, rows, s)
+                   : launch_l<DT, OUT, kPaged, true>(a, rows, s);
+    return tnd ? launch_l<DT, OUT, kTnd, false>(a, rows, s)
+               : launch_l<DT, OUT, kPaged, false>(a, rows, s);
 }
 
 }  // namespace

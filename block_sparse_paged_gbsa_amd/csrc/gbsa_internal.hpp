@@ -59,8 +59,11 @@ struct FwdArgs {
     float* ws_l;           // [2P, M]  running sum
     int64_t kv_stride;     // elements per storage unit: a page (paged) or a row (token-major)
     int64_t kv_rows;       // token-major: rows of key (= of value); paged: unused
+    const uint8_t* umask;  // user attention mask or null: [rows, cols] per sequence or shared
+    int64_t um_bstride;    // bytes between sequences' masks (0: shared)
+    int32_t um_rstride, um_rows, um_cols;  // row stride (bytes) and extent
     int32_t B, N1, N2, G, X, topK, tqb, maxb, P, M, nst;
-    int32_t mask, wl, wr, return_lse;
+    int32_t mask, wl, wr, return_lse;  // mask: 0 none, 1 causal bottom-right, 2 top-left
     float scale_log2;      // softmax scale * log2(e)
     int32_t expect[kHeaderWords];  // expected header words (0, 1, 2 and 7..21 are checked)
 };

@@ -77,6 +77,10 @@ class Problem:
     kv_storage: Optional[np.ndarray] = None  # int64 [B]: cached KV length of each sequence
     kv_layout: str = "PA_BBND"  # or "TND"
     cu_seqlens_kv: Optional[np.ndarray] = None  # int64 [B+1] (TND only)
+    # user attention mask: uint8 [1 or B, rows, row_stride], entries [:, :, :atten_mask_cols]
+    # (nonzero = masked out); the bytes past atten_mask_cols are row padding
+    atten_mask: Optional[np.ndarray] = None
+    atten_mask_cols: int = 0
 
     @property
     def total_q(self) -> int:
@@ -445,3 +449,27 @@ def to_tnd(p: Problem, keep_seqused_kv: bool = True, tail_rows: int = 0) -> Prob
         p, name=p.name + "_tnd", k=rows(p.k), v=rows(p.v), block_table=None,
         num_pages=int(cu_kv[-1]) + tail_rows, kv_storage=storage, kv_layout="TND",
         cu_seqlens_kv=cu_kv, seqused_kv=p.seqused_kv if keep_seqused_kv else None)
+
+
+def with_atten_mask(p: Problem, seed: int, density: float = 0.3, per_batch: bool = True,
+                    rows: Optional[int] = None, cols: Optional[int] = None,
+                    pad: int = 4) -> Problem:
+    """The same problem with a random user attention mask.
+
+    Entry (t, p) is masked (a random nonzero byte) with probability `density`. rows / cols
+    default to the longest query storage / visible KV length; smaller values leave the rest
+    unmasked. Each row is followed by `pad` padding bytes (row stride rounded up to 4) set to
+    0xFF, which must never be read as mask entries.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed + 9_000_000))
+    qlen = np.diff(p.cu_seqlens_q)
+    kvl = [p.kv_len(b) for b in range(p.batch)]
+    rows = int(qlen.max()) if rows is None else int(rows)
+    cols = int(max(kvl)) if cols is None else int(cols)
+    stride = -(-(cols + pad) // 4) * 4
+    nb = p.batch if per_batch else 1
+    m = np.full((nb, rows, stride), 0xFF, dtype=np.uint8)
+    body = rng.random((nb, rows, cols)) < density
+    vals = rng.integers(1, 256, size=(nb, rows, cols), dtype=np.uint8)
+    m[:, :, :cols] = np.where(body, vals, 0).astype(np.uint8)
+    return dataclasses.replace(p, name=p.name + "_umask", atten_mask=m, atten_mask_cols=cols)

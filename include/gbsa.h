@@ -76,8 +76,14 @@ typedef enum gbsa_dtype {
     GBSA_DTYPE_FP8_E4M3 = 2   /* OCP e4m3fn, the article's FP8 E4M3 full-quant path */
 } gbsa_dtype;
 
-/* "mask" section: 1 = built-in causal. 0 = no mask. */
-typedef enum gbsa_mask_mode { GBSA_MASK_NONE = 0, GBSA_MASK_CAUSAL = 1 } gbsa_mask_mode;
+/* "mask" section: 1 = the built-in causal mask (aligned to the bottom-right corner when query
+ * and key lengths differ). 0 = no mask. 2 = causal aligned to the top-left corner (keys
+ * p <= t), an addition to the article's single mask type. */
+typedef enum gbsa_mask_mode {
+    GBSA_MASK_NONE = 0,
+    GBSA_MASK_CAUSAL = 1,
+    GBSA_MASK_CAUSAL_TOP_LEFT = 2
+} gbsa_mask_mode;
 
 /* Key/value layouts ("parameters" section: layoutKv). PA_BBND pages are located through
  * block_table; TND rows through cu_seqlens_kv ("general constraints": dual lengths, which
@@ -116,7 +122,8 @@ typedef struct gbsa_params {
     int32_t out_dtype;          /* gbsa_dtype of attention_out: F16 or BF16. With quant 0 it
                                    must equal dtype; with quant 5 it is required */
     int32_t mask_mode;          /* gbsa_mask_mode */
-    int32_t win_left;           /* -1 unbounded, else keys p >= t + off - win_left */
+    int32_t win_left;           /* -1 unbounded, else keys p >= t + off - win_left (off: see
+                                   gbsa_forward; 0 with GBSA_MASK_CAUSAL_TOP_LEFT) */
     int32_t win_right;          /* -1 unbounded, else keys p <= t + off + win_right */
     int32_t quant_mode;         /* gbsa_quant_mode; 5 requires dtype FP8_E4M3 */
     int32_t softmax_precision;  /* 0 or 1 ("softmax precision" section); computed in fp32 */
@@ -191,7 +198,8 @@ gbsa_status gbsa_workspace_size(const gbsa_params* params, size_t* bytes);
  *   workspace / workspace_bytes: device buffer of at least gbsa_workspace_size bytes
  * Visibility of key position p = 128*j + r from batch-local query row t: p < seqused_kv[b];
  * causal: p <= t + off; window: t + off - win_left <= p <= t + off + win_right, with
- * off = seqused_kv[b] - (seqused_q[b] or the storage length).
+ * off = seqused_kv[b] - (seqused_q[b] or the storage length), or off = 0 with
+ * GBSA_MASK_CAUSAL_TOP_LEFT (whose causal rule is then p <= t).
  * Values the caller must guarantee (not checked, as in the article): lengths within
  * storage, block_table entries in [0, num_pages) for every selected block below
  * seqused_kv. The kernels skip a slot whose index is negative or whose block starts at or
@@ -240,6 +248,56 @@ gbsa_status gbsa_forward_tnd(const gbsa_params* params, const void* query, const
                              const float* q_scale, const float* k_scale, const float* v_scale,
                              const float* p_scale, void* attention_out, float* softmax_lse,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Every tensor of the main call in one block: the article's aclnn form, one call taking all
+ * optional tensors ("aclnn API" section), including the user attention mask it lists as
+ * attenMaskOptional. Pointers that do not apply must be NULL.
+ */
+typedef struct gbsa_forward_args {
+    const void* query;                 /* [T, N1, 128] dtype */
+    const void* key;                   /* PA_BBND [num_pages, 128, N2, 128] or TND [T_kv, N2, 128] */
+    const void* value;                 /* same layout as key */
+    const int32_t* sparse_block_idx;   /* [N2, total_q_blocks, top_k] */
+    const int32_t* sparse_block_count; /* [N2, total_q_blocks] */
+    const int32_t* metadata;           /* [1024] from gbsa_metadata */
+    const int64_t* cu_seqlens_q;       /* [B+1] */
+    const int32_t* seqused_q;          /* [B] or NULL (must match has_seqused_q) */
+    const int64_t* cu_seqlens_kv;      /* [B+1], TND only */
+    const int32_t* seqused_kv;         /* [B]: required with PA_BBND, optional with TND */
+    const int32_t* block_table;        /* [B, max_blocks_per_seq], PA_BBND only */
+    const float* q_scale;              /* dequant scales, quant 5 only (see gbsa_forward) */
+    const float* k_scale;
+    const float* v_scale;
+    const float* p_scale;              /* must be NULL */
+    /* User attention mask, uint8, or NULL. Entry [t][p] nonzero removes key position p for
+     * the batch-local query row t of every head of a sequence, on top of every other rule;
+     * entries outside rows x cols do not mask. Layout: entry (b, t, p) at byte
+     * b * mask_batch_stride + t * mask_row_stride + p (mask_batch_stride 0: one mask shared
+     * by all sequences). The base must be 4-byte aligned, mask_row_stride and
+     * mask_batch_stride multiples of 4, mask_row_stride >= mask_cols, and one sequence's
+     * rows x mask_row_stride below 2^31 (else GBSA_ERR_SHAPE). The fields are ignored when
+     * atten_mask is NULL. */
+    const uint8_t* atten_mask;
+    int64_t mask_batch_stride;
+    int64_t mask_row_stride;
+    int32_t mask_rows;
+    int32_t mask_cols;
+    void* attention_out;               /* [T, N1, 128] out_dtype */
+    float* softmax_lse;                /* [T, N1] or NULL (must match return_lse) */
+    void* workspace;
+    size_t workspace_bytes;
+} gbsa_forward_args;
+
+/*
+ * Stage 2 with every option: either KV layout (params->kv_layout), an optional user
+ * attention mask, any mask mode. Same computation, validation and device-side behaviour as
+ * gbsa_forward / gbsa_forward_tnd, which are this call with atten_mask NULL.
+ * Errors: those of gbsa_forward; GBSA_ERR_NULL if args is NULL; GBSA_ERR_SHAPE for a mask
+ * whose alignment, strides or extent break the rules above.
+ */
+gbsa_status gbsa_forward_ex(const gbsa_params* params, const gbsa_forward_args* args,
+                            hipStream_t stream);
 
 /* Human-readable text for a status (static storage). */
 const char* gbsa_status_string(gbsa_status status);

@@ -40,6 +40,14 @@ Readings where the pages are silent (each is listed in the design notes):
     rows 128*j .. 128*j+127, and the visible length is seqused_kv[b] when given,
     else the storage length. A seqused_kv above the storage length (which the
     pages forbid) is read as the storage length.
+  * mask_mode 2 (not on the pages, which support only the built-in causal mask) is
+    causal aligned to the top-left corner: off = 0, keys p <= t (windows are then
+    relative to the same diagonal).
+  * The user attention mask (the pages list attenMaskOptional and require it to be
+    absent): uint8 entries indexed by the batch-local query row t and key position
+    p, one [rows, cols] array shared by every sequence or one per sequence; a
+    nonzero entry removes the key for that row, on top of every other rule. Entries
+    outside [0, rows) x [0, cols) do not mask.
 """
 from __future__ import annotations
 
@@ -73,7 +81,7 @@ def visible(p: np.ndarray, t: np.ndarray, skv: int, off: int, mask_mode: int,
     P = p[None, :]
     d = t[:, None] + off  # the diagonal position of each row
     ok = P < skv
-    if mask_mode == 1:
+    if mask_mode in (1, 2):  # causal (bottom-right or top-left: the caller's off)
         ok = ok & (P <= d)
     if win_left >= 0:
         ok = ok & (P >= d - win_left)
@@ -88,10 +96,11 @@ class Inputs:
     def __init__(self, q, k, v, sparse_block_idx, sparse_block_count, cu_seqlens_q, seqused_q,
                  seqused_kv, block_table, *, dtype: str, block_x: int, scale: float,
                  mask_mode: int, win_left: int = -1, win_right: int = -1,
-                 q_scale=None, k_scale=None, v_scale=None, cu_seqlens_kv=None):
+                 q_scale=None, k_scale=None, v_scale=None, cu_seqlens_kv=None,
+                 atten_mask=None):
         """Paged key/value [pages, 128, N2, D] with block_table and seqused_kv, or, when
         cu_seqlens_kv is given, token-major key/value [T_kv, N2, D] (block_table unused,
-        seqused_kv optional)."""
+        seqused_kv optional). atten_mask: uint8 [rows, cols] (shared) or [B, rows, cols]."""
         self.q, self.k, self.v = q, k, v
         self.idx = np.asarray(sparse_block_idx)
         self.cnt = np.asarray(sparse_block_count)
@@ -117,6 +126,10 @@ class Inputs:
         self.ks = None if k_scale is None else np.asarray(k_scale, dtype=np.float64)
         self.vs = None if v_scale is None else np.asarray(v_scale, dtype=np.float64)
         self.starts = q_block_starts(self.cu, self.X)
+        self.umask = None
+        if atten_mask is not None:
+            m = np.asarray(atten_mask)
+            self.umask = m[None] if m.ndim == 2 else m
 
     @property
     def B(self) -> int:
@@ -201,8 +214,15 @@ def attention_unit(inp: Inputs, b: int, n2: int, gl: int, rows: Optional[np.ndar
         qv = qv * inp.qs[heads][None, :, None]
     z = inp.scale * np.einsum("rgd,nd->rgn", qv, K)  # [r, G, n]
     skv = inp.kv_len(b)
-    off = skv - sq
+    off = 0 if inp.mask_mode == 2 else skv - sq
     vis = visible(pos, rows, skv, off, inp.mask_mode, inp.wl, inp.wr)  # [r, n]
+    if inp.umask is not None:
+        um = inp.umask[b if inp.umask.shape[0] > 1 else 0]
+        inside = (rows[:, None] < um.shape[0]) & (pos[None, :] < um.shape[1])
+        r_i = np.minimum(rows, um.shape[0] - 1)[:, None]
+        p_i = np.minimum(pos, um.shape[1] - 1)[None, :]
+        if um.size:
+            vis = vis & ~(inside & (um[r_i, p_i] != 0))
     z = np.where(vis[:, None, :], z, -np.inf)
     O = np.zeros((len(rows), G, inp.D))
     lse = np.full((len(rows), G), -np.inf)

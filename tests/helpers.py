@@ -28,7 +28,15 @@ def oracle_inputs(p, q=None, k=None, v=None) -> Inputs:
                   scale=p.scale, mask_mode=p.mask_mode, win_left=p.win_left,
                   win_right=p.win_right, q_scale=p.q_scale, k_scale=p.k_scale,
                   v_scale=p.v_scale,
-                  cu_seqlens_kv=p.cu_seqlens_kv if p.kv_layout == "TND" else None)
+                  cu_seqlens_kv=p.cu_seqlens_kv if p.kv_layout == "TND" else None,
+                  atten_mask=user_mask(p))
+
+
+def user_mask(p):
+    """The user attention mask's entries [1 or B, rows, cols] without the row padding."""
+    if p.atten_mask is None:
+        return None
+    return p.atten_mask[:, :, :p.atten_mask_cols]
 
 
 def dequant(t: torch.Tensor, dtype: str, scale=None, head_axis=None) -> torch.Tensor:
@@ -80,6 +88,12 @@ class GpuProblem:
         self.tnd = p.kv_layout == "TND"
         self.table = None if self.tnd else torch.as_tensor(p.block_table).to(d)
         self.cu_kv = torch.as_tensor(p.cu_seqlens_kv).to(d) if self.tnd else None
+        self.umask = None
+        if p.atten_mask is not None:  # [1 or B, rows, stride] -> the entries' view
+            full = torch.as_tensor(p.atten_mask).to(d)
+            self.umask = full[:, :, :p.atten_mask_cols]
+            if full.shape[0] == 1:
+                self.umask = self.umask[0]
         f = lambda s: None if s is None else torch.as_tensor(s, dtype=torch.float32).to(d)
         self.qs, self.ks, self.vs = f(p.q_scale), f(p.k_scale), f(p.v_scale)
 
@@ -88,8 +102,15 @@ class GpuProblem:
         return gbsa_metadata(params, self.cnt, self.cu, self.squ, self.skv, metadata)
 
     def forward(self, params, meta, out=None, lse=None, workspace=None):
-        from block_sparse_paged_gbsa_amd.api import gbsa_forward, gbsa_forward_tnd
+        from block_sparse_paged_gbsa_amd.api import (gbsa_forward, gbsa_forward_ex,
+                                                     gbsa_forward_tnd)
         p = self.p
+        if self.umask is not None:
+            return gbsa_forward_ex(params, p.q, p.k, p.v, self.idx, self.cnt, meta, self.cu,
+                                   self.squ, cu_seqlens_kv=self.cu_kv, seqused_kv=self.skv,
+                                   block_table=self.table, q_scale=self.qs, k_scale=self.ks,
+                                   v_scale=self.vs, atten_mask=self.umask, out=out, lse=lse,
+                                   workspace=workspace)
         if self.tnd:
             return gbsa_forward_tnd(params, p.q, p.k, p.v, self.idx, self.cnt, meta, self.cu,
                                     self.squ, self.cu_kv, self.skv, self.qs, self.ks, self.vs,

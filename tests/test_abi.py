@@ -32,23 +32,25 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert set(names) <= exported
 
 
-def test_params_struct_layout_matches_c():
+@pytest.mark.parametrize("cname,pystruct", [("gbsa_params", _lib.GbsaParams),
+                                             ("gbsa_forward_args", _lib.GbsaForwardArgs)])
+def test_struct_layouts_match_c(cname, pystruct):
     """Compile a tiny C program against the header and compare sizeof/offsetof."""
-    fields = [f for f, _ in _lib.GbsaParams._fields_]
+    fields = [f for f, _ in pystruct._fields_]
     src = ['#include <stdio.h>', '#include <stddef.h>', '#include "gbsa.h"', 'int main(void){',
-           'printf("%zu\\n", sizeof(gbsa_params));']
-    src += [f'printf("%zu\\n", offsetof(gbsa_params, {f}));' for f in fields]
+           f'printf("%zu\\n", sizeof({cname}));']
+    src += [f'printf("%zu\\n", offsetof({cname}, {f}));' for f in fields]
     src += ['return 0;}']
-    tmp = os.path.join("/tmp", f"gbsa_layout_{os.getpid()}")
+    tmp = os.path.join("/tmp", f"gbsa_layout_{cname}_{os.getpid()}")
     with open(tmp + ".c", "w") as fh:
         fh.write("\n".join(src))
     subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
                     "-I", "/opt/rocm/include", tmp + ".c", "-o", tmp], check=True)
     vals = [int(x) for x in subprocess.run([tmp], capture_output=True, text=True,
                                            check=True).stdout.split()]
-    assert vals[0] == ctypes.sizeof(_lib.GbsaParams)
+    assert vals[0] == ctypes.sizeof(pystruct)
     for f, off in zip(fields, vals[1:]):
-        assert getattr(_lib.GbsaParams, f).offset == off, f
+        assert getattr(pystruct, f).offset == off, f
 
 
 def _good(**kw):
@@ -71,7 +73,7 @@ def test_valid_params_pass():
     ("head_dim", 64, 2), ("block_y", 64, 2), ("page_size", 256, 2), ("num_heads_kv", 3, 2),
     ("top_k", 257, 2), ("win_left", -2, 2), ("num_workers", 1000, 2), ("kv_page_stride", 100, 2),
     ("batch", 0, 5), ("total_q", 0, 5), ("top_k", 0, 5), ("num_pages", 0, 5),
-    ("quant_mode", 3, 4), ("mask_mode", 2, 4), ("is_packed_gqa", 0, 4), ("softmax_precision", 2, 4),
+    ("quant_mode", 3, 4), ("mask_mode", 3, 4), ("is_packed_gqa", 0, 4), ("softmax_precision", 2, 4),
     ("dtype", 2, 3), ("out_dtype", 2, 3), ("batch", 20000, 4),
 ])
 def test_rejections(field, value, code):
@@ -159,3 +161,41 @@ def test_tnd_entry_point_validation():
     # metadata: seqused_kv optional with TND, required with PA_BBND
     assert lib.gbsa_metadata(ctypes.byref(tnd), dummy, dummy, None, None, None, None) == 7
     assert lib.gbsa_metadata(ctypes.byref(paged), dummy, dummy, None, None, dummy, None) == 1
+
+
+def _args(**kw):
+    g = _lib.GbsaForwardArgs()
+    for f in ("query", "key", "value", "sparse_block_idx", "sparse_block_count", "metadata",
+              "cu_seqlens_q", "seqused_kv", "block_table", "attention_out", "workspace"):
+        setattr(g, f, 0x1000)
+    for k, v in kw.items():
+        setattr(g, k, v)
+    return g
+
+
+def test_forward_ex_validation():
+    """The all-options entry point: mask geometry rules, one layout's tensors only, mask
+    mode 2 accepted; every case stops before any device work."""
+    lib = _lib.load()
+    good = _good()
+    fx = lambda p, g: lib.gbsa_forward_ex(ctypes.byref(p), None if g is None else ctypes.byref(g),
+                                         None)
+    assert fx(good, None) == 1
+    assert fx(good, _args(workspace_bytes=0)) == 6  # reaches the workspace check
+    mask = dict(atten_mask=0x2000, mask_rows=64, mask_cols=100, mask_row_stride=100)
+    assert fx(good, _args(workspace_bytes=0, **mask)) == 6  # a valid mask
+    assert fx(good, _args(workspace_bytes=0, **dict(mask, atten_mask=0x2001))) == 2  # alignment
+    assert fx(good, _args(workspace_bytes=0, **dict(mask, mask_row_stride=102))) == 2
+    assert fx(good, _args(workspace_bytes=0, **dict(mask, mask_row_stride=96))) == 2  # < cols
+    assert fx(good, _args(workspace_bytes=0, **dict(mask, mask_batch_stride=6))) == 2
+    assert fx(good, _args(workspace_bytes=0, **dict(mask, mask_rows=1 << 24,
+                                                    mask_row_stride=1 << 8))) == 2  # 2^32 B
+    assert fx(good, _args(workspace_bytes=0, **dict(mask, mask_cols=-1))) == 2
+    # the layout not in use takes no tensors
+    assert fx(good, _args(workspace_bytes=0, cu_seqlens_kv=0x3000)) == 1
+    tnd = _good(kv_layout=_lib.KV_TND, max_blocks_per_seq=0, num_pages=1000)
+    assert fx(tnd, _args(workspace_bytes=0)) == 1  # block_table given with TND
+    assert fx(tnd, _args(workspace_bytes=0, block_table=None, cu_seqlens_kv=0x3000)) == 6
+    assert fx(tnd, _args(workspace_bytes=0, block_table=None)) == 1  # cu_seqlens_kv missing
+    # mask mode 2 (causal, top-left) is accepted
+    assert _check(_good(mask_mode=_lib.MASK_CAUSAL_TOP_LEFT)) == 0

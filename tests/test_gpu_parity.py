@@ -314,6 +314,82 @@ def test_keys_past_visible_length_never_reach_the_output(case, layout):
         _full_check(pp, num_workers=P, label=f"poison{seed} {layout} P={P}")
 
 
+# ---------------------------------------------------------------------------
+# user attention masks and the top-left causal mask
+# ---------------------------------------------------------------------------
+
+# one case per kernel (decode, 16-row waves, key-split, row-split), both layouts, shared and
+# per-sequence masks, masks covering only part of the rows / keys, mask modes 0, 1 and 2
+UMASK_CASES = [
+    dict(seed=151, prob=dict(dtype="bf16", decode=True, batch=5, block_x=1, num_heads_q=16,
+                             num_heads_kv=4, mask_mode=1),
+         mask=dict(density=0.3, per_batch=True), tnd=False),
+    dict(seed=152, prob=dict(dtype="f16", block_x=32, mask_mode=2, use_seqused_q=True),
+         mask=dict(density=0.5, per_batch=False), tnd=True),
+    dict(seed=153, prob=dict(dtype="fp8", batch=2, max_len=500, block_x=96, num_heads_q=4,
+                             num_heads_kv=4, top_k=4, mask_mode=0, out_dtype="f16"),
+         mask=dict(density=0.2, per_batch=True, rows=300, cols=333), tnd=False),
+    dict(seed=154, prob=dict(dtype="f16", batch=2, max_len=500, block_x=40, num_heads_q=16,
+                             num_heads_kv=2, top_k=6, mask_mode=1, win_left=100, win_right=0,
+                             use_seqused_q=True),
+         mask=dict(density=0.4, per_batch=True), tnd=True),
+    dict(seed=155, prob=dict(dtype="bf16", batch=1, max_len=700, block_x=128, num_heads_q=8,
+                             num_heads_kv=1, top_k=6, mask_mode=2),
+         mask=dict(density=0.7, per_batch=False, cols=257), tnd=False),
+    dict(seed=156, prob=dict(dtype="fp8", decode=True, batch=4, block_x=2, num_heads_q=8,
+                             num_heads_kv=2, top_k=5, mask_mode=0),
+         mask=dict(density=0.5, per_batch=True, rows=1), tnd=True),
+]
+
+
+@pytest.mark.parametrize("case", UMASK_CASES, ids=[str(c["seed"]) for c in UMASK_CASES])
+def test_user_mask_all_rows(case):
+    p = gi.random_problem(case["seed"], device="cuda", **case["prob"])
+    if case["tnd"]:
+        p = gi.to_tnd(p)
+    p = gi.with_atten_mask(p, case["seed"], **case["mask"])
+    for P in (0, 7):
+        _full_check(p, num_workers=P, label=f"umask{case['seed']} P={P}")
+
+
+@pytest.mark.parametrize("kw", [
+    dict(dtype="bf16", decode=True, batch=4, block_x=1, num_heads_q=8, num_heads_kv=2),
+    dict(dtype="f16", block_x=32, use_seqused_q=True),
+    dict(dtype="bf16", batch=2, max_len=400, block_x=64, num_heads_q=4, num_heads_kv=2),
+    dict(dtype="f16", batch=2, max_len=500, block_x=40, num_heads_q=16, num_heads_kv=2,
+         win_left=60, win_right=0),
+], ids=["decode", "rows64", "rows128", "rows320"])
+def test_top_left_causal_all_rows(kw):
+    p = gi.random_problem(157, device="cuda", mask_mode=2, **kw)
+    for P in (0, 5):
+        _full_check(p, num_workers=P, label=f"topleft P={P}")
+
+
+def test_keyword_interface_bool_mask():
+    """The article-style keyword call with a bool mask whose rows are not 4-byte multiples."""
+    from block_sparse_paged_gbsa_amd import (generic_block_sparse_attention,
+                                             generic_block_sparse_attention_metadata)
+    p = gi.random_problem(158, device="cuda", dtype="f16", batch=2, mask_mode=1)
+    cols = max(p.kv_len(b) for b in range(p.batch)) | 1  # odd: needs padding
+    rows = int(np.diff(p.cu_seqlens_q).max())
+    rng = np.random.default_rng(5)
+    m = rng.random((rows, cols)) < 0.3
+    pm = dataclasses.replace(p, atten_mask=np.where(m, 1, 0).astype(np.uint8)[None],
+                             atten_mask_cols=cols)
+    gp = GpuProblem(pm)
+    meta = generic_block_sparse_attention_metadata(
+        gp.idx, gp.cnt, p.num_heads_q, p.num_heads_kv, 128, [p.block_x, 128],
+        cu_seqlens_q=gp.cu, seqused_kv=gp.skv, mask_mode=1, num_workers=6)
+    out, lse = generic_block_sparse_attention(
+        p.q, p.k, p.v, gp.idx, gp.cnt, [p.block_x, 128], metadata=meta,
+        attn_mask=torch.as_tensor(m, device="cuda"), cu_seqlens_q=gp.cu, seqused_kv=gp.skv,
+        block_table=gp.table, softmax_scale=p.scale, mask_mode=1, return_softmax_lse=True,
+        num_workers=6)
+    torch.cuda.synchronize()
+    O, L, done = oa.sparse_attention(oracle_inputs(pm))
+    compare(pm, out, lse[..., 0], O, L, done, "keyword bool mask")
+
+
 def test_metadata_mismatch_is_refused():
     p = gi.random_problem(123, device="cuda", mask_mode=1)
     gp = GpuProblem(p)

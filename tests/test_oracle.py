@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import gbsa_inputs as gi
-from helpers import dequant, oracle_inputs
+from helpers import dequant, oracle_inputs, user_mask
 from oracle import attention as oa
 from oracle import formats
 
@@ -107,7 +107,7 @@ def _sdpa_reference(p):
         storage = int(p.cu_seqlens_q[b + 1]) - c0
         sq = storage if p.seqused_q is None else int(p.seqused_q[b])
         skv = p.kv_len(b)
-        off = skv - sq
+        off = 0 if p.mask_mode == 2 else skv - sq
         for n2 in range(p.num_heads_kv):
             k, v = _logical_kv(p, b, n2)
             mask = torch.zeros((sq, skv), dtype=torch.bool)
@@ -119,8 +119,12 @@ def _sdpa_reference(p):
                         mask[t, 128 * j:128 * (j + 1)] = True
             tt = torch.arange(sq)[:, None] + off
             pp = torch.arange(skv)[None, :]
-            if p.mask_mode == 1:
+            if p.mask_mode in (1, 2):
                 mask &= pp <= tt
+            if p.atten_mask is not None:  # user mask entries inside its extent
+                um = torch.as_tensor(user_mask(p)[b if p.atten_mask.shape[0] > 1 else 0])
+                r, c = min(sq, um.shape[0]), min(skv, um.shape[1])
+                mask[:r, :c] &= um[:r, :c] == 0
             if p.win_left >= 0:
                 mask &= pp >= tt - p.win_left
             if p.win_right >= 0:
@@ -219,6 +223,66 @@ def test_tnd_seqused_kv_above_storage_reads_as_storage():
     for x, y in ((a, b), (a, c)):
         assert np.array_equal(x[0], y[0], equal_nan=True)
         assert np.array_equal(x[1], y[1], equal_nan=True)
+
+
+@pytest.mark.parametrize("seed,kw,mk", [
+    (61, dict(mask_mode=1, use_seqused_q=True), dict(density=0.3, per_batch=True)),
+    (62, dict(mask_mode=0, num_heads_q=8, num_heads_kv=2), dict(density=0.6, per_batch=False)),
+    (63, dict(mask_mode=2, use_seqused_q=True), dict(density=0.2, per_batch=True, rows=50,
+                                                     cols=150)),
+    (64, dict(mask_mode=0, win_left=60, win_right=10, dtype="bf16"), dict(density=0.5)),
+    (65, dict(mask_mode=1, dtype="fp8", std=0.7, decode=True, batch=3, block_x=1),
+     dict(density=0.4)),
+])
+def test_user_mask_and_top_left_causal_match_sdpa(seed, kw, mk):
+    """User attention masks (shared or per sequence, full or partial extent) and mask mode 2
+    against SDPA with an independently built boolean mask."""
+    p = gi.with_atten_mask(gi.random_problem(seed, **kw), seed, **mk)
+    O, L, done = oa.sparse_attention(oracle_inputs(p))
+    Or, Lr = _sdpa_reference(p)
+    assert done.sum() > 0
+    np.testing.assert_allclose(O[done], Or[done], rtol=0, atol=1e-12)
+    fin = np.isfinite(Lr[done])
+    assert np.array_equal(fin, np.isfinite(L[done]))
+    np.testing.assert_allclose(L[done][fin], Lr[done][fin], rtol=1e-12, atol=1e-12)
+
+
+def test_user_mask_encoding_causal_equals_built_in_causal():
+    """A user mask holding exactly the bottom-right causal pattern, with mask mode 0, is
+    bit-identical to mask mode 1 (pins the mask's row/column orientation and offset)."""
+    p = gi.random_problem(66, mask_mode=1, use_seqused_q=True, batch=3)
+    rows = int(np.diff(p.cu_seqlens_q).max())
+    cols = max(p.kv_len(b) for b in range(p.batch))
+    m = np.zeros((p.batch, rows, cols), dtype=np.uint8)
+    for b in range(p.batch):
+        sq, skv = int(p.seqused_q[b]), p.kv_len(b)
+        t = np.arange(rows)[:, None]
+        q = np.arange(cols)[None, :]
+        m[b] = np.where(q > t + (skv - sq), 7, 0)
+    a = oa.sparse_attention(oracle_inputs(p))
+    bm = oa.sparse_attention(oracle_inputs(_set(p, mask_mode=0, atten_mask=m,
+                                                atten_mask_cols=cols)))
+    assert np.array_equal(a[0], bm[0], equal_nan=True) and np.array_equal(a[1], bm[1],
+                                                                           equal_nan=True)
+
+
+def test_top_left_causal():
+    """Mode 2 equals mode 1 when query and KV lengths agree, and a user mask p > t otherwise."""
+    p = gi.random_problem(67, mask_mode=1, batch=3)  # kv lengths exceed the query lengths
+    same = _set(p, seqused_kv=np.diff(p.cu_seqlens_q).astype(np.int32), kv_storage=None)
+    x = oa.sparse_attention(oracle_inputs(same))
+    y = oa.sparse_attention(oracle_inputs(_set(same, mask_mode=2)))
+    assert np.array_equal(x[0], y[0], equal_nan=True) and np.array_equal(x[1], y[1],
+                                                                         equal_nan=True)
+    rows = int(np.diff(p.cu_seqlens_q).max())
+    cols = max(p.kv_len(b) for b in range(p.batch))
+    m = np.where(np.arange(cols)[None, None, :] > np.arange(rows)[None, :, None], 1, 0)
+    u = oa.sparse_attention(oracle_inputs(_set(p, mask_mode=0, atten_mask=m.astype(np.uint8),
+                                               atten_mask_cols=cols)))
+    v = oa.sparse_attention(oracle_inputs(_set(p, mask_mode=2)))
+    assert np.array_equal(u[0], v[0], equal_nan=True) and np.array_equal(u[1], v[1],
+                                                                         equal_nan=True)
+    assert not np.array_equal(v[0], oa.sparse_attention(oracle_inputs(p))[0], equal_nan=True)
 
 
 def test_all_causal_blocks_equal_dense_causal():

@@ -189,7 +189,10 @@ gbsa_status gbsa_metadata(const gbsa_params* p, const int32_t* sparse_block_coun
     a.tqb = p->total_q_blocks;
     a.P = P;
     {
-        const int64_t lds_cap = 160 * 1024 / (int64_t)sizeof(int) - 2 * ((int64_t)p->batch + 1);
+        // the chunked scheduler's dynamic LDS: two per-sequence tables and the cached counts,
+        // next to its own static shared variables (kMetaStaticLds bytes at most)
+        const int64_t lds_cap = (160 * 1024 - kMetaStaticLds) / (int64_t)sizeof(int) -
+                                2 * ((int64_t)p->batch + 1);
         int64_t ucap = (int64_t)p->num_heads_kv * p->total_q_blocks;
         if (ucap > 16384) ucap = 16384;
         if (ucap > lds_cap) ucap = lds_cap;

@@ -25,6 +25,10 @@ constexpr int kCheckFirst = 7, kCheckLast = 21;
 
 enum DType : int { kF16 = 0, kBF16 = 1, kFP8 = 2 };
 
+// Upper bound of the scheduler kernels' static shared variables (bytes); the host sizes their
+// dynamic LDS so that both fit in the 160 KiB of a CU.
+constexpr int kMetaStaticLds = 512;
+
 struct MetaArgs {
     const int32_t* count;  // [N2, tqb]
     const int64_t* cu;     // [B+1]

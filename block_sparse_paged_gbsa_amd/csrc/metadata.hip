@@ -96,6 +96,7 @@ __global__ __launch_bounds__(1024) void metadata_kernel(MetaArgs a) {
     extern __shared__ int tabs[];  // qbase[B+1], ubase[B+1], counts of the first ucap units
     __shared__ long long sh64[16];
     __shared__ int sh_split;
+    static_assert(sizeof(sh64) + sizeof(sh_split) <= kMetaStaticLds, "static LDS budget");
     const int tid = threadIdx.x, nt = blockDim.x;
     int* qbase = tabs;
     int* ubase = tabs + a.B + 1;
@@ -203,6 +204,7 @@ __global__ __launch_bounds__(1024) void metadata_fast_kernel(MetaArgs a) {
     extern __shared__ int tabs[];  // qbase[B+1], ubase[B+1], counts[N2*tqb], pre[N2*tqb+1], sp[1024]
     __shared__ int sh_a[16], sh_b[16], sh_c[16];
     __shared__ int sh_split;
+    static_assert(sizeof(sh_a) * 3 + sizeof(sh_split) <= kMetaStaticLds, "static LDS budget");
     const int tid = threadIdx.x, nt = blockDim.x;
     const int NC = a.N2 * a.tqb;
     int* qbase = tabs;
@@ -313,7 +315,7 @@ hipError_t launch_metadata(const MetaArgs& a, hipStream_t s) {
     // fast path: every table in LDS (the unit count is at most N2 * tqb)
     const size_t nc = (size_t)a.N2 * (size_t)a.tqb;
     const size_t fast_bytes = sizeof(int) * (2 * ((size_t)a.B + 1) + 2 * nc + 1 + 1024);
-    if (a.B <= 1024 && a.P <= 1024 && fast_bytes <= lds_max) {
+    if (a.B <= 1024 && a.P <= 1024 && fast_bytes + kMetaStaticLds <= lds_max) {
         if (fast_bytes > 64 * 1024) {
             hipError_t e = hipFuncSetAttribute((const void*)metadata_fast_kernel,
                                                hipFuncAttributeMaxDynamicSharedMemorySize,

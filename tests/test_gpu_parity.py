@@ -88,12 +88,16 @@ def test_metadata_bit_exact_random(seed):
     np.testing.assert_array_equal(meta, _ref_meta(p, P))
 
 
-@pytest.mark.parametrize("case", ["many_sequences", "large_tables"])
+@pytest.mark.parametrize("case", ["many_sequences", "large_tables", "max_batch"])
 def test_metadata_bit_exact_beyond_lds(case):
-    """More than 1024 sequences, or N2 x q-block tables larger than LDS: the scheduler's chunked
-    path, which must give the same split word for word."""
+    """More than 1024 sequences (up to GBSA_MAX_BATCH, whose tables fill the LDS), or N2 x
+    q-block tables larger than LDS: the scheduler's chunked path, which must give the same
+    split word for word."""
     if case == "many_sequences":
         p = gi.random_problem(31, values=False, decode=True, batch=1500, num_heads_q=8,
+                              num_heads_kv=2, block_x=1, top_k=4, use_seqused_q=True)
+    elif case == "max_batch":
+        p = gi.random_problem(33, values=False, decode=True, batch=16384, num_heads_q=8,
                               num_heads_kv=2, block_x=1, top_k=4, use_seqused_q=True)
     else:
         p = gi.random_problem(32, values=False, batch=12, max_len=4096, block_x=8,
@@ -166,6 +170,43 @@ def test_random_problem_all_rows(case):
     p = gi.random_problem(seed, device="cuda", **kw)
     for P in (0, 5, 200):
         _full_check(p, num_workers=P, label=f"random{seed} P={P}")
+
+
+@pytest.mark.parametrize("block_x,dtype", [(1, "bf16"), (2, "f16"), (3, "fp8")],
+                         ids=["rows128", "rows256", "rows384"])
+def test_maximum_group_and_top_k(block_x, dtype):
+    """The largest packed GQA group (128 query heads on one KV head) with top_k = 256 slots:
+    128, 256 and 384 packed rows per unit, long selections split across workers."""
+    p = gi.build_problem("group128", seed=171, q_lens=[7, 4], kv_lens=[33000, 20000],
+                         kv_storage=[33100, 20000], num_heads_q=128, num_heads_kv=1,
+                         block_x=block_x, top_k=256, dtype=dtype,
+                         select=gi.select_uniform_count(256), causal_eligible=False,
+                         mask_mode=0, return_lse=True, scale=1.0 / 128 ** 0.5, device="cuda")
+    assert p.sparse_block_count.max() > 200
+    for P in (0, 3):
+        _full_check(p, num_workers=P, label=f"group128 x{block_x} P={P}")
+
+
+def test_maximum_batch():
+    """GBSA_MAX_BATCH = 16384 decode-shaped sequences (the scheduler's chunked path), checked
+    on sampled sequences including the first and the last."""
+    rng = np.random.default_rng(172)
+    B = 16384
+    kv = rng.integers(1, 400, size=B)
+    p = gi.build_problem("max_batch", seed=172, q_lens=[1] * B, kv_lens=kv.tolist(),
+                         num_heads_q=4, num_heads_kv=2, block_x=1, top_k=3, dtype="bf16",
+                         select=gi.select_uniform_count(3), causal_eligible=False, mask_mode=0,
+                         return_lse=True, scale=1.0 / 128 ** 0.5, device="cuda")
+    _log("[parity] max batch: gpu")
+    params, meta, out, lse, ws = GpuProblem(p).run(0)
+    assert int(ws[:4].view(torch.int32)[0].item()) == 0
+    from block_sparse_paged_gbsa_amd import gbsa_num_workers
+    np.testing.assert_array_equal(meta.cpu().numpy(), _ref_meta(p, gbsa_num_workers(params)))
+    rows = sorted({0, 1, B - 1, B - 2} | set(rng.choice(B, 200, replace=False).tolist()))
+    inp = compact_oracle_inputs(p, [(b, 0) for b in rows])  # row b is sequence b's only row
+    O, L, done = oa.sparse_attention(inp, rows=rows)
+    err, lerr = compare(p, out, lse, O, L, done, "max batch")
+    _log(f"max batch: rows {int(done.sum())} O max-abs {err:.3e} LSE rel {lerr:.3e}")
 
 
 def test_empty_selections_and_inactive_sequences():

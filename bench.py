@@ -127,6 +127,93 @@ def algorithmic_work(p, units=None):
     return kv_bytes + qo_bytes + lse_bytes + meta_bytes, flops
 
 
+def gather_offsets(p):
+    """Byte offsets (into key and value) of every selected, visible block's head slice: the
+    decode kernel's reads, in task order."""
+    import gbsa_inputs as gi
+    es = ESIZE[p.dtype]
+    G = p.num_heads_q // p.num_heads_kv
+    starts = gi.q_block_starts(p.cu_seqlens_q, p.block_x)
+    unit_bytes = (p.kv_page_stride * es if p.kv_layout != "TND"
+                  else p.num_heads_kv * 128 * es)
+    offs = []
+    for b in range(p.batch):
+        storage = int(p.cu_seqlens_q[b + 1] - p.cu_seqlens_q[b])
+        sq = storage if p.seqused_q is None else min(int(p.seqused_q[b]), storage)
+        skv = p.kv_len(b)
+        for gl in range(-(-sq // p.block_x)):
+            g = starts[b] + gl
+            for n2 in range(p.num_heads_kv):
+                c = min(max(int(p.sparse_block_count[n2, g]), 0), p.top_k)
+                for j in p.sparse_block_idx[n2, g, :c]:
+                    if j < 0 or 128 * int(j) >= skv:
+                        continue
+                    unit = (int(p.block_table[b, j]) if p.kv_layout != "TND"
+                            else int(p.cu_seqlens_kv[b]) + 128 * int(j))
+                    offs.append(unit * unit_bytes + n2 * 128 * es)
+    return np.asarray(offs, dtype=np.int64)
+
+
+def timed(fn, iters: int, stream) -> float:
+    """Average ms of `iters` calls of fn launched back to back between two events."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fn()
+    e0.record(stream)
+    for _ in range(iters):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+def ceilings(p, hbm_bound: bool, stream):
+    """What this GPU delivers for the same kind of work, measured beside the kernel.
+
+    HBM-bound workloads: a gather-only kernel reading exactly the selected K/V head slices
+    (the decode kernel's bytes and pattern, nothing computed) and a contiguous read of the same
+    byte count. MFMA-bound ones: a dense square GEMM in the workload's dtype (hipBLASLt via
+    torch; fp8 through torch._scaled_mm when this torch build offers it)."""
+    import torch
+    from block_sparse_paged_gbsa_amd import probe
+    out = {}
+    if hbm_bound:
+        offs = torch.as_tensor(gather_offsets(p), device=p.k.device)
+        es = ESIZE[p.dtype]
+        row_bytes, row_stride = 128 * es, p.num_heads_kv * 128 * es
+        nbytes = int(offs.numel()) * 2 * 128 * row_bytes
+        sink = torch.empty(max(int(offs.numel()), 1024) * 4096, dtype=torch.uint8,
+                           device=p.k.device)
+        ms = timed(lambda: probe.gather(p.k, p.v, offs, row_bytes, row_stride, sink, stream),
+                   50, stream)
+        out["gather_GBs"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+        flat = p.k.reshape(-1).view(torch.uint8)
+        n = min(nbytes, flat.numel()) // 16 * 16
+        ms = timed(lambda: probe.stream_read(flat, n, 2048, sink, stream), 50, stream)
+        out["contiguous_read_GBs"] = round(n / (ms * 1e-3) / 1e9, 1)
+        out["bytes"] = nbytes
+    else:
+        n = 8192
+        if p.dtype == "fp8":
+            a = torch.randn(n, n, device=p.q.device).to(torch.float8_e4m3fn)
+            b = torch.randn(n, n, device=p.q.device).to(torch.float8_e4m3fn).t()
+            one = torch.ones((), device=p.q.device)
+            try:
+                ms = timed(lambda: torch._scaled_mm(a, b, scale_a=one, scale_b=one,
+                                                    out_dtype=torch.bfloat16), 20, stream)
+                out["gemm_fp8_TFLOPs"] = round(2 * n ** 3 / (ms * 1e-3) / 1e12, 1)
+            except (RuntimeError, AttributeError) as e:  # not offered by this build
+                out["gemm_fp8_TFLOPs"] = None
+                out["gemm_fp8_note"] = str(e).splitlines()[0][:120]
+        dt = torch.float16 if p.dtype == "f16" else torch.bfloat16
+        a = torch.randn(n, n, device=p.q.device, dtype=dt)
+        b = torch.randn(n, n, device=p.q.device, dtype=dt)
+        ms = timed(lambda: torch.matmul(a, b), 20, stream)
+        out[f"gemm_{'f16' if dt == torch.float16 else 'bf16'}_TFLOPs"] = round(
+            2 * n ** 3 / (ms * 1e-3) / 1e12, 1)
+    return out
+
+
 def cpu_baseline(p, budget_s: float):
     """The float64 oracle on a bounded sample of the same workload (rows of whole q-blocks)."""
     import torch
@@ -341,13 +428,33 @@ def main(argv=None):
     f1.record(stream)
     torch.cuda.synchronize()
     fwd_ms = f0.elapsed_time(f1) / a.steps
+    meta_ms = timed(lambda: gbsa_metadata(params, cnt, cu, squ, skv, meta), a.steps, stream)
     status = int(ws[:4].view(torch.int32)[0].item())
     assert status == 0, "metadata mismatch flagged by the kernels"
     log(f"[bench] step {ms_step:.4f} ms, forward {fwd_ms:.4f} ms, wall {wall:.3f} s")
 
+    hbm_bound = a.config == 2
+    fwd_cold_ms = None
+    if hbm_bound:
+        # every launch after a 1 GiB write that evicts the L2s and the Infinity Cache: the
+        # selected K/V bytes then come from HBM
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        times = []
+        for i in range(20):
+            flush.fill_(i & 0xff)
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c0.record(stream)
+            forward()
+            c1.record(stream)
+            torch.cuda.synchronize()
+            times.append(c0.elapsed_time(c1))
+        fwd_cold_ms = float(np.median(times))
+        del flush
+    ceil = ceilings(p, hbm_bound, stream)
+    log(f"[bench] metadata {meta_ms:.4f} ms, cold forward {fwd_cold_ms} ms, ceilings {ceil}")
+
     gbs = alg_bytes / (ms_step * 1e-3) / 1e9
     tflops = alg_flops / (ms_step * 1e-3) / 1e12
-    hbm_bound = a.config == 2
     rows = p.block_x * p.num_heads_q // p.num_heads_kv  # packed GQA rows per unit
     kernel = ("fwd_decode_kernel" if rows <= 16 else
               "fwd_prefill_pp32_kernel" if rows > 256 else
@@ -388,7 +495,9 @@ def main(argv=None):
                    "head_dim": 128, "block_shape": [p.block_x, 128], "top_k": p.top_k,
                    ("kv_rows" if tnd else "kv_pages"): p.num_pages, "workers": P},
         "effective_tflops": round(tflops, 3), "hbm_gbs": round(gbs, 2),
-        "forward_ms": round(fwd_ms, 5), "kernel": kernel, "algorithmic_bytes": alg_bytes,
+        "forward_ms": round(fwd_ms, 5), "metadata_ms": round(meta_ms, 5),
+        "forward_cold_ms": None if fwd_cold_ms is None else round(fwd_cold_ms, 5),
+        "ceilings": ceil, "kernel": kernel, "algorithmic_bytes": alg_bytes,
         "algorithmic_flops": alg_flops, "roofline": roof, "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

@@ -199,3 +199,18 @@ def test_forward_ex_validation():
     assert fx(tnd, _args(workspace_bytes=0, block_table=None)) == 1  # cu_seqlens_kv missing
     # mask mode 2 (causal, top-left) is accepted
     assert _check(_good(mask_mode=_lib.MASK_CAUSAL_TOP_LEFT)) == 0
+
+
+def test_probe_library_exports_its_header():
+    from block_sparse_paged_gbsa_amd import probe
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "gbsa_probe.h")).read(),
+                  flags=re.S)
+    names = sorted(set(re.findall(r"\b(gbsa_probe_[a-z_]+)\s*\(", text)))
+    assert set(names) == set(probe.EXPORTED)
+    lib = probe.load()
+    for n in names:
+        assert hasattr(lib, n)
+    # invalid arguments are refused before any launch
+    assert lib.gbsa_probe_gather(None, None, None, 0, 256, 2048, None, None) == -1
+    assert lib.gbsa_probe_stream(ctypes.c_void_p(0x1000), 15, 1, ctypes.c_void_p(0x1000),
+                                 None) == -1

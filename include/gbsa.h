@@ -174,7 +174,11 @@ gbsa_status gbsa_metadata(const gbsa_params* params, const int32_t* sparse_block
 /*
  * Workspace bytes gbsa_forward needs, from shapes only (the aclnn GetWorkspaceSize
  * stage). It holds a status word, per-worker split-KV partial results (O, running max,
- * running sum) and their descriptors.
+ * running sum) and the arrival counters of split units.
+ * A workspace must be zero-filled once before its first use (e.g. hipMemsetAsync to 0).
+ * Every call leaves the arrival counters at zero again, so a workspace can be reused by
+ * later calls of any shape whose gbsa_workspace_size fits in it, in stream order. The status
+ * word (word 0) is sticky: once a call sets it, it stays set until the caller clears it.
  */
 gbsa_status gbsa_workspace_size(const gbsa_params* params, size_t* bytes);
 

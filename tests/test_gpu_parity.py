@@ -431,6 +431,26 @@ def test_keyword_interface_bool_mask():
     compare(pm, out, lse[..., 0], O, L, done, "keyword bool mask")
 
 
+@pytest.mark.parametrize("kw", [dict(decode=True, batch=4, block_x=1, num_heads_q=8,
+                                     num_heads_kv=2),
+                                dict(batch=2, max_len=500, block_x=40, num_heads_q=16,
+                                     num_heads_kv=2, top_k=6)], ids=["decode", "prefill"])
+def test_workspace_reuse(kw):
+    """Split-KV units leave their arrival counters at zero: a workspace reused by several calls
+    (same worker count) gives bit-identical results to a fresh one every time."""
+    p = gi.random_problem(181, device="cuda", mask_mode=1, **kw)
+    gp = GpuProblem(p)
+    params = gpu_params(p, 7)  # few workers: most units are split
+    meta = gp.metadata(params)
+    ref, lref, _ = gp.forward(params, meta)
+    ws = None
+    for i in range(3):
+        out, lse, ws = gp.forward(params, meta, workspace=ws)
+        torch.cuda.synchronize()
+        assert int(ws[:4].view(torch.int32)[0].item()) == 0
+        assert torch.equal(out, ref) and torch.equal(lse, lref), f"call {i}"
+
+
 def test_metadata_mismatch_is_refused():
     p = gi.random_problem(123, device="cuda", mask_mode=1)
     gp = GpuProblem(p)

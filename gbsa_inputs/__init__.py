@@ -473,3 +473,37 @@ def with_atten_mask(p: Problem, seed: int, density: float = 0.3, per_batch: bool
     vals = rng.integers(1, 256, size=(nb, rows, cols), dtype=np.uint8)
     m[:, :, :cols] = np.where(body, vals, 0).astype(np.uint8)
     return dataclasses.replace(p, name=p.name + "_umask", atten_mask=m, atten_mask_cols=cols)
+
+
+def sweep_problem(seed: int, device="cpu", max_len: int = 300) -> Problem:
+    """A random combination of every option (dtype, GQA shape, rows per q-block, selection
+    size, mask mode, window, dual lengths, KV layout, user mask, page padding), for sweeps."""
+    rng = np.random.Generator(np.random.PCG64(seed + 11_000_000))
+    dtype = str(rng.choice(["f16", "bf16", "fp8"]))
+    n2 = int(rng.choice([1, 2, 4]))
+    g = int(rng.choice([1, 2, 4, 8, 16]))
+    kw = dict(dtype=dtype, num_heads_q=n2 * g, num_heads_kv=n2,
+              block_x=int(rng.choice([1, 2, 5, 16, 32, 64, 100, 128])),
+              top_k=int(rng.integers(1, 9)), mask_mode=int(rng.integers(0, 3)),
+              use_seqused_q=bool(rng.random() < 0.4), batch=int(rng.integers(1, 4)),
+              max_len=max_len, return_lse=bool(rng.random() < 0.7),
+              std=float(rng.choice([0.5, 1.0])))
+    if dtype == "fp8":
+        kw["out_dtype"] = str(rng.choice(["f16", "bf16"]))
+        kw["std"] = 0.7
+    if rng.random() < 0.3:
+        kw["win_left"] = int(rng.integers(0, 200))
+    if rng.random() < 0.2:
+        kw["win_right"] = int(rng.integers(0, 50))
+    if kw["mask_mode"] != 1:  # selections over every block, not only causal-eligible ones
+        kw["causal_eligible"] = False
+    layout = str(rng.choice(["paged", "paged", "tnd", "tnd_single"]))
+    if layout == "paged" and rng.random() < 0.4:
+        kw["page_pad"] = int(rng.choice([128, 512]))
+    p = random_problem(seed, device=device, **kw)
+    if layout != "paged":
+        p = to_tnd(p, keep_seqused_kv=(layout == "tnd"), tail_rows=int(rng.integers(0, 2)) * 7)
+    if rng.random() < 0.3:
+        p = with_atten_mask(p, seed, density=float(rng.choice([0.1, 0.5])),
+                            per_batch=bool(rng.random() < 0.5))
+    return dataclasses.replace(p, name=f"sweep_{seed}")

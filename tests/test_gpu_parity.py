@@ -209,6 +209,16 @@ def test_maximum_batch():
     _log(f"max batch: rows {int(done.sum())} O max-abs {err:.3e} LSE rel {lerr:.3e}")
 
 
+@pytest.mark.parametrize("seed", range(200, 232))
+def test_random_sweep(seed):
+    """Random combinations of every option (see gbsa_inputs.sweep_problem) on every kernel,
+    at the library's worker count and at a small random one (forcing split-KV merges)."""
+    p = gi.sweep_problem(seed, device="cuda")
+    P = int(np.random.default_rng(seed).integers(1, 40))
+    for workers in (0, P):
+        _full_check(p, num_workers=workers, label=f"sweep{seed} P={workers}")
+
+
 def test_empty_selections_and_inactive_sequences():
     p = gi.random_problem(120, device="cuda", batch=4, use_seqused_q=True, mask_mode=1)
     cnt = p.sparse_block_count.copy()

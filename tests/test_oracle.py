@@ -285,6 +285,18 @@ def test_top_left_causal():
     assert not np.array_equal(v[0], oa.sparse_attention(oracle_inputs(p))[0], equal_nan=True)
 
 
+@pytest.mark.parametrize("seed", range(10))
+def test_oracle_sweep_matches_sdpa(seed):
+    """Random combinations of every option against SDPA with an independently built mask."""
+    p = gi.sweep_problem(seed, max_len=150)
+    O, L, done = oa.sparse_attention(oracle_inputs(p))
+    Or, Lr = _sdpa_reference(p)
+    np.testing.assert_allclose(O[done], Or[done], rtol=0, atol=1e-12)
+    fin = np.isfinite(Lr[done])
+    assert np.array_equal(fin, np.isfinite(L[done]))
+    np.testing.assert_allclose(L[done][fin], Lr[done][fin], rtol=1e-12, atol=1e-12)
+
+
 def test_all_causal_blocks_equal_dense_causal():
     """Selecting every causal block with a causal mask equals dense causal attention."""
     p = gi.build_problem("dense", seed=11, q_lens=[300, 130], kv_lens=[300, 130],

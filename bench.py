@@ -132,7 +132,6 @@ def gather_offsets(p):
     decode kernel's reads, in task order."""
     import gbsa_inputs as gi
     es = ESIZE[p.dtype]
-    G = p.num_heads_q // p.num_heads_kv
     starts = gi.q_block_starts(p.cu_seqlens_q, p.block_x)
     unit_bytes = (p.kv_page_stride * es if p.kv_layout != "TND"
                   else p.num_heads_kv * 128 * es)
@@ -294,8 +293,23 @@ def cpu_baseline(p, budget_s: float):
             elapsed += time.perf_counter() - t0
             done_units += batch_units
             n *= 2
+        # a workload the oracle finishes early is timed over repeated passes of all of it
+        passes = 1
+        if len(done_units) == len(units) and elapsed < budget_s:
+            inp = host_inputs(done_units)
+            rows = []
+            for (b, gl) in done_units:
+                lo = gl * p.block_x
+                hi = min((gl + 1) * p.block_x, inp.sq(b), inp.storage(b))
+                rows += list(int(p.cu_seqlens_q[b]) + np.arange(lo, hi))
+            while elapsed < budget_s:
+                t0 = time.perf_counter()
+                oa.sparse_attention(inp, rows=rows)
+                elapsed += time.perf_counter() - t0
+                passes += 1
     bytes_s, flops_s = algorithmic_work(p, set(done_units))
-    return dict(units=len(done_units), seconds=elapsed, bytes=bytes_s, flops=flops_s)
+    return dict(units=len(done_units), seconds=elapsed, bytes=bytes_s * passes,
+                flops=flops_s * passes, passes=passes, whole=len(done_units) == len(units))
 
 
 def main(argv=None):
@@ -480,8 +494,10 @@ def main(argv=None):
         cb = cpu_baseline(p, a.cpu_budget)
         v = (cb["bytes"] / cb["seconds"] / 1e9) if hbm_bound else (cb["flops"] / cb["seconds"] / 1e12)
         cpu = {"value": round(v, 6), "unit": unit, "cores": 1, "kind": "oracle",
-               "sample": f"{cb['units']} q-blocks (all KV heads) of the same workload, "
-                         f"{cb['seconds']:.1f} s of single-threaded float64 numpy"}
+               "sample": (f"all {cb['units']} q-blocks (all KV heads) of the workload, "
+                          f"{cb['passes']} passes" if cb["whole"] else
+                          f"{cb['units']} q-blocks (all KV heads) of the same workload") +
+                         f", {cb['seconds']:.1f} s of single-threaded float64 numpy"}
     res = {
         "metric": "block-sparse attn effective TFLOP/s + HBM GB/s, % of roofline, 1 MI355X",
         "value": round(metric_value, 3), "unit": unit, "n_gpus": 1, "steps": a.steps,

@@ -10,6 +10,7 @@ from .api import (  # noqa: F401
     gbsa_forward,
     gbsa_forward_tnd,
     gbsa_forward_ex,
+    gbsa_validate,
     gbsa_metadata,
     gbsa_num_workers,
     gbsa_workspace_size,

@@ -29,7 +29,12 @@ KV_PA_BBND, KV_TND = 0, 1
 MAX_KV_ROWS = 2147483520
 
 EXPORTED = ("gbsa_check_params", "gbsa_num_workers", "gbsa_metadata", "gbsa_workspace_size",
-            "gbsa_forward", "gbsa_forward_tnd", "gbsa_forward_ex", "gbsa_status_string")
+            "gbsa_forward", "gbsa_forward_tnd", "gbsa_forward_ex", "gbsa_validate",
+            "gbsa_status_string")
+# gbsa_validate violation bits (include/gbsa.h)
+VALIDATE_BITS = {0x01: "cu_seqlens_q", 0x02: "seqused_q", 0x04: "kv_length",
+                 0x08: "cu_seqlens_kv", 0x10: "block_table", 0x20: "count", 0x40: "selection",
+                 0x80: "mask_extent"}
 MASK_NONE, MASK_CAUSAL, MASK_CAUSAL_TOP_LEFT = 0, 1, 2
 
 
@@ -130,6 +135,8 @@ def load() -> ctypes.CDLL:
     lib.gbsa_forward_tnd.restype = ctypes.c_int
     lib.gbsa_forward_ex.argtypes = [P, ctypes.POINTER(GbsaForwardArgs), vp]
     lib.gbsa_forward_ex.restype = ctypes.c_int
+    lib.gbsa_validate.argtypes = [P, ctypes.POINTER(GbsaForwardArgs), vp, vp]
+    lib.gbsa_validate.restype = ctypes.c_int
     lib.gbsa_status_string.argtypes = [ctypes.c_int]
     lib.gbsa_status_string.restype = ctypes.c_char_p
     _lib = lib

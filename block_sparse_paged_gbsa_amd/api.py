@@ -217,6 +217,31 @@ def aligned_mask(atten_mask: torch.Tensor) -> torch.Tensor:
     return out[..., :cols]
 
 
+def gbsa_validate(params: GbsaParams, sparse_block_idx, sparse_block_count, cu_seqlens_q,
+                  seqused_q=None, *, cu_seqlens_kv=None, seqused_kv=None, block_table=None,
+                  atten_mask=None, stream=None) -> int:
+    """Opt-in check of the tensor values the forward calls trust; returns the violation bits
+    (0 = none; names in _lib.VALIDATE_BITS). Synchronises the stream to read the result."""
+    g = _lib.GbsaForwardArgs()
+    ptr = lambda t: None if t is None else t.data_ptr()
+    g.sparse_block_idx = ptr(sparse_block_idx)
+    g.sparse_block_count = ptr(sparse_block_count)
+    g.cu_seqlens_q = ptr(cu_seqlens_q)
+    g.seqused_q = ptr(seqused_q)
+    g.cu_seqlens_kv = ptr(cu_seqlens_kv)
+    g.seqused_kv = ptr(seqused_kv)
+    g.block_table = ptr(block_table)
+    if atten_mask is not None:
+        m = atten_mask.view(torch.uint8) if atten_mask.dtype == torch.bool else atten_mask
+        bs, rs, rows, cols = _mask_geometry(m)
+        g.atten_mask = m.data_ptr()
+        g.mask_batch_stride, g.mask_row_stride, g.mask_rows, g.mask_cols = bs, rs, rows, cols
+    flags = torch.zeros(1, dtype=torch.int32, device=sparse_block_count.device)
+    check("gbsa_validate", _lib.load().gbsa_validate(ctypes.byref(params), ctypes.byref(g),
+                                                     _ptr(flags), _stream(stream)))
+    return int(flags.item())
+
+
 def gbsa_forward_ex(params: GbsaParams, q, k, v, sparse_block_idx, sparse_block_count,
                     metadata, cu_seqlens_q, seqused_q=None, *, cu_seqlens_kv=None,
                     seqused_kv=None, block_table=None, q_scale=None, k_scale=None,

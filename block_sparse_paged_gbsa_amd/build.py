@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgbsa.so")
-SOURCES = ["api.hip", "metadata.hip", "fwd_decode.hip", "fwd_prefill.hip"]
+SOURCES = ["api.hip", "metadata.hip", "fwd_decode.hip", "fwd_prefill.hip", "validate.hip"]
 # measurement probes (HBM ceilings for the benchmark), a library of their own
 PROBE_LIB = os.path.join(HERE, "libgbsa_probe.so")
 PROBE_SOURCES = ["probe.hip"]

@@ -402,6 +402,44 @@ gbsa_status gbsa_forward_ex(const gbsa_params* p, const gbsa_forward_args* args,
     return forward_impl(p, args, stream);
 }
 
+gbsa_status gbsa_validate(const gbsa_params* p, const gbsa_forward_args* g,
+                          int32_t* violations, hipStream_t stream) {
+    gbsa_status st = gbsa_check_params(p);
+    if (st != GBSA_OK) return st;
+    if (g == nullptr || violations == nullptr) return GBSA_ERR_NULL;
+    const bool tnd = p->kv_layout == GBSA_KV_TND;
+    if (g->sparse_block_idx == nullptr || g->sparse_block_count == nullptr ||
+        g->cu_seqlens_q == nullptr)
+        return GBSA_ERR_NULL;
+    if (tnd ? (g->cu_seqlens_kv == nullptr || g->block_table != nullptr)
+            : (g->seqused_kv == nullptr || g->block_table == nullptr || g->cu_seqlens_kv != nullptr))
+        return GBSA_ERR_NULL;
+    if ((g->seqused_q != nullptr) != (p->has_seqused_q == 1)) return GBSA_ERR_NULL;
+    ValArgs a;
+    memset(&a, 0, sizeof(a));
+    a.cu = g->cu_seqlens_q;
+    a.squ = g->seqused_q;
+    a.skv = g->seqused_kv;
+    a.cu_kv = tnd ? g->cu_seqlens_kv : nullptr;
+    a.table = tnd ? nullptr : g->block_table;
+    a.cnt = g->sparse_block_count;
+    a.idx = g->sparse_block_idx;
+    a.umask = g->atten_mask;
+    a.out = violations;
+    a.total_q = p->total_q;
+    a.num_pages = p->num_pages;
+    a.kv_rows = tnd ? p->num_pages : 0;
+    a.B = p->batch;
+    a.N2 = p->num_heads_kv;
+    a.X = p->block_x;
+    a.tqb = p->total_q_blocks;
+    a.topK = p->top_k;
+    a.maxb = tnd ? 0 : p->max_blocks_per_seq;
+    a.um_rows = g->atten_mask != nullptr ? g->mask_rows : 0;
+    a.um_cols = g->atten_mask != nullptr ? g->mask_cols : 0;
+    return launch_validate(a, stream) == hipSuccess ? GBSA_OK : GBSA_ERR_HIP;
+}
+
 const char* gbsa_status_string(gbsa_status s) {
     switch (s) {
         case GBSA_OK: return "ok";

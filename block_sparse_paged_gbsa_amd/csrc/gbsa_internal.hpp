@@ -72,6 +72,21 @@ struct FwdArgs {
     int32_t expect[kHeaderWords];  // expected header words (0, 1, 2 and 7..21 are checked)
 };
 
+// Arguments of the opt-in value check (gbsa_validate).
+struct ValArgs {
+    const int64_t* cu;      // [B+1]
+    const int32_t* squ;     // [B] or null
+    const int32_t* skv;     // [B] or null
+    const int64_t* cu_kv;   // [B+1] token-major, else null
+    const int32_t* table;   // [B, maxb] paged, else null
+    const int32_t* cnt;     // [N2, tqb]
+    const int32_t* idx;     // [N2, tqb, topK]
+    const uint8_t* umask;   // user mask or null (only its extent is checked)
+    int32_t* out;           // device flags
+    int64_t total_q, num_pages, kv_rows;
+    int32_t B, N2, X, tqb, topK, maxb, um_rows, um_cols;
+};
+
 // Workspace layout (byte offsets), a pure function of P and M.
 struct WsLayout {
     size_t status, arrive, o, m, l, total;
@@ -92,6 +107,7 @@ inline WsLayout ws_layout(int64_t P, int64_t M, int64_t nst) {
 
 // Launchers (each defined next to its kernel).
 hipError_t launch_metadata(const MetaArgs& a, hipStream_t s);
+hipError_t launch_validate(const ValArgs& a, hipStream_t s);
 // Main kernel choice: rows per unit M = blockShapeX * G. M <= 16 uses the decode kernel
 // (KV slots spread over the waves), larger M the prefill kernel (rows over the waves).
 hipError_t launch_decode(const FwdArgs& a, int dtype, int out_dtype, hipStream_t s);

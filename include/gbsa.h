@@ -304,6 +304,34 @@ typedef struct gbsa_forward_args {
 gbsa_status gbsa_forward_ex(const gbsa_params* params, const gbsa_forward_args* args,
                             hipStream_t stream);
 
+/*
+ * Opt-in check of the tensor VALUES that the forward calls take on trust (the article's
+ * "general constraints": tiling reads no tensor values, so the caller guarantees them). Runs
+ * one small kernel over the same argument block as gbsa_forward_ex and ORs into *violations
+ * (device int32, which the caller zeroes beforehand) one bit per broken rule:
+ */
+#define GBSA_BAD_CU_SEQLENS_Q 0x01  /* cu_seqlens_q: negative start, decreasing, past total_q,
+                                       or implying another total_q_blocks */
+#define GBSA_BAD_SEQUSED_Q 0x02     /* seqused_q[b] outside [0, q storage length of b] */
+#define GBSA_BAD_KV_LENGTH 0x04     /* seqused_kv[b] < 0, or above the KV storage (PA_BBND:
+                                       max_blocks_per_seq * 128; TND: cu_seqlens_kv span) */
+#define GBSA_BAD_CU_SEQLENS_KV 0x08 /* TND: cu_seqlens_kv negative, decreasing or past T_kv */
+#define GBSA_BAD_BLOCK_TABLE 0x10   /* PA_BBND: a page of a visible block outside
+                                       [0, num_pages) */
+#define GBSA_BAD_COUNT 0x20         /* sparse_block_count outside [0, top_k] (clamped) */
+#define GBSA_BAD_SELECTION 0x40     /* a selected index (slot < count, >= 0) past the
+                                       sequence's visible KV blocks (skipped by the kernels) */
+#define GBSA_BAD_MASK_EXTENT 0x80   /* user mask rows/cols do not cover every active query row
+                                       and visible key (the uncovered ones are not masked) */
+/*
+ * Rules 0x20, 0x40 and 0x80 describe inputs the kernels handle in a defined way (clamp, skip,
+ * leave unmasked); the others make the forward read undefined data. Errors (returned, nothing
+ * enqueued): as gbsa_forward_ex, minus the metadata/workspace/output pointers, which are not
+ * needed here; GBSA_ERR_NULL if violations is NULL.
+ */
+gbsa_status gbsa_validate(const gbsa_params* params, const gbsa_forward_args* args,
+                          int32_t* violations, hipStream_t stream);
+
 /* Human-readable text for a status (static storage). */
 const char* gbsa_status_string(gbsa_status status);
 

@@ -214,3 +214,17 @@ def test_probe_library_exports_its_header():
     assert lib.gbsa_probe_gather(None, None, None, 0, 256, 2048, None, None) == -1
     assert lib.gbsa_probe_stream(ctypes.c_void_p(0x1000), 15, 1, ctypes.c_void_p(0x1000),
                                  None) == -1
+
+
+def test_validate_argument_checks():
+    """gbsa_validate refuses missing or inconsistent pointers before any device work."""
+    lib = _lib.load()
+    good = _good()
+    d = ctypes.c_void_p(0x1000)
+    v = lambda p, g, out: lib.gbsa_validate(ctypes.byref(p), None if g is None else
+                                            ctypes.byref(g), out, None)
+    assert v(good, _args(), None) == 1  # violations pointer
+    assert v(good, None, d) == 1
+    assert v(good, _args(block_table=None), d) == 1  # paged needs the block table
+    assert v(good, _args(cu_seqlens_kv=0x3000), d) == 1  # and no cu_seqlens_kv
+    assert v(_good(head_dim=64), _args(), d) == 2  # parameter errors first

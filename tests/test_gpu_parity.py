@@ -461,6 +461,50 @@ def test_workspace_reuse(kw):
         assert torch.equal(out, ref) and torch.equal(lse, lref), f"call {i}"
 
 
+def _validate(p, **over):
+    from block_sparse_paged_gbsa_amd import gbsa_validate
+    gp = GpuProblem(p)
+    t = dict(cnt=gp.cnt, idx=gp.idx, cu=gp.cu, squ=gp.squ, skv=gp.skv, table=gp.table,
+             cu_kv=gp.cu_kv, umask=gp.umask)
+    t.update(over)
+    return gbsa_validate(gpu_params(p), t["idx"], t["cnt"], t["cu"], t["squ"],
+                         cu_seqlens_kv=t["cu_kv"], seqused_kv=t["skv"], block_table=t["table"],
+                         atten_mask=t["umask"])
+
+
+def test_validate_reports_each_broken_rule():
+    """The opt-in value check is silent on valid inputs and names each planted violation."""
+    from block_sparse_paged_gbsa_amd._lib import VALIDATE_BITS
+    bit = {v: k for k, v in VALIDATE_BITS.items()}
+    p = gi.random_problem(191, device="cuda", batch=3, mask_mode=1, use_seqused_q=True)
+    assert _validate(p) == 0
+    gp = GpuProblem(p)
+    dev = lambda a: torch.as_tensor(np.ascontiguousarray(a)).to("cuda")
+    cu = p.cu_seqlens_q.copy(); cu[1] = cu[2] + 1  # decreasing
+    assert _validate(p, cu=dev(cu)) & bit["cu_seqlens_q"]
+    squ = p.seqused_q.copy(); squ[0] = np.diff(p.cu_seqlens_q)[0] + 1
+    assert _validate(p, squ=dev(squ)) == bit["seqused_q"]
+    skv = p.seqused_kv.copy(); skv[2] = p.block_table.shape[1] * 128 + 1
+    assert _validate(p, skv=dev(skv)) & bit["kv_length"]
+    tab = p.block_table.copy(); tab[1, 0] = p.num_pages
+    assert _validate(p, table=dev(tab)) == bit["block_table"]
+    cnt = p.sparse_block_count.copy(); cnt[0, 0] = p.top_k + 1
+    assert _validate(p, cnt=dev(cnt)) == bit["count"]
+    idx = p.sparse_block_idx.copy(); c0 = int(p.sparse_block_count[0, 0])
+    assert c0 > 0
+    idx[0, 0, 0] = 10_000
+    assert _validate(p, idx=dev(idx)) == bit["selection"]
+    # token-major key/value: cu_seqlens_kv past the tensor
+    t = gi.to_tnd(p)
+    assert _validate(t) == 0
+    cukv = t.cu_seqlens_kv.copy(); cukv[-1] = t.num_pages + 5
+    assert _validate(t, cu_kv=dev(cukv)) & bit["cu_seqlens_kv"]
+    # a user mask that covers too few keys
+    m = gi.with_atten_mask(p, 191, cols=10)
+    assert _validate(m) == bit["mask_extent"]
+    assert _validate(gi.with_atten_mask(p, 191)) == 0
+
+
 def test_metadata_mismatch_is_refused():
     p = gi.random_problem(123, device="cuda", mask_mode=1)
     gp = GpuProblem(p)

@@ -182,7 +182,7 @@ __device__ __forceinline__ void compute_quarter(const FwdArgs& a, const Quarter&
 template <int DT, int OUT, int LAYOUT, bool UM>
 __global__ __launch_bounds__(256, 2) void fwd_decode_kernel(FwdArgs a) {
     __shared__ __attribute__((aligned(16))) unsigned char smem[Lds<DT>::bytes];
-    __shared__ int flag[1];
+    static_assert(sizeof(smem) >= kPieceListBytes, "the split merge borrows the stages");
     constexpr int esz = (DT == kFP8) ? 1 : 2;
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -364,21 +364,22 @@ __global__ __launch_bounds__(256, 2) void fwd_decode_kernel(FwdArgs a) {
                     // 32-bit unsigned indices (2P x 16 rows fit): the compiler cannot split
                     // them into a per-lane 64-bit part and keep it live across the unit loop
                     const uint32_t mi = (uint32_t)slot * (uint32_t)a.M + (uint32_t)c;
-                    float* po = a.ws_o + (mi * 128u + (uint32_t)d0);
-                    *(f32x4*)po = (f32x4){acc[0], acc[1], acc[2], acc[3]} * vscale;
-                    *(f32x4*)(po + 4) = (f32x4){acc[4], acc[5], acc[6], acc[7]} * vscale;
+                    const rsrc_t ro = ws_o_rsrc(a, slot);
+                    ws_put4(ro, (c * 128 + d0) * 4,
+                            (f32x4){acc[0], acc[1], acc[2], acc[3]} * vscale);
+                    ws_put4(ro, (c * 128 + d0 + 4) * 4,
+                            (f32x4){acc[4], acc[5], acc[6], acc[7]} * vscale);
                     if (d0 == 0) {
-                        a.ws_m[mi] = mstar;
-                        a.ws_l[mi] = lsum;
+                        ws_put1(a.ws_m + mi, mstar);
+                        ws_put1(a.ws_l + mi, lsum);
                     }
                 }
             }
         }
         if (!complete) {
-            const int w_a = unit_starter(a.meta, w, u);
-            const int np = count_pieces(a.meta, w_a, u);
-            if (piece_arrive(a, w_a, np, flag))
-                merge_rows<OUT>(a, w_a, u, 0, rows_exist, it.b, it.n2, t0, it.row0, it.sq);
+            int* list = (int*)smem;  // the stages are free until the next unit
+            const int np = piece_arrive(a, w, u, 0, 1, list);
+            if (np > 0) merge_rows<OUT>(a, list, np, 0, rows_exist, it.n2, t0, it.row0, it.sq);
         }
         __syncthreads();
         advance_unit(a, it);

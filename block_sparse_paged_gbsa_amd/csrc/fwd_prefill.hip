@@ -386,15 +386,15 @@ __device__ __forceinline__ void write_rows(const FwdArgs& a, const UnitIter& it,
             if (a.return_lse && lgrp == 0)
                 a.lse[orow] = ltot > 0.f ? (mrun[nq] + __log2f(ltot)) * kLn2 : kNegInf;
         } else {
-            float* po = a.ws_o + ((int64_t)slot * a.M + r) * 128;
+            const rsrc_t ro = ws_o_rsrc(a, slot);
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) {
                 const int d = dt * 16 + lgrp * 4;
-                *(f32x4*)(po + d) = o[dt][nq] * vscale;
+                ws_put4(ro, (r * 128 + d) * 4, o[dt][nq] * vscale);
             }
             if (lgrp == 0) {
-                a.ws_m[(int64_t)slot * a.M + r] = mrun[nq];
-                a.ws_l[(int64_t)slot * a.M + r] = ltot;
+                ws_put1(a.ws_m + (int64_t)slot * a.M + r, mrun[nq]);
+                ws_put1(a.ws_l + (int64_t)slot * a.M + r, ltot);
             }
         }
     }
@@ -406,7 +406,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_prefill_kernel(FwdArgs a) {
     constexpr int R = NW * NQ * 16;
     constexpr int esz = (DT == kFP8) ? 1 : 2;
     __shared__ __attribute__((aligned(16))) unsigned char smem[2 * PageStage<DT>::bytes];
-    __shared__ int flag[1];
+    static_assert(sizeof(smem) >= kPieceListBytes, "the split merge borrows the stages");
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform for the compiler
@@ -524,11 +524,11 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_prefill_kernel(FwdArgs a) {
             write_rows<DT, OUT, NQ>(a, it, complete, 2 * w + (sa > 0 ? 0 : 1),
                                     row_base + wave * NQ * 16, lane, trow, rvalid, mrun, lrun, o);
             if (!complete) {
-                const int w_a = unit_starter(a.meta, w, u);
-                const int np = count_pieces(a.meta, w_a, u);
-                if (piece_arrive(a, w_a * a.nst + st, np, flag))
-                    merge_rows<OUT>(a, w_a, u, row_base, min(row_base + R, rows_exist), it.b,
-                                    it.n2, t0, it.row0, it.sq);
+                int* list = (int*)smem;  // the stages are free until the next task
+                const int np = piece_arrive(a, w, u, st, a.nst, list);
+                if (np > 0)
+                    merge_rows<OUT>(a, list, np, row_base, min(row_base + R, rows_exist), it.n2,
+                                    t0, it.row0, it.sq);
                 __syncthreads();
             }
         }
@@ -806,18 +806,19 @@ __device__ __forceinline__ void write_rows32(const FwdArgs& a, const UnitIter& i
         if (a.return_lse && h2 == 0)
             a.lse[orow] = ltot > 0.f ? (mrun + __log2f(ltot)) * kLn2 : kNegInf;
     } else {
-        float* po = a.ws_o + ((int64_t)slot * a.M + r) * 128;
+        const rsrc_t ro = ws_o_rsrc(a, slot);
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int d = dt * 32 + 8 * g + 4 * h2;
-                *(f32x4*)(po + d) = (f32x4){o[dt][4 * g], o[dt][4 * g + 1], o[dt][4 * g + 2],
-                                            o[dt][4 * g + 3]} * vscale;
+                ws_put4(ro, (r * 128 + d) * 4,
+                        (f32x4){o[dt][4 * g], o[dt][4 * g + 1], o[dt][4 * g + 2],
+                                o[dt][4 * g + 3]} * vscale);
             }
         if (h2 == 0) {
-            a.ws_m[(int64_t)slot * a.M + r] = mrun;
-            a.ws_l[(int64_t)slot * a.M + r] = ltot;
+            ws_put1(a.ws_m + (int64_t)slot * a.M + r, mrun);
+            ws_put1(a.ws_l + (int64_t)slot * a.M + r, ltot);
         }
     }
 }
@@ -834,7 +835,8 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32_kernel(FwdArgs a) {
     __shared__ __attribute__((aligned(16))) unsigned char smem[2 * KB + 2 * VB];
     // the task's visible blocks in order: (unit, j * 4 + class, records of half 0, of half 1)
     __shared__ int4 plist[256];
-    __shared__ int flag[2];
+    __shared__ int flag[1];
+    static_assert(sizeof(smem) >= kPieceListBytes, "the split merge borrows the stages");
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -914,10 +916,10 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32_kernel(FwdArgs a) {
                     }
                     n += __builtin_popcountll(m);
                 }
-                if (lane == 0) flag[1] = n;
+                if (lane == 0) flag[0] = n;
             }
             __syncthreads();
-            const int nh = 2 * __builtin_amdgcn_readfirstlane(flag[1]);  // half pages
+            const int nh = 2 * __builtin_amdgcn_readfirstlane(flag[0]);  // half pages
 
             // address of half page q (K or V) of this head in HBM
             auto half_src = [&](const unsigned char* base, int q) {
@@ -1014,11 +1016,11 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32_kernel(FwdArgs a) {
             write_rows32<DT, OUT>(a, it, complete, 2 * w + (sa > 0 ? 0 : 1), row0, lane, trow, rvalid,
                                   mrun, lrun, o);
             if (!complete) {
-                const int w_a = unit_starter(a.meta, w, u);
-                const int np = count_pieces(a.meta, w_a, u);
-                if (piece_arrive(a, w_a * a.nst + st, np, flag))
-                    merge_rows<OUT>(a, w_a, u, row_base, min(row_base + R, rows_exist), it.b,
-                                    it.n2, t0, it.row0, it.sq);
+                int* list = (int*)smem;  // the stages are free until the next task
+                const int np = piece_arrive(a, w, u, st, a.nst, list);
+                if (np > 0)
+                    merge_rows<OUT>(a, list, np, row_base, min(row_base + R, rows_exist), it.n2,
+                                    t0, it.row0, it.sq);
                 __syncthreads();
             }
         }
@@ -1053,7 +1055,8 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32_kernel(FwdArgs a) {
     // [K buffer 0][K buffer 1][V buffer 0][V buffer 1]; reused for the final merge
     __shared__ __attribute__((aligned(16))) unsigned char smem[kLds];
     __shared__ int4 plist[256];  // as in the row-split kernel
-    __shared__ int flag[2];
+    __shared__ int flag[1];
+    static_assert(sizeof(smem) >= kPieceListBytes, "the split merge borrows the stages");
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1132,10 +1135,10 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32_kernel(FwdArgs a) {
                     }
                     n += __builtin_popcountll(m);
                 }
-                if (lane == 0) flag[1] = n;
+                if (lane == 0) flag[0] = n;
             }
             __syncthreads();
-            const int n = __builtin_amdgcn_readfirstlane(flag[1]);  // items per group
+            const int n = __builtin_amdgcn_readfirstlane(flag[0]);  // items per group
             const int nh = 2 * n;                                   // half pages
 
             // address of half page q (K or V) of this head in HBM; q is clamped into the stream
@@ -1256,11 +1259,11 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32_kernel(FwdArgs a) {
             }
             __syncthreads();  // LDS is reused by the next task
             if (!complete) {
-                const int w_a = unit_starter(a.meta, w, u);
-                const int np = count_pieces(a.meta, w_a, u);
-                if (piece_arrive(a, w_a * a.nst + st, np, flag))
-                    merge_rows<OUT>(a, w_a, u, row_base, min(row_base + R, rows_exist), it.b,
-                                    it.n2, t0, it.row0, it.sq);
+                int* list = (int*)smem;  // the stages are free until the next task
+                const int np = piece_arrive(a, w, u, st, a.nst, list);
+                if (np > 0)
+                    merge_rows<OUT>(a, list, np, row_base, min(row_base + R, rows_exist), it.n2,
+                                    t0, it.row0, it.sq);
                 __syncthreads();
             }
         }

@@ -187,6 +187,21 @@ def test_maximum_group_and_top_k(block_x, dtype):
         _full_check(p, num_workers=P, label=f"group128 x{block_x} P={P}")
 
 
+@pytest.mark.parametrize("num_heads_kv", [1, 4])
+def test_unit_split_into_many_pieces(num_heads_kv):
+    """One decode query over a 256-slot selection per KV head, cut into hundreds of pieces:
+    with one KV head most of the 999 workers are empty (pieces are separated by empty
+    workers); with four, nearly every worker holds a one-slot piece, so a unit's pieces span
+    more than 64 consecutive workers. The merge must find and combine all of them."""
+    p = gi.build_problem("many_pieces", seed=181, q_lens=[1], kv_lens=[32768],
+                         num_heads_q=4 * num_heads_kv, num_heads_kv=num_heads_kv, block_x=1,
+                         top_k=256, dtype="bf16", select=gi.select_decode_last_plus(255),
+                         causal_eligible=False, mask_mode=0, return_lse=True,
+                         scale=1.0 / 128 ** 0.5, device="cuda")
+    for P in (999, 300, 0):
+        _full_check(p, num_workers=P, label=f"many pieces N2={num_heads_kv} P={P}")
+
+
 def test_maximum_batch():
     """GBSA_MAX_BATCH = 16384 decode-shaped sequences (the scheduler's chunked path), checked
     on sampled sequences including the first and the last."""

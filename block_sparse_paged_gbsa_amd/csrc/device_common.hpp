@@ -200,12 +200,14 @@ __device__ __forceinline__ KvSrc kv_src(const void* base, int64_t off, int rs, i
 // ---------------------------------------------------------------------------
 // Metadata access shared by the main and combine kernels.
 // ---------------------------------------------------------------------------
+// Every word is compared (no short circuit), so the loads issue together: one round trip.
 __device__ __forceinline__ bool header_ok(const FwdArgs& a) {
     const int32_t* m = a.meta;
-    bool ok = (m[0] == a.expect[0]) && (m[1] == a.expect[1]) && (m[2] == a.expect[2]);
+    uint32_t diff = (uint32_t)(m[0] ^ a.expect[0]) | (uint32_t)(m[1] ^ a.expect[1]) |
+                    (uint32_t)(m[2] ^ a.expect[2]);
 #pragma unroll
-    for (int i = kCheckFirst; i <= kCheckLast; ++i) ok = ok && (m[i] == a.expect[i]);
-    return ok;
+    for (int i = kCheckFirst; i <= kCheckLast; ++i) diff |= (uint32_t)(m[i] ^ a.expect[i]);
+    return diff == 0;
 }
 
 struct Bound {
@@ -242,21 +244,41 @@ __device__ __forceinline__ void batch_lengths(const FwdArgs& a, int b, int64_t* 
     *sq = s;
 }
 
+// Lengths of sequence b (zeros past the last one), one sequence per lane.
+struct SeqLens {
+    int64_t r0;  // cu_seqlens_q[b]
+    int st, sq;  // storage and active length
+};
+__device__ __forceinline__ SeqLens seq_lens(const FwdArgs& a, int b) {
+    SeqLens l{0, 0, 0};
+    if (b < a.B) {
+        // all three loads issue together: without seqused_q the third one rereads cu_seqlens_q
+        const int32_t* su = a.squ != nullptr ? a.squ + b : (const int32_t*)(a.cu + b);
+        const int64_t c0 = a.cu[b], c1 = a.cu[b + 1];
+        const int sv = *su;
+        l.r0 = c0;
+        l.st = (int)(c1 - c0);
+        l.sq = a.squ != nullptr ? min(max(sv, 0), l.st) : l.st;
+    }
+    return l;
+}
+
 // Find the batch holding unit u0. Every wave scans the batches on its own (64 per step, wave
 // prefix sums, no LDS and no barrier), so all lanes of the block end with the same answer.
-// Returns it.b = -1 when u0 lies beyond the last unit.
-__device__ inline UnitIter locate_unit(const FwdArgs& a, int u0) {
+// `first` may carry the lengths of sequences 0..63 (lane = sequence), loaded early by the
+// caller so that their latency overlaps its own first loads. Returns it.b = -1 when u0 lies
+// beyond the last unit.
+__device__ inline UnitIter locate_unit(const FwdArgs& a, int u0, const SeqLens* first = nullptr) {
     const int lane = threadIdx.x & 63;
     int ucarry = 0, qcarry = 0, found_b = -1, found_u = 0, found_q = 0;
+    UnitIter it;
     for (int base = 0; base < a.B && found_b < 0; base += 64) {
         const int b = base + lane;
+        const SeqLens l = (base == 0 && first != nullptr) ? *first : seq_lens(a, b);
         int nu = 0, nq = 0;
         if (b < a.B) {
-            int64_t r0;
-            int st, sq;
-            batch_lengths(a, b, &r0, &st, &sq);
-            nq = ceil_div_i(st, a.X);
-            nu = a.N2 * ceil_div_i(sq, a.X);
+            nq = ceil_div_i(l.st, a.X);
+            nu = a.N2 * ceil_div_i(l.sq, a.X);
         }
         int iu = nu, iq = nq;  // inclusive wave scans
 #pragma unroll
@@ -271,19 +293,23 @@ __device__ inline UnitIter locate_unit(const FwdArgs& a, int u0) {
         const uint64_t hit = __ballot(b < a.B && nu > 0 && u0 >= uex && u0 < uex + nu);
         // values read across lanes are uniform: tell the compiler (scalar registers)
         if (hit) {
-            const int l = __builtin_ctzll(hit);
-            found_b = base + l;
-            found_u = __builtin_amdgcn_readlane(uex, l);
-            found_q = __builtin_amdgcn_readlane(qex, l);
+            const int h = __builtin_ctzll(hit);
+            found_b = base + h;
+            found_u = __builtin_amdgcn_readlane(uex, h);
+            found_q = __builtin_amdgcn_readlane(qex, h);
+            const uint64_t r0 = (uint64_t)l.r0;
+            it.row0 = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(r0 >> 32), h)
+                                 << 32) |
+                                (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)r0, h));
+            it.storage = __builtin_amdgcn_readlane(l.st, h);
+            it.sq = __builtin_amdgcn_readlane(l.sq, h);
         }
         ucarry += __builtin_amdgcn_readlane(iu, 63);
         qcarry += __builtin_amdgcn_readlane(iq, 63);
     }
-    UnitIter it;
     it.b = found_b;
     if (found_b < 0) return it;
     const int local = u0 - found_u;
-    batch_lengths(a, found_b, &it.row0, &it.storage, &it.sq);
     it.nact = ceil_div_i(it.sq, a.X);
     it.n2 = local / it.nact;
     it.gl = local % it.nact;

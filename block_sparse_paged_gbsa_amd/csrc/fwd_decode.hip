@@ -190,14 +190,18 @@ __global__ __launch_bounds__(256, 2) void fwd_decode_kernel(FwdArgs a) {
     const int lrow = lane & 15, lgrp = lane >> 4;
     const int w = xcd_remap(blockIdx.x, gridDim.x);
 
-    if (!header_ok(a)) {
+    // one round trip for the header, this worker's bounds and the first 64 sequences' lengths
+    // (the metadata buffer always holds kMetaWords words, so the bound reads stay inside it)
+    const bool ok = header_ok(a);
+    const Bound b0 = read_bound(a.meta, w), b1 = read_bound(a.meta, w + 1);
+    const int U = a.meta[3];
+    const SeqLens first = seq_lens(a, lane);
+    if (!ok) {
         if (tid == 0) atomicOr(a.ws_status, 1);
         return;
     }
-    const Bound b0 = read_bound(a.meta, w), b1 = read_bound(a.meta, w + 1);
-    const int U = a.meta[3];
     if (!bound_less(b0, b1) || b0.u >= U) return;
-    UnitIter it = locate_unit(a, b0.u);
+    UnitIter it = locate_unit(a, b0.u, &first);
     if (it.b < 0) return;
 
     unsigned char* stage = smem + wave * Stage<DT>::bytes;
@@ -208,6 +212,11 @@ __global__ __launch_bounds__(256, 2) void fwd_decode_kernel(FwdArgs a) {
         const int sa = (u == b0.u) ? b0.s : 0;
         if (u >= U || u > b1.u || (u == b1.u && sa >= b1.s)) break;
         const int g = it.qbase + it.gl;
+        const int32_t* sel = a.idx + ((int64_t)it.n2 * a.tqb + g) * a.topK;
+        // the first 64 slots are read together with their count (in-row reads past the count
+        // are ignored)
+        int jfirst = -1;
+        if (g < a.tqb && sa + lane < a.topK) jfirst = sel[sa + lane];
         int cnt = 0;
         if (g < a.tqb) cnt = min(max(a.cnt[(int64_t)it.n2 * a.tqb + g], 0), a.topK);
         const int se = (u == b1.u) ? b1.s : cnt;
@@ -250,7 +259,6 @@ __global__ __launch_bounds__(256, 2) void fwd_decode_kernel(FwdArgs a) {
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) st.o[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-        const int32_t* sel = a.idx + ((int64_t)it.n2 * a.tqb + g) * a.topK;
         const int64_t qbyte = (int64_t)wave * 32 * rs;  // this wave's token quarter
         for (int c0 = sa; c0 < se; c0 += 64) {
             // slots c0 .. c0+63: lane l holds slot c0 + l
@@ -259,7 +267,7 @@ __global__ __launch_bounds__(256, 2) void fwd_decode_kernel(FwdArgs a) {
             // the records of this wave's quarter window
             int jcl = 0, pl = 0, rl = 0;
             if (lane < n) {
-                const int jl = sel[c0 + lane];
+                const int jl = (c0 == sa) ? jfirst : sel[c0 + lane];
                 if (jl >= 0) {
                     const int cl = block_class(a, (int64_t)jl * 128, skv, off, t_lo, t_hi);
                     if (cl != 0) {

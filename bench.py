@@ -324,6 +324,11 @@ def main(argv=None):
                     help="causal: replace the built-in causal mask of a causal workload with an "
                          "equal user attention mask (same visible keys, timed through the "
                          "per-element mask path)")
+    ap.add_argument("--batch", type=int, default=64,
+                    help="workload 2 only: number of decode queries (fewer than 64 splits "
+                         "each unit over several workers)")
+    ap.add_argument("--top-k", type=int, default=16,
+                    help="workload 2 only: pages selected per query (at most 256)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -346,7 +351,14 @@ def main(argv=None):
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     log(f"[bench] generating workload {a.config} on the GPU")
-    p = gi.config(a.config, device=dev)
+    if (a.batch, a.top_k) != (64, 16):
+        if a.config != 2 or not 1 <= a.batch <= 4096 or not 1 <= a.top_k <= 256:
+            print("--batch / --top-k apply to workload 2 (1..4096 queries, 1..256 pages)",
+                  file=sys.stderr)
+            return 2
+        p = gi.decode_workload(a.batch, a.top_k, device=dev)
+    else:
+        p = gi.config(a.config, device=dev)
     tnd = a.kv_layout == "tnd"
     if tnd:
         log("[bench] rewriting key/value into the token-major TND layout")
@@ -473,8 +485,8 @@ def main(argv=None):
     kernel = ("fwd_decode_kernel" if rows <= 16 else
               "fwd_prefill_pp32_kernel" if rows > 256 else
               "fwd_prefill_ks32_kernel" if rows > 64 else "fwd_prefill_kernel")
-    workload = (gi.CONFIG_NAMES[a.config] + ("_tnd" if tnd else "") +
-                ("_user_mask" if umask is not None else ""))
+    # the name carries "_tnd" after the layout rewrite
+    workload = p.name + ("_user_mask" if umask is not None else "")
     traffic = measured_traffic(kernel, workload)
     if hbm_bound:
         achieved = alg_bytes / (fwd_ms * 1e-3) / 1e9

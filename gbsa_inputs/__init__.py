@@ -332,6 +332,19 @@ CONFIG_NAMES = {
 }
 
 
+def decode_workload(batch: int = 64, top_k: int = 16, device="cpu",
+                    values: bool = True) -> Problem:
+    """Workload 2 and its variants: `batch` single-token queries over 32768-token paged
+    sequences (N1=32, N2=8, bf16), each selecting its last page plus top_k - 1 random ones.
+    Smaller batches and longer selections cut each unit over several workers (split-KV)."""
+    name = CONFIG_NAMES[2] if (batch, top_k) == (64, 16) else f"decode_bf16_b{batch}_top{top_k}"
+    return build_problem(name, seed=1002, q_lens=[1] * batch, kv_lens=[32768] * batch,
+                         num_heads_q=32, num_heads_kv=8, block_x=1, top_k=top_k, dtype="bf16",
+                         select=select_decode_last_plus(top_k - 1), causal_eligible=False,
+                         mask_mode=0, return_lse=False, scale=1.0 / math.sqrt(HEAD_DIM),
+                         device=device, values=values)
+
+
 def config(cfg_id: int, device="cpu", values: bool = True) -> Problem:
     """Workloads 1..5: seeds 1000 + id, shapes and selection recipes as documented."""
     seed = 1000 + cfg_id
@@ -342,11 +355,7 @@ def config(cfg_id: int, device="cpu", values: bool = True) -> Problem:
                              select=select_uniform_count(4), mask_mode=0, return_lse=True,
                              scale=sc, device=device, values=values)
     if cfg_id == 2:
-        B = 64
-        return build_problem(CONFIG_NAMES[2], seed=seed, q_lens=[1] * B, kv_lens=[32768] * B,
-                             num_heads_q=32, num_heads_kv=8, block_x=1, top_k=16, dtype="bf16",
-                             select=select_decode_last_plus(15), causal_eligible=False,
-                             mask_mode=0, return_lse=False, scale=sc, device=device, values=values)
+        return decode_workload(64, 16, device=device, values=values)
     if cfg_id == 3:
         B = 4
         return build_problem(CONFIG_NAMES[3], seed=seed, q_lens=[32768] * B, kv_lens=[32768] * B,

@@ -1,14 +1,16 @@
 // Main kernel for units with at most 16 query rows (packed-GQA tile M = blockShapeX * G <= 16),
 // the decode shape. These units are bound by the bytes of the gathered KV pages, so the design
-// keeps many page loads in flight on every compute unit:
-//  * a workgroup of 4 waves per worker, two workgroups per CU (<= 256 VGPRs per lane);
+// keeps page loads in flight on every compute unit:
+//  * a workgroup of 4 waves per worker; two fit on a CU (<= 256 VGPRs per lane), the default
+//    worker count puts one on each;
 //  * wave q owns token quarter q (32 tokens) of every selected page of the task and keeps its
 //    own online-softmax state for the <= 16 query columns; the four states are merged through
 //    LDS at the end of the task (fixed order);
-//  * the next page's quarter is loaded into registers while the current one is computed;
-//  * K goes straight from HBM into MFMA A-operand registers (S^T = K Q^T, 16x16x32); V is
-//    loaded with full-row coalescing, staged in a wave-private LDS buffer and read back with the
-//    gfx950 transpose read as the A operand of O^T = V^T P^T;
+//  * the next page's quarter is loaded into registers (full 256-byte rows, coalesced) while
+//    the current one is computed;
+//  * K and V of the quarter are staged in a wave-private LDS buffer: K is read back in MFMA
+//    A-operand layout (S^T = K Q^T, 16x16x32), V with the gfx950 transpose read as the A
+//    operand of O^T = V^T P^T;
 //  * split units are merged in-kernel by the last arriving workgroup (split_merge.hpp).
 // GenericBlockSparseAttention article (cf-1.com), "sparse attention mechanism" and
 // "implementation architecture"; FlashAttention article (ai6s.net), "three steps".

@@ -24,10 +24,7 @@ namespace {
 // Bytes per V row in LDS (16-bit values). 320 = 256 + 64 shifts successive rows by 16 banks,
 // so the eight rows of a transposing V read cover every bank equally often (LDS bank-conflict
 // counter 0 on the bf16 prefill, against 13 % of the time with K's 304).
-#ifndef GBSA_VPITCH
-#define GBSA_VPITCH 320
-#endif
-constexpr int kVPitch = GBSA_VPITCH;
+constexpr int kVPitch = 320;
 
 template <int DT>
 struct KLds {

@@ -557,9 +557,8 @@ struct HalfStage {
     static constexpr int v_bytes = 64 * kVPitch;
 };
 
-#ifndef GBSA_PIPE_DEPTH
-#define GBSA_PIPE_DEPTH 4
-#endif
+// LDS fragments in flight in the MFMA item
+constexpr int kPipeDepth = 4;
 
 // One LDS operand fragment of the MFMA item (b is used by the fp8 QK step only).
 struct Frag {
@@ -647,7 +646,7 @@ __device__ __forceinline__ void mfma_item32(const unsigned char* ks, const unsig
     constexpr int KP = KLds<DT>::pitch;
     constexpr int QS = qk ? ((DT == kFP8) ? 2 : 8) : 0;  // QK steps per 32-key tile
     constexpr int VS = pv ? 8 : 0;                       // PV steps per 32-key tile (2 chunks x 4 d)
-    constexpr int PC = QS + VS, NS = 2 * PC, D = GBSA_PIPE_DEPTH;
+    constexpr int PC = QS + VS, NS = 2 * PC, D = kPipeDepth;
     const int h2 = lane >> 5;
     const unsigned char* krow = ks + (lane & 31) * KP;
     // transpose-read address of this lane (row offset within a 4-row group, column block)

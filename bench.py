@@ -454,6 +454,26 @@ def main(argv=None):
     f1.record(stream)
     torch.cuda.synchronize()
     fwd_ms = f0.elapsed_time(f1) / a.steps
+
+    # the same step replayed from a HIP graph (metadata + forward captured once): what a serving
+    # loop that captures its step pays, without per-call launch work
+    graph_ms = None
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            step()
+            side.synchronize()
+            with torch.cuda.graph(graph, stream=side):
+                step()
+        stream.wait_stream(side)
+        graph.replay()
+        torch.cuda.synchronize()
+        graph_ms = timed(graph.replay, a.steps, stream)
+        del graph
+    except RuntimeError as e:  # capture unavailable: report the eager figures only
+        log(f"[bench] graph capture failed: {e}")
     meta_ms = timed(lambda: gbsa_metadata(params, cnt, cu, squ, skv, meta), a.steps, stream)
     status = int(ws[:4].view(torch.int32)[0].item())
     assert status == 0, "metadata mismatch flagged by the kernels"
@@ -524,6 +544,7 @@ def main(argv=None):
                    ("kv_rows" if tnd else "kv_pages"): p.num_pages, "workers": P},
         "effective_tflops": round(tflops, 3), "hbm_gbs": round(gbs, 2),
         "forward_ms": round(fwd_ms, 5), "metadata_ms": round(meta_ms, 5),
+        "ms_per_step_graph": None if graph_ms is None else round(graph_ms, 5),
         "forward_cold_ms": None if fwd_cold_ms is None else round(fwd_cold_ms, 5),
         "ceilings": ceil, "kernel": kernel, "algorithmic_bytes": alg_bytes,
         "algorithmic_flops": alg_flops, "roofline": roof, "cpu_baseline": cpu,

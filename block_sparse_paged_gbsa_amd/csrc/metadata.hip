@@ -8,6 +8,7 @@
 // arithmetic, so the result is bit-exact and deterministic ("general constraints":
 // deterministic by default).
 #include "device_common.hpp"
+#include "launch_lds.hpp"
 
 namespace gbsa {
 namespace {
@@ -316,12 +317,10 @@ hipError_t launch_metadata(const MetaArgs& a, hipStream_t s) {
     const size_t nc = (size_t)a.N2 * (size_t)a.tqb;
     const size_t fast_bytes = sizeof(int) * (2 * ((size_t)a.B + 1) + 2 * nc + 1 + 1024);
     if (a.B <= 1024 && a.P <= 1024 && fast_bytes + kMetaStaticLds <= lds_max) {
-        if (fast_bytes > 64 * 1024) {
-            hipError_t e = hipFuncSetAttribute((const void*)metadata_fast_kernel,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               (int)fast_bytes);
-            if (e != hipSuccess) return e;
-        }
+        static std::atomic<int> granted[kMaxDevices];
+        const hipError_t e =
+            ensure_dynamic_lds((const void*)metadata_fast_kernel, granted, fast_bytes);
+        if (e != hipSuccess) return e;
         hipLaunchKernelGGL(metadata_fast_kernel, dim3(1), dim3(1024), fast_bytes, s, a);
         return hipGetLastError();
     }
@@ -329,11 +328,9 @@ hipError_t launch_metadata(const MetaArgs& a, hipStream_t s) {
     // within 160 KiB of LDS
     const size_t tab_bytes = sizeof(int) * 2 * (size_t)(a.B + 1);
     const size_t lds = tab_bytes + sizeof(int) * (size_t)a.ucap;
-    if (lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute((const void*)metadata_kernel,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-    }
+    static std::atomic<int> granted[kMaxDevices];
+    const hipError_t e = ensure_dynamic_lds((const void*)metadata_kernel, granted, lds);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(metadata_kernel, dim3(1), dim3(1024), lds, s, a);
     return hipGetLastError();
 }

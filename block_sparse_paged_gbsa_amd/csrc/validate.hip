@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "gbsa.h"
+#include "launch_lds.hpp"
 #include "gbsa_internal.hpp"
 
 namespace gbsa {
@@ -137,11 +138,9 @@ __global__ __launch_bounds__(kThreads) void validate_kernel(ValArgs a) {
 
 hipError_t launch_validate(const ValArgs& a, hipStream_t s) {
     const size_t lds = sizeof(int) * ((size_t)a.B + 1);
-    if (lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute((const void*)validate_kernel,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-    }
+    static std::atomic<int> granted[kMaxDevices];
+    const hipError_t e = ensure_dynamic_lds((const void*)validate_kernel, granted, lds);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(validate_kernel, dim3(1), dim3(kThreads), lds, s, a);
     return hipGetLastError();
 }

@@ -114,11 +114,6 @@ __device__ __forceinline__ int xcd_remap(int bid, int grid) {
     return (bid % kXcd) * per + bid / kXcd;
 }
 
-template <typename T>
-__device__ __forceinline__ T load_nt(const T* p) {
-    return __builtin_nontemporal_load(p);
-}
-
 // Buffer resource over a wave-uniform base: one VGPR offset per lane, per-instruction
 // constants in the scalar offset. `records` bytes from the base are readable (at most
 // 2^31-1); a dword at or beyond it reads as zero without a memory access. The range check
@@ -133,9 +128,6 @@ constexpr int kCached = 0, kNT = 2;
 template <int POLICY = kCached>
 __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, int voff, int soff) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, POLICY));
-}
-__device__ __forceinline__ u32x2 buf_load8(rsrc_t r, int voff, int soff) {
-    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
 }
 
 // ---------------------------------------------------------------------------
@@ -404,11 +396,6 @@ __device__ __forceinline__ void key_range(const FwdArgs& a, int64_t p0, int skv,
 // New running max (log2 domain) under lazy rescaling; mx is the block max already scaled.
 __device__ __forceinline__ float lazy_max(float mrun, float mx) {
     return (mx > mrun + kLazyMax) ? mx : mrun;
-}
-
-template <int OUT>
-__device__ __forceinline__ uint32_t pack_out2(float x, float y) {
-    return pack2<OUT>(x, y);
 }
 
 }  // namespace gbsa

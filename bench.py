@@ -336,6 +336,11 @@ def main(argv=None):
     a = ap.parse_args(argv)
     if a.copy_calibration:
         return copy_calibration(a.copy_calibration)
+    if (a.batch, a.top_k) != (64, 16) and (a.config != 2 or not 1 <= a.batch <= 4096 or
+                                           not 1 <= a.top_k <= 256):
+        print("--batch / --top-k apply to workload 2 (1..4096 queries, 1..256 pages)",
+              file=sys.stderr)
+        return 2
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the kernel has no cross-GPU path in this build "
               "(run with --gpus 1)", file=sys.stderr)
@@ -352,10 +357,6 @@ def main(argv=None):
     dev = torch.device("cuda:0")
     log(f"[bench] generating workload {a.config} on the GPU")
     if (a.batch, a.top_k) != (64, 16):
-        if a.config != 2 or not 1 <= a.batch <= 4096 or not 1 <= a.top_k <= 256:
-            print("--batch / --top-k apply to workload 2 (1..4096 queries, 1..256 pages)",
-                  file=sys.stderr)
-            return 2
         p = gi.decode_workload(a.batch, a.top_k, device=dev)
     else:
         p = gi.config(a.config, device=dev)

@@ -538,9 +538,9 @@ def test_metadata_mismatch_is_refused():
 # full-size workloads, sampled rows, benchmark launch configuration
 # ---------------------------------------------------------------------------
 
-def _sampled_check(cfg, units, rows_per_unit=None, seed=0, tnd=False):
+def _sampled_check(cfg, units, rows_per_unit=None, seed=0, tnd=False, problem=None):
     _log(f"[parity] workload {cfg}{' TND' if tnd else ''}: generating on the GPU")
-    p = gi.config(cfg, device="cuda")
+    p = gi.config(cfg, device="cuda") if problem is None else problem
     if tnd:
         p = gi.to_tnd(p)
     gp = GpuProblem(p)
@@ -572,6 +572,14 @@ def _sampled_check(cfg, units, rows_per_unit=None, seed=0, tnd=False):
 
 def test_workload2_decode_sampled():
     _sampled_check(2, [(b, 0) for b in range(0, 64, 3)])
+
+
+@pytest.mark.parametrize("batch,top_k", [(8, 16), (1, 256)], ids=["b8_top16", "b1_top256"])
+def test_split_kv_decode_sampled(batch, top_k):
+    """The split-KV decode shapes the benchmark times (`--batch`, `--top-k`): every unit cut
+    over several of the default workers and merged in the kernel; all queries checked."""
+    p = gi.decode_workload(batch, top_k, device="cuda")
+    _sampled_check(2, [(b, 0) for b in range(batch)], problem=p)
 
 
 def test_workload3_block_sparse_prefill_sampled():

@@ -329,6 +329,9 @@ def main(argv=None):
                          "each unit over several workers)")
     ap.add_argument("--top-k", type=int, default=16,
                     help="workload 2 only: pages selected per query (at most 256)")
+    ap.add_argument("--block-x", type=int, default=128,
+                    help="workload 3 only: query rows per q-block (fewer than 16 packs fewer "
+                         "rows per unit and selects the 17-64 or 65-256 row kernels)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -340,6 +343,9 @@ def main(argv=None):
                                            not 1 <= a.top_k <= 256):
         print("--batch / --top-k apply to workload 2 (1..4096 queries, 1..256 pages)",
               file=sys.stderr)
+        return 2
+    if a.block_x != 128 and (a.config != 3 or not 1 <= a.block_x <= 128):
+        print("--block-x applies to workload 3 (1..128 rows)", file=sys.stderr)
         return 2
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the kernel has no cross-GPU path in this build "
@@ -358,6 +364,8 @@ def main(argv=None):
     log(f"[bench] generating workload {a.config} on the GPU")
     if (a.batch, a.top_k) != (64, 16):
         p = gi.decode_workload(a.batch, a.top_k, device=dev)
+    elif a.block_x != 128:
+        p = gi.block_sparse_prefill(a.block_x, device=dev)
     else:
         p = gi.config(a.config, device=dev)
     tnd = a.kv_layout == "tnd"

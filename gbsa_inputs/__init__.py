@@ -345,6 +345,18 @@ def decode_workload(batch: int = 64, top_k: int = 16, device="cpu",
                          device=device, values=values)
 
 
+def block_sparse_prefill(block_x: int = 128, device="cpu", values: bool = True) -> Problem:
+    """Workload 3 and its variants: 4 x 32768 causal tokens (N1=32, N2=4, bf16), each q-block
+    of block_x rows selecting block 0, its 8 most recent eligible blocks and random others, 64
+    in all. Smaller block_x gives fewer packed rows per unit (block_x * 8), which moves the
+    work to the kernels for 17-64 and 65-256 rows."""
+    name = CONFIG_NAMES[3] if block_x == 128 else f"block_sparse_prefill_bf16_x{block_x}"
+    return build_problem(name, seed=1003, q_lens=[32768] * 4, kv_lens=[32768] * 4,
+                         num_heads_q=32, num_heads_kv=4, block_x=block_x, top_k=64, dtype="bf16",
+                         select=select_sink_recent_random(64, 8), mask_mode=1, return_lse=False,
+                         scale=1.0 / math.sqrt(HEAD_DIM), device=device, values=values)
+
+
 def config(cfg_id: int, device="cpu", values: bool = True) -> Problem:
     """Workloads 1..5: seeds 1000 + id, shapes and selection recipes as documented."""
     seed = 1000 + cfg_id
@@ -357,11 +369,7 @@ def config(cfg_id: int, device="cpu", values: bool = True) -> Problem:
     if cfg_id == 2:
         return decode_workload(64, 16, device=device, values=values)
     if cfg_id == 3:
-        B = 4
-        return build_problem(CONFIG_NAMES[3], seed=seed, q_lens=[32768] * B, kv_lens=[32768] * B,
-                             num_heads_q=32, num_heads_kv=4, block_x=128, top_k=64, dtype="bf16",
-                             select=select_sink_recent_random(64, 8), mask_mode=1,
-                             return_lse=False, scale=sc, device=device, values=values)
+        return block_sparse_prefill(128, device=device, values=values)
     if cfg_id == 4:
         return build_problem(CONFIG_NAMES[4], seed=seed, q_lens=[131072], kv_lens=[120000],
                              kv_storage=[131072], seqused_q=[120000], num_heads_q=64,

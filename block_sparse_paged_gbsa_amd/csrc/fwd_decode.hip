@@ -274,7 +274,7 @@ __global__ __launch_bounds__(256, 2) void fwd_decode_kernel(FwdArgs a) {
                     const int cl = block_class(a, (int64_t)jl * 128, skv, off, t_lo, t_hi);
                     if (cl != 0) {
                         jcl = jl * 4 + cl;
-                        pl = kv.unit<LAYOUT>(jl);
+                        if constexpr (LAYOUT == kPaged) pl = kv.unit<LAYOUT>(jl);
                         rl = kv_records(rs, skv - 128 * jl - 32 * wave);
                     }
                 }
@@ -282,7 +282,10 @@ __global__ __launch_bounds__(256, 2) void fwd_decode_kernel(FwdArgs a) {
             uint64_t todo = __ballot(jcl != 0);
             if (todo == 0) continue;
             auto base_of = [&](int i, const void* p) {
-                const int unit = __builtin_amdgcn_readlane(pl, i);
+                // token-major: the unit follows from the block index packed in jcl
+                const int unit = (LAYOUT == kPaged)
+                                     ? __builtin_amdgcn_readlane(pl, i)
+                                     : kv.unit<LAYOUT>(__builtin_amdgcn_readlane(jcl, i) >> 2);
                 return KvSrc{(const unsigned char*)p +
                                  ((int64_t)unit * a.kv_stride + (int64_t)it.n2 * 128) * esz +
                                  qbyte,

@@ -144,9 +144,11 @@ typedef struct gbsa_params {
 gbsa_status gbsa_check_params(const gbsa_params* params);
 
 /*
- * Number of workers (task-split segments) the two calls will use on the current device.
- * Depends only on the shapes and the device's compute-unit count. Errors: any
- * gbsa_check_params error; GBSA_ERR_HIP when the device cannot be queried.
+ * Number of workers (task-split segments) the two calls will use on the current device:
+ * params->num_workers if set, else one per compute unit for units of at most 16 packed rows
+ * (decode shapes) and two per compute unit divided by the workgroups per unit otherwise
+ * (at most GBSA_MAX_WORKERS). Depends only on the shapes and the device's compute-unit count.
+ * Errors: any gbsa_check_params error; GBSA_ERR_HIP when the device cannot be queried.
  */
 gbsa_status gbsa_num_workers(const gbsa_params* params, int32_t* num_workers);
 

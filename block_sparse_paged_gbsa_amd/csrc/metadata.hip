@@ -134,31 +134,54 @@ __global__ __launch_bounds__(1024) void metadata_kernel(MetaArgs a) {
     const int U = (int)cu;
     const int P = a.P;
 
-    // Total cost (counts kept in LDS for the boundary pass).
+    // Total cost (counts kept in LDS for the boundary pass). Eight units per thread and step:
+    // their count loads are independent and travel together.
+    constexpr int kLoadBatch = 8;
     long long part = 0;
-    for (int u = tid; u < U; u += nt) {
-        const int c = unit_count(a, qbase, ubase, u);
-        if (u < a.ucap) ucount[u] = c;
-        part += c + 1;
+    for (int u0 = tid; u0 < U; u0 += kLoadBatch * nt) {
+        int c[kLoadBatch];
+#pragma unroll
+        for (int k = 0; k < kLoadBatch; ++k) {
+            const int u = u0 + k * nt;
+            c[k] = (u < U) ? unit_count(a, qbase, ubase, u) : 0;
+        }
+#pragma unroll
+        for (int k = 0; k < kLoadBatch; ++k) {
+            const int u = u0 + k * nt;
+            if (u < U) {
+                if (u < a.ucap) ucount[u] = c[k];
+                part += c[k] + 1;
+            }
+        }
     }
     long long W;
     (void)block_exclusive_scan<long long>(part, &W, sh64);  // ends with a barrier
 
     // Boundaries: unit u owns the targets floor(w*W/P) that fall in [C_u, C_u + cost_u).
+    // Each thread takes kRun consecutive units of a chunk: a local prefix over its run, one
+    // block scan of the run totals per chunk.
+    constexpr int kRun = 4;
     long long carry = 0;
-    for (int base = 0; base < U; base += nt) {
-        const int u = base + tid;
-        int c = 0;
-        long long cost = 0;
-        if (u < U) {
-            c = u < a.ucap ? ucount[u] : unit_count(a, qbase, ubase, u);
-            cost = c + 1;
+    for (int base = 0; base < U; base += kRun * nt) {
+        const int u0 = base + tid * kRun;
+        int c[kRun];
+#pragma unroll
+        for (int k = 0; k < kRun; ++k) {
+            const int u = u0 + k;
+            c[k] = (u >= U) ? -1 : (u < a.ucap ? ucount[u] : unit_count(a, qbase, ubase, u));
         }
+        long long run = 0;
+#pragma unroll
+        for (int k = 0; k < kRun; ++k) run += (c[k] >= 0) ? c[k] + 1 : 0;
         long long tot;
-        const long long Cu = carry + block_exclusive_scan<long long>(cost, &tot, sh64);
-        if (u < U) {
-            const int nslots = max(c, 1);
-            bool split = false;
+        long long Cu = carry + block_exclusive_scan<long long>(run, &tot, sh64);
+#pragma unroll
+        for (int k = 0; k < kRun; ++k) {
+            if (c[k] < 0) break;
+            const int u = u0 + k;
+            const long long cost = c[k] + 1;
+            const int nslots = max(c[k], 1);
+            bool split = false;  // a boundary strictly inside unit u
             for (long long w = (Cu * P + W - 1) / W; w < P; ++w) {
                 const long long t = (w * W) / P;
                 if (t >= Cu + cost) break;
@@ -173,6 +196,7 @@ __global__ __launch_bounds__(1024) void metadata_kernel(MetaArgs a) {
                 a.meta[kHeaderWords + w] = (int32_t)word;
             }
             if (split) atomicAdd(&sh_split, 1);
+            Cu += cost;
         }
         carry += tot;
     }

@@ -79,19 +79,33 @@ __device__ __forceinline__ int upper_bound_batch(const int* ubase, int B, int u)
     return lo;
 }
 
-__device__ __forceinline__ int unit_count(const MetaArgs& a, const int* qbase, const int* ubase,
-                                          int u) {
+// A unit's place in (sequence, KV head, q-block) order, found once and then advanced one unit
+// at a time without divisions (the chunked path's cost is per-unit integer work).
+struct UnitPos {
+    int b, n2, gl, nact;
+};
+__device__ __forceinline__ UnitPos unit_pos(const MetaArgs& a, const int* ubase, int u) {
     const int b = upper_bound_batch(ubase, a.B, u);
-    const int nu = ubase[b + 1] - ubase[b];
-    const int nact = nu / a.N2;
+    const int nact = (ubase[b + 1] - ubase[b]) / a.N2;
     const int local = u - ubase[b];
-    const int n2 = local / nact, gl = local % nact;
-    const int g = qbase[b] + gl;
+    return UnitPos{b, local / nact, local % nact, nact};
+}
+__device__ __forceinline__ void unit_next(const MetaArgs& a, const int* ubase, UnitPos& p) {
+    if (++p.gl < p.nact) return;
+    p.gl = 0;
+    if (++p.n2 < a.N2) return;
+    p.n2 = 0;
+    do {
+        if (++p.b >= a.B) return;
+        p.nact = (ubase[p.b + 1] - ubase[p.b]) / a.N2;
+    } while (p.nact == 0);
+}
+__device__ __forceinline__ int pos_count(const MetaArgs& a, const int* qbase, const UnitPos& p) {
+    const int g = qbase[p.b] + p.gl;
     int c = 0;
-    if (g < a.tqb) c = a.count[(int64_t)n2 * a.tqb + g];
+    if (p.b < a.B && g < a.tqb) c = a.count[(int64_t)p.n2 * a.tqb + g];
     return min(max(c, 0), a.topK);
 }
-
 
 __global__ __launch_bounds__(1024) void metadata_kernel(MetaArgs a) {
     extern __shared__ int tabs[];  // qbase[B+1], ubase[B+1], counts of the first ucap units
@@ -134,23 +148,28 @@ __global__ __launch_bounds__(1024) void metadata_kernel(MetaArgs a) {
     const int U = (int)cu;
     const int P = a.P;
 
-    // Total cost (counts kept in LDS for the boundary pass). Eight units per thread and step:
-    // their count loads are independent and travel together.
+    // Total cost (counts kept in LDS for the boundary pass). Each thread walks a contiguous
+    // run of units, issuing eight independent count loads at a time.
     constexpr int kLoadBatch = 8;
     long long part = 0;
-    for (int u0 = tid; u0 < U; u0 += kLoadBatch * nt) {
-        int c[kLoadBatch];
+    {
+        const int R = (U + nt - 1) / nt;
+        const int ua = min(tid * R, U), ub = min(ua + R, U);
+        UnitPos pos = ua < ub ? unit_pos(a, ubase, ua) : UnitPos{0, 0, 0, 1};
+        for (int u0 = ua; u0 < ub; u0 += kLoadBatch) {
+            int c[kLoadBatch];
 #pragma unroll
-        for (int k = 0; k < kLoadBatch; ++k) {
-            const int u = u0 + k * nt;
-            c[k] = (u < U) ? unit_count(a, qbase, ubase, u) : 0;
-        }
+            for (int k = 0; k < kLoadBatch; ++k) {
+                c[k] = (u0 + k < ub) ? pos_count(a, qbase, pos) : 0;
+                if (u0 + k < ub) unit_next(a, ubase, pos);
+            }
 #pragma unroll
-        for (int k = 0; k < kLoadBatch; ++k) {
-            const int u = u0 + k * nt;
-            if (u < U) {
-                if (u < a.ucap) ucount[u] = c[k];
-                part += c[k] + 1;
+            for (int k = 0; k < kLoadBatch; ++k) {
+                const int u = u0 + k;
+                if (u < ub) {
+                    if (u < a.ucap) ucount[u] = c[k];
+                    part += c[k] + 1;
+                }
             }
         }
     }
@@ -159,44 +178,58 @@ __global__ __launch_bounds__(1024) void metadata_kernel(MetaArgs a) {
 
     // Boundaries: unit u owns the targets floor(w*W/P) that fall in [C_u, C_u + cost_u).
     // Each thread takes kRun consecutive units of a chunk: a local prefix over its run, one
-    // block scan of the run totals per chunk.
+    // block scan of the run totals per chunk; the first target at or after the run's start is
+    // found with one division, and the targets are then walked (one division per boundary).
     constexpr int kRun = 4;
     long long carry = 0;
     for (int base = 0; base < U; base += kRun * nt) {
         const int u0 = base + tid * kRun;
         int c[kRun];
+        if (u0 < U) {
+            // counts past the LDS cache are read from memory, walking from the first such unit
+            const int uw = max(u0, a.ucap);
+            UnitPos pos = uw < min(u0 + kRun, U) ? unit_pos(a, ubase, uw) : UnitPos{0, 0, 0, 1};
 #pragma unroll
-        for (int k = 0; k < kRun; ++k) {
-            const int u = u0 + k;
-            c[k] = (u >= U) ? -1 : (u < a.ucap ? ucount[u] : unit_count(a, qbase, ubase, u));
+            for (int k = 0; k < kRun; ++k) {
+                const int u = u0 + k;
+                c[k] = (u >= U) ? -1 : (u < a.ucap ? ucount[u] : pos_count(a, qbase, pos));
+                if (u >= a.ucap && u < U) unit_next(a, ubase, pos);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < kRun; ++k) c[k] = -1;
         }
         long long run = 0;
 #pragma unroll
         for (int k = 0; k < kRun; ++k) run += (c[k] >= 0) ? c[k] + 1 : 0;
         long long tot;
         long long Cu = carry + block_exclusive_scan<long long>(run, &tot, sh64);
+        if (run > 0) {
+            long long w = (Cu * P + W - 1) / W;  // first worker whose target is >= Cu
+            long long t = w < P ? (w * W) / P : 0;
 #pragma unroll
-        for (int k = 0; k < kRun; ++k) {
-            if (c[k] < 0) break;
-            const int u = u0 + k;
-            const long long cost = c[k] + 1;
-            const int nslots = max(c[k], 1);
-            bool split = false;  // a boundary strictly inside unit u
-            for (long long w = (Cu * P + W - 1) / W; w < P; ++w) {
-                const long long t = (w * W) / P;
-                if (t >= Cu + cost) break;
-                const int s = (int)(t - Cu);
-                uint32_t word;
-                if (s < nslots) {
-                    word = ((uint32_t)u << kSlotBits) | (uint32_t)s;
-                    split = split || (s > 0);
-                } else {
-                    word = (uint32_t)(u + 1) << kSlotBits;
+            for (int k = 0; k < kRun; ++k) {
+                if (c[k] < 0) break;
+                const int u = u0 + k;
+                const long long cost = c[k] + 1;
+                const int nslots = max(c[k], 1);
+                bool split = false;  // a boundary strictly inside unit u
+                while (w < P && t < Cu + cost) {
+                    const int s = (int)(t - Cu);
+                    uint32_t word;
+                    if (s < nslots) {
+                        word = ((uint32_t)u << kSlotBits) | (uint32_t)s;
+                        split = split || (s > 0);
+                    } else {
+                        word = (uint32_t)(u + 1) << kSlotBits;
+                    }
+                    a.meta[kHeaderWords + w] = (int32_t)word;
+                    ++w;
+                    t = w < P ? (w * W) / P : 0;
                 }
-                a.meta[kHeaderWords + w] = (int32_t)word;
+                if (split) atomicAdd(&sh_split, 1);
+                Cu += cost;
             }
-            if (split) atomicAdd(&sh_split, 1);
-            Cu += cost;
         }
         carry += tot;
     }

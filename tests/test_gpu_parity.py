@@ -88,12 +88,14 @@ def test_metadata_bit_exact_random(seed):
     np.testing.assert_array_equal(meta, _ref_meta(p, P))
 
 
-@pytest.mark.parametrize("case", ["many_sequences", "large_tables", "max_batch"])
+@pytest.mark.parametrize("case", ["many_sequences", "large_tables", "max_batch", "huge_units"])
 def test_metadata_bit_exact_beyond_lds(case):
     """More than 1024 sequences (up to GBSA_MAX_BATCH, whose tables fill the LDS), or N2 x
-    q-block tables larger than LDS: the scheduler's chunked path, which must give the same
-    split word for word."""
-    if case == "many_sequences":
+    q-block tables larger than LDS (up to 65536 units: workload 3 with 8-row q-blocks): the
+    scheduler's chunked path, which must give the same split word for word."""
+    if case == "huge_units":
+        p = gi.block_sparse_prefill(8, values=False)
+    elif case == "many_sequences":
         p = gi.random_problem(31, values=False, decode=True, batch=1500, num_heads_q=8,
                               num_heads_kv=2, block_x=1, top_k=4, use_seqused_q=True)
     elif case == "max_batch":

@@ -15,7 +15,8 @@
 //    softmax items on the same SIMDs over half pages (schedules described with each), on 32x32
 //    MFMA tiles;
 //  * fwd_prefill_kernel (17-64 rows): all waves in phase, 16 rows each, whole pages through a
-//    double-buffered LDS stage with one barrier per page, 16x16 MFMA tiles.
+//    double-buffered LDS stage with one barrier per page, each page's keys split over 2
+//    (33-64 rows) or 4 (17-32 rows) wave groups that hold the same rows, 16x16 MFMA tiles.
 #include "split_merge.hpp"
 
 namespace gbsa {
@@ -139,9 +140,10 @@ __device__ __forceinline__ void qk_tile(const unsigned char* ks, const QTile<NQ>
     }
 }
 
-// Mask (when needed) and the running-max update of one half page; returns the max to use.
-template <int NQ, bool UM>
-__device__ __forceinline__ void half_max(const FwdArgs& a, f32x4 (&s)[4][NQ], int half, int cls,
+// Mask (when needed) and the running-max update of TT 16-token tiles starting at token tok0 of
+// the page; returns the max to use.
+template <int NQ, bool UM, int TT = 4>
+__device__ __forceinline__ void half_max(const FwdArgs& a, f32x4 (&s)[TT][NQ], int tok0, int cls,
                                          const int (&vlo)[NQ], const int (&vhi)[NQ], int64_t p0,
                                          const UMaskRow (&um)[NQ], const float (&colscale)[NQ],
                                          int lgrp, float (&mrun)[NQ], float (&muse)[NQ],
@@ -150,10 +152,10 @@ __device__ __forceinline__ void half_max(const FwdArgs& a, f32x4 (&s)[4][NQ], in
 #pragma unroll
         for (int nq = 0; nq < NQ; ++nq)
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt)
+            for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int rel = half * 64 + tt * 16 + lgrp * 4 + i;
+                    const int rel = tok0 + tt * 16 + lgrp * 4 + i;
                     if (rel < vlo[nq] || rel > vhi[nq]) s[tt][nq][i] = kNegInf;
                 }
     }
@@ -161,8 +163,8 @@ __device__ __forceinline__ void half_max(const FwdArgs& a, f32x4 (&s)[4][NQ], in
 #pragma unroll
         for (int nq = 0; nq < NQ; ++nq)
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-                const uint32_t w = umask_word(a, um[nq], p0 + half * 64 + tt * 16 + lgrp * 4);
+            for (int tt = 0; tt < TT; ++tt) {
+                const uint32_t w = umask_word(a, um[nq], p0 + tok0 + tt * 16 + lgrp * 4);
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     if ((w >> (8 * i)) & 0xffu) s[tt][nq][i] = kNegInf;
@@ -172,7 +174,7 @@ __device__ __forceinline__ void half_max(const FwdArgs& a, f32x4 (&s)[4][NQ], in
     for (int nq = 0; nq < NQ; ++nq) {
         float mx = kNegInf;
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
+        for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[tt][nq][i]);
         mx = wave_max_cols(mx);
@@ -238,87 +240,54 @@ __device__ __forceinline__ void rescale(float (&alpha)[NQ], f32x4 (&o)[8][NQ]) {
     }
 }
 
-// State carried from the first to the second part of a page.
-template <int NQ>
-struct PageMid {
-    f32x4 s1[4][NQ];
-    uint32_t p0[4][NQ][2];
-    float muse[NQ], alpha[NQ];
+// State carried from the first to the second part of a key slice.
+template <int NQ, int TT>
+struct SliceMid {
+    uint32_t p[TT][NQ][2];
 };
 
-// One page (128 tokens) for this wave's NQ query tiles, software-pipelined in two halves so
-// that independent MFMA and VALU work sit next to each other in the instruction stream:
-//   part A: QK(h0); [QK(h1) | exp(h0)]      part B: [PV(h0) | exp(h1)]; PV(h1)
-// The caller moves the next page's K (between the parts) and V (after part B) into the other
-// LDS buffer, so only one tensor's share is held in registers at a time.
-template <int DT, int NQ, bool UM>
-__device__ __forceinline__ void page_part_a(const FwdArgs& a, const unsigned char* stage,
-                                            const QTile<NQ>& qt, const float (&colscale)[NQ],
-                                            const int (&trow)[NQ], const UMaskRow (&um)[NQ],
-                                            int j, int cls, int skv, int off, int lane,
-                                            float (&mrun)[NQ],
-                                            float (&lrun)[NQ], f32x4 (&o)[8][NQ],
-                                            PageMid<NQ>& mid) {
+// The wave's key slice of a page when the workgroup splits the keys: the TT 16-token tiles
+// from token tok0 (a multiple of 32). Part A: QK^T, mask, running max, rescale, exp2 and row
+// sums; part B: PV.
+template <int DT, int NQ, bool UM, int TT>
+__device__ __forceinline__ void slice_part_a(const FwdArgs& a, const unsigned char* stage,
+                                             const QTile<NQ>& qt, const float (&colscale)[NQ],
+                                             const int (&trow)[NQ], const UMaskRow (&um)[NQ],
+                                             int j, int cls, int skv, int off, int lane, int tok0,
+                                             float (&mrun)[NQ], float (&lrun)[NQ],
+                                             f32x4 (&o)[8][NQ], SliceMid<NQ, TT>& mid) {
     constexpr int PT = (DT == kF16) ? kF16 : kBF16;
     const int lrow = lane & 15, lgrp = lane >> 4;
-    const unsigned char* ks = stage;
     int vlo[NQ], vhi[NQ];
     if (cls == 2) {
 #pragma unroll
         for (int nq = 0; nq < NQ; ++nq)
             key_range(a, (int64_t)j * 128, skv, (int64_t)trow[nq] + off, &vlo[nq], &vhi[nq]);
     }
-    f32x4 s0[4][NQ];
-    float ls[NQ];
+    f32x4 s[TT][NQ];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-        qk_tile<DT, NQ>(ks, qt, tt * 16 + lrow, lgrp, s0[tt]);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    half_max<NQ, UM>(a, s0, 0, cls, vlo, vhi, (int64_t)j * 128, um, colscale, lgrp, mrun,
-                     mid.muse, mid.alpha);
-    rescale<NQ>(mid.alpha, o);
+    for (int tt = 0; tt < TT; ++tt) qk_tile<DT, NQ>(stage, qt, tok0 + tt * 16 + lrow, lgrp, s[tt]);
+    float muse[NQ], alpha[NQ], ls[NQ];
+    half_max<NQ, UM, TT>(a, s, tok0, cls, vlo, vhi, (int64_t)j * 128, um, colscale, lgrp, mrun,
+                         muse, alpha);
+    rescale<NQ>(alpha, o);
 #pragma unroll
     for (int nq = 0; nq < NQ; ++nq) ls[nq] = 0.f;
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-        qk_tile<DT, NQ>(ks, qt, 64 + tt * 16 + lrow, lgrp, mid.s1[tt]);
-        exp_tile<PT, NQ>(s0[tt], colscale, mid.muse, mid.p0[tt], ls);
-        __builtin_amdgcn_sched_barrier(0);
-    }
+    for (int tt = 0; tt < TT; ++tt) exp_tile<PT, NQ>(s[tt], colscale, muse, mid.p[tt], ls);
 #pragma unroll
-    for (int nq = 0; nq < NQ; ++nq) lrun[nq] = lrun[nq] * mid.alpha[nq] + ls[nq];
-    half_max<NQ, UM>(a, mid.s1, 1, cls, vlo, vhi, (int64_t)j * 128, um, colscale, lgrp, mrun,
-                     mid.muse, mid.alpha);
+    for (int nq = 0; nq < NQ; ++nq) lrun[nq] = lrun[nq] * alpha[nq] + ls[nq];
 }
 
-template <int DT, int NQ>
-__device__ __forceinline__ void page_part_b(const unsigned char* stage, const float (&colscale)[NQ],
-                                            int lane, float (&lrun)[NQ], f32x4 (&o)[8][NQ],
-                                            PageMid<NQ>& mid) {
+template <int DT, int NQ, int TT>
+__device__ __forceinline__ void slice_part_b(const unsigned char* stage, int lane, int tok0,
+                                             f32x4 (&o)[8][NQ], const SliceMid<NQ, TT>& mid) {
     constexpr int PT = (DT == kF16) ? kF16 : kBF16;
     const unsigned char* vs = stage + PageStage<DT>::k_bytes;
-    uint32_t p1[4][NQ][2];
-    float ls[NQ];
 #pragma unroll
-    for (int nq = 0; nq < NQ; ++nq) ls[nq] = 0.f;
-#pragma unroll
-    for (int kc2 = 0; kc2 < 2; ++kc2) {
-        pv_chunk<PT, NQ>(vs, kc2, mid.p0[2 * kc2], mid.p0[2 * kc2 + 1], lane, o);
-        exp_tile<PT, NQ>(mid.s1[2 * kc2], colscale, mid.muse, p1[2 * kc2], ls);
-        exp_tile<PT, NQ>(mid.s1[2 * kc2 + 1], colscale, mid.muse, p1[2 * kc2 + 1], ls);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int nq = 0; nq < NQ; ++nq) lrun[nq] = lrun[nq] * mid.alpha[nq] + ls[nq];
-    rescale<NQ>(mid.alpha, o);  // after PV(h0): the new max applies to everything accumulated
-#pragma unroll
-    for (int kc2 = 0; kc2 < 2; ++kc2) {
-        pv_chunk<PT, NQ>(vs, 2 + kc2, p1[2 * kc2], p1[2 * kc2 + 1], lane, o);
-        __builtin_amdgcn_sched_barrier(0);
-    }
+    for (int c = 0; c < TT / 2; ++c)
+        pv_chunk<PT, NQ>(vs, tok0 / 32 + c, mid.p[2 * c], mid.p[2 * c + 1], lane, o);
 }
-
 
 // Query tiles of this wave (B operand of S^T = K Q^T) and the per-column state.
 template <int DT, int NQ>
@@ -397,16 +366,26 @@ __device__ __forceinline__ void write_rows(const FwdArgs& a, const UnitIter& it,
     }
 }
 
-template <int DT, int OUT, int NW, int NQ, int LAYOUT, bool UM>
+// Every page's keys are split KS ways: waves rw, rw + RW, ... (RW = NW / KS) hold the same
+// NQ*16 rows and take token slices 0, 128/KS, ... of each page, so each staged page is read
+// from LDS KS times rather than once per wave; the slices' softmax states are combined through
+// LDS at the end of the task (FA article, "three steps").
+template <int DT, int OUT, int NW, int NQ, int KS, int LAYOUT, bool UM>
 __global__ __launch_bounds__(NW * 64, 1) void fwd_prefill_kernel(FwdArgs a) {
     constexpr int NT = NW * 64;
-    constexpr int R = NW * NQ * 16;
+    constexpr int RW = NW / KS;  // waves per key slice
+    constexpr int R = RW * NQ * 16;
+    constexpr int TT = 128 / KS / 16;  // 16-token tiles per key slice
     constexpr int esz = (DT == kFP8) ? 1 : 2;
     __shared__ __attribute__((aligned(16))) unsigned char smem[2 * PageStage<DT>::bytes];
     static_assert(sizeof(smem) >= kPieceListBytes, "the split merge borrows the stages");
+    static_assert(KS > 1 && NQ == 1 && NW % KS == 0 && TT % 2 == 0, "key split shape");
+    static_assert((KS - 1) * RW * (8 * 64 * 16 + 2 * 64 * 4) <= (int)sizeof(smem),
+                  "the key-slice merge fits in the stages");
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform for the compiler
+    const int rw = wave % RW, kp = wave / RW;  // row wave and key slice
     const int lrow = lane & 15, lgrp = lane >> 4;
     const int lin = xcd_remap(blockIdx.x, gridDim.x);
     const int w = lin / a.nst, st = lin - (lin / a.nst) * a.nst;
@@ -443,7 +422,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_prefill_kernel(FwdArgs a) {
             float colscale[NQ];
             int trow[NQ];
             bool rvalid[NQ];
-            load_q<DT, NQ>(a, it, t0, rows_exist, row_base + wave * NQ * 16, lane, qt, colscale,
+            load_q<DT, NQ>(a, it, t0, rows_exist, row_base + rw * NQ * 16, lane, qt, colscale,
                            trow, rvalid);
             UMaskRow um[NQ];
 #pragma unroll
@@ -469,7 +448,8 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_prefill_kernel(FwdArgs a) {
             // ---- stream the task's visible pages through the double-buffered stage ------
             // lane l of every wave holds slot c0 + l of the current 64-slot chunk
             PageRegs<DT, NT, 128> pr;
-            PageMid<NQ> mid;
+            SliceMid<NQ, TT> smid;
+            const int tok0 = kp * (128 / KS);
             int buf = 0;
             bool have_prev = false;  // a page is waiting in stage[buf]
             int prev_j = 0, prev_cls = 0;
@@ -496,11 +476,12 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_prefill_kernel(FwdArgs a) {
                     unsigned char* dst = have_prev ? smem + (buf ^ 1) * PageStage<DT>::bytes : cur;
                     page_load<DT, NT>(pr, kv_src(a.k, pb, rs, nv), rs, tid);
                     if (have_prev)
-                        page_part_a<DT, NQ, UM>(a, cur, qt, colscale, trow, um, prev_j, prev_cls,
-                                                skv, off, lane, mrun, lrun, o, mid);
+                        slice_part_a<DT, NQ, UM, TT>(a, cur, qt, colscale, trow, um, prev_j,
+                                                     prev_cls, skv, off, lane, tok0, mrun, lrun,
+                                                     o, smid);
                     store_k<DT, NT>(pr, dst, tid);
                     page_load<DT, NT>(pr, kv_src(a.v, pb, rs, nv), rs, tid);
-                    if (have_prev) page_part_b<DT, NQ>(cur, colscale, lane, lrun, o, mid);
+                    if (have_prev) slice_part_b<DT, NQ, TT>(cur, lane, tok0, o, smid);
                     store_v<DT, NT>(pr, dst + PageStage<DT>::k_bytes, tid);
                     if (have_prev) buf ^= 1;
                     __syncthreads();
@@ -511,15 +492,48 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_prefill_kernel(FwdArgs a) {
             }
             if (have_prev) {
                 unsigned char* cur = smem + buf * PageStage<DT>::bytes;
-                page_part_a<DT, NQ, UM>(a, cur, qt, colscale, trow, um, prev_j, prev_cls, skv,
-                                        off, lane, mrun, lrun, o, mid);
-                page_part_b<DT, NQ>(cur, colscale, lane, lrun, o, mid);
+                slice_part_a<DT, NQ, UM, TT>(a, cur, qt, colscale, trow, um, prev_j, prev_cls,
+                                             skv, off, lane, tok0, mrun, lrun, o, smid);
+                slice_part_b<DT, NQ, TT>(cur, lane, tok0, o, smid);
             }
             __syncthreads();  // the stage is reused by the next task
 
+            {
+                // key slices 1..KS-1 hand (O, running max, row sums) to slice 0 through the
+                // free stage memory; the lane layout is the same in every slice
+                f32x4* so = (f32x4*)smem;
+                float* sml = (float*)(smem + (KS - 1) * RW * 8 * 64 * 16);
+                if (kp > 0) {
+                    const int slot = (kp - 1) * RW + rw;
+#pragma unroll
+                    for (int dt = 0; dt < 8; ++dt) so[(slot * 8 + dt) * 64 + lane] = o[dt][0];
+                    sml[slot * 128 + lane] = mrun[0];
+                    sml[slot * 128 + 64 + lane] = lrun[0];
+                }
+                __syncthreads();
+                if (kp == 0) {
+#pragma unroll
+                    for (int k = 1; k < KS; ++k) {
+                        const int slot = (k - 1) * RW + rw;
+                        const float m1 = sml[slot * 128 + lane], l1 = sml[slot * 128 + 64 + lane];
+                        const float m = fmaxf(mrun[0], m1);
+                        const float f0 = (m == kNegInf) ? 0.f : fast_exp2(mrun[0] - m);
+                        const float f1 = (m == kNegInf) ? 0.f : fast_exp2(m1 - m);
+                        mrun[0] = m;
+                        lrun[0] = lrun[0] * f0 + l1 * f1;
+#pragma unroll
+                        for (int dt = 0; dt < 8; ++dt)
+                            o[dt][0] = o[dt][0] * f0 + so[(slot * 8 + dt) * 64 + lane] * f1;
+                    }
+                }
+                __syncthreads();  // the stage is reused by the next task
+            }
+
             // ---- epilogue: normalised output + LSE, or a split-KV partial --------------
-            write_rows<DT, OUT, NQ>(a, it, complete, 2 * w + (sa > 0 ? 0 : 1),
-                                    row_base + wave * NQ * 16, lane, trow, rvalid, mrun, lrun, o);
+            if (kp == 0)
+                write_rows<DT, OUT, NQ>(a, it, complete, 2 * w + (sa > 0 ? 0 : 1),
+                                        row_base + rw * NQ * 16, lane, trow, rvalid, mrun, lrun,
+                                        o);
             if (!complete) {
                 int* list = (int*)smem;  // the stages are free until the next task
                 const int np = piece_arrive(a, w, u, st, a.nst, list);
@@ -1278,9 +1292,14 @@ hipError_t launch_l(const FwdArgs& a, int rows, hipStream_t s) {
     } else if (a.M > 64) {
         hipLaunchKernelGGL((fwd_prefill_ks32_kernel<DT, OUT, LAYOUT, UM>), dim3(grid), dim3(512),
                            0, s, a);
+    } else if (a.M > 32) {
+        // 17-64 rows: the keys of every page are split over 2 or 4 wave groups, so that no
+        // wave computes on missing rows and each page goes through LDS 2 or 4 times, not 8
+        hipLaunchKernelGGL((fwd_prefill_kernel<DT, OUT, 8, 1, 2, LAYOUT, UM>), dim3(grid),
+                           dim3(512), 0, s, a);
     } else {
-        hipLaunchKernelGGL((fwd_prefill_kernel<DT, OUT, 8, 1, LAYOUT, UM>), dim3(grid), dim3(512),
-                           0, s, a);
+        hipLaunchKernelGGL((fwd_prefill_kernel<DT, OUT, 8, 1, 4, LAYOUT, UM>), dim3(grid),
+                           dim3(512), 0, s, a);
     }
     return hipGetLastError();
 }

@@ -162,6 +162,10 @@ CASES = [
          num_heads_kv=4, top_k=4, mask_mode=1, out_dtype="f16"),
     dict(seed=119, dtype="f16", batch=3, max_len=300, block_x=32, num_heads_q=8,
          num_heads_kv=1, top_k=4, mask_mode=1, win_left=50, win_right=-1),
+    # 17-32 rows (every page's keys in four slices): fp8 causal with dual lengths, bf16 with a
+    # two-sided window
+    dict(seed=120, dtype="fp8", block_x=12, mask_mode=1, use_seqused_q=True),
+    dict(seed=121, dtype="bf16", block_x=16, mask_mode=1, win_left=70, win_right=10),
 ]
 
 

@@ -593,6 +593,18 @@ def test_workload3_block_sparse_prefill_sampled():
     _sampled_check(3, units, rows_per_unit=12)
 
 
+@pytest.mark.parametrize("block_x", [8, 4], ids=["x8", "x4"])
+def test_small_qblock_prefill_sampled(block_x):
+    """Workload 3 with 8- and 4-row q-blocks (`--block-x`), as the benchmark times them: 64 and
+    32 packed rows per unit, the in-phase kernel with every page's keys in two or four slices.
+    First q-blocks, both sides of a 128-token block edge, and q-blocks in later sequences up to
+    the last one; every row of each."""
+    n = 32768 // block_x
+    e = 128 // block_x
+    units = [(0, 0), (0, 1), (0, e - 1), (0, e), (1, n // 4), (2, n // 2 + 1), (3, n - 1)]
+    _sampled_check(3, units, problem=gi.block_sparse_prefill(block_x, device="cuda"))
+
+
 def test_workload4_long_context_sampled():
     # first blocks, the window edge (rows 32256.. start dropping the sinks), the partial
     # last KV block (seqused 120000), the last active q-block

@@ -43,6 +43,18 @@ int gbsa_probe_gather(const void* key, const void* value, const int64_t* slice_o
 int gbsa_probe_stream(const void* src, int64_t bytes, int32_t grid, void* sink,
                       hipStream_t stream);
 
+/*
+ * LDS read rate (context for the main kernels, which stage K/V pages in LDS and read operand
+ * fragments from there): `grid` workgroups of 512 threads, one per CU (96 KiB static LDS),
+ * each read 512 * 16 * 8 bytes per iteration for `iters` iterations (1 .. 2^24) with 16-byte,
+ * bank-conflict-free loads. ticks: device buffer of 2 * grid uint64; workgroup g writes its
+ * shader-clock cycles (s_memtime) at 2g and 100 MHz ticks (s_memrealtime) at 2g + 1 over the
+ * read loop. Bytes per clock per CU = 65536 * iters / ticks[2g]. sink: at least grid * 8192
+ * bytes (written only as above).
+ */
+int gbsa_probe_lds_read(int32_t iters, int32_t grid, uint64_t* ticks, void* sink,
+                        hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -214,6 +214,9 @@ def test_probe_library_exports_its_header():
     assert lib.gbsa_probe_gather(None, None, None, 0, 256, 2048, None, None) == -1
     assert lib.gbsa_probe_stream(ctypes.c_void_p(0x1000), 15, 1, ctypes.c_void_p(0x1000),
                                  None) == -1
+    assert lib.gbsa_probe_lds_read(0, 1, ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1000),
+                                   None) == -1
+    assert lib.gbsa_probe_lds_read(1, 1, None, ctypes.c_void_p(0x1000), None) == -1
 
 
 def test_validate_argument_checks():

@@ -213,23 +213,62 @@ def ceilings(p, hbm_bound: bool, stream):
     return out
 
 
-def cpu_baseline(p, budget_s: float):
-    """The float64 oracle on a bounded sample of the same workload (rows of whole q-blocks)."""
-    import torch
+# --- CPU baseline: the float64 oracle over units on a pool of forked processes ------------
+_CPU_INPUTS = None  # set before the fork: the workers share the host inputs without a copy
+
+
+def _cpu_unit(task):
+    """One q-block (all KV heads) through the oracle's per-unit definition; seconds spent."""
     from threadpoolctl import threadpool_limits
+
+    from oracle.attention import attention_unit
+    b, gl, ts = task
+    with threadpool_limits(limits=1):  # one BLAS thread per process: the pool owns the cores
+        t0 = time.perf_counter()
+        for n2 in range(_CPU_INPUTS.N2):
+            attention_unit(_CPU_INPUTS, b, n2, gl, ts)
+        return time.perf_counter() - t0
+
+
+def host_cpu():
+    """(cores usable by this process, CPU model) of the host."""
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return int(cores or 1), model
+
+
+def cpu_baseline(p, budget_s: float, max_workers: int = 16):
+    """The float64 oracle on a bounded sample of the same workload (whole q-blocks, every KV
+    head), one q-block per task on a pool of processes over the host's cores. The sample grows
+    until about budget_s seconds of wall time have been spent; a workload the pool finishes
+    early is timed over repeated passes of all of it. Input preparation and the pool's start
+    are outside the timed region."""
+    import multiprocessing
+
+    import torch
 
     import gbsa_inputs as gi
     from oracle import attention as oa
+    global _CPU_INPUTS
 
     starts = gi.q_block_starts(p.cu_seqlens_q, p.block_x)
     units = []
     for b in range(p.batch):
         storage = int(p.cu_seqlens_q[b + 1] - p.cu_seqlens_q[b])
-        sq = storage if p.seqused_q is None else int(p.seqused_q[b])
+        sq = storage if p.seqused_q is None else min(int(p.seqused_q[b]), storage)
         for gl in range(-(-sq // p.block_x)):
-            units.append((b, gl))
+            lo, hi = gl * p.block_x, min((gl + 1) * p.block_x, sq)
+            units.append((b, gl, np.arange(lo, hi, dtype=np.int64)))
     rng = np.random.default_rng(7)
-    rng.shuffle(units)
+    order = rng.permutation(len(units))
+    units = [units[i] for i in order]
 
     def host(t):
         t = t.detach()
@@ -239,27 +278,24 @@ def cpu_baseline(p, budget_s: float):
             return t.view(torch.uint8).cpu().numpy()
         return t.cpu().numpy()
 
-    def host_inputs_tnd(sample):
-        # the sampled sequences' rows only; every other sequence becomes an empty range
-        seqs = {b for (b, _) in sample}
-        cu = p.cu_seqlens_kv
-        new_cu = np.zeros(p.batch + 1, dtype=np.int64)
-        for b in range(p.batch):
-            new_cu[b + 1] = new_cu[b] + (int(cu[b + 1] - cu[b]) if b in seqs else 0)
-        sel = torch.cat([torch.arange(int(cu[b]), int(cu[b + 1]), device=p.k.device)
-                         for b in sorted(seqs)])
-        return oa.Inputs(host(p.q), host(p.k[sel]), host(p.v[sel]), p.sparse_block_idx,
-                         p.sparse_block_count, p.cu_seqlens_q, p.seqused_q, p.seqused_kv,
-                         None, dtype=p.dtype, block_x=p.block_x, scale=p.scale,
-                         mask_mode=p.mask_mode, win_left=p.win_left, win_right=p.win_right,
-                         q_scale=p.q_scale, k_scale=p.k_scale, v_scale=p.v_scale,
-                         cu_seqlens_kv=new_cu)
-
     def host_inputs(sample):
+        """Oracle inputs holding only what the sampled units read."""
+        common = dict(dtype=p.dtype, block_x=p.block_x, scale=p.scale, mask_mode=p.mask_mode,
+                      win_left=p.win_left, win_right=p.win_right, q_scale=p.q_scale,
+                      k_scale=p.k_scale, v_scale=p.v_scale)
         if p.kv_layout == "TND":
-            return host_inputs_tnd(sample)
+            seqs = {b for (b, _, _) in sample}
+            cu = p.cu_seqlens_kv
+            new_cu = np.zeros(p.batch + 1, dtype=np.int64)
+            for b in range(p.batch):
+                new_cu[b + 1] = new_cu[b] + (int(cu[b + 1] - cu[b]) if b in seqs else 0)
+            sel = torch.cat([torch.arange(int(cu[b]), int(cu[b + 1]), device=p.k.device)
+                             for b in sorted(seqs)])
+            return oa.Inputs(host(p.q), host(p.k[sel]), host(p.v[sel]), p.sparse_block_idx,
+                             p.sparse_block_count, p.cu_seqlens_q, p.seqused_q, p.seqused_kv,
+                             None, cu_seqlens_kv=new_cu, **common)
         pages = set()
-        for (b, gl) in sample:
+        for (b, gl, _) in sample:
             g = starts[b] + gl
             for n2 in range(p.num_heads_kv):
                 c = min(max(int(p.sparse_block_count[n2, g]), 0), p.top_k)
@@ -273,43 +309,173 @@ def cpu_baseline(p, budget_s: float):
         table = np.where(p.block_table >= 0, remap[np.maximum(p.block_table, 0)], -1)
         return oa.Inputs(host(p.q), host(p.k[sel]), host(p.v[sel]), p.sparse_block_idx,
                          p.sparse_block_count, p.cu_seqlens_q, p.seqused_q, p.seqused_kv,
-                         table, dtype=p.dtype, block_x=p.block_x, scale=p.scale,
-                         mask_mode=p.mask_mode, win_left=p.win_left, win_right=p.win_right,
-                         q_scale=p.q_scale, k_scale=p.k_scale, v_scale=p.v_scale)
+                         table, **common)
 
-    # grow the sample until the oracle has run for about budget_s seconds
-    n, done_units, elapsed = 1, [], 0.0
-    with threadpool_limits(limits=1):
-        while elapsed < budget_s and len(done_units) < len(units):
-            batch_units = units[len(done_units):len(done_units) + n]
-            inp = host_inputs(batch_units)
-            rows = []
-            for (b, gl) in batch_units:
-                lo = gl * p.block_x
-                hi = min((gl + 1) * p.block_x, inp.sq(b), inp.storage(b))
-                rows += list(int(p.cu_seqlens_q[b]) + np.arange(lo, hi))
+    cores, model = host_cpu()
+    workers = max(1, min(cores, max_workers))
+    _CPU_INPUTS = host_inputs(units)
+    # units in growing chunks (at least one per process) until the budget is spent; a workload
+    # the pool finishes early is timed over repeated passes of all of it
+    done, passes, elapsed, k = [], 0, 0.0, workers
+    with multiprocessing.get_context("fork").Pool(workers) as pool:
+        pool.map(_cpu_unit, units[:workers], chunksize=1)  # start every worker (untimed)
+        while elapsed < budget_s:
+            if len(done) < len(units):
+                batch = units[len(done):len(done) + k]
+                k *= 2
+            else:
+                batch = units
             t0 = time.perf_counter()
-            oa.sparse_attention(inp, rows=rows)
+            pool.map(_cpu_unit, batch, chunksize=1)
             elapsed += time.perf_counter() - t0
-            done_units += batch_units
-            n *= 2
-        # a workload the oracle finishes early is timed over repeated passes of all of it
-        passes = 1
-        if len(done_units) == len(units) and elapsed < budget_s:
-            inp = host_inputs(done_units)
-            rows = []
-            for (b, gl) in done_units:
-                lo = gl * p.block_x
-                hi = min((gl + 1) * p.block_x, inp.sq(b), inp.storage(b))
-                rows += list(int(p.cu_seqlens_q[b]) + np.arange(lo, hi))
-            while elapsed < budget_s:
-                t0 = time.perf_counter()
-                oa.sparse_attention(inp, rows=rows)
-                elapsed += time.perf_counter() - t0
+            if len(done) < len(units):
+                done += batch
+            else:
                 passes += 1
-    bytes_s, flops_s = algorithmic_work(p, set(done_units))
-    return dict(units=len(done_units), seconds=elapsed, bytes=bytes_s * passes,
-                flops=flops_s * passes, passes=passes, whole=len(done_units) == len(units))
+    _CPU_INPUTS = None
+    bytes_s, flops_s = algorithmic_work(p, {(b, gl) for (b, gl, _) in done})
+    whole = len(done) == len(units)
+    if whole:
+        passes += 1
+    return dict(units=len(done), seconds=elapsed, bytes=bytes_s * max(passes, 1),
+                flops=flops_s * max(passes, 1), passes=max(passes, 1), whole=whole,
+                cores=workers, host_cores=cores, cpu_model=model)
+
+
+# --- one workload on the GPU ------------------------------------------------------------------
+class Workload:
+    """A problem's tensors on the GPU and the two calls of the path (marshalling only)."""
+
+    def __init__(self, p, dev, tnd=False, umask=None):
+        import torch
+
+        import gbsa_inputs as gi
+        from block_sparse_paged_gbsa_amd import gbsa_num_workers, gbsa_workspace_size, make_params
+        self.p, self.tnd, self.umask = p, tnd, umask
+        self.params = make_params(
+            batch=p.batch, num_heads_q=p.num_heads_q, num_heads_kv=p.num_heads_kv,
+            total_q=p.total_q, total_q_blocks=p.total_q_blocks, top_k=p.top_k,
+            block_x=p.block_x, max_blocks_per_seq=0 if tnd else p.block_table.shape[1],
+            num_pages=p.num_pages, kv_page_stride=p.kv_page_stride,
+            dtype=gi.TORCH_DTYPES[p.dtype], out_dtype=gi.TORCH_DTYPES[p.out_dtype],
+            mask_mode=p.mask_mode, win_left=p.win_left, win_right=p.win_right,
+            quant_mode=p.quant_mode, return_lse=p.return_lse,
+            has_seqused_q=p.seqused_q is not None, scale=p.scale, kv_layout=1 if tnd else 0)
+        t = lambda x: None if x is None else torch.as_tensor(x).to(dev)
+        self.idx, self.cnt, self.cu, self.skv = (t(p.sparse_block_idx), t(p.sparse_block_count),
+                                                 t(p.cu_seqlens_q), t(p.seqused_kv))
+        self.table = None if tnd else t(p.block_table)
+        self.cu_kv = t(p.cu_seqlens_kv) if tnd else None
+        self.squ = None if p.seqused_q is None else t(p.seqused_q)
+        f32 = lambda s: None if s is None else torch.as_tensor(s, dtype=torch.float32).to(dev)
+        self.qs, self.ks, self.vs = f32(p.q_scale), f32(p.k_scale), f32(p.v_scale)
+        self.meta = torch.empty(1024, dtype=torch.int32, device=dev)
+        self.out = torch.empty(p.q.shape, dtype=gi.TORCH_DTYPES[p.out_dtype], device=dev)
+        self.lse = (torch.empty(p.q.shape[:2], dtype=torch.float32, device=dev)
+                    if p.return_lse else None)
+        self.ws = torch.zeros(gbsa_workspace_size(self.params), dtype=torch.uint8, device=dev)
+        self.P = gbsa_num_workers(self.params)
+        rows = p.block_x * p.num_heads_q // p.num_heads_kv  # packed GQA rows per unit
+        self.kernel = ("fwd_decode_kernel" if rows <= 16 else
+                       "fwd_prefill_pp32_kernel" if rows > 256 else
+                       "fwd_prefill_ks32_kernel" if rows > 64 else "fwd_prefill_kernel")
+
+    def metadata(self):
+        from block_sparse_paged_gbsa_amd import gbsa_metadata
+        gbsa_metadata(self.params, self.cnt, self.cu, self.squ, self.skv, self.meta)
+
+    def forward(self):
+        from block_sparse_paged_gbsa_amd import gbsa_forward, gbsa_forward_ex, gbsa_forward_tnd
+        p = self.p
+        if self.umask is not None:
+            gbsa_forward_ex(self.params, p.q, p.k, p.v, self.idx, self.cnt, self.meta, self.cu,
+                            self.squ, cu_seqlens_kv=self.cu_kv, seqused_kv=self.skv,
+                            block_table=self.table, q_scale=self.qs, k_scale=self.ks,
+                            v_scale=self.vs, atten_mask=self.umask, out=self.out, lse=self.lse,
+                            workspace=self.ws)
+        elif self.tnd:
+            gbsa_forward_tnd(self.params, p.q, p.k, p.v, self.idx, self.cnt, self.meta, self.cu,
+                             self.squ, self.cu_kv, self.skv, self.qs, self.ks, self.vs, None,
+                             self.out, self.lse, self.ws)
+        else:
+            gbsa_forward(self.params, p.q, p.k, p.v, self.idx, self.cnt, self.meta, self.cu,
+                         self.squ, self.skv, self.table, self.qs, self.ks, self.vs, None,
+                         self.out, self.lse, self.ws)
+
+    def step(self):
+        self.metadata()
+        self.forward()
+
+    def status(self) -> int:
+        return int(self.ws[:4].view(__import__("torch").int32)[0].item())
+
+
+def cache_flusher(dev):
+    """A read of 1 GiB that evicts the L2s and the Infinity Cache (256 MiB) without leaving
+    dirty lines behind, so the next kernel finds none of its data cached and has no unrelated
+    write-back to do."""
+    import torch
+    flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    acc = torch.empty((), dtype=torch.int64, device=dev)
+    return lambda: torch.sum(flush, dtype=torch.int64, out=acc)
+
+
+def cold_forward_ms(w, flush, iters: int, stream) -> float:
+    """The forward's average duration when every launch follows a cache-evicting read:
+    (flush + forward) x iters minus flush x iters, each back to back between two events."""
+    both = timed(lambda: (flush(), w.forward()), iters, stream)
+    alone = timed(flush, iters, stream)
+    return both - alone
+
+
+def roofline(w, alg_bytes, alg_flops, fwd_ms):
+    """roofline object of the workload's dominant kernel from the forward's duration."""
+    p = w.p
+    if w.kernel == "fwd_decode_kernel":
+        achieved = alg_bytes / (fwd_ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    achieved = alg_flops / (fwd_ms * 1e-3) / 1e12
+    peak = MFMA_PEAK_TFLOPS[p.dtype]
+    return {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4)}
+
+
+def config_sweep(dev, stream, iters: int, skip=None, known=None):
+    """Every workload in the benchmark's launch configuration: forward ms (launches back to
+    back), rate and roofline fraction of its kernel. `known` carries a workload already timed
+    in this run (reused as is)."""
+    import torch
+
+    import gbsa_inputs as gi
+    out = {}
+    for cfg in sorted(gi.CONFIG_NAMES):
+        name = gi.CONFIG_NAMES[cfg]
+        if known is not None and name in known:
+            out[name] = known[name]
+            continue
+        log(f"[bench] sweep: workload {cfg} ({name})")
+        p = gi.config(cfg, device=dev)
+        w = Workload(p, dev)
+        alg_bytes, alg_flops = algorithmic_work(p)
+        w.step()
+        torch.cuda.synchronize()
+        per = timed(w.forward, 1, stream)
+        n = int(min(iters, max(3, 2000.0 / max(per, 1e-3))))  # about 2 s per workload at most
+        w.metadata()
+        fwd_ms = timed(w.forward, n, stream)
+        meta_ms = timed(w.metadata, n, stream)
+        assert w.status() == 0, f"{name}: metadata mismatch flagged by the kernels"
+        roof = roofline(w, alg_bytes, alg_flops, fwd_ms)
+        out[name] = {"kernel": w.kernel, "forward_ms": round(fwd_ms, 5),
+                     "metadata_ms": round(meta_ms, 5), "launches": n, "workers": w.P,
+                     "dtype": p.dtype, "tflops": round(alg_flops / (fwd_ms * 1e-3) / 1e12, 2),
+                     "gbs": round(alg_bytes / (fwd_ms * 1e-3) / 1e9, 1), "roofline": roof}
+        log(f"[bench] sweep: {name} forward {fwd_ms:.4f} ms, {roof['achieved']} "
+            f"{roof['unit']} = {roof['frac']} of peak")
+        del w, p
+        torch.cuda.empty_cache()
+    return out
 
 
 def main(argv=None):
@@ -333,7 +499,12 @@ def main(argv=None):
                     help="workload 3 only: query rows per q-block (fewer than 16 packs fewer "
                          "rows per unit and selects the 17-64 or 65-256 row kernels)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
-                    help="seconds of oracle work for the CPU baseline (0 = skip)")
+                    help="seconds of oracle wall time for the CPU baseline (0 = skip)")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip timing the other workloads (the `configs` object)")
+    ap.add_argument("--cold-only", action="store_true",
+                    help="only run cache-flushed forward launches of the workload (for a "
+                         "kernel-trace profile of them) and print their count")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter scale reference)")
     a = ap.parse_args(argv)
@@ -355,9 +526,6 @@ def main(argv=None):
     import torch
 
     import gbsa_inputs as gi
-    from block_sparse_paged_gbsa_amd import (gbsa_forward, gbsa_forward_ex, gbsa_forward_tnd,
-                                             gbsa_metadata, gbsa_num_workers,
-                                             gbsa_workspace_size, make_params)
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
@@ -391,62 +559,35 @@ def main(argv=None):
         umask = (p_idx > t_idx + off).to(torch.uint8)
         del t_idx, p_idx
         p.mask_mode = 0
-    params = make_params(batch=p.batch, num_heads_q=p.num_heads_q, num_heads_kv=p.num_heads_kv,
-                         total_q=p.total_q, total_q_blocks=p.total_q_blocks, top_k=p.top_k,
-                         block_x=p.block_x,
-                         max_blocks_per_seq=0 if tnd else p.block_table.shape[1],
-                         num_pages=p.num_pages, kv_page_stride=p.kv_page_stride,
-                         dtype=gi.TORCH_DTYPES[p.dtype], out_dtype=gi.TORCH_DTYPES[p.out_dtype],
-                         mask_mode=p.mask_mode, win_left=p.win_left, win_right=p.win_right,
-                         quant_mode=p.quant_mode, return_lse=p.return_lse,
-                         has_seqused_q=p.seqused_q is not None, scale=p.scale,
-                         kv_layout=1 if tnd else 0)
-    t = lambda x: None if x is None else torch.as_tensor(x).to(dev)
-    idx, cnt, cu, skv = (t(p.sparse_block_idx), t(p.sparse_block_count), t(p.cu_seqlens_q),
-                         t(p.seqused_kv))
-    table = None if tnd else t(p.block_table)
-    cu_kv = t(p.cu_seqlens_kv) if tnd else None
-    squ = None if p.seqused_q is None else t(p.seqused_q)
-    f32 = lambda s: None if s is None else torch.as_tensor(s, dtype=torch.float32).to(dev)
-    qs, ks, vs = f32(p.q_scale), f32(p.k_scale), f32(p.v_scale)
-    meta = torch.empty(1024, dtype=torch.int32, device=dev)
-    out = torch.empty(p.q.shape, dtype=gi.TORCH_DTYPES[p.out_dtype], device=dev)
-    lse = torch.empty(p.q.shape[:2], dtype=torch.float32, device=dev) if p.return_lse else None
-    ws = torch.zeros(gbsa_workspace_size(params), dtype=torch.uint8, device=dev)
-    P = gbsa_num_workers(params)
+    w = Workload(p, dev, tnd, umask)
+    stream = torch.cuda.current_stream()
+    hbm_bound = w.kernel == "fwd_decode_kernel"
 
-    def forward():
-        if umask is not None:
-            gbsa_forward_ex(params, p.q, p.k, p.v, idx, cnt, meta, cu, squ,
-                            cu_seqlens_kv=cu_kv, seqused_kv=skv, block_table=table, q_scale=qs,
-                            k_scale=ks, v_scale=vs, atten_mask=umask, out=out, lse=lse,
-                            workspace=ws)
-        elif tnd:
-            gbsa_forward_tnd(params, p.q, p.k, p.v, idx, cnt, meta, cu, squ, cu_kv, skv, qs,
-                             ks, vs, None, out, lse, ws)
-        else:
-            gbsa_forward(params, p.q, p.k, p.v, idx, cnt, meta, cu, squ, skv, table, qs, ks,
-                         vs, None, out, lse, ws)
-
-    def step():
-        gbsa_metadata(params, cnt, cu, squ, skv, meta)
-        forward()
+    if a.cold_only:
+        flush = cache_flusher(dev)
+        w.step()
+        for _ in range(a.steps):
+            flush()
+            w.forward()
+        torch.cuda.synchronize()
+        assert w.status() == 0, "metadata mismatch flagged by the kernels"
+        print(json.dumps({"cold_forward_launches": a.steps, "kernel": w.kernel,
+                          "workload": p.name}), flush=True)
+        return 0
 
     alg_bytes, alg_flops = algorithmic_work(p)
-    log(f"[bench] workers={P} algorithmic bytes={alg_bytes} flops={alg_flops}")
+    log(f"[bench] workers={w.P} algorithmic bytes={alg_bytes} flops={alg_flops}")
     for _ in range(a.warmup):
-        step()
+        w.step()
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
 
     # whole steps, back to back
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(a.steps):
-        step()
+        w.step()
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -455,14 +596,7 @@ def main(argv=None):
     # the forward launch alone (main kernel with its fused split-KV combine): K launches back
     # to back between two events on their stream, so the average is the kernel's duration
     # without per-launch gaps
-    f0 = torch.cuda.Event(enable_timing=True)
-    f1 = torch.cuda.Event(enable_timing=True)
-    f0.record(stream)
-    for _ in range(a.steps):
-        forward()
-    f1.record(stream)
-    torch.cuda.synchronize()
-    fwd_ms = f0.elapsed_time(f1) / a.steps
+    fwd_ms = timed(w.forward, a.steps, stream)
 
     # the same step replayed from a HIP graph (metadata + forward captured once): what a serving
     # loop that captures its step pays, without per-call launch work
@@ -472,10 +606,10 @@ def main(argv=None):
         side.wait_stream(stream)
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.stream(side):
-            step()
+            w.step()
             side.synchronize()
             with torch.cuda.graph(graph, stream=side):
-                step()
+                w.step()
         stream.wait_stream(side)
         graph.replay()
         torch.cuda.synchronize()
@@ -483,80 +617,90 @@ def main(argv=None):
         del graph
     except RuntimeError as e:  # capture unavailable: report the eager figures only
         log(f"[bench] graph capture failed: {e}")
-    meta_ms = timed(lambda: gbsa_metadata(params, cnt, cu, squ, skv, meta), a.steps, stream)
-    status = int(ws[:4].view(torch.int32)[0].item())
-    assert status == 0, "metadata mismatch flagged by the kernels"
+    meta_ms = timed(w.metadata, a.steps, stream)
+    assert w.status() == 0, "metadata mismatch flagged by the kernels"
     log(f"[bench] step {ms_step:.4f} ms, forward {fwd_ms:.4f} ms, wall {wall:.3f} s")
 
-    hbm_bound = a.config == 2
-    fwd_cold_ms = None
-    if hbm_bound:
-        # every launch after a 1 GiB write that evicts the L2s and the Infinity Cache: the
-        # selected K/V bytes then come from HBM
-        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        times = []
-        for i in range(20):
-            flush.fill_(i & 0xff)
-            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            c0.record(stream)
-            forward()
-            c1.record(stream)
-            torch.cuda.synchronize()
-            times.append(c0.elapsed_time(c1))
-        fwd_cold_ms = float(np.median(times))
-        del flush
+    # every forward launch after a 1 GiB read that evicts the L2s and the Infinity Cache: the
+    # selected K/V bytes then come from HBM
+    flush = cache_flusher(dev)
+    fwd_cold_ms = cold_forward_ms(w, flush, a.steps, stream)
+    del flush
+    torch.cuda.empty_cache()
     ceil = ceilings(p, hbm_bound, stream)
-    log(f"[bench] metadata {meta_ms:.4f} ms, cold forward {fwd_cold_ms} ms, ceilings {ceil}")
+    log(f"[bench] metadata {meta_ms:.4f} ms, cold forward {fwd_cold_ms:.4f} ms, ceilings {ceil}")
 
     gbs = alg_bytes / (ms_step * 1e-3) / 1e9
     tflops = alg_flops / (ms_step * 1e-3) / 1e12
-    rows = p.block_x * p.num_heads_q // p.num_heads_kv  # packed GQA rows per unit
-    kernel = ("fwd_decode_kernel" if rows <= 16 else
-              "fwd_prefill_pp32_kernel" if rows > 256 else
-              "fwd_prefill_ks32_kernel" if rows > 64 else "fwd_prefill_kernel")
     # the name carries "_tnd" after the layout rewrite
     workload = p.name + ("_user_mask" if umask is not None else "")
-    traffic = measured_traffic(kernel, workload)
+    traffic = measured_traffic(w.kernel, workload)
     if hbm_bound:
-        achieved = alg_bytes / (fwd_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
+        # the roofline of the HBM-bound kernel is taken on cache-flushed launches; the warm
+        # figure (launches back to back) is reported beside it
+        roof = roofline(w, alg_bytes, alg_flops, fwd_cold_ms)
+        roof["timing"] = "cache-flushed launches"
+        roof["achieved_warm"] = roofline(w, alg_bytes, alg_flops, fwd_ms)["achieved"]
         metric_value, unit = gbs, "GB/s"
     else:
-        achieved = alg_flops / (fwd_ms * 1e-3) / 1e12
-        peak = MFMA_PEAK_TFLOPS[p.dtype]
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic}
+        roof = roofline(w, alg_bytes, alg_flops, fwd_ms)
+        roof["timing"] = "launches back to back"
         metric_value, unit = tflops, "TFLOP/s"
+    roof["traffic"] = traffic
+    main_entry = {"kernel": w.kernel, "forward_ms": round(fwd_ms, 5),
+                  "forward_cold_ms": round(fwd_cold_ms, 5), "metadata_ms": round(meta_ms, 5),
+                  "launches": a.steps, "workers": w.P, "dtype": p.dtype,
+                  "tflops": round(alg_flops / (fwd_ms * 1e-3) / 1e12, 2),
+                  "gbs": round(alg_bytes / (fwd_ms * 1e-3) / 1e9, 1),
+                  "roofline": roofline(w, alg_bytes, alg_flops,
+                                       fwd_cold_ms if hbm_bound else fwd_ms)}
+    default_shape = (not tnd and umask is None and (a.batch, a.top_k) == (64, 16) and
+                     a.block_x == 128)
+    config = {"workload": workload, "kv_layout": "TND" if tnd else "PA_BBND",
+              "mask": "user (causal pattern)" if umask is not None else
+                      {0: "none", 1: "causal", 2: "causal top-left"}[p.mask_mode],
+              "batch": p.batch, "num_heads_q": p.num_heads_q, "num_heads_kv": p.num_heads_kv,
+              "head_dim": 128, "block_shape": [p.block_x, 128], "top_k": p.top_k,
+              ("kv_rows" if tnd else "kv_pages"): p.num_pages, "workers": w.P}
 
     cpu = None
     if a.cpu_budget > 0 and umask is None:
-        log("[bench] timing the float64 oracle on a sample")
+        log("[bench] timing the float64 oracle on a sample, all host cores")
         cb = cpu_baseline(p, a.cpu_budget)
         v = (cb["bytes"] / cb["seconds"] / 1e9) if hbm_bound else (cb["flops"] / cb["seconds"] / 1e12)
-        cpu = {"value": round(v, 6), "unit": unit, "cores": 1, "kind": "oracle",
+        cpu = {"value": round(v, 6), "unit": unit, "cores": cb["cores"], "kind": "oracle",
                "sample": (f"all {cb['units']} q-blocks (all KV heads) of the workload, "
                           f"{cb['passes']} passes" if cb["whole"] else
                           f"{cb['units']} q-blocks (all KV heads) of the same workload") +
-                         f", {cb['seconds']:.1f} s of single-threaded float64 numpy"}
+                         f", {cb['seconds']:.1f} s wall of float64 numpy on a pool of "
+                         f"{cb['cores']} processes, one q-block per task",
+               "cpu_model": cb["cpu_model"], "host_cores": cb["host_cores"],
+               "blas_threads_per_process": 1}
+        log(f"[bench] oracle: {cpu}")
+
+    configs = None
+    if not a.no_sweep:
+        del w
+        torch.cuda.empty_cache()
+        known = {p.name: main_entry} if default_shape else None
+        del p
+        torch.cuda.empty_cache()
+        configs = config_sweep(dev, stream, a.steps, known=known)
+        p = None
     res = {
         "metric": "block-sparse attn effective TFLOP/s + HBM GB/s, % of roofline, 1 MI355X",
         "value": round(metric_value, 3), "unit": unit, "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": p.dtype, "data": "synthetic",
-        "config": {"workload": workload, "kv_layout": "TND" if tnd else "PA_BBND",
-                   "mask": "user (causal pattern)" if umask is not None else
-                           {0: "none", 1: "causal", 2: "causal top-left"}[p.mask_mode],
-                   "batch": p.batch,
-                   "num_heads_q": p.num_heads_q, "num_heads_kv": p.num_heads_kv,
-                   "head_dim": 128, "block_shape": [p.block_x, 128], "top_k": p.top_k,
-                   ("kv_rows" if tnd else "kv_pages"): p.num_pages, "workers": P},
+        "scaling": "weak", "vs_baseline": None, "dtype": main_entry["dtype"],
+        "data": "synthetic",
+        "config": config,
         "effective_tflops": round(tflops, 3), "hbm_gbs": round(gbs, 2),
         "forward_ms": round(fwd_ms, 5), "metadata_ms": round(meta_ms, 5),
         "ms_per_step_graph": None if graph_ms is None else round(graph_ms, 5),
-        "forward_cold_ms": None if fwd_cold_ms is None else round(fwd_cold_ms, 5),
-        "ceilings": ceil, "kernel": kernel, "algorithmic_bytes": alg_bytes,
+        "forward_cold_ms": round(fwd_cold_ms, 5),
+        "ceilings": ceil, "kernel": main_entry["kernel"], "algorithmic_bytes": alg_bytes,
         "algorithmic_flops": alg_flops, "roofline": roof, "cpu_baseline": cpu,
+        "configs": configs,
     }
     print(json.dumps(res), flush=True)
     return 0

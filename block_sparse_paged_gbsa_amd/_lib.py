@@ -34,7 +34,7 @@ EXPORTED = ("gbsa_check_params", "gbsa_num_workers", "gbsa_metadata", "gbsa_work
 # gbsa_validate violation bits (include/gbsa.h)
 VALIDATE_BITS = {0x01: "cu_seqlens_q", 0x02: "seqused_q", 0x04: "kv_length",
                  0x08: "cu_seqlens_kv", 0x10: "block_table", 0x20: "count", 0x40: "selection",
-                 0x80: "mask_extent"}
+                 0x80: "mask_extent", 0x100: "max_seqlen"}
 MASK_NONE, MASK_CAUSAL, MASK_CAUSAL_TOP_LEFT = 0, 1, 2
 
 
@@ -66,7 +66,9 @@ class GbsaParams(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("num_workers", ctypes.c_int32),
         ("kv_layout", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 3),
+        ("max_seqlen_q", ctypes.c_int32),
+        ("max_seqlen_kv", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 1),
     ]
 
 

@@ -49,8 +49,10 @@ def make_params(*, batch: int, num_heads_q: int, num_heads_kv: int, total_q: int
                 out_dtype=None, mask_mode: int = 1, win_left: int = -1, win_right: int = -1,
                 quant_mode: int = 0, softmax_precision: int = 1, return_lse: bool = False,
                 has_seqused_q: bool = False, scale: float = 0.0, num_workers: int = 0,
-                block_y: int = 128, head_dim: int = 128, kv_layout: int = 0) -> GbsaParams:
-    """kv_layout 0 = PA_BBND (num_pages pages), 1 = TND (num_pages = rows of key/value)."""
+                block_y: int = 128, head_dim: int = 128, kv_layout: int = 0,
+                max_seqlen_q: int = -1, max_seqlen_kv: int = -1) -> GbsaParams:
+    """kv_layout 0 = PA_BBND (num_pages pages), 1 = TND (num_pages = rows of key/value).
+    max_seqlen_q / max_seqlen_kv: -1 (not given) or bounds that gbsa_validate checks."""
     p = GbsaParams()
     p.batch = batch
     p.num_heads_q = num_heads_q
@@ -79,6 +81,8 @@ def make_params(*, batch: int, num_heads_q: int, num_heads_kv: int, total_q: int
     p.scale = float(scale)
     p.num_workers = int(num_workers)
     p.kv_layout = int(kv_layout)
+    p.max_seqlen_q = int(max_seqlen_q)
+    p.max_seqlen_kv = int(max_seqlen_kv)
     return p
 
 
@@ -333,10 +337,13 @@ def generic_block_sparse_attention_metadata(
     if seqused_kv is None and layout_kv == "PA_BBND":
         raise ValueError("seqused_kv is required with PA_BBND")
     dt = torch.float8_e4m3fn if int(quant_mode) == 5 else torch.float16
-    # total_q, max_blocks_per_seq and num_pages do not enter the task split
-    p = make_params(total_q=1, max_blocks_per_seq=1, num_pages=1, dtype=dt,
+    # total_q, max_blocks_per_seq and num_pages do not enter the task split: they only have to
+    # hold the given length bounds, which are range-checked like the main call's
+    msq, mskv = int(max_seqlen_q), int(max_seqlen_kv)
+    p = make_params(total_q=max(1, msq), max_blocks_per_seq=max(1, -(-mskv // 128)),
+                    num_pages=max(1, mskv), dtype=dt,
                     out_dtype=torch.bfloat16 if int(quant_mode) == 5 else None,
-                    num_workers=num_workers, **c)
+                    num_workers=num_workers, max_seqlen_q=msq, max_seqlen_kv=mskv, **c)
     return gbsa_metadata(p, sparse_block_count.contiguous(), cu_seqlens_q.contiguous(),
                          None if seqused_q is None else seqused_q.contiguous(),
                          None if seqused_kv is None else seqused_kv.contiguous())

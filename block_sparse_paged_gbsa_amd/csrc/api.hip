@@ -136,8 +136,12 @@ gbsa_status gbsa_check_params(const gbsa_params* p) {
     if (p->is_packed_gqa != 1) return GBSA_ERR_UNSUPPORTED;
     if (p->has_seqused_q != 0 && p->has_seqused_q != 1) return GBSA_ERR_SHAPE;
     if (p->return_lse != 0 && p->return_lse != 1) return GBSA_ERR_SHAPE;
-    for (int i = 0; i < 3; ++i)
-        if (p->reserved[i] != 0) return GBSA_ERR_UNSUPPORTED;
+    if (p->reserved[0] != 0) return GBSA_ERR_UNSUPPORTED;
+    // max_seqlen_q / max_seqlen_kv: -1 or 0 = not given; a given bound must fit the storage
+    if (p->max_seqlen_q < -1 || p->max_seqlen_kv < -1) return GBSA_ERR_SHAPE;
+    if (p->max_seqlen_q > p->total_q) return GBSA_ERR_SHAPE;
+    if (p->max_seqlen_kv > (tnd ? p->num_pages : (int64_t)p->max_blocks_per_seq * GBSA_PAGE_SIZE))
+        return GBSA_ERR_SHAPE;
     if (!(p->scale == p->scale)) return GBSA_ERR_SHAPE;  // NaN
     return GBSA_OK;
 }
@@ -310,6 +314,8 @@ static gbsa_status forward_impl(const gbsa_params* p, const gbsa_forward_args* g
     a.return_lse = p->return_lse;
     const double scale = p->scale > 0.f ? (double)p->scale : 1.0 / sqrt((double)p->head_dim);
     a.scale_log2 = (float)(scale * 1.4426950408889634);
+    a.T = p->total_q;
+    a.out_nan2 = p->out_dtype == GBSA_DTYPE_F16 ? 0x7e007e00u : 0x7fc07fc0u;
     a.expect[0] = (int32_t)kMagic;
     a.expect[1] = kVersion;
     a.expect[2] = P;
@@ -439,6 +445,8 @@ gbsa_status gbsa_validate(const gbsa_params* p, const gbsa_forward_args* g,
     a.maxb = tnd ? 0 : p->max_blocks_per_seq;
     a.um_rows = g->atten_mask != nullptr ? g->mask_rows : 0;
     a.um_cols = g->atten_mask != nullptr ? g->mask_cols : 0;
+    a.max_sq = p->max_seqlen_q > 0 ? p->max_seqlen_q : 0;
+    a.max_skv = p->max_seqlen_kv > 0 ? p->max_seqlen_kv : 0;
     return launch_validate(a, stream) == hipSuccess ? GBSA_OK : GBSA_ERR_HIP;
 }
 

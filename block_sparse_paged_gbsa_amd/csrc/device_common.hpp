@@ -202,6 +202,21 @@ __device__ __forceinline__ bool header_ok(const FwdArgs& a) {
     return diff == 0;
 }
 
+// A call whose metadata does not match its parameters computes nothing. Every workgroup of
+// the grid fills its share of attention_out and softmax_lse with NaN, so that a caller who
+// does not read the status word cannot take stale memory for a result, and the first one
+// sets the status word.
+__device__ __forceinline__ void refuse(const FwdArgs& a) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(a.ws_status, 1);
+    const int64_t nthr = (int64_t)gridDim.x * blockDim.x;
+    const int64_t first = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t n16 = a.T * a.N1 * 128 * 2 / 16;  // 16-bit outputs, 16 bytes per store
+    const u32x4 nan8 = (u32x4){a.out_nan2, a.out_nan2, a.out_nan2, a.out_nan2};
+    for (int64_t i = first; i < n16; i += nthr) ((u32x4*)a.out)[i] = nan8;
+    if (a.lse != nullptr)
+        for (int64_t i = first; i < a.T * a.N1; i += nthr) a.lse[i] = __builtin_nanf("");
+}
+
 struct Bound {
     int u, s;
 };

@@ -199,7 +199,7 @@ __global__ __launch_bounds__(256, 2) void fwd_decode_kernel(FwdArgs a) {
     const int U = a.meta[3];
     const SeqLens first = seq_lens(a, lane);
     if (!ok) {
-        if (tid == 0) atomicOr(a.ws_status, 1);
+        refuse(a);
         return;
     }
     if (!bound_less(b0, b1) || b0.u >= U) return;

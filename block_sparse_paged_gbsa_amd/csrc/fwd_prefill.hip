@@ -391,7 +391,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_prefill_kernel(FwdArgs a) {
     const int w = lin / a.nst, st = lin - (lin / a.nst) * a.nst;
 
     if (!header_ok(a)) {
-        if (tid == 0) atomicOr(a.ws_status, 1);
+        refuse(a);
         return;
     }
     const Bound b0 = read_bound(a.meta, w), b1 = read_bound(a.meta, w + 1);
@@ -856,7 +856,7 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32_kernel(FwdArgs a) {
     const int w = lin / a.nst, st = lin - (lin / a.nst) * a.nst;
 
     if (!header_ok(a)) {
-        if (tid == 0) atomicOr(a.ws_status, 1);
+        refuse(a);
         return;
     }
     const Bound b0 = read_bound(a.meta, w), b1 = read_bound(a.meta, w + 1);
@@ -1076,7 +1076,7 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32_kernel(FwdArgs a) {
     const int w = lin / a.nst, st = lin - (lin / a.nst) * a.nst;
 
     if (!header_ok(a)) {
-        if (tid == 0) atomicOr(a.ws_status, 1);
+        refuse(a);
         return;
     }
     const Bound b0 = read_bound(a.meta, w), b1 = read_bound(a.meta, w + 1);

@@ -69,6 +69,8 @@ struct FwdArgs {
     int32_t B, N1, N2, G, X, topK, tqb, maxb, P, M, nst;
     int32_t mask, wl, wr, return_lse;  // mask: 0 none, 1 causal bottom-right, 2 top-left
     float scale_log2;      // softmax scale * log2(e)
+    int64_t T;             // rows of query / attention_out / softmax_lse
+    uint32_t out_nan2;     // two quiet NaNs of the output type, packed (refused calls)
     int32_t expect[kHeaderWords];  // expected header words (0, 1, 2 and 7..21 are checked)
 };
 
@@ -85,6 +87,7 @@ struct ValArgs {
     int32_t* out;           // device flags
     int64_t total_q, num_pages, kv_rows;
     int32_t B, N2, X, tqb, topK, maxb, um_rows, um_cols;
+    int32_t max_sq, max_skv;  // given length bounds, or 0
 };
 
 // Workspace layout (byte offsets), a pure function of P and M.

@@ -40,35 +40,6 @@ __global__ __launch_bounds__(256) void stream_kernel(const u32x4* src, int64_t n
     sink_if(acc, sink);
 }
 
-// LDS read rate: eight waves read a 64 KiB window of a 96 KiB LDS array with 16-byte loads,
-// each wave a contiguous 1 KiB per load (no bank conflicts); the static size keeps one
-// workgroup per CU. Per workgroup: shader-clock cycles (s_memtime) and 100 MHz ticks
-// (s_memrealtime) over the read loop.
-constexpr int kLdsProbeBytes = 96 * 1024;
-constexpr int kLdsReadsPerIter = 8;
-__global__ __launch_bounds__(512, 1) void lds_read_kernel(int iters, uint64_t* ticks,
-                                                          u32x4* sink) {
-    __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsProbeBytes];
-    const int tid = threadIdx.x;
-    for (int i = tid; i < kLdsProbeBytes / 16; i += 512)
-        ((u32x4*)lds)[i] = (u32x4){(uint32_t)i, (uint32_t)i + 1, (uint32_t)i + 2, (uint32_t)i + 3};
-    __syncthreads();
-    u32x4 acc = {0, 0, 0, 0};
-    const uint64_t c0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
-    for (int it = 0; it < iters; ++it) {
-#pragma unroll
-        for (int k = 0; k < kLdsReadsPerIter; ++k)
-            acc ^= *(const u32x4*)(lds + ((tid * 16 + k * 8192 + it * 16) & 65535));
-    }
-    __syncthreads();
-    const uint64_t c1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
-    if (tid == 0) {
-        ticks[2 * blockIdx.x] = c1 - c0;
-        ticks[2 * blockIdx.x + 1] = r1 - r0;
-    }
-    if ((acc[0] ^ acc[1] ^ acc[2] ^ acc[3]) == kNever) sink[blockIdx.x * 512 + tid] = acc;
-}
-
 }  // namespace
 
 extern "C" {
@@ -96,15 +67,6 @@ int gbsa_probe_stream(const void* src, int64_t bytes, int32_t grid, void* sink,
         return -1;
     hipLaunchKernelGGL(stream_kernel, dim3(grid), dim3(256), 0, stream, (const u32x4*)src,
                        bytes / 16, (u32x4*)sink);
-    return (int)hipGetLastError();
-}
-
-int gbsa_probe_lds_read(int32_t iters, int32_t grid, uint64_t* ticks, void* sink,
-                        hipStream_t stream) {
-    if (ticks == nullptr || sink == nullptr || iters <= 0 || iters > (1 << 24) || grid <= 0)
-        return -1;
-    hipLaunchKernelGGL(lds_read_kernel, dim3(grid), dim3(512), 0, stream, iters, ticks,
-                       (u32x4*)sink);
     return (int)hipGetLastError();
 }
 

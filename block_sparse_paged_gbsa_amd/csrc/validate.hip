@@ -71,6 +71,8 @@ __global__ __launch_bounds__(kThreads) void validate_kernel(ValArgs a) {
             }
             if (a.umask != nullptr && (sq > a.um_rows || kl > a.um_cols))
                 f |= GBSA_BAD_MASK_EXTENT;
+            if ((a.max_sq > 0 && st > a.max_sq) || (a.max_skv > 0 && kl > a.max_skv))
+                f |= GBSA_BAD_MAX_SEQLEN;
         }
         int tot;
         const int ex = block_prefix(nq, scan, &tot);

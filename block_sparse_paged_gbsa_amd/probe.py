@@ -9,7 +9,7 @@ import ctypes
 import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgbsa_probe.so")
-EXPORTED = ("gbsa_probe_gather", "gbsa_probe_stream", "gbsa_probe_lds_read")
+EXPORTED = ("gbsa_probe_gather", "gbsa_probe_stream")
 
 _lib = None
 
@@ -27,8 +27,6 @@ def load() -> ctypes.CDLL:
         lib.gbsa_probe_gather.restype = ctypes.c_int
         lib.gbsa_probe_stream.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, vp, vp]
         lib.gbsa_probe_stream.restype = ctypes.c_int
-        lib.gbsa_probe_lds_read.argtypes = [ctypes.c_int32, ctypes.c_int32, vp, vp, vp]
-        lib.gbsa_probe_lds_read.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -47,19 +45,3 @@ def gather(key, value, slice_offsets, row_bytes: int, row_stride: int, sink, str
 def stream_read(src, nbytes: int, grid: int, sink, stream) -> None:
     _check("gbsa_probe_stream", load().gbsa_probe_stream(src.data_ptr(), nbytes, grid,
                                                          sink.data_ptr(), stream.cuda_stream))
-
-
-def lds_read(iters: int = 20000, grid: int = 256, device="cuda") -> dict:
-    """LDS read rate per CU: median bytes per shader clock over the workgroups, and the shader
-    clock those cycles ran at (s_memtime against the 100 MHz s_memrealtime)."""
-    import torch
-    ticks = torch.zeros(2 * grid, dtype=torch.int64, device=device)
-    sink = torch.empty(grid * 8192, dtype=torch.uint8, device=device)
-    stream = torch.cuda.current_stream(device)
-    _check("gbsa_probe_lds_read", load().gbsa_probe_lds_read(
-        iters, grid, ticks.data_ptr(), sink.data_ptr(), stream.cuda_stream))
-    torch.cuda.synchronize(device)
-    t = ticks.view(grid, 2).cpu().double()
-    bpc = (65536.0 * iters / t[:, 0]).median().item()
-    ghz = (t[:, 0] / (t[:, 1] / 100e6) / 1e9).median().item()
-    return {"bytes_per_clock_per_cu": bpc, "shader_clock_ghz": ghz}

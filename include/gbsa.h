@@ -134,7 +134,17 @@ typedef struct gbsa_params {
     int32_t num_workers;        /* 0 = chosen by the library from the shapes, else 1..999 */
     int32_t kv_layout;          /* gbsa_kv_layout: GBSA_KV_PA_BBND (gbsa_forward) or
                                    GBSA_KV_TND (gbsa_forward_tnd) */
-    int32_t reserved[3];        /* must be 0 */
+    int32_t max_seqlen_q;       /* -1 or 0: not given (the article's default -1). Else an
+                                   upper bound on every sequence's query storage length
+                                   (cu_seqlens_q[b+1] - cu_seqlens_q[b]); at most total_q */
+    int32_t max_seqlen_kv;      /* -1 or 0: not given. Else an upper bound on every
+                                   sequence's visible KV length (seqused_kv, or the TND
+                                   storage length without it); at most what the KV storage
+                                   holds (max_blocks_per_seq * 128, or T_kv with TND).
+                                   Both bounds are the metadata operator's max_seqlen_q /
+                                   max_seqlen_kv ("PyTorch API" section); the kernels need
+                                   neither, gbsa_validate checks them against the tensors */
+    int32_t reserved[1];        /* must be 0 */
 } gbsa_params;
 
 /*
@@ -212,8 +222,9 @@ gbsa_status gbsa_workspace_size(const gbsa_params* params, size_t* bytes);
  * seqused_kv. The kernels skip a slot whose index is negative or whose block starts at or
  * beyond seqused_kv[b], and never read past the selection arrays.
  * If the metadata's magic, worker count or parameter fingerprint do not match these
- * params, the kernels write nothing to the outputs and set word 0 of the workspace to a
- * non-zero value (readable by the caller after the stream completes).
+ * params, the kernels compute nothing: they fill attention_out (all T x N1 x 128 entries)
+ * and softmax_lse with NaN and set word 0 of the workspace to a non-zero value (readable by
+ * the caller after the stream completes).
  * Errors: gbsa_check_params errors; GBSA_ERR_NULL; GBSA_ERR_METADATA; GBSA_ERR_WORKSPACE;
  * GBSA_ERR_DTYPE (scales inconsistent with quant_mode); GBSA_ERR_UNSUPPORTED (kv_layout is
  * not PA_BBND); GBSA_ERR_HIP on a failed launch.
@@ -325,16 +336,23 @@ gbsa_status gbsa_forward_ex(const gbsa_params* params, const gbsa_forward_args* 
                                        sequence's visible KV blocks (skipped by the kernels) */
 #define GBSA_BAD_MASK_EXTENT 0x80   /* user mask rows/cols do not cover every active query row
                                        and visible key (the uncovered ones are not masked) */
+#define GBSA_BAD_MAX_SEQLEN 0x100   /* a sequence longer than params->max_seqlen_q (query
+                                       storage) or max_seqlen_kv (visible KV), when given */
 /*
- * Rules 0x20, 0x40 and 0x80 describe inputs the kernels handle in a defined way (clamp, skip,
- * leave unmasked); the others make the forward read undefined data. Errors (returned, nothing
+ * Rules 0x20, 0x40, 0x80 and 0x100 describe inputs the kernels handle in a defined way (clamp,
+ * skip, leave unmasked, bounds unused); the others make the forward read undefined data. Errors (returned, nothing
  * enqueued): as gbsa_forward_ex, minus the metadata/workspace/output pointers, which are not
  * needed here; GBSA_ERR_NULL if violations is NULL.
  */
 gbsa_status gbsa_validate(const gbsa_params* params, const gbsa_forward_args* args,
                           int32_t* violations, hipStream_t stream);
 
-/* Human-readable text for a status (static storage). */
+/*
+ * Human-readable text for a status (static storage, never NULL; unknown values give
+ * "unknown status"). The article's "aclnn API" section has the first stage validate its
+ * arguments and answer with a status code; its code table is not on the page, so the codes
+ * and their texts are this library's own (gbsa_status above).
+ */
 const char* gbsa_status_string(gbsa_status status);
 
 #ifdef __cplusplus

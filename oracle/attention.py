@@ -275,12 +275,3 @@ def sparse_attention(inp: Inputs, rows: Optional[Iterable[int]] = None
             L[tg[:, None], heads[None, :]] = lse
         done[inp.cu[b] + ts] = True
     return O, L, done
-
-
-def unit_flops(inp: Inputs, b: int, n2: int, gl: int) -> int:
-    """Effective FLOPs of one unit: 4*D per (row, head, gathered key) (QK^T and PV)."""
-    g = inp.starts[b] + gl
-    sq = inp.sq(b)
-    nrows = min((gl + 1) * inp.X, sq, inp.storage(b)) - gl * inp.X
-    pos, _, _ = gather_unit(inp, b, n2, g)
-    return 4 * inp.D * nrows * inp.G * len(pos)

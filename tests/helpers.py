@@ -1,6 +1,10 @@
 """Test-side marshalling: problems from gbsa_inputs to oracle inputs (numpy bit patterns)."""
 from __future__ import annotations
 
+import json
+import multiprocessing
+import os
+
 import numpy as np
 import torch
 
@@ -55,6 +59,11 @@ def dequant(t: torch.Tensor, dtype: str, scale=None, head_axis=None) -> torch.Te
 
 TOL = {"f16": 4e-3, "bf16": 1.6e-2, "fp8": 6e-2}
 LSE_RTOL = 1e-3
+# Absolute allowance of the LSE check, for rows whose LSE is zero to within rounding (a single
+# visible logit near 0, where a relative error is undefined): the fp32 rounding of a logit and
+# of the final log, a few 1e-6 for the logit magnitudes of these inputs. It only matters below
+# |LSE| = LSE_ATOL / LSE_RTOL = 0.03; every other row is held to the plain relative bar.
+LSE_ATOL = 3e-5
 
 
 def gpu_params(p, num_workers: int = 0):
@@ -127,29 +136,42 @@ class GpuProblem:
         return params, meta, out, lse, ws
 
 
-def out_f64(out: torch.Tensor) -> np.ndarray:
-    return out.detach().float().cpu().numpy().astype(np.float64)
+def out_f64(out: torch.Tensor, rows=None) -> np.ndarray:
+    """float64 copy of an output (optionally only the rows of a boolean mask over its first
+    axis, selected before the conversion so that never-written rows are not touched)."""
+    x = out.detach()
+    if rows is not None:
+        x = x[torch.as_tensor(np.asarray(rows), device=x.device)]
+    return x.float().cpu().numpy().astype(np.float64)
 
 
 def compare(p, out, lse, O_ref, L_ref, rows_mask, label=""):
     """Max-abs O error and LSE relative error on the oracle's computed rows; asserts the bar."""
-    O = out_f64(out)[rows_mask]
-    Oref = O_ref[rows_mask]
+    return compare_rows(p, out, lse, np.nonzero(rows_mask)[0], O_ref[rows_mask],
+                        L_ref[rows_mask], label)
+
+
+def compare_rows(p, out, lse, rows, Oref, Lr_all, label=""):
+    """compare() on explicit global rows with the oracle's values of just those rows."""
+    rows_mask = np.asarray(rows, dtype=np.int64)
+    O = out_f64(out, rows_mask)
     assert np.isfinite(O).all(), f"{label}: non-finite output"
     err = float(np.max(np.abs(O - Oref))) if O.size else 0.0
     assert err <= TOL[p.dtype], f"{label}: O max-abs {err} > {TOL[p.dtype]}"
     lerr = 0.0
     if lse is not None:
-        L = lse.detach().cpu().numpy().astype(np.float64)[rows_mask]
-        Lr = L_ref[rows_mask]
+        L = out_f64(lse, rows_mask)
+        Lr = Lr_all
         fin = np.isfinite(Lr)
         assert np.array_equal(fin, np.isfinite(L)), f"{label}: LSE -inf pattern differs"
         assert np.all(L[~fin] == -np.inf)
         if fin.any():
-            # relative error with a unit floor: a row whose only visible logit is ~0 has
-            # LSE ~0, where a pure relative error is undefined
-            lerr = float(np.max(np.abs(L[fin] - Lr[fin]) / np.maximum(np.abs(Lr[fin]), 1.0)))
-        assert lerr <= LSE_RTOL, f"{label}: LSE rel {lerr}"
+            d = np.abs(L[fin] - Lr[fin])
+            bound = LSE_RTOL * np.abs(Lr[fin]) + LSE_ATOL
+            assert np.all(d <= bound), f"{label}: LSE error {float(np.max(d - bound))} over the bar"
+            # reported: the relative error where it is defined (|LSE| above the floor)
+            big = np.abs(Lr[fin]) > LSE_ATOL / LSE_RTOL
+            lerr = float(np.max(d[big] / np.abs(Lr[fin][big]))) if big.any() else 0.0
     return err, lerr
 
 
@@ -204,3 +226,63 @@ def compact_oracle_inputs(p, units):
                   scale=p.scale, mask_mode=p.mask_mode, win_left=p.win_left,
                   win_right=p.win_right, q_scale=p.q_scale, k_scale=p.k_scale,
                   v_scale=p.v_scale)
+
+
+# ---------------------------------------------------------------------------
+# the oracle over many q-blocks: one q-block per task, on a pool of forked processes
+# ---------------------------------------------------------------------------
+
+_POOL_INPUTS = None  # set before the fork, so the workers share the inputs without a copy
+
+
+def _oracle_group(task):
+    """Rows ts of q-block gl of sequence b, every KV head: the oracle's own per-unit function
+    (sparse_attention is the same calls assembled into [T, N1, D] arrays)."""
+    from oracle.attention import attention_unit
+    b, gl, ts = task
+    inp = _POOL_INPUTS
+    O = np.empty((len(ts), inp.N1, inp.D))
+    L = np.empty((len(ts), inp.N1))
+    for n2 in range(inp.N2):
+        _, o, lse = attention_unit(inp, b, n2, gl, np.asarray(ts, dtype=np.int64))
+        heads = n2 * inp.G + np.arange(inp.G)
+        O[:, heads] = o
+        L[:, heads] = lse
+    return int(inp.cu[b]) + np.asarray(ts, dtype=np.int64), O, L
+
+
+def oracle_rows(inp: Inputs, rows, block_x: int, cu_seqlens_q, workers: int = 8):
+    """The oracle on the given global rows: (row indices ascending, O [n, N1, D], LSE [n, N1]).
+    Each q-block's rows are one task of a pool of forked processes; rows past a sequence's
+    active length are dropped, as sparse_attention drops them."""
+    global _POOL_INPUTS
+    groups = {}
+    for tg in sorted({int(t) for t in rows}):
+        b = int(np.searchsorted(cu_seqlens_q, tg, side="right") - 1)
+        t = tg - int(cu_seqlens_q[b])
+        if t < min(inp.sq(b), inp.storage(b)):
+            groups.setdefault((b, t // block_x), []).append(t)
+    tasks = [(b, gl, ts) for (b, gl), ts in sorted(groups.items())]
+    n = max(1, min(workers, len(tasks), os.cpu_count() or 1))
+    _POOL_INPUTS = inp
+    try:
+        if n == 1:
+            results = [_oracle_group(t) for t in tasks]
+        else:
+            with multiprocessing.get_context("fork").Pool(n) as pool:
+                results = pool.map(_oracle_group, tasks, chunksize=1)
+    finally:
+        _POOL_INPUTS = None
+    if not results:
+        return np.zeros(0, dtype=np.int64), np.zeros((0, inp.N1, inp.D)), np.zeros((0, inp.N1))
+    idx = np.concatenate([r[0] for r in results])
+    return idx, np.concatenate([r[1] for r in results]), np.concatenate([r[2] for r in results])
+
+
+def record_margin(label: str, **fields) -> None:
+    """Append one parity result (error margins against the bars) to the GPU run's output
+    folder when there is one, so that a run's margins can be read back from it."""
+    out = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out")
+    if os.path.isdir(out):
+        with open(os.path.join(out, "parity_margins.jsonl"), "a") as fh:
+            fh.write(json.dumps(dict(case=label, **fields)) + "\n")

@@ -93,6 +93,28 @@ def test_group_limit_and_quant_dtype_rules():
     assert _check(_good(kv_page_stride=128 * 2 * 128 + 100)) == 2
 
 
+def test_max_seqlen_bounds():
+    """max_seqlen_q / max_seqlen_kv (the metadata operator's keyword arguments): -1 or 0 mean
+    "not given"; a given bound must fit the query rows and the KV storage (3 pages of 128)."""
+    assert _check(_good(max_seqlen_q=-1, max_seqlen_kv=-1)) == 0
+    assert _check(_good(max_seqlen_q=0, max_seqlen_kv=0)) == 0
+    assert _check(_good(max_seqlen_q=384, max_seqlen_kv=384)) == 0
+    assert _check(_good(max_seqlen_q=640)) == 0
+    assert _check(_good(max_seqlen_q=641)) == 2  # longer than total_q
+    assert _check(_good(max_seqlen_kv=385)) == 2  # more than max_blocks_per_seq * 128 keys
+    assert _check(_good(max_seqlen_q=-2)) == 2
+    assert _check(_good(max_seqlen_kv=-5)) == 2
+    tnd = _good(kv_layout=_lib.KV_TND, max_blocks_per_seq=0, num_pages=1000)
+    assert _check(tnd) == 0
+    tnd.max_seqlen_kv = 1000
+    assert _check(tnd) == 0
+    tnd.max_seqlen_kv = 1001  # more than the T_kv rows
+    assert _check(tnd) == 2
+    p = _good()
+    p.reserved[0] = 1
+    assert _check(p) == 4
+
+
 def test_entry_points_validate_before_device_work():
     lib = _lib.load()
     bad = _good(head_dim=64)
@@ -214,9 +236,6 @@ def test_probe_library_exports_its_header():
     assert lib.gbsa_probe_gather(None, None, None, 0, 256, 2048, None, None) == -1
     assert lib.gbsa_probe_stream(ctypes.c_void_p(0x1000), 15, 1, ctypes.c_void_p(0x1000),
                                  None) == -1
-    assert lib.gbsa_probe_lds_read(0, 1, ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1000),
-                                   None) == -1
-    assert lib.gbsa_probe_lds_read(1, 1, None, ctypes.c_void_p(0x1000), None) == -1
 
 
 def test_validate_argument_checks():

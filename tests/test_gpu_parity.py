@@ -12,8 +12,8 @@ import pytest
 import torch
 
 import gbsa_inputs as gi
-from helpers import (GpuProblem, compact_oracle_inputs, compare, gpu_params, oracle_inputs,
-                     out_f64)
+from helpers import (TOL, GpuProblem, compact_oracle_inputs, compare, compare_rows,
+                     gpu_params, oracle_inputs, oracle_rows, out_f64, record_margin)
 from oracle import attention as oa
 from oracle import scheduler as sch
 
@@ -482,13 +482,15 @@ def test_workspace_reuse(kw):
         assert torch.equal(out, ref) and torch.equal(lse, lref), f"call {i}"
 
 
-def _validate(p, **over):
+def _validate(p, max_seqlen=(-1, -1), **over):
     from block_sparse_paged_gbsa_amd import gbsa_validate
     gp = GpuProblem(p)
     t = dict(cnt=gp.cnt, idx=gp.idx, cu=gp.cu, squ=gp.squ, skv=gp.skv, table=gp.table,
              cu_kv=gp.cu_kv, umask=gp.umask)
     t.update(over)
-    return gbsa_validate(gpu_params(p), t["idx"], t["cnt"], t["cu"], t["squ"],
+    params = gpu_params(p)
+    params.max_seqlen_q, params.max_seqlen_kv = max_seqlen
+    return gbsa_validate(params, t["idx"], t["cnt"], t["cu"], t["squ"],
                          cu_seqlens_kv=t["cu_kv"], seqused_kv=t["skv"], block_table=t["table"],
                          atten_mask=t["umask"])
 
@@ -524,6 +526,12 @@ def test_validate_reports_each_broken_rule():
     m = gi.with_atten_mask(p, 191, cols=10)
     assert _validate(m) == bit["mask_extent"]
     assert _validate(gi.with_atten_mask(p, 191)) == 0
+    # length bounds: exact bounds pass, one below the longest sequence is reported
+    lq = int(np.diff(p.cu_seqlens_q).max())
+    lkv = int(max(p.kv_len(b) for b in range(p.batch)))
+    assert _validate(p, max_seqlen=(lq, lkv)) == 0
+    assert _validate(p, max_seqlen=(lq - 1, lkv)) == bit["max_seqlen"]
+    assert _validate(p, max_seqlen=(lq, lkv - 1)) == bit["max_seqlen"]
 
 
 def test_metadata_mismatch_is_refused():
@@ -534,50 +542,98 @@ def test_metadata_mismatch_is_refused():
     other.mask_mode = 0  # metadata built for different attributes
     meta = gp.metadata(other)
     out = torch.full(p.q.shape, 3.0, dtype=gi.TORCH_DTYPES[p.out_dtype], device="cuda")
-    _, _, ws = gp.forward(good, meta, out)
+    lse = torch.zeros(p.q.shape[:2], dtype=torch.float32, device="cuda") if p.return_lse else None
+    _, _, ws = gp.forward(good, meta, out, lse)
     torch.cuda.synchronize()
     assert int(ws[:4].view(torch.int32)[0].item()) != 0
-    assert torch.all(out == 3.0)
+    # nothing computed: every output entry is NaN, whatever the buffer held
+    assert torch.isnan(out.float()).all()
+    if lse is not None:
+        assert torch.isnan(lse).all()
+
+
+def test_metadata_mismatch_keyword_path_gives_nan():
+    """The article-style keyword call returns no workspace, so a refused call must show in its
+    outputs: metadata built for causal attention, main call without a mask."""
+    from block_sparse_paged_gbsa_amd import (generic_block_sparse_attention,
+                                             generic_block_sparse_attention_metadata)
+    p = gi.random_problem(124, device="cuda", mask_mode=1)
+    gp = GpuProblem(p)
+    bs = [p.block_x, 128]
+    meta = generic_block_sparse_attention_metadata(
+        gp.idx, gp.cnt, p.num_heads_q, p.num_heads_kv, 128, bs, cu_seqlens_q=gp.cu,
+        seqused_q=gp.squ, seqused_kv=gp.skv, mask_mode=1)
+    kw = dict(metadata=meta, cu_seqlens_q=gp.cu, seqused_q=gp.squ, seqused_kv=gp.skv,
+              block_table=gp.table, softmax_scale=p.scale, return_softmax_lse=True)
+    out, lse = generic_block_sparse_attention(p.q, p.k, p.v, gp.idx, gp.cnt, bs, mask_mode=1,
+                                              **kw)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out.float()).any()
+    out, lse = generic_block_sparse_attention(p.q, p.k, p.v, gp.idx, gp.cnt, bs, mask_mode=0,
+                                              **kw)
+    torch.cuda.synchronize()
+    assert torch.isnan(out.float()).all() and torch.isnan(lse).all()
 
 
 # ---------------------------------------------------------------------------
 # full-size workloads, sampled rows, benchmark launch configuration
 # ---------------------------------------------------------------------------
 
+def _sampled_rows(p, units, rows_per_unit, rng):
+    """Global rows of the given (b, q-block) units: every active row, or rows_per_unit of
+    them always including the q-block's first and last active rows."""
+    rows = []
+    for (b, gl) in units:
+        storage = int(p.cu_seqlens_q[b + 1] - p.cu_seqlens_q[b])
+        sq = storage if p.seqused_q is None else min(int(p.seqused_q[b]), storage)
+        lo, hi = gl * p.block_x, min((gl + 1) * p.block_x, sq)
+        assert lo < hi, f"q-block {gl} of sequence {b} has no active row"
+        ts = np.arange(lo, hi)
+        if rows_per_unit is not None and len(ts) > rows_per_unit:
+            ts = np.unique(np.concatenate([[lo, hi - 1], rng.choice(ts[1:-1], rows_per_unit - 2,
+                                                                    replace=False)]))
+        rows += list(int(p.cu_seqlens_q[b]) + ts)
+    return rows
+
+
 def _sampled_check(cfg, units, rows_per_unit=None, seed=0, tnd=False, problem=None):
-    _log(f"[parity] workload {cfg}{' TND' if tnd else ''}: generating on the GPU")
+    """A full-size workload in the benchmark's launch configuration, checked against the
+    oracle on the rows of the given q-blocks (all KV heads, so every query head), plus an
+    all-finite check of every active row. Records the error margins."""
+    label = f"workload{cfg}{'_tnd' if tnd else ''}" if problem is None else problem.name
+    _log(f"[parity] {label}: generating on the GPU")
     p = gi.config(cfg, device="cuda") if problem is None else problem
     if tnd:
         p = gi.to_tnd(p)
     gp = GpuProblem(p)
     params, meta, out, lse, ws = gp.run(0)
     assert int(ws[:4].view(torch.int32)[0].item()) == 0
-    _log(f"[parity] workload {cfg}: gpu done, oracle on {len(units)} sampled q-blocks")
-    inp = compact_oracle_inputs(p, units)
-    rng = np.random.default_rng(seed)
-    rows = []
-    for (b, gl) in units:
-        lo = gl * p.block_x
-        hi = min((gl + 1) * p.block_x, inp.sq(b), inp.storage(b))
-        ts = np.arange(lo, hi)
-        if rows_per_unit is not None and len(ts) > rows_per_unit:
-            ts = np.unique(np.concatenate([[lo, hi - 1], rng.choice(ts, rows_per_unit - 2,
-                                                                    replace=False)]))
-        rows += list(int(p.cu_seqlens_q[b]) + ts)
-    O, L, done = oa.sparse_attention(inp, rows=rows)
-    err, lerr = compare(p, out, lse if p.return_lse else None, O, L, done, f"workload{cfg}")
-    _log(f"workload{cfg}: rows {int(done.sum())} O max-abs {err:.3e} LSE rel {lerr:.3e}")
-    # every active row must be finite
-    o = out_f64(out)
+    # every active row finite (checked on the device, rows past seqused_q are never written)
     for b in range(p.batch):
         c0 = int(p.cu_seqlens_q[b])
-        sq = inp.sq(b)
-        assert np.isfinite(o[c0:c0 + sq]).all()
+        storage = int(p.cu_seqlens_q[b + 1]) - c0
+        sq = storage if p.seqused_q is None else min(int(p.seqused_q[b]), storage)
+        assert bool(torch.isfinite(out[c0:c0 + sq].float()).all()), f"{label}: sequence {b}"
+    _log(f"[parity] {label}: gpu done, oracle on {len(units)} q-blocks")
+    inp = compact_oracle_inputs(p, units)
+    rows = _sampled_rows(p, units, rows_per_unit, np.random.default_rng(seed))
+    idx, O, L = oracle_rows(inp, rows, p.block_x, p.cu_seqlens_q)
+    assert len(idx) == len(set(rows)), "a sampled row is not active"
+    err, lerr = compare_rows(p, out, lse if p.return_lse else None, idx, O, L, label)
+    _log(f"[parity] {label}: {len(idx)} rows x {p.num_heads_q} heads, O max-abs "
+         f"{err:.3e} (bar {TOL[p.dtype]:.1e}), LSE rel {lerr:.3e}")
+    record_margin(label, rows=len(idx), heads=p.num_heads_q, q_blocks=len(units),
+                  o_max_abs=err, o_bar=TOL[p.dtype], lse_rel=lerr if p.return_lse else None)
     return p, out
 
 
+def _qblocks(n_active, extra=()):
+    """First, second, middle, second-to-last and last q-block, plus the given ones."""
+    return sorted({0, 1, n_active // 2, n_active - 2, n_active - 1, *extra})
+
+
 def test_workload2_decode_sampled():
-    _sampled_check(2, [(b, 0) for b in range(0, 64, 3)])
+    _sampled_check(2, [(b, 0) for b in range(64)])
 
 
 @pytest.mark.parametrize("batch,top_k", [(8, 16), (1, 256)], ids=["b8_top16", "b1_top256"])
@@ -589,8 +645,10 @@ def test_split_kv_decode_sampled(batch, top_k):
 
 
 def test_workload3_block_sparse_prefill_sampled():
-    units = [(0, 0), (0, 1), (0, 63), (0, 64), (1, 65), (2, 200), (3, 255)]
-    _sampled_check(3, units, rows_per_unit=12)
+    """Every sequence: first, middle and last q-blocks, and both sides of q-block 64 where
+    the selection stops being every causal block (sink + 8 recent + random after it)."""
+    units = [(b, gl) for b in range(4) for gl in _qblocks(256, (63, 64, 65))]
+    _sampled_check(3, units, rows_per_unit=32)
 
 
 @pytest.mark.parametrize("block_x", [8, 4], ids=["x8", "x4"])
@@ -606,27 +664,33 @@ def test_small_qblock_prefill_sampled(block_x):
 
 
 def test_workload4_long_context_sampled():
-    # first blocks, the window edge (rows 32256.. start dropping the sinks), the partial
-    # last KV block (seqused 120000), the last active q-block
-    units = [(0, 0), (0, 3), (0, 503), (0, 504), (0, 505), (0, 1000), (0, 1873), (0, 1874)]
-    _sampled_check(4, units, rows_per_unit=10)
+    """First q-blocks (the sinks are the whole selection), both sides of the window edge
+    (from row 32256 the sink blocks leave the window while still selected), a middle
+    q-block, the q-blocks whose diagonal is the partial last KV block (seqused_kv = 120000,
+    block 937 holds 64 keys) and the last active q-block (rows 119936..119999)."""
+    units = [(0, gl) for gl in (0, 1, 2, 3, 503, 504, 505, 937, 1872, 1873, 1874)]
+    _sampled_check(4, units, rows_per_unit=32)
 
 
 def test_workload5_dense_equivalent_fp8_sampled():
-    units = [(0, 0), (0, 1), (0, 100), (1, 255), (1, 128)]
-    _sampled_check(5, units, rows_per_unit=10)
+    """Both sequences: first, middle and last q-blocks and a few in between (every causal
+    block selected: the result must be dense causal attention)."""
+    units = [(b, gl) for b in range(2) for gl in _qblocks(256, (100, 128))]
+    _sampled_check(5, units, rows_per_unit=32)
 
 
 def test_workload2_decode_tnd_sampled():
-    _sampled_check(2, [(b, 0) for b in range(0, 64, 9)], tnd=True)
+    _sampled_check(2, [(b, 0) for b in range(64)], tnd=True)
 
 
 def test_workload3_block_sparse_prefill_tnd_sampled():
-    _sampled_check(3, [(0, 0), (1, 64), (3, 255)], rows_per_unit=12, tnd=True)
+    units = [(b, gl) for b in range(4) for gl in (0, 64, 255)]
+    _sampled_check(3, units, rows_per_unit=32, tnd=True)
 
 
 def test_workload5_dense_equivalent_fp8_tnd_sampled():
-    _sampled_check(5, [(0, 1), (1, 255)], rows_per_unit=10, tnd=True)
+    units = [(b, gl) for b in range(2) for gl in (0, 1, 128, 255)]
+    _sampled_check(5, units, rows_per_unit=32, tnd=True)
 
 
 GRAPH_CASES = [

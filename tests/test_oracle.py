@@ -502,3 +502,16 @@ def test_slot_order_changes_only_rounding():
             idx[h, g, :c] = idx[h, g, :c][::-1]
     O2, L2, _ = oa.sparse_attention(oracle_inputs(_set(p, sparse_block_idx=idx)))
     np.testing.assert_allclose(O[done], O2[done], atol=1e-13)
+
+
+def test_pooled_oracle_equals_one_call():
+    """The tests' process-pool evaluation of many q-blocks (one q-block per task) gives the
+    oracle's own single-call result bit for bit: q-blocks are independent units."""
+    from helpers import oracle_rows
+    p = gi.random_problem(77, batch=3, max_len=200, block_x=16, mask_mode=1)
+    inp = oracle_inputs(p)
+    rows = [t for t in range(int(p.cu_seqlens_q[-1])) if t % 3 != 1]
+    O1, L1, d1 = oa.sparse_attention(inp, rows=rows)
+    idx, O2, L2 = oracle_rows(inp, rows, p.block_x, p.cu_seqlens_q, workers=4)
+    assert np.array_equal(np.nonzero(d1)[0], idx) and len(idx) > 0
+    assert np.array_equal(O1[d1], O2) and np.array_equal(L1[d1], L2)

@@ -293,6 +293,45 @@ def gbsa_forward_ex(params: GbsaParams, q, k, v, sparse_block_idx, sparse_block_
     return out, lse, workspace
 
 
+def gbsa_forward_ex_noalloc(params: GbsaParams, q, k, v, sparse_block_idx, sparse_block_count,
+                            metadata, cu_seqlens_q, seqused_q=None, *, cu_seqlens_kv=None,
+                            seqused_kv=None, block_table=None, q_scale=None, k_scale=None,
+                            v_scale=None, p_scale=None, atten_mask=None, out, lse=None,
+                            stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """gbsa_forward_ex without a workspace: the library's fixed device array holds the split
+    partial results. The caller passes the outputs (out, and lse when params.return_lse);
+    nothing is allocated here or in the library. Returns (attention_out, softmax_lse)."""
+    _need(q, "query")
+    _need(sparse_block_idx, "sparse_block_idx", torch.int32)
+    _need(sparse_block_count, "sparse_block_count", torch.int32)
+    _need(out, "out")
+    g = _lib.GbsaForwardArgs()
+    g.query, g.key, g.value = q.data_ptr(), k.data_ptr(), v.data_ptr()
+    ptr = lambda t: None if t is None else t.data_ptr()
+    g.sparse_block_idx = ptr(sparse_block_idx)
+    g.sparse_block_count = ptr(sparse_block_count)
+    g.metadata = ptr(metadata)
+    g.cu_seqlens_q = ptr(cu_seqlens_q)
+    g.seqused_q = ptr(seqused_q)
+    g.cu_seqlens_kv = ptr(cu_seqlens_kv)
+    g.seqused_kv = ptr(seqused_kv)
+    g.block_table = ptr(block_table)
+    g.q_scale, g.k_scale, g.v_scale, g.p_scale = (ptr(q_scale), ptr(k_scale), ptr(v_scale),
+                                                  ptr(p_scale))
+    if atten_mask is not None:
+        _need(atten_mask, "atten_mask", contiguous=False)
+        m = atten_mask.view(torch.uint8) if atten_mask.dtype == torch.bool else atten_mask
+        bs, rs, rows, cols = _mask_geometry(m)
+        g.atten_mask = m.data_ptr()
+        g.mask_batch_stride, g.mask_row_stride, g.mask_rows, g.mask_cols = bs, rs, rows, cols
+    g.attention_out = out.data_ptr()
+    g.softmax_lse = ptr(lse)
+    check("gbsa_forward_ex_noalloc",
+          _lib.load().gbsa_forward_ex_noalloc(ctypes.byref(params), ctypes.byref(g),
+                                              _stream(stream)))
+    return out, lse
+
+
 def workspace_status(workspace: torch.Tensor) -> int:
     """Word 0 of the workspace: non-zero after a metadata/parameter mismatch (sticky)."""
     return int(workspace[:4].view(torch.int32)[0].item())

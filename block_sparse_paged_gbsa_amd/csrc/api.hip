@@ -208,8 +208,65 @@ gbsa_status gbsa_metadata(const gbsa_params* p, const int32_t* sparse_block_coun
     return launch_metadata(a, stream) == hipSuccess ? GBSA_OK : GBSA_ERR_HIP;
 }
 
+// ---------------------------------------------------------------------------------------
+// Allocation-free variant: the workspace is a fixed device array of the library. Its layout
+// does not depend on the call (the arrival counters have a region of their own), so a call
+// never finds another call's partial results where it expects zeroed counters.
+// ---------------------------------------------------------------------------------------
+constexpr size_t kScratchBytes = (size_t)GBSA_NOALLOC_SCRATCH_BYTES;
+constexpr int64_t kScratchCounters = GBSA_NOALLOC_MAX_COUNTERS;
+constexpr size_t kScratchCounterBytes = sizeof(int32_t) * (size_t)kScratchCounters;
+
+static __device__ __align__(256) unsigned char scratch[GBSA_NOALLOC_SCRATCH_BYTES];
+
+// scratch: [status word][arrival counters, fixed region][partial O][running max][running sum]
+static WsLayout scratch_layout(int64_t P, int64_t M) {
+    WsLayout w;
+    w.status = 0;
+    w.arrive = 256;
+    w.o = align_up(w.arrive + kScratchCounterBytes, 256);
+    w.m = align_up(w.o + sizeof(float) * 2 * P * M * 128, 256);
+    w.l = align_up(w.m + sizeof(float) * 2 * P * M, 256);
+    w.total = align_up(w.l + sizeof(float) * 2 * P * M, 256);
+    return w;
+}
+
+namespace {
+// Zeroes `n` words (the status word and the counter region) once per device.
+__global__ void clear_words_kernel(int32_t* p, int n) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
+        p[i] = 0;
+}
+
+std::mutex g_scratch_mu;
+unsigned char* g_scratch[kMaxDevices] = {nullptr};
+}  // namespace
+
+// Device address of this device's copy of `scratch`, looked up once per device with that
+// device current (the array's name is a host-side stand-in, not a device address). The first
+// call on a device also clears the status word and the counter region on `stream`, with a
+// kernel (capturable) rather than a memset.
+static gbsa_status scratch_base(hipStream_t stream, unsigned char** base) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GBSA_ERR_HIP;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch[dev] == nullptr) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+            return GBSA_ERR_HIP;
+        const int words = (int)((256 + kScratchCounterBytes) / sizeof(int32_t));
+        hipLaunchKernelGGL(clear_words_kernel, dim3(64), dim3(256), 0, stream, (int32_t*)ptr,
+                           words);
+        if (hipGetLastError() != hipSuccess) return GBSA_ERR_HIP;
+        g_scratch[dev] = (unsigned char*)ptr;
+    }
+    *base = g_scratch[dev];
+    return GBSA_OK;
+}
+
+// fixed_ws: false = the caller's workspace (args->workspace), true = the array `scratch`.
 static gbsa_status forward_impl(const gbsa_params* p, const gbsa_forward_args* g,
-                                hipStream_t stream) {
+                                hipStream_t stream, const bool fixed_ws = false) {
     const void* query = g->query;
     const void* key = g->key;
     const void* value = g->value;
@@ -257,8 +314,20 @@ static gbsa_status forward_impl(const gbsa_params* p, const gbsa_forward_args* g
     st = plan_workers(p, &P);
     if (st != GBSA_OK) return st;
     const int64_t M = rows_per_unit(p);
-    const WsLayout L = ws_layout(P, M, subtiles(M));
-    if (workspace == nullptr || workspace_bytes < L.total) return GBSA_ERR_WORKSPACE;
+    WsLayout L;
+    unsigned char* ws = (unsigned char*)workspace;
+    if (fixed_ws) {
+        // the caller brings no workspace; the shapes must fit the fixed array
+        if (workspace != nullptr || workspace_bytes != 0) return GBSA_ERR_WORKSPACE;
+        L = scratch_layout(P, M);
+        if ((int64_t)P * subtiles(M) > kScratchCounters || L.total > kScratchBytes)
+            return GBSA_ERR_WORKSPACE;
+        st = scratch_base(stream, &ws);
+        if (st != GBSA_OK) return st;
+    } else {
+        L = ws_layout(P, M, subtiles(M));
+        if (workspace == nullptr || workspace_bytes < L.total) return GBSA_ERR_WORKSPACE;
+    }
 
     FwdArgs a;
     memset(&a, 0, sizeof(a));
@@ -285,7 +354,6 @@ static gbsa_status forward_impl(const gbsa_params* p, const gbsa_forward_args* g
         a.um_cols = g->mask_cols;
     }
     a.lse = softmax_lse;
-    unsigned char* ws = (unsigned char*)workspace;
     a.ws_status = (int32_t*)(ws + L.status);
     a.ws_arrive = (int32_t*)(ws + L.arrive);
     a.ws_o = (float*)(ws + L.o);
@@ -408,6 +476,17 @@ gbsa_status gbsa_forward_ex(const gbsa_params* p, const gbsa_forward_args* args,
                                     : args->cu_seqlens_kv != nullptr)
         return GBSA_ERR_NULL;
     return forward_impl(p, args, stream);
+}
+
+gbsa_status gbsa_forward_ex_noalloc(const gbsa_params* p, const gbsa_forward_args* args,
+                                    hipStream_t stream) {
+    gbsa_status st = gbsa_check_params(p);
+    if (st != GBSA_OK) return st;
+    if (args == nullptr) return GBSA_ERR_NULL;
+    if (p->kv_layout == GBSA_KV_TND ? args->block_table != nullptr
+                                    : args->cu_seqlens_kv != nullptr)
+        return GBSA_ERR_NULL;
+    return forward_impl(p, args, stream, true);
 }
 
 gbsa_status gbsa_validate(const gbsa_params* p, const gbsa_forward_args* g,

@@ -318,6 +318,33 @@ gbsa_status gbsa_forward_ex(const gbsa_params* params, const gbsa_forward_args* 
                             hipStream_t stream);
 
 /*
+ * gbsa_forward_ex for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation. The call allocates nothing
+ * and needs no workspace: the split-KV partial results, the arrival counters and the status
+ * word live in a fixed device array of the library (one per GPU, held until the process
+ * ends) of GBSA_NOALLOC_SCRATCH_BYTES bytes. args->workspace must be NULL and
+ * args->workspace_bytes 0; every other argument is that of gbsa_forward_ex, and the result
+ * is the same, bit for bit.
+ * Limits: the workspace gbsa_workspace_size would report for these params (partial results
+ * of 2 x workers x rows per unit, rows per unit = block_x * N1 / N2) must fit the array, and
+ * workers x row subtiles (ceil(rows per unit / 256) above 16 rows, else 1) must not exceed
+ * GBSA_NOALLOC_MAX_COUNTERS; otherwise GBSA_ERR_WORKSPACE is returned and nothing is
+ * enqueued. Choose num_workers to fit (the decode shapes fit with the default count).
+ * Sharing: all calls on one GPU use the same array. Calls that overlap on one GPU (on
+ * different streams, or from several host threads without ordering) race and give undefined
+ * results; calls ordered on one stream are safe. Every call leaves the arrival counters at
+ * zero for the next; the first call on a GPU also clears them (and the status word) with a
+ * small kernel on its stream. A refused call (metadata mismatch) fills attention_out and
+ * softmax_lse with NaN, as gbsa_forward does; its status word is not readable by the caller.
+ * Errors: those of gbsa_forward_ex; GBSA_ERR_WORKSPACE as above; GBSA_ERR_HIP if the array's
+ * device address cannot be obtained.
+ */
+#define GBSA_NOALLOC_SCRATCH_BYTES (32u << 20)
+#define GBSA_NOALLOC_MAX_COUNTERS 16384
+gbsa_status gbsa_forward_ex_noalloc(const gbsa_params* params, const gbsa_forward_args* args,
+                                    hipStream_t stream);
+
+/*
  * Opt-in check of the tensor VALUES that the forward calls take on trust (the article's
  * "general constraints": tiling reads no tensor values, so the caller guarantees them). Runs
  * one small kernel over the same argument block as gbsa_forward_ex and ORs into *violations

@@ -238,6 +238,20 @@ def test_probe_library_exports_its_header():
                                  None) == -1
 
 
+def test_noalloc_forward_argument_checks():
+    """gbsa_forward_ex_noalloc takes no workspace and refuses shapes whose partial results do
+    not fit its fixed array, before touching a device."""
+    lib = _lib.load()
+    fx = lambda p, g: lib.gbsa_forward_ex_noalloc(ctypes.byref(p), ctypes.byref(g), None)
+    assert lib.gbsa_forward_ex_noalloc(ctypes.byref(_good()), None, None) == 1
+    assert fx(_good(head_dim=64), _args()) == 2  # parameter errors first
+    assert fx(_good(), _args()) == 6  # a workspace is given
+    # 999 workers x 256 rows per unit: 2 * 999 * 256 rows of 128 floats > 32 MiB
+    big = _good(num_workers=999)
+    assert fx(big, _args(workspace=None, workspace_bytes=0)) == 6
+    assert _lib.NOALLOC_SCRATCH_BYTES == 32 << 20
+
+
 def test_validate_argument_checks():
     """gbsa_validate refuses missing or inconsistent pointers before any device work."""
     lib = _lib.load()

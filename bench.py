@@ -37,6 +37,7 @@ KERNEL_SOURCES = {
     "fwd_decode_kernel": ["fwd_decode.hip"],
     "fwd_prefill_kernel": ["fwd_prefill.hip"],
     "fwd_prefill_pp32_kernel": ["fwd_prefill.hip"],
+    "fwd_prefill_pp32d_kernel": ["fwd_prefill.hip"],
     "fwd_prefill_ks32_kernel": ["fwd_prefill.hip"],
 }
 SHARED_SOURCES = ["device_common.hpp", "gbsa_internal.hpp", "split_merge.hpp"]
@@ -377,7 +378,8 @@ class Workload:
         self.P = gbsa_num_workers(self.params)
         rows = p.block_x * p.num_heads_q // p.num_heads_kv  # packed GQA rows per unit
         self.kernel = ("fwd_decode_kernel" if rows <= 16 else
-                       "fwd_prefill_pp32_kernel" if rows > 256 else
+                       ("fwd_prefill_pp32_kernel" if p.dtype == "fp8" else
+                        "fwd_prefill_pp32d_kernel") if rows > 256 else
                        "fwd_prefill_ks32_kernel" if rows > 64 else "fwd_prefill_kernel")
 
     def metadata(self):
@@ -502,6 +504,9 @@ def main(argv=None):
                     help="seconds of oracle wall time for the CPU baseline (0 = skip)")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip timing the other workloads (the `configs` object)")
+    ap.add_argument("--forward-only", type=int, default=0, metavar="N",
+                    help="only run the metadata and N forward launches of the workload back to "
+                         "back (for counter and kernel-trace profiles) and print their count")
     ap.add_argument("--cold-only", action="store_true",
                     help="only run cache-flushed forward launches of the workload (for a "
                          "kernel-trace profile of them) and print their count")
@@ -563,6 +568,15 @@ def main(argv=None):
     stream = torch.cuda.current_stream()
     hbm_bound = w.kernel == "fwd_decode_kernel"
 
+    if a.forward_only > 0:
+        w.step()
+        for _ in range(a.forward_only):
+            w.forward()
+        torch.cuda.synchronize()
+        assert w.status() == 0, "metadata mismatch flagged by the kernels"
+        print(json.dumps({"forward_launches": a.forward_only + 1, "kernel": w.kernel,
+                          "workload": p.name}), flush=True)
+        return 0
     if a.cold_only:
         flush = cache_flusher(dev)
         w.step()

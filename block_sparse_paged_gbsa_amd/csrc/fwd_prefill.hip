@@ -10,13 +10,16 @@
 // that the MFMA result is already P^T in the B-operand layout of O^T = V^T P^T, and V^T is read
 // with the gfx950 transpose read. Split units are merged in kernel by the last arriving
 // workgroup (split_merge.hpp). Three kernels by unit size:
-//  * fwd_prefill_pp32_kernel (more than 256 rows, 256-row subtiles) and
-//    fwd_prefill_ks32_kernel (65-256 rows, 128-row subtiles): two wave groups alternate MFMA and
-//    softmax items on the same SIMDs over half pages (schedules described with each), on 32x32
-//    MFMA tiles;
+//  * fwd_prefill_pp32d_kernel (more than 256 rows, 16-bit key/value), fwd_prefill_pp32_kernel
+//    (more than 256 rows, fp8), both on 256-row subtiles, and fwd_prefill_ks32_kernel (65-256
+//    rows, 128-row subtiles): two wave groups alternate MFMA and softmax items on the same SIMDs
+//    over half pages (schedules described with each), on 32x32 MFMA tiles; pp32d moves K and V
+//    into LDS by DMA, the others through registers;
 //  * fwd_prefill_kernel (17-64 rows): all waves in phase, 16 rows each, whole pages through a
 //    double-buffered LDS stage with one barrier per page, each page's keys split over 2
 //    (33-64 rows) or 4 (17-32 rows) wave groups that hold the same rows, 16x16 MFMA tiles.
+#include <stdint.h>
+
 #include "split_merge.hpp"
 
 namespace gbsa {
@@ -1040,6 +1043,282 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32_kernel(FwdArgs a) {
 
 
 // ---------------------------------------------------------------------------------------------
+// The 256-row ping-pong kernel with K/V moved by LDS DMA (16-bit key/value): the moved half
+// pages go from memory straight into LDS (buffer loads with the LDS destination), so the
+// softmax wave neither stages them in registers nor spends its item storing them.
+//
+// LDS layout of a half page (64 rows of 256 B) written by 16 DMA instructions of 1 KB: DMA
+// instruction i (0..15) holds logical rows i, i + 16, i + 32, i + 48 in four 256-byte slots at
+// byte i * 1088 + 256 * (row / 16), and inside a slot physical 16-byte chunk p holds logical
+// chunk p ^ (i >> 2). Rows four apart sit 64 bytes apart in bank position (the eight rows of a
+// transposing V read cover every bank), and sixteen consecutive rows map one logical chunk to
+// sixteen distinct bank groups (the K fragment reads); both read patterns are conflict-free.
+// Four buffers per operand (power-of-two indexing keeps the fragment addresses cheap): the DMA
+// of a half page is issued at least two slots before its first reader, into a buffer whose last
+// reader finished two slots earlier, and every wave lets only its newest DMA batch stay in
+// flight across a barrier.
+// ---------------------------------------------------------------------------------------------
+constexpr int kDmaStride = 1088;             // bytes between the DMA instructions of a half page
+constexpr int kDmaHalf = 16 * kDmaStride;    // one half page
+
+// DMA instructions [i0, i0 + n) of half page `src` into the half-page buffer `dst`.
+__device__ __forceinline__ void dma_half16(const KvSrc& src, int rs, unsigned char* dst, int i0,
+                                           int n, int lane) {
+    const rsrc_t r = make_rsrc(src.p, src.records);
+#pragma unroll
+    for (int x = 0; x < n; ++x) {
+        const int i = i0 + x;
+        const int row = i + 16 * (lane >> 4);
+        const int voff = row * rs + 16 * ((lane & 15) ^ (i >> 2));
+        const uint32_t m0 = (uint32_t)(uintptr_t)(GBSA_LDS unsigned char*)(dst + i * kDmaStride);
+        // no destination register: the data goes to LDS; completion is awaited with vmcnt
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                     :
+                     : "s"(m0), "v"(voff), "s"(r)
+                     : "memory", "m0");
+    }
+}
+// Waits until at most n of this wave's vector-memory loads are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// MFMA item of the 256-row kernel on the DMA layout (as mfma_item32, 16-bit types).
+template <int DT, bool qk, bool pv>
+__device__ __forceinline__ void mfma_item32d(const unsigned char* ks, const unsigned char* vs,
+                                             const QCol32& qc, f32x16 (&s)[2],
+                                             const u32x4 (&p)[4], f32x16 (&o)[4], int lane) {
+    constexpr int QS = qk ? 8 : 0;
+    constexpr int VS = pv ? 8 : 0;
+    constexpr int PC = QS + VS, NS = 2 * PC, D = kPipeDepth;
+    const int h2 = lane >> 5, m = (lane & 15) >> 2, g = (lane >> 4) & 1, cc = lane & 3;
+    // K: row t * 32 + (lane & 31) -> instruction lane & 15, slot 2 t + g; chunk 2 j + h2
+    const unsigned char* kl = ks + (lane & 15) * kDmaStride + g * 256;
+    const unsigned char* ka0 = kl + 16 * (h2 ^ m);        // even j
+    const unsigned char* ka1 = kl + 16 * ((2 + h2) ^ m);  // odd j
+    // V^T: rows 4 h + (lane & 15) / 4 (+ 8), chunk 2 g + cc / 2, 8-byte half cc & 1
+    const int i0 = 4 * h2 + m;
+    const unsigned char* vb0 = vs + i0 * kDmaStride + 16 * ((2 * g + (cc >> 1)) ^ h2) + 8 * (cc & 1);
+    const unsigned char* vb1 =
+        vs + (i0 + 8) * kDmaStride + 16 * ((2 * g + (cc >> 1)) ^ (h2 + 2)) + 8 * (cc & 1);
+    const f32x16 zero = {};
+    auto load = [&](int st) {
+        Frag f;
+        const int t = st / PC, j = st % PC;
+        if (j < QS) {
+            f.a = *(const u32x4*)(((j & 1) ? ka1 : ka0) + t * 512 + 64 * (j >> 1));
+        } else {
+            const int v = j - QS, a2 = v >> 2, dt = v & 3;
+            const int o2 = (2 * t + a2) * 256 + dt * 64;
+            const u32x2 v0 = lds_read_tr16(vb0 + o2);
+            const u32x2 v1 = lds_read_tr16(vb1 + o2);
+            f.a = (u32x4){v0[0], v0[1], v1[0], v1[1]};
+        }
+        return f;
+    };
+    auto compute = [&](int st, const Frag& f) {
+        const int t = st / PC, j = st % PC;
+        if (j < QS) {
+            s[t] = mfma_32x32x16<DT>(f.a, qc.q[j], j == 0 ? zero : s[t]);
+        } else {
+            const int v = j - QS, a2 = v >> 2, dt = v & 3;
+            o[dt] = mfma_32x32x16<DT>(f.a, p[2 * t + a2], o[dt]);
+        }
+    };
+    Frag fr[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i)
+        if (i < NS) fr[i] = load(i);
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+        const Frag f = fr[st % D];
+        if (st + D < NS) fr[st % D] = load(st + D);
+        compute(st, f);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+template <int DT, int OUT, int LAYOUT, bool UM>
+__global__ __launch_bounds__(512, 1) void fwd_prefill_pp32d_kernel(FwdArgs a) {
+    static_assert(DT != kFP8, "the DMA layout holds 16-bit rows");
+    constexpr int R = 256;
+    constexpr int esz = 2;
+    // [K buffers 0..3][V buffers 0..3], one half page each
+    __shared__ __attribute__((aligned(16))) unsigned char smem[8 * kDmaHalf];
+    __shared__ int4 plist[256];
+    __shared__ int flag[1];
+    static_assert(sizeof(smem) >= kPieceListBytes, "the split merge borrows the stages");
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2;
+    const int gw = wave & 3;  // wave within its group
+    const int lin = xcd_remap(blockIdx.x, gridDim.x);
+    const int w = lin / a.nst, st = lin - (lin / a.nst) * a.nst;
+
+    if (!header_ok(a)) {
+        refuse(a);
+        return;
+    }
+    const Bound b0 = read_bound(a.meta, w), b1 = read_bound(a.meta, w + 1);
+    const int U = a.meta[3];
+    if (!bound_less(b0, b1) || b0.u >= U) return;
+    UnitIter it = locate_unit(a, b0.u);
+    if (it.b < 0) return;
+
+    const int rs = a.N2 * 128 * esz;
+    const unsigned char* kbase = (const unsigned char*)a.k;
+    const unsigned char* vbase = (const unsigned char*)a.v;
+    unsigned char* const kst = smem;
+    unsigned char* const vst = smem + 4 * kDmaHalf;
+
+    for (int u = b0.u;; ++u) {
+        const int sa = (u == b0.u) ? b0.s : 0;
+        if (u >= U || u > b1.u || (u == b1.u && sa >= b1.s)) break;
+        const int g = it.qbase + it.gl;
+        int cnt = 0;
+        if (g < a.tqb) cnt = min(max(a.cnt[(int64_t)it.n2 * a.tqb + g], 0), a.topK);
+        const int se = (u == b1.u) ? b1.s : cnt;
+        const bool complete = (sa == 0) && (se == cnt);
+
+        const int t0 = it.gl * a.X;
+        const int rows_exist = min(a.X, it.storage - t0) * a.G;
+        const int row_base = st * R;
+        if (row_base < rows_exist) {
+            const KvSeq kv = kv_seq<LAYOUT>(a, it.b);
+            const int skv = kv.len;
+            const int off = diag_off(a, skv, it.sq);
+            const int row0 = row_base + wave * 32;
+            QCol32 qc;
+            float colscale, mrun = kNegInf, lrun = 0.f;
+            int trow;
+            bool rvalid;
+            load_q32<DT>(a, it, t0, rows_exist, row0, lane, qc, colscale, trow, rvalid);
+            const UMaskRow um =
+                UM ? umask_row(a, it.b, trow, rvalid) : UMaskRow{make_rsrc(nullptr, 0), -1};
+            f32x16 o[4];
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) o[dt] = (f32x16){};
+            const int t_lo = t0 + row_base / a.G;
+            const int t_hi = t0 + (min(row_base + R, rows_exist) - 1) / a.G;
+            const int32_t* sel = a.idx + ((int64_t)it.n2 * a.tqb + g) * a.topK;
+            const int64_t head_off = (int64_t)it.n2 * 128 * esz;
+
+            if (wave == 0) {
+                int n = 0;
+                for (int c0 = sa; c0 < se; c0 += 64) {
+                    int jl = -1, pl = 0, cl = 0;
+                    if (c0 + lane < se) {
+                        jl = sel[c0 + lane];
+                        if (jl >= 0) {
+                            cl = block_class(a, (int64_t)jl * 128, skv, off, t_lo, t_hi);
+                            if (cl != 0) pl = kv.unit<LAYOUT>(jl);
+                        }
+                    }
+                    const uint64_t mm = __ballot(cl != 0);
+                    if (cl != 0) {
+                        const int pos = n + __builtin_amdgcn_mbcnt_hi(
+                                                (uint32_t)(mm >> 32),
+                                                __builtin_amdgcn_mbcnt_lo((uint32_t)mm, 0));
+                        plist[pos] = make_int4(pl, jl * 4 + cl,
+                                               kv_records(rs, skv - 128 * jl),
+                                               kv_records(rs, skv - 128 * jl - 64));
+                    }
+                    n += __builtin_popcountll(mm);
+                }
+                if (lane == 0) flag[0] = n;
+            }
+            __syncthreads();
+            const int nh = 2 * __builtin_amdgcn_readfirstlane(flag[0]);  // half pages
+
+            // half page q (clamped into the stream) of K or V of this head
+            auto half_src = [&](const unsigned char* base, int q) {
+                q = min(q, nh - 1);
+                const int4 e = plist[q >> 1];
+                const int unit = __builtin_amdgcn_readfirstlane(e.x);
+                const int rec = __builtin_amdgcn_readfirstlane((q & 1) ? e.w : e.z);
+                return KvSrc{base + (int64_t)unit * a.kv_stride * esz + head_off +
+                                 (q & 1) * 64 * rs,
+                             rec};
+            };
+            if (nh > 0) {
+                f32x16 s[2];
+                u32x4 p[4];
+                // Readers: MFMA item k reads K_k (K buffer k % 4) and V_{k-1} (V buffer
+                // (k - 1) % 4). Writers: group 0's softmax item k - 1 moves V_k, group 1's
+                // moves K_{k+2} (each group's four waves issue four DMA instructions each).
+                // Before the first slot: K_0 by all eight waves, K_1 and V_0 by group 1
+                // and 0 (their moves of "softmax item -1").
+                dma_half16(half_src(kbase, 0), rs, kst, 2 * wave, 2, lane);
+                if (grp == 1)
+                    dma_half16(half_src(kbase, 1), rs, kst + kDmaHalf, 4 * gw, 4, lane);
+                else
+                    dma_half16(half_src(vbase, 0), rs, vst, 4 * gw, 4, lane);
+                wait_vm<0>();
+                __syncthreads();
+                if (grp == 1) {  // group 1 starts one slot late; its K_2 move goes out now
+                    dma_half16(half_src(kbase, 2), rs, kst + 2 * kDmaHalf, 4 * gw, 4, lane);
+                    __syncthreads();
+                }
+                int jc_next = __builtin_amdgcn_readfirstlane(plist[0].y);
+                uint32_t umw[8];  // user-mask words of the next softmax item
+                auto softmax_and_move = [&](int k) {
+                    const int jc = jc_next;
+                    __builtin_amdgcn_sched_barrier(0);
+                    softmax_item32<DT, UM>(a, s, p, colscale, trow, umw, jc >> 2, k & 1, jc & 3,
+                                           skv, off, lane, mrun, lrun, o);
+                    __builtin_amdgcn_sched_barrier(0);
+                    // the move of this item: group 0 V_{k+1}, group 1 K_{k+3}
+                    if (grp == 0)
+                        dma_half16(half_src(vbase, k + 1), rs, vst + ((k + 1) & 3) * kDmaHalf,
+                                   4 * gw, 4, lane);
+                    else
+                        dma_half16(half_src(kbase, k + 3), rs, kst + ((k + 3) & 3) * kDmaHalf,
+                                   4 * gw, 4, lane);
+                    const int jn = plist[min(k + 1, nh - 1) >> 1].y;
+                    wait_vm<4>();  // all but this item's batch are in LDS
+                    __syncthreads();
+                    jc_next = __builtin_amdgcn_readfirstlane(jn);
+                };
+                if constexpr (UM) umask_words32(a, um, jc_next >> 2, 0, lane, umw);
+                mfma_item32d<DT, true, false>(kst, vst, qc, s, p, o, lane);
+                wait_vm<UM ? 12 : 4>();
+                __syncthreads();
+                softmax_and_move(0);
+                for (int k = 1; k < nh; ++k) {
+                    if constexpr (UM) umask_words32(a, um, jc_next >> 2, k & 1, lane, umw);
+                    mfma_item32d<DT, true, true>(kst + (k & 3) * kDmaHalf,
+                                                 vst + ((k - 1) & 3) * kDmaHalf, qc, s, p, o,
+                                                 lane);
+                    wait_vm<UM ? 12 : 4>();
+                    __syncthreads();
+                    softmax_and_move(k);
+                }
+                mfma_item32d<DT, false, true>(kst, vst + ((nh - 1) & 3) * kDmaHalf, qc, s, p, o,
+                                              lane);
+                wait_vm<0>();  // nothing may land in LDS after the task
+                if (grp == 0) __syncthreads();
+            }
+            __syncthreads();
+
+            write_rows32<DT, OUT>(a, it, complete, 2 * w + (sa > 0 ? 0 : 1), row0, lane, trow,
+                                  rvalid, mrun, lrun, o);
+            if (!complete) {
+                int* list = (int*)smem;
+                const int np = piece_arrive(a, w, u, st, a.nst, list);
+                if (np > 0)
+                    merge_rows<OUT>(a, list, np, row_base, min(row_base + R, rows_exist), it.n2,
+                                    t0, it.row0, it.sq);
+                __syncthreads();
+            }
+        }
+        advance_unit(a, it);
+    }
+}
+
+
+// ---------------------------------------------------------------------------------------------
 // Units of 65-256 rows: 128-row subtiles, two-group ping-pong with the keys split.
 //
 // Both groups hold the same 128 query rows (4 waves x 32 rows). Group 0 takes the first half
@@ -1286,7 +1565,11 @@ hipError_t launch_l(const FwdArgs& a, int rows, hipStream_t s) {
     const int grid = a.P * a.nst;
     // 8 waves per workgroup either way: 32 rows per wave for large units, 16 below (more
     // workgroups, fewer registers)
-    if (rows == 256) {
+    if (rows == 256 && DT != kFP8) {
+        // (the dtype expression keeps the fp8 instantiation, which never runs, compilable)
+        hipLaunchKernelGGL((fwd_prefill_pp32d_kernel<(DT == kFP8 ? kBF16 : DT), OUT, LAYOUT, UM>),
+                           dim3(grid), dim3(512), 0, s, a);
+    } else if (rows == 256) {
         hipLaunchKernelGGL((fwd_prefill_pp32_kernel<DT, OUT, LAYOUT, UM>), dim3(grid), dim3(512),
                            0, s, a);
     } else if (a.M > 64) {

@@ -793,6 +793,15 @@ __device__ __forceinline__ void softmax_item32(const FwdArgs& a, f32x16 (&s)[2],
     lrun = lrun * alpha + ls;
 }
 
+// Fixes the softmax item's results where they are computed. The exponentials and conversions
+// are plain arithmetic, which the compiler may sink past the barrier that follows into the next
+// slot; there they would run one after the other with the wave's own MFMA item instead of beside
+// the partner wave's. The empty statement claims to read and rewrite them, so nothing that
+// produces them can move below it.
+__device__ __forceinline__ void pin_softmax(u32x4 (&p)[4], float& lrun) {
+    asm volatile("" : "+v"(p[0]), "+v"(p[1]), "+v"(p[2]), "+v"(p[3]), "+v"(lrun));
+}
+
 // Normalised O and LSE of a wave's 32 rows (lane pair l, l + 32 per row), or the split partial.
 template <int DT, int OUT>
 __device__ __forceinline__ void write_rows32(const FwdArgs& a, const UnitIter& it, bool complete,
@@ -1001,6 +1010,7 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32_kernel(FwdArgs a) {
                     __builtin_amdgcn_sched_barrier(0);
                     softmax_item32<DT, UM>(a, s, p, colscale, trow, umw, jc >> 2, k & 1, jc & 3,
                                            skv, off, lane, mrun, lrun, o);
+                    pin_softmax(p, lrun);
                     __builtin_amdgcn_sched_barrier(0);
                     const int jn = plist[min(k + 1, nh - 1) >> 1].y;
                     const int qn = move_half(k + 2);
@@ -1061,34 +1071,58 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32_kernel(FwdArgs a) {
 constexpr int kDmaStride = 1088;             // bytes between the DMA instructions of a half page
 constexpr int kDmaHalf = 16 * kDmaStride;    // one half page
 
+// DMA instruction i (0..15) of the half page behind buffer resource r into the half-page buffer
+// dst. No destination register: the data goes to LDS; completion is awaited with vmcnt.
+__device__ __forceinline__ void dma_one(rsrc_t r, int rs, unsigned char* dst, int i, int lane) {
+    const int row = i + 16 * (lane >> 4);
+    const int voff = row * rs + 16 * ((lane & 15) ^ (i >> 2));
+    const uint32_t m0 = (uint32_t)(uintptr_t)(GBSA_LDS unsigned char*)(dst + i * kDmaStride);
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(m0), "v"(voff), "s"(r)
+                 : "memory", "m0");
+}
 // DMA instructions [i0, i0 + n) of half page `src` into the half-page buffer `dst`.
 __device__ __forceinline__ void dma_half16(const KvSrc& src, int rs, unsigned char* dst, int i0,
                                            int n, int lane) {
     const rsrc_t r = make_rsrc(src.p, src.records);
 #pragma unroll
-    for (int x = 0; x < n; ++x) {
-        const int i = i0 + x;
-        const int row = i + 16 * (lane >> 4);
-        const int voff = row * rs + 16 * ((lane & 15) ^ (i >> 2));
-        const uint32_t m0 = (uint32_t)(uintptr_t)(GBSA_LDS unsigned char*)(dst + i * kDmaStride);
-        // no destination register: the data goes to LDS; completion is awaited with vmcnt
-        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                     :
-                     : "s"(m0), "v"(voff), "s"(r)
-                     : "memory", "m0");
-    }
+    for (int x = 0; x < n; ++x) dma_one(r, rs, dst, i0 + x, lane);
 }
+
+// Page-list entry of the DMA kernel: byte offset of the page's head slice from the K (or V)
+// base, and the readable bytes of its two half pages (0 past the visible keys).
+__device__ __forceinline__ KvSrc page_half(const unsigned char* base, u32x4 e, int half, int rs) {
+    const uint64_t off = (uint64_t)__builtin_amdgcn_readfirstlane(e[0]) |
+                         ((uint64_t)__builtin_amdgcn_readfirstlane(e[1]) << 32);
+    const int rec = (int)__builtin_amdgcn_readfirstlane(half ? e[3] : e[2]);
+    return KvSrc{base + off + half * 64 * rs, rec};
+}
+
+// One wave's share (four DMA instructions) of moving a half page, issued from inside an MFMA
+// item: the page-list entry is read at step 0 and the instructions go out at steps 3, 5, 7, 9,
+// where the wave waits for the matrix pipe anyway.
+struct ItemMove {
+    const u32x4* entry;  // LDS page-list entry of the half page
+    int half;           // which half of the page
+    const unsigned char* base;
+    unsigned char* dst;  // half-page buffer
+    int i0;              // first of the wave's four DMA instructions
+};
+
 // Waits until at most n of this wave's vector-memory loads are in flight.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// MFMA item of the 256-row kernel on the DMA layout (as mfma_item32, 16-bit types).
-template <int DT, bool qk, bool pv>
+// MFMA item of the 256-row kernel on the DMA layout (as mfma_item32, 16-bit types), optionally
+// issuing one half-page move (MOVE) between its MFMAs.
+template <int DT, bool qk, bool pv, bool MOVE = false>
 __device__ __forceinline__ void mfma_item32d(const unsigned char* ks, const unsigned char* vs,
                                              const QCol32& qc, f32x16 (&s)[2],
-                                             const u32x4 (&p)[4], f32x16 (&o)[4], int lane) {
+                                             const u32x4 (&p)[4], f32x16 (&o)[4], int lane,
+                                             const ItemMove& mv = ItemMove{}, int rs = 0) {
     constexpr int QS = qk ? 8 : 0;
     constexpr int VS = pv ? 8 : 0;
     constexpr int PC = QS + VS, NS = 2 * PC, D = kPipeDepth;
@@ -1126,6 +1160,9 @@ __device__ __forceinline__ void mfma_item32d(const unsigned char* ks, const unsi
             o[dt] = mfma_32x32x16<DT>(f.a, p[2 * t + a2], o[dt]);
         }
     };
+    static_assert(!MOVE || NS >= 10, "the move needs ten steps");
+    u32x4 ent;
+    rsrc_t mr;
     Frag fr[D];
 #pragma unroll
     for (int i = 0; i < D; ++i)
@@ -1134,6 +1171,14 @@ __device__ __forceinline__ void mfma_item32d(const unsigned char* ks, const unsi
     for (int st = 0; st < NS; ++st) {
         const Frag f = fr[st % D];
         if (st + D < NS) fr[st % D] = load(st + D);
+        if constexpr (MOVE) {
+            if (st == 0) ent = *(const GBSA_LDS u32x4*)mv.entry;
+            if (st == 2) {
+                const KvSrc src = page_half(mv.base, ent, mv.half, rs);
+                mr = make_rsrc(src.p, src.records);
+            }
+            if (st >= 3 && st <= 9 && (st & 1)) dma_one(mr, rs, mv.dst, mv.i0 + (st - 3) / 2, lane);
+        }
         compute(st, f);
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -1146,7 +1191,9 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32d_kernel(FwdArgs a) {
     constexpr int esz = 2;
     // [K buffers 0..3][V buffers 0..3], one half page each
     __shared__ __attribute__((aligned(16))) unsigned char smem[8 * kDmaHalf];
-    __shared__ int4 plist[256];
+    // per visible page: byte offset of this head's slice, readable bytes of its two halves
+    __shared__ u32x4 plist[256];
+    __shared__ int jlist[256];  // per visible page: block index * 4 + mask class
     __shared__ int flag[1];
     static_assert(sizeof(smem) >= kPieceListBytes, "the split merge borrows the stages");
 
@@ -1221,9 +1268,11 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32d_kernel(FwdArgs a) {
                         const int pos = n + __builtin_amdgcn_mbcnt_hi(
                                                 (uint32_t)(mm >> 32),
                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)mm, 0));
-                        plist[pos] = make_int4(pl, jl * 4 + cl,
-                                               kv_records(rs, skv - 128 * jl),
-                                               kv_records(rs, skv - 128 * jl - 64));
+                        const uint64_t po = (uint64_t)((int64_t)pl * a.kv_stride * esz + head_off);
+                        plist[pos] = (u32x4){(uint32_t)po, (uint32_t)(po >> 32),
+                                             (uint32_t)kv_records(rs, skv - 128 * jl),
+                                             (uint32_t)kv_records(rs, skv - 128 * jl - 64)};
+                        jlist[pos] = jl * 4 + cl;
                     }
                     n += __builtin_popcountll(mm);
                 }
@@ -1235,21 +1284,29 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32d_kernel(FwdArgs a) {
             // half page q (clamped into the stream) of K or V of this head
             auto half_src = [&](const unsigned char* base, int q) {
                 q = min(q, nh - 1);
-                const int4 e = plist[q >> 1];
-                const int unit = __builtin_amdgcn_readfirstlane(e.x);
-                const int rec = __builtin_amdgcn_readfirstlane((q & 1) ? e.w : e.z);
-                return KvSrc{base + (int64_t)unit * a.kv_stride * esz + head_off +
-                                 (q & 1) * 64 * rs,
-                             rec};
+                return page_half(base, plist[q >> 1], q & 1, rs);
             };
             if (nh > 0) {
                 f32x16 s[2];
                 u32x4 p[4];
                 // Readers: MFMA item k reads K_k (K buffer k % 4) and V_{k-1} (V buffer
-                // (k - 1) % 4). Writers: group 0's softmax item k - 1 moves V_k, group 1's
-                // moves K_{k+2} (each group's four waves issue four DMA instructions each).
+                // (k - 1) % 4); group 0 runs it in slot 2 k, group 1 in slot 2 k + 1.
+                // Writers (each group's four waves issue four DMA instructions each): group 0
+                // moves V_{k+1}, group 1 K_{k+3}, during their MFMA item k (without a user
+                // mask: the wave has issue slots to spare between its MFMAs) or else at the
+                // end of their softmax item k, a slot later. Either way a move lands in a
+                // buffer whose last reader is past a barrier, and a wave lets only its newest
+                // batch stay in flight across a barrier, so every batch has two slots to land
+                // before its first reader. (With a user mask, the compiler's own vmcnt waits
+                // for the mask words would also wait for DMA issued after them.)
                 // Before the first slot: K_0 by all eight waves, K_1 and V_0 by group 1
-                // and 0 (their moves of "softmax item -1").
+                // and 0, and K_2 by group 1 in its first slot.
+                // Issue priority: the two waves on a SIMD compete for instruction issue, and
+                // the older one wins ties. Unless its MFMAs go out as soon as the matrix pipe
+                // frees, the pipe idles while the softmax wave issues; so the MFMA item runs
+                // at raised priority and the softmax item takes the remaining issue cycles
+                // (without the raise, the slots where the younger group does its MFMA item
+                // ran about 40 % longer).
                 dma_half16(half_src(kbase, 0), rs, kst, 2 * wave, 2, lane);
                 if (grp == 1)
                     dma_half16(half_src(kbase, 1), rs, kst + kDmaHalf, 4 * gw, 4, lane);
@@ -1261,42 +1318,61 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32d_kernel(FwdArgs a) {
                     dma_half16(half_src(kbase, 2), rs, kst + 2 * kDmaHalf, 4 * gw, 4, lane);
                     __syncthreads();
                 }
-                int jc_next = __builtin_amdgcn_readfirstlane(plist[0].y);
+                int jc_next = __builtin_amdgcn_readfirstlane(jlist[0]);
+                constexpr bool kItemMove = !UM;
+                auto raise = [] { if constexpr (kItemMove) __builtin_amdgcn_s_setprio(3); };
+                auto lower = [] { if constexpr (kItemMove) __builtin_amdgcn_s_setprio(0); };
+                auto move_of = [&](int k) {
+                    const int q = min(grp == 0 ? k + 1 : k + 3, nh - 1);
+                    return ItemMove{plist + (q >> 1), q & 1, grp == 0 ? vbase : kbase,
+                                    grp == 0 ? vst + ((k + 1) & 3) * kDmaHalf
+                                             : kst + ((k + 3) & 3) * kDmaHalf,
+                                    4 * gw};
+                };
                 uint32_t umw[8];  // user-mask words of the next softmax item
                 auto softmax_and_move = [&](int k) {
                     const int jc = jc_next;
                     __builtin_amdgcn_sched_barrier(0);
                     softmax_item32<DT, UM>(a, s, p, colscale, trow, umw, jc >> 2, k & 1, jc & 3,
                                            skv, off, lane, mrun, lrun, o);
+                    pin_softmax(p, lrun);
                     __builtin_amdgcn_sched_barrier(0);
-                    // the move of this item: group 0 V_{k+1}, group 1 K_{k+3}
-                    if (grp == 0)
-                        dma_half16(half_src(vbase, k + 1), rs, vst + ((k + 1) & 3) * kDmaHalf,
-                                   4 * gw, 4, lane);
-                    else
-                        dma_half16(half_src(kbase, k + 3), rs, kst + ((k + 3) & 3) * kDmaHalf,
-                                   4 * gw, 4, lane);
-                    const int jn = plist[min(k + 1, nh - 1) >> 1].y;
+                    if constexpr (!kItemMove) {  // group 0 V_{k+1}, group 1 K_{k+3}
+                        if (grp == 0)
+                            dma_half16(half_src(vbase, k + 1), rs,
+                                       vst + ((k + 1) & 3) * kDmaHalf, 4 * gw, 4, lane);
+                        else
+                            dma_half16(half_src(kbase, k + 3), rs,
+                                       kst + ((k + 3) & 3) * kDmaHalf, 4 * gw, 4, lane);
+                    }
+                    const int jn = jlist[min(k + 1, nh - 1) >> 1];
                     wait_vm<4>();  // all but this item's batch are in LDS
                     __syncthreads();
                     jc_next = __builtin_amdgcn_readfirstlane(jn);
                 };
                 if constexpr (UM) umask_words32(a, um, jc_next >> 2, 0, lane, umw);
-                mfma_item32d<DT, true, false>(kst, vst, qc, s, p, o, lane);
+                raise();
+                mfma_item32d<DT, true, false, kItemMove>(kst, vst, qc, s, p, o, lane, move_of(0),
+                                                         rs);
+                lower();
                 wait_vm<UM ? 12 : 4>();
                 __syncthreads();
                 softmax_and_move(0);
                 for (int k = 1; k < nh; ++k) {
                     if constexpr (UM) umask_words32(a, um, jc_next >> 2, k & 1, lane, umw);
-                    mfma_item32d<DT, true, true>(kst + (k & 3) * kDmaHalf,
-                                                 vst + ((k - 1) & 3) * kDmaHalf, qc, s, p, o,
-                                                 lane);
+                    raise();
+                    mfma_item32d<DT, true, true, kItemMove>(kst + (k & 3) * kDmaHalf,
+                                                            vst + ((k - 1) & 3) * kDmaHalf, qc, s,
+                                                            p, o, lane, move_of(k), rs);
+                    lower();
                     wait_vm<UM ? 12 : 4>();
                     __syncthreads();
                     softmax_and_move(k);
                 }
+                raise();
                 mfma_item32d<DT, false, true>(kst, vst + ((nh - 1) & 3) * kDmaHalf, qc, s, p, o,
                                               lane);
+                lower();
                 wait_vm<0>();  // nothing may land in LDS after the task
                 if (grp == 0) __syncthreads();
             }
@@ -1478,6 +1554,7 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32_kernel(FwdArgs a) {
                     __builtin_amdgcn_sched_barrier(0);
                     softmax_item32<DT, UM>(a, s, p, colscale, trow, umw, jc >> 2, grp, jc & 3,
                                            skv, off, lane, mrun, lrun, o);
+                    pin_softmax(p, lrun);
                     __builtin_amdgcn_sched_barrier(0);
                     store_k<DT, 256, 64>(pr, my_k, tg);
                     __syncthreads();

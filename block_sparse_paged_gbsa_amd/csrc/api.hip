@@ -356,6 +356,7 @@ static gbsa_status forward_impl(const gbsa_params* p, const gbsa_forward_args* g
     a.lse = softmax_lse;
     a.ws_status = (int32_t*)(ws + L.status);
     a.ws_arrive = (int32_t*)(ws + L.arrive);
+    a.ws_queue = a.ws_status + 16;  // the rest of the zero-filled status page
     a.ws_o = (float*)(ws + L.o);
     a.ws_m = (float*)(ws + L.m);
     a.ws_l = (float*)(ws + L.l);
@@ -390,6 +391,10 @@ static gbsa_status forward_impl(const gbsa_params* p, const gbsa_forward_args* g
     fill_fingerprint(p, a.expect);
 
     a.nst = (int32_t)subtiles(M);
+    int cus = 0;
+    st = device_cus(&cus);
+    if (st != GBSA_OK) return st;
+    a.cus = cus;
     hipError_t e;
     if (M <= kDecodeMaxRows)
         e = launch_decode(a, p->dtype, p->out_dtype, stream);

@@ -230,6 +230,115 @@ __device__ __forceinline__ bool bound_less(Bound a, Bound b) {
 
 __device__ __forceinline__ int ceil_div_i(int64_t a, int b) { return (int)((a + b - 1) / b); }
 
+// ---------------------------------------------------------------------------
+// Task assignment of the prefill kernels.
+//
+// A task is one row subtile of a range of units. With the worker plan (small problems), task
+// w * nst + st is worker w's range of unit slots (split units merged by the last piece) and
+// every workgroup of the grid runs one task. With unit tasks (unit_tasks != 0; the host picks
+// this when there are many more units than resident workgroups), task u * nst + st is all of
+// unit u, and a grid of resident workgroups takes tasks until none are left: the XCDs of one
+// device do not run at one clock under load, and a fixed share per XCD waits for the slowest.
+// Each XCD has a queue over a contiguous eighth of the tasks (neighbouring units share key
+// pages in that XCD's L2); a workgroup drains its own XCD's queue, then the others in turn.
+// ---------------------------------------------------------------------------
+struct Task {
+    int w, st;      // worker (-1 for a unit task) and row subtile
+    Bound b0, b1;   // unit slots [b0, b1)
+};
+
+constexpr int kQueues = 8;         // one per XCD
+constexpr int kQueueStride = 4;    // words between queue counters
+constexpr int kQueueDone = kQueues * kQueueStride;  // word of the finished-workgroup counter
+
+// Thread 0: next task of the queues, starting at this workgroup's own (home) and moving on
+// when one is empty; -1 when all are. `probe` (thread 0's) counts the queues found empty.
+__device__ __forceinline__ int task_grab(int32_t* q, int ntask, int home, int& probe) {
+    while (probe < kQueues) {
+        const int x = (home + probe) & (kQueues - 1);
+        const int lo = (int)((int64_t)ntask * x / kQueues);
+        const int hi = (int)((int64_t)ntask * (x + 1) / kQueues);
+        if (hi > lo) {
+            const int t = __hip_atomic_fetch_add(q + x * kQueueStride, 1, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+            if (t < hi - lo) return lo + t;
+        }
+        ++probe;
+    }
+    return -1;
+}
+
+// Thread 0, once per workgroup after its last (failed) grab: the last workgroup of the grid
+// to get here sets the counters back to zero for the next call. Every grab of every
+// workgroup has returned before that workgroup counts itself here (the grabs return values
+// it waits for), so no grab can land after the reset.
+__device__ __forceinline__ void task_finish(int32_t* q) {
+    const int done = __hip_atomic_fetch_add(q + kQueueDone, 1, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+    if (done == (int)gridDim.x - 1) {
+        for (int x = 0; x < kQueues; ++x)
+            __hip_atomic_store(q + x * kQueueStride, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(q + kQueueDone, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// The kernel's FwdArgs, read through a pointer the compiler cannot follow: the body then loads
+// each argument where it uses it, instead of the compiler hoisting the loads to the top (out of
+// the task loop) and keeping the values live, in spilled scalar registers, through every item
+// of every task. The kernels take FwdArgs as their only argument, at the start of the kernel
+// argument segment (taking the address of the parameter itself would copy it to private
+// memory).
+__device__ __forceinline__ const FwdArgs& opaque_args() {
+    using KernArgs = const __attribute__((address_space(4))) FwdArgs;
+    KernArgs* kp = (KernArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(kp));
+    return *(const FwdArgs*)kp;
+}
+
+// Runs body(args, Task) for this workgroup's tasks. Whole workgroup; `word` points to two LDS ints
+// (the next task, and thread 0's count of queues found empty), so that no loop state stays in
+// registers across the body. The body may use barriers and LDS freely: the next task starts
+// after a barrier. (One call site, so that the body is inlined once.) Kernels built without
+// DYN run the worker plan only, with no loop around the body (their launcher never asks for
+// unit tasks): the variants at the register limit keep their allocation.
+template <bool DYN, class F>
+__device__ __forceinline__ void run_tasks(const FwdArgs& a, int U, int* word, F&& body) {
+    if constexpr (!DYN) {
+        const int lin = xcd_remap(blockIdx.x, gridDim.x);
+        const int w = lin / a.nst;
+        body(opaque_args(), Task{w, lin - w * a.nst, read_bound(a.meta, w), read_bound(a.meta, w + 1)});
+        return;
+    }
+    if (threadIdx.x == 0) word[1] = 0;
+    for (;;) {
+        if (threadIdx.x == 0) {
+            int lin = -1;
+            if (a.unit_tasks) {
+                int probe = word[1];
+                lin = task_grab(a.ws_queue, U * a.nst, blockIdx.x & (kQueues - 1), probe);
+                word[1] = probe;
+            } else if (word[1] == 0) {
+                lin = xcd_remap(blockIdx.x, gridDim.x);  // the workgroup's one worker task
+                word[1] = 1;
+            }
+            word[0] = lin;
+        }
+        __syncthreads();
+        const int lin = __builtin_amdgcn_readfirstlane(word[0]);
+        if (lin < 0) break;
+        const int q = lin / a.nst;  // unit or worker
+        Task tk{-1, lin - q * a.nst, Bound{q, 0}, Bound{q + 1, 0}};
+        if (!a.unit_tasks) {
+            tk.w = q;
+            tk.b0 = read_bound(a.meta, q);
+            tk.b1 = read_bound(a.meta, q + 1);
+        }
+        body(opaque_args(), tk);
+        __syncthreads();
+    }
+    if (a.unit_tasks && threadIdx.x == 0) task_finish(a.ws_queue);
+}
+
 // Position in the ordered unit list (b, n2, active q-block gl).
 struct UnitIter {
     int b, n2, gl;

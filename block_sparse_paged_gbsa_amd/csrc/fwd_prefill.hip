@@ -20,6 +20,8 @@
 //    (33-64 rows) or 4 (17-32 rows) wave groups that hold the same rows, 16x16 MFMA tiles.
 #include <stdint.h>
 
+#include <atomic>
+
 #include "split_merge.hpp"
 
 namespace gbsa {
@@ -390,164 +392,165 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_prefill_kernel(FwdArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform for the compiler
     const int rw = wave % RW, kp = wave / RW;  // row wave and key slice
     const int lrow = lane & 15, lgrp = lane >> 4;
-    const int lin = xcd_remap(blockIdx.x, gridDim.x);
-    const int w = lin / a.nst, st = lin - (lin / a.nst) * a.nst;
-
     if (!header_ok(a)) {
         refuse(a);
         return;
     }
-    const Bound b0 = read_bound(a.meta, w), b1 = read_bound(a.meta, w + 1);
     const int U = a.meta[3];
-    if (!bound_less(b0, b1) || b0.u >= U) return;
-    UnitIter it = locate_unit(a, b0.u);
-    if (it.b < 0) return;
+    __shared__ int task_word[2];
+    run_tasks<!UM>(a, U, task_word, [&](const FwdArgs& a, const Task& tk) {
+        const int w = tk.w, st = tk.st;
+        const Bound b0 = tk.b0, b1 = tk.b1;
+        if (!bound_less(b0, b1) || b0.u >= U) return;
+        UnitIter it = locate_unit(a, b0.u);
+        if (it.b < 0) return;
 
-    const int rs = a.N2 * 128 * esz;  // bytes between tokens of a page
+        const int rs = a.N2 * 128 * esz;  // bytes between tokens of a page
 
-    for (int u = b0.u;; ++u) {
-        const int sa = (u == b0.u) ? b0.s : 0;
-        if (u >= U || u > b1.u || (u == b1.u && sa >= b1.s)) break;
-        const int g = it.qbase + it.gl;
-        int cnt = 0;
-        if (g < a.tqb) cnt = min(max(a.cnt[(int64_t)it.n2 * a.tqb + g], 0), a.topK);
-        const int se = (u == b1.u) ? b1.s : cnt;
-        const bool complete = (sa == 0) && (se == cnt);
+        for (int u = b0.u;; ++u) {
+            const int sa = (u == b0.u) ? b0.s : 0;
+            if (u >= U || u > b1.u || (u == b1.u && sa >= b1.s)) break;
+            const int g = it.qbase + it.gl;
+            int cnt = 0;
+            if (g < a.tqb) cnt = min(max(a.cnt[(int64_t)it.n2 * a.tqb + g], 0), a.topK);
+            const int se = (u == b1.u) ? b1.s : cnt;
+            const bool complete = (sa == 0) && (se == cnt);
 
-        const int t0 = it.gl * a.X;  // batch-local first row of the q-block
-        const int rows_exist = min(a.X, it.storage - t0) * a.G;
-        const int row_base = st * R;
-        if (row_base < rows_exist) {
-            const KvSeq kv = kv_seq<LAYOUT>(a, it.b);
-            const int skv = kv.len;
-            const int off = diag_off(a, skv, it.sq);
-            QTile<NQ> qt;
-            float colscale[NQ];
-            int trow[NQ];
-            bool rvalid[NQ];
-            load_q<DT, NQ>(a, it, t0, rows_exist, row_base + rw * NQ * 16, lane, qt, colscale,
-                           trow, rvalid);
-            UMaskRow um[NQ];
+            const int t0 = it.gl * a.X;  // batch-local first row of the q-block
+            const int rows_exist = min(a.X, it.storage - t0) * a.G;
+            const int row_base = st * R;
+            if (row_base < rows_exist) {
+                const KvSeq kv = kv_seq<LAYOUT>(a, it.b);
+                const int skv = kv.len;
+                const int off = diag_off(a, skv, it.sq);
+                QTile<NQ> qt;
+                float colscale[NQ];
+                int trow[NQ];
+                bool rvalid[NQ];
+                load_q<DT, NQ>(a, it, t0, rows_exist, row_base + rw * NQ * 16, lane, qt, colscale,
+                               trow, rvalid);
+                UMaskRow um[NQ];
 #pragma unroll
-            for (int nq = 0; nq < NQ; ++nq)
-                um[nq] = UM ? umask_row(a, it.b, trow[nq], rvalid[nq])
-                            : UMaskRow{make_rsrc(nullptr, 0), -1};
-            float mrun[NQ], lrun[NQ];
-            f32x4 o[8][NQ];
+                for (int nq = 0; nq < NQ; ++nq)
+                    um[nq] = UM ? umask_row(a, it.b, trow[nq], rvalid[nq])
+                                : UMaskRow{make_rsrc(nullptr, 0), -1};
+                float mrun[NQ], lrun[NQ];
+                f32x4 o[8][NQ];
 #pragma unroll
-            for (int nq = 0; nq < NQ; ++nq) {
-                mrun[nq] = kNegInf;
-                lrun[nq] = 0.f;
+                for (int nq = 0; nq < NQ; ++nq) {
+                    mrun[nq] = kNegInf;
+                    lrun[nq] = 0.f;
 #pragma unroll
-                for (int dt = 0; dt < 8; ++dt) o[dt][nq] = (f32x4){0.f, 0.f, 0.f, 0.f};
-            }
-            // rows of this workgroup, for block classification
-            const int t_lo = t0 + row_base / a.G;
-            const int t_hi = t0 + (min(row_base + R, rows_exist) - 1) / a.G;
+                    for (int dt = 0; dt < 8; ++dt) o[dt][nq] = (f32x4){0.f, 0.f, 0.f, 0.f};
+                }
+                // rows of this workgroup, for block classification
+                const int t_lo = t0 + row_base / a.G;
+                const int t_hi = t0 + (min(row_base + R, rows_exist) - 1) / a.G;
 
-            const int32_t* sel = a.idx + ((int64_t)it.n2 * a.tqb + g) * a.topK;
-            const int64_t head_off = (int64_t)it.n2 * 128 * esz;
+                const int32_t* sel = a.idx + ((int64_t)it.n2 * a.tqb + g) * a.topK;
+                const int64_t head_off = (int64_t)it.n2 * 128 * esz;
 
-            // ---- stream the task's visible pages through the double-buffered stage ------
-            // lane l of every wave holds slot c0 + l of the current 64-slot chunk
-            PageRegs<DT, NT, 128> pr;
-            SliceMid<NQ, TT> smid;
-            const int tok0 = kp * (128 / KS);
-            int buf = 0;
-            bool have_prev = false;  // a page is waiting in stage[buf]
-            int prev_j = 0, prev_cls = 0;
-            for (int c0 = sa; c0 < se; c0 += 64) {
-                const int n = min(64, se - c0);
-                int jl = -1, pl = 0, cl = 0;
-                if (lane < n) {
-                    jl = sel[c0 + lane];
-                    if (jl >= 0) {
-                        cl = block_class(a, (int64_t)jl * 128, skv, off, t_lo, t_hi);
-                        if (cl != 0) pl = kv.unit<LAYOUT>(jl);
+                // ---- stream the task's visible pages through the double-buffered stage ------
+                // lane l of every wave holds slot c0 + l of the current 64-slot chunk
+                PageRegs<DT, NT, 128> pr;
+                SliceMid<NQ, TT> smid;
+                const int tok0 = kp * (128 / KS);
+                int buf = 0;
+                bool have_prev = false;  // a page is waiting in stage[buf]
+                int prev_j = 0, prev_cls = 0;
+                for (int c0 = sa; c0 < se; c0 += 64) {
+                    const int n = min(64, se - c0);
+                    int jl = -1, pl = 0, cl = 0;
+                    if (lane < n) {
+                        jl = sel[c0 + lane];
+                        if (jl >= 0) {
+                            cl = block_class(a, (int64_t)jl * 128, skv, off, t_lo, t_hi);
+                            if (cl != 0) pl = kv.unit<LAYOUT>(jl);
+                        }
+                    }
+                    uint64_t todo = __ballot(cl != 0);
+                    while (todo) {
+                        const int i = __builtin_ctzll(todo);
+                        todo &= todo - 1;
+                        const int unit = __builtin_amdgcn_readlane(pl, i);
+                        const int64_t pb = (int64_t)unit * a.kv_stride * esz + head_off;
+                        const int nv = skv - 128 * __builtin_amdgcn_readlane(jl, i);
+                        // the first page goes straight into stage[buf]; later ones into the
+                        // other buffer while stage[buf] is consumed
+                        unsigned char* cur = smem + buf * PageStage<DT>::bytes;
+                        unsigned char* dst = have_prev ? smem + (buf ^ 1) * PageStage<DT>::bytes : cur;
+                        page_load<DT, NT>(pr, kv_src(a.k, pb, rs, nv), rs, tid);
+                        if (have_prev)
+                            slice_part_a<DT, NQ, UM, TT>(a, cur, qt, colscale, trow, um, prev_j,
+                                                         prev_cls, skv, off, lane, tok0, mrun, lrun,
+                                                         o, smid);
+                        store_k<DT, NT>(pr, dst, tid);
+                        page_load<DT, NT>(pr, kv_src(a.v, pb, rs, nv), rs, tid);
+                        if (have_prev) slice_part_b<DT, NQ, TT>(cur, lane, tok0, o, smid);
+                        store_v<DT, NT>(pr, dst + PageStage<DT>::k_bytes, tid);
+                        if (have_prev) buf ^= 1;
+                        __syncthreads();
+                        have_prev = true;
+                        prev_j = __builtin_amdgcn_readlane(jl, i);
+                        prev_cls = __builtin_amdgcn_readlane(cl, i);
                     }
                 }
-                uint64_t todo = __ballot(cl != 0);
-                while (todo) {
-                    const int i = __builtin_ctzll(todo);
-                    todo &= todo - 1;
-                    const int unit = __builtin_amdgcn_readlane(pl, i);
-                    const int64_t pb = (int64_t)unit * a.kv_stride * esz + head_off;
-                    const int nv = skv - 128 * __builtin_amdgcn_readlane(jl, i);
-                    // the first page goes straight into stage[buf]; later ones into the
-                    // other buffer while stage[buf] is consumed
+                if (have_prev) {
                     unsigned char* cur = smem + buf * PageStage<DT>::bytes;
-                    unsigned char* dst = have_prev ? smem + (buf ^ 1) * PageStage<DT>::bytes : cur;
-                    page_load<DT, NT>(pr, kv_src(a.k, pb, rs, nv), rs, tid);
-                    if (have_prev)
-                        slice_part_a<DT, NQ, UM, TT>(a, cur, qt, colscale, trow, um, prev_j,
-                                                     prev_cls, skv, off, lane, tok0, mrun, lrun,
-                                                     o, smid);
-                    store_k<DT, NT>(pr, dst, tid);
-                    page_load<DT, NT>(pr, kv_src(a.v, pb, rs, nv), rs, tid);
-                    if (have_prev) slice_part_b<DT, NQ, TT>(cur, lane, tok0, o, smid);
-                    store_v<DT, NT>(pr, dst + PageStage<DT>::k_bytes, tid);
-                    if (have_prev) buf ^= 1;
-                    __syncthreads();
-                    have_prev = true;
-                    prev_j = __builtin_amdgcn_readlane(jl, i);
-                    prev_cls = __builtin_amdgcn_readlane(cl, i);
-                }
-            }
-            if (have_prev) {
-                unsigned char* cur = smem + buf * PageStage<DT>::bytes;
-                slice_part_a<DT, NQ, UM, TT>(a, cur, qt, colscale, trow, um, prev_j, prev_cls,
-                                             skv, off, lane, tok0, mrun, lrun, o, smid);
-                slice_part_b<DT, NQ, TT>(cur, lane, tok0, o, smid);
-            }
-            __syncthreads();  // the stage is reused by the next task
-
-            {
-                // key slices 1..KS-1 hand (O, running max, row sums) to slice 0 through the
-                // free stage memory; the lane layout is the same in every slice
-                f32x4* so = (f32x4*)smem;
-                float* sml = (float*)(smem + (KS - 1) * RW * 8 * 64 * 16);
-                if (kp > 0) {
-                    const int slot = (kp - 1) * RW + rw;
-#pragma unroll
-                    for (int dt = 0; dt < 8; ++dt) so[(slot * 8 + dt) * 64 + lane] = o[dt][0];
-                    sml[slot * 128 + lane] = mrun[0];
-                    sml[slot * 128 + 64 + lane] = lrun[0];
-                }
-                __syncthreads();
-                if (kp == 0) {
-#pragma unroll
-                    for (int k = 1; k < KS; ++k) {
-                        const int slot = (k - 1) * RW + rw;
-                        const float m1 = sml[slot * 128 + lane], l1 = sml[slot * 128 + 64 + lane];
-                        const float m = fmaxf(mrun[0], m1);
-                        const float f0 = (m == kNegInf) ? 0.f : fast_exp2(mrun[0] - m);
-                        const float f1 = (m == kNegInf) ? 0.f : fast_exp2(m1 - m);
-                        mrun[0] = m;
-                        lrun[0] = lrun[0] * f0 + l1 * f1;
-#pragma unroll
-                        for (int dt = 0; dt < 8; ++dt)
-                            o[dt][0] = o[dt][0] * f0 + so[(slot * 8 + dt) * 64 + lane] * f1;
-                    }
+                    slice_part_a<DT, NQ, UM, TT>(a, cur, qt, colscale, trow, um, prev_j, prev_cls,
+                                                 skv, off, lane, tok0, mrun, lrun, o, smid);
+                    slice_part_b<DT, NQ, TT>(cur, lane, tok0, o, smid);
                 }
                 __syncthreads();  // the stage is reused by the next task
-            }
 
-            // ---- epilogue: normalised output + LSE, or a split-KV partial --------------
-            if (kp == 0)
-                write_rows<DT, OUT, NQ>(a, it, complete, 2 * w + (sa > 0 ? 0 : 1),
-                                        row_base + rw * NQ * 16, lane, trow, rvalid, mrun, lrun,
-                                        o);
-            if (!complete) {
-                int* list = (int*)smem;  // the stages are free until the next task
-                const int np = piece_arrive(a, w, u, st, a.nst, list);
-                if (np > 0)
-                    merge_rows<OUT>(a, list, np, row_base, min(row_base + R, rows_exist), it.n2,
-                                    t0, it.row0, it.sq);
-                __syncthreads();
+                {
+                    // key slices 1..KS-1 hand (O, running max, row sums) to slice 0 through the
+                    // free stage memory; the lane layout is the same in every slice
+                    f32x4* so = (f32x4*)smem;
+                    float* sml = (float*)(smem + (KS - 1) * RW * 8 * 64 * 16);
+                    if (kp > 0) {
+                        const int slot = (kp - 1) * RW + rw;
+#pragma unroll
+                        for (int dt = 0; dt < 8; ++dt) so[(slot * 8 + dt) * 64 + lane] = o[dt][0];
+                        sml[slot * 128 + lane] = mrun[0];
+                        sml[slot * 128 + 64 + lane] = lrun[0];
+                    }
+                    __syncthreads();
+                    if (kp == 0) {
+#pragma unroll
+                        for (int k = 1; k < KS; ++k) {
+                            const int slot = (k - 1) * RW + rw;
+                            const float m1 = sml[slot * 128 + lane], l1 = sml[slot * 128 + 64 + lane];
+                            const float m = fmaxf(mrun[0], m1);
+                            const float f0 = (m == kNegInf) ? 0.f : fast_exp2(mrun[0] - m);
+                            const float f1 = (m == kNegInf) ? 0.f : fast_exp2(m1 - m);
+                            mrun[0] = m;
+                            lrun[0] = lrun[0] * f0 + l1 * f1;
+#pragma unroll
+                            for (int dt = 0; dt < 8; ++dt)
+                                o[dt][0] = o[dt][0] * f0 + so[(slot * 8 + dt) * 64 + lane] * f1;
+                        }
+                    }
+                    __syncthreads();  // the stage is reused by the next task
+                }
+
+                // ---- epilogue: normalised output + LSE, or a split-KV partial --------------
+                if (kp == 0)
+                    write_rows<DT, OUT, NQ>(a, it, complete, 2 * w + (sa > 0 ? 0 : 1),
+                                            row_base + rw * NQ * 16, lane, trow, rvalid, mrun, lrun,
+                                            o);
+                if (!complete) {
+                    int* list = (int*)smem;  // the stages are free until the next task
+                    const int np = piece_arrive(a, w, u, st, a.nst, list);
+                    if (np > 0)
+                        merge_rows<OUT>(a, list, np, row_base, min(row_base + R, rows_exist), it.n2,
+                                        t0, it.row0, it.sq);
+                    __syncthreads();
+                }
             }
+            advance_unit(a, it);
         }
-        advance_unit(a, it);
-    }
+    });
 }
 
 
@@ -864,191 +867,192 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32_kernel(FwdArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int grp = wave >> 2;  // waves w and w + 4 share a SIMD
     const int tg = tid & 255;   // thread index within the group
-    const int lin = xcd_remap(blockIdx.x, gridDim.x);
-    const int w = lin / a.nst, st = lin - (lin / a.nst) * a.nst;
-
     if (!header_ok(a)) {
         refuse(a);
         return;
     }
-    const Bound b0 = read_bound(a.meta, w), b1 = read_bound(a.meta, w + 1);
     const int U = a.meta[3];
-    if (!bound_less(b0, b1) || b0.u >= U) return;
-    UnitIter it = locate_unit(a, b0.u);
-    if (it.b < 0) return;
+    __shared__ int task_word[2];
+    run_tasks<!UM>(a, U, task_word, [&](const FwdArgs& a, const Task& tk) {
+        const int w = tk.w, st = tk.st;
+        const Bound b0 = tk.b0, b1 = tk.b1;
+        if (!bound_less(b0, b1) || b0.u >= U) return;
+        UnitIter it = locate_unit(a, b0.u);
+        if (it.b < 0) return;
 
-    const int rs = a.N2 * 128 * esz;  // bytes between tokens of a page
-    const unsigned char* kbase = (const unsigned char*)a.k;
-    const unsigned char* vbase = (const unsigned char*)a.v;
-    unsigned char* const kst = smem;
-    unsigned char* const vst = smem + 2 * KB;
+        const int rs = a.N2 * 128 * esz;  // bytes between tokens of a page
+        const unsigned char* kbase = (const unsigned char*)a.k;
+        const unsigned char* vbase = (const unsigned char*)a.v;
+        unsigned char* const kst = smem;
+        unsigned char* const vst = smem + 2 * KB;
 
-    for (int u = b0.u;; ++u) {
-        const int sa = (u == b0.u) ? b0.s : 0;
-        if (u >= U || u > b1.u || (u == b1.u && sa >= b1.s)) break;
-        const int g = it.qbase + it.gl;
-        int cnt = 0;
-        if (g < a.tqb) cnt = min(max(a.cnt[(int64_t)it.n2 * a.tqb + g], 0), a.topK);
-        const int se = (u == b1.u) ? b1.s : cnt;
-        const bool complete = (sa == 0) && (se == cnt);
+        for (int u = b0.u;; ++u) {
+            const int sa = (u == b0.u) ? b0.s : 0;
+            if (u >= U || u > b1.u || (u == b1.u && sa >= b1.s)) break;
+            const int g = it.qbase + it.gl;
+            int cnt = 0;
+            if (g < a.tqb) cnt = min(max(a.cnt[(int64_t)it.n2 * a.tqb + g], 0), a.topK);
+            const int se = (u == b1.u) ? b1.s : cnt;
+            const bool complete = (sa == 0) && (se == cnt);
 
-        const int t0 = it.gl * a.X;
-        const int rows_exist = min(a.X, it.storage - t0) * a.G;
-        const int row_base = st * R;
-        if (row_base < rows_exist) {
-            const KvSeq kv = kv_seq<LAYOUT>(a, it.b);
-            const int skv = kv.len;
-            const int off = diag_off(a, skv, it.sq);
-            const int row0 = row_base + wave * 32;
-            QCol32 qc;
-            float colscale, mrun = kNegInf, lrun = 0.f;
-            int trow;
-            bool rvalid;
-            load_q32<DT>(a, it, t0, rows_exist, row0, lane, qc, colscale, trow, rvalid);
-            const UMaskRow um =
-                UM ? umask_row(a, it.b, trow, rvalid) : UMaskRow{make_rsrc(nullptr, 0), -1};
-            f32x16 o[4];
+            const int t0 = it.gl * a.X;
+            const int rows_exist = min(a.X, it.storage - t0) * a.G;
+            const int row_base = st * R;
+            if (row_base < rows_exist) {
+                const KvSeq kv = kv_seq<LAYOUT>(a, it.b);
+                const int skv = kv.len;
+                const int off = diag_off(a, skv, it.sq);
+                const int row0 = row_base + wave * 32;
+                QCol32 qc;
+                float colscale, mrun = kNegInf, lrun = 0.f;
+                int trow;
+                bool rvalid;
+                load_q32<DT>(a, it, t0, rows_exist, row0, lane, qc, colscale, trow, rvalid);
+                const UMaskRow um =
+                    UM ? umask_row(a, it.b, trow, rvalid) : UMaskRow{make_rsrc(nullptr, 0), -1};
+                f32x16 o[4];
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt) o[dt] = (f32x16){};
-            const int t_lo = t0 + row_base / a.G;
-            const int t_hi = t0 + (min(row_base + R, rows_exist) - 1) / a.G;
-            const int32_t* sel = a.idx + ((int64_t)it.n2 * a.tqb + g) * a.topK;
-            const int64_t head_off = (int64_t)it.n2 * 128 * esz;
+                for (int dt = 0; dt < 4; ++dt) o[dt] = (f32x16){};
+                const int t_lo = t0 + row_base / a.G;
+                const int t_hi = t0 + (min(row_base + R, rows_exist) - 1) / a.G;
+                const int32_t* sel = a.idx + ((int64_t)it.n2 * a.tqb + g) * a.topK;
+                const int64_t head_off = (int64_t)it.n2 * 128 * esz;
 
-            // ---- visible pages of this task's selection range, compacted in order ---------
-            if (wave == 0) {
-                int n = 0;
-                for (int c0 = sa; c0 < se; c0 += 64) {
-                    int jl = -1, pl = 0, cl = 0;
-                    if (c0 + lane < se) {
-                        jl = sel[c0 + lane];
-                        if (jl >= 0) {
-                            cl = block_class(a, (int64_t)jl * 128, skv, off, t_lo, t_hi);
-                            if (cl != 0) pl = kv.unit<LAYOUT>(jl);
+                // ---- visible pages of this task's selection range, compacted in order ---------
+                if (wave == 0) {
+                    int n = 0;
+                    for (int c0 = sa; c0 < se; c0 += 64) {
+                        int jl = -1, pl = 0, cl = 0;
+                        if (c0 + lane < se) {
+                            jl = sel[c0 + lane];
+                            if (jl >= 0) {
+                                cl = block_class(a, (int64_t)jl * 128, skv, off, t_lo, t_hi);
+                                if (cl != 0) pl = kv.unit<LAYOUT>(jl);
+                            }
                         }
+                        const uint64_t m = __ballot(cl != 0);
+                        if (cl != 0) {
+                            const int pos = n + __builtin_amdgcn_mbcnt_hi(
+                                                    (uint32_t)(m >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+                            plist[pos] = make_int4(pl, jl * 4 + cl,
+                                                   kv_records(rs, skv - 128 * jl),
+                                                   kv_records(rs, skv - 128 * jl - 64));
+                        }
+                        n += __builtin_popcountll(m);
                     }
-                    const uint64_t m = __ballot(cl != 0);
-                    if (cl != 0) {
-                        const int pos = n + __builtin_amdgcn_mbcnt_hi(
-                                                (uint32_t)(m >> 32),
-                                                __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-                        plist[pos] = make_int4(pl, jl * 4 + cl,
-                                               kv_records(rs, skv - 128 * jl),
-                                               kv_records(rs, skv - 128 * jl - 64));
-                    }
-                    n += __builtin_popcountll(m);
-                }
-                if (lane == 0) flag[0] = n;
-            }
-            __syncthreads();
-            const int nh = 2 * __builtin_amdgcn_readfirstlane(flag[0]);  // half pages
-
-            // address of half page q (K or V) of this head in HBM
-            auto half_src = [&](const unsigned char* base, int q) {
-                const int4 e = plist[q >> 1];
-                const int unit = __builtin_amdgcn_readfirstlane(e.x);
-                const int rec = __builtin_amdgcn_readfirstlane((q & 1) ? e.w : e.z);
-                return KvSrc{base + (int64_t)unit * a.kv_stride * esz + head_off +
-                                 (q & 1) * 64 * rs,
-                             rec};
-            };
-            if (nh > 0) {
-                f32x16 s[2];
-                u32x4 p[4];  // P^T of the last softmax item, as PV B operands
-                {  // K_0 by the whole workgroup before the first slot
-                    PageRegs<DT, 512, 64> pr0;
-                    page_load<DT, 512, 64>(pr0, half_src(kbase, 0), rs, tid);
-                    store_k<DT, 512, 64>(pr0, kst, tid);
+                    if (lane == 0) flag[0] = n;
                 }
                 __syncthreads();
-                // Each group's share of the KV stream is loaded one softmax item ahead of its
-                // store, so the load latency spans an MFMA and a softmax item. Softmax item k
-                // stores V_k (group 0) or K_{k+2} (group 1) into buffer k % 2. Past the end of
-                // the stream the index is clamped: group 1 then rewrites a K half that nobody
-                // reads again, and the last load is simply not stored.
-                auto move_half = [&](int k) { return min(grp == 0 ? k : k + 2, nh - 1); };
-                PageRegs<DT, 256, 64> pr;  // the group's next move, in flight
-                if (grp == 1) {            // group 1 starts one slot late: K_1 moves meanwhile
-                    PageRegs<DT, 256, 64> pr1;
-                    page_load<DT, 256, 64>(pr1, half_src(kbase, 1), rs, tg);
-                    page_load<DT, 256, 64>(pr, half_src(kbase, move_half(0)), rs, tg);
-                    store_k<DT, 256, 64>(pr1, kst + KB, tg);
-                    __syncthreads();
-                } else {
-                    page_load<DT, 256, 64>(pr, half_src(vbase, move_half(0)), rs, tg);
-                }
-                // page-list entries for the next softmax item, read before its LDS stores are
-                // queued (a wait on the list read would otherwise also wait for the stores)
-                int jc_next = __builtin_amdgcn_readfirstlane(plist[0].y);
-                uint32_t umw[8];  // user-mask words of the next softmax item
-                const int4 m1 = plist[move_half(1) >> 1];
-                int mv_page = __builtin_amdgcn_readfirstlane(m1.x);
-                int mv_rec = __builtin_amdgcn_readfirstlane((move_half(1) & 1) ? m1.w : m1.z);
-                auto softmax_and_move = [&](int k) {
-                    const int jc = jc_next;
-                    if constexpr (DT == kFP8) {  // V is widened to bf16 on its way into LDS
-                        if (grp == 0)
-                            store_v<DT, 256, 64>(pr, vst + (k & 1) * VB, tg);
-                        else
-                            store_k<DT, 256, 64>(pr, kst + (k & 1) * KB, tg);
-                    } else if constexpr (kSharedPitch) {  // one store for both groups
-                        store_k<DT, 256, 64>(pr, grp == 0 ? vst + (k & 1) * VB : kst + (k & 1) * KB, tg);
-                    } else {
-                        if (grp == 0)
-                            store_v<DT, 256, 64>(pr, vst + (k & 1) * VB, tg);
-                        else
-                            store_k<DT, 256, 64>(pr, kst + (k & 1) * KB, tg);
-                    }
-                    {
-                        const int q = move_half(k + 1);
-                        const KvSrc src{(grp == 0 ? vbase : kbase) +
-                                            (int64_t)mv_page * a.kv_stride * esz + head_off +
-                                            (q & 1) * 64 * rs,
-                                        mv_rec};
-                        page_load<DT, 256, 64>(pr, src, rs, tg);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                    softmax_item32<DT, UM>(a, s, p, colscale, trow, umw, jc >> 2, k & 1, jc & 3,
-                                           skv, off, lane, mrun, lrun, o);
-                    pin_softmax(p, lrun);
-                    __builtin_amdgcn_sched_barrier(0);
-                    const int jn = plist[min(k + 1, nh - 1) >> 1].y;
-                    const int qn = move_half(k + 2);
-                    const int4 mn = plist[qn >> 1];
-                    __syncthreads();
-                    jc_next = __builtin_amdgcn_readfirstlane(jn);
-                    mv_page = __builtin_amdgcn_readfirstlane(mn.x);
-                    mv_rec = __builtin_amdgcn_readfirstlane((qn & 1) ? mn.w : mn.z);
+                const int nh = 2 * __builtin_amdgcn_readfirstlane(flag[0]);  // half pages
+
+                // address of half page q (K or V) of this head in HBM
+                auto half_src = [&](const unsigned char* base, int q) {
+                    const int4 e = plist[q >> 1];
+                    const int unit = __builtin_amdgcn_readfirstlane(e.x);
+                    const int rec = __builtin_amdgcn_readfirstlane((q & 1) ? e.w : e.z);
+                    return KvSrc{base + (int64_t)unit * a.kv_stride * esz + head_off +
+                                     (q & 1) * 64 * rs,
+                                 rec};
                 };
-                if constexpr (UM) umask_words32(a, um, jc_next >> 2, 0, lane, umw);
-                mfma_item32<DT, true, false>(kst, vst, qc, s, p, o, lane);
-                __syncthreads();
-                softmax_and_move(0);
-                for (int k = 1; k < nh; ++k) {
-                    if constexpr (UM) umask_words32(a, um, jc_next >> 2, k & 1, lane, umw);
-                    mfma_item32<DT, true, true>(kst + (k & 1) * KB, vst + ((k - 1) & 1) * VB, qc, s,
-                                                p, o, lane);
+                if (nh > 0) {
+                    f32x16 s[2];
+                    u32x4 p[4];  // P^T of the last softmax item, as PV B operands
+                    {  // K_0 by the whole workgroup before the first slot
+                        PageRegs<DT, 512, 64> pr0;
+                        page_load<DT, 512, 64>(pr0, half_src(kbase, 0), rs, tid);
+                        store_k<DT, 512, 64>(pr0, kst, tid);
+                    }
                     __syncthreads();
-                    softmax_and_move(k);
+                    // Each group's share of the KV stream is loaded one softmax item ahead of its
+                    // store, so the load latency spans an MFMA and a softmax item. Softmax item k
+                    // stores V_k (group 0) or K_{k+2} (group 1) into buffer k % 2. Past the end of
+                    // the stream the index is clamped: group 1 then rewrites a K half that nobody
+                    // reads again, and the last load is simply not stored.
+                    auto move_half = [&](int k) { return min(grp == 0 ? k : k + 2, nh - 1); };
+                    PageRegs<DT, 256, 64> pr;  // the group's next move, in flight
+                    if (grp == 1) {            // group 1 starts one slot late: K_1 moves meanwhile
+                        PageRegs<DT, 256, 64> pr1;
+                        page_load<DT, 256, 64>(pr1, half_src(kbase, 1), rs, tg);
+                        page_load<DT, 256, 64>(pr, half_src(kbase, move_half(0)), rs, tg);
+                        store_k<DT, 256, 64>(pr1, kst + KB, tg);
+                        __syncthreads();
+                    } else {
+                        page_load<DT, 256, 64>(pr, half_src(vbase, move_half(0)), rs, tg);
+                    }
+                    // page-list entries for the next softmax item, read before its LDS stores are
+                    // queued (a wait on the list read would otherwise also wait for the stores)
+                    int jc_next = __builtin_amdgcn_readfirstlane(plist[0].y);
+                    uint32_t umw[8];  // user-mask words of the next softmax item
+                    const int4 m1 = plist[move_half(1) >> 1];
+                    int mv_page = __builtin_amdgcn_readfirstlane(m1.x);
+                    int mv_rec = __builtin_amdgcn_readfirstlane((move_half(1) & 1) ? m1.w : m1.z);
+                    auto softmax_and_move = [&](int k) {
+                        const int jc = jc_next;
+                        if constexpr (DT == kFP8) {  // V is widened to bf16 on its way into LDS
+                            if (grp == 0)
+                                store_v<DT, 256, 64>(pr, vst + (k & 1) * VB, tg);
+                            else
+                                store_k<DT, 256, 64>(pr, kst + (k & 1) * KB, tg);
+                        } else if constexpr (kSharedPitch) {  // one store for both groups
+                            store_k<DT, 256, 64>(pr, grp == 0 ? vst + (k & 1) * VB : kst + (k & 1) * KB, tg);
+                        } else {
+                            if (grp == 0)
+                                store_v<DT, 256, 64>(pr, vst + (k & 1) * VB, tg);
+                            else
+                                store_k<DT, 256, 64>(pr, kst + (k & 1) * KB, tg);
+                        }
+                        {
+                            const int q = move_half(k + 1);
+                            const KvSrc src{(grp == 0 ? vbase : kbase) +
+                                                (int64_t)mv_page * a.kv_stride * esz + head_off +
+                                                (q & 1) * 64 * rs,
+                                            mv_rec};
+                            page_load<DT, 256, 64>(pr, src, rs, tg);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                        softmax_item32<DT, UM>(a, s, p, colscale, trow, umw, jc >> 2, k & 1, jc & 3,
+                                               skv, off, lane, mrun, lrun, o);
+                        pin_softmax(p, lrun);
+                        __builtin_amdgcn_sched_barrier(0);
+                        const int jn = plist[min(k + 1, nh - 1) >> 1].y;
+                        const int qn = move_half(k + 2);
+                        const int4 mn = plist[qn >> 1];
+                        __syncthreads();
+                        jc_next = __builtin_amdgcn_readfirstlane(jn);
+                        mv_page = __builtin_amdgcn_readfirstlane(mn.x);
+                        mv_rec = __builtin_amdgcn_readfirstlane((qn & 1) ? mn.w : mn.z);
+                    };
+                    if constexpr (UM) umask_words32(a, um, jc_next >> 2, 0, lane, umw);
+                    mfma_item32<DT, true, false>(kst, vst, qc, s, p, o, lane);
+                    __syncthreads();
+                    softmax_and_move(0);
+                    for (int k = 1; k < nh; ++k) {
+                        if constexpr (UM) umask_words32(a, um, jc_next >> 2, k & 1, lane, umw);
+                        mfma_item32<DT, true, true>(kst + (k & 1) * KB, vst + ((k - 1) & 1) * VB, qc, s,
+                                                    p, o, lane);
+                        __syncthreads();
+                        softmax_and_move(k);
+                    }
+                    mfma_item32<DT, false, true>(kst, vst + ((nh - 1) & 1) * VB, qc, s, p, o, lane);
+                    if (grp == 0) __syncthreads();
                 }
-                mfma_item32<DT, false, true>(kst, vst + ((nh - 1) & 1) * VB, qc, s, p, o, lane);
-                if (grp == 0) __syncthreads();
-            }
-            __syncthreads();  // LDS (stages, page list) is reused by the next task
+                __syncthreads();  // LDS (stages, page list) is reused by the next task
 
-            write_rows32<DT, OUT>(a, it, complete, 2 * w + (sa > 0 ? 0 : 1), row0, lane, trow, rvalid,
-                                  mrun, lrun, o);
-            if (!complete) {
-                int* list = (int*)smem;  // the stages are free until the next task
-                const int np = piece_arrive(a, w, u, st, a.nst, list);
-                if (np > 0)
-                    merge_rows<OUT>(a, list, np, row_base, min(row_base + R, rows_exist), it.n2,
-                                    t0, it.row0, it.sq);
-                __syncthreads();
+                write_rows32<DT, OUT>(a, it, complete, 2 * w + (sa > 0 ? 0 : 1), row0, lane, trow, rvalid,
+                                      mrun, lrun, o);
+                if (!complete) {
+                    int* list = (int*)smem;  // the stages are free until the next task
+                    const int np = piece_arrive(a, w, u, st, a.nst, list);
+                    if (np > 0)
+                        merge_rows<OUT>(a, list, np, row_base, min(row_base + R, rows_exist), it.n2,
+                                        t0, it.row0, it.sq);
+                    __syncthreads();
+                }
             }
+            advance_unit(a, it);
         }
-        advance_unit(a, it);
-    }
+    });
 }
 
 
@@ -1201,196 +1205,197 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32d_kernel(FwdArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int grp = wave >> 2;
     const int gw = wave & 3;  // wave within its group
-    const int lin = xcd_remap(blockIdx.x, gridDim.x);
-    const int w = lin / a.nst, st = lin - (lin / a.nst) * a.nst;
-
     if (!header_ok(a)) {
         refuse(a);
         return;
     }
-    const Bound b0 = read_bound(a.meta, w), b1 = read_bound(a.meta, w + 1);
     const int U = a.meta[3];
-    if (!bound_less(b0, b1) || b0.u >= U) return;
-    UnitIter it = locate_unit(a, b0.u);
-    if (it.b < 0) return;
+    __shared__ int task_word[2];
+    run_tasks<!UM>(a, U, task_word, [&](const FwdArgs& a, const Task& tk) {
+        const int w = tk.w, st = tk.st;
+        const Bound b0 = tk.b0, b1 = tk.b1;
+        if (!bound_less(b0, b1) || b0.u >= U) return;
+        UnitIter it = locate_unit(a, b0.u);
+        if (it.b < 0) return;
 
-    const int rs = a.N2 * 128 * esz;
-    const unsigned char* kbase = (const unsigned char*)a.k;
-    const unsigned char* vbase = (const unsigned char*)a.v;
-    unsigned char* const kst = smem;
-    unsigned char* const vst = smem + 4 * kDmaHalf;
+        const int rs = a.N2 * 128 * esz;
+        const unsigned char* kbase = (const unsigned char*)a.k;
+        const unsigned char* vbase = (const unsigned char*)a.v;
+        unsigned char* const kst = smem;
+        unsigned char* const vst = smem + 4 * kDmaHalf;
 
-    for (int u = b0.u;; ++u) {
-        const int sa = (u == b0.u) ? b0.s : 0;
-        if (u >= U || u > b1.u || (u == b1.u && sa >= b1.s)) break;
-        const int g = it.qbase + it.gl;
-        int cnt = 0;
-        if (g < a.tqb) cnt = min(max(a.cnt[(int64_t)it.n2 * a.tqb + g], 0), a.topK);
-        const int se = (u == b1.u) ? b1.s : cnt;
-        const bool complete = (sa == 0) && (se == cnt);
+        for (int u = b0.u;; ++u) {
+            const int sa = (u == b0.u) ? b0.s : 0;
+            if (u >= U || u > b1.u || (u == b1.u && sa >= b1.s)) break;
+            const int g = it.qbase + it.gl;
+            int cnt = 0;
+            if (g < a.tqb) cnt = min(max(a.cnt[(int64_t)it.n2 * a.tqb + g], 0), a.topK);
+            const int se = (u == b1.u) ? b1.s : cnt;
+            const bool complete = (sa == 0) && (se == cnt);
 
-        const int t0 = it.gl * a.X;
-        const int rows_exist = min(a.X, it.storage - t0) * a.G;
-        const int row_base = st * R;
-        if (row_base < rows_exist) {
-            const KvSeq kv = kv_seq<LAYOUT>(a, it.b);
-            const int skv = kv.len;
-            const int off = diag_off(a, skv, it.sq);
-            const int row0 = row_base + wave * 32;
-            QCol32 qc;
-            float colscale, mrun = kNegInf, lrun = 0.f;
-            int trow;
-            bool rvalid;
-            load_q32<DT>(a, it, t0, rows_exist, row0, lane, qc, colscale, trow, rvalid);
-            const UMaskRow um =
-                UM ? umask_row(a, it.b, trow, rvalid) : UMaskRow{make_rsrc(nullptr, 0), -1};
-            f32x16 o[4];
+            const int t0 = it.gl * a.X;
+            const int rows_exist = min(a.X, it.storage - t0) * a.G;
+            const int row_base = st * R;
+            if (row_base < rows_exist) {
+                const KvSeq kv = kv_seq<LAYOUT>(a, it.b);
+                const int skv = kv.len;
+                const int off = diag_off(a, skv, it.sq);
+                const int row0 = row_base + wave * 32;
+                QCol32 qc;
+                float colscale, mrun = kNegInf, lrun = 0.f;
+                int trow;
+                bool rvalid;
+                load_q32<DT>(a, it, t0, rows_exist, row0, lane, qc, colscale, trow, rvalid);
+                const UMaskRow um =
+                    UM ? umask_row(a, it.b, trow, rvalid) : UMaskRow{make_rsrc(nullptr, 0), -1};
+                f32x16 o[4];
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt) o[dt] = (f32x16){};
-            const int t_lo = t0 + row_base / a.G;
-            const int t_hi = t0 + (min(row_base + R, rows_exist) - 1) / a.G;
-            const int32_t* sel = a.idx + ((int64_t)it.n2 * a.tqb + g) * a.topK;
-            const int64_t head_off = (int64_t)it.n2 * 128 * esz;
+                for (int dt = 0; dt < 4; ++dt) o[dt] = (f32x16){};
+                const int t_lo = t0 + row_base / a.G;
+                const int t_hi = t0 + (min(row_base + R, rows_exist) - 1) / a.G;
+                const int32_t* sel = a.idx + ((int64_t)it.n2 * a.tqb + g) * a.topK;
+                const int64_t head_off = (int64_t)it.n2 * 128 * esz;
 
-            if (wave == 0) {
-                int n = 0;
-                for (int c0 = sa; c0 < se; c0 += 64) {
-                    int jl = -1, pl = 0, cl = 0;
-                    if (c0 + lane < se) {
-                        jl = sel[c0 + lane];
-                        if (jl >= 0) {
-                            cl = block_class(a, (int64_t)jl * 128, skv, off, t_lo, t_hi);
-                            if (cl != 0) pl = kv.unit<LAYOUT>(jl);
+                if (wave == 0) {
+                    int n = 0;
+                    for (int c0 = sa; c0 < se; c0 += 64) {
+                        int jl = -1, pl = 0, cl = 0;
+                        if (c0 + lane < se) {
+                            jl = sel[c0 + lane];
+                            if (jl >= 0) {
+                                cl = block_class(a, (int64_t)jl * 128, skv, off, t_lo, t_hi);
+                                if (cl != 0) pl = kv.unit<LAYOUT>(jl);
+                            }
                         }
+                        const uint64_t mm = __ballot(cl != 0);
+                        if (cl != 0) {
+                            const int pos = n + __builtin_amdgcn_mbcnt_hi(
+                                                    (uint32_t)(mm >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mm, 0));
+                            const uint64_t po = (uint64_t)((int64_t)pl * a.kv_stride * esz + head_off);
+                            plist[pos] = (u32x4){(uint32_t)po, (uint32_t)(po >> 32),
+                                                 (uint32_t)kv_records(rs, skv - 128 * jl),
+                                                 (uint32_t)kv_records(rs, skv - 128 * jl - 64)};
+                            jlist[pos] = jl * 4 + cl;
+                        }
+                        n += __builtin_popcountll(mm);
                     }
-                    const uint64_t mm = __ballot(cl != 0);
-                    if (cl != 0) {
-                        const int pos = n + __builtin_amdgcn_mbcnt_hi(
-                                                (uint32_t)(mm >> 32),
-                                                __builtin_amdgcn_mbcnt_lo((uint32_t)mm, 0));
-                        const uint64_t po = (uint64_t)((int64_t)pl * a.kv_stride * esz + head_off);
-                        plist[pos] = (u32x4){(uint32_t)po, (uint32_t)(po >> 32),
-                                             (uint32_t)kv_records(rs, skv - 128 * jl),
-                                             (uint32_t)kv_records(rs, skv - 128 * jl - 64)};
-                        jlist[pos] = jl * 4 + cl;
-                    }
-                    n += __builtin_popcountll(mm);
+                    if (lane == 0) flag[0] = n;
                 }
-                if (lane == 0) flag[0] = n;
-            }
-            __syncthreads();
-            const int nh = 2 * __builtin_amdgcn_readfirstlane(flag[0]);  // half pages
+                __syncthreads();
+                const int nh = 2 * __builtin_amdgcn_readfirstlane(flag[0]);  // half pages
 
-            // half page q (clamped into the stream) of K or V of this head
-            auto half_src = [&](const unsigned char* base, int q) {
-                q = min(q, nh - 1);
-                return page_half(base, plist[q >> 1], q & 1, rs);
-            };
-            if (nh > 0) {
-                f32x16 s[2];
-                u32x4 p[4];
-                // Readers: MFMA item k reads K_k (K buffer k % 4) and V_{k-1} (V buffer
-                // (k - 1) % 4); group 0 runs it in slot 2 k, group 1 in slot 2 k + 1.
-                // Writers (each group's four waves issue four DMA instructions each): group 0
-                // moves V_{k+1}, group 1 K_{k+3}, during their MFMA item k (without a user
-                // mask: the wave has issue slots to spare between its MFMAs) or else at the
-                // end of their softmax item k, a slot later. Either way a move lands in a
-                // buffer whose last reader is past a barrier, and a wave lets only its newest
-                // batch stay in flight across a barrier, so every batch has two slots to land
-                // before its first reader. (With a user mask, the compiler's own vmcnt waits
-                // for the mask words would also wait for DMA issued after them.)
-                // Before the first slot: K_0 by all eight waves, K_1 and V_0 by group 1
-                // and 0, and K_2 by group 1 in its first slot.
-                // Issue priority: the two waves on a SIMD compete for instruction issue, and
-                // the older one wins ties. Unless its MFMAs go out as soon as the matrix pipe
-                // frees, the pipe idles while the softmax wave issues; so the MFMA item runs
-                // at raised priority and the softmax item takes the remaining issue cycles
-                // (without the raise, the slots where the younger group does its MFMA item
-                // ran about 40 % longer).
-                dma_half16(half_src(kbase, 0), rs, kst, 2 * wave, 2, lane);
-                if (grp == 1)
-                    dma_half16(half_src(kbase, 1), rs, kst + kDmaHalf, 4 * gw, 4, lane);
-                else
-                    dma_half16(half_src(vbase, 0), rs, vst, 4 * gw, 4, lane);
-                wait_vm<0>();
-                __syncthreads();
-                if (grp == 1) {  // group 1 starts one slot late; its K_2 move goes out now
-                    dma_half16(half_src(kbase, 2), rs, kst + 2 * kDmaHalf, 4 * gw, 4, lane);
-                    __syncthreads();
-                }
-                int jc_next = __builtin_amdgcn_readfirstlane(jlist[0]);
-                constexpr bool kItemMove = !UM;
-                auto raise = [] { if constexpr (kItemMove) __builtin_amdgcn_s_setprio(3); };
-                auto lower = [] { if constexpr (kItemMove) __builtin_amdgcn_s_setprio(0); };
-                auto move_of = [&](int k) {
-                    const int q = min(grp == 0 ? k + 1 : k + 3, nh - 1);
-                    return ItemMove{plist + (q >> 1), q & 1, grp == 0 ? vbase : kbase,
-                                    grp == 0 ? vst + ((k + 1) & 3) * kDmaHalf
-                                             : kst + ((k + 3) & 3) * kDmaHalf,
-                                    4 * gw};
+                // half page q (clamped into the stream) of K or V of this head
+                auto half_src = [&](const unsigned char* base, int q) {
+                    q = min(q, nh - 1);
+                    return page_half(base, plist[q >> 1], q & 1, rs);
                 };
-                uint32_t umw[8];  // user-mask words of the next softmax item
-                auto softmax_and_move = [&](int k) {
-                    const int jc = jc_next;
-                    __builtin_amdgcn_sched_barrier(0);
-                    softmax_item32<DT, UM>(a, s, p, colscale, trow, umw, jc >> 2, k & 1, jc & 3,
-                                           skv, off, lane, mrun, lrun, o);
-                    pin_softmax(p, lrun);
-                    __builtin_amdgcn_sched_barrier(0);
-                    if constexpr (!kItemMove) {  // group 0 V_{k+1}, group 1 K_{k+3}
-                        if (grp == 0)
-                            dma_half16(half_src(vbase, k + 1), rs,
-                                       vst + ((k + 1) & 3) * kDmaHalf, 4 * gw, 4, lane);
-                        else
-                            dma_half16(half_src(kbase, k + 3), rs,
-                                       kst + ((k + 3) & 3) * kDmaHalf, 4 * gw, 4, lane);
+                if (nh > 0) {
+                    f32x16 s[2];
+                    u32x4 p[4];
+                    // Readers: MFMA item k reads K_k (K buffer k % 4) and V_{k-1} (V buffer
+                    // (k - 1) % 4); group 0 runs it in slot 2 k, group 1 in slot 2 k + 1.
+                    // Writers (each group's four waves issue four DMA instructions each): group 0
+                    // moves V_{k+1}, group 1 K_{k+3}, during their MFMA item k (without a user
+                    // mask: the wave has issue slots to spare between its MFMAs) or else at the
+                    // end of their softmax item k, a slot later. Either way a move lands in a
+                    // buffer whose last reader is past a barrier, and a wave lets only its newest
+                    // batch stay in flight across a barrier, so every batch has two slots to land
+                    // before its first reader. (With a user mask, the compiler's own vmcnt waits
+                    // for the mask words would also wait for DMA issued after them.)
+                    // Before the first slot: K_0 by all eight waves, K_1 and V_0 by group 1
+                    // and 0, and K_2 by group 1 in its first slot.
+                    // Issue priority: the two waves on a SIMD compete for instruction issue, and
+                    // the older one wins ties. Unless its MFMAs go out as soon as the matrix pipe
+                    // frees, the pipe idles while the softmax wave issues; so the MFMA item runs
+                    // at raised priority and the softmax item takes the remaining issue cycles
+                    // (without the raise, the slots where the younger group does its MFMA item
+                    // ran about 40 % longer).
+                    dma_half16(half_src(kbase, 0), rs, kst, 2 * wave, 2, lane);
+                    if (grp == 1)
+                        dma_half16(half_src(kbase, 1), rs, kst + kDmaHalf, 4 * gw, 4, lane);
+                    else
+                        dma_half16(half_src(vbase, 0), rs, vst, 4 * gw, 4, lane);
+                    wait_vm<0>();
+                    __syncthreads();
+                    if (grp == 1) {  // group 1 starts one slot late; its K_2 move goes out now
+                        dma_half16(half_src(kbase, 2), rs, kst + 2 * kDmaHalf, 4 * gw, 4, lane);
+                        __syncthreads();
                     }
-                    const int jn = jlist[min(k + 1, nh - 1) >> 1];
-                    wait_vm<4>();  // all but this item's batch are in LDS
-                    __syncthreads();
-                    jc_next = __builtin_amdgcn_readfirstlane(jn);
-                };
-                if constexpr (UM) umask_words32(a, um, jc_next >> 2, 0, lane, umw);
-                raise();
-                mfma_item32d<DT, true, false, kItemMove>(kst, vst, qc, s, p, o, lane, move_of(0),
-                                                         rs);
-                lower();
-                wait_vm<UM ? 12 : 4>();
-                __syncthreads();
-                softmax_and_move(0);
-                for (int k = 1; k < nh; ++k) {
-                    if constexpr (UM) umask_words32(a, um, jc_next >> 2, k & 1, lane, umw);
+                    int jc_next = __builtin_amdgcn_readfirstlane(jlist[0]);
+                    constexpr bool kItemMove = !UM;
+                    auto raise = [] { if constexpr (kItemMove) __builtin_amdgcn_s_setprio(3); };
+                    auto lower = [] { if constexpr (kItemMove) __builtin_amdgcn_s_setprio(0); };
+                    auto move_of = [&](int k) {
+                        const int q = min(grp == 0 ? k + 1 : k + 3, nh - 1);
+                        return ItemMove{plist + (q >> 1), q & 1, grp == 0 ? vbase : kbase,
+                                        grp == 0 ? vst + ((k + 1) & 3) * kDmaHalf
+                                                 : kst + ((k + 3) & 3) * kDmaHalf,
+                                        4 * gw};
+                    };
+                    uint32_t umw[8];  // user-mask words of the next softmax item
+                    auto softmax_and_move = [&](int k) {
+                        const int jc = jc_next;
+                        __builtin_amdgcn_sched_barrier(0);
+                        softmax_item32<DT, UM>(a, s, p, colscale, trow, umw, jc >> 2, k & 1, jc & 3,
+                                               skv, off, lane, mrun, lrun, o);
+                        pin_softmax(p, lrun);
+                        __builtin_amdgcn_sched_barrier(0);
+                        if constexpr (!kItemMove) {  // group 0 V_{k+1}, group 1 K_{k+3}
+                            if (grp == 0)
+                                dma_half16(half_src(vbase, k + 1), rs,
+                                           vst + ((k + 1) & 3) * kDmaHalf, 4 * gw, 4, lane);
+                            else
+                                dma_half16(half_src(kbase, k + 3), rs,
+                                           kst + ((k + 3) & 3) * kDmaHalf, 4 * gw, 4, lane);
+                        }
+                        const int jn = jlist[min(k + 1, nh - 1) >> 1];
+                        wait_vm<4>();  // all but this item's batch are in LDS
+                        __syncthreads();
+                        jc_next = __builtin_amdgcn_readfirstlane(jn);
+                    };
+                    if constexpr (UM) umask_words32(a, um, jc_next >> 2, 0, lane, umw);
                     raise();
-                    mfma_item32d<DT, true, true, kItemMove>(kst + (k & 3) * kDmaHalf,
-                                                            vst + ((k - 1) & 3) * kDmaHalf, qc, s,
-                                                            p, o, lane, move_of(k), rs);
+                    mfma_item32d<DT, true, false, kItemMove>(kst, vst, qc, s, p, o, lane, move_of(0),
+                                                             rs);
                     lower();
                     wait_vm<UM ? 12 : 4>();
                     __syncthreads();
-                    softmax_and_move(k);
+                    softmax_and_move(0);
+                    for (int k = 1; k < nh; ++k) {
+                        if constexpr (UM) umask_words32(a, um, jc_next >> 2, k & 1, lane, umw);
+                        raise();
+                        mfma_item32d<DT, true, true, kItemMove>(kst + (k & 3) * kDmaHalf,
+                                                                vst + ((k - 1) & 3) * kDmaHalf, qc, s,
+                                                                p, o, lane, move_of(k), rs);
+                        lower();
+                        wait_vm<UM ? 12 : 4>();
+                        __syncthreads();
+                        softmax_and_move(k);
+                    }
+                    raise();
+                    mfma_item32d<DT, false, true>(kst, vst + ((nh - 1) & 3) * kDmaHalf, qc, s, p, o,
+                                                  lane);
+                    lower();
+                    wait_vm<0>();  // nothing may land in LDS after the task
+                    if (grp == 0) __syncthreads();
                 }
-                raise();
-                mfma_item32d<DT, false, true>(kst, vst + ((nh - 1) & 3) * kDmaHalf, qc, s, p, o,
-                                              lane);
-                lower();
-                wait_vm<0>();  // nothing may land in LDS after the task
-                if (grp == 0) __syncthreads();
-            }
-            __syncthreads();
-
-            write_rows32<DT, OUT>(a, it, complete, 2 * w + (sa > 0 ? 0 : 1), row0, lane, trow,
-                                  rvalid, mrun, lrun, o);
-            if (!complete) {
-                int* list = (int*)smem;
-                const int np = piece_arrive(a, w, u, st, a.nst, list);
-                if (np > 0)
-                    merge_rows<OUT>(a, list, np, row_base, min(row_base + R, rows_exist), it.n2,
-                                    t0, it.row0, it.sq);
                 __syncthreads();
+
+                write_rows32<DT, OUT>(a, it, complete, 2 * w + (sa > 0 ? 0 : 1), row0, lane, trow,
+                                      rvalid, mrun, lrun, o);
+                if (!complete) {
+                    int* list = (int*)smem;
+                    const int np = piece_arrive(a, w, u, st, a.nst, list);
+                    if (np > 0)
+                        merge_rows<OUT>(a, list, np, row_base, min(row_base + R, rows_exist), it.n2,
+                                        t0, it.row0, it.sq);
+                    __syncthreads();
+                }
             }
+            advance_unit(a, it);
         }
-        advance_unit(a, it);
-    }
+    });
 }
 
 
@@ -1427,241 +1432,261 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32_kernel(FwdArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int grp = wave >> 2;  // waves w and w + 4 share a SIMD and the same query rows
     const int tg = tid & 255;
-    const int lin = xcd_remap(blockIdx.x, gridDim.x);
-    const int w = lin / a.nst, st = lin - (lin / a.nst) * a.nst;
-
     if (!header_ok(a)) {
         refuse(a);
         return;
     }
-    const Bound b0 = read_bound(a.meta, w), b1 = read_bound(a.meta, w + 1);
     const int U = a.meta[3];
-    if (!bound_less(b0, b1) || b0.u >= U) return;
-    UnitIter it = locate_unit(a, b0.u);
-    if (it.b < 0) return;
+    __shared__ int task_word[2];
+    run_tasks<!UM>(a, U, task_word, [&](const FwdArgs& a, const Task& tk) {
+        const int w = tk.w, st = tk.st;
+        const Bound b0 = tk.b0, b1 = tk.b1;
+        if (!bound_less(b0, b1) || b0.u >= U) return;
+        UnitIter it = locate_unit(a, b0.u);
+        if (it.b < 0) return;
 
-    const int rs = a.N2 * 128 * esz;
-    const unsigned char* kbase = (const unsigned char*)a.k;
-    const unsigned char* vbase = (const unsigned char*)a.v;
-    unsigned char* const kst = smem;
-    unsigned char* const vst = smem + 2 * KB;
+        const int rs = a.N2 * 128 * esz;
+        const unsigned char* kbase = (const unsigned char*)a.k;
+        const unsigned char* vbase = (const unsigned char*)a.v;
+        unsigned char* const kst = smem;
+        unsigned char* const vst = smem + 2 * KB;
 
-    for (int u = b0.u;; ++u) {
-        const int sa = (u == b0.u) ? b0.s : 0;
-        if (u >= U || u > b1.u || (u == b1.u && sa >= b1.s)) break;
-        const int g = it.qbase + it.gl;
-        int cnt = 0;
-        if (g < a.tqb) cnt = min(max(a.cnt[(int64_t)it.n2 * a.tqb + g], 0), a.topK);
-        const int se = (u == b1.u) ? b1.s : cnt;
-        const bool complete = (sa == 0) && (se == cnt);
+        for (int u = b0.u;; ++u) {
+            const int sa = (u == b0.u) ? b0.s : 0;
+            if (u >= U || u > b1.u || (u == b1.u && sa >= b1.s)) break;
+            const int g = it.qbase + it.gl;
+            int cnt = 0;
+            if (g < a.tqb) cnt = min(max(a.cnt[(int64_t)it.n2 * a.tqb + g], 0), a.topK);
+            const int se = (u == b1.u) ? b1.s : cnt;
+            const bool complete = (sa == 0) && (se == cnt);
 
-        const int t0 = it.gl * a.X;
-        const int rows_exist = min(a.X, it.storage - t0) * a.G;
-        const int row_base = st * R;
-        if (row_base < rows_exist) {
-            const KvSeq kv = kv_seq<LAYOUT>(a, it.b);
-            const int skv = kv.len;
-            const int off = diag_off(a, skv, it.sq);
-            const int row0 = row_base + (wave & 3) * 32;
-            QCol32 qc;
-            float colscale, mrun = kNegInf, lrun = 0.f;
-            int trow;
-            bool rvalid;
-            load_q32<DT>(a, it, t0, rows_exist, row0, lane, qc, colscale, trow, rvalid);
-            const UMaskRow um =
-                UM ? umask_row(a, it.b, trow, rvalid) : UMaskRow{make_rsrc(nullptr, 0), -1};
-            f32x16 o[4];
+            const int t0 = it.gl * a.X;
+            const int rows_exist = min(a.X, it.storage - t0) * a.G;
+            const int row_base = st * R;
+            if (row_base < rows_exist) {
+                const KvSeq kv = kv_seq<LAYOUT>(a, it.b);
+                const int skv = kv.len;
+                const int off = diag_off(a, skv, it.sq);
+                const int row0 = row_base + (wave & 3) * 32;
+                QCol32 qc;
+                float colscale, mrun = kNegInf, lrun = 0.f;
+                int trow;
+                bool rvalid;
+                load_q32<DT>(a, it, t0, rows_exist, row0, lane, qc, colscale, trow, rvalid);
+                const UMaskRow um =
+                    UM ? umask_row(a, it.b, trow, rvalid) : UMaskRow{make_rsrc(nullptr, 0), -1};
+                f32x16 o[4];
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt) o[dt] = (f32x16){};
-            const int t_lo = t0 + row_base / a.G;
-            const int t_hi = t0 + (min(row_base + R, rows_exist) - 1) / a.G;
-            const int32_t* sel = a.idx + ((int64_t)it.n2 * a.tqb + g) * a.topK;
-            const int64_t head_off = (int64_t)it.n2 * 128 * esz;
+                for (int dt = 0; dt < 4; ++dt) o[dt] = (f32x16){};
+                const int t_lo = t0 + row_base / a.G;
+                const int t_hi = t0 + (min(row_base + R, rows_exist) - 1) / a.G;
+                const int32_t* sel = a.idx + ((int64_t)it.n2 * a.tqb + g) * a.topK;
+                const int64_t head_off = (int64_t)it.n2 * 128 * esz;
 
-            if (wave == 0) {
-                int n = 0;
-                for (int c0 = sa; c0 < se; c0 += 64) {
-                    int jl = -1, pl = 0, cl = 0;
-                    if (c0 + lane < se) {
-                        jl = sel[c0 + lane];
-                        if (jl >= 0) {
-                            cl = block_class(a, (int64_t)jl * 128, skv, off, t_lo, t_hi);
-                            if (cl != 0) pl = kv.unit<LAYOUT>(jl);
+                if (wave == 0) {
+                    int n = 0;
+                    for (int c0 = sa; c0 < se; c0 += 64) {
+                        int jl = -1, pl = 0, cl = 0;
+                        if (c0 + lane < se) {
+                            jl = sel[c0 + lane];
+                            if (jl >= 0) {
+                                cl = block_class(a, (int64_t)jl * 128, skv, off, t_lo, t_hi);
+                                if (cl != 0) pl = kv.unit<LAYOUT>(jl);
+                            }
                         }
+                        const uint64_t m = __ballot(cl != 0);
+                        if (cl != 0) {
+                            const int pos = n + __builtin_amdgcn_mbcnt_hi(
+                                                    (uint32_t)(m >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+                            plist[pos] = make_int4(pl, jl * 4 + cl,
+                                                   kv_records(rs, skv - 128 * jl),
+                                                   kv_records(rs, skv - 128 * jl - 64));
+                        }
+                        n += __builtin_popcountll(m);
                     }
-                    const uint64_t m = __ballot(cl != 0);
-                    if (cl != 0) {
-                        const int pos = n + __builtin_amdgcn_mbcnt_hi(
-                                                (uint32_t)(m >> 32),
-                                                __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-                        plist[pos] = make_int4(pl, jl * 4 + cl,
-                                               kv_records(rs, skv - 128 * jl),
-                                               kv_records(rs, skv - 128 * jl - 64));
-                    }
-                    n += __builtin_popcountll(m);
+                    if (lane == 0) flag[0] = n;
                 }
-                if (lane == 0) flag[0] = n;
-            }
-            __syncthreads();
-            const int n = __builtin_amdgcn_readfirstlane(flag[0]);  // items per group
-            const int nh = 2 * n;                                   // half pages
+                __syncthreads();
+                const int n = __builtin_amdgcn_readfirstlane(flag[0]);  // items per group
+                const int nh = 2 * n;                                   // half pages
 
-            // address of half page q (K or V) of this head in HBM; q is clamped into the stream
-            auto half_src = [&](const unsigned char* base, int q) {
-                q = min(max(q, 0), nh - 1);
-                const int4 e = plist[q >> 1];
-                const int unit = __builtin_amdgcn_readfirstlane(e.x);
-                const int rec = __builtin_amdgcn_readfirstlane((q & 1) ? e.w : e.z);
-                return KvSrc{base + (int64_t)unit * a.kv_stride * esz + head_off +
-                                 (q & 1) * 64 * rs,
-                             rec};
-            };
-            if (n > 0) {
-                f32x16 s[2];
-                u32x4 p[4];
-                {  // K_0 by the whole workgroup before the first slot
-                    PageRegs<DT, 512, 64> pr0;
-                    page_load<DT, 512, 64>(pr0, half_src(kbase, 0), rs, tid);
-                    store_k<DT, 512, 64>(pr0, kst, tid);
-                }
-                __syncthreads();
-                if (grp == 1) {  // group 1 starts one slot late: K_1 moves meanwhile
-                    PageRegs<DT, 256, 64> pr1;
-                    page_load<DT, 256, 64>(pr1, half_src(kbase, 1), rs, tg);
-                    store_k<DT, 256, 64>(pr1, kst + KB, tg);
-                    __syncthreads();
-                }
-                unsigned char* const my_k = kst + grp * KB;
-                unsigned char* const my_v = vst + grp * VB;
-                unsigned char* const other_v = vst + (grp ^ 1) * VB;
-                // V of the half page the partner has just exponentiated, into its V buffer
-                auto v_move_store = [&](const PageRegs<DT, 256, 64>& pr) {
-                    if constexpr (DT == kFP8 || !kSharedPitch)
-                        store_v<DT, 256, 64>(pr, other_v, tg);
-                    else
-                        store_k<DT, 256, 64>(pr, other_v, tg);  // same row pitch as K
+                // address of half page q (K or V) of this head in HBM; q is clamped into the stream
+                auto half_src = [&](const unsigned char* base, int q) {
+                    q = min(max(q, 0), nh - 1);
+                    const int4 e = plist[q >> 1];
+                    const int unit = __builtin_amdgcn_readfirstlane(e.x);
+                    const int rec = __builtin_amdgcn_readfirstlane((q & 1) ? e.w : e.z);
+                    return KvSrc{base + (int64_t)unit * a.kv_stride * esz + head_off +
+                                     (q & 1) * 64 * rs,
+                                 rec};
                 };
-                uint32_t umw[8];  // user-mask words of the next softmax item
-                auto mask_words = [&](int k) {
-                    if constexpr (UM)
-                        umask_words32(a, um, __builtin_amdgcn_readfirstlane(plist[k].y) >> 2, grp,
-                                      lane, umw);
-                };
-                auto softmax_and_move = [&](int k) {
-                    const int jc = __builtin_amdgcn_readfirstlane(plist[k].y);
-                    PageRegs<DT, 256, 64> pr;
-                    page_load<DT, 256, 64>(pr, half_src(kbase, 2 * k + 2 + grp), rs, tg);
-                    __builtin_amdgcn_sched_barrier(0);
-                    softmax_item32<DT, UM>(a, s, p, colscale, trow, umw, jc >> 2, grp, jc & 3,
-                                           skv, off, lane, mrun, lrun, o);
-                    pin_softmax(p, lrun);
-                    __builtin_amdgcn_sched_barrier(0);
-                    store_k<DT, 256, 64>(pr, my_k, tg);
-                    __syncthreads();
-                };
-                {
-                    PageRegs<DT, 256, 64> pr;
-                    page_load<DT, 256, 64>(pr, half_src(vbase, grp - 1), rs, tg);
-                    mask_words(0);
-                    __builtin_amdgcn_sched_barrier(0);
-                    mfma_item32<DT, true, false>(my_k, my_v, qc, s, p, o, lane);
-                    __builtin_amdgcn_sched_barrier(0);
-                    v_move_store(pr);
-                }
-                __syncthreads();
-                softmax_and_move(0);
-                for (int k = 1; k < n; ++k) {
-                    PageRegs<DT, 256, 64> pr;
-                    page_load<DT, 256, 64>(pr, half_src(vbase, 2 * k + grp - 1), rs, tg);
-                    mask_words(k);
-                    __builtin_amdgcn_sched_barrier(0);
-                    mfma_item32<DT, true, true>(my_k, my_v, qc, s, p, o, lane);
-                    __builtin_amdgcn_sched_barrier(0);
-                    v_move_store(pr);
-                    __syncthreads();
-                    softmax_and_move(k);
-                }
-                {
-                    PageRegs<DT, 256, 64> pr;
-                    page_load<DT, 256, 64>(pr, half_src(vbase, 2 * n + grp - 1), rs, tg);
-                    __builtin_amdgcn_sched_barrier(0);
-                    mfma_item32<DT, false, true>(my_k, my_v, qc, s, p, o, lane);
-                    __builtin_amdgcn_sched_barrier(0);
-                    v_move_store(pr);
-                }
-                if (grp == 0) __syncthreads();
-            }
-            __syncthreads();  // stages are free: group 1 hands its row states to group 0
-
-            if (grp == 1) {
-                f32x4* so = (f32x4*)(smem + (wave - 4) * (64 * 64 * 4 + 64 * 16));
-#pragma unroll
-                for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-                    for (int g4 = 0; g4 < 4; ++g4)
-                        so[(dt * 4 + g4) * 64 + lane] = (f32x4){o[dt][4 * g4], o[dt][4 * g4 + 1],
-                                                               o[dt][4 * g4 + 2], o[dt][4 * g4 + 3]};
-                so[16 * 64 + lane] = (f32x4){mrun, lrun, 0.f, 0.f};
-            }
-            __syncthreads();
-            if (grp == 0) {
-                const f32x4* so = (const f32x4*)(smem + wave * (64 * 64 * 4 + 64 * 16));
-                const f32x4 ml = so[16 * 64 + lane];
-                const float m = fmaxf(mrun, ml[0]);
-                const float a0 = (m == kNegInf) ? 0.f : fast_exp2(mrun - m);
-                const float a1 = (m == kNegInf) ? 0.f : fast_exp2(ml[0] - m);
-                mrun = m;
-                lrun = lrun * a0 + ml[1] * a1;
-#pragma unroll
-                for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-                    for (int g4 = 0; g4 < 4; ++g4) {
-                        const f32x4 x = so[(dt * 4 + g4) * 64 + lane];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) o[dt][4 * g4 + e] = o[dt][4 * g4 + e] * a0 + x[e] * a1;
+                if (n > 0) {
+                    f32x16 s[2];
+                    u32x4 p[4];
+                    {  // K_0 by the whole workgroup before the first slot
+                        PageRegs<DT, 512, 64> pr0;
+                        page_load<DT, 512, 64>(pr0, half_src(kbase, 0), rs, tid);
+                        store_k<DT, 512, 64>(pr0, kst, tid);
                     }
-                write_rows32<DT, OUT>(a, it, complete, 2 * w + (sa > 0 ? 0 : 1), row0, lane, trow,
-                                      rvalid, mrun, lrun, o);
-            }
-            __syncthreads();  // LDS is reused by the next task
-            if (!complete) {
-                int* list = (int*)smem;  // the stages are free until the next task
-                const int np = piece_arrive(a, w, u, st, a.nst, list);
-                if (np > 0)
-                    merge_rows<OUT>(a, list, np, row_base, min(row_base + R, rows_exist), it.n2,
-                                    t0, it.row0, it.sq);
+                    __syncthreads();
+                    if (grp == 1) {  // group 1 starts one slot late: K_1 moves meanwhile
+                        PageRegs<DT, 256, 64> pr1;
+                        page_load<DT, 256, 64>(pr1, half_src(kbase, 1), rs, tg);
+                        store_k<DT, 256, 64>(pr1, kst + KB, tg);
+                        __syncthreads();
+                    }
+                    unsigned char* const my_k = kst + grp * KB;
+                    unsigned char* const my_v = vst + grp * VB;
+                    unsigned char* const other_v = vst + (grp ^ 1) * VB;
+                    // V of the half page the partner has just exponentiated, into its V buffer
+                    auto v_move_store = [&](const PageRegs<DT, 256, 64>& pr) {
+                        if constexpr (DT == kFP8 || !kSharedPitch)
+                            store_v<DT, 256, 64>(pr, other_v, tg);
+                        else
+                            store_k<DT, 256, 64>(pr, other_v, tg);  // same row pitch as K
+                    };
+                    uint32_t umw[8];  // user-mask words of the next softmax item
+                    auto mask_words = [&](int k) {
+                        if constexpr (UM)
+                            umask_words32(a, um, __builtin_amdgcn_readfirstlane(plist[k].y) >> 2, grp,
+                                          lane, umw);
+                    };
+                    auto softmax_and_move = [&](int k) {
+                        const int jc = __builtin_amdgcn_readfirstlane(plist[k].y);
+                        PageRegs<DT, 256, 64> pr;
+                        page_load<DT, 256, 64>(pr, half_src(kbase, 2 * k + 2 + grp), rs, tg);
+                        __builtin_amdgcn_sched_barrier(0);
+                        softmax_item32<DT, UM>(a, s, p, colscale, trow, umw, jc >> 2, grp, jc & 3,
+                                               skv, off, lane, mrun, lrun, o);
+                        pin_softmax(p, lrun);
+                        __builtin_amdgcn_sched_barrier(0);
+                        store_k<DT, 256, 64>(pr, my_k, tg);
+                        __syncthreads();
+                    };
+                    {
+                        PageRegs<DT, 256, 64> pr;
+                        page_load<DT, 256, 64>(pr, half_src(vbase, grp - 1), rs, tg);
+                        mask_words(0);
+                        __builtin_amdgcn_sched_barrier(0);
+                        mfma_item32<DT, true, false>(my_k, my_v, qc, s, p, o, lane);
+                        __builtin_amdgcn_sched_barrier(0);
+                        v_move_store(pr);
+                    }
+                    __syncthreads();
+                    softmax_and_move(0);
+                    for (int k = 1; k < n; ++k) {
+                        PageRegs<DT, 256, 64> pr;
+                        page_load<DT, 256, 64>(pr, half_src(vbase, 2 * k + grp - 1), rs, tg);
+                        mask_words(k);
+                        __builtin_amdgcn_sched_barrier(0);
+                        mfma_item32<DT, true, true>(my_k, my_v, qc, s, p, o, lane);
+                        __builtin_amdgcn_sched_barrier(0);
+                        v_move_store(pr);
+                        __syncthreads();
+                        softmax_and_move(k);
+                    }
+                    {
+                        PageRegs<DT, 256, 64> pr;
+                        page_load<DT, 256, 64>(pr, half_src(vbase, 2 * n + grp - 1), rs, tg);
+                        __builtin_amdgcn_sched_barrier(0);
+                        mfma_item32<DT, false, true>(my_k, my_v, qc, s, p, o, lane);
+                        __builtin_amdgcn_sched_barrier(0);
+                        v_move_store(pr);
+                    }
+                    if (grp == 0) __syncthreads();
+                }
+                __syncthreads();  // stages are free: group 1 hands its row states to group 0
+
+                if (grp == 1) {
+                    f32x4* so = (f32x4*)(smem + (wave - 4) * (64 * 64 * 4 + 64 * 16));
+#pragma unroll
+                    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                        for (int g4 = 0; g4 < 4; ++g4)
+                            so[(dt * 4 + g4) * 64 + lane] = (f32x4){o[dt][4 * g4], o[dt][4 * g4 + 1],
+                                                                   o[dt][4 * g4 + 2], o[dt][4 * g4 + 3]};
+                    so[16 * 64 + lane] = (f32x4){mrun, lrun, 0.f, 0.f};
+                }
                 __syncthreads();
+                if (grp == 0) {
+                    const f32x4* so = (const f32x4*)(smem + wave * (64 * 64 * 4 + 64 * 16));
+                    const f32x4 ml = so[16 * 64 + lane];
+                    const float m = fmaxf(mrun, ml[0]);
+                    const float a0 = (m == kNegInf) ? 0.f : fast_exp2(mrun - m);
+                    const float a1 = (m == kNegInf) ? 0.f : fast_exp2(ml[0] - m);
+                    mrun = m;
+                    lrun = lrun * a0 + ml[1] * a1;
+#pragma unroll
+                    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                        for (int g4 = 0; g4 < 4; ++g4) {
+                            const f32x4 x = so[(dt * 4 + g4) * 64 + lane];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) o[dt][4 * g4 + e] = o[dt][4 * g4 + e] * a0 + x[e] * a1;
+                        }
+                    write_rows32<DT, OUT>(a, it, complete, 2 * w + (sa > 0 ? 0 : 1), row0, lane, trow,
+                                          rvalid, mrun, lrun, o);
+                }
+                __syncthreads();  // LDS is reused by the next task
+                if (!complete) {
+                    int* list = (int*)smem;  // the stages are free until the next task
+                    const int np = piece_arrive(a, w, u, st, a.nst, list);
+                    if (np > 0)
+                        merge_rows<OUT>(a, list, np, row_base, min(row_base + R, rows_exist), it.n2,
+                                        t0, it.row0, it.sq);
+                    __syncthreads();
+                }
             }
+            advance_unit(a, it);
         }
-        advance_unit(a, it);
+    });
+}
+
+// Whole units per task pay off once the units outnumber the resident workgroups this many
+// times over (the last tasks then are a small share of every workgroup's time).
+constexpr int kUnitTaskFactor = 8;
+
+// Launches KERN with its grid: one workgroup per worker and row subtile (the worker plan), or,
+// with many units and a kernel built for them (DYN), as many workgroups as stay resident on
+// the device, taking whole units.
+template <auto KERN, bool DYN>
+hipError_t launch_k(FwdArgs a, hipStream_t s) {
+    static std::atomic<int> per_cu{0};  // resident workgroups per CU (0: not yet asked)
+    int occ = per_cu.load(std::memory_order_relaxed);
+    if (occ == 0) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, KERN, 512, 0) != hipSuccess ||
+            n < 1)
+            n = 1;
+        per_cu.store(n, std::memory_order_relaxed);
+        occ = n;
     }
+    const int64_t resident = (int64_t)a.cus * occ;
+    int64_t grid = (int64_t)a.P * a.nst;
+    a.unit_tasks = 0;
+    if (DYN && (int64_t)a.N2 * a.tqb * a.nst >= kUnitTaskFactor * resident) {
+        a.unit_tasks = 1;
+        grid = resident >= kQueues ? resident / kQueues * kQueues : resident;
+    }
+    hipLaunchKernelGGL(KERN, dim3((unsigned)grid), dim3(512), 0, s, a);
+    return hipGetLastError();
 }
 
 template <int DT, int OUT, int LAYOUT, bool UM>
 hipError_t launch_l(const FwdArgs& a, int rows, hipStream_t s) {
-    const int grid = a.P * a.nst;
     // 8 waves per workgroup either way: 32 rows per wave for large units, 16 below (more
     // workgroups, fewer registers)
-    if (rows == 256 && DT != kFP8) {
+    if (rows == 256 && DT != kFP8)
         // (the dtype expression keeps the fp8 instantiation, which never runs, compilable)
-        hipLaunchKernelGGL((fwd_prefill_pp32d_kernel<(DT == kFP8 ? kBF16 : DT), OUT, LAYOUT, UM>),
-                           dim3(grid), dim3(512), 0, s, a);
-    } else if (rows == 256) {
-        hipLaunchKernelGGL((fwd_prefill_pp32_kernel<DT, OUT, LAYOUT, UM>), dim3(grid), dim3(512),
-                           0, s, a);
-    } else if (a.M > 64) {
-        hipLaunchKernelGGL((fwd_prefill_ks32_kernel<DT, OUT, LAYOUT, UM>), dim3(grid), dim3(512),
-                           0, s, a);
-    } else if (a.M > 32) {
-        // 17-64 rows: the keys of every page are split over 2 or 4 wave groups, so that no
-        // wave computes on missing rows and each page goes through LDS 2 or 4 times, not 8
-        hipLaunchKernelGGL((fwd_prefill_kernel<DT, OUT, 8, 1, 2, LAYOUT, UM>), dim3(grid),
-                           dim3(512), 0, s, a);
-    } else {
-        hipLaunchKernelGGL((fwd_prefill_kernel<DT, OUT, 8, 1, 4, LAYOUT, UM>), dim3(grid),
-                           dim3(512), 0, s, a);
-    }
-    return hipGetLastError();
+        return launch_k<fwd_prefill_pp32d_kernel<(DT == kFP8 ? kBF16 : DT), OUT, LAYOUT, UM>, !UM>(a,
+                                                                                             s);
+    if (rows == 256) return launch_k<fwd_prefill_pp32_kernel<DT, OUT, LAYOUT, UM>, !UM>(a, s);
+    if (a.M > 64) return launch_k<fwd_prefill_ks32_kernel<DT, OUT, LAYOUT, UM>, !UM>(a, s);
+    // 17-64 rows: the keys of every page are split over 2 or 4 wave groups, so that no wave
+    // computes on missing rows and each page goes through LDS 2 or 4 times, not 8
+    if (a.M > 32) return launch_k<fwd_prefill_kernel<DT, OUT, 8, 1, 2, LAYOUT, UM>, !UM>(a, s);
+    return launch_k<fwd_prefill_kernel<DT, OUT, 8, 1, 4, LAYOUT, UM>, !UM>(a, s);
 }
 
 // The KV layout and the user mask are template arguments, so that the plain paged kernels

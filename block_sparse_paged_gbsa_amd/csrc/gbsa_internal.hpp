@@ -58,6 +58,9 @@ struct FwdArgs {
     float* lse;            // [T, N1] or null
     int32_t* ws_status;    // workspace word 0: non-zero = metadata mismatch
     int32_t* ws_arrive;    // [P * nst] arrival counters of split units (left at zero)
+    int32_t* ws_queue;     // workspace words 16..48: task queue counters (left at zero)
+    int32_t unit_tasks;    // 1: tasks are whole units taken from the queues; 0: worker plan
+    int32_t cus;           // compute units of the device
     float* ws_o;           // [2P, M, 128]
     float* ws_m;           // [2P, M]  running max, log2 domain
     float* ws_l;           // [2P, M]  running sum

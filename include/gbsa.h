@@ -185,12 +185,13 @@ gbsa_status gbsa_metadata(const gbsa_params* params, const int32_t* sparse_block
 
 /*
  * Workspace bytes gbsa_forward needs, from shapes only (the aclnn GetWorkspaceSize
- * stage). It holds a status word, per-worker split-KV partial results (O, running max,
- * running sum) and the arrival counters of split units.
+ * stage). It holds a status word, the counters from which the prefill workgroups take their
+ * tasks, per-worker split-KV partial results (O, running max, running sum) and the arrival
+ * counters of split units.
  * A workspace must be zero-filled before its first use (e.g. hipMemsetAsync to 0). Every
- * call leaves its arrival counters at zero again, so later calls with the same worker count
- * and rows per unit (block_x * N1 / N2) can reuse it as it is, in stream order; the counter
- * region grows with both, so after a call with other values zero-fill it again. The status
+ * call leaves its task and arrival counters at zero again, so later calls with the same
+ * worker count and rows per unit (block_x * N1 / N2) can reuse it as it is, in stream order;
+ * the counter region grows with both, so after a call with other values zero-fill it again. The status
  * word (word 0) is sticky: once a call sets it, it stays set until the caller clears it.
  */
 gbsa_status gbsa_workspace_size(const gbsa_params* params, size_t* bytes);

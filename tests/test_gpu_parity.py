@@ -607,7 +607,10 @@ def _sampled_check(cfg, units, rows_per_unit=None, seed=0, tnd=False, problem=No
         p = gi.to_tnd(p)
     gp = GpuProblem(p)
     params, meta, out, lse, ws = gp.run(0)
-    assert int(ws[:4].view(torch.int32)[0].item()) == 0
+    words = ws[:256].view(torch.int32).cpu()
+    assert int(words[0]) == 0
+    # the prefill task queue counters (status page words 16..48) are back at zero
+    assert not bool(words[16:49].any()), f"{label}: task counters left at {words[16:49]}"
     # every active row finite (checked on the device, rows past seqused_q are never written)
     for b in range(p.batch):
         c0 = int(p.cu_seqlens_q[b])
@@ -677,6 +680,22 @@ def test_workload5_dense_equivalent_fp8_sampled():
     block selected: the result must be dense causal attention)."""
     units = [(b, gl) for b in range(2) for gl in _qblocks(256, (100, 128))]
     _sampled_check(5, units, rows_per_unit=32)
+
+
+def test_unit_tasks_repeat_bit_identical():
+    """The fp8 dense-equivalent workload runs as whole units taken from the per-XCD task
+    queues (its units outnumber the resident workgroups many times over). Which workgroup
+    takes which unit changes from call to call; the result must not: three more calls on the
+    same workspace give the same bytes, and leave the queue counters at zero."""
+    p = gi.config(5, device="cuda")
+    gp = GpuProblem(p)
+    params, meta, ref, _, ws = gp.run(0)
+    for i in range(3):
+        out, _, ws = gp.forward(params, meta, workspace=ws)
+        torch.cuda.synchronize()
+        words = ws[:256].view(torch.int32).cpu()
+        assert int(words[0]) == 0 and not bool(words[16:49].any()), f"call {i}"
+        assert torch.equal(out, ref), f"call {i}"
 
 
 def test_workload2_decode_tnd_sampled():

@@ -71,6 +71,57 @@ def measured_traffic(kernel: str, workload: str):
         return None
 
 
+TRACE_EVENTS = {1: "softmax start", 2: "softmax end", 3: "softmax barrier in",
+                4: "softmax barrier out", 5: "MFMA start", 6: "MFMA end", 7: "MFMA barrier out"}
+
+
+def slot_trace(w, p) -> int:
+    """Forward launches on the slot-trace build; per group (waves 0-3 and 4-7), the median
+    shader-clock cycles between consecutive events of the traced unit, and the cycles per slot
+    pair (one MFMA and one softmax item of every wave)."""
+    import ctypes
+    import numpy as np
+    import torch
+    from block_sparse_paged_gbsa_amd import _lib
+    if w.kernel != "fwd_prefill_pp32d_kernel":
+        print(f"--slot-trace traces fwd_prefill_pp32d_kernel; this workload runs {w.kernel}",
+              file=sys.stderr)
+        return 2
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    lib.gbsa_slot_trace_read.argtypes = [ctypes.c_void_p]
+    w.step()
+    torch.cuda.synchronize()
+    out = {"workload": p.name, "kernel": w.kernel, "clock": "s_memtime (shader clock)",
+           "launches": []}
+    for rep in range(3):
+        assert lib.gbsa_slot_trace_reset() == 0
+        w.forward()
+        torch.cuda.synchronize()
+        rec = np.zeros(8 * 1024, dtype=np.uint64)
+        assert lib.gbsa_slot_trace_read(rec.ctypes.data) == 0
+        rec = rec.reshape(8, 1024)
+        code = (rec >> np.uint64(56)).astype(np.int64)
+        clk = (rec & np.uint64((1 << 56) - 1)).astype(np.int64)
+        launch = {}
+        for grp, waves in ((0, range(0, 4)), (1, range(4, 8))):
+            pairs, periods = {}, []
+            for wv in waves:
+                n = int((code[wv] > 0).sum())
+                c, t = code[wv, :n], clk[wv, :n]
+                for i in range(1, n):
+                    key = f"{TRACE_EVENTS[int(c[i - 1])]} -> {TRACE_EVENTS[int(c[i])]}"
+                    pairs.setdefault(key, []).append(int(t[i] - t[i - 1]))
+                starts = t[c == 5]
+                periods += list(np.diff(starts))
+            launch[f"group{grp}"] = {k: int(np.median(v)) for k, v in sorted(pairs.items())}
+            launch[f"group{grp}"]["slot pair"] = int(np.median(periods)) if periods else None
+            launch[f"group{grp}"]["items traced"] = len(periods) // len(waves)
+        out["launches"].append(launch)
+    assert w.status() == 0, "metadata mismatch flagged by the kernels"
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def copy_calibration(mib: int) -> int:
     """A plain device-to-device copy of a known size (scale reference for FETCH/WRITE_SIZE)."""
     import torch
@@ -512,7 +563,18 @@ def main(argv=None):
                          "kernel-trace profile of them) and print their count")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter scale reference)")
+    ap.add_argument("--slot-trace", action="store_true",
+                    help="run the workload on the slot-trace build of the library "
+                         "(libgbsa_slot_trace.so, include/gbsa_slot_trace.h) and print the "
+                         "item durations of one traced unit of the 256-row DMA kernel")
     a = ap.parse_args(argv)
+    if a.slot_trace:
+        from block_sparse_paged_gbsa_amd import _lib
+        _lib.LIB_PATH = os.path.join(os.path.dirname(_lib.LIB_PATH), "libgbsa_slot_trace.so")
+        if not os.path.exists(_lib.LIB_PATH):
+            print(f"{_lib.LIB_PATH} is missing: build it with "
+                  "`python -m block_sparse_paged_gbsa_amd.build`", file=sys.stderr)
+            return 2
     if a.copy_calibration:
         return copy_calibration(a.copy_calibration)
     if (a.batch, a.top_k) != (64, 16) and (a.config != 2 or not 1 <= a.batch <= 4096 or
@@ -577,6 +639,8 @@ def main(argv=None):
         print(json.dumps({"forward_launches": a.forward_only + 1, "kernel": w.kernel,
                           "workload": p.name}), flush=True)
         return 0
+    if a.slot_trace:
+        return slot_trace(w, p)
     if a.cold_only:
         flush = cache_flusher(dev)
         w.step()

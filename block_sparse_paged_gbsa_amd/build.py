@@ -20,6 +20,10 @@ SOURCES = ["api.hip", "metadata.hip", "fwd_decode.hip", "fwd_prefill.hip", "vali
 # measurement probes (HBM ceilings for the benchmark), a library of their own
 PROBE_LIB = os.path.join(HERE, "libgbsa_probe.so")
 PROBE_SOURCES = ["probe.hip"]
+# diagnostic build: libgbsa with the prefill slot trace (include/gbsa_slot_trace.h); only the
+# prefill kernels' source is compiled differently
+TRACE_LIB = os.path.join(HERE, "libgbsa_slot_trace.so")
+TRACE_SOURCE = "fwd_prefill.hip"
 ARCH = "gfx950"
 
 
@@ -40,9 +44,11 @@ def flags():
     ]
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, verbose: bool, trace: bool = False) -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ("_slot_trace" if trace else "") + ".o")
     cmd = [hipcc(), "-c", os.path.join(CSRC, src), "-o", obj] + flags()
+    if trace:
+        cmd.append("-DGBSA_SLOT_TRACE")
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -68,10 +74,14 @@ def _link(objs, lib: str, verbose: bool) -> None:
 
 def build(jobs: int = 8, verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
+    jobs_list = [(s, False) for s in SOURCES + PROBE_SOURCES] + [(TRACE_SOURCE, True)]
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES + PROBE_SOURCES))
-    _link(objs[:len(SOURCES)], LIB, verbose)
-    _link(objs[len(SOURCES):], PROBE_LIB, verbose)
+        objs = list(ex.map(lambda j: _compile(j[0], verbose, j[1]), jobs_list))
+    main = objs[:len(SOURCES)]
+    _link(main, LIB, verbose)
+    _link(objs[len(SOURCES):len(SOURCES) + len(PROBE_SOURCES)], PROBE_LIB, verbose)
+    traced = [objs[-1] if src == TRACE_SOURCE else o for src, o in zip(SOURCES, main)]
+    _link(traced, TRACE_LIB, verbose)
     return LIB
 
 

@@ -1072,6 +1072,44 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32_kernel(FwdArgs a) {
 // reader finished two slots earlier, and every wave lets only its newest DMA batch stay in
 // flight across a barrier.
 // ---------------------------------------------------------------------------------------------
+// Slot trace (diagnostic build, -DGBSA_SLOT_TRACE, libgbsa_slot_trace.so). The first unit of
+// at least 12 pages that a workgroup of the DMA kernel meets (one per launch, claimed with an
+// atomic) records, per wave, an s_memtime stamp (shader clock) at every item boundary of its
+// loop: event codes 1 softmax item start, 2 softmax item end, 3 before its barrier, 4 after it,
+// 5 MFMA item start, 6 MFMA item end (loads waited for), 7 after its barrier. In the normal
+// build the marks compile to nothing.
+constexpr int kTraceEvents = 1024;  // per wave
+#ifdef GBSA_SLOT_TRACE
+__device__ unsigned long long g_slot_trace[8 * kTraceEvents];
+__device__ int g_slot_trace_claim;
+struct SlotTrace {
+    unsigned long long* p = nullptr;
+    int ev = 0;
+    __device__ void begin(bool on, int wave) {
+        p = on ? g_slot_trace + wave * kTraceEvents : nullptr;
+        ev = 0;
+    }
+    __device__ void mark(int code, int lane) {
+        __builtin_amdgcn_sched_barrier(0);
+        const unsigned long long t = __builtin_amdgcn_s_memtime();
+        if (p != nullptr && lane == 0 && ev < kTraceEvents)
+            p[ev] = ((unsigned long long)code << 56) | (t & ((1ull << 56) - 1));
+        ev += p != nullptr ? 1 : 0;
+        __builtin_amdgcn_sched_barrier(0);
+    }
+};
+// one wave's lane 0, with the unit's visible page count: whether this unit is the traced one
+__device__ __forceinline__ int slot_trace_claim(int pages) {
+    return pages >= 12 && atomicCAS(&g_slot_trace_claim, 0, 1) == 0;
+}
+#else
+struct SlotTrace {
+    __device__ void begin(bool, int) {}
+    __device__ void mark(int, int) {}
+};
+__device__ __forceinline__ int slot_trace_claim(int) { return 0; }
+#endif
+
 constexpr int kDmaStride = 1088;             // bytes between the DMA instructions of a half page
 constexpr int kDmaHalf = 16 * kDmaStride;    // one half page
 
@@ -1198,7 +1236,7 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32d_kernel(FwdArgs a) {
     // per visible page: byte offset of this head's slice, readable bytes of its two halves
     __shared__ u32x4 plist[256];
     __shared__ int jlist[256];  // per visible page: block index * 4 + mask class
-    __shared__ int flag[1];
+    __shared__ int flag[2];  // visible pages of the unit; slot trace on
     static_assert(sizeof(smem) >= kPieceListBytes, "the split merge borrows the stages");
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -1280,10 +1318,15 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32d_kernel(FwdArgs a) {
                         }
                         n += __builtin_popcountll(mm);
                     }
-                    if (lane == 0) flag[0] = n;
+                    if (lane == 0) {
+                        flag[0] = n;
+                        flag[1] = slot_trace_claim(n);
+                    }
                 }
                 __syncthreads();
                 const int nh = 2 * __builtin_amdgcn_readfirstlane(flag[0]);  // half pages
+                SlotTrace tr;
+                tr.begin(__builtin_amdgcn_readfirstlane(flag[1]) != 0, wave);
 
                 // half page q (clamped into the stream) of K or V of this head
                 auto half_src = [&](const unsigned char* base, int q) {
@@ -1337,10 +1380,12 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32d_kernel(FwdArgs a) {
                     auto softmax_and_move = [&](int k) {
                         const int jc = jc_next;
                         __builtin_amdgcn_sched_barrier(0);
+                        tr.mark(1, lane);
                         softmax_item32<DT, UM>(a, s, p, colscale, trow, umw, jc >> 2, k & 1, jc & 3,
                                                skv, off, lane, mrun, lrun, o);
                         pin_softmax(p, lrun);
                         __builtin_amdgcn_sched_barrier(0);
+                        tr.mark(2, lane);
                         if constexpr (!kItemMove) {  // group 0 V_{k+1}, group 1 K_{k+3}
                             if (grp == 0)
                                 dma_half16(half_src(vbase, k + 1), rs,
@@ -1351,7 +1396,9 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32d_kernel(FwdArgs a) {
                         }
                         const int jn = jlist[min(k + 1, nh - 1) >> 1];
                         wait_vm<4>();  // all but this item's batch are in LDS
+                        tr.mark(3, lane);
                         __syncthreads();
+                        tr.mark(4, lane);
                         jc_next = __builtin_amdgcn_readfirstlane(jn);
                     };
                     if constexpr (UM) umask_words32(a, um, jc_next >> 2, 0, lane, umw);
@@ -1364,13 +1411,16 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32d_kernel(FwdArgs a) {
                     softmax_and_move(0);
                     for (int k = 1; k < nh; ++k) {
                         if constexpr (UM) umask_words32(a, um, jc_next >> 2, k & 1, lane, umw);
+                        tr.mark(5, lane);
                         raise();
                         mfma_item32d<DT, true, true, kItemMove>(kst + (k & 3) * kDmaHalf,
                                                                 vst + ((k - 1) & 3) * kDmaHalf, qc, s,
                                                                 p, o, lane, move_of(k), rs);
                         lower();
                         wait_vm<UM ? 12 : 4>();
+                        tr.mark(6, lane);
                         __syncthreads();
+                        tr.mark(7, lane);
                         softmax_and_move(k);
                     }
                     raise();
@@ -1711,3 +1761,18 @@ hipError_t launch_prefill(const FwdArgs& a, int dtype, int out_dtype, int rows, 
 }
 
 }  // namespace gbsa
+
+#ifdef GBSA_SLOT_TRACE
+// Readout of the diagnostic build (declared in gbsa_slot_trace.h).
+extern "C" int gbsa_slot_trace_read(unsigned long long* host_dst) {
+    return (int)hipMemcpyFromSymbol(host_dst, HIP_SYMBOL(gbsa::g_slot_trace),
+                                    sizeof(unsigned long long) * 8 * gbsa::kTraceEvents);
+}
+extern "C" int gbsa_slot_trace_reset(void) {
+    static unsigned long long zeros[8 * gbsa::kTraceEvents];
+    static const int zero = 0;
+    hipError_t e = hipMemcpyToSymbol(HIP_SYMBOL(gbsa::g_slot_trace_claim), &zero, sizeof(int));
+    if (e != hipSuccess) return (int)e;
+    return (int)hipMemcpyToSymbol(HIP_SYMBOL(gbsa::g_slot_trace), zeros, sizeof(zeros));
+}
+#endif

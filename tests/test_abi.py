@@ -238,6 +238,23 @@ def test_probe_library_exports_its_header():
                                  None) == -1
 
 
+def test_slot_trace_library_exports_both_headers():
+    """The diagnostic build is the library plus the two readout calls of gbsa_slot_trace.h;
+    the normal build has neither."""
+    trace = os.path.join(os.path.dirname(_lib.LIB_PATH), "libgbsa_slot_trace.so")
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "gbsa_slot_trace.h")).read(),
+                  flags=re.S)
+    extra = sorted(set(re.findall(r"\b(gbsa_slot_trace_[a-z_]+)\s*\(", text)))
+    assert extra == ["gbsa_slot_trace_read", "gbsa_slot_trace_reset"]
+
+    def exports(path):
+        out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True,
+                             text=True, check=True).stdout
+        return set(re.findall(r" T (gbsa_\w+)", out))
+    assert exports(trace) == exports(_lib.LIB_PATH) | set(extra)
+    assert not exports(_lib.LIB_PATH) & set(extra)
+
+
 def test_noalloc_forward_argument_checks():
     """gbsa_forward_ex_noalloc takes no workspace and refuses shapes whose partial results do
     not fit its fixed array, before touching a device."""

@@ -154,8 +154,11 @@ struct KvSeq {
         return table ? table[j] : row0 + 128 * j;
     }
 };
+// (b is clamped into [0, B): after the last unit advance_unit leaves b == B, and a load for
+// that state must not reach past seqused_kv or the block table.)
 template <int L = kAnyLayout>
 __device__ __forceinline__ KvSeq kv_seq(const FwdArgs& a, int b) {
+    b = min(max(b, 0), a.B - 1);
     KvSeq s;
     if (!is_tnd<L>(a)) {
         s.table = a.table + (int64_t)b * a.maxb;
@@ -433,6 +436,12 @@ __device__ inline UnitIter locate_unit(const FwdArgs& a, int u0, const SeqLens* 
     return it;
 }
 
+// Next unit in (b, n2, gl) order. After the last unit of the grid it leaves it.b == B, it.gl
+// == it.n2 == 0 and qbase + gl == totalQBlocks, with the other fields those of the last
+// sequence: no unit. Callers test the unit bound before loading anything for the new state;
+// code that loads ahead for the next unit must not treat that state as a unit (its count and
+// selection row are another KV head's or past the arrays, and its batch is one past
+// seqused_kv and the block table).
 __device__ __forceinline__ void advance_unit(const FwdArgs& a, UnitIter& it) {
     if (++it.gl < it.nact) return;
     it.gl = 0;

@@ -47,12 +47,14 @@ def make_params(*, batch: int, num_heads_q: int, num_heads_kv: int, total_q: int
                 total_q_blocks: int, top_k: int, block_x: int, max_blocks_per_seq: int,
                 num_pages: int, kv_page_stride: int = 0, dtype=torch.float16,
                 out_dtype=None, mask_mode: int = 1, win_left: int = -1, win_right: int = -1,
-                quant_mode: int = 0, softmax_precision: int = 1, return_lse: bool = False,
+                quant_mode: int = 0, softmax_precision: int = 0, return_lse: bool = False,
                 has_seqused_q: bool = False, scale: float = 0.0, num_workers: int = 0,
                 block_y: int = 128, head_dim: int = 128, kv_layout: int = 0,
                 max_seqlen_q: int = -1, max_seqlen_kv: int = -1) -> GbsaParams:
     """kv_layout 0 = PA_BBND (num_pages pages), 1 = TND (num_pages = rows of key/value).
-    max_seqlen_q / max_seqlen_kv: -1 (not given) or bounds that gbsa_validate checks."""
+    max_seqlen_q / max_seqlen_kv: -1 (not given) or bounds that gbsa_validate checks.
+    softmax_precision: 0 (fp32, the default here) or 1 (the 16-bit online softmax with f16;
+    the keyword interface keeps the article's default of 1)."""
     p = GbsaParams()
     p.batch = batch
     p.num_heads_q = num_heads_q

@@ -381,6 +381,7 @@ static gbsa_status forward_impl(const gbsa_params* p, const gbsa_forward_args* g
     a.wl = p->win_left;
     a.wr = p->win_right;
     a.return_lse = p->return_lse;
+    a.half_softmax = p->softmax_precision == 1 && p->dtype == GBSA_DTYPE_F16;
     const double scale = p->scale > 0.f ? (double)p->scale : 1.0 / sqrt((double)p->head_dim);
     a.scale_log2 = (float)(scale * 1.4426950408889634);
     a.T = p->total_q;

@@ -734,7 +734,13 @@ __device__ __forceinline__ void umask_words32(const FwdArgs& a, const UMaskRow& 
             w[4 * t + q] = umask_word(a, um, (int64_t)j * 128 + half * 64 + 32 * t + 8 * q + 4 * h2);
 }
 
-template <int DT, bool UM>
+// HS (f16 only): softmax precision 1 of the GBSA article's "softmax precision" section. The
+// online-softmax stage runs in the output's 16-bit type: the logits are rounded to f16, and the
+// scaling and max subtraction (packed f16 FMA) and the exponentials are f16; the block max is
+// taken on the fp32 logits and the running max kept at an f16 value, and the rescale of O and
+// the row sums stay fp32 (the sums accumulate the f16 exponentials with v_dot2_f32_f16, so they
+// add exactly the P that the PV product uses).
+template <int DT, bool UM, bool HS = false>
 __device__ __forceinline__ void softmax_item32(const FwdArgs& a, f32x16 (&s)[2], u32x4 (&p)[4],
                                                float colscale, int trow, const uint32_t (&umw)[8],
                                                int j, int half, int cls, int skv, int off,
@@ -766,6 +772,51 @@ __device__ __forceinline__ void softmax_item32(const FwdArgs& a, f32x16 (&s)[2],
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     if ((umw[4 * t + q] >> (8 * r)) & 0xffu) s[t][4 * q + r] = kNegInf;
+    }
+    if constexpr (HS) {
+        static_assert(DT == kF16, "the 16-bit softmax is the f16 path");
+        // pair q = 4 c + e holds elements 8 (c & 1) + 2 e and + 1 of tile c >> 1: the order of P
+        f16x2 h[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int t = q >> 3, i = 8 * ((q >> 2) & 1) + 2 * (q & 3);
+            const float x0 = s[t][i], x1 = s[t][i + 1];
+            h[q] = __builtin_convertvector((f32x2){x0, x1}, f16x2);
+        }
+        // the block max from the fp32 logits, and a running max that f16 represents exactly:
+        // the f16 subtraction then removes exactly the max the LSE is built on
+        float mx = kNegInf;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[t][i]);
+        mx = pair_max(mx, true);
+        float mnew = lazy_max(mrun, mx == kNegInf ? kNegInf : mx * colscale);
+        if (mnew != mrun && mnew != kNegInf) mnew = (float)(_Float16)mnew;
+        const float muse = (mnew == kNegInf) ? 0.f : mnew;
+        const float alpha = fast_exp2(mrun - muse);
+        mrun = mnew;
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+        }
+        const _Float16 c16 = (_Float16)colscale, m16 = (_Float16)(-muse);
+        const f16x2 cc = {c16, c16}, mm = {m16, m16}, one = {(_Float16)1.f, (_Float16)1.f};
+        float ls = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            uint32_t w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const f16x2 x = __builtin_elementwise_fma(h[4 * c + e], cc, mm);
+                const f16x2 e2 = __builtin_elementwise_exp2(x);
+                ls = __builtin_amdgcn_fdot2(e2, one, ls, false);
+                w[e] = __builtin_bit_cast(uint32_t, e2);
+            }
+            p[c] = (u32x4){w[0], w[1], w[2], w[3]};
+        }
+        lrun = lrun * alpha + ls;
+        return;
     }
     float mx = kNegInf;
 #pragma unroll
@@ -1226,7 +1277,7 @@ __device__ __forceinline__ void mfma_item32d(const unsigned char* ks, const unsi
     }
 }
 
-template <int DT, int OUT, int LAYOUT, bool UM>
+template <int DT, int OUT, int LAYOUT, bool UM, bool HS = false>
 __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32d_kernel(FwdArgs a) {
     static_assert(DT != kFP8, "the DMA layout holds 16-bit rows");
     constexpr int R = 256;
@@ -1381,7 +1432,7 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32d_kernel(FwdArgs a) {
                         const int jc = jc_next;
                         __builtin_amdgcn_sched_barrier(0);
                         tr.mark(1, lane);
-                        softmax_item32<DT, UM>(a, s, p, colscale, trow, umw, jc >> 2, k & 1, jc & 3,
+                        softmax_item32<DT, UM, HS>(a, s, p, colscale, trow, umw, jc >> 2, k & 1, jc & 3,
                                                skv, off, lane, mrun, lrun, o);
                         pin_softmax(p, lrun);
                         __builtin_amdgcn_sched_barrier(0);
@@ -1465,7 +1516,7 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32d_kernel(FwdArgs a) {
 // ---------------------------------------------------------------------------------------------
 // The 128-row kernel (schedule above) on 32x32 tiles: each wave's 32 query rows are one
 // 32-column tile.
-template <int DT, int OUT, int LAYOUT, bool UM>
+template <int DT, int OUT, int LAYOUT, bool UM, bool HS = false>
 __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32_kernel(FwdArgs a) {
     constexpr int R = 128;
     constexpr int esz = (DT == kFP8) ? 1 : 2;
@@ -1607,7 +1658,7 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32_kernel(FwdArgs a) {
                         PageRegs<DT, 256, 64> pr;
                         page_load<DT, 256, 64>(pr, half_src(kbase, 2 * k + 2 + grp), rs, tg);
                         __builtin_amdgcn_sched_barrier(0);
-                        softmax_item32<DT, UM>(a, s, p, colscale, trow, umw, jc >> 2, grp, jc & 3,
+                        softmax_item32<DT, UM, HS>(a, s, p, colscale, trow, umw, jc >> 2, grp, jc & 3,
                                                skv, off, lane, mrun, lrun, o);
                         pin_softmax(p, lrun);
                         __builtin_amdgcn_sched_barrier(0);
@@ -1727,12 +1778,24 @@ template <int DT, int OUT, int LAYOUT, bool UM>
 hipError_t launch_l(const FwdArgs& a, int rows, hipStream_t s) {
     // 8 waves per workgroup either way: 32 rows per wave for large units, 16 below (more
     // workgroups, fewer registers)
-    if (rows == 256 && DT != kFP8)
+    // softmax precision 1 with f16 runs the 16-bit softmax item in the two ping-pong kernels
+    // (the other kernels and the user-mask variants compute it in fp32, which the mode allows)
+    constexpr bool kHalf = DT == kF16 && !UM;
+    if (rows == 256 && DT != kFP8) {
+        if constexpr (kHalf)
+            if (a.half_softmax)
+                return launch_k<fwd_prefill_pp32d_kernel<kF16, OUT, LAYOUT, false, true>, true>(a, s);
         // (the dtype expression keeps the fp8 instantiation, which never runs, compilable)
         return launch_k<fwd_prefill_pp32d_kernel<(DT == kFP8 ? kBF16 : DT), OUT, LAYOUT, UM>, !UM>(a,
                                                                                              s);
+    }
     if (rows == 256) return launch_k<fwd_prefill_pp32_kernel<DT, OUT, LAYOUT, UM>, !UM>(a, s);
-    if (a.M > 64) return launch_k<fwd_prefill_ks32_kernel<DT, OUT, LAYOUT, UM>, !UM>(a, s);
+    if (a.M > 64) {
+        if constexpr (kHalf)
+            if (a.half_softmax)
+                return launch_k<fwd_prefill_ks32_kernel<kF16, OUT, LAYOUT, false, true>, true>(a, s);
+        return launch_k<fwd_prefill_ks32_kernel<DT, OUT, LAYOUT, UM>, !UM>(a, s);
+    }
     // 17-64 rows: the keys of every page are split over 2 or 4 wave groups, so that no wave
     // computes on missing rows and each page goes through LDS 2 or 4 times, not 8
     if (a.M > 32) return launch_k<fwd_prefill_kernel<DT, OUT, 8, 1, 2, LAYOUT, UM>, !UM>(a, s);

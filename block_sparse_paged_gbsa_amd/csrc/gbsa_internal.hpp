@@ -61,6 +61,7 @@ struct FwdArgs {
     int32_t* ws_queue;     // workspace words 16..48: task queue counters (left at zero)
     int32_t unit_tasks;    // 1: tasks are whole units taken from the queues; 0: worker plan
     int32_t cus;           // compute units of the device
+    int32_t half_softmax;  // softmax precision 1 with f16: the 16-bit softmax item
     float* ws_o;           // [2P, M, 128]
     float* ws_m;           // [2P, M]  running max, log2 domain
     float* ws_l;           // [2P, M]  running sum

@@ -126,7 +126,10 @@ typedef struct gbsa_params {
                                    gbsa_forward; 0 with GBSA_MASK_CAUSAL_TOP_LEFT) */
     int32_t win_right;          /* -1 unbounded, else keys p <= t + off + win_right */
     int32_t quant_mode;         /* gbsa_quant_mode; 5 requires dtype FP8_E4M3 */
-    int32_t softmax_precision;  /* 0 or 1 ("softmax precision" section); computed in fp32 */
+    int32_t softmax_precision;  /* 0: fp32 online softmax; 1 ("softmax precision" section):
+                                   with f16, the online-softmax stage of the kernels for more
+                                   than 64 rows per unit runs in f16 (rescale and row sums in
+                                   fp32); bf16, fp8 and the other kernels compute it in fp32 */
     int32_t return_lse;         /* 1: write softmax_lse */
     int32_t is_packed_gqa;      /* must be 1 */
     int32_t has_seqused_q;      /* 1: seqused_q is passed to both calls */

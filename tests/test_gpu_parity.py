@@ -698,6 +698,70 @@ def test_unit_tasks_repeat_bit_identical():
         assert torch.equal(out, ref), f"call {i}"
 
 
+# Softmax precision 1 (GBSA article, "softmax precision": online softmax in the output's 16-bit
+# type, rescale in fp32; it may overflow). With f16 the two ping-pong kernels compute it in f16;
+# bf16 and fp8 keep fp32 there. Bars: the logits rounded to f16 (relative 2^-11) and the f16
+# scaling, subtraction and exponential (2^-11 each, the exponential's approximation within one
+# ulp) give each exponential a relative error of at most eps = ln2 * 2^-11 * (2|t| + |x|) +
+# 3 * 2^-11 (t the logit in log2 units, x = t - m); the weighted mean of those errors moves LSE
+# by at most eps and O by at most 2 eps max|v|. For these inputs (unit-variance Q/K/V, D = 128)
+# the logits stay within |t| <= 8 and the weight of keys with x < -16 is negligible, so
+# eps <= 0.013: LSE within 1e-3 |LSE| + 1.3e-2, O within the bf16 bar of a 16-bit softmax
+# stage, 1.6e-2 (the margins recorded show how far inside they stay).
+HALF_SM_CASES = [
+    dict(seed=161, num_heads_q=16, num_heads_kv=2, block_x=16, top_k=6, mask_mode=1,
+         max_len=600),
+    dict(seed=162, num_heads_q=32, num_heads_kv=4, block_x=64, top_k=5, mask_mode=1,
+         max_len=900, use_seqused_q=True),
+    dict(seed=163, num_heads_q=64, num_heads_kv=2, block_x=16, top_k=4, mask_mode=0,
+         win_left=200, win_right=50, max_len=700),
+    dict(seed=116, num_heads_q=16, num_heads_kv=2, block_x=32, top_k=6, mask_mode=1,
+         max_len=500),
+]
+
+
+@pytest.mark.parametrize("case", HALF_SM_CASES, ids=[str(c["seed"]) for c in HALF_SM_CASES])
+def test_half_precision_softmax_f16(case):
+    """Both ping-pong kernels (128 and 512 packed rows per unit) in softmax precision 1, every
+    row against the oracle; the same problem in precision 0 for comparison."""
+    kw = {k: v for k, v in case.items() if k != "seed"}
+    p = gi.random_problem(case["seed"], device="cuda", dtype="f16", return_lse=True, **kw)
+    gp = GpuProblem(p)
+    O, L, done = oa.sparse_attention(oracle_inputs(p))
+    errs = {}
+    for mode in (1, 0):
+        params = gpu_params(p)
+        params.softmax_precision = mode
+        meta = gp.metadata(params)
+        out, lse, ws = gp.forward(params, meta)
+        torch.cuda.synchronize()
+        assert int(ws[:4].view(torch.int32)[0].item()) == 0
+        label = f"half_softmax_{case['seed']}_mode{mode}"
+        bars = dict(o_tol=1.6e-2, lse_atol=1.3e-2) if mode == 1 else {}
+        errs[mode] = compare(p, out, lse, O, L, done, label, **bars)
+        record_margin(label, rows=int(done.sum()), heads=p.num_heads_q, o_max_abs=errs[mode][0],
+                      o_bar=bars.get("o_tol", TOL["f16"]), lse_rel=errs[mode][1])
+    _log(f"[parity] half softmax {case['seed']}: O {errs[1][0]:.2e} (fp32 {errs[0][0]:.2e}), "
+         f"LSE rel {errs[1][1]:.2e} (fp32 {errs[0][1]:.2e})")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_half_precision_softmax_other_dtypes_compute_fp32(dtype):
+    """Softmax precision 1 with bf16 or fp8 is computed in fp32 (the mode permits the lower
+    precision; only the f16 kernels use it): bit-identical to precision 0."""
+    p = gi.random_problem(164, device="cuda", dtype=dtype, num_heads_q=16, num_heads_kv=2,
+                          block_x=32, top_k=5, mask_mode=1, max_len=500, return_lse=True)
+    gp = GpuProblem(p)
+    res = []
+    for mode in (0, 1):
+        params = gpu_params(p)
+        params.softmax_precision = mode
+        out, lse, _ = gp.forward(params, gp.metadata(params))
+        torch.cuda.synchronize()
+        res.append((out.clone(), lse.clone()))
+    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+
+
 def test_workload2_decode_tnd_sampled():
     _sampled_check(2, [(b, 0) for b in range(64)], tnd=True)
 

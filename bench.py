@@ -421,6 +421,7 @@ class Workload:
         self.squ = None if p.seqused_q is None else t(p.seqused_q)
         f32 = lambda s: None if s is None else torch.as_tensor(s, dtype=torch.float32).to(dev)
         self.qs, self.ks, self.vs = f32(p.q_scale), f32(p.k_scale), f32(p.v_scale)
+        self.ps = None  # [N1] P quantisation scales (quant mode 5: fp8 P·V), `--p-scale`
         self.meta = torch.empty(1024, dtype=torch.int32, device=dev)
         self.out = torch.empty(p.q.shape, dtype=gi.TORCH_DTYPES[p.out_dtype], device=dev)
         self.lse = (torch.empty(p.q.shape[:2], dtype=torch.float32, device=dev)
@@ -444,15 +445,15 @@ class Workload:
             gbsa_forward_ex(self.params, p.q, p.k, p.v, self.idx, self.cnt, self.meta, self.cu,
                             self.squ, cu_seqlens_kv=self.cu_kv, seqused_kv=self.skv,
                             block_table=self.table, q_scale=self.qs, k_scale=self.ks,
-                            v_scale=self.vs, atten_mask=self.umask, out=self.out, lse=self.lse,
-                            workspace=self.ws)
+                            v_scale=self.vs, p_scale=self.ps, atten_mask=self.umask,
+                            out=self.out, lse=self.lse, workspace=self.ws)
         elif self.tnd:
             gbsa_forward_tnd(self.params, p.q, p.k, p.v, self.idx, self.cnt, self.meta, self.cu,
-                             self.squ, self.cu_kv, self.skv, self.qs, self.ks, self.vs, None,
+                             self.squ, self.cu_kv, self.skv, self.qs, self.ks, self.vs, self.ps,
                              self.out, self.lse, self.ws)
         else:
             gbsa_forward(self.params, p.q, p.k, p.v, self.idx, self.cnt, self.meta, self.cu,
-                         self.squ, self.skv, self.table, self.qs, self.ks, self.vs, None,
+                         self.squ, self.skv, self.table, self.qs, self.ks, self.vs, self.ps,
                          self.out, self.lse, self.ws)
 
     def step(self):
@@ -563,6 +564,9 @@ def main(argv=None):
                          "kernel-trace profile of them) and print their count")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter scale reference)")
+    ap.add_argument("--p-scale", type=float, default=0.0, metavar="S",
+                    help="fp8 workloads: pass p_quant_scale S for every query head, so that P is "
+                         "cast to e4m3 and P·V runs on fp8 MFMA (name suffixed `_p8`)")
     ap.add_argument("--slot-trace", action="store_true",
                     help="run the workload on the slot-trace build of the library "
                          "(libgbsa_slot_trace.so, include/gbsa_slot_trace.h) and print the "
@@ -627,6 +631,12 @@ def main(argv=None):
         del t_idx, p_idx
         p.mask_mode = 0
     w = Workload(p, dev, tnd, umask)
+    if a.p_scale > 0:
+        if p.dtype != "fp8":
+            print("--p-scale applies to fp8 workloads (workload 5)", file=sys.stderr)
+            return 2
+        w.ps = torch.full((p.num_heads_q,), a.p_scale, dtype=torch.float32, device=dev)
+        p.name += "_p8"
     stream = torch.cuda.current_stream()
     hbm_bound = w.kernel == "fwd_decode_kernel"
 

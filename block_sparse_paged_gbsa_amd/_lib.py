@@ -71,7 +71,7 @@ class GbsaParams(ctypes.Structure):
         ("kv_layout", ctypes.c_int32),
         ("max_seqlen_q", ctypes.c_int32),
         ("max_seqlen_kv", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 1),
+        ("dst_type_max", ctypes.c_float),
     ]
 
 

@@ -50,7 +50,8 @@ def make_params(*, batch: int, num_heads_q: int, num_heads_kv: int, total_q: int
                 quant_mode: int = 0, softmax_precision: int = 0, return_lse: bool = False,
                 has_seqused_q: bool = False, scale: float = 0.0, num_workers: int = 0,
                 block_y: int = 128, head_dim: int = 128, kv_layout: int = 0,
-                max_seqlen_q: int = -1, max_seqlen_kv: int = -1) -> GbsaParams:
+                max_seqlen_q: int = -1, max_seqlen_kv: int = -1,
+                dst_type_max: float = 0.0) -> GbsaParams:
     """kv_layout 0 = PA_BBND (num_pages pages), 1 = TND (num_pages = rows of key/value).
     max_seqlen_q / max_seqlen_kv: -1 (not given) or bounds that gbsa_validate checks.
     softmax_precision: 0 (fp32, the default here) or 1 (the 16-bit online softmax with f16;
@@ -77,6 +78,7 @@ def make_params(*, batch: int, num_heads_q: int, num_heads_kv: int, total_q: int
     p.win_right = int(win_right)
     p.quant_mode = int(quant_mode)
     p.softmax_precision = int(softmax_precision)
+    p.dst_type_max = float(dst_type_max)
     p.return_lse = int(bool(return_lse))
     p.is_packed_gqa = 1
     p.has_seqused_q = int(bool(has_seqused_q))
@@ -404,8 +406,6 @@ def generic_block_sparse_attention(
     a nonzero entry (t, p) removes key position p for the batch-local query row t, on top of
     mask_mode (0 none, 1 causal bottom-right, 2 causal top-left) and the window.
     """
-    if dst_type_max != 0.0:
-        raise ValueError("dst_type_max must be 0.0")
     if metadata is None:
         raise ValueError("metadata from generic_block_sparse_attention_metadata is required")
     tnd = layout_kv == "TND"
@@ -429,7 +429,8 @@ def generic_block_sparse_attention(
                         max_blocks_per_seq=0 if tnd else block_table.shape[1],
                         num_pages=k.shape[0], kv_page_stride=0 if tnd else k.stride(0),
                         dtype=q.dtype, out_dtype=out_dtype, return_lse=return_softmax_lse,
-                        scale=float(softmax_scale), num_workers=num_workers, **c)
+                        scale=float(softmax_scale), num_workers=num_workers,
+                        dst_type_max=float(dst_type_max), **c)
         out, lse, _ = gbsa_forward_ex(
             p, q.contiguous(), k.contiguous() if tnd else k, v.contiguous() if tnd else v,
             sparse_block_idx.contiguous(), sparse_block_count.contiguous(), metadata,
@@ -442,7 +443,8 @@ def generic_block_sparse_attention(
     elif tnd:
         p = make_params(total_q=q.shape[0], max_blocks_per_seq=0, num_pages=k.shape[0],
                         dtype=q.dtype, out_dtype=out_dtype, return_lse=return_softmax_lse,
-                        scale=float(softmax_scale), num_workers=num_workers, **c)
+                        scale=float(softmax_scale), num_workers=num_workers,
+                        dst_type_max=float(dst_type_max), **c)
         out, lse, _ = gbsa_forward_tnd(
             p, q.contiguous(), k.contiguous(), v.contiguous(), sparse_block_idx.contiguous(),
             sparse_block_count.contiguous(), metadata, cu_seqlens_q.contiguous(), squ,
@@ -452,7 +454,8 @@ def generic_block_sparse_attention(
         p = make_params(total_q=q.shape[0], max_blocks_per_seq=block_table.shape[1],
                         num_pages=k.shape[0], kv_page_stride=k.stride(0), dtype=q.dtype,
                         out_dtype=out_dtype, return_lse=return_softmax_lse,
-                        scale=float(softmax_scale), num_workers=num_workers, **c)
+                        scale=float(softmax_scale), num_workers=num_workers,
+                        dst_type_max=float(dst_type_max), **c)
         out, lse, _ = gbsa_forward(
             p, q.contiguous(), k, v, sparse_block_idx.contiguous(),
             sparse_block_count.contiguous(), metadata, cu_seqlens_q.contiguous(), squ,

@@ -136,7 +136,7 @@ gbsa_status gbsa_check_params(const gbsa_params* p) {
     if (p->is_packed_gqa != 1) return GBSA_ERR_UNSUPPORTED;
     if (p->has_seqused_q != 0 && p->has_seqused_q != 1) return GBSA_ERR_SHAPE;
     if (p->return_lse != 0 && p->return_lse != 1) return GBSA_ERR_SHAPE;
-    if (p->reserved[0] != 0) return GBSA_ERR_UNSUPPORTED;
+    if (!(p->dst_type_max >= 0.f) || p->dst_type_max > 3.0e38f) return GBSA_ERR_UNSUPPORTED;
     // max_seqlen_q / max_seqlen_kv: -1 or 0 = not given; a given bound must fit the storage
     if (p->max_seqlen_q < -1 || p->max_seqlen_kv < -1) return GBSA_ERR_SHAPE;
     if (p->max_seqlen_q > p->total_q) return GBSA_ERR_SHAPE;
@@ -302,7 +302,7 @@ static gbsa_status forward_impl(const gbsa_params* p, const gbsa_forward_args* g
         return GBSA_ERR_DTYPE;
     if (!quant && (q_scale != nullptr || k_scale != nullptr || v_scale != nullptr))
         return GBSA_ERR_DTYPE;
-    if (p_scale != nullptr) return GBSA_ERR_UNSUPPORTED;
+    if (p_scale != nullptr && !quant) return GBSA_ERR_DTYPE;
     if (g->atten_mask != nullptr) {
         const int64_t rs = g->mask_row_stride, bs = g->mask_batch_stride;
         if (((uintptr_t)g->atten_mask & 3) != 0 || g->mask_rows < 0 || g->mask_cols < 0 ||
@@ -382,6 +382,8 @@ static gbsa_status forward_impl(const gbsa_params* p, const gbsa_forward_args* g
     a.wr = p->win_right;
     a.return_lse = p->return_lse;
     a.half_softmax = p->softmax_precision == 1 && p->dtype == GBSA_DTYPE_F16;
+    a.ps = p_scale;
+    a.ps_max = (p->dst_type_max > 0.f && p->dst_type_max < 448.f) ? p->dst_type_max : 448.f;
     const double scale = p->scale > 0.f ? (double)p->scale : 1.0 / sqrt((double)p->head_dim);
     a.scale_log2 = (float)(scale * 1.4426950408889634);
     a.T = p->total_q;

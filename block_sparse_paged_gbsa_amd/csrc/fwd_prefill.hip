@@ -101,6 +101,7 @@ __device__ __forceinline__ void store_v(const PageRegs<DT, NT, ROWS>& r, unsigne
 }
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 // e4m3 x e4m3 with K = 128 per instruction (a 16-token tile against the whole head dim).
 // A and B are loaded with the same head-dim assignment, so the product is the full dot
@@ -571,11 +572,36 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_prefill_kernel(FwdArgs a) {
 // 16-bit K and V rows with one LDS pitch can share one store routine
 constexpr bool kSharedPitch = KLds<kBF16>::pitch == kVPitch;
 
-template <int DT>
+// Bytes per fp8 V row in LDS when P·V runs on fp8 MFMA (V kept as e4m3): 160 = 128 + 32 puts the
+// eight rows of each half-wave of an 8-bit transposing read (32 bytes per row) on distinct
+// 8-bank groups (row r at bank 40 r mod 64).
+constexpr int kV8Pitch = 160;
+
+template <int DT, bool P8 = false>
 struct HalfStage {
     static constexpr int k_bytes = 64 * KLds<DT>::pitch;
-    static constexpr int v_bytes = 64 * kVPitch;
+    static constexpr int v_bytes = 64 * (P8 ? kV8Pitch : kVPitch);
 };
+
+// fp8 V rows as they are (P·V on fp8 MFMA) into the V area `vs` of a stage, pitch kV8Pitch
+template <int NT, int ROWS>
+__device__ __forceinline__ void store_v8(const PageRegs<kFP8, NT, ROWS>& r, unsigned char* vs,
+                                         int tid) {
+    constexpr int lanes_per_row = 8;
+    constexpr int rows_per_pass = NT / lanes_per_row;
+    const int row0 = tid / lanes_per_row, col = tid % lanes_per_row;
+#pragma unroll
+    for (int i = 0; i < PageRegs<kFP8, NT, ROWS>::n16; ++i)
+        *(u32x4*)(vs + (row0 + i * rows_per_pass) * kV8Pitch + col * 16) = r.x[i];
+}
+
+// 8-bit transpose read from LDS (ds_read_b64_tr_b8). Within each group of 16 lanes, lanes 2r and
+// 2r + 1 supply the two 8-byte halves of row r of an 8 x 16-byte block; lane i receives column
+// i, i.e. the bytes block[0..7][i].
+__device__ __forceinline__ u32x2 lds_read_tr8(const void* p) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                                         (GBSA_LDS i32x2*)(p)));
+}
 
 // LDS fragments in flight in the MFMA item
 constexpr int kPipeDepth = 4;
@@ -658,20 +684,30 @@ __device__ __forceinline__ void load_q32(const FwdArgs& a, const UnitIter& it, i
 
 // MFMA item on 32x32 tiles: QK^T of a half page (two 32-key tiles) and PV of the previous one,
 // as a software-pipelined sequence of steps (one LDS fragment and the MFMA that uses it).
-template <int DT, bool qk, bool pv>
+// P8 (fp8 with a P quantisation scale): PV on v_mfma_scale_f32_32x32x64_f8f6f4, one instruction
+// per 32 head dims for the whole half page, V^T read from the fp8 rows with the 8-bit transpose
+// read (four reads give a lane its 32 keys in order) and P as fp8 in the same key order (p[0],
+// p[1], from the softmax item).
+template <int DT, bool qk, bool pv, bool P8 = false>
 __device__ __forceinline__ void mfma_item32(const unsigned char* ks, const unsigned char* vs,
                                             const QCol32& qc, f32x16 (&s)[2],
                                             const u32x4 (&p)[4], f32x16 (&o)[4], int lane) {
+    static_assert(!P8 || DT == kFP8, "fp8 P is the fp8 path");
     constexpr int PT = (DT == kF16) ? kF16 : kBF16;
     constexpr int KP = KLds<DT>::pitch;
     constexpr int QS = qk ? ((DT == kFP8) ? 2 : 8) : 0;  // QK steps per 32-key tile
-    constexpr int VS = pv ? 8 : 0;                       // PV steps per 32-key tile (2 chunks x 4 d)
+    // PV steps per 32-key tile: 2 chunks x 4 d tiles, or with fp8 P two d tiles of 64 keys
+    constexpr int VS = pv ? (P8 ? 2 : 8) : 0;
     constexpr int PC = QS + VS, NS = 2 * PC, D = kPipeDepth;
     const int h2 = lane >> 5;
     const unsigned char* krow = ks + (lane & 31) * KP;
     // transpose-read address of this lane (row offset within a 4-row group, column block)
     const unsigned char* vbase = vs + (4 * h2 + ((lane & 15) >> 2)) * kVPitch +
                                  (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+    // fp8 V^T: this lane's row within the 8-row block of read m (keys 32 h + 8 m ..) and byte
+    // column (head dims 16 (lane / 16 % 2) + 8 (lane % 2) of the d tile)
+    const unsigned char* v8base = vs + (32 * h2 + ((lane & 15) >> 1)) * kV8Pitch +
+                                  16 * ((lane >> 4) & 1) + 8 * (lane & 1);
     const f32x16 zero = {};
 
     auto load = [&](int st) {
@@ -685,6 +721,13 @@ __device__ __forceinline__ void mfma_item32(const unsigned char* ks, const unsig
             } else {
                 f.a = *(const u32x4*)(krow + t * 32 * KP + (16 * j + 8 * h2) * 2);
             }
+        } else if constexpr (P8) {
+            const int dt = 2 * t + (j - QS);  // d tile: head dims 32 dt .. 32 dt + 31
+            const unsigned char* vr = v8base + 32 * dt;
+            const u32x2 r0 = lds_read_tr8(vr), r1 = lds_read_tr8(vr + 8 * kV8Pitch);
+            const u32x2 r2 = lds_read_tr8(vr + 16 * kV8Pitch), r3 = lds_read_tr8(vr + 24 * kV8Pitch);
+            f.a = (u32x4){r0[0], r0[1], r1[0], r1[1]};
+            f.b = (u32x4){r2[0], r2[1], r3[0], r3[1]};
         } else {
             const int v = j - QS, a2 = v >> 2, dt = v & 3;  // chunk 2t + a2, d tile dt
             const unsigned char* vr = vbase + (32 * t + 16 * a2) * kVPitch + dt * 64;
@@ -701,6 +744,9 @@ __device__ __forceinline__ void mfma_item32(const unsigned char* ks, const unsig
                 s[t] = mfma_32x32x64_fp8(f.a, f.b, qc.q[2 * j], qc.q[2 * j + 1], j == 0 ? zero : s[t]);
             else
                 s[t] = mfma_32x32x16<DT>(f.a, qc.q[j], j == 0 ? zero : s[t]);
+        } else if constexpr (P8) {
+            const int dt = 2 * t + (j - QS);
+            o[dt] = mfma_32x32x64_fp8(f.a, f.b, p[0], p[1], o[dt]);
         } else {
             const int v = j - QS, a2 = v >> 2, dt = v & 3;
             o[dt] = mfma_32x32x16<PT>(f.a, p[2 * t + a2], o[dt]);
@@ -740,12 +786,19 @@ __device__ __forceinline__ void umask_words32(const FwdArgs& a, const UMaskRow& 
 // taken on the fp32 logits and the running max kept at an f16 value, and the rescale of O and
 // the row sums stay fp32 (the sums accumulate the f16 exponentials with v_dot2_f32_f16, so they
 // add exactly the P that the PV product uses).
-template <int DT, bool UM, bool HS = false>
+// P8 (quant mode 5 with a P quantisation scale, GBSA article "quantisation": FP8_E4M3_STATIC_CAST_P):
+// P is cast to e4m3 after scaling by pq (the row's p_quant_scale, at most the destination
+// type's max) and handed to the fp8 P·V product in its B-operand order: lane l needs the 32 keys
+// 32 h .. 32 h + 31 (h = l / 32) in order and holds, per 32-key tile, the 16 keys 8 u + 4 h + r;
+// one v_permlane32_swap per dword u trades the other lane half's share (tile 0 to the low half,
+// tile 1 to the high half). The running max is exact (no lazy threshold), so P <= 1 and
+// P * pq stays within the type. The row sums add the unquantised P in fp32.
+template <int DT, bool UM, bool HS = false, bool P8 = false>
 __device__ __forceinline__ void softmax_item32(const FwdArgs& a, f32x16 (&s)[2], u32x4 (&p)[4],
                                                float colscale, int trow, const uint32_t (&umw)[8],
                                                int j, int half, int cls, int skv, int off,
                                                int lane, float& mrun, float& lrun,
-                                               f32x16 (&o)[4]) {
+                                               f32x16 (&o)[4], float pq = 1.f) {
     constexpr int PT = (DT == kF16) ? kF16 : kBF16;
     const int h2 = lane >> 5;
     if (cls == 2) {
@@ -824,13 +877,43 @@ __device__ __forceinline__ void softmax_item32(const FwdArgs& a, f32x16 (&s)[2],
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[t][i]);
     mx = pair_max(mx, true);
-    const float mnew = lazy_max(mrun, mx == kNegInf ? kNegInf : mx * colscale);
+    const float bmax = mx == kNegInf ? kNegInf : mx * colscale;
+    const float mnew = P8 ? fmaxf(mrun, bmax) : lazy_max(mrun, bmax);
     const float muse = (mnew == kNegInf) ? 0.f : mnew;
     const float alpha = fast_exp2(mrun - muse);
     mrun = mnew;
     if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {  // skipped unless some running max moved
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+    }
+    if constexpr (P8) {
+        float ls = 0.f;
+        uint32_t q8[2][4];  // [tile][u]: keys 8 u + 4 h .. + 3, e4m3, scaled by pq
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                float pv[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    pv[r] = fast_exp2(__builtin_fmaf(s[t][4 * u + r], colscale, -muse));
+                    ls += pv[r];
+                }
+                int w = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0] * pq, pv[1] * pq, 0, false);
+                w = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2] * pq, pv[3] * pq, w, true);
+                q8[t][u] = (uint32_t)w;
+            }
+        uint32_t b[8];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const auto r = __builtin_amdgcn_permlane32_swap(q8[0][u], q8[1][u], false, false);
+            b[2 * u] = (uint32_t)r[0];
+            b[2 * u + 1] = (uint32_t)r[1];
+        }
+        p[0] = (u32x4){b[0], b[1], b[2], b[3]};
+        p[1] = (u32x4){b[4], b[5], b[6], b[7]};
+        lrun = lrun * alpha + ls;
+        return;
     }
     float ls = 0.f;
 #pragma unroll
@@ -856,16 +939,27 @@ __device__ __forceinline__ void pin_softmax(u32x4 (&p)[4], float& lrun) {
     asm volatile("" : "+v"(p[0]), "+v"(p[1]), "+v"(p[2]), "+v"(p[3]), "+v"(lrun));
 }
 
+// The P quantisation scale of this lane's query row (quant mode 5 with p_quant_scale): the
+// row's head's scale, at most the destination type's max (P <= 1, so P * scale stays in range).
+__device__ __forceinline__ float p_quant(const FwdArgs& a, const UnitIter& it, int row0,
+                                         int rows_exist, int lane) {
+    const int r = row0 + (lane & 31);
+    const int h = it.n2 * a.G + (r < rows_exist ? r % a.G : 0);
+    return fminf(a.ps[h], a.ps_max);
+}
+
 // Normalised O and LSE of a wave's 32 rows (lane pair l, l + 32 per row), or the split partial.
 template <int DT, int OUT>
 __device__ __forceinline__ void write_rows32(const FwdArgs& a, const UnitIter& it, bool complete,
                                              int slot, int row0, int lane, int trow, bool rvalid,
-                                             float mrun, float lrun, const f32x16 (&o)[4]) {
+                                             float mrun, float lrun, const f32x16 (&o)[4],
+                                             float pdeq = 1.f) {
     const int h2 = lane >> 5;
     const float ltot = pair_sum(lrun, true);
     const int r = row0 + (lane & 31);
     if (!rvalid) return;
-    const float vscale = (DT == kFP8) ? a.vs[it.n2] : 1.f;
+    // (pdeq: 1 / the P quantisation scale when P·V ran on fp8)
+    const float vscale = ((DT == kFP8) ? a.vs[it.n2] : 1.f) * pdeq;
     if (complete) {
         const float inv = ltot > 0.f ? vscale / ltot : 0.f;
         const int h = it.n2 * a.G + r % a.G;
@@ -902,11 +996,11 @@ __device__ __forceinline__ void write_rows32(const FwdArgs& a, const UnitIter& i
 
 // The 256-row kernel (schedule above) on 32x32 tiles: each wave's 32 query rows are one
 // 32-column tile.
-template <int DT, int OUT, int LAYOUT, bool UM>
+template <int DT, int OUT, int LAYOUT, bool UM, bool P8 = false>
 __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32_kernel(FwdArgs a) {
     constexpr int R = 256;
     constexpr int esz = (DT == kFP8) ? 1 : 2;
-    constexpr int KB = HalfStage<DT>::k_bytes, VB = HalfStage<DT>::v_bytes;
+    constexpr int KB = HalfStage<DT, P8>::k_bytes, VB = HalfStage<DT, P8>::v_bytes;
     // [K buffer 0][K buffer 1][V buffer 0][V buffer 1]
     __shared__ __attribute__((aligned(16))) unsigned char smem[2 * KB + 2 * VB];
     // the task's visible blocks in order: (unit, j * 4 + class, records of half 0, of half 1)
@@ -959,6 +1053,7 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32_kernel(FwdArgs a) {
                 int trow;
                 bool rvalid;
                 load_q32<DT>(a, it, t0, rows_exist, row0, lane, qc, colscale, trow, rvalid);
+                const float pq = P8 ? p_quant(a, it, row0, rows_exist, lane) : 1.f;
                 const UMaskRow um =
                     UM ? umask_row(a, it.b, trow, rvalid) : UMaskRow{make_rsrc(nullptr, 0), -1};
                 f32x16 o[4];
@@ -1040,7 +1135,12 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32_kernel(FwdArgs a) {
                     int mv_rec = __builtin_amdgcn_readfirstlane((move_half(1) & 1) ? m1.w : m1.z);
                     auto softmax_and_move = [&](int k) {
                         const int jc = jc_next;
-                        if constexpr (DT == kFP8) {  // V is widened to bf16 on its way into LDS
+                        if constexpr (P8) {  // fp8 V as it is (P·V on fp8 MFMA)
+                            if (grp == 0)
+                                store_v8<256, 64>(pr, vst + (k & 1) * VB, tg);
+                            else
+                                store_k<DT, 256, 64>(pr, kst + (k & 1) * KB, tg);
+                        } else if constexpr (DT == kFP8) {  // V is widened to bf16 into LDS
                             if (grp == 0)
                                 store_v<DT, 256, 64>(pr, vst + (k & 1) * VB, tg);
                             else
@@ -1062,8 +1162,9 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32_kernel(FwdArgs a) {
                             page_load<DT, 256, 64>(pr, src, rs, tg);
                         }
                         __builtin_amdgcn_sched_barrier(0);
-                        softmax_item32<DT, UM>(a, s, p, colscale, trow, umw, jc >> 2, k & 1, jc & 3,
-                                               skv, off, lane, mrun, lrun, o);
+                        softmax_item32<DT, UM, false, P8>(a, s, p, colscale, trow, umw, jc >> 2,
+                                                          k & 1, jc & 3, skv, off, lane, mrun,
+                                                          lrun, o, pq);
                         pin_softmax(p, lrun);
                         __builtin_amdgcn_sched_barrier(0);
                         const int jn = plist[min(k + 1, nh - 1) >> 1].y;
@@ -1075,23 +1176,24 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32_kernel(FwdArgs a) {
                         mv_rec = __builtin_amdgcn_readfirstlane((qn & 1) ? mn.w : mn.z);
                     };
                     if constexpr (UM) umask_words32(a, um, jc_next >> 2, 0, lane, umw);
-                    mfma_item32<DT, true, false>(kst, vst, qc, s, p, o, lane);
+                    mfma_item32<DT, true, false, P8>(kst, vst, qc, s, p, o, lane);
                     __syncthreads();
                     softmax_and_move(0);
                     for (int k = 1; k < nh; ++k) {
                         if constexpr (UM) umask_words32(a, um, jc_next >> 2, k & 1, lane, umw);
-                        mfma_item32<DT, true, true>(kst + (k & 1) * KB, vst + ((k - 1) & 1) * VB, qc, s,
-                                                    p, o, lane);
+                        mfma_item32<DT, true, true, P8>(kst + (k & 1) * KB, vst + ((k - 1) & 1) * VB,
+                                                        qc, s, p, o, lane);
                         __syncthreads();
                         softmax_and_move(k);
                     }
-                    mfma_item32<DT, false, true>(kst, vst + ((nh - 1) & 1) * VB, qc, s, p, o, lane);
+                    mfma_item32<DT, false, true, P8>(kst, vst + ((nh - 1) & 1) * VB, qc, s, p, o,
+                                                     lane);
                     if (grp == 0) __syncthreads();
                 }
                 __syncthreads();  // LDS (stages, page list) is reused by the next task
 
                 write_rows32<DT, OUT>(a, it, complete, 2 * w + (sa > 0 ? 0 : 1), row0, lane, trow, rvalid,
-                                      mrun, lrun, o);
+                                      mrun, lrun, o, 1.f / pq);
                 if (!complete) {
                     int* list = (int*)smem;  // the stages are free until the next task
                     const int np = piece_arrive(a, w, u, st, a.nst, list);
@@ -1516,11 +1618,11 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32d_kernel(FwdArgs a) {
 // ---------------------------------------------------------------------------------------------
 // The 128-row kernel (schedule above) on 32x32 tiles: each wave's 32 query rows are one
 // 32-column tile.
-template <int DT, int OUT, int LAYOUT, bool UM, bool HS = false>
+template <int DT, int OUT, int LAYOUT, bool UM, bool HS = false, bool P8 = false>
 __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32_kernel(FwdArgs a) {
     constexpr int R = 128;
     constexpr int esz = (DT == kFP8) ? 1 : 2;
-    constexpr int KB = HalfStage<DT>::k_bytes, VB = HalfStage<DT>::v_bytes;
+    constexpr int KB = HalfStage<DT, P8>::k_bytes, VB = HalfStage<DT, P8>::v_bytes;
     constexpr int kStateBytes = 4 * (64 * 64 * 4 + 64 * 16);  // group 1's O, m, l for the merge
     constexpr int kLds = (2 * KB + 2 * VB > kStateBytes) ? 2 * KB + 2 * VB : kStateBytes;
     // [K buffer 0][K buffer 1][V buffer 0][V buffer 1]; reused for the final merge
@@ -1574,6 +1676,7 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32_kernel(FwdArgs a) {
                 int trow;
                 bool rvalid;
                 load_q32<DT>(a, it, t0, rows_exist, row0, lane, qc, colscale, trow, rvalid);
+                const float pq = P8 ? p_quant(a, it, row0, rows_exist, lane) : 1.f;
                 const UMaskRow um =
                     UM ? umask_row(a, it.b, trow, rvalid) : UMaskRow{make_rsrc(nullptr, 0), -1};
                 f32x16 o[4];
@@ -1642,7 +1745,9 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32_kernel(FwdArgs a) {
                     unsigned char* const other_v = vst + (grp ^ 1) * VB;
                     // V of the half page the partner has just exponentiated, into its V buffer
                     auto v_move_store = [&](const PageRegs<DT, 256, 64>& pr) {
-                        if constexpr (DT == kFP8 || !kSharedPitch)
+                        if constexpr (P8)
+                            store_v8<256, 64>(pr, other_v, tg);  // fp8 V as it is
+                        else if constexpr (DT == kFP8 || !kSharedPitch)
                             store_v<DT, 256, 64>(pr, other_v, tg);
                         else
                             store_k<DT, 256, 64>(pr, other_v, tg);  // same row pitch as K
@@ -1658,8 +1763,8 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32_kernel(FwdArgs a) {
                         PageRegs<DT, 256, 64> pr;
                         page_load<DT, 256, 64>(pr, half_src(kbase, 2 * k + 2 + grp), rs, tg);
                         __builtin_amdgcn_sched_barrier(0);
-                        softmax_item32<DT, UM, HS>(a, s, p, colscale, trow, umw, jc >> 2, grp, jc & 3,
-                                               skv, off, lane, mrun, lrun, o);
+                        softmax_item32<DT, UM, HS, P8>(a, s, p, colscale, trow, umw, jc >> 2, grp,
+                                                       jc & 3, skv, off, lane, mrun, lrun, o, pq);
                         pin_softmax(p, lrun);
                         __builtin_amdgcn_sched_barrier(0);
                         store_k<DT, 256, 64>(pr, my_k, tg);
@@ -1670,7 +1775,7 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32_kernel(FwdArgs a) {
                         page_load<DT, 256, 64>(pr, half_src(vbase, grp - 1), rs, tg);
                         mask_words(0);
                         __builtin_amdgcn_sched_barrier(0);
-                        mfma_item32<DT, true, false>(my_k, my_v, qc, s, p, o, lane);
+                        mfma_item32<DT, true, false, P8>(my_k, my_v, qc, s, p, o, lane);
                         __builtin_amdgcn_sched_barrier(0);
                         v_move_store(pr);
                     }
@@ -1681,7 +1786,7 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32_kernel(FwdArgs a) {
                         page_load<DT, 256, 64>(pr, half_src(vbase, 2 * k + grp - 1), rs, tg);
                         mask_words(k);
                         __builtin_amdgcn_sched_barrier(0);
-                        mfma_item32<DT, true, true>(my_k, my_v, qc, s, p, o, lane);
+                        mfma_item32<DT, true, true, P8>(my_k, my_v, qc, s, p, o, lane);
                         __builtin_amdgcn_sched_barrier(0);
                         v_move_store(pr);
                         __syncthreads();
@@ -1691,7 +1796,7 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32_kernel(FwdArgs a) {
                         PageRegs<DT, 256, 64> pr;
                         page_load<DT, 256, 64>(pr, half_src(vbase, 2 * n + grp - 1), rs, tg);
                         __builtin_amdgcn_sched_barrier(0);
-                        mfma_item32<DT, false, true>(my_k, my_v, qc, s, p, o, lane);
+                        mfma_item32<DT, false, true, P8>(my_k, my_v, qc, s, p, o, lane);
                         __builtin_amdgcn_sched_barrier(0);
                         v_move_store(pr);
                     }
@@ -1727,7 +1832,7 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32_kernel(FwdArgs a) {
                             for (int e = 0; e < 4; ++e) o[dt][4 * g4 + e] = o[dt][4 * g4 + e] * a0 + x[e] * a1;
                         }
                     write_rows32<DT, OUT>(a, it, complete, 2 * w + (sa > 0 ? 0 : 1), row0, lane, trow,
-                                          rvalid, mrun, lrun, o);
+                                          rvalid, mrun, lrun, o, 1.f / pq);
                 }
                 __syncthreads();  // LDS is reused by the next task
                 if (!complete) {
@@ -1789,11 +1894,23 @@ hipError_t launch_l(const FwdArgs& a, int rows, hipStream_t s) {
         return launch_k<fwd_prefill_pp32d_kernel<(DT == kFP8 ? kBF16 : DT), OUT, LAYOUT, UM>, !UM>(a,
                                                                                              s);
     }
-    if (rows == 256) return launch_k<fwd_prefill_pp32_kernel<DT, OUT, LAYOUT, UM>, !UM>(a, s);
+    // quant mode 5 with a P quantisation scale: P·V on fp8 MFMA in the two fp8 ping-pong
+    // kernels (the user-mask variants, the decode and the 17-64-row kernels keep P in bf16)
+    constexpr bool kP8 = DT == kFP8 && !UM;
+    if (rows == 256) {
+        if constexpr (kP8)
+            if (a.ps != nullptr)
+                return launch_k<fwd_prefill_pp32_kernel<kFP8, OUT, LAYOUT, false, true>, true>(a, s);
+        return launch_k<fwd_prefill_pp32_kernel<DT, OUT, LAYOUT, UM>, !UM>(a, s);
+    }
     if (a.M > 64) {
         if constexpr (kHalf)
             if (a.half_softmax)
                 return launch_k<fwd_prefill_ks32_kernel<kF16, OUT, LAYOUT, false, true>, true>(a, s);
+        if constexpr (kP8)
+            if (a.ps != nullptr)
+                return launch_k<fwd_prefill_ks32_kernel<kFP8, OUT, LAYOUT, false, false, true>,
+                                true>(a, s);
         return launch_k<fwd_prefill_ks32_kernel<DT, OUT, LAYOUT, UM>, !UM>(a, s);
     }
     // 17-64 rows: the keys of every page are split over 2 or 4 wave groups, so that no wave

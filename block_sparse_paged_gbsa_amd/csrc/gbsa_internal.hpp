@@ -62,6 +62,8 @@ struct FwdArgs {
     int32_t unit_tasks;    // 1: tasks are whole units taken from the queues; 0: worker plan
     int32_t cus;           // compute units of the device
     int32_t half_softmax;  // softmax precision 1 with f16: the 16-bit softmax item
+    const float* ps;       // [N1] P quantisation scales (quant 5), or null: P stays 16-bit
+    float ps_max;          // largest P * scale: the destination type's max, at most 448
     float* ws_o;           // [2P, M, 128]
     float* ws_m;           // [2P, M]  running max, log2 domain
     float* ws_l;           // [2P, M]  running sum

@@ -147,7 +147,10 @@ typedef struct gbsa_params {
                                    Both bounds are the metadata operator's max_seqlen_q /
                                    max_seqlen_kv ("PyTorch API" section); the kernels need
                                    neither, gbsa_validate checks them against the tensors */
-    int32_t reserved[1];        /* must be 0 */
+    float dst_type_max;         /* quant 5 with p_scale: the largest value P * p_scale may take
+                                   before P is cast to e4m3 ("aclnn API" section's dstTypeMax);
+                                   0 = the type's max, 448; larger values are taken as 448.
+                                   Must be finite and >= 0 */
 } gbsa_params;
 
 /*
@@ -211,8 +214,13 @@ gbsa_status gbsa_workspace_size(const gbsa_params* params, size_t* bytes);
  *   cu_seqlens_q [B+1] int64; seqused_q [B] int32 or NULL; seqused_kv [B] int32
  *   block_table  [B, max_blocks_per_seq] int32: physical page of logical block j
  *   q_scale [N1], k_scale [N2], v_scale [N2] float32 dequant scales: required with quant 5,
- *                must be NULL with quant 0; p_scale is accepted for interface parity and
- *                must be NULL (P is kept in 16-bit precision)
+ *                must be NULL with quant 0
+ *   p_scale [N1] float32 or NULL: quant 5 only ("quantisation" section, FP8_E4M3_STATIC_CAST_P:
+ *                the softmax probabilities P of query head h, in [0, 1], are cast to e4m3 after
+ *                scaling by min(p_scale[h], dst_type_max) and P·V runs on fp8; O is divided
+ *                by the scale again). Used by the kernels for more than 64 rows per unit
+ *                without a user mask; the others, and every kernel when p_scale is NULL, keep
+ *                P in bf16 (the more precise form of the same result)
  *   attention_out [T, N1, 128] out_dtype; rows t >= seqused_q[b] are not written
  *   softmax_lse   [T, N1] float32 natural-log LSE of the scaled logits, -inf for a row
  *                 with no visible key (whose output row is 0); required iff return_lse
@@ -291,7 +299,7 @@ typedef struct gbsa_forward_args {
     const float* q_scale;              /* dequant scales, quant 5 only (see gbsa_forward) */
     const float* k_scale;
     const float* v_scale;
-    const float* p_scale;              /* must be NULL */
+    const float* p_scale;              /* [N1] or NULL, as in gbsa_forward */
     /* User attention mask, uint8, or NULL. Entry [t][p] nonzero removes key position p for
      * the batch-local query row t of every head of a sequence, on top of every other rule;
      * entries outside rows x cols do not mask. Layout: entry (b, t, p) at byte

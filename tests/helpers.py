@@ -105,6 +105,7 @@ class GpuProblem:
                 self.umask = self.umask[0]
         f = lambda s: None if s is None else torch.as_tensor(s, dtype=torch.float32).to(d)
         self.qs, self.ks, self.vs = f(p.q_scale), f(p.k_scale), f(p.v_scale)
+        self.ps = None  # [N1] P quantisation scales (quant mode 5), set by a test
 
     def metadata(self, params, metadata=None):
         from block_sparse_paged_gbsa_amd.api import gbsa_metadata
@@ -118,14 +119,14 @@ class GpuProblem:
             return gbsa_forward_ex(params, p.q, p.k, p.v, self.idx, self.cnt, meta, self.cu,
                                    self.squ, cu_seqlens_kv=self.cu_kv, seqused_kv=self.skv,
                                    block_table=self.table, q_scale=self.qs, k_scale=self.ks,
-                                   v_scale=self.vs, atten_mask=self.umask, out=out, lse=lse,
-                                   workspace=workspace)
+                                   v_scale=self.vs, p_scale=self.ps, atten_mask=self.umask,
+                                   out=out, lse=lse, workspace=workspace)
         if self.tnd:
             return gbsa_forward_tnd(params, p.q, p.k, p.v, self.idx, self.cnt, meta, self.cu,
                                     self.squ, self.cu_kv, self.skv, self.qs, self.ks, self.vs,
-                                    None, out, lse, workspace)
+                                    self.ps, out, lse, workspace)
         return gbsa_forward(params, p.q, p.k, p.v, self.idx, self.cnt, meta, self.cu, self.squ,
-                            self.skv, self.table, self.qs, self.ks, self.vs, None, out, lse,
+                            self.skv, self.table, self.qs, self.ks, self.vs, self.ps, out, lse,
                             workspace)
 
     def run(self, num_workers=0, out=None, lse=None):

@@ -110,9 +110,13 @@ def test_max_seqlen_bounds():
     assert _check(tnd) == 0
     tnd.max_seqlen_kv = 1001  # more than the T_kv rows
     assert _check(tnd) == 2
+    for bad in (-1.0, float("nan"), float("inf")):
+        p = _good()
+        p.dst_type_max = bad
+        assert _check(p) == 4
     p = _good()
-    p.reserved[0] = 1
-    assert _check(p) == 4
+    p.dst_type_max = 240.0
+    assert _check(p) == 0
 
 
 def test_entry_points_validate_before_device_work():
@@ -136,8 +140,8 @@ def test_entry_points_validate_before_device_work():
     args2[11] = dummy  # a dequant scale with quant 0
     assert lib.gbsa_forward(ctypes.byref(good), *args2, 1 << 40, None) == 3
     args3 = list(args)
-    args3[13] = dummy  # p_scale is not supported
-    assert lib.gbsa_forward(ctypes.byref(good), *args3, 1 << 40, None) == 4
+    args3[13] = dummy  # p_scale needs quant mode 5
+    assert lib.gbsa_forward(ctypes.byref(good), *args3, 1 << 40, None) == 3
     sz = ctypes.c_size_t(0)
     assert lib.gbsa_workspace_size(ctypes.byref(good), ctypes.byref(sz)) == 0 and sz.value > 0
     n = ctypes.c_int32(0)

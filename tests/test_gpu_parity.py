@@ -596,16 +596,21 @@ def _sampled_rows(p, units, rows_per_unit, rng):
     return rows
 
 
-def _sampled_check(cfg, units, rows_per_unit=None, seed=0, tnd=False, problem=None):
+def _sampled_check(cfg, units, rows_per_unit=None, seed=0, tnd=False, problem=None,
+                   p_scale=None, o_tol=None):
     """A full-size workload in the benchmark's launch configuration, checked against the
     oracle on the rows of the given q-blocks (all KV heads, so every query head), plus an
     all-finite check of every active row. Records the error margins."""
     label = f"workload{cfg}{'_tnd' if tnd else ''}" if problem is None else problem.name
+    if p_scale is not None:
+        label += "_p8"
     _log(f"[parity] {label}: generating on the GPU")
     p = gi.config(cfg, device="cuda") if problem is None else problem
     if tnd:
         p = gi.to_tnd(p)
     gp = GpuProblem(p)
+    if p_scale is not None:
+        gp.ps = torch.full((p.num_heads_q,), p_scale, dtype=torch.float32, device="cuda")
     params, meta, out, lse, ws = gp.run(0)
     words = ws[:256].view(torch.int32).cpu()
     assert int(words[0]) == 0
@@ -622,12 +627,13 @@ def _sampled_check(cfg, units, rows_per_unit=None, seed=0, tnd=False, problem=No
     rows = _sampled_rows(p, units, rows_per_unit, np.random.default_rng(seed))
     idx, O, L = oracle_rows(inp, rows, p.block_x, p.cu_seqlens_q)
     assert len(idx) == len(set(rows)), "a sampled row is not active"
-    err, lerr = compare_rows(p, out, lse if p.return_lse else None, idx, O, L, label)
+    err, lerr = compare_rows(p, out, lse if p.return_lse else None, idx, O, L, label,
+                             o_tol=o_tol)
     _log(f"[parity] {label}: {len(idx)} rows x {p.num_heads_q} heads, O max-abs "
          f"{err:.3e} (bar {TOL[p.dtype]:.1e}), LSE rel {lerr:.3e}")
     record_margin(label, rows=len(idx), heads=p.num_heads_q, q_blocks=len(units),
                   o_max_abs=err, o_bar=TOL[p.dtype], lse_rel=lerr if p.return_lse else None)
-    return p, out
+    return p, out, err
 
 
 def _qblocks(n_active, extra=()):
@@ -760,6 +766,85 @@ def test_half_precision_softmax_other_dtypes_compute_fp32(dtype):
         torch.cuda.synchronize()
         res.append((out.clone(), lse.clone()))
     assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+
+
+# Quant mode 5 with p_quant_scale (GBSA article, "quantisation": FP8_E4M3_STATIC_CAST_P): P is
+# cast to e4m3 after scaling and P·V runs on fp8 MFMA in the 65-256-row and 256-row fp8
+# kernels. The oracle never quantises P (the definition is the same attention), so the result is
+# held to the fp8 bar, 6e-2; LSE uses the unquantised row sums and keeps its bar.
+P8_CASES = [
+    dict(seed=171, num_heads_q=16, num_heads_kv=2, block_x=16, top_k=6, mask_mode=1,
+         max_len=600, scale=448.0),
+    dict(seed=172, num_heads_q=32, num_heads_kv=4, block_x=64, top_k=5, mask_mode=1,
+         max_len=900, use_seqused_q=True, scale=448.0),
+    dict(seed=173, num_heads_q=8, num_heads_kv=1, block_x=32, top_k=8, mask_mode=0,
+         win_left=150, win_right=20, max_len=700, scale=None),  # per-head scales (below)
+    dict(seed=174, num_heads_q=16, num_heads_kv=4, block_x=128, top_k=4, mask_mode=1,
+         max_len=500, scale=1000.0, dst_type_max=240.0),  # the scale clamped to 240
+]
+
+
+@pytest.mark.parametrize("case", P8_CASES, ids=[str(c["seed"]) for c in P8_CASES])
+def test_fp8_p_quantised_pv(case):
+    """fp8 P·V (both fp8 ping-pong kernels), every row against the oracle, at one and at three
+    worker counts' splits; without p_quant_scale the same problem keeps P in bf16."""
+    kw = {k: v for k, v in case.items() if k not in ("seed", "scale", "dst_type_max")}
+    p = gi.random_problem(case["seed"], device="cuda", dtype="fp8", return_lse=True, **kw)
+    gp = GpuProblem(p)
+    O, L, done = oa.sparse_attention(oracle_inputs(p))
+    scale = case["scale"]
+    # per-head scales that e4m3 holds exactly, so that each row's largest weight (P = 1) is cast
+    # without error (a scale such as 100 puts a 4 % error on it, and the O error of that case
+    # doubles: a property of the cast, reproduced by a CPU emulation of it)
+    per_head = [448.0, 256.0, 224.0, 192.0, 160.0, 128.0, 112.0, 96.0]
+    gp.ps = (torch.full((p.num_heads_q,), scale, dtype=torch.float32, device="cuda")
+             if scale is not None else
+             torch.tensor([per_head[h % 8] for h in range(p.num_heads_q)], dtype=torch.float32,
+                          device="cuda"))
+    for workers in (0, 5):
+        params = gpu_params(p, workers)
+        params.dst_type_max = case.get("dst_type_max", 0.0)
+        meta = gp.metadata(params)
+        out, lse, ws = gp.forward(params, meta)
+        torch.cuda.synchronize()
+        assert int(ws[:4].view(torch.int32)[0].item()) == 0
+        label = f"fp8_p_{case['seed']}_w{workers}"
+        err, lerr = compare(p, out, lse, O, L, done, label)
+        record_margin(label, rows=int(done.sum()), heads=p.num_heads_q, o_max_abs=err,
+                      o_bar=TOL["fp8"], lse_rel=lerr)
+    gp.ps = None
+    params = gpu_params(p)
+    out16, _, _ = gp.forward(params, gp.metadata(params))
+    err16, _ = compare(p, out16, None, O, L, done, f"fp8_p_{case['seed']}_bf16P")
+    _log(f"[parity] fp8 P {case['seed']}: O {err:.2e} (bf16 P {err16:.2e}), LSE rel {lerr:.2e}")
+
+
+def test_fp8_p_scale_ignored_where_p_stays_bf16():
+    """The decode and 17-64-row kernels keep P in bf16: p_quant_scale leaves their output bit
+    for bit as without it."""
+    for kw in (dict(decode=True, batch=4, block_x=1, num_heads_q=8, num_heads_kv=2),
+               dict(batch=2, max_len=400, block_x=8, num_heads_q=8, num_heads_kv=2)):
+        p = gi.random_problem(175, device="cuda", dtype="fp8", top_k=5, mask_mode=1, **kw)
+        gp = GpuProblem(p)
+        params = gpu_params(p)
+        meta = gp.metadata(params)
+        ref, _, _ = gp.forward(params, meta)
+        gp.ps = torch.full((p.num_heads_q,), 448.0, dtype=torch.float32, device="cuda")
+        out, _, _ = gp.forward(params, meta)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), kw
+
+
+@pytest.mark.xfail(strict=True, reason="casting P to e4m3 (3 mantissa bits: up to 6 % per weight) "
+                   "puts workload 5's largest O error at 0.066, over the 6e-2 fp8 bar; the "
+                   "default keeps P in bf16 (0.009)")
+def test_workload5_fp8_p_quantised_sampled():
+    """Workload 5 with p_quant_scale 448 for every head: P cast to e4m3 and P·V on fp8 MFMA,
+    in the benchmark's launch configuration; the same q-blocks as the bf16-P check. The error
+    is measured and recorded first, then held to the fp8 bar (which it misses: expected)."""
+    units = [(b, gl) for b in range(2) for gl in _qblocks(256, (100, 128))]
+    _, _, err = _sampled_check(5, units, rows_per_unit=32, p_scale=448.0, o_tol=float("inf"))
+    assert err <= TOL["fp8"], f"fp8 P: O max-abs {err}"
 
 
 def test_workload2_decode_tnd_sampled():

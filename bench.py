@@ -39,6 +39,7 @@ KERNEL_SOURCES = {
     "fwd_prefill_pp32_kernel": ["fwd_prefill.hip"],
     "fwd_prefill_pp32d_kernel": ["fwd_prefill.hip"],
     "fwd_prefill_ks32_kernel": ["fwd_prefill.hip"],
+    "fwd_prefill_ks32d_kernel": ["fwd_prefill.hip"],
 }
 SHARED_SOURCES = ["device_common.hpp", "gbsa_internal.hpp", "split_merge.hpp"]
 
@@ -72,7 +73,9 @@ def measured_traffic(kernel: str, workload: str):
 
 
 TRACE_EVENTS = {1: "softmax start", 2: "softmax end", 3: "softmax barrier in",
-                4: "softmax barrier out", 5: "MFMA start", 6: "MFMA end", 7: "MFMA barrier out"}
+                4: "softmax barrier out", 5: "MFMA start", 6: "MFMA end", 7: "MFMA barrier out",
+                8: "K stored", 9: "MFMA issued"}
+TRACED_KERNELS = ("fwd_prefill_pp32d_kernel", "fwd_prefill_ks32_kernel", "fwd_prefill_ks32d_kernel")
 
 
 def slot_trace(w, p) -> int:
@@ -83,8 +86,8 @@ def slot_trace(w, p) -> int:
     import numpy as np
     import torch
     from block_sparse_paged_gbsa_amd import _lib
-    if w.kernel != "fwd_prefill_pp32d_kernel":
-        print(f"--slot-trace traces fwd_prefill_pp32d_kernel; this workload runs {w.kernel}",
+    if w.kernel not in TRACED_KERNELS:
+        print(f"--slot-trace traces {', '.join(TRACED_KERNELS)}; this workload runs {w.kernel}",
               file=sys.stderr)
         return 2
     lib = ctypes.CDLL(_lib.LIB_PATH)
@@ -428,11 +431,21 @@ class Workload:
                     if p.return_lse else None)
         self.ws = torch.zeros(gbsa_workspace_size(self.params), dtype=torch.uint8, device=dev)
         self.P = gbsa_num_workers(self.params)
-        rows = p.block_x * p.num_heads_q // p.num_heads_kv  # packed GQA rows per unit
-        self.kernel = ("fwd_decode_kernel" if rows <= 16 else
-                       ("fwd_prefill_pp32_kernel" if p.dtype == "fp8" else
-                        "fwd_prefill_pp32d_kernel") if rows > 256 else
-                       "fwd_prefill_ks32_kernel" if rows > 64 else "fwd_prefill_kernel")
+        self.rows = p.block_x * p.num_heads_q // p.num_heads_kv  # packed GQA rows per unit
+
+    @property
+    def kernel(self):
+        """The main kernel the library picks for this workload (rows per unit, dtype, options)."""
+        rows, fp8 = self.rows, self.p.dtype == "fp8"
+        if rows <= 16:
+            return "fwd_decode_kernel"
+        if rows > 256:
+            return "fwd_prefill_pp32_kernel" if fp8 else "fwd_prefill_pp32d_kernel"
+        if rows > 64:
+            # fp8 without a user mask or P quantisation scale: the DMA key-split kernel
+            dma = fp8 and self.umask is None and self.ps is None
+            return "fwd_prefill_ks32d_kernel" if dma else "fwd_prefill_ks32_kernel"
+        return "fwd_prefill_kernel"
 
     def metadata(self):
         from block_sparse_paged_gbsa_amd import gbsa_metadata

@@ -1226,11 +1226,13 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32_kernel(FwdArgs a) {
 // flight across a barrier.
 // ---------------------------------------------------------------------------------------------
 // Slot trace (diagnostic build, -DGBSA_SLOT_TRACE, libgbsa_slot_trace.so). The first unit of
-// at least 12 pages that a workgroup of the DMA kernel meets (one per launch, claimed with an
-// atomic) records, per wave, an s_memtime stamp (shader clock) at every item boundary of its
-// loop: event codes 1 softmax item start, 2 softmax item end, 3 before its barrier, 4 after it,
-// 5 MFMA item start, 6 MFMA item end (loads waited for), 7 after its barrier. In the normal
-// build the marks compile to nothing.
+// at least 12 pages that a workgroup of one of the ping-pong kernels (the two DMA kernels, the
+// register-staged key-split kernel) meets (one per launch, claimed with an atomic) records, per
+// wave, an s_memtime stamp (shader clock) at every item boundary of its loop: event codes 1
+// softmax item start, 2 softmax item end, 3 before its barrier, 4 after it, 5 MFMA item start,
+// 6 MFMA item end (loads waited for), 7 after its barrier; the register-staged key-split kernel
+// adds 8 K stored (its load waited for) and 9 MFMA instructions issued (before the V store). In
+// the normal build the marks compile to nothing.
 constexpr int kTraceEvents = 1024;  // per wave
 #ifdef GBSA_SLOT_TRACE
 __device__ unsigned long long g_slot_trace[8 * kTraceEvents];
@@ -1628,7 +1630,7 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32_kernel(FwdArgs a) {
     // [K buffer 0][K buffer 1][V buffer 0][V buffer 1]; reused for the final merge
     __shared__ __attribute__((aligned(16))) unsigned char smem[kLds];
     __shared__ int4 plist[256];  // as in the row-split kernel
-    __shared__ int flag[1];
+    __shared__ int flag[2];
     static_assert(sizeof(smem) >= kPieceListBytes, "the split merge borrows the stages");
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -1709,10 +1711,15 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32_kernel(FwdArgs a) {
                         }
                         n += __builtin_popcountll(m);
                     }
-                    if (lane == 0) flag[0] = n;
+                    if (lane == 0) {
+                        flag[0] = n;
+                        flag[1] = slot_trace_claim(n);
+                    }
                 }
                 __syncthreads();
                 const int n = __builtin_amdgcn_readfirstlane(flag[0]);  // items per group
+                SlotTrace tr;
+                tr.begin(__builtin_amdgcn_readfirstlane(flag[1]) != 0, wave);
                 const int nh = 2 * n;                                   // half pages
 
                 // address of half page q (K or V) of this head in HBM; q is clamped into the stream
@@ -1760,6 +1767,7 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32_kernel(FwdArgs a) {
                     };
                     auto softmax_and_move = [&](int k) {
                         const int jc = __builtin_amdgcn_readfirstlane(plist[k].y);
+                        tr.mark(1, lane);
                         PageRegs<DT, 256, 64> pr;
                         page_load<DT, 256, 64>(pr, half_src(kbase, 2 * k + 2 + grp), rs, tg);
                         __builtin_amdgcn_sched_barrier(0);
@@ -1767,8 +1775,11 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32_kernel(FwdArgs a) {
                                                        jc & 3, skv, off, lane, mrun, lrun, o, pq);
                         pin_softmax(p, lrun);
                         __builtin_amdgcn_sched_barrier(0);
+                        tr.mark(2, lane);
                         store_k<DT, 256, 64>(pr, my_k, tg);
+                        tr.mark(8, lane);
                         __syncthreads();
+                        tr.mark(4, lane);
                     };
                     {
                         PageRegs<DT, 256, 64> pr;
@@ -1782,14 +1793,18 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32_kernel(FwdArgs a) {
                     __syncthreads();
                     softmax_and_move(0);
                     for (int k = 1; k < n; ++k) {
+                        tr.mark(5, lane);
                         PageRegs<DT, 256, 64> pr;
                         page_load<DT, 256, 64>(pr, half_src(vbase, 2 * k + grp - 1), rs, tg);
                         mask_words(k);
                         __builtin_amdgcn_sched_barrier(0);
                         mfma_item32<DT, true, true, P8>(my_k, my_v, qc, s, p, o, lane);
                         __builtin_amdgcn_sched_barrier(0);
+                        tr.mark(9, lane);
                         v_move_store(pr);
+                        tr.mark(6, lane);
                         __syncthreads();
+                        tr.mark(7, lane);
                         softmax_and_move(k);
                     }
                     {
@@ -1833,6 +1848,370 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32_kernel(FwdArgs a) {
                         }
                     write_rows32<DT, OUT>(a, it, complete, 2 * w + (sa > 0 ? 0 : 1), row0, lane, trow,
                                           rvalid, mrun, lrun, o, 1.f / pq);
+                }
+                __syncthreads();  // LDS is reused by the next task
+                if (!complete) {
+                    int* list = (int*)smem;  // the stages are free until the next task
+                    const int np = piece_arrive(a, w, u, st, a.nst, list);
+                    if (np > 0)
+                        merge_rows<OUT>(a, list, np, row_base, min(row_base + R, rows_exist), it.n2,
+                                        t0, it.row0, it.sq);
+                    __syncthreads();
+                }
+            }
+            advance_unit(a, it);
+        }
+    });
+}
+
+// ---------------------------------------------------------------------------------------------
+// The 128-row key-split kernel with K and V moved by LDS DMA (fp8 key/value, no user mask, P in
+// bf16). Same slots and items as fwd_prefill_ks32_kernel, but the half pages reach LDS as e4m3
+// rows by `buffer_load ... lds` issued from inside the MFMA items, so no load has to land within
+// the slot that issues it: global half page q (group q % 2's item q / 2) has K_q read in slot q
+// and V_q in slot q + 2; the group running its MFMA item in slot s moves K_{s+4} and V_{s+2}
+// (clamped into the stream, so every item issues the same four instructions per wave), each wave
+// two DMA instructions of each. Before the barrier that ends its softmax item a wave waits for all
+// but its newest batch, so a move issued in slot s has landed by the end of slot s + 3, before
+// its reader in slot s + 4; both rings (eight half-page buffers each, indexed q % 8) are
+// rewritten only after their last reader. V^T comes from the e4m3 rows with the 8-bit
+// transposing read and is widened exactly to bf16 in registers right before its MFMA.
+//
+// LDS layout of an fp8 half page (64 rows of 128 B): DMA instruction i (0..7) writes rows
+// 8 i .. 8 i + 7 as 1 KB at byte 1024 i; 16-byte chunk c of row r (head dims 16 c ..) sits at
+// position c ^ sw8(r) of the row. sw8 permutes the three bits of (r / 2) % 8 so that both read
+// patterns are free of bank conflicts: the K fragment reads (16 consecutive rows, one chunk)
+// cover the 16 bank groups of 256 B once, and so do the transposing V reads of a half wave
+// (rows b .. b + 3 and b + 8 .. b + 11 for b a multiple of 4, two adjacent chunks).
+// ---------------------------------------------------------------------------------------------
+constexpr int kHalf8 = 64 * 128;  // one fp8 half page
+
+__device__ __forceinline__ int sw8(int r) {
+    const int x = (r >> 1) & 7;
+    return ((x & 1) << 2) | (x >> 1);
+}
+
+// DMA instruction i (0..7) of the fp8 half page behind buffer resource r into buffer dst.
+__device__ __forceinline__ void dma8_one(rsrc_t r, int rs, unsigned char* dst, int i, int lane) {
+    const int row = 8 * i + (lane >> 3);
+    const int voff = row * rs + 16 * ((lane & 7) ^ sw8(row));
+    const uint32_t m0 = (uint32_t)(uintptr_t)(GBSA_LDS unsigned char*)(dst + i * 1024);
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(m0), "v"(voff), "s"(r)
+                 : "memory", "m0");
+}
+
+// The two half-page moves of one MFMA item (K_{s+4} and V_{s+2}), two DMA instructions each per
+// wave.
+struct ItemMove8 {
+    const u32x4* kent;  // LDS page-list entries of the two half pages
+    const u32x4* vent;
+    unsigned char* kdst;  // their buffers
+    unsigned char* vdst;
+    int khalf, vhalf;  // which half of each page
+    int i0;            // first of the wave's two DMA instructions of each move
+};
+
+// Both moves of an item at once (the first item, which has too few steps to spread them).
+__device__ __forceinline__ void moves8_now(const ItemMove8& mv, const unsigned char* kbase,
+                                           const unsigned char* vbase, int rs, int lane) {
+    const KvSrc ks = page_half(kbase, *(const GBSA_LDS u32x4*)mv.kent, mv.khalf, rs);
+    const rsrc_t rk = make_rsrc(ks.p, ks.records);
+    dma8_one(rk, rs, mv.kdst, mv.i0, lane);
+    dma8_one(rk, rs, mv.kdst, mv.i0 + 1, lane);
+    const KvSrc vsrc = page_half(vbase, *(const GBSA_LDS u32x4*)mv.vent, mv.vhalf, rs);
+    const rsrc_t rv = make_rsrc(vsrc.p, vsrc.records);
+    dma8_one(rv, rs, mv.vdst, mv.i0, lane);
+    dma8_one(rv, rs, mv.vdst, mv.i0 + 1, lane);
+}
+
+// MFMA item of the fp8 DMA kernel: QK^T of a half page on v_mfma_scale_f32_32x32x64_f8f6f4 (two
+// steps per 32-key tile) and PV of the previous one on bf16 MFMA (eight steps per tile, V^T
+// widened from e4m3 in registers), optionally issuing the item's two moves between its MFMAs
+// (entries read at steps 0 and 1, DMA at steps 4, 6, 8, 10).
+template <bool qk, bool pv, bool MOVE = false>
+__device__ __forceinline__ void mfma_item32d8(const unsigned char* ks, const unsigned char* vs,
+                                              const QCol32& qc, f32x16 (&s)[2],
+                                              const u32x4 (&p)[4], f32x16 (&o)[4], int lane,
+                                              const ItemMove8& mv = ItemMove8{},
+                                              const unsigned char* kbase = nullptr,
+                                              const unsigned char* vbase = nullptr, int rs = 0) {
+    constexpr int QS = qk ? 2 : 0;
+    constexpr int VS = pv ? 8 : 0;
+    constexpr int PC = QS + VS, NS = 2 * PC, D = kPipeDepth;
+    const int h2 = lane >> 5;
+    // K: row 32 t + lane % 32, chunks 4 e + 2 h and + 1 (head dims 64 e + 32 h ..)
+    const int kr = lane & 31, ksw = sw8(kr);
+    const unsigned char* krow = ks + kr * 128;
+    // V^T: block row (lane % 16) / 2 is key 4 h + m % 4 + 8 (m / 4) of each 16-key chunk, byte
+    // half lane % 2 of chunk 2 dt + (lane / 16) % 2
+    const int m = (lane & 15) >> 1, kv = 4 * h2 + (m & 3) + 8 * (m >> 2);
+    const int vseg = (lane >> 4) & 1, vsw = sw8(kv);
+    const unsigned char* vrow = vs + kv * 128 + 8 * (lane & 1);
+    const f32x16 zero = {};
+    auto load = [&](int st) {
+        Frag f;
+        const int t = st / PC, j = st % PC;
+        if (j < QS) {
+            const unsigned char* kp = krow + t * 4096;
+            f.a = *(const u32x4*)(kp + 16 * ((4 * j + 2 * h2) ^ ksw));
+            f.b = *(const u32x4*)(kp + 16 * ((4 * j + 2 * h2 + 1) ^ ksw));
+        } else {
+            const int v = j - QS, a2 = v >> 2, dt = v & 3;
+            const u32x2 r = lds_read_tr8(vrow + (32 * t + 16 * a2) * 128 + 16 * ((2 * dt + vseg) ^ vsw));
+            f.a = (u32x4){r[0], r[1], 0u, 0u};
+        }
+        return f;
+    };
+    auto compute = [&](int st, const Frag& f) {
+        const int t = st / PC, j = st % PC;
+        if (j < QS) {
+            s[t] = mfma_32x32x64_fp8(f.a, f.b, qc.q[2 * j], qc.q[2 * j + 1], j == 0 ? zero : s[t]);
+        } else {
+            const int v = j - QS, a2 = v >> 2, dt = v & 3;
+            const u32x2 w0 = fp8x4_to_bf16x4(f.a[0]), w1 = fp8x4_to_bf16x4(f.a[1]);
+            o[dt] = mfma_32x32x16<kBF16>((u32x4){w0[0], w0[1], w1[0], w1[1]}, p[2 * t + a2], o[dt]);
+        }
+    };
+    static_assert(!MOVE || NS >= 11, "the moves need eleven steps");
+    u32x4 ek, ev;
+    rsrc_t rk, rv;
+    Frag fr[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i)
+        if (i < NS) fr[i] = load(i);
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+        const Frag f = fr[st % D];
+        if (st + D < NS) fr[st % D] = load(st + D);
+        if constexpr (MOVE) {
+            if (st == 0) ek = *(const GBSA_LDS u32x4*)mv.kent;
+            if (st == 1) ev = *(const GBSA_LDS u32x4*)mv.vent;
+            if (st == 2) {
+                const KvSrc src = page_half(kbase, ek, mv.khalf, rs);
+                rk = make_rsrc(src.p, src.records);
+            }
+            if (st == 3) {
+                const KvSrc src = page_half(vbase, ev, mv.vhalf, rs);
+                rv = make_rsrc(src.p, src.records);
+            }
+            if (st == 4 || st == 6) dma8_one(rk, rs, mv.kdst, mv.i0 + (st - 4) / 2, lane);
+            if (st == 8 || st == 10) dma8_one(rv, rs, mv.vdst, mv.i0 + (st - 8) / 2, lane);
+        }
+        compute(st, f);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+template <int OUT, int LAYOUT>
+__global__ __launch_bounds__(512, 1) void fwd_prefill_ks32d_kernel(FwdArgs a) {
+    constexpr int DT = kFP8;
+    constexpr int R = 128;
+    constexpr int esz = 1;
+    constexpr int kStateBytes = 4 * (64 * 64 * 4 + 64 * 16);  // group 1's O, m, l for the merge
+    constexpr int kLds = (16 * kHalf8 > kStateBytes) ? 16 * kHalf8 : kStateBytes;
+    // [K buffers 0..7][V buffers 0..7], one fp8 half page each; reused for the final merge
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kLds];
+    // per visible page: byte offset of this head's slice, readable bytes of its two halves
+    __shared__ u32x4 plist[256];
+    __shared__ int jlist[256];  // per visible page: block index * 4 + mask class
+    __shared__ int flag[2];     // visible pages of the unit; slot trace on
+    static_assert(sizeof(smem) >= kPieceListBytes, "the split merge borrows the stages");
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2;  // waves w and w + 4 share a SIMD and the same query rows
+    const int gw = wave & 3;    // wave within its group
+    if (!header_ok(a)) {
+        refuse(a);
+        return;
+    }
+    const int U = a.meta[3];
+    __shared__ int task_word[2];
+    run_tasks<true>(a, U, task_word, [&](const FwdArgs& a, const Task& tk) {
+        const int w = tk.w, st = tk.st;
+        const Bound b0 = tk.b0, b1 = tk.b1;
+        if (!bound_less(b0, b1) || b0.u >= U) return;
+        UnitIter it = locate_unit(a, b0.u);
+        if (it.b < 0) return;
+
+        const int rs = a.N2 * 128 * esz;
+        const unsigned char* kbase = (const unsigned char*)a.k;
+        const unsigned char* vbase = (const unsigned char*)a.v;
+        unsigned char* const kst = smem;
+        unsigned char* const vst = smem + 8 * kHalf8;
+
+        for (int u = b0.u;; ++u) {
+            const int sa = (u == b0.u) ? b0.s : 0;
+            if (u >= U || u > b1.u || (u == b1.u && sa >= b1.s)) break;
+            const int g = it.qbase + it.gl;
+            int cnt = 0;
+            if (g < a.tqb) cnt = min(max(a.cnt[(int64_t)it.n2 * a.tqb + g], 0), a.topK);
+            const int se = (u == b1.u) ? b1.s : cnt;
+            const bool complete = (sa == 0) && (se == cnt);
+
+            const int t0 = it.gl * a.X;
+            const int rows_exist = min(a.X, it.storage - t0) * a.G;
+            const int row_base = st * R;
+            if (row_base < rows_exist) {
+                const KvSeq kv = kv_seq<LAYOUT>(a, it.b);
+                const int skv = kv.len;
+                const int off = diag_off(a, skv, it.sq);
+                const int row0 = row_base + gw * 32;
+                QCol32 qc;
+                float colscale, mrun = kNegInf, lrun = 0.f;
+                int trow;
+                bool rvalid;
+                load_q32<DT>(a, it, t0, rows_exist, row0, lane, qc, colscale, trow, rvalid);
+                f32x16 o[4];
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) o[dt] = (f32x16){};
+                const int t_lo = t0 + row_base / a.G;
+                const int t_hi = t0 + (min(row_base + R, rows_exist) - 1) / a.G;
+                const int32_t* sel = a.idx + ((int64_t)it.n2 * a.tqb + g) * a.topK;
+                const int64_t head_off = (int64_t)it.n2 * 128 * esz;
+
+                if (wave == 0) {
+                    int n = 0;
+                    for (int c0 = sa; c0 < se; c0 += 64) {
+                        int jl = -1, pl = 0, cl = 0;
+                        if (c0 + lane < se) {
+                            jl = sel[c0 + lane];
+                            if (jl >= 0) {
+                                cl = block_class(a, (int64_t)jl * 128, skv, off, t_lo, t_hi);
+                                if (cl != 0) pl = kv.unit<LAYOUT>(jl);
+                            }
+                        }
+                        const uint64_t mm = __ballot(cl != 0);
+                        if (cl != 0) {
+                            const int pos = n + __builtin_amdgcn_mbcnt_hi(
+                                                    (uint32_t)(mm >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mm, 0));
+                            const uint64_t po = (uint64_t)((int64_t)pl * a.kv_stride * esz + head_off);
+                            plist[pos] = (u32x4){(uint32_t)po, (uint32_t)(po >> 32),
+                                                 (uint32_t)kv_records(rs, skv - 128 * jl),
+                                                 (uint32_t)kv_records(rs, skv - 128 * jl - 64)};
+                            jlist[pos] = jl * 4 + cl;
+                        }
+                        n += __builtin_popcountll(mm);
+                    }
+                    if (lane == 0) {
+                        flag[0] = n;
+                        flag[1] = slot_trace_claim(n);
+                    }
+                }
+                __syncthreads();
+                const int n = __builtin_amdgcn_readfirstlane(flag[0]);  // items per group
+                const int nh = 2 * n;                                   // half pages
+                SlotTrace tr;
+                tr.begin(__builtin_amdgcn_readfirstlane(flag[1]) != 0, wave);
+
+                if (n > 0) {
+                    f32x16 s[2];
+                    u32x4 p[4];
+                    const uint32_t umw[8] = {};  // (no user mask)
+                    // Before the first slot: K_0 .. K_3, V_0 and V_1 by all eight waves
+                    // (instruction `wave` of each); group 1 then starts one slot late.
+                    auto pre_move = [&](const unsigned char* base, int q, unsigned char* dst) {
+                        q = min(q, nh - 1);
+                        const KvSrc src = page_half(base, plist[q >> 1], q & 1, rs);
+                        dma8_one(make_rsrc(src.p, src.records), rs, dst, wave, lane);
+                    };
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) pre_move(kbase, q, kst + q * kHalf8);
+                    pre_move(vbase, 0, vst);
+                    pre_move(vbase, 1, vst + kHalf8);
+                    wait_vm<0>();
+                    __syncthreads();
+                    if (grp == 1) __syncthreads();
+                    // the moves of this group's MFMA item k (slot q = 2 k + grp): K_{q+4} and
+                    // V_{q+2}, sources clamped into the stream (a clamped move fills a buffer
+                    // that is not read again)
+                    auto move_of = [&](int k) {
+                        const int q = 2 * k + grp;
+                        const int kq = min(q + 4, nh - 1), vq = min(q + 2, nh - 1);
+                        return ItemMove8{plist + (kq >> 1), plist + (vq >> 1),
+                                         kst + ((q + 4) & 7) * kHalf8, vst + ((q + 2) & 7) * kHalf8,
+                                         kq & 1, vq & 1, 2 * gw};
+                    };
+                    int jc_next = __builtin_amdgcn_readfirstlane(jlist[0]);
+                    auto softmax_item = [&](int k) {
+                        const int jc = jc_next;
+                        __builtin_amdgcn_sched_barrier(0);
+                        tr.mark(1, lane);
+                        softmax_item32<DT, false>(a, s, p, colscale, trow, umw, jc >> 2, grp,
+                                                  jc & 3, skv, off, lane, mrun, lrun, o);
+                        pin_softmax(p, lrun);
+                        __builtin_amdgcn_sched_barrier(0);
+                        tr.mark(2, lane);
+                        const int jn = jlist[min(k + 1, n - 1)];
+                        wait_vm<4>();  // all but the moves of this wave's last MFMA item are in LDS
+                        tr.mark(3, lane);
+                        __syncthreads();
+                        tr.mark(4, lane);
+                        jc_next = __builtin_amdgcn_readfirstlane(jn);
+                    };
+                    // Issue priority as in the 256-row DMA kernel: the MFMA items run raised.
+                    {
+                        moves8_now(move_of(0), kbase, vbase, rs, lane);
+                        __builtin_amdgcn_s_setprio(3);
+                        mfma_item32d8<true, false>(kst + grp * kHalf8, vst, qc, s, p, o, lane);
+                        __builtin_amdgcn_s_setprio(0);
+                        __syncthreads();
+                    }
+                    softmax_item(0);
+                    for (int k = 1; k < n; ++k) {
+                        const int q = 2 * k + grp;
+                        tr.mark(5, lane);
+                        __builtin_amdgcn_s_setprio(3);
+                        mfma_item32d8<true, true, true>(kst + (q & 7) * kHalf8,
+                                                        vst + ((q - 2) & 7) * kHalf8, qc, s, p, o,
+                                                        lane, move_of(k), kbase, vbase, rs);
+                        __builtin_amdgcn_s_setprio(0);
+                        tr.mark(6, lane);
+                        __syncthreads();
+                        tr.mark(7, lane);
+                        softmax_item(k);
+                    }
+                    __builtin_amdgcn_s_setprio(3);
+                    mfma_item32d8<false, true>(kst, vst + ((nh - 2 + grp) & 7) * kHalf8, qc, s, p, o,
+                                               lane);
+                    __builtin_amdgcn_s_setprio(0);
+                    wait_vm<0>();  // nothing may land in LDS after the task
+                    if (grp == 0) __syncthreads();
+                }
+                __syncthreads();  // stages are free: group 1 hands its row states to group 0
+
+                if (grp == 1) {
+                    f32x4* so = (f32x4*)(smem + gw * (64 * 64 * 4 + 64 * 16));
+#pragma unroll
+                    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                        for (int g4 = 0; g4 < 4; ++g4)
+                            so[(dt * 4 + g4) * 64 + lane] = (f32x4){o[dt][4 * g4], o[dt][4 * g4 + 1],
+                                                                   o[dt][4 * g4 + 2], o[dt][4 * g4 + 3]};
+                    so[16 * 64 + lane] = (f32x4){mrun, lrun, 0.f, 0.f};
+                }
+                __syncthreads();
+                if (grp == 0) {
+                    const f32x4* so = (const f32x4*)(smem + gw * (64 * 64 * 4 + 64 * 16));
+                    const f32x4 ml = so[16 * 64 + lane];
+                    const float m = fmaxf(mrun, ml[0]);
+                    const float a0 = (m == kNegInf) ? 0.f : fast_exp2(mrun - m);
+                    const float a1 = (m == kNegInf) ? 0.f : fast_exp2(ml[0] - m);
+                    mrun = m;
+                    lrun = lrun * a0 + ml[1] * a1;
+#pragma unroll
+                    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                        for (int g4 = 0; g4 < 4; ++g4) {
+                            const f32x4 x = so[(dt * 4 + g4) * 64 + lane];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) o[dt][4 * g4 + e] = o[dt][4 * g4 + e] * a0 + x[e] * a1;
+                        }
+                    write_rows32<DT, OUT>(a, it, complete, 2 * w + (sa > 0 ? 0 : 1), row0, lane, trow,
+                                          rvalid, mrun, lrun, o);
                 }
                 __syncthreads();  // LDS is reused by the next task
                 if (!complete) {
@@ -1911,7 +2290,11 @@ hipError_t launch_l(const FwdArgs& a, int rows, hipStream_t s) {
             if (a.ps != nullptr)
                 return launch_k<fwd_prefill_ks32_kernel<kFP8, OUT, LAYOUT, false, false, true>,
                                 true>(a, s);
-        return launch_k<fwd_prefill_ks32_kernel<DT, OUT, LAYOUT, UM>, !UM>(a, s);
+        // fp8 without a user mask: the DMA kernel
+        if constexpr (DT == kFP8 && !UM)
+            return launch_k<fwd_prefill_ks32d_kernel<OUT, LAYOUT>, true>(a, s);
+        else
+            return launch_k<fwd_prefill_ks32_kernel<DT, OUT, LAYOUT, UM>, !UM>(a, s);
     }
     // 17-64 rows: the keys of every page are split over 2 or 4 wave groups, so that no wave
     // computes on missing rows and each page goes through LDS 2 or 4 times, not 8

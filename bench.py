@@ -488,11 +488,21 @@ def cache_flusher(dev):
 
 
 def cold_forward_ms(w, flush, iters: int, stream) -> float:
-    """The forward's average duration when every launch follows a cache-evicting read:
-    (flush + forward) x iters minus flush x iters, each back to back between two events."""
-    both = timed(lambda: (flush(), w.forward()), iters, stream)
-    alone = timed(flush, iters, stream)
-    return both - alone
+    """The forward's average duration when every launch follows a cache-evicting read: each
+    launch timed on its own between two events on its stream, recorded after the read has
+    finished there (subtracting a separately timed read would add that read's jitter)."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(iters)]
+    flush()
+    w.forward()
+    for e0, e1 in ev:
+        flush()
+        e0.record(stream)
+        w.forward()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return sum(e0.elapsed_time(e1) for e0, e1 in ev) / iters
 
 
 def roofline(w, alg_bytes, alg_flops, fwd_ms):

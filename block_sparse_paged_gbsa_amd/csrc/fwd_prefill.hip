@@ -878,14 +878,17 @@ __device__ __forceinline__ void softmax_item32(const FwdArgs& a, f32x16 (&s)[2],
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[t][i]);
     mx = pair_max(mx, true);
     const float bmax = mx == kNegInf ? kNegInf : mx * colscale;
-    const float mnew = P8 ? fmaxf(mrun, bmax) : lazy_max(mrun, bmax);
-    const float muse = (mnew == kNegInf) ? 0.f : mnew;
-    const float alpha = fast_exp2(mrun - muse);
-    mrun = mnew;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {  // skipped unless some running max moved
+    float alpha = 1.f;
+    // The running max, its exp2 and the O rescale only where some row's max moves (always
+    // on a row's first visible block; rarely later with the lazy max): elsewhere alpha is 1.
+    if (__builtin_amdgcn_ballot_w64(P8 ? bmax > mrun : bmax > mrun + kLazyMax)) {
+        const float mnew = P8 ? fmaxf(mrun, bmax) : lazy_max(mrun, bmax);
+        alpha = fast_exp2(mrun - ((mnew == kNegInf) ? 0.f : mnew));
+        mrun = mnew;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
     }
+    const float muse = (mrun == kNegInf) ? 0.f : mrun;
     if constexpr (P8) {
         float ls = 0.f;
         uint32_t q8[2][4];  // [tile][u]: keys 8 u + 4 h .. + 3, e4m3, scaled by pq

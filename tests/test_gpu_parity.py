@@ -230,6 +230,37 @@ def test_maximum_batch():
     _log(f"max batch: rows {int(done.sum())} O max-abs {err:.3e} LSE rel {lerr:.3e}")
 
 
+# The fp8 key-split kernel with K and V moved by LDS DMA (65-256 rows per unit, no user mask,
+# no P scale): two 128-row subtiles, a ragged second subtile with f16 output, one-page units
+# (every move past the unit's stream clamped), a sliding window with dual lengths, token-major
+# key/value; at the library's worker count, three workers and 200 (split units merged).
+DMA8_CASES = [
+    dict(seed=181, batch=2, max_len=700, block_x=128, num_heads_q=4, num_heads_kv=2, top_k=6,
+         mask_mode=1),
+    dict(seed=182, batch=2, max_len=600, block_x=100, num_heads_q=4, num_heads_kv=2, top_k=5,
+         mask_mode=1, out_dtype="f16"),
+    dict(seed=183, batch=3, max_len=500, block_x=128, num_heads_q=2, num_heads_kv=2, top_k=1,
+         mask_mode=0),
+    dict(seed=184, batch=2, max_len=900, block_x=80, num_heads_q=8, num_heads_kv=8, top_k=7,
+         mask_mode=1, win_left=200, win_right=0, use_seqused_q=True),
+    dict(seed=185, batch=2, max_len=600, block_x=128, num_heads_q=4, num_heads_kv=4, top_k=5,
+         mask_mode=1, tnd=True),
+]
+
+
+@pytest.mark.parametrize("case", DMA8_CASES, ids=[str(c["seed"]) for c in DMA8_CASES])
+def test_fp8_dma_key_split_all_rows(case):
+    kw = dict(case)
+    seed, tnd = kw.pop("seed"), kw.pop("tnd", False)
+    p = gi.random_problem(seed, device="cuda", dtype="fp8", **kw)
+    if tnd:
+        p = gi.to_tnd(p, keep_seqused_kv=True, tail_rows=0)
+    rows = p.block_x * p.num_heads_q // p.num_heads_kv
+    assert 64 < rows <= 256
+    for P in (0, 3, 200):
+        _full_check(p, num_workers=P, label=f"dma8 {seed} rows={rows} P={P}")
+
+
 @pytest.mark.parametrize("seed", range(200, 232))
 def test_random_sweep(seed):
     """Random combinations of every option (see gbsa_inputs.sweep_problem) on every kernel,

@@ -1494,6 +1494,79 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32d_kernel(FwdArgs a) {
                 if (nh > 0) {
                     f32x16 s[2];
                     u32x4 p[4];
+                    if constexpr (!UM) {
+                        // Intervals, one barrier per item pair. In interval i both groups run
+                        // MFMA item i (QK^T of K_i, PV of V_{i-1}): group 0 before its softmax
+                        // item i, group 1 after its softmax item i - 1, so that on each SIMD one
+                        // wave issues MFMAs while its partner exponentiates, twice per interval,
+                        // and neither waits at a barrier between the two. Moves of interval i,
+                        // from inside the MFMA item: group 0 V_{i+1}, group 1 K_{i+2} (clamped
+                        // into the stream, so every MFMA item with QK^T issues four DMA
+                        // instructions per wave). Before the barrier that ends an interval a
+                        // wave waits for all but its newest batch: a move of interval i is in
+                        // LDS from interval i + 2, its first reader, and replaces a half page
+                        // whose last reader ran in interval i - 2. Before the first interval:
+                        // K_0, K_1 and V_0 by all eight waves.
+                        dma_half16(half_src(kbase, 0), rs, kst, 2 * wave, 2, lane);
+                        dma_half16(half_src(kbase, 1), rs, kst + kDmaHalf, 2 * wave, 2, lane);
+                        dma_half16(half_src(vbase, 0), rs, vst, 2 * wave, 2, lane);
+                        wait_vm<0>();
+                        __syncthreads();
+                        auto imove = [&](int i) {
+                            const int q = min(grp == 0 ? i + 1 : i + 2, nh - 1);
+                            return ItemMove{plist + (q >> 1), q & 1, grp == 0 ? vbase : kbase,
+                                            grp == 0 ? vst + ((i + 1) & 3) * kDmaHalf
+                                                     : kst + ((i + 2) & 3) * kDmaHalf,
+                                            4 * gw};
+                        };
+                        const uint32_t umw0[8] = {};  // (no user mask)
+                        int jc_next = __builtin_amdgcn_readfirstlane(jlist[0]);
+                        auto softmax = [&](int k) {
+                            const int jc = jc_next;
+                            __builtin_amdgcn_sched_barrier(0);
+                            tr.mark(1, lane);
+                            softmax_item32<DT, false, HS>(a, s, p, colscale, trow, umw0, jc >> 2,
+                                                          k & 1, jc & 3, skv, off, lane, mrun, lrun,
+                                                          o);
+                            pin_softmax(p, lrun);
+                            __builtin_amdgcn_sched_barrier(0);
+                            tr.mark(2, lane);
+                        };
+                        // knext: the half page of this wave's next softmax item
+                        auto end_interval = [&](int knext) {
+                            const int jn = jlist[min(knext, nh - 1) >> 1];
+                            wait_vm<4>();  // all but this interval's batch are in LDS
+                            tr.mark(3, lane);
+                            __syncthreads();
+                            tr.mark(4, lane);
+                            jc_next = __builtin_amdgcn_readfirstlane(jn);
+                        };
+                        tr.mark(5, lane);
+                        __builtin_amdgcn_s_setprio(3);
+                        mfma_item32d<DT, true, false, true>(kst, vst, qc, s, p, o, lane, imove(0), rs);
+                        __builtin_amdgcn_s_setprio(0);
+                        tr.mark(6, lane);
+                        if (grp == 0) softmax(0);
+                        end_interval(grp == 0 ? 1 : 0);
+                        for (int i = 1; i < nh; ++i) {
+                            if (grp == 1) softmax(i - 1);
+                            tr.mark(5, lane);
+                            __builtin_amdgcn_s_setprio(3);
+                            mfma_item32d<DT, true, true, true>(kst + (i & 3) * kDmaHalf,
+                                                               vst + ((i - 1) & 3) * kDmaHalf, qc, s,
+                                                               p, o, lane, imove(i), rs);
+                            __builtin_amdgcn_s_setprio(0);
+                            tr.mark(6, lane);
+                            if (grp == 0) softmax(i);
+                            end_interval(grp == 0 ? i + 1 : i);
+                        }
+                        if (grp == 1) softmax(nh - 1);
+                        __builtin_amdgcn_s_setprio(3);
+                        mfma_item32d<DT, false, true>(kst, vst + ((nh - 1) & 3) * kDmaHalf, qc, s, p,
+                                                      o, lane);
+                        __builtin_amdgcn_s_setprio(0);
+                        wait_vm<0>();  // nothing may land in LDS after the task
+                    } else {
                     // Readers: MFMA item k reads K_k (K buffer k % 4) and V_{k-1} (V buffer
                     // (k - 1) % 4); group 0 runs it in slot 2 k, group 1 in slot 2 k + 1.
                     // Writers (each group's four waves issue four DMA instructions each): group 0
@@ -1587,6 +1660,7 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_pp32d_kernel(FwdArgs a) {
                     lower();
                     wait_vm<0>();  // nothing may land in LDS after the task
                     if (grp == 0) __syncthreads();
+                    }
                 }
                 __syncthreads();
 

@@ -2188,8 +2188,15 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32d_kernel(FwdArgs a) {
                     f32x16 s[2];
                     u32x4 p[4];
                     const uint32_t umw[8] = {};  // (no user mask)
-                    // Before the first slot: K_0 .. K_3, V_0 and V_1 by all eight waves
-                    // (instruction `wave` of each); group 1 then starts one slot late.
+                    // Intervals, one barrier per item pair: in interval i group 0 runs its MFMA
+                    // item i (half page 2 i) and then its softmax item i, group 1 its softmax
+                    // item i - 1 and then its MFMA item i (half page 2 i + 1), so that on each
+                    // SIMD one wave issues MFMAs while its partner exponentiates, twice per
+                    // interval. The moves of MFMA item i of group g (K_{2i+4+g}, V_{2i+2+g}) are
+                    // read in interval i + 2: before the barrier that ends an interval a wave
+                    // waits for all but its newest batch. Each replaces a half page whose last
+                    // reader ran in interval i - 2. Before the first interval: K_0 .. K_3, V_0
+                    // and V_1 by all eight waves (instruction `wave` of each).
                     auto pre_move = [&](const unsigned char* base, int q, unsigned char* dst) {
                         q = min(q, nh - 1);
                         const KvSrc src = page_half(base, plist[q >> 1], q & 1, rs);
@@ -2201,9 +2208,8 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32d_kernel(FwdArgs a) {
                     pre_move(vbase, 1, vst + kHalf8);
                     wait_vm<0>();
                     __syncthreads();
-                    if (grp == 1) __syncthreads();
-                    // the moves of this group's MFMA item k (slot q = 2 k + grp): K_{q+4} and
-                    // V_{q+2}, sources clamped into the stream (a clamped move fills a buffer
+                    // the moves of this group's MFMA item k (half page q = 2 k + grp): K_{q+4}
+                    // and V_{q+2}, sources clamped into the stream (a clamped move fills a buffer
                     // that is not read again)
                     auto move_of = [&](int k) {
                         const int q = 2 * k + grp;
@@ -2222,24 +2228,28 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32d_kernel(FwdArgs a) {
                         pin_softmax(p, lrun);
                         __builtin_amdgcn_sched_barrier(0);
                         tr.mark(2, lane);
-                        const int jn = jlist[min(k + 1, n - 1)];
-                        wait_vm<4>();  // all but the moves of this wave's last MFMA item are in LDS
+                    };
+                    // knext: the page of this wave's next softmax item
+                    auto end_interval = [&](int knext) {
+                        const int jn = jlist[min(knext, n - 1)];
+                        wait_vm<4>();  // all but this interval's moves are in LDS
                         tr.mark(3, lane);
                         __syncthreads();
                         tr.mark(4, lane);
                         jc_next = __builtin_amdgcn_readfirstlane(jn);
                     };
                     // Issue priority as in the 256-row DMA kernel: the MFMA items run raised.
-                    {
-                        moves8_now(move_of(0), kbase, vbase, rs, lane);
-                        __builtin_amdgcn_s_setprio(3);
-                        mfma_item32d8<true, false>(kst + grp * kHalf8, vst, qc, s, p, o, lane);
-                        __builtin_amdgcn_s_setprio(0);
-                        __syncthreads();
-                    }
-                    softmax_item(0);
+                    moves8_now(move_of(0), kbase, vbase, rs, lane);
+                    tr.mark(5, lane);
+                    __builtin_amdgcn_s_setprio(3);
+                    mfma_item32d8<true, false>(kst + grp * kHalf8, vst, qc, s, p, o, lane);
+                    __builtin_amdgcn_s_setprio(0);
+                    tr.mark(6, lane);
+                    if (grp == 0) softmax_item(0);
+                    end_interval(grp == 0 ? 1 : 0);
                     for (int k = 1; k < n; ++k) {
                         const int q = 2 * k + grp;
+                        if (grp == 1) softmax_item(k - 1);
                         tr.mark(5, lane);
                         __builtin_amdgcn_s_setprio(3);
                         mfma_item32d8<true, true, true>(kst + (q & 7) * kHalf8,
@@ -2247,16 +2257,15 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32d_kernel(FwdArgs a) {
                                                         lane, move_of(k), kbase, vbase, rs);
                         __builtin_amdgcn_s_setprio(0);
                         tr.mark(6, lane);
-                        __syncthreads();
-                        tr.mark(7, lane);
-                        softmax_item(k);
+                        if (grp == 0) softmax_item(k);
+                        end_interval(grp == 0 ? k + 1 : k);
                     }
+                    if (grp == 1) softmax_item(n - 1);
                     __builtin_amdgcn_s_setprio(3);
                     mfma_item32d8<false, true>(kst, vst + ((nh - 2 + grp) & 7) * kHalf8, qc, s, p, o,
                                                lane);
                     __builtin_amdgcn_s_setprio(0);
                     wait_vm<0>();  // nothing may land in LDS after the task
-                    if (grp == 0) __syncthreads();
                 }
                 __syncthreads();  // stages are free: group 1 hands its row states to group 0
 

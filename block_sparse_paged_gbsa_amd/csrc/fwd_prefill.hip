@@ -1952,20 +1952,25 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32_kernel(FwdArgs a) {
 // but its newest batch, so a move issued in slot s has landed by the end of slot s + 3, before
 // its reader in slot s + 4; both rings (eight half-page buffers each, indexed q % 8) are
 // rewritten only after their last reader. V^T comes from the e4m3 rows with the 8-bit
-// transposing read and is widened exactly to bf16 in registers right before its MFMA.
+// transposing read and is widened exactly to bf16 in registers right before its MFMA; with a
+// P quantisation scale (P8) P·V runs on fp8 MFMA straight from the e4m3 rows, as in the
+// register-staged kernel.
 //
 // LDS layout of an fp8 half page (64 rows of 128 B): DMA instruction i (0..7) writes rows
 // 8 i .. 8 i + 7 as 1 KB at byte 1024 i; 16-byte chunk c of row r (head dims 16 c ..) sits at
-// position c ^ sw8(r) of the row. sw8 permutes the three bits of (r / 2) % 8 so that both read
-// patterns are free of bank conflicts: the K fragment reads (16 consecutive rows, one chunk)
-// cover the 16 bank groups of 256 B once, and so do the transposing V reads of a half wave
-// (rows b .. b + 3 and b + 8 .. b + 11 for b a multiple of 4, two adjacent chunks).
+// position c ^ sw8(r) of the row, sw8(r) = f((r / 2) % 8) with f(x) = 4 (x1 ^ x2) + 2 x0 + x2
+// (x2 x1 x0 the bits of x): a permutation of 0..7 whose two high bits differ across x = 0..3,
+// 4..7, {0, 1, 4, 5} and {2, 3, 6, 7}. All three read patterns are then free of bank conflicts
+// (checked for every row and chunk): the K fragment reads (16 consecutive rows, one chunk) cover
+// the 16 bank groups of 256 B once, and so do the 8-bit transposing V reads of a half wave,
+// rows b .. b + 3 and b + 8 .. b + 11 (b a multiple of 4; bf16 P) or rows 8 m .. 8 m + 7 (fp8
+// P), two adjacent chunks each.
 // ---------------------------------------------------------------------------------------------
 constexpr int kHalf8 = 64 * 128;  // one fp8 half page
 
 __device__ __forceinline__ int sw8(int r) {
-    const int x = (r >> 1) & 7;
-    return ((x & 1) << 2) | (x >> 1);
+    const int x = (r >> 1) & 7, x0 = x & 1, x1 = (x >> 1) & 1, x2 = x >> 2;
+    return ((x1 ^ x2) << 2) | (x0 << 1) | x2;
 }
 
 // DMA instruction i (0..7) of the fp8 half page behind buffer resource r into buffer dst.
@@ -2007,7 +2012,7 @@ __device__ __forceinline__ void moves8_now(const ItemMove8& mv, const unsigned c
 // steps per 32-key tile) and PV of the previous one on bf16 MFMA (eight steps per tile, V^T
 // widened from e4m3 in registers), optionally issuing the item's two moves between its MFMAs
 // (entries read at steps 0 and 1, DMA at steps 4, 6, 8, 10).
-template <bool qk, bool pv, bool MOVE = false>
+template <bool qk, bool pv, bool MOVE = false, bool P8 = false>
 __device__ __forceinline__ void mfma_item32d8(const unsigned char* ks, const unsigned char* vs,
                                               const QCol32& qc, f32x16 (&s)[2],
                                               const u32x4 (&p)[4], f32x16 (&o)[4], int lane,
@@ -2015,7 +2020,9 @@ __device__ __forceinline__ void mfma_item32d8(const unsigned char* ks, const uns
                                               const unsigned char* kbase = nullptr,
                                               const unsigned char* vbase = nullptr, int rs = 0) {
     constexpr int QS = qk ? 2 : 0;
-    constexpr int VS = pv ? 8 : 0;
+    // PV steps per 32-key tile: 2 chunks x 4 d tiles, or with fp8 P two d tiles of the whole
+    // half page (64 keys) each
+    constexpr int VS = pv ? (P8 ? 2 : 8) : 0;
     constexpr int PC = QS + VS, NS = 2 * PC, D = kPipeDepth;
     const int h2 = lane >> 5;
     // K: row 32 t + lane % 32, chunks 4 e + 2 h and + 1 (head dims 64 e + 32 h ..)
@@ -2026,6 +2033,12 @@ __device__ __forceinline__ void mfma_item32d8(const unsigned char* ks, const uns
     const int m = (lane & 15) >> 1, kv = 4 * h2 + (m & 3) + 8 * (m >> 2);
     const int vseg = (lane >> 4) & 1, vsw = sw8(kv);
     const unsigned char* vrow = vs + kv * 128 + 8 * (lane & 1);
+    // fp8 P: read r (0..3) of d tile dt gives a lane keys 32 h + 8 r .. + 7 (block row
+    // (lane % 16) / 2), byte half lane % 2 of chunk 2 dt + (lane / 16) % 2. The row's swizzle
+    // sw8(32 h + 8 r + m) depends on r only through r % 2: 4 ((m / 4) % 2) + 2 ((m / 2) % 2) for
+    // even r, that ^ 5 for odd r.
+    const unsigned char* v8row = vs + (32 * h2 + m) * 128 + 8 * (lane & 1);
+    const int v8x = vseg ^ (4 * ((m >> 2) & 1) + 2 * ((m >> 1) & 1));
     const f32x16 zero = {};
     auto load = [&](int st) {
         Frag f;
@@ -2034,6 +2047,14 @@ __device__ __forceinline__ void mfma_item32d8(const unsigned char* ks, const uns
             const unsigned char* kp = krow + t * 4096;
             f.a = *(const u32x4*)(kp + 16 * ((4 * j + 2 * h2) ^ ksw));
             f.b = *(const u32x4*)(kp + 16 * ((4 * j + 2 * h2 + 1) ^ ksw));
+        } else if constexpr (P8) {
+            const int dt = 2 * t + (j - QS);  // d tile: head dims 32 dt .. 32 dt + 31
+            u32x2 r[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                r[q] = lds_read_tr8(v8row + 8 * q * 128 + 16 * ((2 * dt) ^ v8x ^ (q & 1 ? 5 : 0)));
+            f.a = (u32x4){r[0][0], r[0][1], r[1][0], r[1][1]};
+            f.b = (u32x4){r[2][0], r[2][1], r[3][0], r[3][1]};
         } else {
             const int v = j - QS, a2 = v >> 2, dt = v & 3;
             const u32x2 r = lds_read_tr8(vrow + (32 * t + 16 * a2) * 128 + 16 * ((2 * dt + vseg) ^ vsw));
@@ -2045,13 +2066,19 @@ __device__ __forceinline__ void mfma_item32d8(const unsigned char* ks, const uns
         const int t = st / PC, j = st % PC;
         if (j < QS) {
             s[t] = mfma_32x32x64_fp8(f.a, f.b, qc.q[2 * j], qc.q[2 * j + 1], j == 0 ? zero : s[t]);
+        } else if constexpr (P8) {
+            const int dt = 2 * t + (j - QS);
+            o[dt] = mfma_32x32x64_fp8(f.a, f.b, p[0], p[1], o[dt]);
         } else {
             const int v = j - QS, a2 = v >> 2, dt = v & 3;
             const u32x2 w0 = fp8x4_to_bf16x4(f.a[0]), w1 = fp8x4_to_bf16x4(f.a[1]);
             o[dt] = mfma_32x32x16<kBF16>((u32x4){w0[0], w0[1], w1[0], w1[1]}, p[2 * t + a2], o[dt]);
         }
     };
-    static_assert(!MOVE || NS >= 11, "the moves need eleven steps");
+    // the moves' DMA instructions go out at steps 4, 6, 8, 10 (every other MFMA), or with fp8 P
+    // (eight steps) at 4, 5, 6, 7
+    constexpr int kDs = P8 ? 1 : 2;
+    static_assert(!MOVE || NS > 4 + 3 * kDs, "the moves need their steps");
     u32x4 ek, ev;
     rsrc_t rk, rv;
     Frag fr[D];
@@ -2073,15 +2100,16 @@ __device__ __forceinline__ void mfma_item32d8(const unsigned char* ks, const uns
                 const KvSrc src = page_half(vbase, ev, mv.vhalf, rs);
                 rv = make_rsrc(src.p, src.records);
             }
-            if (st == 4 || st == 6) dma8_one(rk, rs, mv.kdst, mv.i0 + (st - 4) / 2, lane);
-            if (st == 8 || st == 10) dma8_one(rv, rs, mv.vdst, mv.i0 + (st - 8) / 2, lane);
+            if (st == 4 || st == 4 + kDs) dma8_one(rk, rs, mv.kdst, mv.i0 + (st - 4) / kDs, lane);
+            if (st == 4 + 2 * kDs || st == 4 + 3 * kDs)
+                dma8_one(rv, rs, mv.vdst, mv.i0 + (st - 4 - 2 * kDs) / kDs, lane);
         }
         compute(st, f);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
 
-template <int OUT, int LAYOUT>
+template <int OUT, int LAYOUT, bool P8 = false>
 __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32d_kernel(FwdArgs a) {
     constexpr int DT = kFP8;
     constexpr int R = 128;
@@ -2141,6 +2169,7 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32d_kernel(FwdArgs a) {
                 int trow;
                 bool rvalid;
                 load_q32<DT>(a, it, t0, rows_exist, row0, lane, qc, colscale, trow, rvalid);
+                const float pq = P8 ? p_quant(a, it, row0, rows_exist, lane) : 1.f;
                 f32x16 o[4];
 #pragma unroll
                 for (int dt = 0; dt < 4; ++dt) o[dt] = (f32x16){};
@@ -2223,8 +2252,9 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32d_kernel(FwdArgs a) {
                         const int jc = jc_next;
                         __builtin_amdgcn_sched_barrier(0);
                         tr.mark(1, lane);
-                        softmax_item32<DT, false>(a, s, p, colscale, trow, umw, jc >> 2, grp,
-                                                  jc & 3, skv, off, lane, mrun, lrun, o);
+                        softmax_item32<DT, false, false, P8>(a, s, p, colscale, trow, umw, jc >> 2,
+                                                             grp, jc & 3, skv, off, lane, mrun, lrun,
+                                                             o, pq);
                         pin_softmax(p, lrun);
                         __builtin_amdgcn_sched_barrier(0);
                         tr.mark(2, lane);
@@ -2242,7 +2272,7 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32d_kernel(FwdArgs a) {
                     moves8_now(move_of(0), kbase, vbase, rs, lane);
                     tr.mark(5, lane);
                     __builtin_amdgcn_s_setprio(3);
-                    mfma_item32d8<true, false>(kst + grp * kHalf8, vst, qc, s, p, o, lane);
+                    mfma_item32d8<true, false, false, P8>(kst + grp * kHalf8, vst, qc, s, p, o, lane);
                     __builtin_amdgcn_s_setprio(0);
                     tr.mark(6, lane);
                     if (grp == 0) softmax_item(0);
@@ -2252,9 +2282,9 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32d_kernel(FwdArgs a) {
                         if (grp == 1) softmax_item(k - 1);
                         tr.mark(5, lane);
                         __builtin_amdgcn_s_setprio(3);
-                        mfma_item32d8<true, true, true>(kst + (q & 7) * kHalf8,
-                                                        vst + ((q - 2) & 7) * kHalf8, qc, s, p, o,
-                                                        lane, move_of(k), kbase, vbase, rs);
+                        mfma_item32d8<true, true, true, P8>(kst + (q & 7) * kHalf8,
+                                                            vst + ((q - 2) & 7) * kHalf8, qc, s, p, o,
+                                                            lane, move_of(k), kbase, vbase, rs);
                         __builtin_amdgcn_s_setprio(0);
                         tr.mark(6, lane);
                         if (grp == 0) softmax_item(k);
@@ -2262,8 +2292,8 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32d_kernel(FwdArgs a) {
                     }
                     if (grp == 1) softmax_item(n - 1);
                     __builtin_amdgcn_s_setprio(3);
-                    mfma_item32d8<false, true>(kst, vst + ((nh - 2 + grp) & 7) * kHalf8, qc, s, p, o,
-                                               lane);
+                    mfma_item32d8<false, true, false, P8>(kst, vst + ((nh - 2 + grp) & 7) * kHalf8, qc,
+                                                          s, p, o, lane);
                     __builtin_amdgcn_s_setprio(0);
                     wait_vm<0>();  // nothing may land in LDS after the task
                 }
@@ -2297,7 +2327,7 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32d_kernel(FwdArgs a) {
                             for (int e = 0; e < 4; ++e) o[dt][4 * g4 + e] = o[dt][4 * g4 + e] * a0 + x[e] * a1;
                         }
                     write_rows32<DT, OUT>(a, it, complete, 2 * w + (sa > 0 ? 0 : 1), row0, lane, trow,
-                                          rvalid, mrun, lrun, o);
+                                          rvalid, mrun, lrun, o, 1.f / pq);
                 }
                 __syncthreads();  // LDS is reused by the next task
                 if (!complete) {
@@ -2374,8 +2404,7 @@ hipError_t launch_l(const FwdArgs& a, int rows, hipStream_t s) {
                 return launch_k<fwd_prefill_ks32_kernel<kF16, OUT, LAYOUT, false, true>, true>(a, s);
         if constexpr (kP8)
             if (a.ps != nullptr)
-                return launch_k<fwd_prefill_ks32_kernel<kFP8, OUT, LAYOUT, false, false, true>,
-                                true>(a, s);
+                return launch_k<fwd_prefill_ks32d_kernel<OUT, LAYOUT, true>, true>(a, s);
         // fp8 without a user mask: the DMA kernel
         if constexpr (DT == kFP8 && !UM)
             return launch_k<fwd_prefill_ks32d_kernel<OUT, LAYOUT>, true>(a, s);

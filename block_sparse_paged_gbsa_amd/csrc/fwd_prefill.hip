@@ -1272,12 +1272,14 @@ constexpr int kDmaStride = 1088;             // bytes between the DMA instructio
 constexpr int kDmaHalf = 16 * kDmaStride;    // one half page
 
 // DMA instruction i (0..15) of the half page behind buffer resource r into the half-page buffer
-// dst. No destination register: the data goes to LDS; completion is awaited with vmcnt.
+// dst. No destination register: the data goes to LDS; completion is awaited with vmcnt. An
+// instruction that reads M0 for an LDS DMA needs one wait state after the M0 write (the
+// compiler keeps that distance for its own buffer-to-LDS loads), hence the nop.
 __device__ __forceinline__ void dma_one(rsrc_t r, int rs, unsigned char* dst, int i, int lane) {
     const int row = i + 16 * (lane >> 4);
     const int voff = row * rs + 16 * ((lane & 15) ^ (i >> 2));
     const uint32_t m0 = (uint32_t)(uintptr_t)(GBSA_LDS unsigned char*)(dst + i * kDmaStride);
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                  :
                  : "s"(m0), "v"(voff), "s"(r)
                  : "memory", "m0");
@@ -1978,7 +1980,7 @@ __device__ __forceinline__ void dma8_one(rsrc_t r, int rs, unsigned char* dst, i
     const int row = 8 * i + (lane >> 3);
     const int voff = row * rs + 16 * ((lane & 7) ^ sw8(row));
     const uint32_t m0 = (uint32_t)(uintptr_t)(GBSA_LDS unsigned char*)(dst + i * 1024);
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                  :
                  : "s"(m0), "v"(voff), "s"(r)
                  : "memory", "m0");

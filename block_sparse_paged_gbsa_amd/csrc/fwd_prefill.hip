@@ -1944,19 +1944,16 @@ __global__ __launch_bounds__(512, 1) void fwd_prefill_ks32_kernel(FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// The 128-row key-split kernel with K and V moved by LDS DMA (fp8 key/value, no user mask, P in
-// bf16). Same slots and items as fwd_prefill_ks32_kernel, but the half pages reach LDS as e4m3
-// rows by `buffer_load ... lds` issued from inside the MFMA items, so no load has to land within
-// the slot that issues it: global half page q (group q % 2's item q / 2) has K_q read in slot q
-// and V_q in slot q + 2; the group running its MFMA item in slot s moves K_{s+4} and V_{s+2}
-// (clamped into the stream, so every item issues the same four instructions per wave), each wave
-// two DMA instructions of each. Before the barrier that ends its softmax item a wave waits for all
-// but its newest batch, so a move issued in slot s has landed by the end of slot s + 3, before
-// its reader in slot s + 4; both rings (eight half-page buffers each, indexed q % 8) are
-// rewritten only after their last reader. V^T comes from the e4m3 rows with the 8-bit
-// transposing read and is widened exactly to bf16 in registers right before its MFMA; with a
-// P quantisation scale (P8) P·V runs on fp8 MFMA straight from the e4m3 rows, as in the
-// register-staged kernel.
+// The 128-row key-split kernel with K and V moved by LDS DMA (fp8 key/value, no user mask). The
+// items of fwd_prefill_ks32_kernel (group g takes half page g of every page: half page q is
+// group q % 2's item q / 2), with the half pages reaching LDS as e4m3 rows by `buffer_load ...
+// lds` issued from inside the MFMA items, so no load has to land within the item that issues it,
+// and one barrier per item pair (the schedule is with the kernel). MFMA item k of group g reads
+// K_q and V_{q-2} (q = 2 k + g) and moves K_{q+4} and V_{q+2} (clamped into the stream, so every
+// item issues the same four instructions per wave), each wave two DMA instructions of each; both
+// rings hold eight half pages (indexed q % 8). V^T comes from the e4m3 rows with the 8-bit
+// transposing read and is widened exactly to bf16 in registers right before its MFMA; with a P
+// quantisation scale (P8) P·V runs on fp8 MFMA straight from the e4m3 rows.
 //
 // LDS layout of an fp8 half page (64 rows of 128 B): DMA instruction i (0..7) writes rows
 // 8 i .. 8 i + 7 as 1 KB at byte 1024 i; 16-byte chunk c of row r (head dims 16 c ..) sits at

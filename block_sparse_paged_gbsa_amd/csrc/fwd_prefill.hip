@@ -871,25 +871,67 @@ __device__ __forceinline__ void softmax_item32(const FwdArgs& a, f32x16 (&s)[2],
         lrun = lrun * alpha + ls;
         return;
     }
-    float mx = kNegInf;
+    // exponentials of the item against the shift mu, packed as the PV B operands; returns the
+    // lane's sum of the fp32 values. Chunk c = 2 t + a: elements 8 a .. 8 a + 7 of tile t.
+    auto exp_pack = [&](float mu) {
+        float ls = 0.f;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+        for (int c = 0; c < 4; ++c) {
+            float pv[8];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[t][i]);
-    mx = pair_max(mx, true);
-    const float bmax = mx == kNegInf ? kNegInf : mx * colscale;
-    float alpha = 1.f;
-    // The running max, its exp2 and the O rescale only where some row's max moves (always
-    // on a row's first visible block; rarely later with the lazy max): elsewhere alpha is 1.
-    if (__builtin_amdgcn_ballot_w64(P8 ? bmax > mrun : bmax > mrun + kLazyMax)) {
-        const float mnew = P8 ? fmaxf(mrun, bmax) : lazy_max(mrun, bmax);
-        alpha = fast_exp2(mrun - ((mnew == kNegInf) ? 0.f : mnew));
-        mrun = mnew;
+            for (int e = 0; e < 8; ++e) {
+                pv[e] = fast_exp2(__builtin_fmaf(s[c >> 1][8 * (c & 1) + e], colscale, -mu));
+                ls += pv[e];
+            }
+            p[c] = (u32x4){pack2<PT>(pv[0], pv[1]), pack2<PT>(pv[2], pv[3]),
+                           pack2<PT>(pv[4], pv[5]), pack2<PT>(pv[6], pv[7])};
+        }
+        return ls;
+    };
+    if constexpr (!P8) {
+        // Against the running max as it stands, without the block max: every probability is at
+        // most the lane's sum, so a sum within 2^kLazyMax keeps the lazy bound. Only where some
+        // lane's sum leaves it (or is not a number), or a row has seen no key yet, is the block
+        // max taken and the item recomputed with the running max moved to it (exact, as the
+        // FA article's online softmax); there O is rescaled. The max is the one the exponentials
+        // use, so the result does not depend on when it moves.
+        float ls = exp_pack((mrun == kNegInf) ? 0.f : mrun);
+        float alpha = 1.f;
+        if (__builtin_amdgcn_ballot_w64(mrun == kNegInf || !(ls <= kLazyBound))) {
+            float mx = kNegInf;
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
-    }
-    const float muse = (mrun == kNegInf) ? 0.f : mrun;
-    if constexpr (P8) {
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[t][i]);
+            mx = pair_max(mx, true);
+            const float mnew = fmaxf(mrun, mx == kNegInf ? kNegInf : mx * colscale);
+            const float muse = (mnew == kNegInf) ? 0.f : mnew;
+            alpha = fast_exp2(mrun - muse);
+            mrun = mnew;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+            ls = exp_pack(muse);
+        }
+        lrun = lrun * alpha + ls;
+    } else {
+        // fp8 P: the exact running max, moved (with its exp2 and the O rescale) only where some
+        // row's block max exceeds it; elsewhere alpha is 1
+        float mx = kNegInf;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[t][i]);
+        mx = pair_max(mx, true);
+        const float bmax = mx == kNegInf ? kNegInf : mx * colscale;
+        float alpha = 1.f;
+        if (__builtin_amdgcn_ballot_w64(bmax > mrun)) {
+            const float mnew = fmaxf(mrun, bmax);
+            alpha = fast_exp2(mrun - ((mnew == kNegInf) ? 0.f : mnew));
+            mrun = mnew;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+        }
+        const float muse = (mrun == kNegInf) ? 0.f : mrun;
         float ls = 0.f;
         uint32_t q8[2][4];  // [tile][u]: keys 8 u + 4 h .. + 3, e4m3, scaled by pq
 #pragma unroll
@@ -916,21 +958,7 @@ __device__ __forceinline__ void softmax_item32(const FwdArgs& a, f32x16 (&s)[2],
         p[0] = (u32x4){b[0], b[1], b[2], b[3]};
         p[1] = (u32x4){b[4], b[5], b[6], b[7]};
         lrun = lrun * alpha + ls;
-        return;
     }
-    float ls = 0.f;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {  // chunk c = 2 t + a: elements 8 a .. 8 a + 7 of tile t
-        float pv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            pv[e] = fast_exp2(__builtin_fmaf(s[c >> 1][8 * (c & 1) + e], colscale, -muse));
-            ls += pv[e];
-        }
-        p[c] = (u32x4){pack2<PT>(pv[0], pv[1]), pack2<PT>(pv[2], pv[3]), pack2<PT>(pv[4], pv[5]),
-                       pack2<PT>(pv[6], pv[7])};
-    }
-    lrun = lrun * alpha + ls;
 }
 
 // Fixes the softmax item's results where they are computed. The exponentials and conversions

@@ -24,11 +24,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 // Lazy rescaling: the running max of a column only moves when a new block exceeds it by more
 // than kLazyMax (log2 units). Probabilities are then bounded by 2^kLazyMax = 256, which fp32
 // sums and 16-bit P represent without loss of relative precision, and the O rescale is skipped
-// for most blocks. The result is unchanged: numerator and denominator use the same max. (The
-// 32-row prefill items test the same bound on the lane's sum of probabilities instead of on the
-// block max, which they then only take where the sum exceeds kLazyBound.)
+// for most blocks. The result is unchanged: numerator and denominator use the same max.
 constexpr float kLazyMax = 8.f;
-constexpr float kLazyBound = 256.f;  // 2^kLazyMax
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_inff();
 

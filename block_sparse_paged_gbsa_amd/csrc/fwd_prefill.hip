@@ -780,6 +780,10 @@ __device__ __forceinline__ void umask_words32(const FwdArgs& a, const UMaskRow& 
             w[4 * t + q] = umask_word(a, um, (int64_t)j * 128 + half * 64 + 32 * t + 8 * q + 4 * h2);
 }
 
+// The lazy bound of the running max (device_common.hpp) on probabilities: 2^kLazyMax. The 32-row
+// softmax items test it on the lane's sum of probabilities, which bounds each of them.
+constexpr float kLazyBound = 256.f;
+
 // HS (f16 only): softmax precision 1 of the GBSA article's "softmax precision" section. The
 // online-softmax stage runs in the output's 16-bit type: the logits are rounded to f16, and the
 // scaling and max subtraction (packed f16 FMA) and the exponentials are f16; the block max is

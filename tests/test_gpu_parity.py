@@ -418,6 +418,62 @@ def test_keys_past_visible_length_never_reach_the_output(case, layout):
 
 
 # ---------------------------------------------------------------------------
+# running max that jumps: the softmax item's exact path (block max taken, O rescaled)
+# ---------------------------------------------------------------------------
+
+# one case per kernel with the 32-row softmax item: 256-row DMA (bf16, f16, with a user mask),
+# 16-bit key-split, fp8 DMA key-split and fp8 register-staged 256-row
+JUMP_CASES = [
+    dict(seed=181, dtype="bf16", block_x=64, num_heads_q=16, num_heads_kv=2),
+    dict(seed=182, dtype="f16", block_x=64, num_heads_q=16, num_heads_kv=2, mask_mode=0),
+    dict(seed=183, dtype="bf16", block_x=64, num_heads_q=16, num_heads_kv=2, umask=True),
+    dict(seed=184, dtype="bf16", block_x=32, num_heads_q=8, num_heads_kv=2),
+    dict(seed=185, dtype="fp8", block_x=32, num_heads_q=8, num_heads_kv=2),
+    dict(seed=186, dtype="fp8", block_x=64, num_heads_q=16, num_heads_kv=2, out_dtype="f16"),
+]
+
+
+def _jumping_logits(p):
+    """The same problem with logits that grow along each sequence: K of logical block j scaled
+    by (1 + j) and Q by 3 (fp8: K of block j re-quantised at (1 + j) / blocks, and the Q
+    dequant scales times 12, so that no byte leaves the e4m3 range), so that block maxima rise
+    by several log2 units from one selected block to the next and most softmax items leave the
+    lazy bound of the running max (the oracle reads the rescaled values). P is then close to
+    one-hot and O close to single rows of V, so V is scaled by 1/4 (exactly; fp8 through its
+    dequant scales): with |O| up to 4.5 one rounding of a bf16 output alone costs up to 2^-6,
+    the whole bf16 bar, while below 2 it costs at most 2^-8 and the bar measures the kernel."""
+    k = p.k.clone()
+    seen = set()
+    for b in range(p.batch):
+        for j, phys in enumerate(p.block_table[b]):
+            if phys < 0 or int(phys) in seen:
+                continue
+            seen.add(int(phys))
+            f = float(1 + j) if p.dtype != "fp8" else float(1 + j) / float(len(p.block_table[b]))
+            k[int(phys)] = (k[int(phys)].float() * f).to(k.dtype)
+    if p.dtype == "fp8":
+        return dataclasses.replace(p, k=k, q_scale=(p.q_scale * 12.0).astype(np.float32),
+                                   v_scale=(p.v_scale * 0.25).astype(np.float32),
+                                   name=p.name + "_jump")
+    q = (p.q.float() * 3.0).to(p.q.dtype)
+    v = (p.v.float() * 0.25).to(p.v.dtype)
+    return dataclasses.replace(p, q=q, k=k, v=v, name=p.name + "_jump")
+
+
+@pytest.mark.parametrize("case", JUMP_CASES, ids=[str(c["seed"]) for c in JUMP_CASES])
+def test_running_max_jumps(case):
+    kw = dict(case)
+    seed, umask = kw.pop("seed"), kw.pop("umask", False)
+    kw.setdefault("mask_mode", 1)
+    p = _jumping_logits(gi.random_problem(seed, device="cuda", batch=2, max_len=700, top_k=6,
+                                          **kw))
+    if umask:
+        p = gi.with_atten_mask(p, seed, density=0.2)
+    for P in (0, 7):
+        _full_check(p, num_workers=P, label=f"jump{seed} P={P}")
+
+
+# ---------------------------------------------------------------------------
 # user attention masks and the top-left causal mask
 # ---------------------------------------------------------------------------
 

@@ -765,8 +765,6 @@ __device__ __forceinline__ void mfma_item32(const unsigned char* ks, const unsig
     }
 }
 
-// Softmax item on 32x32 tiles for half page `half` of block j (class cls): mask, lazy running
-// max (in-lane max over 32 keys, then the lane pair l, l ^ 32), rescale, P^T as PV B operands.
 // User-mask words of one softmax item (keys half * 64 .. + 63 of block j) for this lane's
 // row, in element order: word 4 t + q holds keys 32 t + 8 q + 4 h .. + 3 of the half page.
 // Loaded one MFMA item ahead of their use, so the latency hides behind it.
@@ -784,6 +782,12 @@ __device__ __forceinline__ void umask_words32(const FwdArgs& a, const UMaskRow& 
 // softmax items test it on the lane's sum of probabilities, which bounds each of them.
 constexpr float kLazyBound = 256.f;
 
+// Softmax item on 32x32 tiles for half page `half` of block j (class cls): mask, then P^T as
+// the PV B operands and the row sums against the running max. The block max (in-lane max over
+// 32 keys, then the lane pair l, l ^ 32) is taken on every item by the fp8-P and HS forms, which
+// move the running max where the block max exceeds it (fp8 P) or exceeds it by more than the
+// lazy bound (HS); the 16-bit-P form takes it only where the item leaves the lazy bound or a row
+// has seen no key yet. O is rescaled only where the running max moves.
 // HS (f16 only): softmax precision 1 of the GBSA article's "softmax precision" section. The
 // online-softmax stage runs in the output's 16-bit type: the logits are rounded to f16, and the
 // scaling and max subtraction (packed f16 FMA) and the exponentials are f16; the block max is

@@ -255,8 +255,11 @@ constexpr int kQueueStride = 4;    // words between queue counters
 constexpr int kQueueDone = kQueues * kQueueStride;  // word of the finished-workgroup counter
 
 // Thread 0: next task of the queues, starting at this workgroup's own (home) and moving on
-// when one is empty; -1 when all are. `probe` (thread 0's) counts the queues found empty.
-__device__ __forceinline__ int task_grab(int32_t* q, int ntask, int home, int& probe) {
+// when one is empty; -1 when all are. `probe` (thread 0's) counts the queues found empty. A
+// queue hands out its tasks in list order, or from its end (desc): with a causal or windowed
+// selection, later q-blocks of a head select more blocks, so from the end the largest units go
+// first and the smallest make up the tail.
+__device__ __forceinline__ int task_grab(int32_t* q, int ntask, int home, int& probe, bool desc) {
     while (probe < kQueues) {
         const int x = (home + probe) & (kQueues - 1);
         const int lo = (int)((int64_t)ntask * x / kQueues);
@@ -264,11 +267,19 @@ __device__ __forceinline__ int task_grab(int32_t* q, int ntask, int home, int& p
         if (hi > lo) {
             const int t = __hip_atomic_fetch_add(q + x * kQueueStride, 1, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
-            if (t < hi - lo) return lo + t;
+            if (t < hi - lo) return desc ? hi - 1 - t : lo + t;
         }
         ++probe;
     }
     return -1;
+}
+
+// Whether the queues go from their ends: when the units' mean cost (selected blocks + 1) is
+// under 3/4 of the most a unit can cost, so that unit sizes vary widely (dense causal
+// selections: 1 .. topK blocks). With nearly equal units the list order measured faster.
+__device__ __forceinline__ bool tasks_descending(const FwdArgs& a, int U) {
+    const uint64_t W = (uint64_t)(uint32_t)a.meta[4] | ((uint64_t)(uint32_t)a.meta[5] << 32);
+    return 4 * W < 3 * (uint64_t)U * (uint64_t)(a.topK + 1);
 }
 
 // Thread 0, once per workgroup after its last (failed) grab: the last workgroup of the grid
@@ -312,14 +323,16 @@ __device__ __forceinline__ void run_tasks(const FwdArgs& a, int U, int* word, F&
         body(opaque_args(), Task{w, lin - w * a.nst, read_bound(a.meta, w), read_bound(a.meta, w + 1)});
         return;
     }
-    if (threadIdx.x == 0) word[1] = 0;
+    // word[1]: the count of queues found empty (low byte) and the queue order (bit 8)
+    if (threadIdx.x == 0) word[1] = (a.unit_tasks && tasks_descending(a, U)) ? 256 : 0;
     for (;;) {
         if (threadIdx.x == 0) {
             int lin = -1;
             if (a.unit_tasks) {
-                int probe = word[1];
-                lin = task_grab(a.ws_queue, U * a.nst, blockIdx.x & (kQueues - 1), probe);
-                word[1] = probe;
+                int probe = word[1] & 255;
+                const bool desc = (word[1] >> 8) != 0;
+                lin = task_grab(a.ws_queue, U * a.nst, blockIdx.x & (kQueues - 1), probe, desc);
+                word[1] = (word[1] & ~255) | probe;
             } else if (word[1] == 0) {
                 lin = xcd_remap(blockIdx.x, gridDim.x);  // the workgroup's one worker task
                 word[1] = 1;
